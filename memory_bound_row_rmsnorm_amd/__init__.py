@@ -1,0 +1,24 @@
+"""MI355X (gfx950) row RMSNorm forward: HIP kernels behind a C-ABI library.
+
+``rmsnorm_fwd(x, w, eps, offset)`` computes, per row of a 2-D bf16/fp16 tensor,
+``y = x * rsqrt(mean(x^2) + eps) * (offset + w)`` and the per-row fp32 ``rstd``
+("Rmsnorm Kernel Optimization", Overview; "Why cutile's rmsnorm required full
+register", kernel listing).  Every step runs in the hand-written kernels of
+``librmsnorm_mi355x.so``; Python only marshals pointers, sizes and the stream.
+
+The binding is imported on first use so that ``workloads`` (input generation
+only) can be imported on a machine without the built library.
+"""
+from __future__ import annotations
+
+__all__ = [
+    "rmsnorm_fwd", "rmsnorm_fwd_out", "plan_query", "status_string", "library_path",
+    "RmsnormError",
+]
+
+
+def __getattr__(name):
+    if name in __all__:
+        from . import binding
+        return getattr(binding, name)
+    raise AttributeError(name)
