@@ -1,0 +1,174 @@
+/*
+ * rmsnorm.h -- C ABI of librmsnorm_mi355x.so, the row RMSNorm forward for
+ * AMD Instinct MI355X (gfx950).
+ *
+ * Operation (per row m of a row-major [M, N] matrix):
+ *
+ *     rstd[m] = 1 / sqrt( (1/N) * sum_j x[m,j]^2 + eps )
+ *     y[m,j]  = x[m,j] * rstd[m] * (offset + w[j])
+ *
+ * Defined by "Rmsnorm Kernel Optimization", section "Overview" (the
+ * normalisation: x over the root of the mean square plus eps, times the
+ * weight) and by the kernel listing in the opening report of "Why cutile's
+ * rmsnorm required full register" (the weight enters as offset + w, with
+ * offset 0.0 for Llama-style and 1.0 for Gemma3-style models; the mean
+ * divides by the true width N; eps and offset are fp32; the per-row
+ * reciprocal root is written out for a backward pass; y is cast to the
+ * input dtype once, at the end).  x and w are read as bf16 or fp16, all
+ * arithmetic is fp32 ("Rmsnorm Kernel Optimization", Key Optimizations and
+ * Common Pitfalls: the sum of squares must not run in the 16-bit type),
+ * the root is the hardware reciprocal square root, and y is rounded to the
+ * input dtype with round-to-nearest-even.
+ *
+ * Conventions shared by every entry point:
+ *   - Pointers named x, w, y, rstd are DEVICE memory owned by the caller; the
+ *     library never allocates, frees or synchronises.
+ *   - x and y are contiguous row-major [M, N] of `dtype`; w is [N] of `dtype`;
+ *     rstd is [M] fp32.
+ *   - y == x (exactly the same pointer) is allowed and normalises in place;
+ *     any other overlap of y with x or w, or of rstd with x, w or y, is
+ *     rejected.
+ *   - Work is enqueued on `stream` (a hipStream_t; NULL is the null stream)
+ *     and the call returns without waiting.  Faults during execution show up
+ *     at the caller's next synchronisation, as usual for HIP.
+ *   - Argument errors are detected on the host BEFORE any HIP call and are
+ *     returned as a status; nothing is enqueued then.
+ *   - Calls are thread-safe.  The only library state is a per-device cache of
+ *     device properties and kernel occupancy, filled on first use.
+ */
+#ifndef RMSNORM_MI355X_H
+#define RMSNORM_MI355X_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Element type of x, w and y. */
+typedef enum rmsnorm_dtype {
+    RMSNORM_BF16 = 0,
+    RMSNORM_FP16 = 1
+} rmsnorm_dtype_t;
+
+/* Status codes. */
+typedef enum rmsnorm_status {
+    RMSNORM_OK = 0,
+    RMSNORM_ERR_NULL = 1,     /* a required pointer is NULL (M > 0) */
+    RMSNORM_ERR_SHAPE = 2,    /* M < 0, N <= 0, or M*N*2 bytes overflows int64 */
+    RMSNORM_ERR_DTYPE = 3,    /* dtype is not an rmsnorm_dtype_t value */
+    RMSNORM_ERR_SCALAR = 4,   /* eps < 0 or non-finite, or offset non-finite */
+    RMSNORM_ERR_OVERLAP = 5,  /* buffers overlap other than y == x */
+    RMSNORM_ERR_HIP = 6,      /* a HIP runtime call failed (text: rmsnorm_last_error) */
+    RMSNORM_ERR_DEVICE = 7,   /* current device is not gfx950 */
+    RMSNORM_ERR_PLAN = 8      /* an explicit plan does not fit this call */
+} rmsnorm_status_t;
+
+/* Kernel families. */
+typedef enum rmsnorm_variant {
+    RMSNORM_VARIANT_AUTO = 0,    /* let the library choose (rmsnorm_plan_query) */
+    RMSNORM_VARIANT_WAVE = 1,    /* one or more rows per 64-lane wavefront, no LDS */
+    RMSNORM_VARIANT_BLOCK = 2,   /* one row per workgroup, cross-wave LDS reduce */
+    RMSNORM_VARIANT_GENERIC = 3  /* any N and alignment: scalar I/O, row read twice */
+} rmsnorm_variant_t;
+
+/*
+ * Launch plan: which kernel runs and how the rows are spread over the chip.
+ *
+ *   variant           RMSNORM_VARIANT_WAVE / _BLOCK / _GENERIC
+ *   vec_elems         elements per lane access: 8 (16-byte loads and stores)
+ *                     for WAVE and BLOCK, 1 for GENERIC
+ *   lanes_per_row     WAVE: lanes sharing one row (16, 32 or 64);
+ *                     BLOCK and GENERIC: threads per row (= block_threads)
+ *   vectors_per_lane  16-byte vectors each lane holds per row (WAVE, BLOCK);
+ *                     lanes_per_row * vectors_per_lane * vec_elems >= N
+ *   row_slots         WAVE: row slots per wave per trip; a slot is
+ *                     64/lanes_per_row rows, and all of a trip's loads are
+ *                     issued before its first reduction.  1 otherwise
+ *   block_threads     workgroup size (a multiple of 64, at most 1024)
+ *   grid              workgroups launched.  When grid times the rows one
+ *                     workgroup covers per trip is below M the workgroups
+ *                     loop over rows (persistent grid) and keep offset + w
+ *                     in registers across trips
+ *   rows_per_trip     rows one workgroup covers per loop trip (derived)
+ *   trips             loop trips of the busiest workgroup (derived)
+ */
+typedef struct rmsnorm_plan {
+    int32_t variant;
+    int32_t vec_elems;
+    int32_t lanes_per_row;
+    int32_t vectors_per_lane;
+    int32_t row_slots;
+    int32_t block_threads;
+    int64_t grid;
+    int64_t rows_per_trip;
+    int64_t trips;
+} rmsnorm_plan_t;
+
+/*
+ * Row RMSNorm forward: y and rstd from x and w, as defined at the top.
+ *   x      [M, N] dtype, device      w    [N] dtype, device
+ *   y      [M, N] dtype, device      rstd [M] fp32, device
+ *   M >= 0 rows (M == 0 is a no-op returning RMSNORM_OK), N >= 1 columns
+ *   eps    >= 0, finite, added to the mean of squares inside the root
+ *   offset finite, added to every weight (0.0 Llama-style, 1.0 Gemma-style)
+ *   dtype  rmsnorm_dtype_t
+ *   stream hipStream_t (NULL = null stream)
+ * The library picks the kernel (rmsnorm_plan_query).  Returns a status.
+ */
+int rmsnorm_fwd(const void* x, const void* w, void* y, float* rstd,
+                int64_t M, int64_t N, float eps, float offset, int dtype, void* stream);
+
+/*
+ * Same as rmsnorm_fwd but with an explicit launch plan (from
+ * rmsnorm_plan_query, possibly edited: variant, lanes_per_row,
+ * vectors_per_lane, row_slots, block_threads and grid are honoured; the
+ * derived fields are ignored).  Returns RMSNORM_ERR_PLAN, before any HIP
+ * call, if the plan's kernel does not exist, does not cover N, or needs an
+ * alignment the pointers lack.  For benchmarks and tests of each kernel.
+ */
+int rmsnorm_fwd_with_plan(const void* x, const void* w, void* y, float* rstd,
+                          int64_t M, int64_t N, float eps, float offset, int dtype,
+                          const rmsnorm_plan_t* plan, void* stream);
+
+/*
+ * The plan rmsnorm_fwd would use for these sizes and pointers (only their
+ * alignment is looked at; they may be NULL, which counts as aligned).
+ * cu_count > 0 plans for that many compute units without touching HIP (host
+ * only); cu_count <= 0 asks the current device.  Writes *out and returns a
+ * status.
+ */
+int rmsnorm_plan_query(int64_t M, int64_t N, int dtype,
+                       const void* x, const void* w, const void* y,
+                       int32_t cu_count, rmsnorm_plan_t* out);
+
+/*
+ * Compiled resources of the kernel a plan selects, read from the loaded code
+ * object (needs a device).  Any of the outputs may be NULL.
+ *   vgprs       vector registers per lane (arch + accumulation)
+ *   sgprs       scalar registers per wave
+ *   lds_bytes   static LDS per workgroup
+ *   scratch     private (spill) bytes per lane; 0 means no spills
+ */
+int rmsnorm_plan_resources(const rmsnorm_plan_t* plan, int dtype,
+                           int32_t* vgprs, int32_t* sgprs, int32_t* lds_bytes,
+                           int32_t* scratch);
+
+/* Static name of a status code ("RMSNORM_OK", ...); never NULL. */
+const char* rmsnorm_status_string(int status);
+
+/*
+ * Detail text of the most recent failing call on the calling thread (for
+ * RMSNORM_ERR_HIP it holds the HIP error string); "" if none.  The pointer
+ * stays valid until the next library call on the same thread.
+ */
+const char* rmsnorm_last_error(void);
+
+/* Library version as major*10000 + minor*100 + patch. */
+int rmsnorm_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* RMSNORM_MI355X_H */

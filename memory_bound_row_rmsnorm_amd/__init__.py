@@ -12,8 +12,8 @@ only) can be imported on a machine without the built library.
 from __future__ import annotations
 
 __all__ = [
-    "rmsnorm_fwd", "rmsnorm_fwd_out", "plan_query", "status_string", "library_path",
-    "RmsnormError",
+    "rmsnorm_fwd", "rmsnorm_fwd_out", "plan_query", "plan_resources", "status_string",
+    "library_path", "version", "Plan", "RmsnormError",
 ]
 
 

@@ -1,0 +1,197 @@
+"""ctypes binding of librmsnorm_mi355x.so (include/rmsnorm.h).
+
+Argument marshalling only: every step of the forward runs in the HIP kernels.
+PyTorch provides device memory and the current stream.  If the library is not
+built, importing this module raises; there is no fallback implementation.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIBRARY = os.path.join(_HERE, "librmsnorm_mi355x.so")
+
+RMSNORM_BF16 = 0
+RMSNORM_FP16 = 1
+DTYPE_CODES = {torch.bfloat16: RMSNORM_BF16, torch.float16: RMSNORM_FP16}
+DTYPE_NAMES = {"bf16": RMSNORM_BF16, "fp16": RMSNORM_FP16}
+
+VARIANT_AUTO, VARIANT_WAVE, VARIANT_BLOCK, VARIANT_GENERIC = 0, 1, 2, 3
+VARIANT_NAMES = {VARIANT_WAVE: "wave", VARIANT_BLOCK: "block", VARIANT_GENERIC: "generic"}
+
+STATUS = {
+    0: "RMSNORM_OK", 1: "RMSNORM_ERR_NULL", 2: "RMSNORM_ERR_SHAPE", 3: "RMSNORM_ERR_DTYPE",
+    4: "RMSNORM_ERR_SCALAR", 5: "RMSNORM_ERR_OVERLAP", 6: "RMSNORM_ERR_HIP",
+    7: "RMSNORM_ERR_DEVICE", 8: "RMSNORM_ERR_PLAN",
+}
+
+# Every symbol include/rmsnorm.h declares.
+EXPORTED = (
+    "rmsnorm_fwd", "rmsnorm_fwd_with_plan", "rmsnorm_plan_query", "rmsnorm_plan_resources",
+    "rmsnorm_status_string", "rmsnorm_last_error", "rmsnorm_version",
+)
+
+
+class RmsnormError(RuntimeError):
+    def __init__(self, status: int, detail: str):
+        self.status = status
+        name = STATUS.get(status, f"status {status}")
+        super().__init__(f"{name}: {detail}" if detail else name)
+
+
+class Plan(ctypes.Structure):
+    """rmsnorm_plan_t"""
+    _fields_ = [
+        ("variant", ctypes.c_int32),
+        ("vec_elems", ctypes.c_int32),
+        ("lanes_per_row", ctypes.c_int32),
+        ("vectors_per_lane", ctypes.c_int32),
+        ("row_slots", ctypes.c_int32),
+        ("block_threads", ctypes.c_int32),
+        ("grid", ctypes.c_int64),
+        ("rows_per_trip", ctypes.c_int64),
+        ("trips", ctypes.c_int64),
+    ]
+
+    def as_dict(self) -> dict:
+        d = {name: getattr(self, name) for name, _ in self._fields_}
+        d["variant_name"] = VARIANT_NAMES.get(self.variant, str(self.variant))
+        return d
+
+    def copy(self, **changes) -> "Plan":
+        p = Plan()
+        ctypes.pointer(p)[0] = self
+        for k, v in changes.items():
+            setattr(p, k, v)
+        return p
+
+
+def _load():
+    if not os.path.exists(LIBRARY):
+        raise ImportError(
+            f"{LIBRARY} is not built; run `python -m memory_bound_row_rmsnorm_amd.build` "
+            "(there is no non-HIP fallback)")
+    lib = ctypes.CDLL(LIBRARY)
+    vp, i64, f32, i32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_float, ctypes.c_int
+    lib.rmsnorm_fwd.argtypes = [vp, vp, vp, vp, i64, i64, f32, f32, i32, vp]
+    lib.rmsnorm_fwd.restype = i32
+    lib.rmsnorm_fwd_with_plan.argtypes = [vp, vp, vp, vp, i64, i64, f32, f32, i32,
+                                          ctypes.POINTER(Plan), vp]
+    lib.rmsnorm_fwd_with_plan.restype = i32
+    lib.rmsnorm_plan_query.argtypes = [i64, i64, i32, vp, vp, vp, ctypes.c_int32, ctypes.POINTER(Plan)]
+    lib.rmsnorm_plan_query.restype = i32
+    i32p = ctypes.POINTER(ctypes.c_int32)
+    lib.rmsnorm_plan_resources.argtypes = [ctypes.POINTER(Plan), i32, i32p, i32p, i32p, i32p]
+    lib.rmsnorm_plan_resources.restype = i32
+    lib.rmsnorm_status_string.argtypes = [i32]
+    lib.rmsnorm_status_string.restype = ctypes.c_char_p
+    lib.rmsnorm_last_error.argtypes = []
+    lib.rmsnorm_last_error.restype = ctypes.c_char_p
+    lib.rmsnorm_version.argtypes = []
+    lib.rmsnorm_version.restype = i32
+    return lib
+
+
+lib = _load()
+
+
+def library_path() -> str:
+    return LIBRARY
+
+
+def status_string(status: int) -> str:
+    return lib.rmsnorm_status_string(status).decode()
+
+
+def _check(status: int) -> None:
+    if status != 0:
+        raise RmsnormError(status, lib.rmsnorm_last_error().decode())
+
+
+def _dtype_code(dtype) -> int:
+    if isinstance(dtype, str):
+        if dtype not in DTYPE_NAMES:
+            raise ValueError(f"dtype must be 'bf16' or 'fp16', got {dtype!r}")
+        return DTYPE_NAMES[dtype]
+    if dtype not in DTYPE_CODES:
+        raise ValueError(f"dtype must be torch.bfloat16 or torch.float16, got {dtype}")
+    return DTYPE_CODES[dtype]
+
+
+def _stream_handle(stream) -> int | None:
+    s = torch.cuda.current_stream() if stream is None else stream
+    return s.cuda_stream or None
+
+
+def _check_tensors(x: torch.Tensor, w: torch.Tensor):
+    if not (x.is_cuda and w.is_cuda):
+        raise ValueError("x and w must be GPU tensors")
+    if x.device != w.device:
+        raise ValueError(f"x on {x.device} but w on {w.device}")
+    if x.dtype != w.dtype:
+        raise ValueError(f"x is {x.dtype} but w is {w.dtype}; both must have the same dtype")
+    _dtype_code(x.dtype)
+    if x.dim() != 2:
+        raise ValueError(f"x must be 2-D [M, N], got shape {tuple(x.shape)}")
+    if w.dim() != 1 or w.shape[0] != x.shape[1]:
+        raise ValueError(f"w must have shape [{x.shape[1]}], got {tuple(w.shape)}")
+    if not (x.is_contiguous() and w.is_contiguous()):
+        raise ValueError("x and w must be contiguous (no implicit copies are made)")
+
+
+def rmsnorm_fwd_out(x: torch.Tensor, w: torch.Tensor, y: torch.Tensor, rstd: torch.Tensor,
+                    eps: float = 1e-6, offset: float = 0.0, plan: Plan | None = None,
+                    stream=None) -> None:
+    """Write y (x's dtype, [M, N]) and rstd (fp32, [M]) in place; enqueue only."""
+    _check_tensors(x, w)
+    M, N = x.shape
+    if y.shape != x.shape or y.dtype != x.dtype or not y.is_contiguous() or y.device != x.device:
+        raise ValueError("y must be a contiguous tensor like x")
+    if (rstd.shape != (M,) or rstd.dtype != torch.float32 or not rstd.is_contiguous()
+            or rstd.device != x.device):
+        raise ValueError(f"rstd must be a contiguous float32 tensor of shape [{M}] on {x.device}")
+    args = (x.data_ptr(), w.data_ptr(), y.data_ptr(), rstd.data_ptr(), M, N, eps, offset,
+            DTYPE_CODES[x.dtype])
+    with torch.cuda.device(x.device):
+        h = _stream_handle(stream)
+        if plan is None:
+            _check(lib.rmsnorm_fwd(*args, h))
+        else:
+            _check(lib.rmsnorm_fwd_with_plan(*args, ctypes.byref(plan), h))
+
+
+def rmsnorm_fwd(x: torch.Tensor, w: torch.Tensor, eps: float = 1e-6, offset: float = 0.0,
+                plan: Plan | None = None, stream=None):
+    """y = x * rsqrt(mean(x^2, -1) + eps) * (offset + w) and rstd, on x's GPU.
+
+    Returns (y, rstd) with y of x's dtype and rstd float32 [M].
+    """
+    _check_tensors(x, w)
+    y = torch.empty_like(x)
+    rstd = torch.empty((x.shape[0],), dtype=torch.float32, device=x.device)
+    rmsnorm_fwd_out(x, w, y, rstd, eps, offset, plan, stream)
+    return y, rstd
+
+
+def plan_query(M: int, N: int, dtype, x_ptr: int = 0, w_ptr: int = 0, y_ptr: int = 0,
+               cu_count: int = 0) -> Plan:
+    """The plan rmsnorm_fwd uses; cu_count > 0 plans on the host only."""
+    p = Plan()
+    _check(lib.rmsnorm_plan_query(M, N, _dtype_code(dtype), x_ptr or None, w_ptr or None,
+                                  y_ptr or None, cu_count, ctypes.byref(p)))
+    return p
+
+
+def plan_resources(plan: Plan, dtype) -> dict:
+    """VGPRs, LDS bytes and scratch bytes of the kernel a plan selects (needs a GPU)."""
+    v, s, l, sc = (ctypes.c_int32() for _ in range(4))
+    _check(lib.rmsnorm_plan_resources(ctypes.byref(plan), _dtype_code(dtype), ctypes.byref(v),
+                                      ctypes.byref(s), ctypes.byref(l), ctypes.byref(sc)))
+    return {"vgprs": v.value, "lds_bytes": l.value, "scratch_bytes": sc.value}
+
+
+def version() -> int:
+    return lib.rmsnorm_version()

@@ -1,0 +1,411 @@
+// rmsnorm_api.cpp -- host side of librmsnorm_mi355x.so: argument checks,
+// launch planning and the C ABI declared in include/rmsnorm.h.
+//
+// Argument checks are pure host code and run before any HIP call, so a bad
+// call never enqueues work.  Planning picks a kernel family and geometry from
+// the row width (the pages' row-parallel design: one program per row, several
+// rows per program when rows are short -- "Rmsnorm Kernel Optimization", Core
+// Technique and Key Optimizations) and caps the grid at what the compute
+// units hold at once (the static persistent grid of the cuTile listing in
+// "Why cutile's rmsnorm required full register").
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdio>
+#include <cstring>
+#include <map>
+#include <mutex>
+#include <string>
+#include <tuple>
+
+#include "../../include/rmsnorm.h"
+#include "rmsnorm_internal.hpp"
+
+using rmsnorm_impl::KernelArgs;
+using rmsnorm_impl::KernelEntry;
+
+namespace {
+
+constexpr int kVersion = 1 * 10000 + 0 * 100 + 0;
+constexpr int kMaxDevices = 64;
+constexpr int kWaveBlockThreads = 256;   // 4 waves per workgroup for the wave family
+constexpr int kMaxThreadsPerCu = 2048;   // 4 SIMDs x 8 waves x 64 lanes
+
+thread_local std::string g_last_error;
+
+int fail(int status, const std::string& msg) {
+    g_last_error = msg;
+    return status;
+}
+
+// ---------------------------------------------------------------------------
+// Per-device cache: compute-unit count, architecture check, and occupancy of
+// each (kernel, block size) the dispatcher has launched.
+// ---------------------------------------------------------------------------
+struct DeviceInfo {
+    std::once_flag once;
+    int status = RMSNORM_OK;
+    std::string error;
+    int cu_count = 0;
+};
+
+DeviceInfo g_devices[kMaxDevices];
+
+int device_info(int* cu_count) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return fail(RMSNORM_ERR_HIP, std::string("hipGetDevice: ") + hipGetErrorString(e));
+    if (dev < 0 || dev >= kMaxDevices) return fail(RMSNORM_ERR_DEVICE, "device ordinal out of range");
+    DeviceInfo& d = g_devices[dev];
+    std::call_once(d.once, [&d, dev]() {
+        hipDeviceProp_t p;
+        hipError_t err = hipGetDeviceProperties(&p, dev);
+        if (err != hipSuccess) {
+            d.status = RMSNORM_ERR_HIP;
+            d.error = std::string("hipGetDeviceProperties: ") + hipGetErrorString(err);
+            return;
+        }
+        if (std::strncmp(p.gcnArchName, "gfx950", 6) != 0) {
+            d.status = RMSNORM_ERR_DEVICE;
+            d.error = std::string("librmsnorm_mi355x is built for gfx950, device is ") + p.gcnArchName;
+            return;
+        }
+        d.cu_count = p.multiProcessorCount;
+    });
+    if (d.status != RMSNORM_OK) return fail(d.status, d.error);
+    *cu_count = d.cu_count;
+    return RMSNORM_OK;
+}
+
+std::mutex g_occ_mu;
+std::map<std::tuple<int, const void*, int>, int> g_occ;  // (device, kernel, threads) -> blocks per CU
+
+// Workgroups of `threads` threads of kernel `func` one CU holds at once.
+int occupancy(const void* func, int threads, int* blocks) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return fail(RMSNORM_ERR_HIP, std::string("hipGetDevice: ") + hipGetErrorString(e));
+    const auto key = std::make_tuple(dev, func, threads);
+    std::lock_guard<std::mutex> lock(g_occ_mu);
+    auto it = g_occ.find(key);
+    if (it != g_occ.end()) {
+        *blocks = it->second;
+        return RMSNORM_OK;
+    }
+    int n = 0;
+    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, func, threads, 0);
+    if (e != hipSuccess)
+        return fail(RMSNORM_ERR_HIP,
+                    std::string("hipOccupancyMaxActiveBlocksPerMultiprocessor: ") + hipGetErrorString(e));
+    if (n < 1) n = 1;
+    g_occ.emplace(key, n);
+    *blocks = n;
+    return RMSNORM_OK;
+}
+
+// ---------------------------------------------------------------------------
+// Argument checks (host only).
+// ---------------------------------------------------------------------------
+bool ranges_overlap(const void* a, int64_t abytes, const void* b, int64_t bbytes) {
+    const uintptr_t a0 = reinterpret_cast<uintptr_t>(a), b0 = reinterpret_cast<uintptr_t>(b);
+    return a0 < b0 + static_cast<uintptr_t>(bbytes) && b0 < a0 + static_cast<uintptr_t>(abytes);
+}
+
+int check_shape_dtype(int64_t M, int64_t N, int dtype) {
+    if (M < 0) return fail(RMSNORM_ERR_SHAPE, "M must be >= 0");
+    if (N <= 0) return fail(RMSNORM_ERR_SHAPE, "N must be >= 1");
+    if (M > 0 && N > INT64_MAX / 2 / M) return fail(RMSNORM_ERR_SHAPE, "M*N*2 bytes overflows int64");
+    if (dtype != RMSNORM_BF16 && dtype != RMSNORM_FP16) return fail(RMSNORM_ERR_DTYPE, "dtype must be RMSNORM_BF16 or RMSNORM_FP16");
+    return RMSNORM_OK;
+}
+
+int check_args(const void* x, const void* w, const void* y, const float* rstd, int64_t M, int64_t N,
+               float eps, float offset, int dtype) {
+    int st = check_shape_dtype(M, N, dtype);
+    if (st != RMSNORM_OK) return st;
+    if (M > 0 && (!x || !w || !y || !rstd)) return fail(RMSNORM_ERR_NULL, "x, w, y and rstd must be non-NULL");
+    if (!std::isfinite(eps) || eps < 0.0f) return fail(RMSNORM_ERR_SCALAR, "eps must be finite and >= 0");
+    if (!std::isfinite(offset)) return fail(RMSNORM_ERR_SCALAR, "offset must be finite");
+    if (M == 0) return RMSNORM_OK;
+    const int64_t xb = M * N * 2, wb = N * 2, rb = M * 4;
+    if (x != y && ranges_overlap(x, xb, y, xb)) return fail(RMSNORM_ERR_OVERLAP, "y partially overlaps x");
+    if (ranges_overlap(y, xb, w, wb)) return fail(RMSNORM_ERR_OVERLAP, "y overlaps w");
+    if (ranges_overlap(rstd, rb, x, xb) || ranges_overlap(rstd, rb, y, xb) || ranges_overlap(rstd, rb, w, wb))
+        return fail(RMSNORM_ERR_OVERLAP, "rstd overlaps x, y or w");
+    return RMSNORM_OK;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// ---------------------------------------------------------------------------
+// Kernel lookup.
+// ---------------------------------------------------------------------------
+const KernelEntry* find_kernel(int variant, int dtype, int lanes, int vpl, int slots) {
+    int n = 0;
+    const KernelEntry* t = rmsnorm_impl::kernel_table(&n);
+    for (int i = 0; i < n; ++i) {
+        const KernelEntry& k = t[i];
+        if (k.variant != variant || k.dtype != dtype) continue;
+        if (variant == RMSNORM_VARIANT_WAVE &&
+            (k.lanes_per_row != lanes || k.vectors_per_lane != vpl || k.row_slots != slots))
+            continue;
+        if (variant == RMSNORM_VARIANT_BLOCK && k.vectors_per_lane != vpl) continue;
+        return &k;
+    }
+    return nullptr;
+}
+
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// Fill the derived fields and check the plan against the call.  Host only.
+int finish_plan(rmsnorm_plan_t* p, int64_t M, int64_t N, int dtype, const void* x, const void* w,
+                const void* y, const KernelEntry** kernel) {
+    if (p->block_threads < 64 || p->block_threads > 1024 || p->block_threads % 64 != 0)
+        return fail(RMSNORM_ERR_PLAN, "block_threads must be a multiple of 64 in [64, 1024]");
+    if (p->grid < 1 || p->grid > 0x7FFFFFFF) return fail(RMSNORM_ERR_PLAN, "grid must be in [1, 2^31)");
+    const KernelEntry* k = nullptr;
+    if (p->variant == RMSNORM_VARIANT_GENERIC) {
+        p->vec_elems = 1;
+        p->lanes_per_row = p->block_threads;
+        p->vectors_per_lane = 0;
+        p->row_slots = 1;
+        p->rows_per_trip = 1;
+        k = find_kernel(RMSNORM_VARIANT_GENERIC, dtype, 0, 0, 1);
+    } else if (p->variant == RMSNORM_VARIANT_WAVE || p->variant == RMSNORM_VARIANT_BLOCK) {
+        if (N % 8 != 0) return fail(RMSNORM_ERR_PLAN, "16-byte kernels need N % 8 == 0");
+        if (!aligned16(x) || !aligned16(w) || !aligned16(y))
+            return fail(RMSNORM_ERR_PLAN, "16-byte kernels need 16-byte aligned x, w and y");
+        p->vec_elems = 8;
+        if (p->variant == RMSNORM_VARIANT_WAVE) {
+            k = find_kernel(RMSNORM_VARIANT_WAVE, dtype, p->lanes_per_row, p->vectors_per_lane, p->row_slots);
+            if (k) {
+                const int64_t cap = static_cast<int64_t>(p->lanes_per_row) * p->vectors_per_lane * 8;
+                if (cap < N) return fail(RMSNORM_ERR_PLAN, "wave plan does not cover N");
+                p->rows_per_trip = static_cast<int64_t>(p->block_threads / 64) * (64 / p->lanes_per_row) * p->row_slots;
+            }
+        } else {
+            p->row_slots = 1;
+            p->lanes_per_row = p->block_threads;
+            k = find_kernel(RMSNORM_VARIANT_BLOCK, dtype, 0, p->vectors_per_lane, 1);
+            if (k) {
+                const int64_t cap = static_cast<int64_t>(p->block_threads) * p->vectors_per_lane * 8;
+                if (cap < N) return fail(RMSNORM_ERR_PLAN, "block plan does not cover N");
+                p->rows_per_trip = 1;
+            }
+        }
+    } else {
+        return fail(RMSNORM_ERR_PLAN, "unknown variant");
+    }
+    if (!k) return fail(RMSNORM_ERR_PLAN, "no compiled kernel for this plan");
+    p->trips = M > 0 ? ceil_div(ceil_div(M, p->rows_per_trip), p->grid) : 0;
+    if (kernel) *kernel = k;
+    return RMSNORM_OK;
+}
+
+// Vectors per lane the block and wave families are compiled for (more would
+// not fit the 128 VGPRs a 1024-thread workgroup allows without spilling).
+constexpr int kBlockVpt[] = {1, 2, 3, 4, 5, 6};
+constexpr int kWaveVpl[] = {1, 2, 3, 4, 5, 6};
+constexpr int64_t kMaxVectorN = 1024LL * 6 * 8;   // widest row the 16-byte kernels hold
+
+// Choose family and geometry.  cu_count and blocks_per_cu size the grid.
+// Returns RMSNORM_OK and a plan without derived fields.
+int choose_plan(int64_t M, int64_t N, const void* x, const void* w, const void* y, rmsnorm_plan_t* p) {
+    std::memset(p, 0, sizeof(*p));
+    const bool vec_ok = (N % 8 == 0) && aligned16(x) && aligned16(w) && aligned16(y) &&
+                        N <= kMaxVectorN;
+    if (!vec_ok) {
+        p->variant = RMSNORM_VARIANT_GENERIC;
+        p->block_threads = N >= 1024 ? 256 : (N >= 256 ? 128 : 64);
+        p->row_slots = 1;
+        return RMSNORM_OK;
+    }
+    const int64_t nvec = N / 8;
+    if (nvec <= 128) {
+        // wave family: short rows live in one wavefront
+        p->variant = RMSNORM_VARIANT_WAVE;
+        p->block_threads = kWaveBlockThreads;
+        if (nvec <= 16) {
+            p->lanes_per_row = 16;
+            p->vectors_per_lane = 1;
+        } else if (nvec <= 32) {
+            p->lanes_per_row = 32;
+            p->vectors_per_lane = 1;
+        } else {
+            p->lanes_per_row = 64;
+            for (int v : kWaveVpl)
+                if (64LL * v >= nvec) { p->vectors_per_lane = v; break; }
+        }
+        // rows in flight per wave: aim at about 2 KiB of loads per wave
+        const int64_t row_bytes = N * 2;
+        const int64_t per_slot = row_bytes * (64 / p->lanes_per_row);
+        int slots = static_cast<int>(2048 / per_slot);
+        if (slots < 1) slots = 1;
+        if (slots > 8) slots = 8;
+        while (slots > 1 && !find_kernel(RMSNORM_VARIANT_WAVE, RMSNORM_BF16, p->lanes_per_row,
+                                         p->vectors_per_lane, slots))
+            slots /= 2;
+        p->row_slots = slots;
+        return RMSNORM_OK;
+    }
+    // block family: least padding first (in 1/32ths of the row), then at most
+    // 4 vectors per thread (fewer registers held per row), then 256, 512,
+    // 128, 1024 threads in that order
+    p->variant = RMSNORM_VARIANT_BLOCK;
+    p->row_slots = 1;
+    int best_t = 0, best_v = 0;
+    int64_t best_key = INT64_MAX;
+    const int order[] = {256, 512, 128, 1024};
+    for (int oi = 0; oi < 4; ++oi) {
+        const int t = order[oi];
+        for (int v : kBlockVpt) {
+            const int64_t cap = static_cast<int64_t>(t) * v;
+            if (cap < nvec) continue;
+            const int64_t pad32 = ceil_div((cap - nvec) * 32, nvec);
+            const int64_t key = pad32 * 100 + (v > 4 ? 10 : 0) + oi;
+            if (key < best_key) { best_key = key; best_t = t; best_v = v; }
+            break;
+        }
+    }
+    p->block_threads = best_t;
+    p->vectors_per_lane = best_v;
+    return best_t ? RMSNORM_OK : fail(RMSNORM_ERR_PLAN, "no block plan covers N");
+}
+
+// Grid: enough workgroups for one trip each, capped at what the CUs hold.
+void size_grid(rmsnorm_plan_t* p, int64_t M, int cu_count, int blocks_per_cu) {
+    int64_t rows_per_trip = 1;
+    if (p->variant == RMSNORM_VARIANT_WAVE)
+        rows_per_trip = static_cast<int64_t>(p->block_threads / 64) * (64 / p->lanes_per_row) * p->row_slots;
+    int64_t need = M > 0 ? ceil_div(M, rows_per_trip) : 1;
+    int64_t cap = static_cast<int64_t>(cu_count) * blocks_per_cu;
+    if (cap < 1) cap = 1;
+    p->grid = need < cap ? need : cap;
+}
+
+int plan_for_call(int64_t M, int64_t N, int dtype, const void* x, const void* w, const void* y,
+                  int cu_count_hint, rmsnorm_plan_t* p, const KernelEntry** kernel) {
+    int st = choose_plan(M, N, x, w, y, p);
+    if (st != RMSNORM_OK) return st;
+    // look the kernel up once with a provisional grid to learn its occupancy
+    p->grid = 1;
+    const KernelEntry* k = nullptr;
+    st = finish_plan(p, M, N, dtype, x, w, y, &k);
+    if (st != RMSNORM_OK) return st;
+    int cu = cu_count_hint, bpc = 0;
+    if (cu > 0) {
+        bpc = kMaxThreadsPerCu / p->block_threads;  // host-only estimate: no register limit
+    } else {
+        st = device_info(&cu);
+        if (st != RMSNORM_OK) return st;
+        st = occupancy(k->func, p->block_threads, &bpc);
+        if (st != RMSNORM_OK) return st;
+    }
+    size_grid(p, M, cu, bpc);
+    return finish_plan(p, M, N, dtype, x, w, y, kernel);
+}
+
+int launch(const KernelEntry* k, const rmsnorm_plan_t* p, const void* x, const void* w, void* y,
+           float* rstd, int64_t M, int64_t N, float eps, float offset, void* stream) {
+    KernelArgs a;
+    a.x = x;
+    a.w = w;
+    a.y = y;
+    a.rstd = rstd;
+    a.M = M;
+    a.N = N;
+    a.inv_n = static_cast<float>(1.0 / static_cast<double>(N));
+    a.eps = eps;
+    a.offset = offset;
+    void* args[] = {&a};
+    hipError_t e = hipLaunchKernel(k->func, dim3(static_cast<unsigned>(p->grid)),
+                                   dim3(static_cast<unsigned>(p->block_threads)), args, 0,
+                                   static_cast<hipStream_t>(stream));
+    if (e != hipSuccess)
+        return fail(RMSNORM_ERR_HIP, std::string("hipLaunchKernel(") + k->name + "): " + hipGetErrorString(e));
+    return RMSNORM_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int rmsnorm_fwd(const void* x, const void* w, void* y, float* rstd, int64_t M, int64_t N, float eps,
+                float offset, int dtype, void* stream) {
+    g_last_error.clear();
+    int st = check_args(x, w, y, rstd, M, N, eps, offset, dtype);
+    if (st != RMSNORM_OK || M == 0) return st;
+    rmsnorm_plan_t p;
+    const KernelEntry* k = nullptr;
+    st = plan_for_call(M, N, dtype, x, w, y, 0, &p, &k);
+    if (st != RMSNORM_OK) return st;
+    return launch(k, &p, x, w, y, rstd, M, N, eps, offset, stream);
+}
+
+int rmsnorm_fwd_with_plan(const void* x, const void* w, void* y, float* rstd, int64_t M, int64_t N,
+                          float eps, float offset, int dtype, const rmsnorm_plan_t* plan, void* stream) {
+    g_last_error.clear();
+    int st = check_args(x, w, y, rstd, M, N, eps, offset, dtype);
+    if (st != RMSNORM_OK) return st;
+    if (!plan) return fail(RMSNORM_ERR_NULL, "plan must be non-NULL");
+    rmsnorm_plan_t p = *plan;
+    const KernelEntry* k = nullptr;
+    st = finish_plan(&p, M, N, dtype, x, w, y, &k);
+    if (st != RMSNORM_OK || M == 0) return st;
+    return launch(k, &p, x, w, y, rstd, M, N, eps, offset, stream);
+}
+
+int rmsnorm_plan_query(int64_t M, int64_t N, int dtype, const void* x, const void* w, const void* y,
+                       int32_t cu_count, rmsnorm_plan_t* out) {
+    g_last_error.clear();
+    if (!out) return fail(RMSNORM_ERR_NULL, "out must be non-NULL");
+    int st = check_shape_dtype(M, N, dtype);
+    if (st != RMSNORM_OK) return st;
+    rmsnorm_plan_t p;
+    st = plan_for_call(M, N, dtype, x, w, y, cu_count, &p, nullptr);
+    if (st != RMSNORM_OK) return st;
+    *out = p;
+    return RMSNORM_OK;
+}
+
+int rmsnorm_plan_resources(const rmsnorm_plan_t* plan, int dtype, int32_t* vgprs, int32_t* sgprs,
+                           int32_t* lds_bytes, int32_t* scratch) {
+    g_last_error.clear();
+    if (!plan) return fail(RMSNORM_ERR_NULL, "plan must be non-NULL");
+    if (dtype != RMSNORM_BF16 && dtype != RMSNORM_FP16) return fail(RMSNORM_ERR_DTYPE, "bad dtype");
+    const KernelEntry* k = nullptr;
+    if (plan->variant == RMSNORM_VARIANT_GENERIC) k = find_kernel(RMSNORM_VARIANT_GENERIC, dtype, 0, 0, 1);
+    else if (plan->variant == RMSNORM_VARIANT_BLOCK) k = find_kernel(RMSNORM_VARIANT_BLOCK, dtype, 0, plan->vectors_per_lane, 1);
+    else if (plan->variant == RMSNORM_VARIANT_WAVE)
+        k = find_kernel(RMSNORM_VARIANT_WAVE, dtype, plan->lanes_per_row, plan->vectors_per_lane, plan->row_slots);
+    if (!k) return fail(RMSNORM_ERR_PLAN, "no compiled kernel for this plan");
+    hipFuncAttributes attr;
+    hipError_t e = hipFuncGetAttributes(&attr, k->func);
+    if (e != hipSuccess) return fail(RMSNORM_ERR_HIP, std::string("hipFuncGetAttributes: ") + hipGetErrorString(e));
+    if (vgprs) *vgprs = attr.numRegs;
+    if (sgprs) *sgprs = -1;  // not exposed by hipFuncGetAttributes
+    if (lds_bytes) *lds_bytes = static_cast<int32_t>(attr.sharedSizeBytes);
+    if (scratch) *scratch = static_cast<int32_t>(attr.localSizeBytes);
+    return RMSNORM_OK;
+}
+
+const char* rmsnorm_status_string(int status) {
+    switch (status) {
+        case RMSNORM_OK: return "RMSNORM_OK";
+        case RMSNORM_ERR_NULL: return "RMSNORM_ERR_NULL";
+        case RMSNORM_ERR_SHAPE: return "RMSNORM_ERR_SHAPE";
+        case RMSNORM_ERR_DTYPE: return "RMSNORM_ERR_DTYPE";
+        case RMSNORM_ERR_SCALAR: return "RMSNORM_ERR_SCALAR";
+        case RMSNORM_ERR_OVERLAP: return "RMSNORM_ERR_OVERLAP";
+        case RMSNORM_ERR_HIP: return "RMSNORM_ERR_HIP";
+        case RMSNORM_ERR_DEVICE: return "RMSNORM_ERR_DEVICE";
+        case RMSNORM_ERR_PLAN: return "RMSNORM_ERR_PLAN";
+        default: return "RMSNORM_ERR_UNKNOWN";
+    }
+}
+
+const char* rmsnorm_last_error(void) { return g_last_error.c_str(); }
+
+int rmsnorm_version(void) { return kVersion; }
+
+}  // extern "C"

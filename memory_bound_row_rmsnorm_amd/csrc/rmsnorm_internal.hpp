@@ -1,0 +1,38 @@
+// rmsnorm_internal.hpp -- what the kernel translation unit exports to the
+// host dispatcher: a table of compiled kernel instances, all with one
+// argument list, so the dispatcher launches any of them the same way.
+#pragma once
+
+#include <stdint.h>
+
+namespace rmsnorm_impl {
+
+// Every kernel takes exactly these arguments, in this order.
+//   x, w, y : 16-bit element buffers (device), rstd : fp32 [M] (device)
+//   M rows, N columns, inv_n = fp32(1/N), eps, offset
+struct KernelArgs {
+    const void* x;
+    const void* w;
+    void* y;
+    float* rstd;
+    int64_t M;
+    int64_t N;
+    float inv_n;
+    float eps;
+    float offset;
+};
+
+struct KernelEntry {
+    int variant;           // rmsnorm_variant_t
+    int dtype;             // rmsnorm_dtype_t
+    int lanes_per_row;     // WAVE: 16/32/64; BLOCK, GENERIC: 0 (= block size)
+    int vectors_per_lane;  // WAVE, BLOCK: 16-byte vectors per lane per row; GENERIC: 0
+    int row_slots;         // WAVE: slots per wave per trip; others 1
+    const void* func;      // host stub of the __global__ function
+    const char* name;
+};
+
+// The compiled instances (defined in rmsnorm_kernels.hip).
+const KernelEntry* kernel_table(int* count);
+
+}  // namespace rmsnorm_impl

@@ -1,0 +1,168 @@
+"""The C-ABI library on the host: loads, exports what include/rmsnorm.h
+declares, rejects bad arguments before any HIP call, and plans launches on the
+host.  No kernel is launched here."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "rmsnorm.h")
+
+bnd = pytest.importorskip("memory_bound_row_rmsnorm_amd.binding",
+                          reason="librmsnorm_mi355x.so not built")
+lib = bnd.lib
+
+OK, NULL, SHAPE, DTYPE, SCALAR, OVERLAP, HIP, DEVICE, PLAN = range(9)
+BF16, FP16 = 0, 1
+A = 0x10000000  # fake, 256-byte aligned, never dereferenced: every call below fails validation
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(rmsnorm_[a-z_]+)\s*\(", text)))
+
+
+def test_header_declarations_are_all_exported():
+    names = declared_functions()
+    assert names == sorted(bnd.EXPORTED)
+    for n in names:
+        assert hasattr(lib, n), n
+    nm = subprocess.run(["nm", "-D", "--defined-only", bnd.LIBRARY], capture_output=True, text=True,
+                        check=True).stdout
+    exported = set(re.findall(r" T (rmsnorm_\w+)", nm))
+    assert set(names) <= exported, set(names) - exported
+
+
+def test_version_and_status_strings():
+    assert lib.rmsnorm_version() == 10000
+    for code, name in bnd.STATUS.items():
+        assert bnd.status_string(code) == name
+    assert bnd.status_string(99) == "RMSNORM_ERR_UNKNOWN"
+
+
+def fwd(x=A, w=A + 0x1000000, y=A + 0x2000000, rstd=A + 0x3000000, M=4, N=512, eps=1e-6,
+        offset=0.0, dtype=BF16):
+    return lib.rmsnorm_fwd(x, w, y, rstd, M, N, eps, offset, dtype, None)
+
+
+@pytest.mark.parametrize("kwargs,status", [
+    (dict(M=-1), SHAPE),
+    (dict(N=0), SHAPE),
+    (dict(N=-5), SHAPE),
+    (dict(M=1 << 40, N=1 << 40), SHAPE),
+    (dict(dtype=2), DTYPE),
+    (dict(dtype=-1), DTYPE),
+    (dict(x=None), NULL),
+    (dict(w=None), NULL),
+    (dict(y=None), NULL),
+    (dict(rstd=None), NULL),
+    (dict(eps=-1e-6), SCALAR),
+    (dict(eps=float("nan")), SCALAR),
+    (dict(eps=float("inf")), SCALAR),
+    (dict(offset=float("nan")), SCALAR),
+    (dict(offset=float("-inf")), SCALAR),
+    (dict(y=A + 16), OVERLAP),                      # y partially overlaps x
+    (dict(y=A + 0x1000000 - 16), OVERLAP),          # y runs into w
+    (dict(rstd=A + 8), OVERLAP),                    # rstd inside x
+    (dict(rstd=A + 0x1000000 + 4), OVERLAP),        # rstd inside w
+    (dict(rstd=A + 0x2000000 + 64), OVERLAP),       # rstd inside y
+])
+def test_argument_errors(kwargs, status):
+    assert fwd(**kwargs) == status
+    assert lib.rmsnorm_last_error().decode() != ""
+
+
+def test_m_zero_is_a_noop_without_pointers():
+    assert fwd(x=None, w=None, y=None, rstd=None, M=0) == OK
+    assert lib.rmsnorm_last_error().decode() == ""
+
+
+def test_m_zero_still_checks_shape_and_scalars():
+    assert fwd(M=0, N=0) == SHAPE
+    assert fwd(M=0, eps=-1.0) == SCALAR
+
+
+def test_errors_are_checked_before_plans():
+    p = bnd.Plan()
+    assert lib.rmsnorm_fwd_with_plan(A, A, A + 16, A + 0x3000000, 4, 512, 1e-6, 0.0, BF16,
+                                     ctypes.byref(p), None) == OVERLAP
+    assert lib.rmsnorm_fwd_with_plan(A, A + 0x1000000, A + 0x2000000, A + 0x3000000, 4, 512, 1e-6,
+                                     0.0, BF16, None, None) == NULL
+
+
+def host_plan(M, N, dtype=BF16, x=None, w=None, y=None, cu=256):
+    p = bnd.Plan()
+    st = lib.rmsnorm_plan_query(M, N, dtype, x, w, y, cu, ctypes.byref(p))
+    assert st == OK, bnd.status_string(st) + " " + lib.rmsnorm_last_error().decode()
+    return p
+
+
+def covers(p, N):
+    if p.variant == bnd.VARIANT_GENERIC:
+        return True
+    return p.lanes_per_row * p.vectors_per_lane * p.vec_elems >= N
+
+
+@pytest.mark.parametrize("M,N", [(64, 512), (16384, 512), (8192, 3000), (32768, 8192),
+                                 (262144, 128), (4096, 16384), (1, 8), (7, 256), (100, 1024),
+                                 (3, 4096), (5, 49152)])
+def test_host_plans_cover_the_row_and_fill_the_chip(M, N):
+    for dtype in (BF16, FP16):
+        p = host_plan(M, N, dtype)
+        assert p.variant in (bnd.VARIANT_WAVE, bnd.VARIANT_BLOCK)
+        assert p.vec_elems == 8 and covers(p, N)
+        assert p.block_threads % 64 == 0 and 64 <= p.block_threads <= 1024
+        groups = -(-M // p.rows_per_trip)
+        assert p.grid == min(groups, 256 * (2048 // p.block_threads))
+        assert p.trips == -(-groups // p.grid)
+        assert p.grid * p.trips * p.rows_per_trip >= M
+
+
+def test_short_rows_go_to_the_wave_family_long_rows_to_the_block_family():
+    assert host_plan(16384, 512).variant == bnd.VARIANT_WAVE
+    p = host_plan(262144, 128)
+    assert (p.variant, p.lanes_per_row) == (bnd.VARIANT_WAVE, 16)
+    assert host_plan(64, 256).lanes_per_row == 32
+    assert host_plan(32768, 8192).variant == bnd.VARIANT_BLOCK
+    p = host_plan(8192, 3000)
+    assert p.variant == bnd.VARIANT_BLOCK and p.block_threads * p.vectors_per_lane * 8 >= 3000
+
+
+@pytest.mark.parametrize("N,x", [(7, None), (3001, None), (127, None), (512, A + 2), (512, A + 8),
+                                 (49160, None), (1 << 17, None)])
+def test_unaligned_or_odd_rows_take_the_generic_kernel(N, x):
+    p = host_plan(10, N, x=x)
+    assert p.variant == bnd.VARIANT_GENERIC and p.vec_elems == 1
+
+
+def test_plans_that_do_not_fit_are_rejected_before_launch():
+    good = host_plan(100, 512)
+    bad = [
+        good.copy(vectors_per_lane=0),                                      # no such kernel
+        good.copy(variant=bnd.VARIANT_WAVE, lanes_per_row=16, vectors_per_lane=1),  # covers 128 < 512
+        good.copy(block_threads=96),
+        good.copy(block_threads=2048),
+        good.copy(grid=0),
+        good.copy(variant=7),
+        good.copy(variant=bnd.VARIANT_BLOCK, block_threads=64, vectors_per_lane=8),  # not compiled
+    ]
+    args = (A, A + 0x1000000, A + 0x2000000, A + 0x3000000, 100, 512, 1e-6, 0.0, BF16)
+    for p in bad:
+        assert lib.rmsnorm_fwd_with_plan(*args, ctypes.byref(p), None) == PLAN, p.as_dict()
+    # a wave plan needs N % 8 == 0 and 16-byte alignment
+    p = good.copy()
+    assert lib.rmsnorm_fwd_with_plan(A, A + 0x1000000, A + 0x2000000, A + 0x3000000, 100, 511,
+                                     1e-6, 0.0, BF16, ctypes.byref(p), None) == PLAN
+    assert lib.rmsnorm_fwd_with_plan(A + 2, A + 0x1000000, A + 0x2000000, A + 0x3000000, 100, 512,
+                                     1e-6, 0.0, BF16, ctypes.byref(p), None) == PLAN
+
+
+def test_plan_query_validates():
+    p = bnd.Plan()
+    assert lib.rmsnorm_plan_query(-1, 8, BF16, None, None, None, 256, ctypes.byref(p)) == SHAPE
+    assert lib.rmsnorm_plan_query(1, 8, 5, None, None, None, 256, ctypes.byref(p)) == DTYPE
+    assert lib.rmsnorm_plan_query(1, 8, BF16, None, None, None, 256, None) == NULL

@@ -1,0 +1,283 @@
+"""GPU parity: the HIP kernels against the fp64 oracle, through the C ABI.
+
+Every case prints what it runs before it runs it, so a failing or stuck case
+names itself.
+"""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+from memory_bound_row_rmsnorm_amd import workloads
+from tests import parity
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+
+
+@pytest.fixture(scope="module")
+def bnd():
+    if not torch.cuda.is_available():
+        pytest.fail("no GPU visible")
+    from memory_bound_row_rmsnorm_amd import binding
+    return binding
+
+
+def announce(*parts):
+    print("CASE", *parts, flush=True)
+
+
+def run_and_compare(bnd, x, w, eps, offset, dtype, what, plan=None):
+    xg, wg = x.to(DEV), w.to(DEV)
+    y, r = bnd.rmsnorm_fwd(xg, wg, eps, offset, plan=plan)
+    torch.cuda.synchronize()
+    y_ref, r_ref = parity.oracle_for(x, w, eps, offset, dtype)
+    return parity.compare(y, r, y_ref, r_ref, dtype, what)
+
+
+# ---------------------------------------------------------------------------
+# 1. Every workload at full size, with the plan rmsnorm_fwd picks (the launch
+#    configuration the benchmark times), compared element by element.
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("name", list(workloads.WORKLOADS))
+def test_workload_full_size(bnd, name):
+    wl = workloads.WORKLOADS[name]
+    announce("full-size", name, wl.M, wl.N, wl.dtype)
+    x, w = workloads.make_inputs(wl, seed=0)
+    stats = run_and_compare(bnd, x, w, wl.eps, wl.offset, wl.dtype, name)
+    plan = bnd.plan_query(wl.M, wl.N, wl.dtype)
+    print(name, plan.as_dict(), stats, flush=True)
+    assert stats["exact_fraction"] > 0.99
+
+
+# ---------------------------------------------------------------------------
+# 2. Every compiled kernel that covers the row, at a reduced row count with a
+#    ragged tail, both with one trip per workgroup and as a small persistent
+#    grid.
+# ---------------------------------------------------------------------------
+def candidate_plans(bnd, M, N, dtype):
+    base = bnd.plan_query(M, N, dtype)
+    out = []
+    for lanes in (16, 32, 64):
+        for vpl in range(1, 9):
+            for slots in (1, 2, 4, 8):
+                if lanes * vpl * 8 < N:
+                    continue
+                out.append(base.copy(variant=bnd.VARIANT_WAVE, lanes_per_row=lanes,
+                                     vectors_per_lane=vpl, row_slots=slots, block_threads=256))
+    for threads in (64, 128, 256, 512, 1024):
+        for vpt in range(1, 9):
+            if threads * vpt * 8 < N:
+                continue
+            out.append(base.copy(variant=bnd.VARIANT_BLOCK, block_threads=threads,
+                                 vectors_per_lane=vpt, row_slots=1))
+    for threads in (64, 256, 1024):
+        out.append(base.copy(variant=bnd.VARIANT_GENERIC, block_threads=threads))
+    return out
+
+
+@pytest.mark.parametrize("name", list(workloads.WORKLOADS))
+def test_every_kernel_on_workload_rows(bnd, name):
+    wl = workloads.WORKLOADS[name]
+    M = 999 if wl.N <= 4096 else 131
+    x, w = workloads.make_inputs(wl, seed=1, rows=M)
+    xg, wg = x.to(DEV), w.to(DEV)
+    y_ref, r_ref = parity.oracle_for(x, w, wl.eps, wl.offset, wl.dtype)
+    ran = 0
+    for plan in candidate_plans(bnd, M, wl.N, wl.dtype):
+        for grid in (M, 3):
+            p = plan.copy(grid=grid)
+            y = torch.empty_like(xg)
+            r = torch.empty(M, dtype=torch.float32, device=DEV)
+            try:
+                bnd.rmsnorm_fwd_out(xg, wg, y, r, wl.eps, wl.offset, plan=p)
+            except bnd.RmsnormError as e:
+                if e.status == 8:      # RMSNORM_ERR_PLAN: no such compiled kernel
+                    continue
+                raise
+            torch.cuda.synchronize()
+            announce(name, p.as_dict())
+            parity.compare(y, r, y_ref, r_ref, wl.dtype, f"{name} {p.as_dict()}")
+            ran += 1
+    assert ran >= 6
+
+
+# ---------------------------------------------------------------------------
+# 3. Sweep of widths around powers of two and tile edges.
+# ---------------------------------------------------------------------------
+SWEEP_N = [1, 2, 3, 7, 8, 9, 63, 64, 65, 127, 128, 129, 255, 256, 511, 512, 513, 1000, 1023,
+           1024, 1025, 2047, 3000, 4095, 4096, 4097, 8191, 8192, 16383, 16384, 16385, 32768]
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp16"])
+@pytest.mark.parametrize("N", SWEEP_N)
+def test_sweep(bnd, N, dtype):
+    g = torch.Generator().manual_seed(N)
+    td = workloads.TORCH_DTYPES[dtype]
+    for M in (1, 3, 65, 257):
+        if M * N > 4_000_000:
+            continue
+        x = (torch.randn(M, N, generator=g) * 3).to(td)
+        w = (torch.randn(N, generator=g) * 0.5).to(td)
+        for offset in (0.0, 1.0):
+            announce("sweep", M, N, dtype, offset)
+            run_and_compare(bnd, x, w, 1e-6, offset, dtype, f"sweep M={M} N={N} {dtype} off={offset}")
+
+
+# ---------------------------------------------------------------------------
+# 4. Guard bands: NaN around x and w must not leak in; sentinels around y and
+#    rstd must not be written.  Aligned offsets take the 16-byte kernels,
+#    odd offsets the generic kernel.
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("dtype", ["bf16", "fp16"])
+@pytest.mark.parametrize("N,lead", [(3000, 8), (127, 8), (1025, 3), (512, 8), (512, 1), (128, 8),
+                                    (8192, 8), (16384, 5), (256, 8)])
+def test_guard_bands(bnd, N, lead, dtype):
+    announce("guard", N, lead, dtype)
+    M = 37
+    td = workloads.TORCH_DTYPES[dtype]
+    nan = 0x7FC0 if dtype == "bf16" else 0x7E00
+    g = torch.Generator().manual_seed(5)
+    x = (torch.randn(M, N, generator=g)).to(td)
+    w = (torch.randn(N, generator=g) * 0.2 + 1).to(td)
+    pad = 4096
+    xbuf = torch.full((lead + M * N + pad,), nan, dtype=torch.int32).to(torch.int16)
+    wbuf = torch.full((lead + N + pad,), nan, dtype=torch.int32).to(torch.int16)
+    ybuf = torch.full((lead + M * N + pad,), 0x5A5A, dtype=torch.int16)
+    rbuf = torch.full((lead + M + pad,), -7.0, dtype=torch.float32)
+    xbuf[lead:lead + M * N] = x.view(torch.int16).reshape(-1)
+    wbuf[lead:lead + N] = w.view(torch.int16)
+    xbuf, wbuf, ybuf, rbuf = (t.to(DEV) for t in (xbuf, wbuf, ybuf, rbuf))
+    xg = xbuf[lead:lead + M * N].view(td).view(M, N)
+    wg = wbuf[lead:lead + N].view(td)
+    yg = ybuf[lead:lead + M * N].view(td).view(M, N)
+    rg = rbuf[lead:lead + M]
+    bnd.rmsnorm_fwd_out(xg, wg, yg, rg, 1e-6, 0.0)
+    torch.cuda.synchronize()
+    y_ref, r_ref = parity.oracle_for(x, w, 1e-6, 0.0, dtype)
+    parity.compare(yg, rg, y_ref, r_ref, dtype, f"guard N={N} lead={lead}")
+    yb = ybuf.cpu()
+    rb = rbuf.cpu()
+    assert torch.all(yb[:lead] == 0x5A5A) and torch.all(yb[lead + M * N:] == 0x5A5A)
+    assert torch.all(rb[:lead] == -7.0) and torch.all(rb[lead + M:] == -7.0)
+
+
+# ---------------------------------------------------------------------------
+# 5. Rows of wildly different magnitude side by side: any cross-row mixing in
+#    a segment, slot or workgroup shows up as a huge error.
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("N", [128, 256, 512, 1024, 3000, 8192, 127, 1025])
+def test_alternating_magnitudes(bnd, N):
+    for dtype, (small, big) in (("bf16", (2.0 ** -20, 2.0 ** 20)), ("fp16", (2.0 ** -5, 2.0 ** 5))):
+        announce("alternating", N, dtype)
+        g = torch.Generator().manual_seed(N + 1)
+        M = 66
+        scale = torch.where(torch.arange(M) % 2 == 0, small, big)[:, None]
+        x = (torch.randn(M, N, generator=g) * scale).to(workloads.TORCH_DTYPES[dtype])
+        w = (torch.randn(N, generator=g) * 0.1 + 1).to(workloads.TORCH_DTYPES[dtype])
+        run_and_compare(bnd, x, w, 0.0, 0.0, dtype, f"alternating N={N} {dtype}")
+
+
+# ---------------------------------------------------------------------------
+# 6. Invariants and execution properties.
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("name", ["rmsnorm_16384x512_bf16", "rmsnorm_8192x3000_bf16_offset1",
+                                  "rmsnorm_262144x128_fp16"])
+def test_in_place(bnd, name):
+    wl = workloads.WORKLOADS[name]
+    announce("in-place", name)
+    x, w = workloads.make_inputs(wl, seed=2, rows=1000)
+    xg, wg = x.to(DEV), w.to(DEV)
+    r = torch.empty(1000, dtype=torch.float32, device=DEV)
+    bnd.rmsnorm_fwd_out(xg, wg, xg, r, wl.eps, wl.offset)
+    torch.cuda.synchronize()
+    y_ref, r_ref = parity.oracle_for(x, w, wl.eps, wl.offset, wl.dtype)
+    parity.compare(xg, r, y_ref, r_ref, wl.dtype, f"in-place {name}")
+
+
+def test_non_default_stream(bnd):
+    wl = workloads.WORKLOADS["rmsnorm_16384x512_bf16"]
+    announce("stream")
+    x, w = workloads.make_inputs(wl, seed=3, rows=4096)
+    xg, wg = x.to(DEV), w.to(DEV)
+    s = torch.cuda.Stream()
+    y = torch.empty_like(xg)
+    r = torch.empty(4096, dtype=torch.float32, device=DEV)
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        bnd.rmsnorm_fwd_out(xg, wg, y, r, wl.eps, wl.offset)
+    s.synchronize()
+    y_ref, r_ref = parity.oracle_for(x, w, wl.eps, wl.offset, wl.dtype)
+    parity.compare(y, r, y_ref, r_ref, wl.dtype, "stream")
+
+
+@pytest.mark.parametrize("name", list(workloads.WORKLOADS))
+def test_deterministic_and_grid_independent(bnd, name):
+    """Bitwise identical results over repeats and over grid sizes (the
+    persistent loop changes which workgroup handles a row, not the row's
+    arithmetic)."""
+    wl = workloads.WORKLOADS[name]
+    announce("determinism", name)
+    M = min(wl.M, 2048)
+    x, w = workloads.make_inputs(wl, seed=4, rows=M)
+    xg, wg = x.to(DEV), w.to(DEV)
+    y0, r0 = bnd.rmsnorm_fwd(xg, wg, wl.eps, wl.offset)
+    for _ in range(10):
+        y1, r1 = bnd.rmsnorm_fwd(xg, wg, wl.eps, wl.offset)
+        assert torch.equal(y0.view(torch.int16), y1.view(torch.int16)) and torch.equal(r0, r1)
+    plan = bnd.plan_query(M, wl.N, wl.dtype)
+    for grid in (1, 2, 7, 64):
+        y2, r2 = bnd.rmsnorm_fwd(xg, wg, wl.eps, wl.offset, plan=plan.copy(grid=grid))
+        assert torch.equal(y0.view(torch.int16), y2.view(torch.int16)) and torch.equal(r0, r2), grid
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp16"])
+def test_sign_symmetry(bnd, dtype):
+    announce("sign", dtype)
+    g = torch.Generator().manual_seed(9)
+    td = workloads.TORCH_DTYPES[dtype]
+    for N in (128, 512, 3000, 8192, 77):
+        x = torch.randn(100, N, generator=g).to(td).to(DEV)
+        w = torch.randn(N, generator=g).to(td).to(DEV)
+        y0, r0 = bnd.rmsnorm_fwd(x, w, 1e-6, 1.0)
+        y1, r1 = bnd.rmsnorm_fwd(-x, w, 1e-6, 1.0)
+        assert torch.equal(r0, r1)
+        a, b = y0.view(torch.int16).int(), y1.view(torch.int16).int()
+        flipped = b ^ torch.tensor(-0x8000, dtype=torch.int32, device=DEV)
+        zero = (a & 0x7FFF) == 0
+        assert torch.all((a == flipped) | zero), N
+
+
+def test_m_zero_writes_nothing(bnd):
+    announce("m-zero")
+    x = torch.empty(0, 512, dtype=torch.bfloat16, device=DEV)
+    w = torch.ones(512, dtype=torch.bfloat16, device=DEV)
+    y, r = bnd.rmsnorm_fwd(x, w)
+    torch.cuda.synchronize()
+    assert y.shape == (0, 512) and r.shape == (0,)
+
+
+def test_python_checks_reject_bad_tensors(bnd):
+    x = torch.randn(4, 64, device=DEV).to(torch.bfloat16)
+    with pytest.raises(ValueError):
+        bnd.rmsnorm_fwd(x, torch.ones(64, dtype=torch.float16, device=DEV))
+    with pytest.raises(ValueError):
+        bnd.rmsnorm_fwd(x.t(), torch.ones(4, dtype=torch.bfloat16, device=DEV))
+    with pytest.raises(ValueError):
+        bnd.rmsnorm_fwd(x.float(), torch.ones(64, device=DEV))
+    with pytest.raises(bnd.RmsnormError):
+        bnd.rmsnorm_fwd(x, torch.ones(64, dtype=torch.bfloat16, device=DEV), eps=-1.0)
+
+
+def test_kernels_do_not_spill(bnd):
+    """Every kernel the planner can pick runs without scratch (no VGPR spills)."""
+    seen = {}
+    for name, wl in workloads.WORKLOADS.items():
+        for dtype in ("bf16", "fp16"):
+            plan = bnd.plan_query(wl.M, wl.N, dtype)
+            res = bnd.plan_resources(plan, dtype)
+            seen[(name, dtype)] = res
+            assert res["scratch_bytes"] == 0, (name, dtype, res)
+    print(seen)
