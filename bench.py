@@ -5,10 +5,12 @@
 
 A step is one pass of the forward (one kernel launch) over one batch: x [M, N]
 read once, y [M, N] and rstd [M] written once, w [N] read once.  Batches
-rotate over enough distinct (x, y, rstd) buffer sets (512 MiB or more in total)
-that a step never finds its batch in the 256 MB Infinity Cache left by the
-previous ones, so the bytes come from HBM.  All batches are resident in HBM
-before the timed region.
+rotate over enough distinct (x, y, rstd) buffer sets that the x read by a
+step was last touched at least 1 GiB of x earlier (four times the 256 MB
+Infinity Cache; y is written with non-temporal stores and does not displace
+x there), so its bytes come from HBM: measured, the time per step stops
+changing once the rotation passes about 400 MB of x.  All batches are
+resident in HBM before the timed region.
 
 GB/s = (2*M*N*s + N*s + 4*M) / seconds / 1e9, the read-plus-write formula of
 "Rmsnorm Kernel Optimization" (Verification), with s = 2 bytes per element.
@@ -36,7 +38,7 @@ if ROOT not in sys.path:
 METRIC = "achieved HBM GB/s and % of MI355X peak, RMSNorm fwd 16384x512 bf16"
 PEAK_GBPS = 8000.0           # MI355X HBM3E, published
 MALL_BYTES = 256 * 2 ** 20   # Infinity Cache
-ROTATION_BYTES = 512 * 2 ** 20
+ROTATION_X_BYTES = 4 * MALL_BYTES
 
 
 def log(*a):
@@ -63,6 +65,58 @@ def measured_traffic(workload: str):
         log(f"traffic: {path} was taken on other kernel sources; reporting null")
         return None
     return t.get("traffic_bytes_per_launch")
+
+
+def counter_median_kib(path: str, kernel_substr: str, counter: str) -> float:
+    import csv
+    import statistics
+
+    vals = [float(r["Counter_Value"]) for r in csv.DictReader(open(path))
+            if kernel_substr in r["Kernel_Name"] and r["Counter_Name"] == counter]
+    if not vals:
+        raise SystemExit(f"no {counter} rows for kernels matching {kernel_substr!r} in {path}")
+    return statistics.median(vals)
+
+
+def traffic_from_counters(wl, name: str, directory: str) -> dict:
+    """HBM bytes per launch from rocprofv3 FETCH_SIZE / WRITE_SIZE runs.
+
+    Expects <dir>/<workload>_<kernel>_<COUNTER>_counter_collection.csv for
+    kernel in (rmsnorm, copy): the runs of this script with --kernel rmsnorm
+    and --kernel copy under `rocprofv3 --pmc FETCH_SIZE` and, separately,
+    `--pmc WRITE_SIZE`.  Each counter is scaled by what it reads for the copy
+    kernel, whose true bytes are known (M*N*2 read, M*N*2 written).
+    """
+    def f(kernel, counter, match):
+        return counter_median_kib(
+            os.path.join(directory, f"{name}_{kernel}_{counter}_counter_collection.csv"), match, counter)
+
+    copy_bytes = wl.M * wl.N * wl.elem_bytes
+    copy_fetch = f("copy", "FETCH_SIZE", "copyBuffer")
+    copy_write = f("copy", "WRITE_SIZE", "copyBuffer")
+    fetch_scale = copy_bytes / (copy_fetch * 1024)
+    write_scale = copy_bytes / (copy_write * 1024)
+    rms_fetch = f("rmsnorm", "FETCH_SIZE", "rmsnorm_")
+    rms_write = f("rmsnorm", "WRITE_SIZE", "rmsnorm_")
+    fetch_b = rms_fetch * 1024 * fetch_scale
+    write_b = rms_write * 1024 * write_scale
+    alg_read = wl.M * wl.N * wl.elem_bytes + wl.N * wl.elem_bytes
+    alg_write = wl.M * wl.N * wl.elem_bytes + 4 * wl.M
+    return {
+        "workload": name,
+        "kernel_source_sha256": kernel_source_sha256(),
+        "counters_kib_per_dispatch": {"rmsnorm_FETCH_SIZE": rms_fetch, "rmsnorm_WRITE_SIZE": rms_write,
+                                      "copy_FETCH_SIZE": copy_fetch, "copy_WRITE_SIZE": copy_write},
+        "copy_bytes_each_way": copy_bytes,
+        "fetch_scale": fetch_scale,
+        "write_scale": write_scale,
+        "fetch_bytes_per_launch": round(fetch_b),
+        "write_bytes_per_launch": round(write_b),
+        "traffic_bytes_per_launch": round(fetch_b + write_b),
+        "algorithmic_read_bytes": alg_read,
+        "algorithmic_write_bytes": alg_write,
+        "traffic_over_algorithmic": (fetch_b + write_b) / (alg_read + alg_write),
+    }
 
 
 def cpu_baseline(wl, x_cpu, w_cpu, seconds: float):
@@ -101,7 +155,26 @@ def main() -> int:
     ap.add_argument("--plan", default=None, help="JSON object overriding plan fields")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--traffic-from", default=None, metavar="DIR",
+                    help="write profiles/traffic_<workload>.json from rocprofv3 counter CSVs in DIR "
+                         "and exit (no GPU needed)")
+    ap.add_argument("--kernel", choices=["rmsnorm", "copy"], default="rmsnorm",
+                    help="copy: time a plain device copy of x into y instead (same rotation, "
+                         "2*M*N*s bytes per step), the practical ceiling and the counter "
+                         "calibration reference")
     args = ap.parse_args()
+
+    if args.traffic_from:
+        from memory_bound_row_rmsnorm_amd import workloads
+
+        name = args.workload or workloads.HEADLINE
+        t = traffic_from_counters(workloads.WORKLOADS[name], name, args.traffic_from)
+        out = os.path.join(ROOT, "profiles", f"traffic_{name}.json")
+        with open(out, "w") as f:
+            json.dump(t, f, indent=1)
+            f.write("\n")
+        print(json.dumps(t))
+        return 0
 
     if args.gpus != 1:
         log(f"bench.py measures one GPU only: --gpus {args.gpus} is not supported. The row "
@@ -117,7 +190,8 @@ def main() -> int:
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     per_set = 2 * wl.M * wl.N * 2 + 4 * wl.M
-    sets = args.sets or max(2, min(64, math.ceil(ROTATION_BYTES / per_set)))
+    x_bytes = wl.M * wl.N * 2
+    sets = args.sets or max(2, min(256, math.ceil(ROTATION_X_BYTES / x_bytes)))
 
     log(f"workload {name}: M={wl.M} N={wl.N} {wl.dtype}, {sets} rotation sets "
         f"({sets * per_set / 2**20:.0f} MiB), mode {args.mode}")
@@ -144,7 +218,12 @@ def main() -> int:
     code = binding.DTYPE_NAMES[wl.dtype]
     argv = [(xs[k].data_ptr(), w_dev.data_ptr(), ys[k].data_ptr(), rs[k].data_ptr()) for k in range(sets)]
 
+    def launch_copy(i: int, stream_handle):
+        ys[i % sets].copy_(xs[i % sets])
+
     def launch(i: int, stream_handle):
+        if args.kernel == "copy":
+            return launch_copy(i, stream_handle)
         xp, wp, yp, rp = argv[i % sets]
         st = lib.rmsnorm_fwd_with_plan(xp, wp, yp, rp, wl.M, wl.N, wl.eps, wl.offset, code, pplan,
                                        stream_handle)
@@ -189,10 +268,10 @@ def main() -> int:
     wall_s = time.perf_counter() - t_wall
     ms_total = start.elapsed_time(end)
     ms_per_step = ms_total / args.steps
-    nbytes = wl.algorithmic_bytes()
+    nbytes = wl.algorithmic_bytes() if args.kernel == "rmsnorm" else 2 * wl.M * wl.N * wl.elem_bytes
     gbps = nbytes / (ms_per_step * 1e-3) / 1e9
 
-    traffic = measured_traffic(name)
+    traffic = measured_traffic(name) if args.kernel == "rmsnorm" else None
     out = {
         "metric": METRIC,
         "value": round(gbps, 2),
@@ -215,6 +294,7 @@ def main() -> int:
             "algorithmic_bytes_per_step": nbytes,
             "rotation_sets": sets,
             "launch": args.mode,
+            "kernel": args.kernel,
             "plan": {k: v for k, v in plan.as_dict().items()},
             "kernel_resources": res,
             "pct_of_peak": round(100 * gbps / PEAK_GBPS, 2),
@@ -229,7 +309,7 @@ def main() -> int:
             "traffic": traffic,
         },
     }
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and args.kernel == "rmsnorm":
         log(f"cpu baseline: oracle for about {args.cpu_seconds:.0f} s")
         out["cpu_baseline"] = cpu_baseline(wl, x0, w0, args.cpu_seconds)
     print(json.dumps(out), flush=True)

@@ -86,12 +86,18 @@ typedef enum rmsnorm_variant {
  *                     64/lanes_per_row rows, and all of a trip's loads are
  *                     issued before its first reduction.  1 otherwise
  *   block_threads     workgroup size (a multiple of 64, at most 1024)
+ *   prefetch          WAVE, BLOCK: 1 = load the next trip's rows before this
+ *                     trip's reduction (pays off when workgroups loop); 0 otherwise
  *   grid              workgroups launched.  When grid times the rows one
  *                     workgroup covers per trip is below M the workgroups
  *                     loop over rows (persistent grid) and keep offset + w
- *                     in registers across trips
+ *                     in registers across trips.  The automatic plan uses
+ *                     one trip per workgroup, measured fastest on MI355X;
+ *                     set grid = resident_grid for a persistent launch
  *   rows_per_trip     rows one workgroup covers per loop trip (derived)
  *   trips             loop trips of the busiest workgroup (derived)
+ *   resident_grid     workgroups of this kernel the device holds at once:
+ *                     compute units x resident workgroups per unit (derived)
  */
 typedef struct rmsnorm_plan {
     int32_t variant;
@@ -100,9 +106,11 @@ typedef struct rmsnorm_plan {
     int32_t vectors_per_lane;
     int32_t row_slots;
     int32_t block_threads;
+    int32_t prefetch;
     int64_t grid;
     int64_t rows_per_trip;
     int64_t trips;
+    int64_t resident_grid;
 } rmsnorm_plan_t;
 
 /*
@@ -122,8 +130,8 @@ int rmsnorm_fwd(const void* x, const void* w, void* y, float* rstd,
 /*
  * Same as rmsnorm_fwd but with an explicit launch plan (from
  * rmsnorm_plan_query, possibly edited: variant, lanes_per_row,
- * vectors_per_lane, row_slots, block_threads and grid are honoured; the
- * derived fields are ignored).  Returns RMSNORM_ERR_PLAN, before any HIP
+ * vectors_per_lane, row_slots, block_threads, prefetch and grid are honoured;
+ * the derived fields are ignored).  Returns RMSNORM_ERR_PLAN, before any HIP
  * call, if the plan's kernel does not exist, does not cover N, or needs an
  * alignment the pointers lack.  For benchmarks and tests of each kernel.
  */
@@ -133,9 +141,11 @@ int rmsnorm_fwd_with_plan(const void* x, const void* w, void* y, float* rstd,
 
 /*
  * The plan rmsnorm_fwd would use for these sizes and pointers (only their
- * alignment is looked at; they may be NULL, which counts as aligned).
- * cu_count > 0 plans for that many compute units without touching HIP (host
- * only); cu_count <= 0 asks the current device.  Writes *out and returns a
+ * alignment is looked at; they may be NULL, which counts as aligned).  The
+ * plan itself is host logic.  cu_count only feeds resident_grid: cu_count > 0
+ * assumes that many compute units and the register-free bound of 2048
+ * threads per unit, touching no HIP API; cu_count <= 0 asks the current
+ * device (unit count and the kernel's occupancy).  Writes *out and returns a
  * status.
  */
 int rmsnorm_plan_query(int64_t M, int64_t N, int dtype,

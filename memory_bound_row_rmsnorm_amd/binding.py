@@ -51,9 +51,11 @@ class Plan(ctypes.Structure):
         ("vectors_per_lane", ctypes.c_int32),
         ("row_slots", ctypes.c_int32),
         ("block_threads", ctypes.c_int32),
+        ("prefetch", ctypes.c_int32),
         ("grid", ctypes.c_int64),
         ("rows_per_trip", ctypes.c_int64),
         ("trips", ctypes.c_int64),
+        ("resident_grid", ctypes.c_int64),
     ]
 
     def as_dict(self) -> dict:
@@ -178,7 +180,7 @@ def rmsnorm_fwd(x: torch.Tensor, w: torch.Tensor, eps: float = 1e-6, offset: flo
 
 def plan_query(M: int, N: int, dtype, x_ptr: int = 0, w_ptr: int = 0, y_ptr: int = 0,
                cu_count: int = 0) -> Plan:
-    """The plan rmsnorm_fwd uses; cu_count > 0 plans on the host only."""
+    """The plan rmsnorm_fwd uses; cu_count > 0 sizes resident_grid without a GPU."""
     p = Plan()
     _check(lib.rmsnorm_plan_query(M, N, _dtype_code(dtype), x_ptr or None, w_ptr or None,
                                   y_ptr or None, cu_count, ctypes.byref(p)))

@@ -140,12 +140,12 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 // ---------------------------------------------------------------------------
 // Kernel lookup.
 // ---------------------------------------------------------------------------
-const KernelEntry* find_kernel(int variant, int dtype, int lanes, int vpl, int slots) {
+const KernelEntry* find_kernel(int variant, int dtype, int lanes, int vpl, int slots, bool prefetch) {
     int n = 0;
     const KernelEntry* t = rmsnorm_impl::kernel_table(&n);
     for (int i = 0; i < n; ++i) {
         const KernelEntry& k = t[i];
-        if (k.variant != variant || k.dtype != dtype) continue;
+        if (k.variant != variant || k.dtype != dtype || k.prefetch != prefetch) continue;
         if (variant == RMSNORM_VARIANT_WAVE &&
             (k.lanes_per_row != lanes || k.vectors_per_lane != vpl || k.row_slots != slots))
             continue;
@@ -169,15 +169,18 @@ int finish_plan(rmsnorm_plan_t* p, int64_t M, int64_t N, int dtype, const void* 
         p->lanes_per_row = p->block_threads;
         p->vectors_per_lane = 0;
         p->row_slots = 1;
+        p->prefetch = 0;
         p->rows_per_trip = 1;
-        k = find_kernel(RMSNORM_VARIANT_GENERIC, dtype, 0, 0, 1);
+        k = find_kernel(RMSNORM_VARIANT_GENERIC, dtype, 0, 0, 1, false);
     } else if (p->variant == RMSNORM_VARIANT_WAVE || p->variant == RMSNORM_VARIANT_BLOCK) {
         if (N % 8 != 0) return fail(RMSNORM_ERR_PLAN, "16-byte kernels need N % 8 == 0");
         if (!aligned16(x) || !aligned16(w) || !aligned16(y))
             return fail(RMSNORM_ERR_PLAN, "16-byte kernels need 16-byte aligned x, w and y");
         p->vec_elems = 8;
+        if (p->prefetch != 0 && p->prefetch != 1) return fail(RMSNORM_ERR_PLAN, "prefetch must be 0 or 1");
         if (p->variant == RMSNORM_VARIANT_WAVE) {
-            k = find_kernel(RMSNORM_VARIANT_WAVE, dtype, p->lanes_per_row, p->vectors_per_lane, p->row_slots);
+            k = find_kernel(RMSNORM_VARIANT_WAVE, dtype, p->lanes_per_row, p->vectors_per_lane, p->row_slots,
+                            p->prefetch != 0);
             if (k) {
                 const int64_t cap = static_cast<int64_t>(p->lanes_per_row) * p->vectors_per_lane * 8;
                 if (cap < N) return fail(RMSNORM_ERR_PLAN, "wave plan does not cover N");
@@ -186,7 +189,7 @@ int finish_plan(rmsnorm_plan_t* p, int64_t M, int64_t N, int dtype, const void* 
         } else {
             p->row_slots = 1;
             p->lanes_per_row = p->block_threads;
-            k = find_kernel(RMSNORM_VARIANT_BLOCK, dtype, 0, p->vectors_per_lane, 1);
+            k = find_kernel(RMSNORM_VARIANT_BLOCK, dtype, 0, p->vectors_per_lane, 1, p->prefetch != 0);
             if (k) {
                 const int64_t cap = static_cast<int64_t>(p->block_threads) * p->vectors_per_lane * 8;
                 if (cap < N) return fail(RMSNORM_ERR_PLAN, "block plan does not cover N");
@@ -204,13 +207,26 @@ int finish_plan(rmsnorm_plan_t* p, int64_t M, int64_t N, int dtype, const void* 
 
 // Vectors per lane the block and wave families are compiled for (more would
 // not fit the 128 VGPRs a 1024-thread workgroup allows without spilling).
-constexpr int kBlockVpt[] = {1, 2, 3, 4, 5, 6};
-constexpr int kWaveVpl[] = {1, 2, 3, 4, 5, 6};
+constexpr int kWaveSlots[] = {8, 4, 2, 1};
 constexpr int64_t kMaxVectorN = 1024LL * 6 * 8;   // widest row the 16-byte kernels hold
+constexpr int64_t kMaxGrid = 0x7FFFFFFF;
+constexpr int64_t kWaveBytesInFlight = 4096;      // row bytes one wave loads per trip
 
-// Choose family and geometry.  cu_count and blocks_per_cu size the grid.
-// Returns RMSNORM_OK and a plan without derived fields.
-int choose_plan(int64_t M, int64_t N, const void* x, const void* w, const void* y, rmsnorm_plan_t* p) {
+// Choose family and geometry (host only; no device needed).  Rules measured
+// on MI355X with inputs cold in HBM:
+//  * rows of at most 1024 elements: the wave family, 16/32/64 lanes per row
+//    so that a row segment is one 16-byte vector per lane (two at 1024),
+//    and enough rows per wave for about 4 KiB of loads per trip;
+//  * longer rows: the block family with 256 threads up to 12288 elements,
+//    512 up to 24576, 1024 beyond, each thread holding ceil(N/8/threads)
+//    vectors;
+//  * N not a multiple of 8, a row wider than 49152, or a pointer not 16-byte
+//    aligned: the generic kernel;
+//  * one trip per workgroup (grid = row groups): launching every row group
+//    measured faster than a grid of resident workgroups looping over rows on
+//    every shape tried.
+int choose_plan(int64_t M, int64_t N, const void* x, const void* w, const void* y, int dtype,
+                rmsnorm_plan_t* p) {
     std::memset(p, 0, sizeof(*p));
     const bool vec_ok = (N % 8 == 0) && aligned16(x) && aligned16(w) && aligned16(y) &&
                         N <= kMaxVectorN;
@@ -218,91 +234,57 @@ int choose_plan(int64_t M, int64_t N, const void* x, const void* w, const void* 
         p->variant = RMSNORM_VARIANT_GENERIC;
         p->block_threads = N >= 1024 ? 256 : (N >= 256 ? 128 : 64);
         p->row_slots = 1;
-        return RMSNORM_OK;
-    }
-    const int64_t nvec = N / 8;
-    if (nvec <= 128) {
-        // wave family: short rows live in one wavefront
+    } else if (N / 8 <= 128) {
+        const int64_t nvec = N / 8;
         p->variant = RMSNORM_VARIANT_WAVE;
         p->block_threads = kWaveBlockThreads;
-        if (nvec <= 16) {
-            p->lanes_per_row = 16;
-            p->vectors_per_lane = 1;
-        } else if (nvec <= 32) {
-            p->lanes_per_row = 32;
-            p->vectors_per_lane = 1;
-        } else {
-            p->lanes_per_row = 64;
-            for (int v : kWaveVpl)
-                if (64LL * v >= nvec) { p->vectors_per_lane = v; break; }
+        p->lanes_per_row = nvec <= 16 ? 16 : (nvec <= 32 ? 32 : 64);
+        p->vectors_per_lane = static_cast<int>(ceil_div(nvec, p->lanes_per_row));
+        const int64_t per_slot = N * 2 * (64 / p->lanes_per_row);
+        p->row_slots = 1;
+        for (int s : kWaveSlots) {
+            if (s * per_slot <= kWaveBytesInFlight &&
+                find_kernel(RMSNORM_VARIANT_WAVE, dtype, p->lanes_per_row, p->vectors_per_lane, s, false)) {
+                p->row_slots = s;
+                break;
+            }
         }
-        // rows in flight per wave: aim at about 2 KiB of loads per wave
-        const int64_t row_bytes = N * 2;
-        const int64_t per_slot = row_bytes * (64 / p->lanes_per_row);
-        int slots = static_cast<int>(2048 / per_slot);
-        if (slots < 1) slots = 1;
-        if (slots > 8) slots = 8;
-        while (slots > 1 && !find_kernel(RMSNORM_VARIANT_WAVE, RMSNORM_BF16, p->lanes_per_row,
-                                         p->vectors_per_lane, slots))
-            slots /= 2;
-        p->row_slots = slots;
-        return RMSNORM_OK;
+    } else {
+        const int64_t nvec = N / 8;
+        p->variant = RMSNORM_VARIANT_BLOCK;
+        p->row_slots = 1;
+        p->block_threads = nvec <= 256 * 6 ? 256 : (nvec <= 512 * 6 ? 512 : 1024);
+        p->vectors_per_lane = static_cast<int>(ceil_div(nvec, p->block_threads));
     }
-    // block family: least padding first (in 1/32ths of the row), then at most
-    // 4 vectors per thread (fewer registers held per row), then 256, 512,
-    // 128, 1024 threads in that order
-    p->variant = RMSNORM_VARIANT_BLOCK;
-    p->row_slots = 1;
-    int best_t = 0, best_v = 0;
-    int64_t best_key = INT64_MAX;
-    const int order[] = {256, 512, 128, 1024};
-    for (int oi = 0; oi < 4; ++oi) {
-        const int t = order[oi];
-        for (int v : kBlockVpt) {
-            const int64_t cap = static_cast<int64_t>(t) * v;
-            if (cap < nvec) continue;
-            const int64_t pad32 = ceil_div((cap - nvec) * 32, nvec);
-            const int64_t key = pad32 * 100 + (v > 4 ? 10 : 0) + oi;
-            if (key < best_key) { best_key = key; best_t = t; best_v = v; }
-            break;
-        }
-    }
-    p->block_threads = best_t;
-    p->vectors_per_lane = best_v;
-    return best_t ? RMSNORM_OK : fail(RMSNORM_ERR_PLAN, "no block plan covers N");
-}
-
-// Grid: enough workgroups for one trip each, capped at what the CUs hold.
-void size_grid(rmsnorm_plan_t* p, int64_t M, int cu_count, int blocks_per_cu) {
     int64_t rows_per_trip = 1;
     if (p->variant == RMSNORM_VARIANT_WAVE)
         rows_per_trip = static_cast<int64_t>(p->block_threads / 64) * (64 / p->lanes_per_row) * p->row_slots;
-    int64_t need = M > 0 ? ceil_div(M, rows_per_trip) : 1;
-    int64_t cap = static_cast<int64_t>(cu_count) * blocks_per_cu;
-    if (cap < 1) cap = 1;
-    p->grid = need < cap ? need : cap;
+    const int64_t need = M > 0 ? ceil_div(M, rows_per_trip) : 1;
+    p->grid = need < kMaxGrid ? need : kMaxGrid;
+    p->prefetch = 0;
+    if (p->variant != RMSNORM_VARIANT_GENERIC && p->grid < need &&
+        find_kernel(p->variant, dtype, p->variant == RMSNORM_VARIANT_WAVE ? p->lanes_per_row : 0,
+                    p->vectors_per_lane, p->row_slots, true))
+        p->prefetch = 1;
+    return RMSNORM_OK;
 }
 
-int plan_for_call(int64_t M, int64_t N, int dtype, const void* x, const void* w, const void* y,
-                  int cu_count_hint, rmsnorm_plan_t* p, const KernelEntry** kernel) {
-    int st = choose_plan(M, N, x, w, y, p);
-    if (st != RMSNORM_OK) return st;
-    // look the kernel up once with a provisional grid to learn its occupancy
-    p->grid = 1;
-    const KernelEntry* k = nullptr;
-    st = finish_plan(p, M, N, dtype, x, w, y, &k);
-    if (st != RMSNORM_OK) return st;
-    int cu = cu_count_hint, bpc = 0;
+// Workgroups of the plan's kernel the device holds at once.  cu_count > 0:
+// that many units at the register-free bound of 2048 threads per unit, host
+// only; otherwise the current device's unit count times the kernel's
+// occupancy.
+int resident_grid(const rmsnorm_plan_t* p, const KernelEntry* k, int cu_count, int64_t* out) {
+    int cu = cu_count, bpc = 0;
     if (cu > 0) {
-        bpc = kMaxThreadsPerCu / p->block_threads;  // host-only estimate: no register limit
+        bpc = kMaxThreadsPerCu / p->block_threads;
     } else {
-        st = device_info(&cu);
+        int st = device_info(&cu);
         if (st != RMSNORM_OK) return st;
         st = occupancy(k->func, p->block_threads, &bpc);
         if (st != RMSNORM_OK) return st;
     }
-    size_grid(p, M, cu, bpc);
-    return finish_plan(p, M, N, dtype, x, w, y, kernel);
+    *out = static_cast<int64_t>(cu) * bpc;
+    return RMSNORM_OK;
 }
 
 int launch(const KernelEntry* k, const rmsnorm_plan_t* p, const void* x, const void* w, void* y,
@@ -337,7 +319,11 @@ int rmsnorm_fwd(const void* x, const void* w, void* y, float* rstd, int64_t M, i
     if (st != RMSNORM_OK || M == 0) return st;
     rmsnorm_plan_t p;
     const KernelEntry* k = nullptr;
-    st = plan_for_call(M, N, dtype, x, w, y, 0, &p, &k);
+    st = choose_plan(M, N, x, w, y, dtype, &p);
+    if (st == RMSNORM_OK) st = finish_plan(&p, M, N, dtype, x, w, y, &k);
+    if (st != RMSNORM_OK) return st;
+    int cu = 0;
+    st = device_info(&cu);  // gfx950 check (cached per device)
     if (st != RMSNORM_OK) return st;
     return launch(k, &p, x, w, y, rstd, M, N, eps, offset, stream);
 }
@@ -352,6 +338,9 @@ int rmsnorm_fwd_with_plan(const void* x, const void* w, void* y, float* rstd, in
     const KernelEntry* k = nullptr;
     st = finish_plan(&p, M, N, dtype, x, w, y, &k);
     if (st != RMSNORM_OK || M == 0) return st;
+    int cu = 0;
+    st = device_info(&cu);  // gfx950 check (cached per device)
+    if (st != RMSNORM_OK) return st;
     return launch(k, &p, x, w, y, rstd, M, N, eps, offset, stream);
 }
 
@@ -362,7 +351,10 @@ int rmsnorm_plan_query(int64_t M, int64_t N, int dtype, const void* x, const voi
     int st = check_shape_dtype(M, N, dtype);
     if (st != RMSNORM_OK) return st;
     rmsnorm_plan_t p;
-    st = plan_for_call(M, N, dtype, x, w, y, cu_count, &p, nullptr);
+    const KernelEntry* k = nullptr;
+    st = choose_plan(M, N, x, w, y, dtype, &p);
+    if (st == RMSNORM_OK) st = finish_plan(&p, M, N, dtype, x, w, y, &k);
+    if (st == RMSNORM_OK) st = resident_grid(&p, k, cu_count, &p.resident_grid);
     if (st != RMSNORM_OK) return st;
     *out = p;
     return RMSNORM_OK;
@@ -374,10 +366,12 @@ int rmsnorm_plan_resources(const rmsnorm_plan_t* plan, int dtype, int32_t* vgprs
     if (!plan) return fail(RMSNORM_ERR_NULL, "plan must be non-NULL");
     if (dtype != RMSNORM_BF16 && dtype != RMSNORM_FP16) return fail(RMSNORM_ERR_DTYPE, "bad dtype");
     const KernelEntry* k = nullptr;
-    if (plan->variant == RMSNORM_VARIANT_GENERIC) k = find_kernel(RMSNORM_VARIANT_GENERIC, dtype, 0, 0, 1);
-    else if (plan->variant == RMSNORM_VARIANT_BLOCK) k = find_kernel(RMSNORM_VARIANT_BLOCK, dtype, 0, plan->vectors_per_lane, 1);
+    const bool pf = plan->prefetch != 0;
+    if (plan->variant == RMSNORM_VARIANT_GENERIC) k = find_kernel(RMSNORM_VARIANT_GENERIC, dtype, 0, 0, 1, false);
+    else if (plan->variant == RMSNORM_VARIANT_BLOCK)
+        k = find_kernel(RMSNORM_VARIANT_BLOCK, dtype, 0, plan->vectors_per_lane, 1, pf);
     else if (plan->variant == RMSNORM_VARIANT_WAVE)
-        k = find_kernel(RMSNORM_VARIANT_WAVE, dtype, plan->lanes_per_row, plan->vectors_per_lane, plan->row_slots);
+        k = find_kernel(RMSNORM_VARIANT_WAVE, dtype, plan->lanes_per_row, plan->vectors_per_lane, plan->row_slots, pf);
     if (!k) return fail(RMSNORM_ERR_PLAN, "no compiled kernel for this plan");
     hipFuncAttributes attr;
     hipError_t e = hipFuncGetAttributes(&attr, k->func);

@@ -28,6 +28,7 @@ struct KernelEntry {
     int lanes_per_row;     // WAVE: 16/32/64; BLOCK, GENERIC: 0 (= block size)
     int vectors_per_lane;  // WAVE, BLOCK: 16-byte vectors per lane per row; GENERIC: 0
     int row_slots;         // WAVE: slots per wave per trip; others 1
+    bool prefetch;         // WAVE, BLOCK: next trip's rows loaded before this trip's reduction
     const void* func;      // host stub of the __global__ function
     const char* name;
 };

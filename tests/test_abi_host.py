@@ -110,26 +110,42 @@ def covers(p, N):
 @pytest.mark.parametrize("M,N", [(64, 512), (16384, 512), (8192, 3000), (32768, 8192),
                                  (262144, 128), (4096, 16384), (1, 8), (7, 256), (100, 1024),
                                  (3, 4096), (5, 49152)])
-def test_host_plans_cover_the_row_and_fill_the_chip(M, N):
+def test_host_plans_cover_the_row_one_trip_per_workgroup(M, N):
     for dtype in (BF16, FP16):
         p = host_plan(M, N, dtype)
         assert p.variant in (bnd.VARIANT_WAVE, bnd.VARIANT_BLOCK)
         assert p.vec_elems == 8 and covers(p, N)
+        # no more vectors per lane than the row needs
+        assert (p.vectors_per_lane - 1) * p.lanes_per_row * 8 < N
         assert p.block_threads % 64 == 0 and 64 <= p.block_threads <= 1024
         groups = -(-M // p.rows_per_trip)
-        assert p.grid == min(groups, 256 * (2048 // p.block_threads))
-        assert p.trips == -(-groups // p.grid)
-        assert p.grid * p.trips * p.rows_per_trip >= M
+        assert p.grid == groups and p.trips == 1 and p.prefetch == 0
+        assert p.resident_grid == 256 * (2048 // p.block_threads)
 
 
-def test_short_rows_go_to_the_wave_family_long_rows_to_the_block_family():
-    assert host_plan(16384, 512).variant == bnd.VARIANT_WAVE
-    p = host_plan(262144, 128)
-    assert (p.variant, p.lanes_per_row) == (bnd.VARIANT_WAVE, 16)
-    assert host_plan(64, 256).lanes_per_row == 32
-    assert host_plan(32768, 8192).variant == bnd.VARIANT_BLOCK
+def test_planner_choices_for_the_workloads():
+    p = host_plan(16384, 512)
+    assert (p.variant, p.lanes_per_row, p.vectors_per_lane, p.row_slots) == (bnd.VARIANT_WAVE, 64, 1, 4)
+    assert p.rows_per_trip == 16 and p.grid == 1024
+    p = host_plan(262144, 128, FP16)
+    assert (p.variant, p.lanes_per_row, p.row_slots) == (bnd.VARIANT_WAVE, 16, 4)
+    p = host_plan(64, 256)
+    assert (p.lanes_per_row, p.row_slots) == (32, 4)
+    p = host_plan(100, 1024)
+    assert (p.lanes_per_row, p.vectors_per_lane, p.row_slots) == (64, 2, 2)
+    p = host_plan(32768, 8192)
+    assert (p.variant, p.block_threads, p.vectors_per_lane) == (bnd.VARIANT_BLOCK, 256, 4)
     p = host_plan(8192, 3000)
-    assert p.variant == bnd.VARIANT_BLOCK and p.block_threads * p.vectors_per_lane * 8 >= 3000
+    assert (p.variant, p.block_threads, p.vectors_per_lane) == (bnd.VARIANT_BLOCK, 256, 2)
+    p = host_plan(4096, 16384, FP16)
+    assert (p.variant, p.block_threads, p.vectors_per_lane) == (bnd.VARIANT_BLOCK, 512, 4)
+    p = host_plan(3, 49152)
+    assert (p.block_threads, p.vectors_per_lane) == (1024, 6)
+
+
+def test_huge_row_counts_loop_with_prefetch():
+    p = host_plan(1 << 40, 8192)
+    assert p.grid == 0x7FFFFFFF and p.trips > 1 and p.prefetch == 1
 
 
 @pytest.mark.parametrize("N,x", [(7, None), (3001, None), (127, None), (512, A + 2), (512, A + 8),

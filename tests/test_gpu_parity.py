@@ -60,19 +60,21 @@ def test_workload_full_size(bnd, name):
 def candidate_plans(bnd, M, N, dtype):
     base = bnd.plan_query(M, N, dtype)
     out = []
-    for lanes in (16, 32, 64):
-        for vpl in range(1, 9):
-            for slots in (1, 2, 4, 8):
-                if lanes * vpl * 8 < N:
+    for pf in (0, 1):
+        for lanes in (16, 32, 64):
+            for vpl in range(1, 9):
+                for slots in (1, 2, 4, 8):
+                    if lanes * vpl * 8 < N:
+                        continue
+                    out.append(base.copy(variant=bnd.VARIANT_WAVE, lanes_per_row=lanes,
+                                         vectors_per_lane=vpl, row_slots=slots, block_threads=256,
+                                         prefetch=pf))
+        for threads in (64, 128, 256, 512, 1024):
+            for vpt in range(1, 9):
+                if threads * vpt * 8 < N:
                     continue
-                out.append(base.copy(variant=bnd.VARIANT_WAVE, lanes_per_row=lanes,
-                                     vectors_per_lane=vpl, row_slots=slots, block_threads=256))
-    for threads in (64, 128, 256, 512, 1024):
-        for vpt in range(1, 9):
-            if threads * vpt * 8 < N:
-                continue
-            out.append(base.copy(variant=bnd.VARIANT_BLOCK, block_threads=threads,
-                                 vectors_per_lane=vpt, row_slots=1))
+                out.append(base.copy(variant=bnd.VARIANT_BLOCK, block_threads=threads,
+                                     vectors_per_lane=vpt, row_slots=1, prefetch=pf))
     for threads in (64, 256, 1024):
         out.append(base.copy(variant=bnd.VARIANT_GENERIC, block_threads=threads))
     return out
