@@ -88,6 +88,14 @@ typedef enum rmsnorm_variant {
  *   block_threads     workgroup size (a multiple of 64, at most 1024)
  *   prefetch          WAVE, BLOCK: 1 = load the next trip's rows before this
  *                     trip's reduction (pays off when workgroups loop); 0 otherwise
+ *   xcd_group         1 to 64: the rows of this many consecutive workgroups
+ *                     run on one XCD (MI355X hands workgroup b to XCD b mod 8;
+ *                     the workgroup index is permuted within windows of
+ *                     8 * xcd_group workgroups).  1 leaves the order alone
+ *   max_blocks_per_cu 0 = no cap; 2 to 32 = at most this many workgroups per
+ *                     compute unit, enforced by giving each workgroup an
+ *                     otherwise unused share of the unit's LDS (an occupancy
+ *                     hint: fewer rows in flight per unit can stream faster)
  *   grid              workgroups launched.  When grid times the rows one
  *                     workgroup covers per trip is below M the workgroups
  *                     loop over rows (persistent grid) and keep offset + w
@@ -107,6 +115,8 @@ typedef struct rmsnorm_plan {
     int32_t row_slots;
     int32_t block_threads;
     int32_t prefetch;
+    int32_t xcd_group;
+    int32_t max_blocks_per_cu;
     int64_t grid;
     int64_t rows_per_trip;
     int64_t trips;
@@ -130,7 +140,8 @@ int rmsnorm_fwd(const void* x, const void* w, void* y, float* rstd,
 /*
  * Same as rmsnorm_fwd but with an explicit launch plan (from
  * rmsnorm_plan_query, possibly edited: variant, lanes_per_row,
- * vectors_per_lane, row_slots, block_threads, prefetch and grid are honoured;
+ * vectors_per_lane, row_slots, block_threads, prefetch, xcd_group,
+ * max_blocks_per_cu and grid are honoured;
  * the derived fields are ignored).  Returns RMSNORM_ERR_PLAN, before any HIP
  * call, if the plan's kernel does not exist, does not cover N, or needs an
  * alignment the pointers lack.  For benchmarks and tests of each kernel.

@@ -52,6 +52,8 @@ class Plan(ctypes.Structure):
         ("row_slots", ctypes.c_int32),
         ("block_threads", ctypes.c_int32),
         ("prefetch", ctypes.c_int32),
+        ("xcd_group", ctypes.c_int32),
+        ("max_blocks_per_cu", ctypes.c_int32),
         ("grid", ctypes.c_int64),
         ("rows_per_trip", ctypes.c_int64),
         ("trips", ctypes.c_int64),

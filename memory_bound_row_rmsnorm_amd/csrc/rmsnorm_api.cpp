@@ -47,11 +47,12 @@ struct DeviceInfo {
     int status = RMSNORM_OK;
     std::string error;
     int cu_count = 0;
+    int lds_per_cu = 0;
 };
 
 DeviceInfo g_devices[kMaxDevices];
 
-int device_info(int* cu_count) {
+int device_info(int* cu_count, int* lds_per_cu = nullptr) {
     int dev = 0;
     hipError_t e = hipGetDevice(&dev);
     if (e != hipSuccess) return fail(RMSNORM_ERR_HIP, std::string("hipGetDevice: ") + hipGetErrorString(e));
@@ -71,9 +72,11 @@ int device_info(int* cu_count) {
             return;
         }
         d.cu_count = p.multiProcessorCount;
+        d.lds_per_cu = static_cast<int>(p.maxSharedMemoryPerMultiProcessor);
     });
     if (d.status != RMSNORM_OK) return fail(d.status, d.error);
     *cu_count = d.cu_count;
+    if (lds_per_cu) *lds_per_cu = d.lds_per_cu;
     return RMSNORM_OK;
 }
 
@@ -163,6 +166,9 @@ int finish_plan(rmsnorm_plan_t* p, int64_t M, int64_t N, int dtype, const void* 
     if (p->block_threads < 64 || p->block_threads > 1024 || p->block_threads % 64 != 0)
         return fail(RMSNORM_ERR_PLAN, "block_threads must be a multiple of 64 in [64, 1024]");
     if (p->grid < 1 || p->grid > 0x7FFFFFFF) return fail(RMSNORM_ERR_PLAN, "grid must be in [1, 2^31)");
+    if (p->xcd_group < 1 || p->xcd_group > 64) return fail(RMSNORM_ERR_PLAN, "xcd_group must be in [1, 64]");
+    if (p->max_blocks_per_cu != 0 && (p->max_blocks_per_cu < 2 || p->max_blocks_per_cu > 32))
+        return fail(RMSNORM_ERR_PLAN, "max_blocks_per_cu must be 0 or in [2, 32]");
     const KernelEntry* k = nullptr;
     if (p->variant == RMSNORM_VARIANT_GENERIC) {
         p->vec_elems = 1;
@@ -211,6 +217,8 @@ constexpr int kWaveSlots[] = {8, 4, 2, 1};
 constexpr int64_t kMaxVectorN = 1024LL * 6 * 8;   // widest row the 16-byte kernels hold
 constexpr int64_t kMaxGrid = 0x7FFFFFFF;
 constexpr int64_t kWaveBytesInFlight = 4096;      // row bytes one wave loads per trip
+constexpr int64_t kXcdGroupBytes = 128 * 1024;    // consecutive row bytes per XCD (block family)
+constexpr int64_t kBytesInFlightPerCu = 64 * 1024; // row bytes resident per compute unit (block family)
 
 // Choose family and geometry (host only; no device needed).  Rules measured
 // on MI355X with inputs cold in HBM:
@@ -224,7 +232,11 @@ constexpr int64_t kWaveBytesInFlight = 4096;      // row bytes one wave loads pe
 //    aligned: the generic kernel;
 //  * one trip per workgroup (grid = row groups): launching every row group
 //    measured faster than a grid of resident workgroups looping over rows on
-//    every shape tried.
+//    every shape tried;
+//  * block family: consecutive rows grouped on one XCD, about 128 KiB per
+//    group (xcd_group: 8 rows at N = 8192, 16 at N = 3000), and at most about
+//    64 KiB of rows resident per compute unit (max_blocks_per_cu 4 at
+//    N = 8192); together 5-6% faster on 32768 x 8192, 4% on 8192 x 3000.
 int choose_plan(int64_t M, int64_t N, const void* x, const void* w, const void* y, int dtype,
                 rmsnorm_plan_t* p) {
     std::memset(p, 0, sizeof(*p));
@@ -261,6 +273,19 @@ int choose_plan(int64_t M, int64_t N, const void* x, const void* w, const void* 
         rows_per_trip = static_cast<int64_t>(p->block_threads / 64) * (64 / p->lanes_per_row) * p->row_slots;
     const int64_t need = M > 0 ? ceil_div(M, rows_per_trip) : 1;
     p->grid = need < kMaxGrid ? need : kMaxGrid;
+    p->xcd_group = 1;
+    p->max_blocks_per_cu = 0;
+    if (p->variant == RMSNORM_VARIANT_BLOCK) {
+        // about 128 KiB of consecutive rows per XCD (a power of two, at least 8 rows)
+        const int64_t row_bytes = N * 2;
+        int g = 8;
+        while (g < 64 && row_bytes * g * 3 < kXcdGroupBytes * 2) g *= 2;  // nearest power of two
+        p->xcd_group = g;
+        // about 64 KiB of rows in flight per compute unit
+        int64_t cap = kBytesInFlightPerCu / row_bytes;
+        if (cap < 2) cap = 2;
+        if (cap < kMaxThreadsPerCu / p->block_threads) p->max_blocks_per_cu = static_cast<int>(cap);
+    }
     p->prefetch = 0;
     if (p->variant != RMSNORM_VARIANT_GENERIC && p->grid < need &&
         find_kernel(p->variant, dtype, p->variant == RMSNORM_VARIANT_WAVE ? p->lanes_per_row : 0,
@@ -272,7 +297,7 @@ int choose_plan(int64_t M, int64_t N, const void* x, const void* w, const void* 
 // Workgroups of the plan's kernel the device holds at once.  cu_count > 0:
 // that many units at the register-free bound of 2048 threads per unit, host
 // only; otherwise the current device's unit count times the kernel's
-// occupancy.
+// occupancy.  Either way no more than the plan's max_blocks_per_cu per unit.
 int resident_grid(const rmsnorm_plan_t* p, const KernelEntry* k, int cu_count, int64_t* out) {
     int cu = cu_count, bpc = 0;
     if (cu > 0) {
@@ -283,12 +308,17 @@ int resident_grid(const rmsnorm_plan_t* p, const KernelEntry* k, int cu_count, i
         st = occupancy(k->func, p->block_threads, &bpc);
         if (st != RMSNORM_OK) return st;
     }
+    if (p->max_blocks_per_cu > 0 && bpc > p->max_blocks_per_cu) bpc = p->max_blocks_per_cu;
     *out = static_cast<int64_t>(cu) * bpc;
     return RMSNORM_OK;
 }
 
 int launch(const KernelEntry* k, const rmsnorm_plan_t* p, const void* x, const void* w, void* y,
-           float* rstd, int64_t M, int64_t N, float eps, float offset, void* stream) {
+           float* rstd, int64_t M, int64_t N, float eps, float offset, int lds_per_cu, void* stream) {
+    // occupancy cap: (cap + 1) workgroups of this much LDS do not fit a unit
+    size_t dyn_lds = 0;
+    if (p->max_blocks_per_cu > 0 && lds_per_cu > 0)
+        dyn_lds = static_cast<size_t>(lds_per_cu / (p->max_blocks_per_cu + 1) + 1);
     KernelArgs a;
     a.x = x;
     a.w = w;
@@ -299,9 +329,10 @@ int launch(const KernelEntry* k, const rmsnorm_plan_t* p, const void* x, const v
     a.inv_n = static_cast<float>(1.0 / static_cast<double>(N));
     a.eps = eps;
     a.offset = offset;
+    a.xcd_group = p->xcd_group;
     void* args[] = {&a};
     hipError_t e = hipLaunchKernel(k->func, dim3(static_cast<unsigned>(p->grid)),
-                                   dim3(static_cast<unsigned>(p->block_threads)), args, 0,
+                                   dim3(static_cast<unsigned>(p->block_threads)), args, dyn_lds,
                                    static_cast<hipStream_t>(stream));
     if (e != hipSuccess)
         return fail(RMSNORM_ERR_HIP, std::string("hipLaunchKernel(") + k->name + "): " + hipGetErrorString(e));
@@ -322,10 +353,10 @@ int rmsnorm_fwd(const void* x, const void* w, void* y, float* rstd, int64_t M, i
     st = choose_plan(M, N, x, w, y, dtype, &p);
     if (st == RMSNORM_OK) st = finish_plan(&p, M, N, dtype, x, w, y, &k);
     if (st != RMSNORM_OK) return st;
-    int cu = 0;
-    st = device_info(&cu);  // gfx950 check (cached per device)
+    int cu = 0, lds = 0;
+    st = device_info(&cu, &lds);  // gfx950 check, unit count and LDS (cached per device)
     if (st != RMSNORM_OK) return st;
-    return launch(k, &p, x, w, y, rstd, M, N, eps, offset, stream);
+    return launch(k, &p, x, w, y, rstd, M, N, eps, offset, lds, stream);
 }
 
 int rmsnorm_fwd_with_plan(const void* x, const void* w, void* y, float* rstd, int64_t M, int64_t N,
@@ -338,10 +369,10 @@ int rmsnorm_fwd_with_plan(const void* x, const void* w, void* y, float* rstd, in
     const KernelEntry* k = nullptr;
     st = finish_plan(&p, M, N, dtype, x, w, y, &k);
     if (st != RMSNORM_OK || M == 0) return st;
-    int cu = 0;
-    st = device_info(&cu);  // gfx950 check (cached per device)
+    int cu = 0, lds = 0;
+    st = device_info(&cu, &lds);  // gfx950 check, unit count and LDS (cached per device)
     if (st != RMSNORM_OK) return st;
-    return launch(k, &p, x, w, y, rstd, M, N, eps, offset, stream);
+    return launch(k, &p, x, w, y, rstd, M, N, eps, offset, lds, stream);
 }
 
 int rmsnorm_plan_query(int64_t M, int64_t N, int dtype, const void* x, const void* w, const void* y,

@@ -10,6 +10,7 @@ namespace rmsnorm_impl {
 // Every kernel takes exactly these arguments, in this order.
 //   x, w, y : 16-bit element buffers (device), rstd : fp32 [M] (device)
 //   M rows, N columns, inv_n = fp32(1/N), eps, offset
+//   xcd_group: consecutive workgroups' worth of rows placed on one XCD (1 = none)
 struct KernelArgs {
     const void* x;
     const void* w;
@@ -20,6 +21,7 @@ struct KernelArgs {
     float inv_n;
     float eps;
     float offset;
+    int32_t xcd_group;
 };
 
 struct KernelEntry {

@@ -120,7 +120,11 @@ def test_host_plans_cover_the_row_one_trip_per_workgroup(M, N):
         assert p.block_threads % 64 == 0 and 64 <= p.block_threads <= 1024
         groups = -(-M // p.rows_per_trip)
         assert p.grid == groups and p.trips == 1 and p.prefetch == 0
-        assert p.resident_grid == 256 * (2048 // p.block_threads)
+        per_cu = 2048 // p.block_threads
+        if p.max_blocks_per_cu:
+            per_cu = min(per_cu, p.max_blocks_per_cu)
+        assert p.resident_grid == 256 * per_cu
+        assert 1 <= p.xcd_group <= 64
 
 
 def test_planner_choices_for_the_workloads():
@@ -135,12 +139,19 @@ def test_planner_choices_for_the_workloads():
     assert (p.lanes_per_row, p.vectors_per_lane, p.row_slots) == (64, 2, 2)
     p = host_plan(32768, 8192)
     assert (p.variant, p.block_threads, p.vectors_per_lane) == (bnd.VARIANT_BLOCK, 256, 4)
+    assert (p.xcd_group, p.max_blocks_per_cu) == (8, 4)
+    assert p.resident_grid == 256 * 4
     p = host_plan(8192, 3000)
     assert (p.variant, p.block_threads, p.vectors_per_lane) == (bnd.VARIANT_BLOCK, 256, 2)
+    assert (p.xcd_group, p.max_blocks_per_cu) == (16, 0)
     p = host_plan(4096, 16384, FP16)
     assert (p.variant, p.block_threads, p.vectors_per_lane) == (bnd.VARIANT_BLOCK, 512, 4)
+    assert (p.xcd_group, p.max_blocks_per_cu) == (8, 2)
     p = host_plan(3, 49152)
-    assert (p.block_threads, p.vectors_per_lane) == (1024, 6)
+    assert (p.block_threads, p.vectors_per_lane, p.max_blocks_per_cu) == (1024, 6, 0)
+    for M, N in ((16384, 512), (262144, 128), (64, 256)):
+        p = host_plan(M, N)
+        assert (p.xcd_group, p.max_blocks_per_cu) == (1, 0)
 
 
 def test_huge_row_counts_loop_with_prefetch():
@@ -165,6 +176,12 @@ def test_plans_that_do_not_fit_are_rejected_before_launch():
         good.copy(grid=0),
         good.copy(variant=7),
         good.copy(variant=bnd.VARIANT_BLOCK, block_threads=64, vectors_per_lane=8),  # not compiled
+        good.copy(xcd_group=0),
+        good.copy(xcd_group=65),
+        good.copy(max_blocks_per_cu=1),
+        good.copy(max_blocks_per_cu=33),
+        good.copy(max_blocks_per_cu=-2),
+        good.copy(prefetch=2),
     ]
     args = (A, A + 0x1000000, A + 0x2000000, A + 0x3000000, 100, 512, 1e-6, 0.0, BF16)
     for p in bad:

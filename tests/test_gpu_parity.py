@@ -107,6 +107,42 @@ def test_every_kernel_on_workload_rows(bnd, name):
 
 
 # ---------------------------------------------------------------------------
+# 2b. Row placement on XCDs and the occupancy cap: every row is written
+#     exactly once (y starts as NaN sentinels) and correct, for window sizes
+#     that do and do not divide the grid, with one trip per workgroup and as
+#     a persistent grid.
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("name", ["rmsnorm_8192x3000_bf16_offset1", "rmsnorm_16384x512_bf16",
+                                  "rmsnorm_262144x128_fp16", "rmsnorm_4096x16384_fp16"])
+def test_xcd_group_and_occupancy_cap_cover_every_row(bnd, name):
+    wl = workloads.WORKLOADS[name]
+    M = 1237 if wl.N <= 4096 else 389
+    x, w = workloads.make_inputs(wl, seed=6, rows=M)
+    xg, wg = x.to(DEV), w.to(DEV)
+    y_ref, r_ref = parity.oracle_for(x, w, wl.eps, wl.offset, wl.dtype)
+    base = bnd.plan_query(M, wl.N, wl.dtype)
+    nan = 0x7FC0 if wl.dtype == "bf16" else 0x7E00
+    for group in (1, 2, 3, 8, 64):
+        for cap in (0, 2, 5):
+            for grid in (base.grid, 37):
+                p = base.copy(xcd_group=group, max_blocks_per_cu=cap, grid=grid,
+                              prefetch=1 if grid < base.grid and base.variant != bnd.VARIANT_GENERIC else 0)
+                announce(name, p.as_dict())
+                y = torch.full((M, wl.N), nan, dtype=torch.int32, device=DEV).to(torch.int16).view(xg.dtype)
+                r = torch.full((M,), float("nan"), dtype=torch.float32, device=DEV)
+                try:
+                    bnd.rmsnorm_fwd_out(xg, wg, y, r, wl.eps, wl.offset, plan=p)
+                except bnd.RmsnormError as e:
+                    if e.status == 8 and p.prefetch:      # prefetch instance not compiled
+                        p = p.copy(prefetch=0)
+                        bnd.rmsnorm_fwd_out(xg, wg, y, r, wl.eps, wl.offset, plan=p)
+                    else:
+                        raise
+                torch.cuda.synchronize()
+                parity.compare(y, r, y_ref, r_ref, wl.dtype, f"{name} {p.as_dict()}")
+
+
+# ---------------------------------------------------------------------------
 # 3. Sweep of widths around powers of two and tile edges.
 # ---------------------------------------------------------------------------
 SWEEP_N = [1, 2, 3, 7, 8, 9, 63, 64, 65, 127, 128, 129, 255, 256, 511, 512, 513, 1000, 1023,
