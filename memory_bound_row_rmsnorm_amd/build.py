@@ -43,7 +43,7 @@ def hipcc() -> str:
 
 def build(verbose: bool = False) -> str:
     os.makedirs(BUILD_DIR, exist_ok=True)
-    tmp = LIBRARY + ".tmp"
+    tmp = f"{LIBRARY}.{os.getpid()}.tmp"
     cmd = [hipcc(), *HIPCC_FLAGS, "-o", tmp, *SOURCES]
     if verbose:
         print(" ".join(cmd), flush=True)

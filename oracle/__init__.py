@@ -30,15 +30,16 @@ _F64P = ctypes.POINTER(ctypes.c_double)
 
 def compile_oracle(src: str, out: str, verbose: bool = False) -> str:
     """gcc, fp64, no fast-math, no FMA contraction, OpenMP over rows."""
+    tmp = f"{out}.{os.getpid()}.tmp"       # concurrent builders never share a temporary
     cmd = [
         "gcc", "-std=c11", "-O2", "-fPIC", "-shared", "-fopenmp",
         "-ffp-contract=off", "-fno-fast-math",
-        "-o", out + ".tmp", src, "-lm",
+        "-o", tmp, src, "-lm",
     ]
     if verbose:
         print(" ".join(cmd))
     subprocess.run(cmd, check=True)
-    os.replace(out + ".tmp", out)
+    os.replace(tmp, out)
     return out
 
 
