@@ -1,4 +1,4 @@
-"""Plain fp64 CPU oracle for the row RMSNorm forward (test infrastructure).
+"""Plain fp64 CPU oracle for the row RMSNorm forward and backward (test infrastructure).
 
 Only the tests, the smoke check and the benchmark's CPU-baseline leg may
 import this package.  The product path (the HIP library and its Python
@@ -78,6 +78,16 @@ class Oracle:
             ctypes.c_int, _U16P, _F64P, _F64P,
         ]
         lib.oracle_rmsnorm_fwd.restype = ctypes.c_int
+        lib.oracle_rmsnorm_fwd_f64.argtypes = [
+            _F64P, _F64P, ctypes.c_int64, ctypes.c_int64, ctypes.c_double, ctypes.c_double,
+            _F64P, _F64P,
+        ]
+        lib.oracle_rmsnorm_fwd_f64.restype = ctypes.c_int
+        lib.oracle_rmsnorm_bwd.argtypes = [
+            _U16P, _U16P, _U16P, _F64P, ctypes.c_int64, ctypes.c_int64, ctypes.c_float,
+            ctypes.c_int, _U16P, _F64P, _F64P, _F64P, _F64P,
+        ]
+        lib.oracle_rmsnorm_bwd.restype = ctypes.c_int
         lib.oracle_max_threads.argtypes = []
         lib.oracle_max_threads.restype = ctypes.c_int
         self.path = path
@@ -127,6 +137,50 @@ class Oracle:
             return y, rstd, ye
         return y, rstd
 
+    def rmsnorm_fwd_f64(self, x, w, eps: float, offset: float):
+        """fp64 forward on fp64 inputs (no codec): returns (y [M, N], rstd [M])."""
+        x = np.ascontiguousarray(x, dtype=np.float64)
+        w = np.ascontiguousarray(w, dtype=np.float64)
+        M, N = x.shape
+        y = np.empty((M, N), dtype=np.float64)
+        r = np.empty((M,), dtype=np.float64)
+        rc = self._lib.oracle_rmsnorm_fwd_f64(x.ctypes.data_as(_F64P), w.ctypes.data_as(_F64P),
+                                              M, N, eps, offset, y.ctypes.data_as(_F64P),
+                                              r.ctypes.data_as(_F64P))
+        if rc != 0:
+            raise ValueError("oracle rejected arguments")
+        return y, r
+
+    def rmsnorm_bwd(self, x_bits, w_bits, dy_bits, rstd, offset: float, dtype: str,
+                    want_exact: bool = False):
+        """Oracle backward.  x_bits, dy_bits uint16 [M, N]; w_bits uint16 [N];
+        rstd [M] (taken as given, widened to fp64).  Returns (dx_bits uint16
+        [M, N], dw float64 [N]) and, if ``want_exact``, also dx before
+        rounding, the per-element term scale of dx and the per-column term
+        scale of dw (see rmsnorm_oracle.c)."""
+        x, w, dy = _u16(x_bits), _u16(w_bits), _u16(dy_bits)
+        if x.ndim != 2 or dy.shape != x.shape or w.shape != (x.shape[1],):
+            raise ValueError(f"shape mismatch: x {x.shape}, dy {dy.shape}, w {w.shape}")
+        M, N = x.shape
+        r = np.ascontiguousarray(rstd, dtype=np.float64)
+        if r.shape != (M,):
+            raise ValueError(f"rstd must have shape [{M}]")
+        dx = np.empty((M, N), dtype=np.uint16)
+        dw = np.empty((N,), dtype=np.float64)
+        ex = np.empty((M, N), dtype=np.float64) if want_exact else None
+        sc = np.empty((M, N), dtype=np.float64) if want_exact else None
+        ws = np.empty((N,), dtype=np.float64) if want_exact else None
+        ptr = lambda a: a.ctypes.data_as(_F64P) if a is not None else None
+        rc = self._lib.oracle_rmsnorm_bwd(
+            x.ctypes.data_as(_U16P), w.ctypes.data_as(_U16P), dy.ctypes.data_as(_U16P),
+            r.ctypes.data_as(_F64P), M, N, ctypes.c_float(offset), _code(dtype),
+            dx.ctypes.data_as(_U16P), dw.ctypes.data_as(_F64P), ptr(ex), ptr(sc), ptr(ws))
+        if rc != 0:
+            raise ValueError(f"oracle rejected arguments (M={M}, N={N}, dtype={dtype})")
+        if want_exact:
+            return dx, dw, ex, sc, ws
+        return dx, dw
+
     def max_threads(self) -> int:
         """Threads the OpenMP loop uses (OMP_NUM_THREADS, else all cores)."""
         return int(self._lib.oracle_max_threads())
@@ -155,6 +209,14 @@ def encode(values, dtype: str) -> np.ndarray:
 
 def rmsnorm_fwd(x_bits, w_bits, eps: float, offset: float, dtype: str, want_exact: bool = False):
     return default().rmsnorm_fwd(x_bits, w_bits, eps, offset, dtype, want_exact)
+
+
+def rmsnorm_fwd_f64(x, w, eps: float, offset: float):
+    return default().rmsnorm_fwd_f64(x, w, eps, offset)
+
+
+def rmsnorm_bwd(x_bits, w_bits, dy_bits, rstd, offset: float, dtype: str, want_exact: bool = False):
+    return default().rmsnorm_bwd(x_bits, w_bits, dy_bits, rstd, offset, dtype, want_exact)
 
 
 def max_threads() -> int:

@@ -1,5 +1,5 @@
 /*
- * rmsnorm_oracle.c -- plain, slow, fp64 CPU oracle for the row RMSNorm forward.
+ * rmsnorm_oracle.c -- plain, slow, fp64 CPU oracle for the row RMSNorm forward and backward.
  *
  * TEST INFRASTRUCTURE ONLY.  Nothing on the product path may include, link,
  * load or call this file: only the tests, the smoke check and the CPU-baseline
@@ -25,6 +25,9 @@
  *   - "Rmsnorm Kernel Optimization", section "Key Optimizations" / "Common
  *     Pitfalls": the reduction must not run in the 16-bit input type.  Here it
  *     runs in fp64, well beyond the fp32 the GPU path uses.
+ *
+ * The backward below is derived by differentiating this forward (the pages
+ * keep rstd for a backward pass but do not print one).
  *
  * Readings taken where the pages are silent:
  *   - eps and offset arrive as fp32 (as in the listing) and are widened exactly.
@@ -177,6 +180,97 @@ int oracle_rmsnorm_fwd(const uint16_t* x, const uint16_t* w, int64_t M, int64_t 
             y[m * N + j] = oracle_encode_rne(ye, dtype);
             if (y_exact) y_exact[m * N + j] = ye;
         }
+    }
+    return 0;
+}
+
+/*
+ * Forward in fp64 on fp64 inputs, with no 16-bit codec on either side: the
+ * same formula as oracle_rmsnorm_fwd.  It exists so that the backward can be
+ * checked by finite differences of the forward on perturbed inputs.
+ *   x [M*N], w [N] fp64; y [M*N] and rstd [M] fp64 outputs.
+ */
+int oracle_rmsnorm_fwd_f64(const double* x, const double* w, int64_t M, int64_t N,
+                           double eps, double offset, double* y, double* rstd)
+{
+    if (M < 0 || N <= 0) return -1;
+    for (int64_t m = 0; m < M; ++m) {
+        const double* xr = x + m * N;
+        double ss = 0.0;
+        for (int64_t j = 0; j < N; ++j) ss += xr[j] * xr[j];
+        const double r = 1.0 / sqrt(ss / (double)N + eps);
+        rstd[m] = r;
+        for (int64_t j = 0; j < N; ++j) y[m * N + j] = xr[j] * r * (offset + w[j]);
+    }
+    return 0;
+}
+
+/*
+ * Row RMSNorm backward, fp64.  The pages store rstd for a backward pass
+ * ("Why cutile's rmsnorm required full register", kernel listing) but give
+ * no formula; this one follows from differentiating the forward.  With
+ * g_j = offset + w_j, r = rstd[m] and y_j = x_j r g_j, where
+ * r = (mean_j x_j^2 + eps)^(-1/2) so that dr/dx_k = -r^3 x_k / N:
+ *
+ *     c[m]     = (1/N) sum_j dy[m,j] g_j x[m,j]
+ *     dx[m,k]  = r (g_k dy[m,k] - r^2 c[m] x[m,k])
+ *     dw[j]    = sum_m dy[m,j] x[m,j] r[m]          (d g_j / d w_j = 1)
+ *
+ *   x, dy   [M*N] 16-bit patterns; w [N] patterns (same dtype)
+ *   rstd    [M] fp64 (the forward's rstd, given, not recomputed)
+ *   offset  fp32, as in the forward
+ *   dx      [M*N] patterns, rounded once to the dtype (nearest even)
+ *   dw      [N] fp64, unrounded
+ *   dx_exact [M*N] fp64 before rounding (may be NULL)
+ *   dx_scale [M*N] fp64 (may be NULL): |r g_k dy_k| + |r^3 x_k| (1/N) sum_j |dy_j g_j x_j|,
+ *            the size of the terms dx is computed from, for error bounds
+ *   dw_scale [N]   fp64 (may be NULL): sum_m |dy x r|, likewise
+ */
+int oracle_rmsnorm_bwd(const uint16_t* x, const uint16_t* w, const uint16_t* dy,
+                       const double* rstd, int64_t M, int64_t N, float offset, int dtype,
+                       uint16_t* dx, double* dw, double* dx_exact, double* dx_scale,
+                       double* dw_scale)
+{
+    if (M < 0 || N <= 0) return -1;
+    if (dtype != ORACLE_BF16 && dtype != ORACLE_FP16) return -1;
+    const double off = (double)offset;
+
+#pragma omp parallel for schedule(static)
+    for (int64_t m = 0; m < M; ++m) {
+        const uint16_t* xr = x + m * N;
+        const uint16_t* dyr = dy + m * N;
+        const double r = rstd[m];
+        double c = 0.0, cabs = 0.0;
+        for (int64_t j = 0; j < N; ++j) {
+            const double t = oracle_decode(dyr[j], dtype) * (off + oracle_decode(w[j], dtype)) *
+                             oracle_decode(xr[j], dtype);
+            c += t;
+            cabs += fabs(t);
+        }
+        c /= (double)N;
+        cabs /= (double)N;
+        for (int64_t k = 0; k < N; ++k) {
+            const double xk = oracle_decode(xr[k], dtype);
+            const double gk = off + oracle_decode(w[k], dtype);
+            const double dyk = oracle_decode(dyr[k], dtype);
+            const double v = r * (gk * dyk - r * r * c * xk);
+            dx[m * N + k] = oracle_encode_rne(v, dtype);
+            if (dx_exact) dx_exact[m * N + k] = v;
+            if (dx_scale) dx_scale[m * N + k] = fabs(r * gk * dyk) + fabs(r * r * r * xk) * cabs;
+        }
+    }
+
+#pragma omp parallel for schedule(static)
+    for (int64_t j = 0; j < N; ++j) {
+        double acc = 0.0, aabs = 0.0;
+        for (int64_t m = 0; m < M; ++m) {
+            const double t = oracle_decode(dy[m * N + j], dtype) * oracle_decode(x[m * N + j], dtype) *
+                             rstd[m];
+            acc += t;
+            aabs += fabs(t);
+        }
+        dw[j] = acc;
+        if (dw_scale) dw_scale[j] = aabs;
     }
     return 0;
 }

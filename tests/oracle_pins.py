@@ -15,7 +15,12 @@ the oracle disagrees with something independent of it:
     weights, power-of-two scale invariance, sign symmetry, offset equivalence,
     row independence;
   * P3's correctness expression ("Rmsnorm Kernel Optimization", Verification)
-    evaluated by torch in float64.
+    evaluated by torch in float64;
+  * for the backward (derived, not on the pages): central finite differences
+    of the fp64 forward, torch's float64 autograd of the same expression, and
+    identities of the derivative (orthogonality to x at eps = 0, oddness,
+    homogeneity and additivity in dy, closed forms for one row and for a
+    constant row).
 
 The same functions run against deliberately mutated copies of the oracle in
 ``test_oracle_mutants.py``: each plausible mistake must trip at least one pin.
@@ -458,6 +463,137 @@ def pin_torch_fp64_expression(o):
                 assert np.allclose(ye, ref, rtol=1e-13, atol=1e-300), (dtype, N, eps)
 
 
+# --------------------------------------------------------------------------
+# backward pins.  The pages keep rstd for a backward pass without printing
+# one; the oracle's backward is the derivative of its forward, so it is pinned
+# against finite differences of that forward, against torch's float64
+# autograd, and against identities of the derivative.
+# --------------------------------------------------------------------------
+def _bwd_case(o, rng, M, N, dtype, eps, offset, xscale=1.0):
+    x = o.encode(rng.normal(0, xscale, size=(M, N)), dtype)
+    w = o.encode(rng.normal(0.3, 0.5, size=N), dtype)
+    dy = o.encode(rng.normal(0, 1, size=(M, N)), dtype)
+    xd, wd, dyd = o.decode(x, dtype), o.decode(w, dtype), o.decode(dy, dtype)
+    _, r = o.rmsnorm_fwd_f64(xd, wd, fp32(eps), fp32(offset))
+    return x, w, dy, xd, wd, dyd, r
+
+
+def pin_bwd_forward_f64_matches(o):
+    """The fp64-input forward used for finite differences equals the codec forward."""
+    rng = np.random.default_rng(41)
+    for dtype in ("bf16", "fp16"):
+        x = o.encode(rng.normal(0, 2, size=(5, 33)), dtype)
+        w = o.encode(rng.normal(1, 0.1, size=33), dtype)
+        for eps, offset in ((1e-6, 0.0), (0.25, 1.0)):
+            _, r, ye = o.rmsnorm_fwd(x, w, eps, offset, dtype, want_exact=True)
+            y2, r2 = o.rmsnorm_fwd_f64(o.decode(x, dtype), o.decode(w, dtype), fp32(eps), fp32(offset))
+            assert np.array_equal(r, r2) and np.array_equal(ye, y2), (dtype, eps)
+
+
+def pin_bwd_finite_differences(o):
+    """dx and dw against central differences of L = sum(dy * y) through the fp64 forward."""
+    rng = np.random.default_rng(43)
+    for dtype in ("bf16", "fp16"):
+        for M, N, eps, offset in ((3, 7, 1e-6, 0.0), (2, 16, 0.5, 1.0), (1, 1, 1e-3, 0.0), (4, 5, 0.0, 1.0)):
+            x, w, dy, xd, wd, dyd, r = _bwd_case(o, rng, M, N, dtype, eps, offset)
+            _, dw, dxe, _, _ = o.rmsnorm_bwd(x, w, dy, r, offset, dtype, want_exact=True)
+            e, off = fp32(eps), fp32(offset)
+
+            def loss(xx, ww):
+                y, _ = o.rmsnorm_fwd_f64(xx, ww, e, off)
+                return float(np.sum(dyd * y))
+
+            fd_x = np.empty_like(xd)
+            for idx in np.ndindex(*xd.shape):
+                h = 1e-6 * max(1.0, abs(xd[idx]))
+                xp, xm = xd.copy(), xd.copy()
+                xp[idx] += h
+                xm[idx] -= h
+                fd_x[idx] = (loss(xp, wd) - loss(xm, wd)) / (2 * h)
+            fd_w = np.empty_like(wd)
+            for j in range(N):
+                h = 1e-6 * max(1.0, abs(wd[j]))
+                wp, wm = wd.copy(), wd.copy()
+                wp[j] += h
+                wm[j] -= h
+                fd_w[j] = (loss(xd, wp) - loss(xd, wm)) / (2 * h)
+            sx = np.max(np.abs(fd_x)) + 1.0
+            sw = np.max(np.abs(fd_w)) + 1.0
+            assert np.allclose(dxe, fd_x, rtol=1e-6, atol=1e-7 * sx), (dtype, M, N, np.max(np.abs(dxe - fd_x)))
+            assert np.allclose(dw, fd_w, rtol=1e-6, atol=1e-7 * sw), (dtype, M, N, np.max(np.abs(dw - fd_w)))
+
+
+def pin_bwd_torch_autograd(o):
+    """torch float64 autograd of x * rsqrt(mean(x^2) + eps) * (offset + w)."""
+    rng = np.random.default_rng(47)
+    for dtype in ("bf16", "fp16"):
+        for M, N, eps, offset in ((6, 128, 1e-6, 0.0), (3, 3000, 1e-2, 1.0), (17, 9, 0.0, 0.0)):
+            x, w, dy, xd, wd, dyd, r = _bwd_case(o, rng, M, N, dtype, eps, offset)
+            _, dw, dxe, _, _ = o.rmsnorm_bwd(x, w, dy, r, offset, dtype, want_exact=True)
+            xt = torch.tensor(xd, requires_grad=True)
+            wt = torch.tensor(wd, requires_grad=True)
+            y = xt * torch.rsqrt(xt.pow(2).mean(-1, keepdim=True) + fp32(eps)) * (fp32(offset) + wt)
+            y.backward(torch.tensor(dyd))
+            assert np.allclose(dxe, xt.grad.numpy(), rtol=1e-9, atol=1e-12 * np.max(np.abs(dxe))), (dtype, M, N)
+            assert np.allclose(dw, wt.grad.numpy(), rtol=1e-9, atol=1e-12 * np.max(np.abs(dw))), (dtype, M, N)
+
+
+def pin_bwd_identities(o):
+    """sum_k dx_k x_k = r N c eps / (ms + eps) (zero at eps = 0: the output does
+    not change along x); dx and dw are odd and homogeneous in dy: exact
+    under dy -> -dy and dy -> 2 dy; additive in dy; M = 1 gives dw = dy x r."""
+    rng = np.random.default_rng(53)
+    for dtype in ("bf16", "fp16"):
+        for eps, offset in ((0.0, 0.0), (0.3, 1.0)):
+            x, w, dy, xd, wd, dyd, r = _bwd_case(o, rng, 5, 40, dtype, eps, offset)
+            _, dw, dxe, _, _ = o.rmsnorm_bwd(x, w, dy, r, offset, dtype, want_exact=True)
+            g = fp32(offset) + wd
+            ms = np.mean(xd * xd, axis=1)
+            c = np.mean(dyd * g * xd, axis=1)
+            lhs = np.sum(dxe * xd, axis=1)
+            rhs = r * 40 * c * fp32(eps) / (ms + fp32(eps))
+            scale = np.sum(np.abs(dxe * xd), axis=1)
+            assert np.all(np.abs(lhs - rhs) <= 1e-12 * scale), (dtype, eps, lhs, rhs)
+            # dy -> -dy and dy -> 2 dy (exact in the dtype and in fp64)
+            _, dwn, dxn, _, _ = o.rmsnorm_bwd(x, w, dy ^ np.uint16(0x8000), r, offset, dtype, want_exact=True)
+            assert np.array_equal(dxn, -dxe) and np.array_equal(dwn, -dw)
+            dy2 = o.encode(2.0 * dyd, dtype)
+            assert np.array_equal(o.decode(dy2, dtype), 2.0 * dyd)
+            _, dw2, dx2, _, _ = o.rmsnorm_bwd(x, w, dy2, r, offset, dtype, want_exact=True)
+            assert np.allclose(dx2, 2.0 * dxe, rtol=1e-15, atol=0) and np.allclose(dw2, 2.0 * dw, rtol=1e-15, atol=0)
+            # additivity on small-integer gradients (sums exact in the dtype)
+            a = rng.integers(-8, 9, size=(5, 40)).astype(np.float64)
+            b = rng.integers(-8, 9, size=(5, 40)).astype(np.float64)
+            outs = [o.rmsnorm_bwd(x, w, o.encode(v, dtype), r, offset, dtype, want_exact=True) for v in (a, b, a + b)]
+            sc = outs[2][3]
+            assert np.all(np.abs(outs[0][2] + outs[1][2] - outs[2][2]) <= 1e-13 * (sc + 1e-300)), dtype
+            assert np.allclose(outs[0][1] + outs[1][1], outs[2][1], rtol=1e-13, atol=1e-13 * np.max(outs[2][4]))
+        # one row: dw_j = dy_j x_j r exactly in fp64
+        x, w, dy, xd, wd, dyd, r = _bwd_case(o, rng, 1, 64, dtype, 1e-6, 0.0)
+        _, dw = o.rmsnorm_bwd(x, w, dy, r, 0.0, dtype)
+        assert np.array_equal(dw, dyd[0] * xd[0] * r[0]), dtype
+        # zero upstream gradient
+        dx0, dw0 = o.rmsnorm_bwd(x, w, np.zeros_like(dy), r, 0.0, dtype)
+        assert np.all((dx0 & 0x7FFF) == 0) and np.all(dw0 == 0)
+
+
+def pin_bwd_constant_row(o):
+    """x = c, w = 1, offset 0, dy = 1: dx_k = r eps / (c^2 + eps) (zero at eps 0), dw_j = M c r."""
+    for dtype in ("bf16", "fp16"):
+        for c in (1.5, -3.0):
+            for eps in (0.0, 0.25):
+                N, M = 12, 3
+                x = np.tile(_bits([c], dtype), (M, N))
+                w = _bits(np.ones(N), dtype)
+                dy = _bits(np.ones((M, N)), dtype)
+                e = fp32(eps)
+                r = np.full(M, 1.0 / math.sqrt(c * c + e))
+                dx, dw, dxe, _, _ = o.rmsnorm_bwd(x, w, dy, r, 0.0, dtype, want_exact=True)
+                want = r[0] * e / (c * c + e)
+                assert np.allclose(dxe, want, rtol=1e-14, atol=1e-15), (dtype, c, eps)
+                assert np.allclose(dw, M * c * r[0], rtol=1e-15, atol=0), (dtype, c, eps)
+
+
 ALL_PINS = [
     pin_decode_all_patterns,
     pin_encode_roundtrip,
@@ -476,4 +612,9 @@ ALL_PINS = [
     pin_row_independence,
     pin_bruteforce_exact,
     pin_torch_fp64_expression,
+    pin_bwd_forward_f64_matches,
+    pin_bwd_finite_differences,
+    pin_bwd_torch_autograd,
+    pin_bwd_identities,
+    pin_bwd_constant_row,
 ]

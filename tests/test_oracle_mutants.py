@@ -1,7 +1,7 @@
 """Plant plausible mistakes in copies of the oracle; the pins must catch each.
 
-Each mutant is a text substitution in ``oracle/rmsnorm_oracle.c`` compiled into
-a temporary library on the CPU.  A pin set that lets a mutant through would
+Each mutant is a text substitution, at the first matching site, in
+``oracle/rmsnorm_oracle.c`` compiled into a temporary library on the CPU.  A pin set that lets a mutant through would
 not have caught that mistake in the real oracle either.
 """
 import os
@@ -24,8 +24,8 @@ MUTANTS = {
     "offset_ignored": [("(off + oracle_decode(w[j], dtype))", "(oracle_decode(w[j], dtype))")],
     "offset_rounded_to_dtype": [("const double off = (double)offset;",
                                  "const double off = oracle_decode(oracle_encode_rne((double)offset, dtype), dtype);")],
-    "weight_reversed": [("w[j]", "w[N - 1 - j]")],
-    "weight_indexed_by_row": [("w[j]", "w[m % N]")],
+    "weight_reversed": [("xv * r * (off + oracle_decode(w[j], dtype))", "xv * r * (off + oracle_decode(w[N - 1 - j], dtype))")],
+    "weight_indexed_by_row": [("xv * r * (off + oracle_decode(w[j], dtype))", "xv * r * (off + oracle_decode(w[m % N], dtype))")],
     "x_transposed": [("xr[j]", "x[j * M + m]")],
     "ties_away_from_zero": [("(r > 0.5 || (r == 0.5 && fmod(n, 2.0) != 0.0))", "(r >= 0.5)")],
     "truncation": [("(r > 0.5 || (r == 0.5 && fmod(n, 2.0) != 0.0))", "(0)")],
@@ -36,6 +36,23 @@ MUTANTS = {
     "encode_flushes_subnormals": [("if (ex < emin) ex = emin;", "if (ex < emin) return (uint16_t)sign;")],
     "encode_saturates_overflow": [("        bits = inf_bits;\n", "        bits = inf_bits - 1;\n")],
     "encode_drops_sign": [("const uint32_t sign = signbit(v) ? 0x8000u : 0u;", "const uint32_t sign = 0u;")],
+    # backward
+    "bwd_second_term_sign": [("const double v = r * (gk * dyk - r * r * c * xk);",
+                              "const double v = r * (gk * dyk + r * r * c * xk);")],
+    "bwd_r_not_cubed": [("const double v = r * (gk * dyk - r * r * c * xk);",
+                         "const double v = r * (gk * dyk - c * xk);")],
+    "bwd_c_without_weight": [("const double t = oracle_decode(dyr[j], dtype) * (off + oracle_decode(w[j], dtype)) *",
+                              "const double t = oracle_decode(dyr[j], dtype) * 1.0 *")],
+    "bwd_first_term_without_weight": [("const double v = r * (gk * dyk - r * r * c * xk);",
+                                       "const double v = r * (dyk - r * r * c * xk);")],
+    "bwd_divisor_padded": [("c /= (double)N;", "c /= (double)(N + 1);")],
+    "bwd_offset_ignored": [("const double gk = off + oracle_decode(w[k], dtype);",
+                            "const double gk = oracle_decode(w[k], dtype);")],
+    "bwd_dw_without_rstd": [("oracle_decode(x[m * N + j], dtype) *\n                             rstd[m];",
+                             "oracle_decode(x[m * N + j], dtype) *\n                             1.0;")],
+    "bwd_dw_times_weight": [("oracle_decode(x[m * N + j], dtype) *\n                             rstd[m];",
+                             "oracle_decode(x[m * N + j], dtype) *\n                             rstd[m] * (off + oracle_decode(w[j], dtype));")],
+    "bwd_dw_wrong_row_stride": [("oracle_decode(dy[m * N + j], dtype)", "oracle_decode(dy[m + j * M], dtype)")],
 }
 
 
@@ -50,7 +67,8 @@ def test_mutant_is_caught(name, source, tmp_path):
     text = source
     for old, new in MUTANTS[name]:
         assert text.count(old) >= 1, f"mutation site for {name} not found: {old!r}"
-        text = text.replace(old, new)
+        text = text.replace(old, new, 1)     # the first site: the forward precedes the backward
+    assert text != source, f"mutant {name} changes nothing"
     src = os.path.join(tmp_path, f"mutant_{name}.c")
     with open(src, "w") as f:
         f.write(text)
