@@ -23,7 +23,6 @@ Prints one JSON line on stdout.
 from __future__ import annotations
 
 import argparse
-import glob
 import hashlib
 import json
 import math
@@ -45,17 +44,27 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
+# the forward kernels' own sources: a change to any of them voids stored counters
+FORWARD_SOURCES = ("rmsnorm_kernels.hip", "rmsnorm_device.hpp", "rmsnorm_internal.hpp")
+
+
 def kernel_source_sha256() -> str:
     h = hashlib.sha256()
-    for p in sorted(glob.glob(os.path.join(ROOT, "memory_bound_row_rmsnorm_amd", "csrc", "*"))):
-        with open(p, "rb") as f:
-            h.update(os.path.basename(p).encode() + b"\0" + f.read())
+    for name in FORWARD_SOURCES:
+        with open(os.path.join(ROOT, "memory_bound_row_rmsnorm_amd", "csrc", name), "rb") as f:
+            h.update(name.encode() + b"\0" + f.read())
     return h.hexdigest()
 
 
-def measured_traffic(workload: str):
+def plan_key(plan_dict: dict) -> dict:
+    """The launch a plan makes (kernel instance, shape, grid), without the
+    device-dependent resident_grid."""
+    return {k: v for k, v in plan_dict.items() if k != "resident_grid"}
+
+
+def measured_traffic(workload: str, plan_dict: dict):
     """HBM bytes per launch from the committed counter summary, if it was taken
-    on the current kernel sources; else None."""
+    on the current forward kernel sources and the same launch plan; else None."""
     path = os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
     if not os.path.exists(path):
         return None
@@ -63,6 +72,9 @@ def measured_traffic(workload: str):
         t = json.load(f)
     if t.get("kernel_source_sha256") != kernel_source_sha256():
         log(f"traffic: {path} was taken on other kernel sources; reporting null")
+        return None
+    if t.get("plan") != plan_key(plan_dict):
+        log(f"traffic: {path} was taken with another launch plan; reporting null")
         return None
     return t.get("traffic_bytes_per_launch")
 
@@ -102,9 +114,13 @@ def traffic_from_counters(wl, name: str, directory: str) -> dict:
     write_b = rms_write * 1024 * write_scale
     alg_read = wl.M * wl.N * wl.elem_bytes + wl.N * wl.elem_bytes
     alg_write = wl.M * wl.N * wl.elem_bytes + 4 * wl.M
+    from memory_bound_row_rmsnorm_amd import binding
+
+    plan = binding.plan_query(wl.M, wl.N, wl.dtype)      # the plan the counted run used (default pointers align)
     return {
         "workload": name,
         "kernel_source_sha256": kernel_source_sha256(),
+        "plan": plan_key(plan.as_dict()),
         "counters_kib_per_dispatch": {"rmsnorm_FETCH_SIZE": rms_fetch, "rmsnorm_WRITE_SIZE": rms_write,
                                       "copy_FETCH_SIZE": copy_fetch, "copy_WRITE_SIZE": copy_write},
         "copy_bytes_each_way": copy_bytes,
@@ -144,6 +160,126 @@ def cpu_baseline(wl, x_cpu, w_cpu, seconds: float):
     }
 
 
+def bwd_algorithmic_bytes(wl) -> int:
+    """x and dy read once, dx written once, w read once, rstd read once, fp32 dw written once."""
+    s = wl.elem_bytes
+    return 3 * wl.M * wl.N * s + wl.N * s + 4 * wl.M + 4 * wl.N
+
+
+def bench_backward(args, wl, name, dev) -> int:
+    import torch
+
+    from memory_bound_row_rmsnorm_amd import binding, workloads
+
+    read_bytes = 2 * wl.M * wl.N * wl.elem_bytes
+    sets = args.sets or max(2, min(256, math.ceil(ROTATION_X_BYTES / read_bytes)))
+    log(f"backward {name}: M={wl.M} N={wl.N} {wl.dtype}, {sets} rotation sets")
+    xs, dys, dxs, rs = [], [], [], []
+    x0 = w0 = dy0 = None
+    for k in range(sets):
+        x, w = workloads.make_inputs(wl, seed=k)
+        dy = workloads.make_grad(wl, seed=k)
+        if k == 0:
+            x0, w0, dy0 = x, w, dy
+        xs.append(x.to(dev))
+        dys.append(dy.to(dev))
+        dxs.append(torch.empty_like(xs[-1]))
+    w_dev = w0.to(dev)
+    for k in range(sets):           # rstd of each batch from the forward (input data only)
+        _, r = binding.rmsnorm_fwd(xs[k], w_dev, wl.eps, wl.offset)
+        rs.append(r)
+    dw = torch.empty(wl.N, dtype=torch.float32, device=dev)
+    plan = binding.bwd_plan_query(wl.M, wl.N, wl.dtype, xs[0].data_ptr(), dys[0].data_ptr(), dxs[0].data_ptr())
+    if args.plan:
+        plan = plan.copy(**json.loads(args.plan))
+    ws_bytes = plan.grid * wl.N * 4
+    ws = torch.empty(ws_bytes // 4 + 4, dtype=torch.float32, device=dev)
+    log("bwd plan", plan.as_dict(), f"workspace {ws_bytes} bytes")
+    lib = binding.lib
+    pplan = binding.ctypes.byref(plan)
+    code = binding.DTYPE_NAMES[wl.dtype]
+
+    def launch(i, h):
+        k = i % sets
+        st = lib.rmsnorm_bwd_with_plan(xs[k].data_ptr(), w_dev.data_ptr(), dys[k].data_ptr(), rs[k].data_ptr(),
+                                       dxs[k].data_ptr(), dw.data_ptr(), wl.M, wl.N, wl.offset, code, pplan,
+                                       ws.data_ptr(), ws.numel() * 4, h)
+        if st != 0:
+            raise binding.RmsnormError(st, lib.rmsnorm_last_error().decode())
+
+    stream = torch.cuda.current_stream()
+    for i in range(args.warmup):
+        launch(i, stream.cuda_stream or None)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    cap = torch.cuda.Stream()
+    cap.wait_stream(stream)
+    with torch.cuda.graph(graph, stream=cap):
+        hc = torch.cuda.current_stream().cuda_stream
+        for i in range(args.steps):
+            launch(i, hc)
+    torch.cuda.synchronize()
+    graph.replay()
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    start.record()
+    graph.replay()
+    end.record()
+    end.synchronize()
+    ms_per_step = start.elapsed_time(end) / args.steps
+    nbytes = bwd_algorithmic_bytes(wl)
+    gbps = nbytes / (ms_per_step * 1e-3) / 1e9
+    out = {
+        "metric": f"achieved HBM GB/s and % of MI355X peak, RMSNorm bwd {wl.M}x{wl.N} {wl.dtype}",
+        "value": round(gbps, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": wl.dtype,
+        "data": "synthetic",
+        "config": {
+            "workload": name,
+            "pass": "bwd",
+            "M": wl.M,
+            "N": wl.N,
+            "offset": wl.offset,
+            "algorithmic_bytes_per_step": nbytes,
+            "workspace_bytes": ws_bytes,
+            "workspace_traffic_bytes_per_step": 2 * ws_bytes,
+            "rotation_sets": sets,
+            "launch": "graph",
+            "plan": plan.as_dict(),
+            "pct_of_peak": round(100 * gbps / PEAK_GBPS, 2),
+        },
+        "roofline": {"bound": "hbm", "achieved": round(gbps, 2), "peak": PEAK_GBPS, "unit": "GB/s",
+                     "frac": round(gbps / PEAK_GBPS, 4), "traffic": None},
+    }
+    if not args.no_cpu_baseline:
+        import oracle
+
+        o = oracle.default()
+        xb, wb, db = (workloads.to_bits(t) for t in (x0, w0, dy0))
+        _, r64 = o.rmsnorm_fwd(xb, wb, wl.eps, wl.offset, wl.dtype)
+        reps, t0 = 0, time.perf_counter()
+        while True:
+            o.rmsnorm_bwd(xb, wb, db, r64, wl.offset, wl.dtype)
+            reps += 1
+            dt = time.perf_counter() - t0
+            if dt >= args.cpu_seconds:
+                break
+        out["cpu_baseline"] = {"value": round(reps * nbytes / dt / 1e9, 3), "unit": "GB/s",
+                               "cores": o.max_threads(), "kind": "oracle",
+                               "sample": f"{reps} full passes of the fp64 oracle backward over one batch ({dt:.1f} s)"}
+    print(json.dumps(out), flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -158,6 +294,8 @@ def main() -> int:
     ap.add_argument("--traffic-from", default=None, metavar="DIR",
                     help="write profiles/traffic_<workload>.json from rocprofv3 counter CSVs in DIR "
                          "and exit (no GPU needed)")
+    ap.add_argument("--pass", dest="direction", choices=["fwd", "bwd"], default="fwd",
+                    help="bwd: time the backward (row pass + dw column pass) instead")
     ap.add_argument("--kernel", choices=["rmsnorm", "copy"], default="rmsnorm",
                     help="copy: time a plain device copy of x into y instead (same rotation, "
                          "2*M*N*s bytes per step), the practical ceiling and the counter "
@@ -189,6 +327,8 @@ def main() -> int:
     wl = workloads.WORKLOADS[name]
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.direction == "bwd":
+        return bench_backward(args, wl, name, dev)
     per_set = 2 * wl.M * wl.N * 2 + 4 * wl.M
     x_bytes = wl.M * wl.N * 2
     sets = args.sets or max(2, min(256, math.ceil(ROTATION_X_BYTES / x_bytes)))
@@ -271,7 +411,7 @@ def main() -> int:
     nbytes = wl.algorithmic_bytes() if args.kernel == "rmsnorm" else 2 * wl.M * wl.N * wl.elem_bytes
     gbps = nbytes / (ms_per_step * 1e-3) / 1e9
 
-    traffic = measured_traffic(name) if args.kernel == "rmsnorm" else None
+    traffic = measured_traffic(name, plan.as_dict()) if args.kernel == "rmsnorm" else None
     out = {
         "metric": METRIC,
         "value": round(gbps, 2),

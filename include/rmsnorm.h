@@ -175,6 +175,65 @@ int rmsnorm_plan_resources(const rmsnorm_plan_t* plan, int dtype,
                            int32_t* vgprs, int32_t* sgprs, int32_t* lds_bytes,
                            int32_t* scratch);
 
+/*
+ * ---------------------------------------------------------------------------
+ * Backward.  The pages store rstd "for backward" ("Why cutile's rmsnorm
+ * required full register", kernel listing) but give no formula; this one is
+ * the derivative of the forward above.  With g_j = offset + w_j and
+ * r = rstd[m] (the forward's output, taken as given):
+ *
+ *     c[m]    = (1/N) sum_j dy[m,j] g_j x[m,j]
+ *     dx[m,k] = r (g_k dy[m,k] - r^2 c[m] x[m,k])
+ *     dw[j]   = sum_m dy[m,j] x[m,j] r[m]
+ *
+ * fp32 arithmetic; x, w, dy, dx of `dtype`; rstd and dw fp32.
+ *
+ * Two passes on `stream`: a row pass over a grid of `plan.grid` workgroups
+ * writes dx and one fp32 partial row of dw per workgroup into `workspace`,
+ * then a column pass adds the partial rows in a fixed order into dw (so dw is
+ * the same on every run).  The workspace is caller-owned device memory of at
+ * least plan.grid * N * 4 bytes; its contents on entry do not matter and on
+ * return are unspecified.
+ * ---------------------------------------------------------------------------
+ */
+
+/*
+ * Plan of the backward row pass (variant, lanes, vectors, slots, block
+ * threads, grid as for the forward; grid is the number of partial rows).
+ * x, dy, dx only inform the alignment check.  cu_count as for
+ * rmsnorm_plan_query.  Host only unless cu_count <= 0.
+ */
+int rmsnorm_bwd_plan_query(int64_t M, int64_t N, int dtype, const void* x, const void* dy,
+                           const void* dx, int32_t cu_count, rmsnorm_plan_t* out);
+
+/* Workspace bytes rmsnorm_bwd needs for these sizes and pointers (host only). */
+int rmsnorm_bwd_workspace_size(int64_t M, int64_t N, int dtype, const void* x, const void* dy,
+                               const void* dx, int64_t* bytes);
+
+/*
+ * Row RMSNorm backward.
+ *   x, dy   [M, N] dtype, device      w  [N] dtype, device
+ *   rstd    [M] fp32, device (from rmsnorm_fwd)
+ *   dx      [M, N] dtype, device; may be exactly dy (in place), no other overlap
+ *   dw      [N] fp32, device (written, not accumulated into)
+ *   offset  finite (as in the forward)
+ *   workspace, workspace_bytes: see above (RMSNORM_ERR_SHAPE if too small)
+ * M == 0 writes dw = 0.  Argument errors return before any HIP call.
+ */
+int rmsnorm_bwd(const void* x, const void* w, const void* dy, const float* rstd, void* dx,
+                float* dw, int64_t M, int64_t N, float offset, int dtype, void* workspace,
+                int64_t workspace_bytes, void* stream);
+
+/* rmsnorm_bwd with an explicit row-pass plan (honoured fields as in
+ * rmsnorm_fwd_with_plan, except xcd_group and max_blocks_per_cu, which must
+ * be 1 and 0; prefetch 1 exists for the wave and block shapes that fit the
+ * register budget with it, RMSNORM_ERR_PLAN otherwise).  The workspace must
+ * hold plan.grid * N * 4 bytes. */
+int rmsnorm_bwd_with_plan(const void* x, const void* w, const void* dy, const float* rstd,
+                          void* dx, float* dw, int64_t M, int64_t N, float offset, int dtype,
+                          const rmsnorm_plan_t* plan, void* workspace, int64_t workspace_bytes,
+                          void* stream);
+
 /* Static name of a status code ("RMSNORM_OK", ...); never NULL. */
 const char* rmsnorm_status_string(int status);
 

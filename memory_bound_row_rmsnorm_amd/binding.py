@@ -31,6 +31,7 @@ STATUS = {
 # Every symbol include/rmsnorm.h declares.
 EXPORTED = (
     "rmsnorm_fwd", "rmsnorm_fwd_with_plan", "rmsnorm_plan_query", "rmsnorm_plan_resources",
+    "rmsnorm_bwd", "rmsnorm_bwd_with_plan", "rmsnorm_bwd_plan_query", "rmsnorm_bwd_workspace_size",
     "rmsnorm_status_string", "rmsnorm_last_error", "rmsnorm_version",
 )
 
@@ -90,6 +91,15 @@ def _load():
     i32p = ctypes.POINTER(ctypes.c_int32)
     lib.rmsnorm_plan_resources.argtypes = [ctypes.POINTER(Plan), i32, i32p, i32p, i32p, i32p]
     lib.rmsnorm_plan_resources.restype = i32
+    lib.rmsnorm_bwd.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, f32, i32, vp, i64, vp]
+    lib.rmsnorm_bwd.restype = i32
+    lib.rmsnorm_bwd_with_plan.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, f32, i32,
+                                          ctypes.POINTER(Plan), vp, i64, vp]
+    lib.rmsnorm_bwd_with_plan.restype = i32
+    lib.rmsnorm_bwd_plan_query.argtypes = [i64, i64, i32, vp, vp, vp, ctypes.c_int32, ctypes.POINTER(Plan)]
+    lib.rmsnorm_bwd_plan_query.restype = i32
+    lib.rmsnorm_bwd_workspace_size.argtypes = [i64, i64, i32, vp, vp, vp, ctypes.POINTER(ctypes.c_int64)]
+    lib.rmsnorm_bwd_workspace_size.restype = i32
     lib.rmsnorm_status_string.argtypes = [i32]
     lib.rmsnorm_status_string.restype = ctypes.c_char_p
     lib.rmsnorm_last_error.argtypes = []
@@ -199,3 +209,69 @@ def plan_resources(plan: Plan, dtype) -> dict:
 
 def version() -> int:
     return lib.rmsnorm_version()
+
+
+# ---------------------------------------------------------------------------
+# Backward
+# ---------------------------------------------------------------------------
+def bwd_plan_query(M: int, N: int, dtype, x_ptr: int = 0, dy_ptr: int = 0, dx_ptr: int = 0,
+                   cu_count: int = 0) -> Plan:
+    """The row-pass plan rmsnorm_bwd uses (grid = number of dw partial rows)."""
+    p = Plan()
+    _check(lib.rmsnorm_bwd_plan_query(M, N, _dtype_code(dtype), x_ptr or None, dy_ptr or None,
+                                      dx_ptr or None, cu_count, ctypes.byref(p)))
+    return p
+
+
+def bwd_workspace_size(M: int, N: int, dtype, x_ptr: int = 0, dy_ptr: int = 0, dx_ptr: int = 0) -> int:
+    b = ctypes.c_int64()
+    _check(lib.rmsnorm_bwd_workspace_size(M, N, _dtype_code(dtype), x_ptr or None, dy_ptr or None,
+                                          dx_ptr or None, ctypes.byref(b)))
+    return b.value
+
+
+def rmsnorm_bwd_out(x: torch.Tensor, w: torch.Tensor, dy: torch.Tensor, rstd: torch.Tensor,
+                    dx: torch.Tensor, dw: torch.Tensor, workspace: torch.Tensor, offset: float = 0.0,
+                    plan: Plan | None = None, stream=None) -> None:
+    """Write dx (x's dtype) and dw (fp32 [N]); workspace is any device tensor
+    of at least the required bytes.  Enqueue only."""
+    _check_tensors(x, w)
+    M, N = x.shape
+    for name, t in (("dy", dy), ("dx", dx)):
+        if t.shape != x.shape or t.dtype != x.dtype or not t.is_contiguous() or t.device != x.device:
+            raise ValueError(f"{name} must be a contiguous tensor like x")
+    if rstd.shape != (M,) or rstd.dtype != torch.float32 or not rstd.is_contiguous() or rstd.device != x.device:
+        raise ValueError(f"rstd must be a contiguous float32 tensor of shape [{M}] on {x.device}")
+    if dw.shape != (N,) or dw.dtype != torch.float32 or not dw.is_contiguous() or dw.device != x.device:
+        raise ValueError(f"dw must be a contiguous float32 tensor of shape [{N}] on {x.device}")
+    if not workspace.is_contiguous() or workspace.device != x.device:
+        raise ValueError("workspace must be a contiguous tensor on x's device")
+    ws_bytes = workspace.numel() * workspace.element_size()
+    args = (x.data_ptr(), w.data_ptr(), dy.data_ptr(), rstd.data_ptr(), dx.data_ptr(), dw.data_ptr(),
+            M, N, offset, DTYPE_CODES[x.dtype])
+    with torch.cuda.device(x.device):
+        h = _stream_handle(stream)
+        if plan is None:
+            _check(lib.rmsnorm_bwd(*args, workspace.data_ptr() or None, ws_bytes, h))
+        else:
+            _check(lib.rmsnorm_bwd_with_plan(*args, ctypes.byref(plan), workspace.data_ptr() or None,
+                                             ws_bytes, h))
+
+
+def rmsnorm_bwd(x: torch.Tensor, w: torch.Tensor, dy: torch.Tensor, rstd: torch.Tensor,
+                offset: float = 0.0, plan: Plan | None = None, stream=None):
+    """Gradients of y = x * rstd * (offset + w) given dy and the forward's rstd.
+
+    Returns (dx of x's dtype, dw float32 [N]).
+    """
+    _check_tensors(x, w)
+    M, N = x.shape
+    dx = torch.empty_like(x)
+    dw = torch.empty((N,), dtype=torch.float32, device=x.device)
+    if plan is None:
+        nbytes = bwd_workspace_size(M, N, x.dtype, x.data_ptr(), dy.data_ptr(), dx.data_ptr())
+    else:
+        nbytes = plan.grid * N * 4 if M > 0 else 0
+    ws = torch.empty((max(nbytes, 16) + 3) // 4, dtype=torch.float32, device=x.device)
+    rmsnorm_bwd_out(x, w, dy, rstd, dx, dw, ws, offset, plan, stream)
+    return dx, dw

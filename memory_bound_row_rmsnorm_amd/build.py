@@ -19,7 +19,8 @@ LIBRARY = os.path.join(HERE, "librmsnorm_mi355x.so")
 BUILD_DIR = os.path.join(HERE, "_build")
 RESOURCES = os.path.join(BUILD_DIR, "kernel_resources.txt")
 
-SOURCES = [os.path.join(CSRC, "rmsnorm_kernels.hip"), os.path.join(CSRC, "rmsnorm_api.cpp")]
+SOURCES = [os.path.join(CSRC, "rmsnorm_kernels.hip"), os.path.join(CSRC, "rmsnorm_bwd_kernels.hip"),
+           os.path.join(CSRC, "rmsnorm_api.cpp")]
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950",

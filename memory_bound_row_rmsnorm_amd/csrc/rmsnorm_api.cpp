@@ -10,6 +10,7 @@
 // "Why cutile's rmsnorm required full register").
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdio>
 #include <cstring>
@@ -21,6 +22,7 @@
 #include "../../include/rmsnorm.h"
 #include "rmsnorm_internal.hpp"
 
+using rmsnorm_impl::BwdArgs;
 using rmsnorm_impl::KernelArgs;
 using rmsnorm_impl::KernelEntry;
 
@@ -339,6 +341,237 @@ int launch(const KernelEntry* k, const rmsnorm_plan_t* p, const void* x, const v
     return RMSNORM_OK;
 }
 
+
+// ---------------------------------------------------------------------------
+// Backward: argument checks, planning, launch.
+// ---------------------------------------------------------------------------
+constexpr int64_t kBwdMaxVectorN = 1024LL * 2 * 8;   // widest row of the 16-byte backward kernels
+constexpr int kBwdWaveThreads = 1024;                // 16 waves share one LDS reduction of dw
+constexpr int64_t kBwdMaxLds = 64 * 1024;
+constexpr int64_t kBwdPlanCus = 256;                 // compute units the backward plan assumes
+constexpr int64_t kBwdPlanWaves = kBwdPlanCus * 16;  // row-pass waves aimed for: 16 per unit
+constexpr int64_t kBwdPartialsGeneric = 1024;        // row-pass grid cap of the generic family
+constexpr int kBwdWaveSlots[] = {4, 2, 1};
+
+const KernelEntry* find_bwd_kernel(int variant, int dtype, int lanes, int vpl, int slots, bool prefetch) {
+    int n = 0;
+    const KernelEntry* t = rmsnorm_impl::bwd_kernel_table(&n);
+    for (int i = 0; i < n; ++i) {
+        const KernelEntry& k = t[i];
+        if (k.variant != variant || k.dtype != dtype || k.prefetch != prefetch) continue;
+        if (variant == RMSNORM_VARIANT_WAVE &&
+            (k.lanes_per_row != lanes || k.vectors_per_lane != vpl || k.row_slots != slots))
+            continue;
+        if (variant == RMSNORM_VARIANT_BLOCK && k.vectors_per_lane != vpl) continue;
+        return &k;
+    }
+    return nullptr;
+}
+
+int64_t bwd_wave_lds(const rmsnorm_plan_t* p, int64_t N) {
+    return static_cast<int64_t>(p->block_threads / 64) * (64 / p->lanes_per_row) * N * 4;
+}
+
+int check_bwd_args(const void* x, const void* w, const void* dy, const float* rstd, const void* dx,
+                   const float* dw, int64_t M, int64_t N, float offset, int dtype) {
+    int st = check_shape_dtype(M, N, dtype);
+    if (st != RMSNORM_OK) return st;
+    if (!dw) return fail(RMSNORM_ERR_NULL, "dw must be non-NULL");
+    if (M > 0 && (!x || !w || !dy || !rstd || !dx))
+        return fail(RMSNORM_ERR_NULL, "x, w, dy, rstd and dx must be non-NULL");
+    if (!std::isfinite(offset)) return fail(RMSNORM_ERR_SCALAR, "offset must be finite");
+    const int64_t xb = M * N * 2, wb = N * 2, rb = M * 4, db = N * 4;
+    if (M > 0) {
+        if (ranges_overlap(dx, xb, x, xb)) return fail(RMSNORM_ERR_OVERLAP, "dx overlaps x");
+        if (dx != dy && ranges_overlap(dx, xb, dy, xb)) return fail(RMSNORM_ERR_OVERLAP, "dx partially overlaps dy");
+        if (ranges_overlap(dx, xb, w, wb) || ranges_overlap(dx, xb, rstd, rb) || ranges_overlap(dx, xb, dw, db))
+            return fail(RMSNORM_ERR_OVERLAP, "dx overlaps w, rstd or dw");
+        if (ranges_overlap(dw, db, x, xb) || ranges_overlap(dw, db, dy, xb) || ranges_overlap(dw, db, w, wb) ||
+            ranges_overlap(dw, db, rstd, rb))
+            return fail(RMSNORM_ERR_OVERLAP, "dw overlaps an input");
+    }
+    return RMSNORM_OK;
+}
+
+int check_workspace(const void* ws, int64_t ws_bytes, int64_t need, const void* x, const void* w,
+                    const void* dy, const float* rstd, const void* dx, const float* dw, int64_t M, int64_t N) {
+    if (need == 0) return RMSNORM_OK;
+    if (!ws) return fail(RMSNORM_ERR_NULL, "workspace must be non-NULL");
+    if (ws_bytes < need)
+        return fail(RMSNORM_ERR_SHAPE, "workspace holds " + std::to_string(ws_bytes) + " bytes, plan needs " +
+                                           std::to_string(need));
+    if ((reinterpret_cast<uintptr_t>(ws) & 15u) != 0) return fail(RMSNORM_ERR_PLAN, "workspace must be 16-byte aligned");
+    const int64_t xb = M * N * 2;
+    if (ranges_overlap(ws, need, x, xb) || ranges_overlap(ws, need, dy, xb) || ranges_overlap(ws, need, dx, xb) ||
+        ranges_overlap(ws, need, w, N * 2) || ranges_overlap(ws, need, rstd, M * 4) ||
+        ranges_overlap(ws, need, dw, N * 4))
+        return fail(RMSNORM_ERR_OVERLAP, "workspace overlaps an argument");
+    return RMSNORM_OK;
+}
+
+int finish_bwd_plan(rmsnorm_plan_t* p, int64_t M, int64_t N, int dtype, const void* x, const void* w,
+                    const void* dy, const void* dx, const KernelEntry** kernel) {
+    if (p->block_threads < 64 || p->block_threads > 1024 || p->block_threads % 64 != 0)
+        return fail(RMSNORM_ERR_PLAN, "block_threads must be a multiple of 64 in [64, 1024]");
+    if (p->grid < 1 || p->grid > 0x7FFFFFFF) return fail(RMSNORM_ERR_PLAN, "grid must be in [1, 2^31)");
+    if (p->prefetch != 0 && p->prefetch != 1) return fail(RMSNORM_ERR_PLAN, "prefetch must be 0 or 1");
+    if (p->xcd_group != 1 || p->max_blocks_per_cu != 0)
+        return fail(RMSNORM_ERR_PLAN, "backward plans take xcd_group 1 and max_blocks_per_cu 0");
+    const bool pf = p->prefetch != 0;
+    const KernelEntry* k = nullptr;
+    if (p->variant == RMSNORM_VARIANT_GENERIC) {
+        p->vec_elems = 1;
+        p->lanes_per_row = p->block_threads;
+        p->vectors_per_lane = 0;
+        p->row_slots = 1;
+        p->rows_per_trip = 1;
+        k = pf ? nullptr : find_bwd_kernel(RMSNORM_VARIANT_GENERIC, dtype, 0, 0, 1, false);
+    } else if (p->variant == RMSNORM_VARIANT_WAVE || p->variant == RMSNORM_VARIANT_BLOCK) {
+        if (N % 8 != 0) return fail(RMSNORM_ERR_PLAN, "16-byte kernels need N % 8 == 0");
+        if (!aligned16(x) || !aligned16(w) || !aligned16(dy) || !aligned16(dx))
+            return fail(RMSNORM_ERR_PLAN, "16-byte kernels need 16-byte aligned x, w, dy and dx");
+        p->vec_elems = 8;
+        if (p->variant == RMSNORM_VARIANT_WAVE) {
+            k = find_bwd_kernel(RMSNORM_VARIANT_WAVE, dtype, p->lanes_per_row, p->vectors_per_lane, p->row_slots, pf);
+            if (k) {
+                if (static_cast<int64_t>(p->lanes_per_row) * p->vectors_per_lane * 8 < N)
+                    return fail(RMSNORM_ERR_PLAN, "wave plan does not cover N");
+                if (bwd_wave_lds(p, N) > kBwdMaxLds)
+                    return fail(RMSNORM_ERR_PLAN, "wave plan needs more than 64 KiB of LDS for dw partials");
+                p->rows_per_trip = static_cast<int64_t>(p->block_threads / 64) * (64 / p->lanes_per_row) * p->row_slots;
+            }
+        } else {
+            p->row_slots = 1;
+            p->lanes_per_row = p->block_threads;
+            k = find_bwd_kernel(RMSNORM_VARIANT_BLOCK, dtype, 0, p->vectors_per_lane, 1, pf);
+            if (k) {
+                if (static_cast<int64_t>(p->block_threads) * p->vectors_per_lane * 8 < N)
+                    return fail(RMSNORM_ERR_PLAN, "block plan does not cover N");
+                p->rows_per_trip = 1;
+            }
+        }
+    } else {
+        return fail(RMSNORM_ERR_PLAN, "unknown variant");
+    }
+    if (!k) return fail(RMSNORM_ERR_PLAN, "no compiled backward kernel for this plan");
+    p->trips = M > 0 ? ceil_div(ceil_div(M, p->rows_per_trip), p->grid) : 0;
+    if (kernel) *kernel = k;
+    return RMSNORM_OK;
+}
+
+// Backward plan: the forward's families and widths and a persistent row
+// pass.  Its grid G, the number of dw partial rows, is the smallest of: the
+// rows' trips (one trip per workgroup), enough workgroups for 16 waves on
+// each of 256 compute units, and 3M/32, which keeps the workspace's write
+// and read within 1/8 of the row pass's 6MN bytes.  The next trip is loaded
+// ahead when a workgroup makes more than one and the grid leaves at most one
+// workgroup per unit: its barriers then stall the whole unit, which the early
+// loads cover; with two or more workgroups per unit they cover each other,
+// and the extra registers of the prefetching form cost more than they hide.
+int choose_bwd_plan(int64_t M, int64_t N, const void* x, const void* w, const void* dy, const void* dx,
+                    int dtype, rmsnorm_plan_t* p) {
+    std::memset(p, 0, sizeof(*p));
+    p->xcd_group = 1;
+    const bool vec_ok = (N % 8 == 0) && aligned16(x) && aligned16(w) && aligned16(dy) && aligned16(dx) &&
+                        N <= kBwdMaxVectorN;
+    if (!vec_ok) {
+        p->variant = RMSNORM_VARIANT_GENERIC;
+        p->block_threads = N >= 1024 ? 256 : (N >= 256 ? 128 : 64);
+        p->row_slots = 1;
+    } else if (N / 8 <= 128) {
+        const int64_t nvec = N / 8;
+        p->variant = RMSNORM_VARIANT_WAVE;
+        p->block_threads = kBwdWaveThreads;
+        p->lanes_per_row = nvec <= 16 ? 16 : (nvec <= 32 ? 32 : 64);
+        p->vectors_per_lane = static_cast<int>(ceil_div(nvec, p->lanes_per_row));
+        const int64_t per_slot = N * 2 * (64 / p->lanes_per_row);
+        p->row_slots = 1;
+        for (int sl : kBwdWaveSlots) {
+            if (sl * per_slot <= kWaveBytesInFlight &&
+                find_bwd_kernel(RMSNORM_VARIANT_WAVE, dtype, p->lanes_per_row, p->vectors_per_lane, sl, false)) {
+                p->row_slots = sl;
+                break;
+            }
+        }
+    } else {
+        const int64_t nvec = N / 8;
+        p->variant = RMSNORM_VARIANT_BLOCK;
+        p->row_slots = 1;
+        p->block_threads = nvec <= 512 ? 256 : (nvec <= 1024 ? 512 : 1024);
+        p->vectors_per_lane = static_cast<int>(ceil_div(nvec, p->block_threads));
+    }
+    int64_t rows_per_trip = 1;
+    if (p->variant == RMSNORM_VARIANT_WAVE)
+        rows_per_trip = static_cast<int64_t>(p->block_threads / 64) * (64 / p->lanes_per_row) * p->row_slots;
+    const int64_t need = M > 0 ? ceil_div(M, rows_per_trip) : 1;
+    int64_t cap = kBwdPartialsGeneric;
+    if (p->variant != RMSNORM_VARIANT_GENERIC) {
+        cap = kBwdPlanWaves / (p->block_threads / 64);
+        const int64_t traffic_cap = std::max<int64_t>(3 * M / 32, 1);
+        cap = std::min(cap, traffic_cap);
+    }
+    p->grid = std::min(need, cap);
+    const bool ahead = need > p->grid && p->grid <= kBwdPlanCus;
+    if (ahead && p->variant == RMSNORM_VARIANT_WAVE &&
+        find_bwd_kernel(RMSNORM_VARIANT_WAVE, dtype, p->lanes_per_row, p->vectors_per_lane, p->row_slots, true))
+        p->prefetch = 1;
+    if (ahead && p->variant == RMSNORM_VARIANT_BLOCK &&
+        find_bwd_kernel(RMSNORM_VARIANT_BLOCK, dtype, 0, p->vectors_per_lane, 1, true))
+        p->prefetch = 1;
+    return RMSNORM_OK;
+}
+
+int launch_bwd(const KernelEntry* k, const rmsnorm_plan_t* p, const void* x, const void* w, const void* dy,
+               const float* rstd, void* dx, float* dw, int64_t M, int64_t N, float offset, void* workspace,
+               void* stream) {
+    const hipStream_t s = static_cast<hipStream_t>(stream);
+    int64_t G = 0;
+    if (M > 0) {
+        BwdArgs a;
+        a.x = x;
+        a.w = w;
+        a.dy = dy;
+        a.rstd = rstd;
+        a.dx = dx;
+        a.partials = static_cast<float*>(workspace);
+        a.M = M;
+        a.N = N;
+        a.inv_n = static_cast<float>(1.0 / static_cast<double>(N));
+        a.offset = offset;
+        void* args[] = {&a};
+        const size_t lds = p->variant == RMSNORM_VARIANT_WAVE ? static_cast<size_t>(bwd_wave_lds(p, N)) : 0;
+        hipError_t e = hipLaunchKernel(k->func, dim3(static_cast<unsigned>(p->grid)),
+                                       dim3(static_cast<unsigned>(p->block_threads)), args, lds, s);
+        if (e != hipSuccess)
+            return fail(RMSNORM_ERR_HIP, std::string("hipLaunchKernel(") + k->name + "): " + hipGetErrorString(e));
+        G = p->grid;
+    }
+    const float* partials = static_cast<const float*>(workspace);
+    int64_t Nn = N;
+    int32_t vec4 = (N % 4 == 0 && aligned16(dw)) ? 1 : 0;
+    void* rargs[] = {&partials, &dw, &G, &Nn, &vec4};
+    const int64_t groups = vec4 ? N / 4 : N;        // column groups, 16 per workgroup
+    const int64_t blocks = ceil_div(groups, 16);
+    hipError_t e = hipLaunchKernel(rmsnorm_impl::dw_reduce_kernel(), dim3(static_cast<unsigned>(blocks)), dim3(256),
+                                   rargs, 0, s);
+    if (e != hipSuccess) return fail(RMSNORM_ERR_HIP, std::string("hipLaunchKernel(rmsnorm_dw_reduce): ") + hipGetErrorString(e));
+    return RMSNORM_OK;
+}
+
+int bwd_common(const void* x, const void* w, const void* dy, const float* rstd, void* dx, float* dw, int64_t M,
+               int64_t N, float offset, int dtype, rmsnorm_plan_t* p, void* ws, int64_t ws_bytes, void* stream) {
+    const KernelEntry* k = nullptr;
+    int st = finish_bwd_plan(p, M, N, dtype, x, w, dy, dx, &k);
+    if (st != RMSNORM_OK) return st;
+    const int64_t need = M > 0 ? p->grid * N * 4 : 0;
+    st = check_workspace(ws, ws_bytes, need, x, w, dy, rstd, dx, dw, M, N);
+    if (st != RMSNORM_OK) return st;
+    int cu = 0;
+    st = device_info(&cu);
+    if (st != RMSNORM_OK) return st;
+    return launch_bwd(k, p, x, w, dy, rstd, dx, dw, M, N, offset, ws, stream);
+}
+
 }  // namespace
 
 extern "C" {
@@ -412,6 +645,56 @@ int rmsnorm_plan_resources(const rmsnorm_plan_t* plan, int dtype, int32_t* vgprs
     if (lds_bytes) *lds_bytes = static_cast<int32_t>(attr.sharedSizeBytes);
     if (scratch) *scratch = static_cast<int32_t>(attr.localSizeBytes);
     return RMSNORM_OK;
+}
+
+
+int rmsnorm_bwd_plan_query(int64_t M, int64_t N, int dtype, const void* x, const void* dy, const void* dx,
+                           int32_t cu_count, rmsnorm_plan_t* out) {
+    g_last_error.clear();
+    if (!out) return fail(RMSNORM_ERR_NULL, "out must be non-NULL");
+    int st = check_shape_dtype(M, N, dtype);
+    if (st != RMSNORM_OK) return st;
+    rmsnorm_plan_t p;
+    const KernelEntry* k = nullptr;
+    choose_bwd_plan(M, N, x, dx, dy, dx, dtype, &p);
+    st = finish_bwd_plan(&p, M, N, dtype, x, dx, dy, dx, &k);
+    if (st == RMSNORM_OK) st = resident_grid(&p, k, cu_count, &p.resident_grid);
+    if (st != RMSNORM_OK) return st;
+    *out = p;
+    return RMSNORM_OK;
+}
+
+int rmsnorm_bwd_workspace_size(int64_t M, int64_t N, int dtype, const void* x, const void* dy, const void* dx,
+                               int64_t* bytes) {
+    g_last_error.clear();
+    if (!bytes) return fail(RMSNORM_ERR_NULL, "bytes must be non-NULL");
+    int st = check_shape_dtype(M, N, dtype);
+    if (st != RMSNORM_OK) return st;
+    rmsnorm_plan_t p;
+    choose_bwd_plan(M, N, x, dx, dy, dx, dtype, &p);
+    *bytes = M > 0 ? p.grid * N * 4 : 0;
+    return RMSNORM_OK;
+}
+
+int rmsnorm_bwd(const void* x, const void* w, const void* dy, const float* rstd, void* dx, float* dw, int64_t M,
+                int64_t N, float offset, int dtype, void* workspace, int64_t workspace_bytes, void* stream) {
+    g_last_error.clear();
+    int st = check_bwd_args(x, w, dy, rstd, dx, dw, M, N, offset, dtype);
+    if (st != RMSNORM_OK) return st;
+    rmsnorm_plan_t p;
+    choose_bwd_plan(M, N, x, w, dy, dx, dtype, &p);
+    return bwd_common(x, w, dy, rstd, dx, dw, M, N, offset, dtype, &p, workspace, workspace_bytes, stream);
+}
+
+int rmsnorm_bwd_with_plan(const void* x, const void* w, const void* dy, const float* rstd, void* dx, float* dw,
+                          int64_t M, int64_t N, float offset, int dtype, const rmsnorm_plan_t* plan,
+                          void* workspace, int64_t workspace_bytes, void* stream) {
+    g_last_error.clear();
+    int st = check_bwd_args(x, w, dy, rstd, dx, dw, M, N, offset, dtype);
+    if (st != RMSNORM_OK) return st;
+    if (!plan) return fail(RMSNORM_ERR_NULL, "plan must be non-NULL");
+    rmsnorm_plan_t p = *plan;
+    return bwd_common(x, w, dy, rstd, dx, dw, M, N, offset, dtype, &p, workspace, workspace_bytes, stream);
 }
 
 const char* rmsnorm_status_string(int status) {

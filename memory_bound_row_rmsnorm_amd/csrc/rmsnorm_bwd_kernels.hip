@@ -1,0 +1,453 @@
+// rmsnorm_bwd_kernels.hip -- row RMSNorm backward for gfx950 (MI355X).
+//
+// The pages keep the forward's per-row rstd "for backward" ("Why cutile's
+// rmsnorm required full register", kernel listing) but give no formula.
+// Differentiating y_j = x_j r (offset + w_j), r = (mean_j x_j^2 + eps)^(-1/2):
+//
+//     g_j      = offset + w_j
+//     c[m]     = (1/N) sum_j dy[m,j] g_j x[m,j]
+//     dx[m,k]  = r (g_k dy[m,k] - r^2 c[m] x[m,k])
+//     dw[j]    = sum_m dy[m,j] x[m,j] r[m]
+//
+// All arithmetic is fp32; x, w, dy and dx are bf16 or fp16, rstd and dw fp32.
+//
+// Two passes.  The row pass runs a grid of G workgroups that loop over rows
+// (a persistent grid: each workgroup keeps its columns' share of dw in
+// registers across all of its rows) and writes one fp32 partial row of dw
+// per workgroup to a workspace [G, N].  The column pass sums the G partial
+// rows in a fixed order, so dw does not depend on timing.  The row pass has
+// the forward's two shapes: rows inside 16/32/64-lane wave segments for
+// N <= 1024 (partials of the segments and waves that share columns are
+// added in LDS at the end), and one row per workgroup for larger N (each
+// thread owns distinct columns, so its partial goes straight out).  A
+// generic kernel takes any N and alignment.
+#include "rmsnorm_device.hpp"
+#include "rmsnorm_internal.hpp"
+#include "../../include/rmsnorm.h"
+
+using namespace rmsnorm_dev;
+using rmsnorm_impl::BwdArgs;
+
+namespace {
+
+constexpr u32x4 kZero = {0u, 0u, 0u, 0u};
+
+__device__ __forceinline__ u32x4 stream_load(const u32x4* p) { return __builtin_nontemporal_load(p); }
+__device__ __forceinline__ void stream_store(u32x4* p, u32x4 v) { __builtin_nontemporal_store(v, p); }
+
+// sum over this lane's 8 columns of one vector of dy * g * x
+template <class D>
+__device__ __forceinline__ float dot_dgx(const u32x4 dq, const u32x4 xq, const float (&g)[8], float acc) {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        acc = __builtin_fmaf(D::lo(dq[k]) * g[2 * k], D::lo(xq[k]), acc);
+        acc = __builtin_fmaf(D::hi(dq[k]) * g[2 * k + 1], D::hi(xq[k]), acc);
+    }
+    return acc;
+}
+
+// dx for one vector, and dw partials += dy * x * r
+template <class D>
+__device__ __forceinline__ u32x4 grad_vector(const u32x4 dq, const u32x4 xq, const float (&g)[8], float r,
+                                             float r2c, float (&dwp)[8]) {
+    u32x4 o;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        const float d0 = D::lo(dq[k]), d1 = D::hi(dq[k]);
+        const float x0 = D::lo(xq[k]), x1 = D::hi(xq[k]);
+        const float v0 = r * (g[2 * k] * d0 - r2c * x0);
+        const float v1 = r * (g[2 * k + 1] * d1 - r2c * x1);
+        dwp[2 * k] = __builtin_fmaf(d0 * x0, r, dwp[2 * k]);
+        dwp[2 * k + 1] = __builtin_fmaf(d1 * x1, r, dwp[2 * k + 1]);
+        o[k] = D::pack(v0, v1);
+    }
+    return o;
+}
+
+// offset + w widened from one packed 16-byte weight vector, at the point of
+// use (the block family keeps w packed: 4 VGPRs per vector instead of 8)
+template <class D>
+__device__ __forceinline__ void widen_g(float (&g)[8], const u32x4 q, float offset) {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        g[2 * k] = offset + D::lo(q[k]);
+        g[2 * k + 1] = offset + D::hi(q[k]);
+    }
+}
+
+}  // namespace
+
+// ---------------------------------------------------------------------------
+// Row pass, wave family (N <= 1024).  Lane layout as in the forward wave
+// kernel.  With PREFETCH the next trip's rows are loaded before this trip's
+// reductions and stores (worth it when a wave makes more than one trip).
+// Dynamic LDS: (waves per workgroup) x (64 / LANES) x N floats.
+// ---------------------------------------------------------------------------
+template <class D, int LANES, int VPL, int SLOTS, bool PREFETCH>
+__global__ __launch_bounds__(1024) void rmsnorm_bwd_wave(BwdArgs a) {
+    extern __shared__ float lds_part[];
+    constexpr int SEG = 64 / LANES;
+    constexpr int ROWS = SEG * SLOTS;
+    const u32x4* __restrict__ x = static_cast<const u32x4*>(a.x);
+    const u32x4* __restrict__ w = static_cast<const u32x4*>(a.w);
+    const u32x4* __restrict__ dy = static_cast<const u32x4*>(a.dy);
+    const float* __restrict__ rstd = a.rstd;
+    u32x4* __restrict__ dx = static_cast<u32x4*>(a.dx);
+    const int64_t M = a.M;
+    const int N = static_cast<int>(a.N);
+    const int nvec = N >> 3;
+    const int lane = threadIdx.x & 63;
+    const int seg = lane / LANES;
+    const int li = lane % LANES;
+    const int wpb = blockDim.x >> 6;
+    const int wid = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
+    const int64_t nwaves = static_cast<int64_t>(gridDim.x) * wpb;
+
+    float g[VPL][8];
+    float dwp[VPL][8];
+#pragma unroll
+    for (int v = 0; v < VPL; ++v) {
+        const int c = v * LANES + li;
+        widen_g<D>(g[v], c < nvec ? w[c] : kZero, a.offset);
+#pragma unroll
+        for (int k = 0; k < 8; ++k) dwp[v][k] = 0.0f;
+    }
+
+    auto load_trip = [&](u32x4 (&xd)[SLOTS][VPL], u32x4 (&dd)[SLOTS][VPL], float (&r)[SLOTS], int64_t gg) {
+#pragma unroll
+        for (int s = 0; s < SLOTS; ++s) {
+            const int64_t row = gg * ROWS + seg + s * SEG;
+            const bool live = row < M;
+            const u32x4* xr = x + row * nvec;
+            const u32x4* dr = dy + row * nvec;
+#pragma unroll
+            for (int v = 0; v < VPL; ++v) {
+                const int c = v * LANES + li;
+                xd[s][v] = (live && c < nvec) ? stream_load(xr + c) : kZero;
+                dd[s][v] = (live && c < nvec) ? stream_load(dr + c) : kZero;
+            }
+            r[s] = live ? rstd[row] : 0.0f;
+        }
+    };
+
+    int64_t gi = static_cast<int64_t>(blockIdx.x) * wpb + wid;
+    u32x4 xd[SLOTS][VPL], dd[SLOTS][VPL];
+    float r[SLOTS];
+    if (PREFETCH && gi * ROWS < M) load_trip(xd, dd, r, gi);
+    while (gi * ROWS < M) {
+        const int64_t gn = gi + nwaves;
+        u32x4 xn[SLOTS][VPL], dn[SLOTS][VPL];
+        float rn[SLOTS];
+        if constexpr (PREFETCH) {
+            if (gn * ROWS < M) load_trip(xn, dn, rn, gn);
+        } else {
+            load_trip(xd, dd, r, gi);
+        }
+#pragma unroll
+        for (int s = 0; s < SLOTS; ++s) {
+            float t = 0.0f;
+#pragma unroll
+            for (int v = 0; v < VPL; ++v) t = dot_dgx<D>(dd[s][v], xd[s][v], g[v], t);
+            const float cm = segment_allreduce<LANES>(t) * a.inv_n;
+            const float r2c = r[s] * r[s] * cm;
+            const int64_t row = gi * ROWS + seg + s * SEG;
+            u32x4* out = dx + row * nvec;
+#pragma unroll
+            for (int v = 0; v < VPL; ++v) {
+                const int c = v * LANES + li;
+                const u32x4 o = grad_vector<D>(dd[s][v], xd[s][v], g[v], r[s], r2c, dwp[v]);
+                if (row < M && c < nvec) stream_store(out + c, o);
+            }
+        }
+        gi = gn;
+        if constexpr (PREFETCH) {
+#pragma unroll
+            for (int s = 0; s < SLOTS; ++s) {
+#pragma unroll
+                for (int v = 0; v < VPL; ++v) {
+                    xd[s][v] = xn[s][v];
+                    dd[s][v] = dn[s][v];
+                }
+                r[s] = rn[s];
+            }
+        }
+    }
+
+    // partials of all segments of all waves cover the same columns: add them
+    // in a fixed order through LDS, then one partial row per workgroup
+    float* mine = lds_part + static_cast<int64_t>(wid * SEG + seg) * N;
+#pragma unroll
+    for (int v = 0; v < VPL; ++v) {
+        const int c = v * LANES + li;
+        if (c < nvec) {
+#pragma unroll
+            for (int k = 0; k < 8; ++k) mine[c * 8 + k] = dwp[v][k];
+        }
+    }
+    __syncthreads();
+    const int parts = wpb * SEG;
+    float* dst = a.partials + static_cast<int64_t>(blockIdx.x) * N;
+    for (int col = threadIdx.x; col < N; col += blockDim.x) {
+        float acc = lds_part[col];
+        for (int i = 1; i < parts; ++i) acc += lds_part[static_cast<int64_t>(i) * N + col];
+        dst[col] = acc;
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Row pass, block family (N > 1024): one row per workgroup per trip, thread t
+// holding vectors v * T + t (with PREFETCH the next row is loaded before this
+// row's reduction); c is reduced across waves through LDS (double buffered,
+// one barrier per row); each thread's dw partial covers its own columns and
+// is written straight to the workspace.
+// ---------------------------------------------------------------------------
+template <class D, int VPT, bool PREFETCH>
+__global__ __launch_bounds__(1024) void rmsnorm_bwd_block(BwdArgs a) {
+    __shared__ float part[2][16];
+    const u32x4* __restrict__ x = static_cast<const u32x4*>(a.x);
+    const u32x4* __restrict__ w = static_cast<const u32x4*>(a.w);
+    const u32x4* __restrict__ dy = static_cast<const u32x4*>(a.dy);
+    const float* __restrict__ rstd = a.rstd;
+    u32x4* __restrict__ dx = static_cast<u32x4*>(a.dx);
+    const int64_t M = a.M;
+    const int nvec = static_cast<int>(a.N >> 3);
+    const int tid = threadIdx.x;
+    const int nt = blockDim.x;
+    const int lane = tid & 63;
+    const int wid = tid >> 6;
+    const int nw = nt >> 6;
+
+    u32x4 wq[VPT];
+    float dwp[VPT][8];
+#pragma unroll
+    for (int v = 0; v < VPT; ++v) {
+        const int c = v * nt + tid;
+        wq[v] = c < nvec ? w[c] : kZero;
+#pragma unroll
+        for (int k = 0; k < 8; ++k) dwp[v][k] = 0.0f;
+    }
+
+    auto load_row = [&](u32x4 (&xd)[VPT], u32x4 (&dd)[VPT], float& r, int64_t rr) {
+        const u32x4* xr = x + rr * nvec;
+        const u32x4* dr = dy + rr * nvec;
+#pragma unroll
+        for (int v = 0; v < VPT; ++v) {
+            const int c = v * nt + tid;
+            xd[v] = c < nvec ? stream_load(xr + c) : kZero;
+            dd[v] = c < nvec ? stream_load(dr + c) : kZero;
+        }
+        r = rstd[rr];
+    };
+
+    int par = 0;
+    int64_t row = blockIdx.x;
+    u32x4 xd[VPT], dd[VPT];
+    float r = 0.0f;
+    if (PREFETCH && row < M) load_row(xd, dd, r, row);
+    while (row < M) {
+        const int64_t next = row + gridDim.x;
+        u32x4 xn[VPT], dn[VPT];
+        float rn = 0.0f;
+        if constexpr (PREFETCH) {
+            if (next < M) load_row(xn, dn, rn, next);
+        } else {
+            load_row(xd, dd, r, row);
+        }
+        float t = 0.0f;
+#pragma unroll
+        for (int v = 0; v < VPT; ++v) {
+            float g[8];
+            widen_g<D>(g, wq[v], a.offset);
+            t = dot_dgx<D>(dd[v], xd[v], g, t);
+        }
+        t = segment_allreduce<64>(t);
+        if (lane == 0) part[par][wid] = t;
+        __syncthreads();
+        float tot = part[par][0];
+        for (int i = 1; i < nw; ++i) tot += part[par][i];
+        const float r2c = r * r * (tot * a.inv_n);
+        u32x4* out = dx + row * nvec;
+#pragma unroll
+        for (int v = 0; v < VPT; ++v) {
+            const int c = v * nt + tid;
+            float g[8];
+            widen_g<D>(g, wq[v], a.offset);
+            const u32x4 o = grad_vector<D>(dd[v], xd[v], g, r, r2c, dwp[v]);
+            if (c < nvec) stream_store(out + c, o);
+        }
+        par ^= 1;
+        row = next;
+        if constexpr (PREFETCH) {
+#pragma unroll
+            for (int v = 0; v < VPT; ++v) {
+                xd[v] = xn[v];
+                dd[v] = dn[v];
+            }
+            r = rn;
+        }
+    }
+
+    float* dst = a.partials + static_cast<int64_t>(blockIdx.x) * a.N;
+#pragma unroll
+    for (int v = 0; v < VPT; ++v) {
+        const int c = v * nt + tid;
+        if (c < nvec) {
+#pragma unroll
+            for (int k = 0; k < 8; ++k) dst[c * 8 + k] = dwp[v][k];
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Row pass, generic (any N and alignment): one row per workgroup per trip,
+// 2-byte accesses, the row read twice (c first, then dx), and the
+// workgroup's partial row of dw updated in the workspace in place (each
+// workgroup owns its own partial row, so no other workgroup touches it).
+// dx may be the same buffer as dy: each element is read, then written, by
+// the same thread, after the barrier that completes c.
+// ---------------------------------------------------------------------------
+template <class D>
+__global__ __launch_bounds__(1024) void rmsnorm_bwd_generic(BwdArgs a) {
+    __shared__ float part[2][16];
+    const uint16_t* x = static_cast<const uint16_t*>(a.x);
+    const uint16_t* __restrict__ w = static_cast<const uint16_t*>(a.w);
+    const uint16_t* dy = static_cast<const uint16_t*>(a.dy);
+    uint16_t* dx = static_cast<uint16_t*>(a.dx);
+    const int64_t M = a.M;
+    const int64_t N = a.N;
+    const int tid = threadIdx.x;
+    const int nt = blockDim.x;
+    const int lane = tid & 63;
+    const int wid = tid >> 6;
+    const int nw = nt >> 6;
+    float* dst = a.partials + static_cast<int64_t>(blockIdx.x) * N;
+    for (int64_t j = tid; j < N; j += nt) dst[j] = 0.0f;
+
+    int par = 0;
+    for (int64_t row = blockIdx.x; row < M; row += gridDim.x) {
+        const uint16_t* xr = x + row * N;
+        const uint16_t* dr = dy + row * N;
+        uint16_t* out = dx + row * N;
+        const float r = a.rstd[row];
+        float t = 0.0f;
+        for (int64_t j = tid; j < N; j += nt)
+            t = __builtin_fmaf(D::one(dr[j]) * (a.offset + D::one(w[j])), D::one(xr[j]), t);
+        t = segment_allreduce<64>(t);
+        if (lane == 0) part[par][wid] = t;
+        __syncthreads();
+        float tot = part[par][0];
+        for (int i = 1; i < nw; ++i) tot += part[par][i];
+        const float r2c = r * r * (tot * a.inv_n);
+        for (int64_t j = tid; j < N; j += nt) {
+            const float d = D::one(dr[j]), xv = D::one(xr[j]);
+            const float gj = a.offset + D::one(w[j]);
+            dst[j] = __builtin_fmaf(d * xv, r, dst[j]);
+            out[j] = D::round1(r * (gj * d - r2c * xv));
+        }
+        par ^= 1;
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Column pass: dw[j] = sum over the G partial rows.  A workgroup of 256
+// threads covers 64 columns (16 groups of 4) and splits the G partial rows 16
+// ways: thread (s, q) adds rows s, s + 16, s + 32, ... of columns 4q .. 4q + 3
+// in that order, and the 16 sub-sums are then added in order of s through
+// LDS -- a fixed order, so dw is the same on every run.  A wave reads four
+// partial rows of 256 contiguous bytes per load.  With vec4 (N % 4 == 0 and
+// dw 16-byte aligned; the workspace always is) columns move as float4,
+// otherwise one column per lane of a group.
+// ---------------------------------------------------------------------------
+constexpr int kRedCols4 = 16;    // column groups per workgroup
+constexpr int kRedSplit = 16;    // ways each column's partial rows are split
+
+__global__ __launch_bounds__(256) void rmsnorm_dw_reduce(const float* __restrict__ partials,
+                                                         float* __restrict__ dw, int64_t G, int64_t N,
+                                                         int32_t vec4) {
+    __shared__ float4 red[kRedSplit][kRedCols4];
+    const int q = threadIdx.x % kRedCols4;
+    const int sp = threadIdx.x / kRedCols4;
+    float4 acc = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+    if (vec4) {
+        const int64_t c = (static_cast<int64_t>(blockIdx.x) * kRedCols4 + q) * 4;
+        if (c < N) {
+            int64_t i = sp;
+#pragma unroll 4
+            for (; i < G; i += kRedSplit) {
+                const float4 p = *reinterpret_cast<const float4*>(partials + i * N + c);
+                acc.x += p.x;
+                acc.y += p.y;
+                acc.z += p.z;
+                acc.w += p.w;
+            }
+        }
+        red[sp][q] = acc;
+        __syncthreads();
+        if (sp == 0 && c < N) {
+            float4 t = red[0][q];
+            for (int k = 1; k < kRedSplit; ++k) {
+                const float4 u = red[k][q];
+                t.x += u.x;
+                t.y += u.y;
+                t.z += u.z;
+                t.w += u.w;
+            }
+            *reinterpret_cast<float4*>(dw + c) = t;
+        }
+    } else {
+        const int64_t c = static_cast<int64_t>(blockIdx.x) * kRedCols4 + q;
+        if (c < N) {
+#pragma unroll 4
+            for (int64_t i = sp; i < G; i += kRedSplit) acc.x += partials[i * N + c];
+        }
+        red[sp][q] = acc;
+        __syncthreads();
+        if (sp == 0 && c < N) {
+            float t = red[0][q].x;
+            for (int k = 1; k < kRedSplit; ++k) t += red[k][q].x;
+            dw[c] = t;
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Instance table.
+// ---------------------------------------------------------------------------
+#define RMS_BWD_WAVE(D, DT, L, V, S, P)                                                        \
+    {RMSNORM_VARIANT_WAVE, DT, L, V, S, P,                                                     \
+     reinterpret_cast<const void*>(&rmsnorm_bwd_wave<D, L, V, S, P>),                          \
+     "rmsnorm_bwd_wave<" #D "," #L "," #V "," #S "," #P ">"}
+#define RMS_BWD_WAVE2(D, DT, L, V, S) RMS_BWD_WAVE(D, DT, L, V, S, false), RMS_BWD_WAVE(D, DT, L, V, S, true)
+#define RMS_BWD_BLOCK(D, DT, V, P)                                                             \
+    {RMSNORM_VARIANT_BLOCK, DT, 0, V, 1, P,                                                    \
+     reinterpret_cast<const void*>(&rmsnorm_bwd_block<D, V, P>),                               \
+     "rmsnorm_bwd_block<" #D "," #V "," #P ">"}
+// Only instances that fit 128 VGPRs without scratch: the block family holds
+// at most two vectors of x and dy per thread (rows up to 1024 x 2 x 8 = 16384),
+// and the widest wave shapes have no prefetching form.
+#define RMS_BWD_FAMILY(D, DT)                                                                  \
+    RMS_BWD_WAVE2(D, DT, 16, 1, 1), RMS_BWD_WAVE2(D, DT, 16, 1, 2),                            \
+    RMS_BWD_WAVE2(D, DT, 32, 1, 1), RMS_BWD_WAVE2(D, DT, 32, 1, 2),                            \
+    RMS_BWD_WAVE2(D, DT, 64, 1, 1), RMS_BWD_WAVE2(D, DT, 64, 1, 2),                            \
+    RMS_BWD_WAVE(D, DT, 64, 1, 4, false), RMS_BWD_WAVE2(D, DT, 64, 2, 1),                      \
+    RMS_BWD_WAVE(D, DT, 64, 2, 2, false),                                                      \
+    RMS_BWD_BLOCK(D, DT, 1, false), RMS_BWD_BLOCK(D, DT, 1, true),                             \
+    RMS_BWD_BLOCK(D, DT, 2, false), RMS_BWD_BLOCK(D, DT, 2, true),                             \
+    {RMSNORM_VARIANT_GENERIC, DT, 0, 0, 1, false,                                              \
+     reinterpret_cast<const void*>(&rmsnorm_bwd_generic<D>), "rmsnorm_bwd_generic<" #D ">"}
+
+namespace rmsnorm_impl {
+
+static const KernelEntry kBwdTable[] = {
+    RMS_BWD_FAMILY(BF16, RMSNORM_BF16),
+    RMS_BWD_FAMILY(FP16, RMSNORM_FP16),
+};
+
+const KernelEntry* bwd_kernel_table(int* count) {
+    *count = static_cast<int>(sizeof(kBwdTable) / sizeof(kBwdTable[0]));
+    return kBwdTable;
+}
+
+const void* dw_reduce_kernel() { return reinterpret_cast<const void*>(&rmsnorm_dw_reduce); }
+
+}  // namespace rmsnorm_impl

@@ -24,6 +24,22 @@ struct KernelArgs {
     int32_t xcd_group;
 };
 
+// Arguments of every backward row-pass kernel.
+//   x, w, dy : 16-bit element buffers (device); rstd : fp32 [M] (device)
+//   dx : 16-bit [M, N] output; partials : fp32 [grid, N] workspace rows
+struct BwdArgs {
+    const void* x;
+    const void* w;
+    const void* dy;
+    const float* rstd;
+    void* dx;
+    float* partials;
+    int64_t M;
+    int64_t N;
+    float inv_n;
+    float offset;
+};
+
 struct KernelEntry {
     int variant;           // rmsnorm_variant_t
     int dtype;             // rmsnorm_dtype_t
@@ -37,5 +53,11 @@ struct KernelEntry {
 
 // The compiled instances (defined in rmsnorm_kernels.hip).
 const KernelEntry* kernel_table(int* count);
+
+// Backward row-pass instances and the column-pass kernel (rmsnorm_bwd_kernels.hip).
+// The column pass takes (const float* partials, float* dw, int64_t G, int64_t N,
+// int32_t vec4): vec4 = 1 when N % 4 == 0 and dw is 16-byte aligned.
+const KernelEntry* bwd_kernel_table(int* count);
+const void* dw_reduce_kernel();
 
 }  // namespace rmsnorm_impl

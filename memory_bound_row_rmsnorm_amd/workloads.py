@@ -98,6 +98,14 @@ def make_inputs(wl: Workload, seed: int = 0, rows: int | None = None):
     return x.to(td), w.to(td)
 
 
+def make_grad(wl: Workload, seed: int = 0, rows: int | None = None) -> torch.Tensor:
+    """Upstream gradient dy for the backward: N(0, 1) in the workload's dtype,
+    from its own generator (seed + 1000003) so it is independent of x and w."""
+    M = wl.M if rows is None else rows
+    g = torch.Generator("cpu").manual_seed(seed + 1000003)
+    return torch.randn(M, wl.N, generator=g, dtype=torch.float32).to(TORCH_DTYPES[wl.dtype])
+
+
 def to_bits(t: torch.Tensor) -> np.ndarray:
     """Bit patterns of a CPU 16-bit tensor as a uint16 numpy array (no copy of values)."""
     if t.dtype not in (torch.bfloat16, torch.float16):

@@ -260,17 +260,26 @@ int oracle_rmsnorm_bwd(const uint16_t* x, const uint16_t* w, const uint16_t* dy,
         }
     }
 
+    /* dw: each column summed over rows in increasing m; columns are taken in
+     * chunks so that the rows are walked in memory order */
+    const int64_t CH = 64;
 #pragma omp parallel for schedule(static)
-    for (int64_t j = 0; j < N; ++j) {
-        double acc = 0.0, aabs = 0.0;
+    for (int64_t j0 = 0; j0 < N; j0 += CH) {
+        const int64_t j1 = j0 + CH < N ? j0 + CH : N;
+        double acc[64], aabs[64];
+        for (int64_t j = j0; j < j1; ++j) { acc[j - j0] = 0.0; aabs[j - j0] = 0.0; }
         for (int64_t m = 0; m < M; ++m) {
-            const double t = oracle_decode(dy[m * N + j], dtype) * oracle_decode(x[m * N + j], dtype) *
-                             rstd[m];
-            acc += t;
-            aabs += fabs(t);
+            for (int64_t j = j0; j < j1; ++j) {
+                const double t = oracle_decode(dy[m * N + j], dtype) * oracle_decode(x[m * N + j], dtype) *
+                                 rstd[m];
+                acc[j - j0] += t;
+                aabs[j - j0] += fabs(t);
+            }
         }
-        dw[j] = acc;
-        if (dw_scale) dw_scale[j] = aabs;
+        for (int64_t j = j0; j < j1; ++j) {
+            dw[j] = acc[j - j0];
+            if (dw_scale) dw_scale[j] = aabs[j - j0];
+        }
     }
     return 0;
 }

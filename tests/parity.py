@@ -84,3 +84,56 @@ def compare(y_gpu: torch.Tensor, rstd_gpu: torch.Tensor, y_ref: np.ndarray, rstd
 
 def oracle_for(x_cpu: torch.Tensor, w_cpu: torch.Tensor, eps: float, offset: float, dtype: str):
     return oracle.rmsnorm_fwd(workloads.to_bits(x_cpu), workloads.to_bits(w_cpu), eps, offset, dtype)
+
+
+# ---------------------------------------------------------------------------
+# Backward.  dx can cancel (r g dy against r^3 c x), so a bound relative to dx
+# itself is meaningless where it nearly vanishes; the bar is relative to the
+# size of the terms it is computed from:
+#   |dx_gpu - dx_exact| <= ulp_dtype(dx_exact) + 2^-16 * (|r g dy| + |r^3 x| mean_j |dy g x|)
+# one ulp for the single rounding to the dtype, and 2^-16 (about 1.5e-5) for
+# fp32 products and a tree of at most 16384 fp32 additions in c (first-order
+# bound (32 + 6 + 16) * 2^-24, with a factor 4 to spare).
+#   |dw_gpu - dw_exact| <= 2 K 2^-24 sum_m |dy x r| + 2^-23 |dw_exact|
+# where K = ceil(M / G) + G + 64 bounds the sequential fp32 additions along
+# any one column (rows of one workgroup, its waves and segments, then the G
+# partial rows), with a factor 2 to spare, plus the final rounding.
+# Both sides use the same rstd values.
+# ---------------------------------------------------------------------------
+FRAC_BITS = {"bf16": 7, "fp16": 10}
+MIN_EXP = {"bf16": -126, "fp16": -14}
+
+
+def ulp_of(v: np.ndarray, dtype: str) -> np.ndarray:
+    _, e = np.frexp(np.abs(v))                      # |v| = m 2^e, m in [0.5, 1)
+    exp = np.maximum(e - 1, MIN_EXP[dtype])
+    return np.ldexp(1.0, exp - FRAC_BITS[dtype])
+
+
+def compare_bwd(dx_gpu: torch.Tensor, dw_gpu: torch.Tensor, dx_exact: np.ndarray, dx_scale: np.ndarray,
+                dw_exact: np.ndarray, dw_scale: np.ndarray, dtype: str, M: int, G: int, what: str = "") -> dict:
+    dxg = oracle.decode(gpu_bits(dx_gpu).reshape(dx_exact.shape), dtype)
+    err = np.abs(dxg - dx_exact)
+    bound = ulp_of(dx_exact, dtype) + 2.0 ** -16 * dx_scale
+    bad = ~(err <= bound)
+    if bad.any():
+        i = np.unravel_index(int(np.argmax(np.where(bad, err / bound, 0))), err.shape)
+        raise AssertionError(f"{what}: dx off at {i}: gpu {dxg[i]!r} exact {dx_exact[i]!r} bound {bound[i]!r} "
+                             f"({int(bad.sum())} elements out of bound)")
+    dwg = dw_gpu.cpu().numpy().astype(np.float64)
+    K = -(-M // max(G, 1)) + G + 64
+    wbound = 2 * K * 2.0 ** -24 * dw_scale + 2.0 ** -23 * np.abs(dw_exact) + 1e-30
+    werr = np.abs(dwg - dw_exact)
+    wbad = ~(werr <= wbound)
+    if wbad.any():
+        j = int(np.argmax(np.where(wbad, werr / wbound, 0)))
+        raise AssertionError(f"{what}: dw[{j}] gpu {dwg[j]!r} exact {dw_exact[j]!r} bound {wbound[j]!r} "
+                             f"({int(wbad.sum())} columns out of bound)")
+    return {"dx_max_err_over_bound": float(np.max(err / bound)) if err.size else 0.0,
+            "dw_max_err_over_bound": float(np.max(werr / wbound)) if werr.size else 0.0}
+
+
+def oracle_bwd_for(x_cpu, w_cpu, dy_cpu, rstd_f32: np.ndarray, offset: float, dtype: str):
+    """Oracle backward on the same rstd values the GPU receives."""
+    return oracle.rmsnorm_bwd(workloads.to_bits(x_cpu), workloads.to_bits(w_cpu), workloads.to_bits(dy_cpu),
+                              np.asarray(rstd_f32, dtype=np.float64), offset, dtype, want_exact=True)

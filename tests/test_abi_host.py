@@ -199,3 +199,90 @@ def test_plan_query_validates():
     assert lib.rmsnorm_plan_query(-1, 8, BF16, None, None, None, 256, ctypes.byref(p)) == SHAPE
     assert lib.rmsnorm_plan_query(1, 8, 5, None, None, None, 256, ctypes.byref(p)) == DTYPE
     assert lib.rmsnorm_plan_query(1, 8, BF16, None, None, None, 256, None) == NULL
+
+
+# ---------------------------------------------------------------------------
+# backward
+# ---------------------------------------------------------------------------
+X, W, DY, R, DX, DW, WS = (A + k * 0x1000000 for k in range(7))
+
+
+def bwd(x=X, w=W, dy=DY, rstd=R, dx=DX, dw=DW, M=4, N=512, offset=0.0, dtype=BF16, ws=WS,
+        ws_bytes=1 << 24):
+    return lib.rmsnorm_bwd(x, w, dy, rstd, dx, dw, M, N, offset, dtype, ws, ws_bytes, None)
+
+
+@pytest.mark.parametrize("kwargs,status", [
+    (dict(M=-1), SHAPE),
+    (dict(N=0), SHAPE),
+    (dict(dtype=7), DTYPE),
+    (dict(dw=None), NULL),
+    (dict(x=None), NULL),
+    (dict(dy=None), NULL),
+    (dict(rstd=None), NULL),
+    (dict(dx=None), NULL),
+    (dict(w=None), NULL),
+    (dict(offset=float("inf")), SCALAR),
+    (dict(dx=X), OVERLAP),                 # dx on x
+    (dict(dx=DY + 16), OVERLAP),           # dx partially over dy
+    (dict(dw=X + 64), OVERLAP),            # dw inside x
+    (dict(dw=DX + 64), OVERLAP),           # dw inside dx
+    (dict(ws=None), NULL),
+    (dict(ws_bytes=100), SHAPE),           # workspace too small
+    (dict(ws=DX + 32), OVERLAP),           # workspace over dx
+    (dict(ws=WS + 4), PLAN),               # workspace not 16-byte aligned
+])
+def test_bwd_argument_errors(kwargs, status):
+    assert bwd(**kwargs) == status, lib.rmsnorm_last_error().decode()
+    assert lib.rmsnorm_last_error().decode() != ""
+
+
+def test_bwd_plans_and_workspace():
+    def plan(M, N, dtype=BF16, x=None):
+        p = bnd.Plan()
+        st = lib.rmsnorm_bwd_plan_query(M, N, dtype, x, None, None, 256, ctypes.byref(p))
+        assert st == OK, lib.rmsnorm_last_error().decode()
+        return p
+
+    def ws(M, N, dtype=BF16, x=None):
+        b = ctypes.c_int64()
+        assert lib.rmsnorm_bwd_workspace_size(M, N, dtype, x, None, None, ctypes.byref(b)) == OK
+        return b.value
+
+    # grid = min(trips, 4096 waves' worth of workgroups, 3M/32); prefetch when a workgroup makes several
+    # trips and the grid is at most one workgroup per unit
+    p = plan(16384, 512)
+    assert (p.variant, p.lanes_per_row, p.vectors_per_lane, p.block_threads) == (bnd.VARIANT_WAVE, 64, 1, 1024)
+    assert (p.grid, p.rows_per_trip, p.trips, p.prefetch) == (256, 64, 1, 0) and ws(16384, 512) == 256 * 512 * 4
+    p = plan(262144, 128, FP16)
+    assert (p.variant, p.lanes_per_row, p.row_slots, p.grid, p.prefetch) == (bnd.VARIANT_WAVE, 16, 2, 256, 1)
+    p = plan(32768, 8192)
+    assert (p.variant, p.block_threads, p.vectors_per_lane, p.grid) == (bnd.VARIANT_BLOCK, 512, 2, 512)
+    assert p.prefetch == 0 and ws(32768, 8192) == 512 * 8192 * 4      # two workgroups per unit: no prefetch
+    p = plan(8192, 3000)
+    assert (p.variant, p.block_threads, p.vectors_per_lane, p.grid) == (bnd.VARIANT_BLOCK, 256, 2, 768)
+    p = plan(4096, 16384, FP16)
+    assert (p.variant, p.block_threads, p.vectors_per_lane, p.grid, p.prefetch) == (bnd.VARIANT_BLOCK, 1024, 2, 256, 1)
+    assert plan(64, 8192).grid == 6                              # 3M/32 bounds the workspace traffic
+    assert plan(10, 16392).variant == bnd.VARIANT_GENERIC      # wider than the 16-byte kernels hold
+    assert plan(10, 511).variant == bnd.VARIANT_GENERIC
+    assert plan(10, 512, x=A + 2).variant == bnd.VARIANT_GENERIC
+    assert plan(3, 512).grid == 1                               # 3 rows fit one 8-wave workgroup
+    assert ws(0, 512) == 0
+    for M, N in ((16384, 512), (32768, 8192), (77, 3000), (5, 7)):
+        p = plan(M, N)
+        cover = p.variant == bnd.VARIANT_GENERIC or p.lanes_per_row * p.vectors_per_lane * 8 >= N
+        assert cover and p.grid * p.trips * p.rows_per_trip >= M
+
+
+def test_bwd_plans_that_do_not_fit_are_rejected():
+    good = bnd.Plan()
+    assert lib.rmsnorm_bwd_plan_query(100, 512, BF16, None, None, None, 256, ctypes.byref(good)) == OK
+    for p in (good.copy(prefetch=1),            # the 4-slot wave shape has no prefetching form
+              good.copy(prefetch=2), good.copy(xcd_group=2), good.copy(max_blocks_per_cu=4),
+              good.copy(vectors_per_lane=3), good.copy(block_threads=1024, lanes_per_row=16, row_slots=1,
+                                                       vectors_per_lane=1),
+              good.copy(variant=bnd.VARIANT_BLOCK, block_threads=64, vectors_per_lane=4)):
+        st = lib.rmsnorm_bwd_with_plan(X, W, DY, R, DX, DW, 100, 512, 0.0, BF16, ctypes.byref(p), WS,
+                                       1 << 24, None)
+        assert st == PLAN, (p.as_dict(), lib.rmsnorm_last_error().decode())

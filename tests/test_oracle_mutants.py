@@ -48,10 +48,10 @@ MUTANTS = {
     "bwd_divisor_padded": [("c /= (double)N;", "c /= (double)(N + 1);")],
     "bwd_offset_ignored": [("const double gk = off + oracle_decode(w[k], dtype);",
                             "const double gk = oracle_decode(w[k], dtype);")],
-    "bwd_dw_without_rstd": [("oracle_decode(x[m * N + j], dtype) *\n                             rstd[m];",
-                             "oracle_decode(x[m * N + j], dtype) *\n                             1.0;")],
-    "bwd_dw_times_weight": [("oracle_decode(x[m * N + j], dtype) *\n                             rstd[m];",
-                             "oracle_decode(x[m * N + j], dtype) *\n                             rstd[m] * (off + oracle_decode(w[j], dtype));")],
+    "bwd_dw_without_rstd": [("oracle_decode(x[m * N + j], dtype) *\n                                 rstd[m];",
+                             "oracle_decode(x[m * N + j], dtype) *\n                                 1.0;")],
+    "bwd_dw_times_weight": [("oracle_decode(x[m * N + j], dtype) *\n                                 rstd[m];",
+                             "oracle_decode(x[m * N + j], dtype) *\n                                 rstd[m] * (off + oracle_decode(w[j], dtype));")],
     "bwd_dw_wrong_row_stride": [("oracle_decode(dy[m * N + j], dtype)", "oracle_decode(dy[m + j * M], dtype)")],
 }
 
