@@ -332,6 +332,8 @@ int launch(const KernelEntry* k, const rmsnorm_plan_t* p, const void* x, const v
     a.eps = eps;
     a.offset = offset;
     a.xcd_group = p->xcd_group;
+    a.grid = p->grid;
+    a.threads = p->block_threads;
     void* args[] = {&a};
     hipError_t e = hipLaunchKernel(k->func, dim3(static_cast<unsigned>(p->grid)),
                                    dim3(static_cast<unsigned>(p->block_threads)), args, dyn_lds,
@@ -538,6 +540,8 @@ int launch_bwd(const KernelEntry* k, const rmsnorm_plan_t* p, const void* x, con
         a.N = N;
         a.inv_n = static_cast<float>(1.0 / static_cast<double>(N));
         a.offset = offset;
+        a.grid = p->grid;
+        a.threads = p->block_threads;
         void* args[] = {&a};
         const size_t lds = p->variant == RMSNORM_VARIANT_WAVE ? static_cast<size_t>(bwd_wave_lds(p, N)) : 0;
         hipError_t e = hipLaunchKernel(k->func, dim3(static_cast<unsigned>(p->grid)),

@@ -99,9 +99,9 @@ __global__ __launch_bounds__(1024) void rmsnorm_bwd_wave(BwdArgs a) {
     const int lane = threadIdx.x & 63;
     const int seg = lane / LANES;
     const int li = lane % LANES;
-    const int wpb = blockDim.x >> 6;
+    const int wpb = a.threads >> 6;
     const int wid = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
-    const int64_t nwaves = static_cast<int64_t>(gridDim.x) * wpb;
+    const int64_t nwaves = a.grid * wpb;
 
     float g[VPL][8];
     float dwp[VPL][8];
@@ -187,7 +187,7 @@ __global__ __launch_bounds__(1024) void rmsnorm_bwd_wave(BwdArgs a) {
     __syncthreads();
     const int parts = wpb * SEG;
     float* dst = a.partials + static_cast<int64_t>(blockIdx.x) * N;
-    for (int col = threadIdx.x; col < N; col += blockDim.x) {
+    for (int col = threadIdx.x; col < N; col += a.threads) {
         float acc = lds_part[col];
         for (int i = 1; i < parts; ++i) acc += lds_part[static_cast<int64_t>(i) * N + col];
         dst[col] = acc;
@@ -212,7 +212,7 @@ __global__ __launch_bounds__(1024) void rmsnorm_bwd_block(BwdArgs a) {
     const int64_t M = a.M;
     const int nvec = static_cast<int>(a.N >> 3);
     const int tid = threadIdx.x;
-    const int nt = blockDim.x;
+    const int nt = a.threads;
     const int lane = tid & 63;
     const int wid = tid >> 6;
     const int nw = nt >> 6;
@@ -245,7 +245,7 @@ __global__ __launch_bounds__(1024) void rmsnorm_bwd_block(BwdArgs a) {
     float r = 0.0f;
     if (PREFETCH && row < M) load_row(xd, dd, r, row);
     while (row < M) {
-        const int64_t next = row + gridDim.x;
+        const int64_t next = row + a.grid;
         u32x4 xn[VPT], dn[VPT];
         float rn = 0.0f;
         if constexpr (PREFETCH) {
@@ -316,7 +316,7 @@ __global__ __launch_bounds__(1024) void rmsnorm_bwd_generic(BwdArgs a) {
     const int64_t M = a.M;
     const int64_t N = a.N;
     const int tid = threadIdx.x;
-    const int nt = blockDim.x;
+    const int nt = a.threads;
     const int lane = tid & 63;
     const int wid = tid >> 6;
     const int nw = nt >> 6;
@@ -324,7 +324,7 @@ __global__ __launch_bounds__(1024) void rmsnorm_bwd_generic(BwdArgs a) {
     for (int64_t j = tid; j < N; j += nt) dst[j] = 0.0f;
 
     int par = 0;
-    for (int64_t row = blockIdx.x; row < M; row += gridDim.x) {
+    for (int64_t row = blockIdx.x; row < M; row += a.grid) {
         const uint16_t* xr = x + row * N;
         const uint16_t* dr = dy + row * N;
         uint16_t* out = dx + row * N;

@@ -11,6 +11,11 @@ namespace rmsnorm_impl {
 //   x, w, y : 16-bit element buffers (device), rstd : fp32 [M] (device)
 //   M rows, N columns, inv_n = fp32(1/N), eps, offset
 //   xcd_group: consecutive workgroups' worth of rows placed on one XCD (1 = none)
+//   grid, threads : the launch's workgroup count and workgroup size, passed
+//   here so the kernels read no launch geometry from the dispatch's hidden
+//   arguments (a second scalar-memory round trip before the first row load)
+//   (the fields the kernels need before their first row load come first, in
+//   the 64 bytes the kernels' first scalar loads fetch together)
 struct KernelArgs {
     const void* x;
     const void* w;
@@ -18,10 +23,12 @@ struct KernelArgs {
     float* rstd;
     int64_t M;
     int64_t N;
+    int64_t grid;
+    int32_t threads;
+    int32_t xcd_group;
     float inv_n;
     float eps;
     float offset;
-    int32_t xcd_group;
 };
 
 // Arguments of every backward row-pass kernel.
@@ -36,6 +43,8 @@ struct BwdArgs {
     float* partials;
     int64_t M;
     int64_t N;
+    int64_t grid;       // launch geometry, as in KernelArgs
+    int32_t threads;
     float inv_n;
     float offset;
 };

@@ -100,17 +100,19 @@ constexpr u32x4 kZero = {0u, 0u, 0u, 0u};
 // with its own L2).  With group g > 1 the workgroup index is remapped inside
 // windows of 8 * g workgroups so that XCD x serves g consecutive row groups,
 // (b mod 8) * g + (b / 8) mod g within the window: a transpose of the window,
-// so every index in [0, gridDim.x) is still used exactly once (a tail shorter
+// so every index in [0, G) is still used exactly once (a tail shorter
 // than a window keeps its own order).  Consecutive rows then share an L2 and
 // reach HBM as longer runs of neighbouring addresses; measured on MI355X it
 // shortens the 32768 x 8192 forward by 4-5%.
-__device__ __forceinline__ int64_t grouped_block(int g) {
-    const int64_t b = blockIdx.x;
-    if (g <= 1) return b;
-    const int64_t span = 8 * static_cast<int64_t>(g);
-    const int64_t full = (static_cast<int64_t>(gridDim.x) / span) * span;
+// (32-bit arithmetic: grids stay below 2^31 workgroups and windows below 2^10.)
+__device__ __forceinline__ int64_t grouped_block(int g, int64_t G) {
+    const uint32_t b = blockIdx.x;
+    if (__builtin_expect(g <= 1, 1)) return b;
+    const uint32_t ug = static_cast<uint32_t>(g);
+    const uint32_t span = 8u * ug;
+    const uint32_t full = (static_cast<uint32_t>(G) / span) * span;
     if (b >= full) return b;
-    return (b / span) * span + (b % 8) * g + (b / 8) % g;
+    return (b / span) * span + (b % 8u) * ug + (b / 8u) % ug;
 }
 
 }  // namespace
@@ -139,11 +141,11 @@ __global__ __launch_bounds__(1024) void rmsnorm_wave(KernelArgs a) {
     const int lane = threadIdx.x & 63;
     const int seg = lane / LANES;
     const int li = lane % LANES;
-    const int wpb = blockDim.x >> 6;
+    const int wpb = a.threads >> 6;
     // the wave's index is the same in all its lanes: keep it in a scalar register
     const int wid = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
-    const int64_t nwaves = static_cast<int64_t>(gridDim.x) * wpb;
-    int64_t g = grouped_block(a.xcd_group) * wpb + wid;
+    const int64_t nwaves = a.grid * wpb;
+    int64_t g = grouped_block(a.xcd_group, a.grid) * wpb + wid;
     if (g * ROWS >= M) return;
 
     auto load_trip = [&](u32x4 (&d)[SLOTS][VPL], int64_t gg) {
@@ -242,11 +244,11 @@ __global__ __launch_bounds__(1024) void rmsnorm_block(KernelArgs a) {
     const int64_t M = a.M;
     const int nvec = static_cast<int>(a.N >> 3);
     const int tid = threadIdx.x;
-    const int nt = blockDim.x;
+    const int nt = a.threads;
     const int lane = tid & 63;
     const int wid = tid >> 6;
     const int nw = nt >> 6;
-    int64_t row = grouped_block(a.xcd_group);
+    int64_t row = grouped_block(a.xcd_group, a.grid);
     if (row >= M) return;
 
     auto load_row = [&](u32x4 (&d)[VPT], int64_t rr) {
@@ -287,14 +289,14 @@ __global__ __launch_bounds__(1024) void rmsnorm_block(KernelArgs a) {
 
     // one row per workgroup (the planned launches): straight through
     if constexpr (!PREFETCH) {
-        if (row + gridDim.x >= M) {
+        if (row + a.grid >= M) {
             finish_row(d, row, 0);
             return;
         }
     }
     int par = 0;
     for (;;) {
-        const int64_t next = row + gridDim.x;
+        const int64_t next = row + a.grid;
         const bool more = next < M;
         u32x4 dn[VPT];
         if constexpr (PREFETCH) {
@@ -327,13 +329,13 @@ __global__ __launch_bounds__(1024) void rmsnorm_generic(KernelArgs a) {
     const int64_t M = a.M;
     const int64_t N = a.N;
     const int tid = threadIdx.x;
-    const int nt = blockDim.x;
+    const int nt = a.threads;
     const int lane = tid & 63;
     const int wid = tid >> 6;
     const int nw = nt >> 6;
 
     int par = 0;
-    for (int64_t row = grouped_block(a.xcd_group); row < M; row += gridDim.x) {
+    for (int64_t row = grouped_block(a.xcd_group, a.grid); row < M; row += a.grid) {
         const uint16_t* xr = x + row * N;
         uint16_t* yr = y + row * N;
         float ss = 0.0f;
