@@ -294,6 +294,9 @@ def main() -> int:
     ap.add_argument("--traffic-from", default=None, metavar="DIR",
                     help="write profiles/traffic_<workload>.json from rocprofv3 counter CSVs in DIR "
                          "and exit (no GPU needed)")
+    ap.add_argument("--tuned", default=None, metavar="JSON",
+                    help="register the tuned plans of this file (python -m memory_bound_row_rmsnorm_amd.tune "
+                         "--save) before planning")
     ap.add_argument("--pass", dest="direction", choices=["fwd", "bwd"], default="fwd",
                     help="bwd: time the backward (row pass + dw column pass) instead")
     ap.add_argument("--kernel", choices=["rmsnorm", "copy"], default="rmsnorm",
@@ -346,6 +349,8 @@ def main() -> int:
         rs.append(torch.empty(wl.M, dtype=torch.float32, device=dev))
     w_dev = w0.to(dev)
 
+    if args.tuned:
+        log("tuned plans registered:", binding.load_tuned(args.tuned))
     plan = binding.plan_query(wl.M, wl.N, wl.dtype, xs[0].data_ptr(), w_dev.data_ptr(),
                               ys[0].data_ptr())
     if args.plan:

@@ -234,6 +234,36 @@ int rmsnorm_bwd_with_plan(const void* x, const void* w, const void* dy, const fl
                           const rmsnorm_plan_t* plan, void* workspace, int64_t workspace_bytes,
                           void* stream);
 
+/*
+ * Completes and checks an explicit forward plan without launching anything:
+ * the derived fields (vec_elems, rows_per_trip, trips) and resident_grid (as
+ * in rmsnorm_plan_query, cu_count likewise) are filled into *out.  Returns
+ * RMSNORM_ERR_PLAN exactly when rmsnorm_fwd_with_plan would reject the plan
+ * for these sizes and pointers (alignment only; they may be NULL).
+ */
+int rmsnorm_plan_validate(int64_t M, int64_t N, int dtype, const void* x, const void* w, const void* y,
+                          const rmsnorm_plan_t* plan, int32_t cu_count, rmsnorm_plan_t* out);
+
+/*
+ * Tuned dispatch (the measured counterpart of the planner's rules, for the
+ * register-budget and occupancy choices the pages tune by hand: "Why cutile's
+ * rmsnorm required full register", opening report and replies).
+ *
+ * rmsnorm_plan_set_tuned registers `plan` (fields as for
+ * rmsnorm_fwd_with_plan) for calls with exactly these M, N and dtype:
+ * rmsnorm_fwd and rmsnorm_plan_query then use it instead of their own rule
+ * whenever it fits the call's pointers, and fall back to the rule otherwise.
+ * The plan is validated here against 16-byte aligned pointers
+ * (RMSNORM_ERR_PLAN if it does not fit, RMSNORM_ERR_SHAPE for M == 0);
+ * registering a shape again replaces its plan.  The table is process-wide,
+ * guarded by a lock, and holds copies (the caller keeps ownership of `plan`).
+ * rmsnorm_plan_clear_tuned empties it; rmsnorm_plan_tuned_count returns its
+ * size.  Host only.
+ */
+int rmsnorm_plan_set_tuned(int64_t M, int64_t N, int dtype, const rmsnorm_plan_t* plan);
+int rmsnorm_plan_clear_tuned(void);
+int rmsnorm_plan_tuned_count(void);
+
 /* Static name of a status code ("RMSNORM_OK", ...); never NULL. */
 const char* rmsnorm_status_string(int status);
 

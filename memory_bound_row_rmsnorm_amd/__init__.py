@@ -16,6 +16,7 @@ __all__ = [
     "rmsnorm_fwd", "rmsnorm_fwd_out", "plan_query", "plan_resources", "status_string",
     "rmsnorm_bwd", "rmsnorm_bwd_out", "bwd_plan_query", "bwd_workspace_size",
     "library_path", "version", "Plan", "RmsnormError",
+    "plan_validate", "set_tuned", "clear_tuned", "tuned_count", "load_tuned",
 ]
 
 

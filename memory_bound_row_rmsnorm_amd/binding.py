@@ -32,6 +32,7 @@ STATUS = {
 EXPORTED = (
     "rmsnorm_fwd", "rmsnorm_fwd_with_plan", "rmsnorm_plan_query", "rmsnorm_plan_resources",
     "rmsnorm_bwd", "rmsnorm_bwd_with_plan", "rmsnorm_bwd_plan_query", "rmsnorm_bwd_workspace_size",
+    "rmsnorm_plan_validate", "rmsnorm_plan_set_tuned", "rmsnorm_plan_clear_tuned", "rmsnorm_plan_tuned_count",
     "rmsnorm_status_string", "rmsnorm_last_error", "rmsnorm_version",
 )
 
@@ -100,6 +101,15 @@ def _load():
     lib.rmsnorm_bwd_plan_query.restype = i32
     lib.rmsnorm_bwd_workspace_size.argtypes = [i64, i64, i32, vp, vp, vp, ctypes.POINTER(ctypes.c_int64)]
     lib.rmsnorm_bwd_workspace_size.restype = i32
+    lib.rmsnorm_plan_validate.argtypes = [i64, i64, i32, vp, vp, vp, ctypes.POINTER(Plan), ctypes.c_int32,
+                                          ctypes.POINTER(Plan)]
+    lib.rmsnorm_plan_validate.restype = i32
+    lib.rmsnorm_plan_set_tuned.argtypes = [i64, i64, i32, ctypes.POINTER(Plan)]
+    lib.rmsnorm_plan_set_tuned.restype = i32
+    lib.rmsnorm_plan_clear_tuned.argtypes = []
+    lib.rmsnorm_plan_clear_tuned.restype = i32
+    lib.rmsnorm_plan_tuned_count.argtypes = []
+    lib.rmsnorm_plan_tuned_count.restype = i32
     lib.rmsnorm_status_string.argtypes = [i32]
     lib.rmsnorm_status_string.restype = ctypes.c_char_p
     lib.rmsnorm_last_error.argtypes = []
@@ -209,6 +219,56 @@ def plan_resources(plan: Plan, dtype) -> dict:
 
 def version() -> int:
     return lib.rmsnorm_version()
+
+
+# ---------------------------------------------------------------------------
+# Tuned dispatch
+# ---------------------------------------------------------------------------
+PLAN_FIELDS = ("variant", "lanes_per_row", "vectors_per_lane", "row_slots", "block_threads", "prefetch",
+               "xcd_group", "max_blocks_per_cu", "grid")
+
+
+def plan_validate(M: int, N: int, dtype, plan: Plan, x_ptr: int = 0, w_ptr: int = 0, y_ptr: int = 0,
+                  cu_count: int = 0):
+    """The completed plan (derived fields, resident_grid), or None if rmsnorm_fwd_with_plan would
+    reject it for these sizes and pointers.  Other errors raise."""
+    out = Plan()
+    st = lib.rmsnorm_plan_validate(M, N, _dtype_code(dtype), x_ptr or None, w_ptr or None, y_ptr or None,
+                                   ctypes.byref(plan), cu_count, ctypes.byref(out))
+    if st == 8:
+        return None
+    _check(st)
+    return out
+
+
+def set_tuned(M: int, N: int, dtype, plan: Plan) -> None:
+    """Register `plan` for forward calls of exactly this shape and dtype."""
+    _check(lib.rmsnorm_plan_set_tuned(M, N, _dtype_code(dtype), ctypes.byref(plan)))
+
+
+def clear_tuned() -> None:
+    _check(lib.rmsnorm_plan_clear_tuned())
+
+
+def tuned_count() -> int:
+    return lib.rmsnorm_plan_tuned_count()
+
+
+def load_tuned(path: str) -> int:
+    """Register every plan of a tuning file (JSON: {"plans": [{"M", "N", "dtype", "plan": {...}}]});
+    returns how many were registered."""
+    import json
+
+    with open(path) as f:
+        doc = json.load(f)
+    n = 0
+    for e in doc["plans"]:
+        p = Plan()
+        for k in PLAN_FIELDS:
+            setattr(p, k, int(e["plan"][k]))
+        set_tuned(int(e["M"]), int(e["N"]), e["dtype"], p)
+        n += 1
+    return n
 
 
 # ---------------------------------------------------------------------------

@@ -11,6 +11,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <atomic>
 #include <cmath>
 #include <cstdio>
 #include <cstring>
@@ -30,7 +31,8 @@ namespace {
 
 constexpr int kVersion = 1 * 10000 + 0 * 100 + 0;
 constexpr int kMaxDevices = 64;
-constexpr int kWaveBlockThreads = 256;   // 4 waves per workgroup for the wave family
+constexpr int kWaveBlockThreads = 256;   // 4 waves per workgroup for the wave family, one row per slot
+constexpr int kWaveBlockThreadsMultiRow = 128;   // 2 waves when a slot holds several rows
 constexpr int kMaxThreadsPerCu = 2048;   // 4 SIMDs x 8 waves x 64 lanes
 
 thread_local std::string g_last_error;
@@ -219,6 +221,7 @@ constexpr int kWaveSlots[] = {8, 4, 2, 1};
 constexpr int64_t kMaxVectorN = 1024LL * 6 * 8;   // widest row the 16-byte kernels hold
 constexpr int64_t kMaxGrid = 0x7FFFFFFF;
 constexpr int64_t kWaveBytesInFlight = 4096;      // row bytes one wave loads per trip
+constexpr int64_t kWaveBytesInFlightMultiRow = 2048;   // the same when a slot holds several rows
 constexpr int64_t kXcdGroupBytes = 128 * 1024;    // consecutive row bytes per XCD (block family)
 constexpr int64_t kBytesInFlightPerCu = 64 * 1024; // row bytes resident per compute unit (block family)
 
@@ -251,13 +254,18 @@ int choose_plan(int64_t M, int64_t N, const void* x, const void* w, const void* 
     } else if (N / 8 <= 128) {
         const int64_t nvec = N / 8;
         p->variant = RMSNORM_VARIANT_WAVE;
-        p->block_threads = kWaveBlockThreads;
         p->lanes_per_row = nvec <= 16 ? 16 : (nvec <= 32 ? 32 : 64);
         p->vectors_per_lane = static_cast<int>(ceil_div(nvec, p->lanes_per_row));
+        // Several rows per 64-lane slot (N <= 256): 2 KiB of loads per wave in
+        // 2-wave workgroups measured best (262144 x 128: 23.4 against 24.0 us
+        // with 4 KiB in 4-wave workgroups); one row per slot: 4 KiB, 4 waves.
+        const bool multi_row = p->lanes_per_row < 64;
+        p->block_threads = multi_row ? kWaveBlockThreadsMultiRow : kWaveBlockThreads;
+        const int64_t budget = multi_row ? kWaveBytesInFlightMultiRow : kWaveBytesInFlight;
         const int64_t per_slot = N * 2 * (64 / p->lanes_per_row);
         p->row_slots = 1;
         for (int s : kWaveSlots) {
-            if (s * per_slot <= kWaveBytesInFlight &&
+            if (s * per_slot <= budget &&
                 find_kernel(RMSNORM_VARIANT_WAVE, dtype, p->lanes_per_row, p->vectors_per_lane, s, false)) {
                 p->row_slots = s;
                 break;
@@ -267,7 +275,9 @@ int choose_plan(int64_t M, int64_t N, const void* x, const void* w, const void* 
         const int64_t nvec = N / 8;
         p->variant = RMSNORM_VARIANT_BLOCK;
         p->row_slots = 1;
-        p->block_threads = nvec <= 256 * 6 ? 256 : (nvec <= 512 * 6 ? 512 : 1024);
+        // 256 threads up to 6 vectors each; wider rows take 1024-thread
+        // workgroups (4096 x 16384: 47.5 us against 49.5 us with 512 x 4)
+        p->block_threads = nvec <= 256 * 6 ? 256 : 1024;
         p->vectors_per_lane = static_cast<int>(ceil_div(nvec, p->block_threads));
     }
     int64_t rows_per_trip = 1;
@@ -576,6 +586,38 @@ int bwd_common(const void* x, const void* w, const void* dy, const float* rstd, 
     return launch_bwd(k, p, x, w, dy, rstd, dx, dw, M, N, offset, ws, stream);
 }
 
+// ---------------------------------------------------------------------------
+// Tuned dispatch: plans measured for exact (M, N, dtype) shapes, registered by
+// the caller (for instance from a tuning run), take precedence over the
+// heuristic in rmsnorm_fwd and rmsnorm_plan_query.  A tuned plan that does not
+// fit a call's pointers (alignment) falls back to the heuristic.
+// ---------------------------------------------------------------------------
+std::mutex g_tuned_mu;
+std::map<std::tuple<int64_t, int64_t, int>, rmsnorm_plan_t> g_tuned;
+std::atomic<int> g_tuned_count{0};
+
+bool tuned_plan(int64_t M, int64_t N, int dtype, rmsnorm_plan_t* out) {
+    if (g_tuned_count.load(std::memory_order_acquire) == 0) return false;
+    std::lock_guard<std::mutex> lock(g_tuned_mu);
+    const auto it = g_tuned.find(std::make_tuple(M, N, dtype));
+    if (it == g_tuned.end()) return false;
+    *out = it->second;
+    return true;
+}
+
+int select_plan(int64_t M, int64_t N, const void* x, const void* w, const void* y, int dtype,
+                rmsnorm_plan_t* p, const KernelEntry** k) {
+    rmsnorm_plan_t t;
+    if (tuned_plan(M, N, dtype, &t) && finish_plan(&t, M, N, dtype, x, w, y, k) == RMSNORM_OK) {
+        *p = t;
+        return RMSNORM_OK;
+    }
+    g_last_error.clear();
+    int st = choose_plan(M, N, x, w, y, dtype, p);
+    if (st == RMSNORM_OK) st = finish_plan(p, M, N, dtype, x, w, y, k);
+    return st;
+}
+
 }  // namespace
 
 extern "C" {
@@ -587,8 +629,7 @@ int rmsnorm_fwd(const void* x, const void* w, void* y, float* rstd, int64_t M, i
     if (st != RMSNORM_OK || M == 0) return st;
     rmsnorm_plan_t p;
     const KernelEntry* k = nullptr;
-    st = choose_plan(M, N, x, w, y, dtype, &p);
-    if (st == RMSNORM_OK) st = finish_plan(&p, M, N, dtype, x, w, y, &k);
+    st = select_plan(M, N, x, w, y, dtype, &p, &k);
     if (st != RMSNORM_OK) return st;
     int cu = 0, lds = 0;
     st = device_info(&cu, &lds);  // gfx950 check, unit count and LDS (cached per device)
@@ -620,8 +661,22 @@ int rmsnorm_plan_query(int64_t M, int64_t N, int dtype, const void* x, const voi
     if (st != RMSNORM_OK) return st;
     rmsnorm_plan_t p;
     const KernelEntry* k = nullptr;
-    st = choose_plan(M, N, x, w, y, dtype, &p);
-    if (st == RMSNORM_OK) st = finish_plan(&p, M, N, dtype, x, w, y, &k);
+    st = select_plan(M, N, x, w, y, dtype, &p, &k);
+    if (st == RMSNORM_OK) st = resident_grid(&p, k, cu_count, &p.resident_grid);
+    if (st != RMSNORM_OK) return st;
+    *out = p;
+    return RMSNORM_OK;
+}
+
+int rmsnorm_plan_validate(int64_t M, int64_t N, int dtype, const void* x, const void* w, const void* y,
+                          const rmsnorm_plan_t* plan, int32_t cu_count, rmsnorm_plan_t* out) {
+    g_last_error.clear();
+    if (!plan || !out) return fail(RMSNORM_ERR_NULL, "plan and out must be non-NULL");
+    int st = check_shape_dtype(M, N, dtype);
+    if (st != RMSNORM_OK) return st;
+    rmsnorm_plan_t p = *plan;
+    const KernelEntry* k = nullptr;
+    st = finish_plan(&p, M, N, dtype, x, w, y, &k);
     if (st == RMSNORM_OK) st = resident_grid(&p, k, cu_count, &p.resident_grid);
     if (st != RMSNORM_OK) return st;
     *out = p;
@@ -700,6 +755,32 @@ int rmsnorm_bwd_with_plan(const void* x, const void* w, const void* dy, const fl
     rmsnorm_plan_t p = *plan;
     return bwd_common(x, w, dy, rstd, dx, dw, M, N, offset, dtype, &p, workspace, workspace_bytes, stream);
 }
+
+int rmsnorm_plan_set_tuned(int64_t M, int64_t N, int dtype, const rmsnorm_plan_t* plan) {
+    g_last_error.clear();
+    if (!plan) return fail(RMSNORM_ERR_NULL, "plan must be non-NULL");
+    int st = check_shape_dtype(M, N, dtype);
+    if (st != RMSNORM_OK) return st;
+    if (M == 0) return fail(RMSNORM_ERR_SHAPE, "a tuned plan needs M > 0");
+    rmsnorm_plan_t p = *plan;
+    const KernelEntry* k = nullptr;
+    st = finish_plan(&p, M, N, dtype, nullptr, nullptr, nullptr, &k);  // aligned pointers
+    if (st != RMSNORM_OK) return st;
+    std::lock_guard<std::mutex> lock(g_tuned_mu);
+    g_tuned[std::make_tuple(M, N, dtype)] = p;
+    g_tuned_count.store(static_cast<int>(g_tuned.size()), std::memory_order_release);
+    return RMSNORM_OK;
+}
+
+int rmsnorm_plan_clear_tuned(void) {
+    g_last_error.clear();
+    std::lock_guard<std::mutex> lock(g_tuned_mu);
+    g_tuned.clear();
+    g_tuned_count.store(0, std::memory_order_release);
+    return RMSNORM_OK;
+}
+
+int rmsnorm_plan_tuned_count(void) { return g_tuned_count.load(std::memory_order_acquire); }
 
 const char* rmsnorm_status_string(int status) {
     switch (status) {

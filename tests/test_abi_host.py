@@ -131,10 +131,11 @@ def test_planner_choices_for_the_workloads():
     p = host_plan(16384, 512)
     assert (p.variant, p.lanes_per_row, p.vectors_per_lane, p.row_slots) == (bnd.VARIANT_WAVE, 64, 1, 4)
     assert p.rows_per_trip == 16 and p.grid == 1024
-    p = host_plan(262144, 128, FP16)
-    assert (p.variant, p.lanes_per_row, p.row_slots) == (bnd.VARIANT_WAVE, 16, 4)
+    p = host_plan(262144, 128, FP16)        # several rows per slot: 2 KiB per wave, 2-wave workgroups
+    assert (p.variant, p.lanes_per_row, p.row_slots, p.block_threads) == (bnd.VARIANT_WAVE, 16, 2, 128)
+    assert p.rows_per_trip == 16 and p.grid == 262144 // 16
     p = host_plan(64, 256)
-    assert (p.lanes_per_row, p.row_slots) == (32, 4)
+    assert (p.lanes_per_row, p.row_slots, p.block_threads) == (32, 2, 128)
     p = host_plan(100, 1024)
     assert (p.lanes_per_row, p.vectors_per_lane, p.row_slots) == (64, 2, 2)
     p = host_plan(32768, 8192)
@@ -145,8 +146,8 @@ def test_planner_choices_for_the_workloads():
     assert (p.variant, p.block_threads, p.vectors_per_lane) == (bnd.VARIANT_BLOCK, 256, 2)
     assert (p.xcd_group, p.max_blocks_per_cu) == (16, 0)
     p = host_plan(4096, 16384, FP16)
-    assert (p.variant, p.block_threads, p.vectors_per_lane) == (bnd.VARIANT_BLOCK, 512, 4)
-    assert (p.xcd_group, p.max_blocks_per_cu) == (8, 2)
+    assert (p.variant, p.block_threads, p.vectors_per_lane) == (bnd.VARIANT_BLOCK, 1024, 2)
+    assert (p.xcd_group, p.max_blocks_per_cu) == (8, 0)
     p = host_plan(3, 49152)
     assert (p.block_threads, p.vectors_per_lane, p.max_blocks_per_cu) == (1024, 6, 0)
     for M, N in ((16384, 512), (262144, 128), (64, 256)):
@@ -286,3 +287,78 @@ def test_bwd_plans_that_do_not_fit_are_rejected():
         st = lib.rmsnorm_bwd_with_plan(X, W, DY, R, DX, DW, 100, 512, 0.0, BF16, ctypes.byref(p), WS,
                                        1 << 24, None)
         assert st == PLAN, (p.as_dict(), lib.rmsnorm_last_error().decode())
+
+
+# ---------------------------------------------------------------------------
+# Tuned dispatch and plan validation (host only)
+# ---------------------------------------------------------------------------
+@pytest.fixture
+def clean_tuned():
+    bnd.clear_tuned()
+    yield
+    bnd.clear_tuned()
+
+
+def test_plan_validate_matches_what_launches_accept():
+    p = bnd.plan_query(16384, 512, "bf16", cu_count=256)
+    v = bnd.plan_validate(16384, 512, "bf16", p.copy(row_slots=2, grid=2048), cu_count=256)
+    assert (v.rows_per_trip, v.trips, v.resident_grid) == (8, 1, 2048)
+    assert bnd.plan_validate(16384, 512, "bf16", p.copy(vectors_per_lane=7), cu_count=256) is None
+    assert bnd.plan_validate(16384, 512, "bf16", p, x_ptr=A + 2, cu_count=256) is None      # unaligned x
+    with pytest.raises(bnd.RmsnormError):
+        bnd.plan_validate(16384, 0, "bf16", p, cu_count=256)                                  # bad shape raises
+
+
+def test_tuned_plan_replaces_the_rule_for_exactly_its_shape(clean_tuned):
+    rule = bnd.plan_query(16384, 512, "bf16", cu_count=256)
+    tuned = rule.copy(row_slots=2, block_threads=128, grid=4096)
+    bnd.set_tuned(16384, 512, "bf16", tuned)
+    assert bnd.tuned_count() == 1
+    got = bnd.plan_query(16384, 512, "bf16", cu_count=256)
+    assert (got.row_slots, got.block_threads, got.grid) == (2, 128, 4096)
+    assert bnd.plan_query(16384, 512, "fp16", cu_count=256).row_slots == rule.row_slots   # other dtype
+    assert bnd.plan_query(16385, 512, "bf16", cu_count=256).block_threads == rule.block_threads
+    # a tuned plan that does not fit the call's pointers falls back to the rule, without an error
+    fb = bnd.plan_query(16384, 512, "bf16", x_ptr=A + 2, cu_count=256)
+    assert fb.variant == bnd.VARIANT_GENERIC and lib.rmsnorm_last_error() == b""
+    bnd.set_tuned(16384, 512, "bf16", tuned.copy(row_slots=4, block_threads=256, grid=1024))  # replace
+    assert bnd.tuned_count() == 1 and bnd.plan_query(16384, 512, "bf16", cu_count=256).row_slots == 4
+    bnd.clear_tuned()
+    assert bnd.tuned_count() == 0
+    assert bnd.plan_query(16384, 512, "bf16", cu_count=256).block_threads == rule.block_threads
+
+
+def test_tuned_plans_are_validated(clean_tuned):
+    rule = bnd.plan_query(4096, 512, "bf16", cu_count=256)
+    for bad in (rule.copy(vectors_per_lane=7), rule.copy(block_threads=96), rule.copy(grid=0),
+                rule.copy(lanes_per_row=16)):                  # 16 lanes x 1 vector do not cover 512 columns
+        with pytest.raises(bnd.RmsnormError) as e:
+            bnd.set_tuned(4096, 512, "bf16", bad)
+        assert e.value.status == PLAN
+    assert lib.rmsnorm_plan_set_tuned(0, 512, BF16, ctypes.byref(rule)) == SHAPE
+    assert lib.rmsnorm_plan_set_tuned(4096, 512, BF16, None) == NULL
+    assert bnd.tuned_count() == 0
+
+
+def test_load_tuned_reads_the_tuner_format(clean_tuned, tmp_path):
+    import json
+    rule = bnd.plan_query(8192, 3000, "bf16", cu_count=256)
+    plan = {f: getattr(rule, f) for f in bnd.PLAN_FIELDS}
+    plan["xcd_group"] = 4
+    path = tmp_path / "t.json"
+    path.write_text(json.dumps({"device": "test", "plans": [{"M": 8192, "N": 3000, "dtype": "bf16", "plan": plan}]}))
+    assert bnd.load_tuned(str(path)) == 1
+    assert bnd.plan_query(8192, 3000, "bf16", cu_count=256).xcd_group == 4
+
+
+def test_tuner_search_space_is_valid_and_contains_the_rule():
+    tune = pytest.importorskip("memory_bound_row_rmsnorm_amd.tune")
+    for M, N, dtype in ((16384, 512, "bf16"), (32768, 8192, "bf16"), (8192, 3000, "bf16"), (262144, 128, "fp16"),
+                        (4096, 16384, "fp16"), (100, 1000, "bf16")):
+        cands = tune.candidates(M, N, dtype, quick=True)
+        keys = {tuple(getattr(p, f) for f in bnd.PLAN_FIELDS) for p in cands}
+        assert len(keys) == len(cands) > 3
+        rule = bnd.plan_query(M, N, dtype, cu_count=256)
+        assert all(bnd.plan_validate(M, N, dtype, p, cu_count=256) is not None for p in cands)
+        fam = {p.variant for p in cands}
+        assert rule.variant in fam and bnd.VARIANT_GENERIC in fam
