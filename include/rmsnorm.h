@@ -14,17 +14,19 @@
  * offset 0.0 for Llama-style and 1.0 for Gemma3-style models; the mean
  * divides by the true width N; eps and offset are fp32; the per-row
  * reciprocal root is written out for a backward pass; y is cast to the
- * input dtype once, at the end).  x and w are read as bf16 or fp16, all
- * arithmetic is fp32 ("Rmsnorm Kernel Optimization", Key Optimizations and
- * Common Pitfalls: the sum of squares must not run in the 16-bit type),
+ * input dtype once, at the end).  x and w are read as bf16, fp16 or fp32,
+ * all arithmetic is fp32 ("Rmsnorm Kernel Optimization", Key Optimizations
+ * and Common Pitfalls: the sum of squares must not run in the 16-bit type),
  * the root is the hardware reciprocal square root, and y is rounded to the
- * input dtype with round-to-nearest-even.
+ * input dtype with round-to-nearest-even.  "Rmsnorm Kernel Optimization",
+ * Verification, writes the operation over the last dimension of a tensor of
+ * any rank: rmsnorm_fwd_ex takes such rows through a strided layout.
  *
  * Conventions shared by every entry point:
  *   - Pointers named x, w, y, rstd are DEVICE memory owned by the caller; the
  *     library never allocates, frees or synchronises.
- *   - x and y are contiguous row-major [M, N] of `dtype`; w is [N] of `dtype`;
- *     rstd is [M] fp32.
+ *   - x and y are contiguous row-major [M, N] of `dtype` (rmsnorm_fwd_ex: rows
+ *     placed by an rmsnorm_layout_t); w is [N] of `dtype`; rstd is [M] fp32.
  *   - y == x (exactly the same pointer) is allowed and normalises in place;
  *     any other overlap of y with x or w, or of rstd with x, w or y, is
  *     rejected.
@@ -48,14 +50,16 @@ extern "C" {
 /* Element type of x, w and y. */
 typedef enum rmsnorm_dtype {
     RMSNORM_BF16 = 0,
-    RMSNORM_FP16 = 1
+    RMSNORM_FP16 = 1,
+    RMSNORM_FP32 = 2     /* forward only */
 } rmsnorm_dtype_t;
 
 /* Status codes. */
 typedef enum rmsnorm_status {
     RMSNORM_OK = 0,
     RMSNORM_ERR_NULL = 1,     /* a required pointer is NULL (M > 0) */
-    RMSNORM_ERR_SHAPE = 2,    /* M < 0, N <= 0, or M*N*2 bytes overflows int64 */
+    RMSNORM_ERR_SHAPE = 2,    /* M < 0, N <= 0, M*N*4 bytes overflows int64, a bad layout,
+                                 or a workspace that is too small */
     RMSNORM_ERR_DTYPE = 3,    /* dtype is not an rmsnorm_dtype_t value */
     RMSNORM_ERR_SCALAR = 4,   /* eps < 0 or non-finite, or offset non-finite */
     RMSNORM_ERR_OVERLAP = 5,  /* buffers overlap other than y == x */
@@ -76,7 +80,8 @@ typedef enum rmsnorm_variant {
  * Launch plan: which kernel runs and how the rows are spread over the chip.
  *
  *   variant           RMSNORM_VARIANT_WAVE / _BLOCK / _GENERIC
- *   vec_elems         elements per lane access: 8 (16-byte loads and stores)
+ *   vec_elems         elements per lane access: 16 bytes' worth, 8 (bf16, fp16)
+ *                     or 4 (fp32),
  *                     for WAVE and BLOCK, 1 for GENERIC
  *   lanes_per_row     WAVE: lanes sharing one row (16, 32 or 64);
  *                     BLOCK and GENERIC: threads per row (= block_threads)
@@ -138,6 +143,36 @@ int rmsnorm_fwd(const void* x, const void* w, void* y, float* rstd,
                 int64_t M, int64_t N, float eps, float offset, int dtype, void* stream);
 
 /*
+ * Placement of rows in memory for rmsnorm_fwd_ex: the M rows form
+ * M / rows batches of `rows` rows; row m = b * rows + s (b the batch, s the
+ * row in it) of x starts at element  b * x_batch_stride + s * x_row_stride
+ * of x, and likewise for y.  A [B, S, N] tensor with strides (sB, sS, 1) is
+ * rows = S, row stride sS, batch stride sB; a 2-D [M, N] view with row
+ * stride ld is rows = 0 (one batch), row stride ld.  Strides count elements
+ * and must be >= 0.  Rows of x may overlap (x is only read: a row stride 0
+ * broadcasts one row); rows of y may not: y_row_stride >= N when a batch
+ * has several rows, and across batches either y_batch_stride >=
+ * (rows - 1) * y_row_stride + N (batch-major) or y_row_stride >=
+ * (batches - 1) * y_batch_stride + N with y_batch_stride >= N (row-major
+ * interleaved).  rows = 0 or rows >= M means one batch; otherwise M must
+ * be a multiple of rows.  Violations: RMSNORM_ERR_SHAPE.  Batches run as
+ * the launch grid's second dimension, and a plan (rmsnorm_plan_query_ex,
+ * or the caller's) describes one batch of `rows` rows; batches whose
+ * strides continue the row stride (batch stride = rows * row stride for
+ * both x and y) are treated as one batch of M rows.  The 16-byte
+ * kernels run when x, w and y are 16-byte aligned and every row starts
+ * 16-byte aligned (row and batch strides times the element size multiples
+ * of 16); N itself may be any width.  Otherwise the generic kernel runs.
+ */
+typedef struct rmsnorm_layout {
+    int64_t rows;
+    int64_t x_row_stride;
+    int64_t x_batch_stride;
+    int64_t y_row_stride;
+    int64_t y_batch_stride;
+} rmsnorm_layout_t;
+
+/*
  * Same as rmsnorm_fwd but with an explicit launch plan (from
  * rmsnorm_plan_query, possibly edited: variant, lanes_per_row,
  * vectors_per_lane, row_slots, block_threads, prefetch, xcd_group,
@@ -151,6 +186,19 @@ int rmsnorm_fwd_with_plan(const void* x, const void* w, void* y, float* rstd,
                           const rmsnorm_plan_t* plan, void* stream);
 
 /*
+ * The general forward: rmsnorm_fwd with
+ *   layout  row placement of x and y (NULL = contiguous [M, N]);
+ *   rstd    may be NULL (nothing is written: inference);
+ *   plan    NULL = the library's plan (tuned or rule), else as in
+ *           rmsnorm_fwd_with_plan.
+ * y == x in place needs the same layout for both.  Overlap checks use each
+ * operand's span, from its first row's start to its last row's end.
+ */
+int rmsnorm_fwd_ex(const void* x, const void* w, void* y, float* rstd,
+                   int64_t M, int64_t N, float eps, float offset, int dtype,
+                   const rmsnorm_layout_t* layout, const rmsnorm_plan_t* plan, void* stream);
+
+/*
  * The plan rmsnorm_fwd would use for these sizes and pointers (only their
  * alignment is looked at; they may be NULL, which counts as aligned).  The
  * plan itself is host logic.  cu_count only feeds resident_grid: cu_count > 0
@@ -162,6 +210,10 @@ int rmsnorm_fwd_with_plan(const void* x, const void* w, void* y, float* rstd,
 int rmsnorm_plan_query(int64_t M, int64_t N, int dtype,
                        const void* x, const void* w, const void* y,
                        int32_t cu_count, rmsnorm_plan_t* out);
+
+/* rmsnorm_plan_query for rmsnorm_fwd_ex's layouts (NULL = contiguous). */
+int rmsnorm_plan_query_ex(int64_t M, int64_t N, int dtype, const void* x, const void* w, const void* y,
+                          const rmsnorm_layout_t* layout, int32_t cu_count, rmsnorm_plan_t* out);
 
 /*
  * Compiled resources of the kernel a plan selects, read from the loaded code

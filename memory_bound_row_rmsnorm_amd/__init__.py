@@ -17,6 +17,7 @@ __all__ = [
     "rmsnorm_bwd", "rmsnorm_bwd_out", "bwd_plan_query", "bwd_workspace_size",
     "library_path", "version", "Plan", "RmsnormError",
     "plan_validate", "set_tuned", "clear_tuned", "tuned_count", "load_tuned",
+    "rmsnorm_fwd_ex", "plan_query_ex", "row_layout", "Layout",
 ]
 
 

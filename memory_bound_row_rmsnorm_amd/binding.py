@@ -16,8 +16,9 @@ LIBRARY = os.path.join(_HERE, "librmsnorm_mi355x.so")
 
 RMSNORM_BF16 = 0
 RMSNORM_FP16 = 1
-DTYPE_CODES = {torch.bfloat16: RMSNORM_BF16, torch.float16: RMSNORM_FP16}
-DTYPE_NAMES = {"bf16": RMSNORM_BF16, "fp16": RMSNORM_FP16}
+RMSNORM_FP32 = 2          # forward only
+DTYPE_CODES = {torch.bfloat16: RMSNORM_BF16, torch.float16: RMSNORM_FP16, torch.float32: RMSNORM_FP32}
+DTYPE_NAMES = {"bf16": RMSNORM_BF16, "fp16": RMSNORM_FP16, "fp32": RMSNORM_FP32}
 
 VARIANT_AUTO, VARIANT_WAVE, VARIANT_BLOCK, VARIANT_GENERIC = 0, 1, 2, 3
 VARIANT_NAMES = {VARIANT_WAVE: "wave", VARIANT_BLOCK: "block", VARIANT_GENERIC: "generic"}
@@ -30,7 +31,8 @@ STATUS = {
 
 # Every symbol include/rmsnorm.h declares.
 EXPORTED = (
-    "rmsnorm_fwd", "rmsnorm_fwd_with_plan", "rmsnorm_plan_query", "rmsnorm_plan_resources",
+    "rmsnorm_fwd", "rmsnorm_fwd_with_plan", "rmsnorm_fwd_ex", "rmsnorm_plan_query", "rmsnorm_plan_query_ex",
+    "rmsnorm_plan_resources",
     "rmsnorm_bwd", "rmsnorm_bwd_with_plan", "rmsnorm_bwd_plan_query", "rmsnorm_bwd_workspace_size",
     "rmsnorm_plan_validate", "rmsnorm_plan_set_tuned", "rmsnorm_plan_clear_tuned", "rmsnorm_plan_tuned_count",
     "rmsnorm_status_string", "rmsnorm_last_error", "rmsnorm_version",
@@ -75,6 +77,17 @@ class Plan(ctypes.Structure):
         return p
 
 
+class Layout(ctypes.Structure):
+    """rmsnorm_layout_t: rows per batch (0 = one batch) and element strides of x and y."""
+    _fields_ = [
+        ("rows", ctypes.c_int64),
+        ("x_row_stride", ctypes.c_int64),
+        ("x_batch_stride", ctypes.c_int64),
+        ("y_row_stride", ctypes.c_int64),
+        ("y_batch_stride", ctypes.c_int64),
+    ]
+
+
 def _load():
     if not os.path.exists(LIBRARY):
         raise ImportError(
@@ -89,6 +102,12 @@ def _load():
     lib.rmsnorm_fwd_with_plan.restype = i32
     lib.rmsnorm_plan_query.argtypes = [i64, i64, i32, vp, vp, vp, ctypes.c_int32, ctypes.POINTER(Plan)]
     lib.rmsnorm_plan_query.restype = i32
+    lib.rmsnorm_fwd_ex.argtypes = [vp, vp, vp, vp, i64, i64, f32, f32, i32, ctypes.POINTER(Layout),
+                                   ctypes.POINTER(Plan), vp]
+    lib.rmsnorm_fwd_ex.restype = i32
+    lib.rmsnorm_plan_query_ex.argtypes = [i64, i64, i32, vp, vp, vp, ctypes.POINTER(Layout), ctypes.c_int32,
+                                          ctypes.POINTER(Plan)]
+    lib.rmsnorm_plan_query_ex.restype = i32
     i32p = ctypes.POINTER(ctypes.c_int32)
     lib.rmsnorm_plan_resources.argtypes = [ctypes.POINTER(Plan), i32, i32p, i32p, i32p, i32p]
     lib.rmsnorm_plan_resources.restype = i32
@@ -138,10 +157,10 @@ def _check(status: int) -> None:
 def _dtype_code(dtype) -> int:
     if isinstance(dtype, str):
         if dtype not in DTYPE_NAMES:
-            raise ValueError(f"dtype must be 'bf16' or 'fp16', got {dtype!r}")
+            raise ValueError(f"dtype must be 'bf16', 'fp16' or 'fp32', got {dtype!r}")
         return DTYPE_NAMES[dtype]
     if dtype not in DTYPE_CODES:
-        raise ValueError(f"dtype must be torch.bfloat16 or torch.float16, got {dtype}")
+        raise ValueError(f"dtype must be torch.bfloat16, torch.float16 or torch.float32, got {dtype}")
     return DTYPE_CODES[dtype]
 
 
@@ -185,6 +204,78 @@ def rmsnorm_fwd_out(x: torch.Tensor, w: torch.Tensor, y: torch.Tensor, rstd: tor
             _check(lib.rmsnorm_fwd(*args, h))
         else:
             _check(lib.rmsnorm_fwd_with_plan(*args, ctypes.byref(plan), h))
+
+
+def row_layout(t: torch.Tensor):
+    """(M, N, rows, row_stride, batch_stride) of the rows of `t` over its last dimension.
+
+    The last dimension must have unit stride.  A 1-D or 2-D tensor is one batch of rows
+    (rows = 0) with t.stride(0) between rows; a tensor of higher rank is batches of
+    t.shape[-2] rows, its leading dimensions collapsing into one batch stride (raises
+    ValueError when they do not).
+    """
+    if t.dim() == 0:
+        raise ValueError("a 0-d tensor has no rows")
+    N = t.shape[-1]
+    if N > 1 and t.stride(-1) != 1:
+        raise ValueError("the last dimension must have unit stride")
+    if t.dim() == 1:
+        return 1, N, 0, N, 0
+    if t.dim() == 2:
+        return t.shape[0], N, 0, t.stride(0), 0
+    S, rs = t.shape[-2], t.stride(-2)
+    lead = [(n, st) for n, st in zip(t.shape[:-2], t.stride()[:-2]) if n != 1]
+    B = 1
+    for n, _ in lead:
+        B *= n
+    bs = lead[-1][1] if lead else 0
+    for (n0, s0), (n1, s1) in zip(lead, lead[1:]):
+        if s0 != s1 * n1:
+            raise ValueError(f"leading dimensions {tuple(t.shape[:-2])} with strides {tuple(t.stride()[:-2])} "
+                             "do not collapse into one batch stride")
+    return B * S, N, S, rs, bs
+
+
+def rmsnorm_fwd_ex(x: torch.Tensor, w: torch.Tensor, eps: float = 1e-6, offset: float = 0.0,
+                   want_rstd: bool = True, out: torch.Tensor | None = None, plan: Plan | None = None,
+                   stream=None):
+    """RMSNorm over the last dimension of x of any rank and strides (unit stride in the last
+    dimension), without copies: (y, rstd) with y shaped like x (or written into `out`) and rstd
+    float32 of shape x.shape[:-1], or None when want_rstd is False.  bf16, fp16 or fp32."""
+    if not (x.is_cuda and w.is_cuda) or x.device != w.device:
+        raise ValueError("x and w must be tensors on the same GPU")
+    if x.dtype != w.dtype:
+        raise ValueError(f"x is {x.dtype} but w is {w.dtype}; both must have the same dtype")
+    code = _dtype_code(x.dtype)
+    if w.dim() != 1 or w.shape[0] != x.shape[-1] or not w.is_contiguous():
+        raise ValueError(f"w must be contiguous with shape [{x.shape[-1]}], got {tuple(w.shape)}")
+    y = torch.empty_like(x) if out is None else out
+    if y.shape != x.shape or y.dtype != x.dtype or y.device != x.device:
+        raise ValueError("out must have x's shape, dtype and device")
+    M, N, rows, xrs, xbs = row_layout(x)
+    _, _, yrows, yrs, ybs = row_layout(y)
+    if x.dim() >= 3 and rows != yrows:
+        raise ValueError("x and out batch their rows differently")
+    lay = Layout(rows, xrs, xbs, yrs, ybs)
+    rstd = torch.empty(x.shape[:-1], dtype=torch.float32, device=x.device) if want_rstd else None
+    with torch.cuda.device(x.device):
+        _check(lib.rmsnorm_fwd_ex(x.data_ptr() or None, w.data_ptr() or None, y.data_ptr() or None,
+                                  rstd.data_ptr() if rstd is not None and rstd.numel() else None, M, N, eps,
+                                  offset, code, ctypes.byref(lay), ctypes.byref(plan) if plan is not None else None,
+                                  _stream_handle(stream)))
+    return y, rstd
+
+
+def plan_query_ex(x: torch.Tensor, w: torch.Tensor, out: torch.Tensor | None = None, cu_count: int = 0) -> Plan:
+    """The plan rmsnorm_fwd_ex uses for these tensors (one batch of rows)."""
+    y = x if out is None else out
+    M, N, rows, xrs, xbs = row_layout(x)
+    _, _, _, yrs, ybs = row_layout(y)
+    p = Plan()
+    _check(lib.rmsnorm_plan_query_ex(M, N, _dtype_code(x.dtype), x.data_ptr() or None, w.data_ptr() or None,
+                                     y.data_ptr() or None, ctypes.byref(Layout(rows, xrs, xbs, yrs, ybs)),
+                                     cu_count, ctypes.byref(p)))
+    return p
 
 
 def rmsnorm_fwd(x: torch.Tensor, w: torch.Tensor, eps: float = 1e-6, offset: float = 0.0,

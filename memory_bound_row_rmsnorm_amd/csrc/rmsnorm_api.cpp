@@ -118,31 +118,110 @@ bool ranges_overlap(const void* a, int64_t abytes, const void* b, int64_t bbytes
     return a0 < b0 + static_cast<uintptr_t>(bbytes) && b0 < a0 + static_cast<uintptr_t>(abytes);
 }
 
-int check_shape_dtype(int64_t M, int64_t N, int dtype) {
+int elem_size(int dtype) { return dtype == RMSNORM_FP32 ? 4 : 2; }
+int elems_per_vector(int dtype) { return 16 / elem_size(dtype); }
+
+// Forward calls take all three dtypes; the backward keeps to 16-bit ones.
+int check_shape_dtype(int64_t M, int64_t N, int dtype, bool forward = true) {
     if (M < 0) return fail(RMSNORM_ERR_SHAPE, "M must be >= 0");
     if (N <= 0) return fail(RMSNORM_ERR_SHAPE, "N must be >= 1");
-    if (M > 0 && N > INT64_MAX / 2 / M) return fail(RMSNORM_ERR_SHAPE, "M*N*2 bytes overflows int64");
-    if (dtype != RMSNORM_BF16 && dtype != RMSNORM_FP16) return fail(RMSNORM_ERR_DTYPE, "dtype must be RMSNORM_BF16 or RMSNORM_FP16");
+    if (M > 0 && N > INT64_MAX / 4 / M) return fail(RMSNORM_ERR_SHAPE, "M*N*4 bytes overflows int64");
+    if (dtype != RMSNORM_BF16 && dtype != RMSNORM_FP16 && !(forward && dtype == RMSNORM_FP32))
+        return fail(RMSNORM_ERR_DTYPE, forward ? "dtype must be RMSNORM_BF16, RMSNORM_FP16 or RMSNORM_FP32"
+                                               : "dtype must be RMSNORM_BF16 or RMSNORM_FP16");
+    return RMSNORM_OK;
+}
+
+// Row layout of x and y in elements, normalised: `rows` rows per batch,
+// M / rows batches.  Contiguous [M, N] is one batch with row stride N.
+struct Layout {
+    int64_t rows;
+    int64_t x_rs, x_bs, y_rs, y_bs;
+    int64_t batches(int64_t M) const { return rows > 0 ? M / rows : 0; }
+    // elements from the first element of row 0 to one past the last element of the last row
+    int64_t x_span(int64_t M, int64_t N) const { return span(M, N, x_rs, x_bs); }
+    int64_t y_span(int64_t M, int64_t N) const { return span(M, N, y_rs, y_bs); }
+    int64_t span(int64_t M, int64_t N, int64_t rs, int64_t bs) const {
+        if (M == 0) return 0;
+        return (batches(M) - 1) * bs + (rows - 1) * rs + N;
+    }
+};
+
+Layout contiguous_layout(int64_t M, int64_t N) { return Layout{M > 0 ? M : 1, N, M * N, N, M * N}; }
+
+// Checks a caller's layout and normalises it.  y's rows must not overlap one
+// another (the kernels write them concurrently): either batch-major
+// (y_batch_stride >= (rows - 1) * y_row_stride + N) or row-major interleaved
+// (y_row_stride >= (batches - 1) * y_batch_stride + N), with y_row_stride >= N
+// when a batch has several rows.  x's rows may overlap (x is only read).
+int normalise_layout(const rmsnorm_layout_t* L, int64_t M, int64_t N, Layout* out) {
+    if (!L) {
+        *out = contiguous_layout(M, N);
+        return RMSNORM_OK;
+    }
+    if (L->rows < 0) return fail(RMSNORM_ERR_SHAPE, "layout rows must be >= 0");
+    if (L->x_row_stride < 0 || L->x_batch_stride < 0 || L->y_row_stride < 0 || L->y_batch_stride < 0)
+        return fail(RMSNORM_ERR_SHAPE, "layout strides must be >= 0");
+    Layout o;
+    o.rows = (L->rows == 0 || L->rows >= M) ? (M > 0 ? M : 1) : L->rows;
+    if (M > 0 && M % o.rows != 0) return fail(RMSNORM_ERR_SHAPE, "M must be a multiple of layout rows");
+    o.x_rs = L->x_row_stride;
+    o.y_rs = L->y_row_stride;
+    const int64_t B = M > 0 ? M / o.rows : 1;
+    o.x_bs = B > 1 ? L->x_batch_stride : 0;
+    o.y_bs = B > 1 ? L->y_batch_stride : 0;
+    const int64_t lim = INT64_MAX / 4;
+    if (o.rows > 1 && o.y_rs < N) return fail(RMSNORM_ERR_SHAPE, "y rows overlap: y_row_stride < N");
+    if (o.x_rs > lim / (o.rows > 1 ? o.rows : 1) || o.y_rs > lim / (o.rows > 1 ? o.rows : 1) ||
+        o.x_bs > lim / B || o.y_bs > lim / B)
+        return fail(RMSNORM_ERR_SHAPE, "layout spans overflow int64");
+    if (B > 1) {
+        const bool batch_major = o.y_bs >= (o.rows - 1) * o.y_rs + N;
+        const bool interleaved = o.y_rs >= (B - 1) * o.y_bs + N && o.y_bs >= N;
+        if (!batch_major && !interleaved) return fail(RMSNORM_ERR_SHAPE, "y rows overlap across batches");
+    }
+    if (o.x_span(M, N) > lim || o.y_span(M, N) > lim) return fail(RMSNORM_ERR_SHAPE, "layout spans overflow int64");
+    if (B > 1 && o.x_bs == o.rows * o.x_rs && o.y_bs == o.rows * o.y_rs) {
+        // batches that continue each other's row stride are one batch
+        o.rows = M;
+        o.x_bs = 0;
+        o.y_bs = 0;
+    }
+    *out = o;
     return RMSNORM_OK;
 }
 
 int check_args(const void* x, const void* w, const void* y, const float* rstd, int64_t M, int64_t N,
-               float eps, float offset, int dtype) {
+               float eps, float offset, int dtype, const Layout& L, bool rstd_optional = false) {
     int st = check_shape_dtype(M, N, dtype);
     if (st != RMSNORM_OK) return st;
-    if (M > 0 && (!x || !w || !y || !rstd)) return fail(RMSNORM_ERR_NULL, "x, w, y and rstd must be non-NULL");
+    if (M > 0 && (!x || !w || !y || (!rstd && !rstd_optional)))
+        return fail(RMSNORM_ERR_NULL, rstd_optional ? "x, w and y must be non-NULL" : "x, w, y and rstd must be non-NULL");
     if (!std::isfinite(eps) || eps < 0.0f) return fail(RMSNORM_ERR_SCALAR, "eps must be finite and >= 0");
     if (!std::isfinite(offset)) return fail(RMSNORM_ERR_SCALAR, "offset must be finite");
     if (M == 0) return RMSNORM_OK;
-    const int64_t xb = M * N * 2, wb = N * 2, rb = M * 4;
-    if (x != y && ranges_overlap(x, xb, y, xb)) return fail(RMSNORM_ERR_OVERLAP, "y partially overlaps x");
-    if (ranges_overlap(y, xb, w, wb)) return fail(RMSNORM_ERR_OVERLAP, "y overlaps w");
-    if (ranges_overlap(rstd, rb, x, xb) || ranges_overlap(rstd, rb, y, xb) || ranges_overlap(rstd, rb, w, wb))
+    const int64_t es = elem_size(dtype);
+    const int64_t xb = L.x_span(M, N) * es, yb = L.y_span(M, N) * es, wb = N * es, rb = M * 4;
+    const bool same_layout = L.x_rs == L.y_rs && L.x_bs == L.y_bs;
+    if (x == y ? !same_layout : ranges_overlap(x, xb, y, yb))
+        return fail(RMSNORM_ERR_OVERLAP, "y overlaps x (in place needs y == x with the same layout)");
+    if (ranges_overlap(y, yb, w, wb)) return fail(RMSNORM_ERR_OVERLAP, "y overlaps w");
+    if (rstd && (ranges_overlap(rstd, rb, x, xb) || ranges_overlap(rstd, rb, y, yb) || ranges_overlap(rstd, rb, w, wb)))
         return fail(RMSNORM_ERR_OVERLAP, "rstd overlaps x, y or w");
     return RMSNORM_OK;
 }
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// The 16-byte kernels need 16-byte aligned x, w and y and row (and batch)
+// strides that keep every row 16-byte aligned; N itself may be anything (a
+// final partial vector moves element by element).
+bool vector_ok(const void* x, const void* w, const void* y, int dtype, const Layout& L, int64_t M) {
+    const int64_t es = elem_size(dtype);
+    const bool rows_ok = (L.x_rs * es) % 16 == 0 && (L.y_rs * es) % 16 == 0;
+    const bool batches_ok = L.batches(M) <= 1 || ((L.x_bs * es) % 16 == 0 && (L.y_bs * es) % 16 == 0);
+    return aligned16(x) && aligned16(w) && aligned16(y) && rows_ok && batches_ok;
+}
 
 // ---------------------------------------------------------------------------
 // Kernel lookup.
@@ -164,9 +243,9 @@ const KernelEntry* find_kernel(int variant, int dtype, int lanes, int vpl, int s
 
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
-// Fill the derived fields and check the plan against the call.  Host only.
-int finish_plan(rmsnorm_plan_t* p, int64_t M, int64_t N, int dtype, const void* x, const void* w,
-                const void* y, const KernelEntry** kernel) {
+// Fill the derived fields and check the plan against the call (`vec`: the
+// call's pointers and strides suit the 16-byte kernels).  Host only.
+int finish_plan(rmsnorm_plan_t* p, int64_t M, int64_t N, int dtype, bool vec, const KernelEntry** kernel) {
     if (p->block_threads < 64 || p->block_threads > 1024 || p->block_threads % 64 != 0)
         return fail(RMSNORM_ERR_PLAN, "block_threads must be a multiple of 64 in [64, 1024]");
     if (p->grid < 1 || p->grid > 0x7FFFFFFF) return fail(RMSNORM_ERR_PLAN, "grid must be in [1, 2^31)");
@@ -183,16 +262,16 @@ int finish_plan(rmsnorm_plan_t* p, int64_t M, int64_t N, int dtype, const void* 
         p->rows_per_trip = 1;
         k = find_kernel(RMSNORM_VARIANT_GENERIC, dtype, 0, 0, 1, false);
     } else if (p->variant == RMSNORM_VARIANT_WAVE || p->variant == RMSNORM_VARIANT_BLOCK) {
-        if (N % 8 != 0) return fail(RMSNORM_ERR_PLAN, "16-byte kernels need N % 8 == 0");
-        if (!aligned16(x) || !aligned16(w) || !aligned16(y))
-            return fail(RMSNORM_ERR_PLAN, "16-byte kernels need 16-byte aligned x, w and y");
-        p->vec_elems = 8;
+        if (!vec)
+            return fail(RMSNORM_ERR_PLAN, "16-byte kernels need 16-byte aligned x, w and y and 16-byte aligned rows");
+        const int epv = elems_per_vector(dtype);
+        p->vec_elems = epv;
         if (p->prefetch != 0 && p->prefetch != 1) return fail(RMSNORM_ERR_PLAN, "prefetch must be 0 or 1");
         if (p->variant == RMSNORM_VARIANT_WAVE) {
             k = find_kernel(RMSNORM_VARIANT_WAVE, dtype, p->lanes_per_row, p->vectors_per_lane, p->row_slots,
                             p->prefetch != 0);
             if (k) {
-                const int64_t cap = static_cast<int64_t>(p->lanes_per_row) * p->vectors_per_lane * 8;
+                const int64_t cap = static_cast<int64_t>(p->lanes_per_row) * p->vectors_per_lane * epv;
                 if (cap < N) return fail(RMSNORM_ERR_PLAN, "wave plan does not cover N");
                 p->rows_per_trip = static_cast<int64_t>(p->block_threads / 64) * (64 / p->lanes_per_row) * p->row_slots;
             }
@@ -201,7 +280,7 @@ int finish_plan(rmsnorm_plan_t* p, int64_t M, int64_t N, int dtype, const void* 
             p->lanes_per_row = p->block_threads;
             k = find_kernel(RMSNORM_VARIANT_BLOCK, dtype, 0, p->vectors_per_lane, 1, p->prefetch != 0);
             if (k) {
-                const int64_t cap = static_cast<int64_t>(p->block_threads) * p->vectors_per_lane * 8;
+                const int64_t cap = static_cast<int64_t>(p->block_threads) * p->vectors_per_lane * epv;
                 if (cap < N) return fail(RMSNORM_ERR_PLAN, "block plan does not cover N");
                 p->rows_per_trip = 1;
             }
@@ -210,6 +289,8 @@ int finish_plan(rmsnorm_plan_t* p, int64_t M, int64_t N, int dtype, const void* 
         return fail(RMSNORM_ERR_PLAN, "unknown variant");
     }
     if (!k) return fail(RMSNORM_ERR_PLAN, "no compiled kernel for this plan");
+    if (!k->tails && N % p->vec_elems != 0)
+        return fail(RMSNORM_ERR_PLAN, "this kernel has no tail path: N must be a multiple of vec_elems");
     p->trips = M > 0 ? ceil_div(ceil_div(M, p->rows_per_trip), p->grid) : 0;
     if (kernel) *kernel = k;
     return RMSNORM_OK;
@@ -218,41 +299,41 @@ int finish_plan(rmsnorm_plan_t* p, int64_t M, int64_t N, int dtype, const void* 
 // Vectors per lane the block and wave families are compiled for (more would
 // not fit the 128 VGPRs a 1024-thread workgroup allows without spilling).
 constexpr int kWaveSlots[] = {8, 4, 2, 1};
-constexpr int64_t kMaxVectorN = 1024LL * 6 * 8;   // widest row the 16-byte kernels hold
+constexpr int64_t kMaxVectors = 1024LL * 6;       // widest row the 16-byte kernels hold, in vectors
 constexpr int64_t kMaxGrid = 0x7FFFFFFF;
 constexpr int64_t kWaveBytesInFlight = 4096;      // row bytes one wave loads per trip
 constexpr int64_t kWaveBytesInFlightMultiRow = 2048;   // the same when a slot holds several rows
 constexpr int64_t kXcdGroupBytes = 128 * 1024;    // consecutive row bytes per XCD (block family)
 constexpr int64_t kBytesInFlightPerCu = 64 * 1024; // row bytes resident per compute unit (block family)
 
-// Choose family and geometry (host only; no device needed).  Rules measured
-// on MI355X with inputs cold in HBM:
-//  * rows of at most 1024 elements: the wave family, 16/32/64 lanes per row
-//    so that a row segment is one 16-byte vector per lane (two at 1024),
-//    and enough rows per wave for about 4 KiB of loads per trip;
-//  * longer rows: the block family with 256 threads up to 12288 elements,
-//    512 up to 24576, 1024 beyond, each thread holding ceil(N/8/threads)
-//    vectors;
-//  * N not a multiple of 8, a row wider than 49152, or a pointer not 16-byte
-//    aligned: the generic kernel;
+// Choose family and geometry (host only; no device needed).  A row is
+// nvec = ceil(N / EPV) 16-byte vectors (EPV = 8 for bf16/fp16, 4 for fp32).
+// Rules measured on MI355X with inputs cold in HBM:
+//  * rows of at most 128 vectors: the wave family, 16/32/64 lanes per row
+//    so that a row segment is one 16-byte vector per lane (two at 128), and
+//    enough rows per wave for about 4 KiB of loads per trip (2 KiB in 2-wave
+//    workgroups when a slot holds several rows);
+//  * longer rows: the block family with 256 threads up to 1536 vectors and
+//    1024 beyond, each thread holding ceil(nvec / threads) vectors;
+//  * pointers or row strides that are not 16-byte aligned, or a row wider
+//    than 6144 vectors: the generic kernel;
 //  * one trip per workgroup (grid = row groups): launching every row group
 //    measured faster than a grid of resident workgroups looping over rows on
 //    every shape tried;
 //  * block family: consecutive rows grouped on one XCD, about 128 KiB per
-//    group (xcd_group: 8 rows at N = 8192, 16 at N = 3000), and at most about
-//    64 KiB of rows resident per compute unit (max_blocks_per_cu 4 at
-//    N = 8192); together 5-6% faster on 32768 x 8192, 4% on 8192 x 3000.
-int choose_plan(int64_t M, int64_t N, const void* x, const void* w, const void* y, int dtype,
-                rmsnorm_plan_t* p) {
+//    group (xcd_group: 8 rows at 16 KiB rows, 16 at 6000-byte rows), and at
+//    most about 64 KiB of rows resident per compute unit (max_blocks_per_cu
+//    4 at 16 KiB rows); together 5-6% faster on 32768 x 8192, 4% on
+//    8192 x 3000.
+int choose_plan(int64_t M, int64_t N, int dtype, bool vec, rmsnorm_plan_t* p) {
     std::memset(p, 0, sizeof(*p));
-    const bool vec_ok = (N % 8 == 0) && aligned16(x) && aligned16(w) && aligned16(y) &&
-                        N <= kMaxVectorN;
-    if (!vec_ok) {
+    const int64_t es = elem_size(dtype);
+    const int64_t nvec = ceil_div(N, elems_per_vector(dtype));
+    if (!vec || nvec > kMaxVectors) {
         p->variant = RMSNORM_VARIANT_GENERIC;
         p->block_threads = N >= 1024 ? 256 : (N >= 256 ? 128 : 64);
         p->row_slots = 1;
-    } else if (N / 8 <= 128) {
-        const int64_t nvec = N / 8;
+    } else if (nvec <= 128) {
         p->variant = RMSNORM_VARIANT_WAVE;
         p->lanes_per_row = nvec <= 16 ? 16 : (nvec <= 32 ? 32 : 64);
         p->vectors_per_lane = static_cast<int>(ceil_div(nvec, p->lanes_per_row));
@@ -262,7 +343,7 @@ int choose_plan(int64_t M, int64_t N, const void* x, const void* w, const void* 
         const bool multi_row = p->lanes_per_row < 64;
         p->block_threads = multi_row ? kWaveBlockThreadsMultiRow : kWaveBlockThreads;
         const int64_t budget = multi_row ? kWaveBytesInFlightMultiRow : kWaveBytesInFlight;
-        const int64_t per_slot = N * 2 * (64 / p->lanes_per_row);
+        const int64_t per_slot = N * es * (64 / p->lanes_per_row);
         p->row_slots = 1;
         for (int s : kWaveSlots) {
             if (s * per_slot <= budget &&
@@ -272,13 +353,20 @@ int choose_plan(int64_t M, int64_t N, const void* x, const void* w, const void* 
             }
         }
     } else {
-        const int64_t nvec = N / 8;
         p->variant = RMSNORM_VARIANT_BLOCK;
         p->row_slots = 1;
         // 256 threads up to 6 vectors each; wider rows take 1024-thread
         // workgroups (4096 x 16384: 47.5 us against 49.5 us with 512 x 4)
         p->block_threads = nvec <= 256 * 6 ? 256 : 1024;
         p->vectors_per_lane = static_cast<int>(ceil_div(nvec, p->block_threads));
+        // rows wider than the compiled instances hold (or a ragged width the
+        // widest ones have no tail path for) take the generic kernel
+        const KernelEntry* k = find_kernel(RMSNORM_VARIANT_BLOCK, dtype, 0, p->vectors_per_lane, 1, false);
+        if (!k || (!k->tails && N % elems_per_vector(dtype) != 0)) {
+            p->variant = RMSNORM_VARIANT_GENERIC;
+            p->block_threads = 256;
+            p->vectors_per_lane = 0;
+        }
     }
     int64_t rows_per_trip = 1;
     if (p->variant == RMSNORM_VARIANT_WAVE)
@@ -289,7 +377,7 @@ int choose_plan(int64_t M, int64_t N, const void* x, const void* w, const void* 
     p->max_blocks_per_cu = 0;
     if (p->variant == RMSNORM_VARIANT_BLOCK) {
         // about 128 KiB of consecutive rows per XCD (a power of two, at least 8 rows)
-        const int64_t row_bytes = N * 2;
+        const int64_t row_bytes = N * es;
         int g = 8;
         while (g < 64 && row_bytes * g * 3 < kXcdGroupBytes * 2) g *= 2;  // nearest power of two
         p->xcd_group = g;
@@ -325,31 +413,45 @@ int resident_grid(const rmsnorm_plan_t* p, const KernelEntry* k, int cu_count, i
     return RMSNORM_OK;
 }
 
+// Launch one plan over every batch of the layout: grid (plan.grid, batches),
+// at most kMaxGridY batches per launch, each launch's pointers moved to its
+// first batch.  M here is the rows of one batch.
+constexpr int64_t kMaxGridY = 65535;
+
 int launch(const KernelEntry* k, const rmsnorm_plan_t* p, const void* x, const void* w, void* y,
-           float* rstd, int64_t M, int64_t N, float eps, float offset, int lds_per_cu, void* stream) {
+           float* rstd, int64_t M, int64_t N, float eps, float offset, int dtype, const Layout& L,
+           int64_t batches, int lds_per_cu, void* stream) {
     // occupancy cap: (cap + 1) workgroups of this much LDS do not fit a unit
     size_t dyn_lds = 0;
     if (p->max_blocks_per_cu > 0 && lds_per_cu > 0)
         dyn_lds = static_cast<size_t>(lds_per_cu / (p->max_blocks_per_cu + 1) + 1);
-    KernelArgs a;
-    a.x = x;
-    a.w = w;
-    a.y = y;
-    a.rstd = rstd;
-    a.M = M;
-    a.N = N;
-    a.inv_n = static_cast<float>(1.0 / static_cast<double>(N));
-    a.eps = eps;
-    a.offset = offset;
-    a.xcd_group = p->xcd_group;
-    a.grid = p->grid;
-    a.threads = p->block_threads;
-    void* args[] = {&a};
-    hipError_t e = hipLaunchKernel(k->func, dim3(static_cast<unsigned>(p->grid)),
-                                   dim3(static_cast<unsigned>(p->block_threads)), args, dyn_lds,
-                                   static_cast<hipStream_t>(stream));
-    if (e != hipSuccess)
-        return fail(RMSNORM_ERR_HIP, std::string("hipLaunchKernel(") + k->name + "): " + hipGetErrorString(e));
+    const int64_t es = elem_size(dtype);
+    for (int64_t b0 = 0; b0 < batches; b0 += kMaxGridY) {
+        const int64_t nb = std::min(batches - b0, kMaxGridY);
+        KernelArgs a;
+        a.x = static_cast<const char*>(x) + b0 * L.x_bs * es;
+        a.w = w;
+        a.y = static_cast<char*>(y) + b0 * L.y_bs * es;
+        a.rstd = rstd != nullptr ? rstd + b0 * M : nullptr;
+        a.M = M;
+        a.N = N;
+        a.inv_n = static_cast<float>(1.0 / static_cast<double>(N));
+        a.eps = eps;
+        a.offset = offset;
+        a.xcd_group = p->xcd_group;
+        a.grid = p->grid;
+        a.threads = p->block_threads;
+        a.x_rs = L.x_rs;
+        a.y_rs = L.y_rs;
+        a.x_bs = L.x_bs;
+        a.y_bs = L.y_bs;
+        void* args[] = {&a};
+        hipError_t e = hipLaunchKernel(k->func, dim3(static_cast<unsigned>(p->grid), static_cast<unsigned>(nb)),
+                                       dim3(static_cast<unsigned>(p->block_threads)), args, dyn_lds,
+                                       static_cast<hipStream_t>(stream));
+        if (e != hipSuccess)
+            return fail(RMSNORM_ERR_HIP, std::string("hipLaunchKernel(") + k->name + "): " + hipGetErrorString(e));
+    }
     return RMSNORM_OK;
 }
 
@@ -386,7 +488,7 @@ int64_t bwd_wave_lds(const rmsnorm_plan_t* p, int64_t N) {
 
 int check_bwd_args(const void* x, const void* w, const void* dy, const float* rstd, const void* dx,
                    const float* dw, int64_t M, int64_t N, float offset, int dtype) {
-    int st = check_shape_dtype(M, N, dtype);
+    int st = check_shape_dtype(M, N, dtype, false);
     if (st != RMSNORM_OK) return st;
     if (!dw) return fail(RMSNORM_ERR_NULL, "dw must be non-NULL");
     if (M > 0 && (!x || !w || !dy || !rstd || !dx))
@@ -605,17 +707,48 @@ bool tuned_plan(int64_t M, int64_t N, int dtype, rmsnorm_plan_t* out) {
     return true;
 }
 
-int select_plan(int64_t M, int64_t N, const void* x, const void* w, const void* y, int dtype,
-                rmsnorm_plan_t* p, const KernelEntry** k) {
+int select_plan(int64_t M, int64_t N, int dtype, bool vec, rmsnorm_plan_t* p, const KernelEntry** k) {
     rmsnorm_plan_t t;
-    if (tuned_plan(M, N, dtype, &t) && finish_plan(&t, M, N, dtype, x, w, y, k) == RMSNORM_OK) {
+    if (tuned_plan(M, N, dtype, &t) && finish_plan(&t, M, N, dtype, vec, k) == RMSNORM_OK) {
         *p = t;
         return RMSNORM_OK;
     }
     g_last_error.clear();
-    int st = choose_plan(M, N, x, w, y, dtype, p);
-    if (st == RMSNORM_OK) st = finish_plan(p, M, N, dtype, x, w, y, k);
+    int st = choose_plan(M, N, dtype, vec, p);
+    if (st == RMSNORM_OK) st = finish_plan(p, M, N, dtype, vec, k);
     return st;
+}
+
+// Every forward entry point: checks, plan (the caller's, a tuned one, or the
+// rule), launch.
+int fwd_common(const void* x, const void* w, void* y, float* rstd, int64_t M, int64_t N, float eps,
+               float offset, int dtype, const rmsnorm_layout_t* layout, const rmsnorm_plan_t* plan,
+               bool plan_required, bool rstd_optional, void* stream) {
+    int st = check_shape_dtype(M, N, dtype);
+    if (st != RMSNORM_OK) return st;
+    Layout L;
+    st = normalise_layout(layout, M, N, &L);
+    if (st != RMSNORM_OK) return st;
+    st = check_args(x, w, y, rstd, M, N, eps, offset, dtype, L, rstd_optional);
+    if (st != RMSNORM_OK) return st;
+    if (plan_required && !plan) return fail(RMSNORM_ERR_NULL, "plan must be non-NULL");
+    const bool vec = vector_ok(x, w, y, dtype, L, M);
+    const int64_t Mb = M > 0 ? L.rows : 0;    // plans cover one batch
+    rmsnorm_plan_t p;
+    const KernelEntry* k = nullptr;
+    if (plan) {
+        p = *plan;
+        st = finish_plan(&p, Mb, N, dtype, vec, &k);
+        if (st != RMSNORM_OK || M == 0) return st;
+    } else {
+        if (M == 0) return RMSNORM_OK;
+        st = select_plan(Mb, N, dtype, vec, &p, &k);
+        if (st != RMSNORM_OK) return st;
+    }
+    int cu = 0, lds = 0;
+    st = device_info(&cu, &lds);  // gfx950 check, unit count and LDS (cached per device)
+    if (st != RMSNORM_OK) return st;
+    return launch(k, &p, x, w, y, rstd, Mb, N, eps, offset, dtype, L, L.batches(M), lds, stream);
 }
 
 }  // namespace
@@ -625,47 +758,43 @@ extern "C" {
 int rmsnorm_fwd(const void* x, const void* w, void* y, float* rstd, int64_t M, int64_t N, float eps,
                 float offset, int dtype, void* stream) {
     g_last_error.clear();
-    int st = check_args(x, w, y, rstd, M, N, eps, offset, dtype);
-    if (st != RMSNORM_OK || M == 0) return st;
-    rmsnorm_plan_t p;
-    const KernelEntry* k = nullptr;
-    st = select_plan(M, N, x, w, y, dtype, &p, &k);
-    if (st != RMSNORM_OK) return st;
-    int cu = 0, lds = 0;
-    st = device_info(&cu, &lds);  // gfx950 check, unit count and LDS (cached per device)
-    if (st != RMSNORM_OK) return st;
-    return launch(k, &p, x, w, y, rstd, M, N, eps, offset, lds, stream);
+    return fwd_common(x, w, y, rstd, M, N, eps, offset, dtype, nullptr, nullptr, false, false, stream);
 }
 
 int rmsnorm_fwd_with_plan(const void* x, const void* w, void* y, float* rstd, int64_t M, int64_t N,
                           float eps, float offset, int dtype, const rmsnorm_plan_t* plan, void* stream) {
     g_last_error.clear();
-    int st = check_args(x, w, y, rstd, M, N, eps, offset, dtype);
-    if (st != RMSNORM_OK) return st;
-    if (!plan) return fail(RMSNORM_ERR_NULL, "plan must be non-NULL");
-    rmsnorm_plan_t p = *plan;
-    const KernelEntry* k = nullptr;
-    st = finish_plan(&p, M, N, dtype, x, w, y, &k);
-    if (st != RMSNORM_OK || M == 0) return st;
-    int cu = 0, lds = 0;
-    st = device_info(&cu, &lds);  // gfx950 check, unit count and LDS (cached per device)
-    if (st != RMSNORM_OK) return st;
-    return launch(k, &p, x, w, y, rstd, M, N, eps, offset, lds, stream);
+    return fwd_common(x, w, y, rstd, M, N, eps, offset, dtype, nullptr, plan, true, false, stream);
 }
 
-int rmsnorm_plan_query(int64_t M, int64_t N, int dtype, const void* x, const void* w, const void* y,
-                       int32_t cu_count, rmsnorm_plan_t* out) {
+int rmsnorm_fwd_ex(const void* x, const void* w, void* y, float* rstd, int64_t M, int64_t N, float eps,
+                   float offset, int dtype, const rmsnorm_layout_t* layout, const rmsnorm_plan_t* plan,
+                   void* stream) {
+    g_last_error.clear();
+    return fwd_common(x, w, y, rstd, M, N, eps, offset, dtype, layout, plan, false, true, stream);
+}
+
+int rmsnorm_plan_query_ex(int64_t M, int64_t N, int dtype, const void* x, const void* w, const void* y,
+                          const rmsnorm_layout_t* layout, int32_t cu_count, rmsnorm_plan_t* out) {
     g_last_error.clear();
     if (!out) return fail(RMSNORM_ERR_NULL, "out must be non-NULL");
     int st = check_shape_dtype(M, N, dtype);
     if (st != RMSNORM_OK) return st;
+    Layout L;
+    st = normalise_layout(layout, M, N, &L);
+    if (st != RMSNORM_OK) return st;
     rmsnorm_plan_t p;
     const KernelEntry* k = nullptr;
-    st = select_plan(M, N, x, w, y, dtype, &p, &k);
+    st = select_plan(M > 0 ? L.rows : 0, N, dtype, vector_ok(x, w, y, dtype, L, M), &p, &k);
     if (st == RMSNORM_OK) st = resident_grid(&p, k, cu_count, &p.resident_grid);
     if (st != RMSNORM_OK) return st;
     *out = p;
     return RMSNORM_OK;
+}
+
+int rmsnorm_plan_query(int64_t M, int64_t N, int dtype, const void* x, const void* w, const void* y,
+                       int32_t cu_count, rmsnorm_plan_t* out) {
+    return rmsnorm_plan_query_ex(M, N, dtype, x, w, y, nullptr, cu_count, out);
 }
 
 int rmsnorm_plan_validate(int64_t M, int64_t N, int dtype, const void* x, const void* w, const void* y,
@@ -676,7 +805,7 @@ int rmsnorm_plan_validate(int64_t M, int64_t N, int dtype, const void* x, const 
     if (st != RMSNORM_OK) return st;
     rmsnorm_plan_t p = *plan;
     const KernelEntry* k = nullptr;
-    st = finish_plan(&p, M, N, dtype, x, w, y, &k);
+    st = finish_plan(&p, M, N, dtype, vector_ok(x, w, y, dtype, contiguous_layout(M, N), M), &k);
     if (st == RMSNORM_OK) st = resident_grid(&p, k, cu_count, &p.resident_grid);
     if (st != RMSNORM_OK) return st;
     *out = p;
@@ -687,7 +816,8 @@ int rmsnorm_plan_resources(const rmsnorm_plan_t* plan, int dtype, int32_t* vgprs
                            int32_t* lds_bytes, int32_t* scratch) {
     g_last_error.clear();
     if (!plan) return fail(RMSNORM_ERR_NULL, "plan must be non-NULL");
-    if (dtype != RMSNORM_BF16 && dtype != RMSNORM_FP16) return fail(RMSNORM_ERR_DTYPE, "bad dtype");
+    if (dtype != RMSNORM_BF16 && dtype != RMSNORM_FP16 && dtype != RMSNORM_FP32)
+        return fail(RMSNORM_ERR_DTYPE, "bad dtype");
     const KernelEntry* k = nullptr;
     const bool pf = plan->prefetch != 0;
     if (plan->variant == RMSNORM_VARIANT_GENERIC) k = find_kernel(RMSNORM_VARIANT_GENERIC, dtype, 0, 0, 1, false);
@@ -711,7 +841,7 @@ int rmsnorm_bwd_plan_query(int64_t M, int64_t N, int dtype, const void* x, const
                            int32_t cu_count, rmsnorm_plan_t* out) {
     g_last_error.clear();
     if (!out) return fail(RMSNORM_ERR_NULL, "out must be non-NULL");
-    int st = check_shape_dtype(M, N, dtype);
+    int st = check_shape_dtype(M, N, dtype, false);
     if (st != RMSNORM_OK) return st;
     rmsnorm_plan_t p;
     const KernelEntry* k = nullptr;
@@ -727,7 +857,7 @@ int rmsnorm_bwd_workspace_size(int64_t M, int64_t N, int dtype, const void* x, c
                                int64_t* bytes) {
     g_last_error.clear();
     if (!bytes) return fail(RMSNORM_ERR_NULL, "bytes must be non-NULL");
-    int st = check_shape_dtype(M, N, dtype);
+    int st = check_shape_dtype(M, N, dtype, false);
     if (st != RMSNORM_OK) return st;
     rmsnorm_plan_t p;
     choose_bwd_plan(M, N, x, dx, dy, dx, dtype, &p);
@@ -764,7 +894,8 @@ int rmsnorm_plan_set_tuned(int64_t M, int64_t N, int dtype, const rmsnorm_plan_t
     if (M == 0) return fail(RMSNORM_ERR_SHAPE, "a tuned plan needs M > 0");
     rmsnorm_plan_t p = *plan;
     const KernelEntry* k = nullptr;
-    st = finish_plan(&p, M, N, dtype, nullptr, nullptr, nullptr, &k);  // aligned pointers
+    st = finish_plan(&p, M, N, dtype, vector_ok(nullptr, nullptr, nullptr, dtype, contiguous_layout(M, N), M),
+                     &k);  // aligned pointers
     if (st != RMSNORM_OK) return st;
     std::lock_guard<std::mutex> lock(g_tuned_mu);
     g_tuned[std::make_tuple(M, N, dtype)] = p;

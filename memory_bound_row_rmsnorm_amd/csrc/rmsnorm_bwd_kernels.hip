@@ -414,12 +414,12 @@ __global__ __launch_bounds__(256) void rmsnorm_dw_reduce(const float* __restrict
 // Instance table.
 // ---------------------------------------------------------------------------
 #define RMS_BWD_WAVE(D, DT, L, V, S, P)                                                        \
-    {RMSNORM_VARIANT_WAVE, DT, L, V, S, P,                                                     \
+    {RMSNORM_VARIANT_WAVE, DT, L, V, S, P, false,                                                     \
      reinterpret_cast<const void*>(&rmsnorm_bwd_wave<D, L, V, S, P>),                          \
      "rmsnorm_bwd_wave<" #D "," #L "," #V "," #S "," #P ">"}
 #define RMS_BWD_WAVE2(D, DT, L, V, S) RMS_BWD_WAVE(D, DT, L, V, S, false), RMS_BWD_WAVE(D, DT, L, V, S, true)
 #define RMS_BWD_BLOCK(D, DT, V, P)                                                             \
-    {RMSNORM_VARIANT_BLOCK, DT, 0, V, 1, P,                                                    \
+    {RMSNORM_VARIANT_BLOCK, DT, 0, V, 1, P, false,                                                    \
      reinterpret_cast<const void*>(&rmsnorm_bwd_block<D, V, P>),                               \
      "rmsnorm_bwd_block<" #D "," #V "," #P ">"}
 // Only instances that fit 128 VGPRs without scratch: the block family holds
@@ -433,7 +433,7 @@ __global__ __launch_bounds__(256) void rmsnorm_dw_reduce(const float* __restrict
     RMS_BWD_WAVE(D, DT, 64, 2, 2, false),                                                      \
     RMS_BWD_BLOCK(D, DT, 1, false), RMS_BWD_BLOCK(D, DT, 1, true),                             \
     RMS_BWD_BLOCK(D, DT, 2, false), RMS_BWD_BLOCK(D, DT, 2, true),                             \
-    {RMSNORM_VARIANT_GENERIC, DT, 0, 0, 1, false,                                              \
+    {RMSNORM_VARIANT_GENERIC, DT, 0, 0, 1, false, false,                                              \
      reinterpret_cast<const void*>(&rmsnorm_bwd_generic<D>), "rmsnorm_bwd_generic<" #D ">"}
 
 namespace rmsnorm_impl {

@@ -14,14 +14,34 @@ typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 
 // ---------------------------------------------------------------------------
-// Element formats.  Each packs two 16-bit elements per 32-bit word, low half
-// first (the memory order of a little-endian row).  Widening is exact; the
-// narrowing conversion rounds to nearest even and keeps subnormals (the
-// compiler emits the hardware converts: v_cvt_pk_bf16_f32 on gfx950 for
-// bf16, v_cvt_f16_f32 for fp16, both honouring the round-to-nearest-even
-// mode; no round-toward-zero packing instruction is used).
+// Element formats.  A 16-byte vector holds EPV elements: eight 16-bit ones,
+// two per 32-bit word with the low half first (the memory order of a
+// little-endian row), or four fp32 ones.  widen() is exact; narrow() and
+// round1() round to nearest even and keep subnormals (the compiler emits the
+// hardware converts: v_cvt_pk_bf16_f32 on gfx950 for bf16, v_cvt_f16_f32 for
+// fp16, both honouring the round-to-nearest-even mode; no round-toward-zero
+// packing instruction is used).  fp32 needs no conversion at all.
 // ---------------------------------------------------------------------------
-struct BF16 {
+template <class D>
+struct Packed16 {
+    static constexpr int EPV = 8;
+    typedef uint16_t elem_t;
+    static __device__ __forceinline__ void widen(const u32x4 q, float (&f)[EPV]) {
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            f[2 * k] = D::lo(q[k]);
+            f[2 * k + 1] = D::hi(q[k]);
+        }
+    }
+    static __device__ __forceinline__ u32x4 narrow(const float (&f)[EPV]) {
+        u32x4 o;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) o[k] = D::pack(f[2 * k], f[2 * k + 1]);
+        return o;
+    }
+};
+
+struct BF16 : Packed16<BF16> {
     static __device__ __forceinline__ float lo(uint32_t u) { return __uint_as_float(u << 16); }
     static __device__ __forceinline__ float hi(uint32_t u) { return __uint_as_float(u & 0xFFFF0000u); }
     static __device__ __forceinline__ float one(uint16_t u) { return __uint_as_float((uint32_t)u << 16); }
@@ -34,7 +54,7 @@ struct BF16 {
     }
 };
 
-struct FP16 {
+struct FP16 : Packed16<FP16> {
     static __device__ __forceinline__ float lo(uint32_t u) {
         return (float)__builtin_bit_cast(_Float16, (uint16_t)(u & 0xFFFFu));
     }
@@ -51,6 +71,23 @@ struct FP16 {
     static __device__ __forceinline__ uint16_t round1(float a) {
         return __builtin_bit_cast(uint16_t, (_Float16)a);
     }
+};
+
+struct F32 {
+    static constexpr int EPV = 4;
+    typedef uint32_t elem_t;
+    static __device__ __forceinline__ void widen(const u32x4 q, float (&f)[EPV]) {
+#pragma unroll
+        for (int k = 0; k < 4; ++k) f[k] = __uint_as_float(q[k]);
+    }
+    static __device__ __forceinline__ u32x4 narrow(const float (&f)[EPV]) {
+        u32x4 o;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) o[k] = __float_as_uint(f[k]);
+        return o;
+    }
+    static __device__ __forceinline__ float one(uint32_t u) { return __uint_as_float(u); }
+    static __device__ __forceinline__ uint32_t round1(float a) { return __float_as_uint(a); }
 };
 
 // ---------------------------------------------------------------------------

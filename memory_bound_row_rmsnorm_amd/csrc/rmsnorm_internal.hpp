@@ -8,14 +8,18 @@
 namespace rmsnorm_impl {
 
 // Every kernel takes exactly these arguments, in this order.
-//   x, w, y : 16-bit element buffers (device), rstd : fp32 [M] (device)
+//   x, w, y : element buffers of the dtype (device), rstd : fp32 [M] (device)
 //   M rows, N columns, inv_n = fp32(1/N), eps, offset
 //   xcd_group: consecutive workgroups' worth of rows placed on one XCD (1 = none)
 //   grid, threads : the launch's workgroup count and workgroup size, passed
 //   here so the kernels read no launch geometry from the dispatch's hidden
 //   arguments (a second scalar-memory round trip before the first row load)
 //   (the fields the kernels need before their first row load come first, in
-//   the 64 bytes the kernels' first scalar loads fetch together)
+//   the bytes the kernels' first scalar loads fetch together)
+//   M is the rows of one batch; the launch's grid y dimension counts the
+//   batches.  Row m of batch b of x starts at element b * x_bs + m * x_rs,
+//   likewise for y, and its rstd is rstd[b * M + m].  rstd may be NULL (not
+//   written).
 struct KernelArgs {
     const void* x;
     const void* w;
@@ -26,6 +30,10 @@ struct KernelArgs {
     int64_t grid;
     int32_t threads;
     int32_t xcd_group;
+    int64_t x_rs;       // row stride of x, elements
+    int64_t y_rs;       // row stride of y, elements
+    int64_t x_bs;       // batch stride of x, elements
+    int64_t y_bs;       // batch stride of y, elements
     float inv_n;
     float eps;
     float offset;
@@ -56,6 +64,7 @@ struct KernelEntry {
     int vectors_per_lane;  // WAVE, BLOCK: 16-byte vectors per lane per row; GENERIC: 0
     int row_slots;         // WAVE: slots per wave per trip; others 1
     bool prefetch;         // WAVE, BLOCK: next trip's rows loaded before this trip's reduction
+    bool tails;            // handles N that is not a multiple of the vector (forward)
     const void* func;      // host stub of the __global__ function
     const char* name;
 };

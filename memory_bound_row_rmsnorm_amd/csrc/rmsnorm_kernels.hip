@@ -5,7 +5,11 @@
 // ("Rmsnorm Kernel Optimization", Overview and Core Technique; "Why cutile's
 // rmsnorm required full register", kernel listing of the opening report).
 //
-// All arithmetic is fp32; x, w and y are bf16 or fp16.  Three families:
+// All arithmetic is fp32; x, w and y are bf16, fp16 or fp32 (a 16-byte
+// vector holds D::EPV = 8 or 4 elements).  Rows may be strided, in one or
+// more batches (the grid's y dimension); a width that is not a multiple of
+// EPV ends in a tail vector moved element by element; rstd may be NULL.
+// Three families:
 //
 //  * rmsnorm_wave   -- a row lives in a segment of 16, 32 or 64 lanes of one
 //    wavefront, each lane holding VPL 16-byte vectors of it; a wave carries
@@ -62,39 +66,82 @@ __device__ __forceinline__ float sum_squares(const u32x4 (&d)[VPL]) {
     float ss = 0.0f;
 #pragma unroll
     for (int v = 0; v < VPL; ++v) {
+        float f[D::EPV];
+        D::widen(d[v], f);
 #pragma unroll
-        for (int k = 0; k < 4; ++k) {
-            const float a = D::lo(d[v][k]);
-            const float b = D::hi(d[v][k]);
-            ss = __builtin_fmaf(a, a, ss);
-            ss = __builtin_fmaf(b, b, ss);
-        }
+        for (int e = 0; e < D::EPV; ++e) ss = __builtin_fmaf(f[e], f[e], ss);
     }
     return ss;
 }
 
-// offset + w for the 8 columns of one 16-byte weight vector (fp32, as the
+// offset + w for the EPV columns of one 16-byte weight vector (fp32, as the
 // listing forms offset + w after widening w).
 template <class D>
-__device__ __forceinline__ void widen_weights(float (&we)[8], const u32x4 q, float offset) {
+__device__ __forceinline__ void widen_weights(float (&we)[D::EPV], const u32x4 q, float offset) {
+    float f[D::EPV];
+    D::widen(q, f);
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-        we[2 * k] = offset + D::lo(q[k]);
-        we[2 * k + 1] = offset + D::hi(q[k]);
-    }
+    for (int e = 0; e < D::EPV; ++e) we[e] = offset + f[e];
 }
 
 template <class D>
-__device__ __forceinline__ u32x4 normalise(const u32x4 q, const float (&we)[8], float r) {
-    u32x4 o;
+__device__ __forceinline__ u32x4 normalise(const u32x4 q, const float (&we)[D::EPV], float r) {
+    float f[D::EPV];
+    D::widen(q, f);
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-        o[k] = D::pack((D::lo(q[k]) * r) * we[2 * k], (D::hi(q[k]) * r) * we[2 * k + 1]);
-    }
-    return o;
+    for (int e = 0; e < D::EPV; ++e) f[e] = (f[e] * r) * we[e];
+    return D::narrow(f);
 }
 
 constexpr u32x4 kZero = {0u, 0u, 0u, 0u};
+
+// Batches of rows run as the grid's y dimension: batch b = blockIdx.y starts
+// b * bs elements into x and y and b * M entries into rstd, and its rows are
+// rs elements apart (no division anywhere).
+__device__ __forceinline__ int64_t batch() { return static_cast<int64_t>(blockIdx.y); }
+
+// The last vector of a row whose width is not a multiple of EPV holds only
+// `tail` elements: they move one element at a time, so nothing past column
+// N - 1 is read or written (the bytes there may belong to something else).
+template <class D>
+__device__ __forceinline__ u32x4 load_tail(const u32x4* p, int tail) {
+    typedef typename D::elem_t E;
+    const E* q = reinterpret_cast<const E*>(p);
+    E e[D::EPV];
+#pragma unroll
+    for (int i = 0; i < D::EPV; ++i) e[i] = i < tail ? q[i] : E(0);
+    return __builtin_bit_cast(u32x4, e);
+}
+
+template <class D>
+__device__ __forceinline__ void store_tail(u32x4* p, u32x4 v, int tail) {
+    typedef typename D::elem_t E;
+    E* q = reinterpret_cast<E*>(p);
+    const auto e = __builtin_bit_cast(E __attribute__((ext_vector_type(D::EPV))), v);
+#pragma unroll
+    for (int i = 0; i < D::EPV; ++i)
+        if (i < tail) q[i] = e[i];
+}
+
+// Vector c of a row: full vectors below nfull; with TAIL, also the tail
+// vector at nfull (instances without TAIL run only when N % EPV == 0).
+template <class D, bool STREAM, bool TAIL>
+__device__ __forceinline__ u32x4 load_vec(const u32x4* row, int c, int nfull, int tail) {
+    if (c < nfull) return STREAM ? load_x(row + c) : row[c];
+    if constexpr (TAIL) {
+        if (__builtin_expect(tail != 0, 0) && c == nfull) return load_tail<D>(row + c, tail);
+    }
+    return kZero;
+}
+
+template <class D, bool TAIL>
+__device__ __forceinline__ void store_vec(u32x4* row, int c, int nfull, int tail, u32x4 v) {
+    if (c < nfull) {
+        store_y(row + c, v);
+    } else if constexpr (TAIL) {
+        if (__builtin_expect(tail != 0, 0) && c == nfull) store_tail<D>(row + c, v, tail);
+    }
+}
 
 // The dispatcher hands workgroup b to XCD b mod 8 (MI355X has 8 XCDs, each
 // with its own L2).  With group g > 1 the workgroup index is remapped inside
@@ -128,16 +175,18 @@ __device__ __forceinline__ int64_t grouped_block(int g, int64_t G) {
 // overlap instead of adding up.  With PREFETCH the next trip's rows are
 // loaded before this trip's reduction.
 // ---------------------------------------------------------------------------
-template <class D, int LANES, int VPL, int SLOTS, bool PREFETCH>
+template <class D, int LANES, int VPL, int SLOTS, bool PREFETCH, bool TAIL>
 __global__ __launch_bounds__(1024) void rmsnorm_wave(KernelArgs a) {
     constexpr int SEG = 64 / LANES;       // rows per slot
     constexpr int ROWS = SEG * SLOTS;     // rows per wave per trip
-    const u32x4* __restrict__ x = static_cast<const u32x4*>(a.x);
-    const u32x4* __restrict__ w = static_cast<const u32x4*>(a.w);
-    u32x4* __restrict__ y = static_cast<u32x4*>(a.y);
-    float* __restrict__ rstd = a.rstd;
     const int64_t M = a.M;
-    const int nvec = static_cast<int>(a.N >> 3);
+    const u32x4* __restrict__ x = static_cast<const u32x4*>(a.x) + batch() * (a.x_bs / D::EPV);
+    const u32x4* __restrict__ w = static_cast<const u32x4*>(a.w);
+    u32x4* __restrict__ y = static_cast<u32x4*>(a.y) + batch() * (a.y_bs / D::EPV);
+    float* __restrict__ rstd = a.rstd != nullptr ? a.rstd + batch() * M : nullptr;
+    const int nfull = static_cast<int>(static_cast<uint64_t>(a.N) / D::EPV);
+    const int tail = static_cast<int>(static_cast<uint64_t>(a.N) % D::EPV);
+    const int64_t x_rs = a.x_rs / D::EPV, y_rs = a.y_rs / D::EPV;   // in vectors
     const int lane = threadIdx.x & 63;
     const int seg = lane / LANES;
     const int li = lane % LANES;
@@ -152,22 +201,22 @@ __global__ __launch_bounds__(1024) void rmsnorm_wave(KernelArgs a) {
 #pragma unroll
         for (int s = 0; s < SLOTS; ++s) {
             const int64_t row = gg * ROWS + seg + s * SEG;
-            const u32x4* xr = x + row * nvec;
+            const u32x4* xr = x + row * x_rs;
 #pragma unroll
             for (int v = 0; v < VPL; ++v) {
                 const int c = v * LANES + li;
-                d[s][v] = (row < M && c < nvec) ? load_x(xr + c) : kZero;
+                d[s][v] = row < M ? load_vec<D, kStreamX, TAIL>(xr, c, nfull, tail) : kZero;
             }
         }
     };
 
     u32x4 d[SLOTS][VPL];
     load_trip(d, g);
-    float we[VPL][8];
+    float we[VPL][D::EPV];
 #pragma unroll
     for (int v = 0; v < VPL; ++v) {
         const int c = v * LANES + li;
-        widen_weights<D>(we[v], c < nvec ? w[c] : kZero, a.offset);
+        widen_weights<D>(we[v], load_vec<D, false, TAIL>(w, c, nfull, tail), a.offset);
     }
 
     // reductions, then every y store of the trip, then its rstd stores
@@ -181,17 +230,19 @@ __global__ __launch_bounds__(1024) void rmsnorm_wave(KernelArgs a) {
 #pragma unroll
         for (int s = 0; s < SLOTS; ++s) {
             const int64_t row = gg * ROWS + seg + s * SEG;
-            u32x4* yr = y + row * nvec;
+            u32x4* yr = y + row * y_rs;
 #pragma unroll
             for (int v = 0; v < VPL; ++v) {
                 const int c = v * LANES + li;
-                if (row < M && c < nvec) store_y(yr + c, normalise<D>(dd[s][v], we[v], r[s]));
+                if (row < M) store_vec<D, TAIL>(yr, c, nfull, tail, normalise<D>(dd[s][v], we[v], r[s]));
             }
         }
+        if (rstd != nullptr) {
 #pragma unroll
-        for (int s = 0; s < SLOTS; ++s) {
-            const int64_t row = gg * ROWS + seg + s * SEG;
-            if (li == 0 && row < M) store_rstd(rstd + row, r[s]);
+            for (int s = 0; s < SLOTS; ++s) {
+                const int64_t row = gg * ROWS + seg + s * SEG;
+                if (li == 0 && row < M) store_rstd(rstd + row, r[s]);
+            }
         }
     };
 
@@ -234,15 +285,17 @@ __global__ __launch_bounds__(1024) void rmsnorm_wave(KernelArgs a) {
 // reads (a wave can be at most one barrier ahead of another).  With PREFETCH
 // the next row is loaded before this row's reduction.
 // ---------------------------------------------------------------------------
-template <class D, int VPT, bool PREFETCH>
+template <class D, int VPT, bool PREFETCH, bool TAIL>
 __global__ __launch_bounds__(1024) void rmsnorm_block(KernelArgs a) {
     __shared__ float part[2][16];
-    const u32x4* __restrict__ x = static_cast<const u32x4*>(a.x);
-    const u32x4* __restrict__ w = static_cast<const u32x4*>(a.w);
-    u32x4* __restrict__ y = static_cast<u32x4*>(a.y);
-    float* __restrict__ rstd = a.rstd;
     const int64_t M = a.M;
-    const int nvec = static_cast<int>(a.N >> 3);
+    const u32x4* __restrict__ x = static_cast<const u32x4*>(a.x) + batch() * (a.x_bs / D::EPV);
+    const u32x4* __restrict__ w = static_cast<const u32x4*>(a.w);
+    u32x4* __restrict__ y = static_cast<u32x4*>(a.y) + batch() * (a.y_bs / D::EPV);
+    float* __restrict__ rstd = a.rstd != nullptr ? a.rstd + batch() * M : nullptr;
+    const int nfull = static_cast<int>(static_cast<uint64_t>(a.N) / D::EPV);
+    const int tail = static_cast<int>(static_cast<uint64_t>(a.N) % D::EPV);
+    const int64_t x_rs = a.x_rs / D::EPV, y_rs = a.y_rs / D::EPV;   // in vectors
     const int tid = threadIdx.x;
     const int nt = a.threads;
     const int lane = tid & 63;
@@ -252,22 +305,16 @@ __global__ __launch_bounds__(1024) void rmsnorm_block(KernelArgs a) {
     if (row >= M) return;
 
     auto load_row = [&](u32x4 (&d)[VPT], int64_t rr) {
-        const u32x4* xr = x + rr * nvec;
+        const u32x4* xr = x + rr * x_rs;
 #pragma unroll
-        for (int v = 0; v < VPT; ++v) {
-            const int c = v * nt + tid;
-            d[v] = c < nvec ? load_x(xr + c) : kZero;
-        }
+        for (int v = 0; v < VPT; ++v) d[v] = load_vec<D, kStreamX, TAIL>(xr, v * nt + tid, nfull, tail);
     };
 
     u32x4 d[VPT];
     load_row(d, row);
-    float we[VPT][8];
+    float we[VPT][D::EPV];
 #pragma unroll
-    for (int v = 0; v < VPT; ++v) {
-        const int c = v * nt + tid;
-        widen_weights<D>(we[v], c < nvec ? w[c] : kZero, a.offset);
-    }
+    for (int v = 0; v < VPT; ++v) widen_weights<D>(we[v], load_vec<D, false, TAIL>(w, v * nt + tid, nfull, tail), a.offset);
 
     // the row's reduction (wave butterfly, then the waves' sums through LDS),
     // every y store, then rstd
@@ -278,13 +325,10 @@ __global__ __launch_bounds__(1024) void rmsnorm_block(KernelArgs a) {
         float tot = part[pp][0];
         for (int i = 1; i < nw; ++i) tot += part[pp][i];
         const float r = rsq(__builtin_fmaf(tot, a.inv_n, a.eps));
-        u32x4* yr = y + rr * nvec;
+        u32x4* yr = y + rr * y_rs;
 #pragma unroll
-        for (int v = 0; v < VPT; ++v) {
-            const int c = v * nt + tid;
-            if (c < nvec) store_y(yr + c, normalise<D>(dd[v], we[v], r));
-        }
-        if (tid == 0) store_rstd(rstd + rr, r);
+        for (int v = 0; v < VPT; ++v) store_vec<D, TAIL>(yr, v * nt + tid, nfull, tail, normalise<D>(dd[v], we[v], r));
+        if (tid == 0 && rstd != nullptr) store_rstd(rstd + rr, r);
     };
 
     // one row per workgroup (the planned launches): straight through
@@ -316,17 +360,20 @@ __global__ __launch_bounds__(1024) void rmsnorm_block(KernelArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// Generic family: any N, any 2-byte alignment.  x and y may be the same
-// buffer: every element is read and then written by the same thread, and the
-// sum of squares of a row is complete (barrier) before any of it is written.
+// Generic family: any N, any element alignment, any strides.  x and y may be
+// the same buffer with the same layout: every element is read and then
+// written by the same thread, and the sum of squares of a row is complete
+// (barrier) before any of it is written.
 // ---------------------------------------------------------------------------
 template <class D>
 __global__ __launch_bounds__(1024) void rmsnorm_generic(KernelArgs a) {
+    typedef typename D::elem_t E;
     __shared__ float part[2][16];
-    const uint16_t* x = static_cast<const uint16_t*>(a.x);
-    const uint16_t* __restrict__ w = static_cast<const uint16_t*>(a.w);
-    uint16_t* y = static_cast<uint16_t*>(a.y);
     const int64_t M = a.M;
+    const E* x = static_cast<const E*>(a.x) + batch() * a.x_bs;
+    const E* __restrict__ w = static_cast<const E*>(a.w);
+    E* y = static_cast<E*>(a.y) + batch() * a.y_bs;
+    float* rstd = a.rstd != nullptr ? a.rstd + batch() * M : nullptr;
     const int64_t N = a.N;
     const int tid = threadIdx.x;
     const int nt = a.threads;
@@ -336,8 +383,8 @@ __global__ __launch_bounds__(1024) void rmsnorm_generic(KernelArgs a) {
 
     int par = 0;
     for (int64_t row = grouped_block(a.xcd_group, a.grid); row < M; row += a.grid) {
-        const uint16_t* xr = x + row * N;
-        uint16_t* yr = y + row * N;
+        const E* xr = x + row * a.x_rs;
+        E* yr = y + row * a.y_rs;
         float ss = 0.0f;
         for (int64_t j = tid; j < N; j += nt) {
             const float f = D::one(xr[j]);
@@ -352,7 +399,7 @@ __global__ __launch_bounds__(1024) void rmsnorm_generic(KernelArgs a) {
         for (int64_t j = tid; j < N; j += nt) {
             yr[j] = D::round1((D::one(xr[j]) * r) * (a.offset + D::one(w[j])));
         }
-        if (tid == 0) store_rstd(a.rstd + row, r);
+        if (tid == 0 && rstd != nullptr) store_rstd(rstd + row, r);
         par ^= 1;
     }
 }
@@ -360,28 +407,34 @@ __global__ __launch_bounds__(1024) void rmsnorm_generic(KernelArgs a) {
 // ---------------------------------------------------------------------------
 // Instance table.
 // ---------------------------------------------------------------------------
-#define RMS_WAVE(D, DT, L, V, S, P)                                                           \
-    {RMSNORM_VARIANT_WAVE, DT, L, V, S, P,                                                        \
-     reinterpret_cast<const void*>(&rmsnorm_wave<D, L, V, S, P>),                                 \
-     "rmsnorm_wave<" #D "," #L "," #V "," #S "," #P ">"}
+#define RMS_WAVE_T(D, DT, L, V, S, P, T)                                                      \
+    {RMSNORM_VARIANT_WAVE, DT, L, V, S, P, T,                                                     \
+     reinterpret_cast<const void*>(&rmsnorm_wave<D, L, V, S, P, T>),                              \
+     "rmsnorm_wave<" #D "," #L "," #V "," #S "," #P "," #T ">"}
+#define RMS_WAVE(D, DT, L, V, S, P) RMS_WAVE_T(D, DT, L, V, S, P, true)
 #define RMS_WAVE2(D, DT, L, V, S) RMS_WAVE(D, DT, L, V, S, false), RMS_WAVE(D, DT, L, V, S, true)
-#define RMS_BLOCK(D, DT, V, P)                                                                  \
-    {RMSNORM_VARIANT_BLOCK, DT, 0, V, 1, P, reinterpret_cast<const void*>(&rmsnorm_block<D, V, P>), \
-     "rmsnorm_block<" #D "," #V "," #P ">"}
+#define RMS_BLOCK_T(D, DT, V, P, T)                                                            \
+    {RMSNORM_VARIANT_BLOCK, DT, 0, V, 1, P, T,                                                    \
+     reinterpret_cast<const void*>(&rmsnorm_block<D, V, P, T>),                                   \
+     "rmsnorm_block<" #D "," #V "," #P "," #T ">"}
+#define RMS_BLOCK(D, DT, V, P) RMS_BLOCK_T(D, DT, V, P, true)
 #define RMS_BLOCK2(D, DT, V) RMS_BLOCK(D, DT, V, false), RMS_BLOCK(D, DT, V, true)
 // Only instances that fit 128 VGPRs (the budget of a 1024-thread workgroup)
-// without scratch are compiled.
+// without scratch are compiled.  The widest forms leave out the tail path
+// (last argument false), which they have no registers for: they serve
+// widths that are a multiple of the vector.  Six vectors per thread fit only
+// for fp32.
 #define RMS_FAMILY(D, DT)                                                                      \
     RMS_WAVE2(D, DT, 16, 1, 1), RMS_WAVE2(D, DT, 16, 1, 2), RMS_WAVE2(D, DT, 16, 1, 4),         \
     RMS_WAVE2(D, DT, 32, 1, 1), RMS_WAVE2(D, DT, 32, 1, 2), RMS_WAVE2(D, DT, 32, 1, 4),         \
     RMS_WAVE2(D, DT, 64, 1, 1), RMS_WAVE2(D, DT, 64, 1, 2), RMS_WAVE2(D, DT, 64, 1, 4),         \
-    RMS_WAVE2(D, DT, 64, 1, 8),                                                                 \
+    RMS_WAVE(D, DT, 64, 1, 8, false), RMS_WAVE_T(D, DT, 64, 1, 8, true, false),                 \
     RMS_WAVE2(D, DT, 64, 2, 1), RMS_WAVE2(D, DT, 64, 2, 2), RMS_WAVE(D, DT, 64, 2, 4, false),   \
     RMS_WAVE2(D, DT, 64, 3, 1), RMS_WAVE2(D, DT, 64, 3, 2),                                     \
     RMS_WAVE2(D, DT, 64, 4, 1), RMS_WAVE2(D, DT, 64, 5, 1), RMS_WAVE(D, DT, 64, 6, 1, false),   \
     RMS_BLOCK2(D, DT, 1), RMS_BLOCK2(D, DT, 2), RMS_BLOCK2(D, DT, 3), RMS_BLOCK2(D, DT, 4),     \
-    RMS_BLOCK2(D, DT, 5), RMS_BLOCK(D, DT, 6, false),                                           \
-    {RMSNORM_VARIANT_GENERIC, DT, 0, 0, 1, false,                                               \
+    RMS_BLOCK(D, DT, 5, false), RMS_BLOCK_T(D, DT, 5, true, false),                             \
+    {RMSNORM_VARIANT_GENERIC, DT, 0, 0, 1, false, true,                                         \
      reinterpret_cast<const void*>(&rmsnorm_generic<D>), "rmsnorm_generic<" #D ">"}
 
 namespace rmsnorm_impl {
@@ -389,6 +442,8 @@ namespace rmsnorm_impl {
 static const KernelEntry kTable[] = {
     RMS_FAMILY(BF16, RMSNORM_BF16),
     RMS_FAMILY(FP16, RMSNORM_FP16),
+    RMS_FAMILY(F32, RMSNORM_FP32),
+    RMS_BLOCK_T(F32, RMSNORM_FP32, 6, false, false),   // fp32 needs no widening registers
 };
 
 const KernelEntry* kernel_table(int* count) {

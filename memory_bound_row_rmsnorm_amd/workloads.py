@@ -29,7 +29,7 @@ import hashlib
 import numpy as np
 import torch
 
-TORCH_DTYPES = {"bf16": torch.bfloat16, "fp16": torch.float16}
+TORCH_DTYPES = {"bf16": torch.bfloat16, "fp16": torch.float16, "fp32": torch.float32}
 
 
 @dataclasses.dataclass(frozen=True)
@@ -37,7 +37,7 @@ class Workload:
     name: str
     M: int
     N: int
-    dtype: str          # "bf16" | "fp16"
+    dtype: str          # "bf16" | "fp16" | "fp32"
     x_sigma: float      # x ~ N(0, sigma^2)
     w_mean: float       # w = w_mean + 0.1 * N(0, 1)
     eps: float
@@ -46,7 +46,7 @@ class Workload:
 
     @property
     def elem_bytes(self) -> int:
-        return 2
+        return 4 if self.dtype == "fp32" else 2
 
     def algorithmic_bytes(self) -> int:
         """x read once, y written once, w read once, fp32 rstd written once."""

@@ -594,6 +594,60 @@ def pin_bwd_constant_row(o):
                 assert np.allclose(dw, M * c * r[0], rtol=1e-15, atol=0), (dtype, c, eps)
 
 
+def pin_fp32_path(o):
+    """fp32 inputs: the oracle's fp64 forward, then one IEEE round-to-nearest-even to binary32.
+
+    The rounding step is numpy's float64 -> float32 cast; pinned here on exact
+    midpoints (ties to even), one fp64 ulp either side of them, overflow at
+    FLT_MAX + half an ulp, and gradual underflow.  The fp64 forward on fp32
+    inputs is pinned by a constant row with eps = 0 (y = sign(c) (offset + w)
+    exactly) and by the brute-force rational result on tiny rows.
+    """
+    one = np.float64(1.0)
+    ulp = 2.0 ** -23
+    mids = np.array([1 + ulp / 2, 1 + 3 * ulp / 2, -(1 + ulp / 2), 2 ** -126 * (1 + ulp / 2)])
+    want = np.array([1.0, 1 + 2 * ulp, -1.0, 2 ** -126], dtype=np.float32)
+    assert np.array_equal(mids.astype(np.float32), want), mids.astype(np.float32)
+    above = np.nextafter(one + ulp / 2, np.inf)
+    below = np.nextafter(one + 3 * ulp / 2, -np.inf)
+    assert np.float32(above) == np.float32(1 + ulp) and np.float32(below) == np.float32(1 + ulp)
+    fmax = float(np.finfo(np.float32).max)
+    assert np.isinf(np.float32(fmax + 2.0 ** (127 - 24))) and np.float32(np.nextafter(fmax + 2.0 ** (127 - 24), 0)) == fmax
+    tiny = 2.0 ** -149
+    assert np.float32(tiny * 1.5) == np.float32(2 * tiny) and np.float32(tiny * 0.5) == 0.0 and np.float32(tiny * 2.5) == np.float32(2 * tiny)
+    # constant rows of a power of two, eps = 0: r = 1/|c| and y = sign(c) * (offset + w), all exact
+    rng = np.random.default_rng(7)
+    for c in (4.0, -0.25, 2.0 ** -70, -(2.0 ** 90)):
+        w = np.float32(rng.standard_normal(33)).astype(np.float64)
+        for off in (0.0, 1.0):
+            y, r = o.rmsnorm_fwd_f64(np.full((2, 33), c), w, 0.0, off)
+            assert np.array_equal(y, np.broadcast_to(np.sign(c) * (off + w), y.shape)), (c, off)
+            assert np.all(r == 1.0 / abs(c)), (c, r)
+    # tiny rows against exact rationals: the rounded fp32 result is the nearest binary32 value
+    from fractions import Fraction
+    for trial in range(40):
+        N = int(rng.integers(1, 9))
+        x = np.float32(rng.standard_normal((1, N)) * 4).astype(np.float64)
+        w = np.float32(rng.standard_normal(N)).astype(np.float64)
+        y, _ = o.rmsnorm_fwd_f64(x, w, 0.0, 0.0)
+        y32 = y.astype(np.float32)
+        ss = sum(Fraction(v) ** 2 for v in x[0])
+        for j in range(N):
+            num = Fraction(x[0, j]) * Fraction(w[j])           # y = num / sqrt(ss / N)
+            # exact y^2 = num^2 * N / ss; compare squares of the neighbours of y32
+            y2 = num * num * N / ss
+            cand = float(y32[0, j])
+            lo, hi = np.nextafter(np.float32(cand), np.float32(-np.inf)), np.nextafter(np.float32(cand), np.float32(np.inf))
+            for other in (lo, hi):
+                mid = (Fraction(cand) + Fraction(float(other))) / 2
+                # y32 must be at least as close to the exact value as each neighbour: the exact
+                # value lies on y32's side of the midpoint (signs agree with num)
+                if num > 0:
+                    assert (mid * mid <= y2) == (float(other) < cand) or mid * mid == y2, (trial, j)
+                elif num < 0:
+                    assert (mid * mid <= y2) == (float(other) > cand) or mid * mid == y2, (trial, j)
+
+
 ALL_PINS = [
     pin_decode_all_patterns,
     pin_encode_roundtrip,
@@ -617,4 +671,5 @@ ALL_PINS = [
     pin_bwd_torch_autograd,
     pin_bwd_identities,
     pin_bwd_constant_row,
+    pin_fp32_path,
 ]

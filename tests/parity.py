@@ -137,3 +137,46 @@ def oracle_bwd_for(x_cpu, w_cpu, dy_cpu, rstd_f32: np.ndarray, offset: float, dt
     """Oracle backward on the same rstd values the GPU receives."""
     return oracle.rmsnorm_bwd(workloads.to_bits(x_cpu), workloads.to_bits(w_cpu), workloads.to_bits(dy_cpu),
                               np.asarray(rstd_f32, dtype=np.float64), offset, dtype, want_exact=True)
+
+
+# ---------------------------------------------------------------------------
+# fp32 input.  The oracle's fp64 forward gives y_exact; the bar is relative
+# to it, derived from the kernels' fp32 arithmetic:
+#   sum of squares: at most 24 sequential FMAs per lane, 6 butterfly and
+#     readlane levels, 15 cross-wave additions: relative error < 46 * 2^-24;
+#   mean and eps: 1/N rounded, one FMA: 2 * 2^-24;
+#   rsqrt: hardware, about 1 ulp: 2 * 2^-24, plus half the mean's error;
+#   offset + w, x * r, (x r) g: three roundings: 3 * 2^-24.
+# First order that is under 30 * 2^-24; the bar takes 64 * 2^-24 (3.8e-6),
+# plus 2^-140 absolute where y_exact is subnormal in fp32.  rstd: as for the
+# 16-bit types.
+# ---------------------------------------------------------------------------
+F32_REL = 64 * 2.0 ** -24
+F32_ABS = 2.0 ** -140
+
+
+def oracle_fp32(x_cpu: torch.Tensor, w_cpu: torch.Tensor, eps: float, offset: float):
+    """(y_exact, rstd) in fp64 for fp32 inputs, with eps and offset taken as fp32."""
+    e = float(np.float32(eps))
+    o = float(np.float32(offset))
+    return oracle.rmsnorm_fwd_f64(x_cpu.double().numpy(), w_cpu.double().numpy(), e, o)
+
+
+def compare_fp32(y_gpu: torch.Tensor, rstd_gpu, y_exact: np.ndarray, rstd_ref: np.ndarray, what: str = "") -> dict:
+    y = y_gpu.cpu().double().numpy().reshape(y_exact.shape)
+    err = np.abs(y - y_exact)
+    bound = F32_REL * np.abs(y_exact) + F32_ABS
+    bad = ~(err <= bound)
+    if bad.any():
+        i = np.unravel_index(int(np.argmax(np.where(bad, err / bound, 0))), err.shape)
+        raise AssertionError(f"{what}: y off at {i}: gpu {y[i]!r} exact {y_exact[i]!r} bound {bound[i]!r} "
+                             f"({int(bad.sum())} elements out of bound)")
+    stats = {"elements": int(y.size), "max_err_over_bound": float(np.max(err / bound)) if y.size else 0.0}
+    if rstd_gpu is not None:
+        r = rstd_gpu.cpu().numpy().astype(np.float64).reshape(rstd_ref.shape)
+        rel = np.abs(r - rstd_ref) / np.abs(rstd_ref)
+        if not np.all(rel <= RSTD_RTOL):
+            m = int(np.argmax(rel))
+            raise AssertionError(f"{what}: rstd row {m}: gpu {r[m]!r} oracle {rstd_ref[m]!r}")
+        stats["rstd_max_rel"] = float(rel.max()) if rel.size else 0.0
+    return stats

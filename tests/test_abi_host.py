@@ -54,7 +54,7 @@ def fwd(x=A, w=A + 0x1000000, y=A + 0x2000000, rstd=A + 0x3000000, M=4, N=512, e
     (dict(N=0), SHAPE),
     (dict(N=-5), SHAPE),
     (dict(M=1 << 40, N=1 << 40), SHAPE),
-    (dict(dtype=2), DTYPE),
+    (dict(dtype=3), DTYPE),
     (dict(dtype=-1), DTYPE),
     (dict(x=None), NULL),
     (dict(w=None), NULL),
@@ -109,7 +109,7 @@ def covers(p, N):
 
 @pytest.mark.parametrize("M,N", [(64, 512), (16384, 512), (8192, 3000), (32768, 8192),
                                  (262144, 128), (4096, 16384), (1, 8), (7, 256), (100, 1024),
-                                 (3, 4096), (5, 49152)])
+                                 (3, 4096), (5, 40960)])
 def test_host_plans_cover_the_row_one_trip_per_workgroup(M, N):
     for dtype in (BF16, FP16):
         p = host_plan(M, N, dtype)
@@ -148,8 +148,9 @@ def test_planner_choices_for_the_workloads():
     p = host_plan(4096, 16384, FP16)
     assert (p.variant, p.block_threads, p.vectors_per_lane) == (bnd.VARIANT_BLOCK, 1024, 2)
     assert (p.xcd_group, p.max_blocks_per_cu) == (8, 0)
-    p = host_plan(3, 49152)
-    assert (p.block_threads, p.vectors_per_lane, p.max_blocks_per_cu) == (1024, 6, 0)
+    p = host_plan(3, 40960)
+    assert (p.block_threads, p.vectors_per_lane, p.max_blocks_per_cu) == (1024, 5, 0)
+    assert host_plan(3, 49152).variant == bnd.VARIANT_GENERIC     # six 16-bit vectors per thread do not fit
     for M, N in ((16384, 512), (262144, 128), (64, 256)):
         p = host_plan(M, N)
         assert (p.xcd_group, p.max_blocks_per_cu) == (1, 0)
@@ -217,6 +218,7 @@ def bwd(x=X, w=W, dy=DY, rstd=R, dx=DX, dw=DW, M=4, N=512, offset=0.0, dtype=BF1
     (dict(M=-1), SHAPE),
     (dict(N=0), SHAPE),
     (dict(dtype=7), DTYPE),
+    (dict(dtype=2), DTYPE),                # fp32 is forward only
     (dict(dw=None), NULL),
     (dict(x=None), NULL),
     (dict(dy=None), NULL),
@@ -362,3 +364,86 @@ def test_tuner_search_space_is_valid_and_contains_the_rule():
         assert all(bnd.plan_validate(M, N, dtype, p, cu_count=256) is not None for p in cands)
         fam = {p.variant for p in cands}
         assert rule.variant in fam and bnd.VARIANT_GENERIC in fam
+
+
+# ---------------------------------------------------------------------------
+# Strided / batched layouts, optional rstd, fp32 (host only)
+# ---------------------------------------------------------------------------
+def fwd_ex(x=A, w=A + 0x1000000, y=A + 0x2000000, rstd=A + 0x3000000, M=4, N=512, dtype=BF16,
+           layout=None, plan=None):
+    lay = ctypes.byref(bnd.Layout(*layout)) if layout is not None else None
+    return lib.rmsnorm_fwd_ex(x, w, y, rstd, M, N, 1e-6, 0.0, dtype, lay,
+                              ctypes.byref(plan) if plan is not None else None, None)
+
+
+@pytest.mark.parametrize("kwargs,status", [
+    (dict(layout=(0, -1, 0, 512, 0)), SHAPE),               # negative stride
+    (dict(layout=(3, 512, 4096, 512, 4096)), SHAPE),        # M = 4 is not a multiple of 3 rows
+    (dict(layout=(0, 512, 0, 256, 0)), SHAPE),              # y rows overlap each other
+    (dict(layout=(2, 512, 512, 512, 512)), SHAPE),          # y batches overlap (neither order is disjoint)
+    (dict(x=None), NULL),
+    (dict(dtype=3), DTYPE),
+    (dict(y=A, layout=(0, 1024, 0, 512, 0)), OVERLAP),       # in place needs the same layout
+    (dict(y=A + 0x1000, layout=(0, 1024, 0, 1024, 0)), OVERLAP),   # spans overlap (x spans 7168 bytes)
+    (dict(rstd=A + 3 * 1024 * 2 + 16, layout=(0, 1024, 0, 512, 0)), OVERLAP),  # rstd inside x's span
+])
+def test_fwd_ex_argument_errors(kwargs, status):
+    assert fwd_ex(**kwargs) == status, lib.rmsnorm_last_error().decode()
+    assert lib.rmsnorm_last_error().decode() != ""
+
+
+def test_fwd_ex_accepts_null_rstd_and_valid_layouts():
+    # valid calls get past every check: on a machine without a GPU they stop at the device
+    for kw in (dict(rstd=None), dict(layout=(0, 1024, 0, 512, 0)), dict(y=A, layout=(0, 1024, 0, 1024, 0)),
+               dict(layout=(2, 1024, 4096, 512, 1024)),       # batch-major y
+               dict(layout=(2, 512, 2048, 1024, 512)),        # row-major interleaved y
+               dict(layout=(0, 0, 0, 512, 0)),                # x broadcast: every row reads row 0
+               dict(dtype=2)):
+        st = fwd_ex(**kw)
+        assert st in (HIP, DEVICE), (kw, st, lib.rmsnorm_last_error().decode())
+
+
+def query_ex(M, N, dtype="bf16", x=A, w=A, y=A, layout=None):
+    p = bnd.Plan()
+    lay = ctypes.byref(bnd.Layout(*layout)) if layout is not None else None
+    st = lib.rmsnorm_plan_query_ex(M, N, bnd.DTYPE_NAMES[dtype], x, w, y, lay, 256, ctypes.byref(p))
+    assert st == OK, lib.rmsnorm_last_error().decode()
+    return p
+
+
+def test_layouts_choose_the_vector_kernels_when_rows_stay_aligned():
+    assert query_ex(4096, 512, layout=(0, 1024, 0, 512, 0)).variant == bnd.VARIANT_WAVE
+    assert query_ex(4096, 512, layout=(0, 516, 0, 512, 0)).variant == bnd.VARIANT_GENERIC   # x rows 8-byte aligned
+    # ragged widths on aligned rows: the vector kernels with their tail path
+    p = query_ex(4096, 3001, layout=(0, 3008, 0, 3008, 0))
+    assert p.variant == bnd.VARIANT_BLOCK and p.block_threads * p.vectors_per_lane * 8 >= 3001
+    assert query_ex(4096, 3001).variant == bnd.VARIANT_GENERIC      # contiguous rows of 3001 are unaligned
+    assert query_ex(4096, 100, layout=(0, 104, 0, 104, 0)).variant == bnd.VARIANT_WAVE
+    # batches: the plan covers one batch's rows
+    p = query_ex(8 * 1000, 512, layout=(1000, 512, 1024 * 512, 512, 1000 * 512))
+    assert p.variant == bnd.VARIANT_WAVE and p.grid * p.rows_per_trip >= 1000 and p.grid * p.rows_per_trip < 8000
+    # batches that continue the row stride collapse into one batch of all rows
+    p = query_ex(8 * 1000, 512, layout=(1000, 512, 1000 * 512, 512, 1000 * 512))
+    assert p.grid * p.rows_per_trip >= 8000
+
+
+def test_fp32_plans():
+    p = query_ex(16384, 512, "fp32")
+    assert (p.variant, p.vec_elems, p.lanes_per_row, p.vectors_per_lane) == (bnd.VARIANT_WAVE, 4, 64, 2)
+    p = query_ex(32768, 8192, "fp32")
+    assert (p.variant, p.vec_elems, p.block_threads, p.vectors_per_lane) == (bnd.VARIANT_BLOCK, 4, 1024, 2)
+    p = query_ex(4, 24576, "fp32")
+    assert (p.variant, p.vectors_per_lane) == (bnd.VARIANT_BLOCK, 6)
+    assert query_ex(4, 24576, "bf16").variant == bnd.VARIANT_BLOCK          # 1024 x 3 vectors of 8
+    assert query_ex(4, 45056, "bf16").variant == bnd.VARIANT_GENERIC        # wider than 1024 x 5 x 8
+    assert query_ex(4, 130, "fp32", layout=(0, 132, 0, 132, 0)).variant == bnd.VARIANT_WAVE
+
+
+def test_widest_instances_refuse_ragged_widths():
+    # fp32 1024 x 6 has no tail path: a ragged row that needs it takes the generic kernel
+    assert query_ex(4, 24576 - 3, "fp32", layout=(0, 24576, 0, 24576, 0)).variant == bnd.VARIANT_GENERIC
+    assert query_ex(4, 24576, "fp32").vectors_per_lane == 6
+    assert query_ex(4, 40960 - 3, layout=(0, 40960, 0, 40960, 0)).vectors_per_lane == 5   # bf16 1024 x 5 has one
+    p = bnd.plan_query(4, 24576, "fp32", cu_count=256)
+    ragged = bnd.plan_validate(4, 24573, "fp32", p, cu_count=256)
+    assert ragged is None                                   # an explicit plan is refused, not run wrong

@@ -1,0 +1,222 @@
+"""GPU parity of the general forward (rmsnorm_fwd_ex): strided 2-D rows, batched 3-D and 4-D
+rows, broadcast rows, widths that are not a multiple of the 16-byte vector, fp32, in place, and
+rstd left out.  Every case writes y into a view of a larger buffer filled with a sentinel and checks
+that nothing outside the view changed."""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+from tests import parity
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+SENTINEL = {torch.bfloat16: 0x7FC1, torch.float16: 0x7E01, torch.float32: 0x7FC00001}
+INT_VIEW = {torch.bfloat16: torch.int16, torch.float16: torch.int16, torch.float32: torch.int32}
+
+
+@pytest.fixture(scope="module")
+def bnd():
+    if not torch.cuda.is_available():
+        pytest.fail("no GPU visible")
+    from memory_bound_row_rmsnorm_amd import binding
+    return binding
+
+
+def announce(*parts):
+    print("CASE", *parts, flush=True)
+
+
+def filled(numel: int, dtype) -> torch.Tensor:
+    t = torch.empty(numel, dtype=dtype, device=DEV)
+    t.view(INT_VIEW[dtype]).fill_(SENTINEL[dtype])
+    return t
+
+
+def view_mask(numel: int, shape, strides, offset) -> torch.Tensor:
+    idx = torch.arange(numel).as_strided(shape, strides, offset)
+    mask = torch.zeros(numel, dtype=torch.bool)
+    mask[idx.reshape(-1)] = True
+    return mask
+
+
+def draw(shape, dtype, seed, sigma=1.0):
+    g = torch.Generator("cpu").manual_seed(seed)
+    return (sigma * torch.randn(*shape, generator=g)).to(dtype)
+
+
+def check(bnd, x: torch.Tensor, w: torch.Tensor, y: torch.Tensor, y_base: torch.Tensor, y_shape, y_strides,
+          y_off, eps=1e-6, offset=0.0, what=""):
+    """Run rmsnorm_fwd_ex into y (a view of y_base) and compare with the oracle on the logical rows."""
+    plan = bnd.plan_query_ex(x, w, y)
+    announce(what, tuple(x.shape), tuple(x.stride()), x.dtype, plan.as_dict()["variant_name"])
+    out, rstd = bnd.rmsnorm_fwd_ex(x, w, eps, offset, out=y)
+    torch.cuda.synchronize()
+    assert out.data_ptr() == y.data_ptr()
+    N = x.shape[-1]
+    xc = x.cpu().contiguous().reshape(-1, N)
+    wc = w.cpu()
+    yc = out.cpu().contiguous().reshape(-1, N)
+    if x.dtype == torch.float32:
+        ye, re = parity.oracle_fp32(xc, wc, eps, offset)
+        stats = parity.compare_fp32(yc, rstd.reshape(-1), ye, re, what)
+    else:
+        dt = "bf16" if x.dtype == torch.bfloat16 else "fp16"
+        yr, rr = parity.oracle_for(xc, wc, eps, offset, dt)
+        stats = parity.compare(yc, rstd.reshape(-1), yr, rr, dt, what)
+    # nothing outside the view was written
+    mask = view_mask(y_base.numel(), y_shape, y_strides, y_off)
+    untouched = y_base.cpu().view(INT_VIEW[x.dtype])[~mask]
+    expect = SENTINEL[x.dtype]
+    assert bool((untouched == expect).all()), f"{what}: {int((untouched != expect).sum())} guard elements written"
+    # rstd left out: the same y, nothing else written
+    y2_base = filled(y_base.numel(), x.dtype)
+    y2 = y2_base.as_strided(y_shape, y_strides, y_off)
+    out2, none = bnd.rmsnorm_fwd_ex(x, w, eps, offset, want_rstd=False, out=y2)
+    torch.cuda.synchronize()
+    assert none is None
+    assert torch.equal(out2.cpu().view(INT_VIEW[x.dtype]), out.cpu().view(INT_VIEW[x.dtype])), what
+    print(what, plan.as_dict()["variant_name"], stats, flush=True)
+    return plan
+
+
+def strided_case(bnd, dtype, M, N, x_ld, y_ld, seed, **kw):
+    xb = draw((M * x_ld,), dtype, seed)
+    x = xb.to(DEV).as_strided((M, N), (x_ld, 1), 0)
+    w = (1.0 + 0.1 * draw((N,), torch.float32, seed + 1)).to(dtype).to(DEV)
+    y_base = filled(M * y_ld + 64, dtype)
+    y = y_base.as_strided((M, N), (y_ld, 1), 32)
+    return check(bnd, x, w, y, y_base, (M, N), (y_ld, 1), 32, what=f"{M}x{N} ld {x_ld}/{y_ld}", **kw)
+
+
+@pytest.mark.parametrize("dtype,M,N,x_ld,y_ld,family", [
+    (torch.bfloat16, 1000, 512, 640, 576, "wave"),
+    (torch.bfloat16, 777, 3001, 3008, 3016, "block"),       # ragged tail of 1 element
+    (torch.float16, 1025, 100, 104, 112, "wave"),           # 16-lane rows, tail of 4
+    (torch.bfloat16, 300, 8191, 8192, 8200, "block"),       # tail of 7
+    (torch.float16, 64, 7, 8, 16, "wave"),                  # narrower than one vector
+    (torch.bfloat16, 100, 4096, 4100, 4096, "generic"),     # x rows not 16-byte aligned
+    (torch.float32, 333, 1027, 1028, 1032, "block"),        # fp32 tail of 3
+    (torch.float32, 500, 130, 132, 136, "wave"),
+])
+def test_strided_rows(bnd, dtype, M, N, x_ld, y_ld, family):
+    plan = strided_case(bnd, dtype, M, N, x_ld, y_ld, seed=11)
+    assert plan.as_dict()["variant_name"] == family
+
+
+@pytest.mark.parametrize("dtype,M,N", [
+    (torch.float32, 4096, 512), (torch.float32, 64, 8192), (torch.float32, 8, 24576), (torch.float32, 300, 96),
+    (torch.bfloat16, 500, 3001), (torch.float16, 333, 1234),        # contiguous ragged rows: generic kernel
+])
+def test_contiguous(bnd, dtype, M, N):
+    sigma = 100.0 if dtype == torch.float16 else 1.0
+    x = draw((M, N), dtype, 21, sigma).to(DEV)
+    w = (1.0 + 0.1 * draw((N,), torch.float32, 22)).to(dtype).to(DEV)
+    y_base = filled(M * N + 16, dtype)
+    y = y_base.as_strided((M, N), (N, 1), 8)
+    check(bnd, x, w, y, y_base, (M, N), (N, 1), 8, offset=1.0, what=f"contiguous {M}x{N}")
+
+
+def test_batches_of_a_sliced_sequence(bnd):
+    B, S_all, S, N = 4, 300, 257, 1024
+    big = draw((B, S_all, N), torch.bfloat16, 31).to(DEV)
+    x = big[:, 10:10 + S, :]                                   # rows 1024 apart, batches 300 * 1024 apart
+    w = (1.0 + 0.1 * draw((N,), torch.float32, 32)).to(torch.bfloat16).to(DEV)
+    y_base = filled(B * 260 * N, torch.bfloat16)
+    shape, strides = (B, S, N), (260 * N, N, 1)
+    y = y_base.as_strided(shape, strides, 0)
+    plan = check(bnd, x, w, y, y_base, shape, strides, 0, what="3-D slice")
+    assert plan.grid * plan.rows_per_trip < B * S               # one batch per grid row
+
+
+def test_batches_interleaved(bnd):
+    S, B, N = 257, 4, 1024
+    base = draw((S, B, N), torch.bfloat16, 41).to(DEV)
+    x = base.transpose(0, 1)                                   # [B, S, N] with strides (N, B * N, 1)
+    w = (0.1 * draw((N,), torch.float32, 42)).to(torch.bfloat16).to(DEV)
+    shape, strides = (B, S, N), (N, B * N, 1)
+    y_base = filled(S * B * N, torch.bfloat16)
+    y = y_base.as_strided(shape, strides, 0)
+    check(bnd, x, w, y, y_base, shape, strides, 0, offset=1.0, what="3-D interleaved")
+
+
+def test_four_dimensional_rows_collapse(bnd):
+    shape = (2, 3, 64, 512)
+    x = draw(shape, torch.float16, 51, 100.0).to(DEV)
+    w = (1.0 + 0.1 * draw((512,), torch.float32, 52)).to(torch.float16).to(DEV)
+    n = x.numel()
+    y_base = filled(n, torch.float16)
+    strides = (3 * 64 * 512, 64 * 512, 512, 1)
+    y = y_base.as_strided(shape, strides, 0)
+    check(bnd, x, w, y, y_base, shape, strides, 0, what="4-D contiguous")
+
+
+def test_broadcast_rows(bnd):
+    M, N = 1000, 512
+    row = draw((1, N), torch.bfloat16, 61).to(DEV)
+    x = row.expand(M, N)                                       # row stride 0
+    w = (1.0 + 0.1 * draw((N,), torch.float32, 62)).to(torch.bfloat16).to(DEV)
+    y_base = filled(M * N, torch.bfloat16)
+    y = y_base.as_strided((M, N), (N, 1), 0)
+    check(bnd, x, w, y, y_base, (M, N), (N, 1), 0, what="broadcast row")
+    assert bool((y == y[0:1]).all())
+
+
+def test_more_batches_than_one_launch_holds(bnd):
+    B, N = 70000, 8                                            # 70000 batches of one row: two launches
+    base = draw((B, 2, N), torch.float16, 71).to(DEV)
+    x = base[:, :1, :]                                         # batch stride 16 elements
+    w = (1.0 + 0.1 * draw((N,), torch.float32, 72)).to(torch.float16).to(DEV)
+    shape, strides = (B, 1, N), (2 * N, N, 1)
+    y_base = filled(B * 2 * N, torch.float16)
+    y = y_base.as_strided(shape, strides, 0)
+    check(bnd, x, w, y, y_base, shape, strides, 0, what="70000 batches")
+
+
+def test_in_place_with_a_layout(bnd):
+    M, N, ld = 513, 1000, 1008
+    base = draw((M * ld,), torch.bfloat16, 81).to(DEV)
+    x = base.as_strided((M, N), (ld, 1), 0)
+    w = (1.0 + 0.1 * draw((N,), torch.float32, 82)).to(torch.bfloat16).to(DEV)
+    before = base.cpu().clone()
+    xc = x.cpu().contiguous()
+    announce("in place", M, N, ld)
+    out, rstd = bnd.rmsnorm_fwd_ex(x, w, 1e-6, 0.0, out=x)
+    torch.cuda.synchronize()
+    yr, rr = parity.oracle_for(xc, w.cpu(), 1e-6, 0.0, "bf16")
+    parity.compare(out.cpu().contiguous(), rstd, yr, rr, "bf16", "in place")
+    after = base.cpu()
+    pad = view_mask(M * ld, (M, N), (ld, 1), 0)
+    assert torch.equal(after.view(torch.int16)[~pad], before.view(torch.int16)[~pad])
+
+
+def test_layout_errors_are_raised(bnd):
+    x = torch.zeros(8, 64, dtype=torch.bfloat16, device=DEV)
+    w = torch.ones(64, dtype=torch.bfloat16, device=DEV)
+    y_overlapping = torch.zeros(8 * 32 + 64, dtype=torch.bfloat16, device=DEV).as_strided((8, 64), (32, 1), 0)
+    with pytest.raises(bnd.RmsnormError) as e:
+        bnd.rmsnorm_fwd_ex(x, w, out=y_overlapping)            # y rows overlap each other
+    assert e.value.status == 2
+    with pytest.raises(ValueError):
+        bnd.rmsnorm_fwd_ex(x.t(), torch.ones(8, dtype=torch.bfloat16, device=DEV))   # last dim not unit stride
+
+
+FP32_SWEEP_N = [1, 3, 4, 5, 63, 64, 65, 127, 128, 129, 255, 256, 511, 512, 513, 1023, 1024, 1025, 3000, 4097,
+                8192, 16385, 24576]
+
+
+@pytest.mark.parametrize("N", FP32_SWEEP_N)
+def test_fp32_sweep(bnd, N):
+    g = torch.Generator().manual_seed(N)
+    for M in (1, 3, 65, 257):
+        if M * N > 2_000_000:
+            continue
+        x = (torch.randn(M, N, generator=g) * 3)
+        w = (torch.randn(N, generator=g) * 0.5)
+        for offset in (0.0, 1.0):
+            announce("fp32 sweep", M, N, offset)
+            y, r = bnd.rmsnorm_fwd_ex(x.to(DEV), w.to(DEV), 1e-6, offset)
+            torch.cuda.synchronize()
+            ye, re = parity.oracle_fp32(x, w, 1e-6, offset)
+            parity.compare_fp32(y, r, ye, re, f"fp32 sweep M={M} N={N} off={offset}")

@@ -93,6 +93,7 @@ def test_every_kernel_on_workload_rows(bnd, name):
             p = plan.copy(grid=grid)
             y = torch.empty_like(xg)
             r = torch.empty(M, dtype=torch.float32, device=DEV)
+            announce(name, p.as_dict())
             try:
                 bnd.rmsnorm_fwd_out(xg, wg, y, r, wl.eps, wl.offset, plan=p)
             except bnd.RmsnormError as e:
@@ -100,7 +101,6 @@ def test_every_kernel_on_workload_rows(bnd, name):
                     continue
                 raise
             torch.cuda.synchronize()
-            announce(name, p.as_dict())
             parity.compare(y, r, y_ref, r_ref, wl.dtype, f"{name} {p.as_dict()}")
             ran += 1
     assert ran >= 6
@@ -304,7 +304,10 @@ def test_python_checks_reject_bad_tensors(bnd):
     with pytest.raises(ValueError):
         bnd.rmsnorm_fwd(x.t(), torch.ones(4, dtype=torch.bfloat16, device=DEV))
     with pytest.raises(ValueError):
-        bnd.rmsnorm_fwd(x.float(), torch.ones(64, device=DEV))
+        bnd.rmsnorm_fwd(x.double(), torch.ones(64, dtype=torch.float64, device=DEV))   # no fp64 kernels
+    with pytest.raises(bnd.RmsnormError) as e:
+        bnd.rmsnorm_bwd(x.float(), torch.ones(64, device=DEV), x.float(), torch.ones(4, device=DEV))
+    assert e.value.status == 3                                                          # fp32 backward: DTYPE
     with pytest.raises(bnd.RmsnormError):
         bnd.rmsnorm_fwd(x, torch.ones(64, dtype=torch.bfloat16, device=DEV), eps=-1.0)
 
