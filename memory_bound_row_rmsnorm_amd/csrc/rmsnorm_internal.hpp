@@ -15,24 +15,26 @@ namespace rmsnorm_impl {
 //   here so the kernels read no launch geometry from the dispatch's hidden
 //   arguments (a second scalar-memory round trip before the first row load)
 //   (the fields the kernels need before their first row load come first, in
-//   the bytes the kernels' first scalar loads fetch together)
+//   the 64 bytes the kernels' first scalar loads fetch together)
 //   M is the rows of one batch; the launch's grid y dimension counts the
 //   batches.  Row m of batch b of x starts at element b * x_bs + m * x_rs,
 //   likewise for y, and its rstd is rstd[b * M + m].  rstd may be NULL (not
 //   written).
 struct KernelArgs {
+    // the first 64 bytes: everything the first row load depends on
     const void* x;
-    const void* w;
-    void* y;
-    float* rstd;
     int64_t M;
     int64_t N;
     int64_t grid;
     int32_t threads;
     int32_t xcd_group;
     int64_t x_rs;       // row stride of x, elements
-    int64_t y_rs;       // row stride of y, elements
     int64_t x_bs;       // batch stride of x, elements
+    const void* w;
+    // the rest: needed after the loads are in flight
+    void* y;
+    float* rstd;
+    int64_t y_rs;       // row stride of y, elements
     int64_t y_bs;       // batch stride of y, elements
     float inv_n;
     float eps;

@@ -123,6 +123,13 @@ __device__ __forceinline__ void store_tail(u32x4* p, u32x4 v, int tail) {
         if (i < tail) q[i] = e[i];
 }
 
+// Strides arrive in elements (never negative); the 16-byte kernels step in
+// vectors.
+template <class D>
+__device__ __forceinline__ int64_t vectors(int64_t elems) {
+    return static_cast<int64_t>(static_cast<uint64_t>(elems) / D::EPV);
+}
+
 // Vector c of a row: full vectors below nfull; with TAIL, also the tail
 // vector at nfull (instances without TAIL run only when N % EPV == 0).
 template <class D, bool STREAM, bool TAIL>
@@ -180,13 +187,12 @@ __global__ __launch_bounds__(1024) void rmsnorm_wave(KernelArgs a) {
     constexpr int SEG = 64 / LANES;       // rows per slot
     constexpr int ROWS = SEG * SLOTS;     // rows per wave per trip
     const int64_t M = a.M;
-    const u32x4* __restrict__ x = static_cast<const u32x4*>(a.x) + batch() * (a.x_bs / D::EPV);
+    const u32x4* __restrict__ x = static_cast<const u32x4*>(a.x) + batch() * vectors<D>(a.x_bs);
     const u32x4* __restrict__ w = static_cast<const u32x4*>(a.w);
-    u32x4* __restrict__ y = static_cast<u32x4*>(a.y) + batch() * (a.y_bs / D::EPV);
-    float* __restrict__ rstd = a.rstd != nullptr ? a.rstd + batch() * M : nullptr;
+    u32x4* __restrict__ y = static_cast<u32x4*>(a.y) + batch() * vectors<D>(a.y_bs);
     const int nfull = static_cast<int>(static_cast<uint64_t>(a.N) / D::EPV);
     const int tail = static_cast<int>(static_cast<uint64_t>(a.N) % D::EPV);
-    const int64_t x_rs = a.x_rs / D::EPV, y_rs = a.y_rs / D::EPV;   // in vectors
+    const int64_t x_rs = vectors<D>(a.x_rs), y_rs = vectors<D>(a.y_rs);
     const int lane = threadIdx.x & 63;
     const int seg = lane / LANES;
     const int li = lane % LANES;
@@ -195,7 +201,9 @@ __global__ __launch_bounds__(1024) void rmsnorm_wave(KernelArgs a) {
     const int wid = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
     const int64_t nwaves = a.grid * wpb;
     int64_t g = grouped_block(a.xcd_group, a.grid) * wpb + wid;
-    if (g * ROWS >= M) return;
+    // No early exit for waves past the last row: every access below is masked
+    // by row < M, and without the branch the compiler fetches all the kernel
+    // arguments the first loads need in one batch of scalar loads.
 
     auto load_trip = [&](u32x4 (&d)[SLOTS][VPL], int64_t gg) {
 #pragma unroll
@@ -237,7 +245,8 @@ __global__ __launch_bounds__(1024) void rmsnorm_wave(KernelArgs a) {
                 if (row < M) store_vec<D, TAIL>(yr, c, nfull, tail, normalise<D>(dd[s][v], we[v], r[s]));
             }
         }
-        if (rstd != nullptr) {
+        if (a.rstd != nullptr) {
+            float* rstd = a.rstd + batch() * M;
 #pragma unroll
             for (int s = 0; s < SLOTS; ++s) {
                 const int64_t row = gg * ROWS + seg + s * SEG;
@@ -289,25 +298,26 @@ template <class D, int VPT, bool PREFETCH, bool TAIL>
 __global__ __launch_bounds__(1024) void rmsnorm_block(KernelArgs a) {
     __shared__ float part[2][16];
     const int64_t M = a.M;
-    const u32x4* __restrict__ x = static_cast<const u32x4*>(a.x) + batch() * (a.x_bs / D::EPV);
+    const u32x4* __restrict__ x = static_cast<const u32x4*>(a.x) + batch() * vectors<D>(a.x_bs);
     const u32x4* __restrict__ w = static_cast<const u32x4*>(a.w);
-    u32x4* __restrict__ y = static_cast<u32x4*>(a.y) + batch() * (a.y_bs / D::EPV);
-    float* __restrict__ rstd = a.rstd != nullptr ? a.rstd + batch() * M : nullptr;
+    u32x4* __restrict__ y = static_cast<u32x4*>(a.y) + batch() * vectors<D>(a.y_bs);
     const int nfull = static_cast<int>(static_cast<uint64_t>(a.N) / D::EPV);
     const int tail = static_cast<int>(static_cast<uint64_t>(a.N) % D::EPV);
-    const int64_t x_rs = a.x_rs / D::EPV, y_rs = a.y_rs / D::EPV;   // in vectors
+    const int64_t x_rs = vectors<D>(a.x_rs), y_rs = vectors<D>(a.y_rs);
     const int tid = threadIdx.x;
     const int nt = a.threads;
     const int lane = tid & 63;
     const int wid = tid >> 6;
     const int nw = nt >> 6;
     int64_t row = grouped_block(a.xcd_group, a.grid);
-    if (row >= M) return;
+    // no early exit for workgroups past the last row (see the wave family):
+    // their loads and stores are masked instead
 
     auto load_row = [&](u32x4 (&d)[VPT], int64_t rr) {
         const u32x4* xr = x + rr * x_rs;
+        const bool live = rr < M;
 #pragma unroll
-        for (int v = 0; v < VPT; ++v) d[v] = load_vec<D, kStreamX, TAIL>(xr, v * nt + tid, nfull, tail);
+        for (int v = 0; v < VPT; ++v) d[v] = live ? load_vec<D, kStreamX, TAIL>(xr, v * nt + tid, nfull, tail) : kZero;
     };
 
     u32x4 d[VPT];
@@ -325,10 +335,12 @@ __global__ __launch_bounds__(1024) void rmsnorm_block(KernelArgs a) {
         float tot = part[pp][0];
         for (int i = 1; i < nw; ++i) tot += part[pp][i];
         const float r = rsq(__builtin_fmaf(tot, a.inv_n, a.eps));
-        u32x4* yr = y + rr * y_rs;
+        if (rr < M) {
+            u32x4* yr = y + rr * y_rs;
 #pragma unroll
-        for (int v = 0; v < VPT; ++v) store_vec<D, TAIL>(yr, v * nt + tid, nfull, tail, normalise<D>(dd[v], we[v], r));
-        if (tid == 0 && rstd != nullptr) store_rstd(rstd + rr, r);
+            for (int v = 0; v < VPT; ++v) store_vec<D, TAIL>(yr, v * nt + tid, nfull, tail, normalise<D>(dd[v], we[v], r));
+            if (tid == 0 && a.rstd != nullptr) store_rstd(a.rstd + batch() * M + rr, r);
+        }
     };
 
     // one row per workgroup (the planned launches): straight through
@@ -373,7 +385,6 @@ __global__ __launch_bounds__(1024) void rmsnorm_generic(KernelArgs a) {
     const E* x = static_cast<const E*>(a.x) + batch() * a.x_bs;
     const E* __restrict__ w = static_cast<const E*>(a.w);
     E* y = static_cast<E*>(a.y) + batch() * a.y_bs;
-    float* rstd = a.rstd != nullptr ? a.rstd + batch() * M : nullptr;
     const int64_t N = a.N;
     const int tid = threadIdx.x;
     const int nt = a.threads;
@@ -399,7 +410,7 @@ __global__ __launch_bounds__(1024) void rmsnorm_generic(KernelArgs a) {
         for (int64_t j = tid; j < N; j += nt) {
             yr[j] = D::round1((D::one(xr[j]) * r) * (a.offset + D::one(w[j])));
         }
-        if (tid == 0 && rstd != nullptr) store_rstd(rstd + row, r);
+        if (tid == 0 && a.rstd != nullptr) store_rstd(a.rstd + batch() * M + row, r);
         par ^= 1;
     }
 }
@@ -422,7 +433,7 @@ __global__ __launch_bounds__(1024) void rmsnorm_generic(KernelArgs a) {
 // Only instances that fit 128 VGPRs (the budget of a 1024-thread workgroup)
 // without scratch are compiled.  The widest forms leave out the tail path
 // (last argument false), which they have no registers for: they serve
-// widths that are a multiple of the vector.  Six vectors per thread fit only
+// widths that are a multiple of the vector.  Six vectors per lane fit only
 // for fp32.
 #define RMS_FAMILY(D, DT)                                                                      \
     RMS_WAVE2(D, DT, 16, 1, 1), RMS_WAVE2(D, DT, 16, 1, 2), RMS_WAVE2(D, DT, 16, 1, 4),         \
@@ -431,7 +442,7 @@ __global__ __launch_bounds__(1024) void rmsnorm_generic(KernelArgs a) {
     RMS_WAVE(D, DT, 64, 1, 8, false), RMS_WAVE_T(D, DT, 64, 1, 8, true, false),                 \
     RMS_WAVE2(D, DT, 64, 2, 1), RMS_WAVE2(D, DT, 64, 2, 2), RMS_WAVE(D, DT, 64, 2, 4, false),   \
     RMS_WAVE2(D, DT, 64, 3, 1), RMS_WAVE2(D, DT, 64, 3, 2),                                     \
-    RMS_WAVE2(D, DT, 64, 4, 1), RMS_WAVE2(D, DT, 64, 5, 1), RMS_WAVE(D, DT, 64, 6, 1, false),   \
+    RMS_WAVE2(D, DT, 64, 4, 1), RMS_WAVE2(D, DT, 64, 5, 1),                                     \
     RMS_BLOCK2(D, DT, 1), RMS_BLOCK2(D, DT, 2), RMS_BLOCK2(D, DT, 3), RMS_BLOCK2(D, DT, 4),     \
     RMS_BLOCK(D, DT, 5, false), RMS_BLOCK_T(D, DT, 5, true, false),                             \
     {RMSNORM_VARIANT_GENERIC, DT, 0, 0, 1, false, true,                                         \
@@ -443,7 +454,8 @@ static const KernelEntry kTable[] = {
     RMS_FAMILY(BF16, RMSNORM_BF16),
     RMS_FAMILY(FP16, RMSNORM_FP16),
     RMS_FAMILY(F32, RMSNORM_FP32),
-    RMS_BLOCK_T(F32, RMSNORM_FP32, 6, false, false),   // fp32 needs no widening registers
+    RMS_BLOCK_T(F32, RMSNORM_FP32, 6, false, false),   // six vectors per thread: fp32 only (no widening
+    RMS_WAVE_T(F32, RMSNORM_FP32, 64, 6, 1, false, false),   // registers)
 };
 
 const KernelEntry* kernel_table(int* count) {
