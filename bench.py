@@ -438,6 +438,8 @@ def main() -> int:
             "offset": wl.offset,
             "algorithmic_bytes_per_step": nbytes,
             "rotation_sets": sets,
+            "inputs": ("cold in HBM" if sets * x_bytes >= ROTATION_X_BYTES
+                       else "warm: rows may be cache-resident (Infinity Cache); not an HBM figure"),
             "launch": args.mode,
             "kernel": args.kernel,
             "plan": {k: v for k, v in plan.as_dict().items()},

@@ -73,7 +73,9 @@ typedef enum rmsnorm_variant {
     RMSNORM_VARIANT_AUTO = 0,    /* let the library choose (rmsnorm_plan_query) */
     RMSNORM_VARIANT_WAVE = 1,    /* one or more rows per 64-lane wavefront, no LDS */
     RMSNORM_VARIANT_BLOCK = 2,   /* one row per workgroup, cross-wave LDS reduce */
-    RMSNORM_VARIANT_GENERIC = 3  /* any N and alignment: scalar I/O, row read twice */
+    RMSNORM_VARIANT_GENERIC = 3, /* any N and alignment: scalar I/O, row read twice */
+    RMSNORM_VARIANT_SHIFTED = 4  /* rows not 16-byte aligned (N % 8 != 0, contiguous): one row
+                                    per workgroup, aligned 16-byte chunks, shifted weights */
 } rmsnorm_variant_t;
 
 /*

@@ -223,6 +223,25 @@ bool vector_ok(const void* x, const void* w, const void* y, int dtype, const Lay
     return aligned16(x) && aligned16(w) && aligned16(y) && rows_ok && batches_ok;
 }
 
+// What a call's pointers and layout allow: the 16-byte kernels (every row
+// 16-byte aligned), or the shifted kernel (rows of x and y equally far past a
+// 16-byte boundary on every row: the same layout and equally aligned bases;
+// w 16-byte aligned).
+struct Access {
+    bool vec;
+    bool shifted;
+};
+
+Access access_of(const void* x, const void* w, const void* y, int dtype, const Layout& L, int64_t M) {
+    const uintptr_t es = static_cast<uintptr_t>(elem_size(dtype));
+    const uintptr_t xa = reinterpret_cast<uintptr_t>(x), ya = reinterpret_cast<uintptr_t>(y);
+    const bool same_layout = L.x_rs == L.y_rs && (L.batches(M) <= 1 || L.x_bs == L.y_bs);
+    Access a;
+    a.vec = vector_ok(x, w, y, dtype, L, M);
+    a.shifted = !a.vec && aligned16(w) && xa % es == 0 && ya % es == 0 && xa % 16 == ya % 16 && same_layout;
+    return a;
+}
+
 // ---------------------------------------------------------------------------
 // Kernel lookup.
 // ---------------------------------------------------------------------------
@@ -235,7 +254,8 @@ const KernelEntry* find_kernel(int variant, int dtype, int lanes, int vpl, int s
         if (variant == RMSNORM_VARIANT_WAVE &&
             (k.lanes_per_row != lanes || k.vectors_per_lane != vpl || k.row_slots != slots))
             continue;
-        if (variant == RMSNORM_VARIANT_BLOCK && k.vectors_per_lane != vpl) continue;
+        if ((variant == RMSNORM_VARIANT_BLOCK || variant == RMSNORM_VARIANT_SHIFTED) && k.vectors_per_lane != vpl)
+            continue;
         return &k;
     }
     return nullptr;
@@ -245,7 +265,8 @@ int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 // Fill the derived fields and check the plan against the call (`vec`: the
 // call's pointers and strides suit the 16-byte kernels).  Host only.
-int finish_plan(rmsnorm_plan_t* p, int64_t M, int64_t N, int dtype, bool vec, const KernelEntry** kernel) {
+int finish_plan(rmsnorm_plan_t* p, int64_t M, int64_t N, int dtype, Access acc, const KernelEntry** kernel) {
+    const bool vec = acc.vec;
     if (p->block_threads < 64 || p->block_threads > 1024 || p->block_threads % 64 != 0)
         return fail(RMSNORM_ERR_PLAN, "block_threads must be a multiple of 64 in [64, 1024]");
     if (p->grid < 1 || p->grid > 0x7FFFFFFF) return fail(RMSNORM_ERR_PLAN, "grid must be in [1, 2^31)");
@@ -285,6 +306,19 @@ int finish_plan(rmsnorm_plan_t* p, int64_t M, int64_t N, int dtype, bool vec, co
                 p->rows_per_trip = 1;
             }
         }
+    } else if (p->variant == RMSNORM_VARIANT_SHIFTED) {
+        if (!acc.shifted)
+            return fail(RMSNORM_ERR_PLAN, "the shifted kernel needs x and y equally aligned with the same layout, "
+                                          "16-byte aligned w, and rows that are not 16-byte aligned");
+        const int epv = elems_per_vector(dtype);
+        p->vec_elems = epv;
+        p->row_slots = 1;
+        p->lanes_per_row = p->block_threads;
+        p->rows_per_trip = 1;
+        if (p->prefetch != 0) return fail(RMSNORM_ERR_PLAN, "the shifted kernel has no prefetching form");
+        k = find_kernel(RMSNORM_VARIANT_SHIFTED, dtype, 0, p->vectors_per_lane, 1, false);
+        if (k && static_cast<int64_t>(p->block_threads) * p->vectors_per_lane * epv < N + epv - 1)
+            return fail(RMSNORM_ERR_PLAN, "shifted plan does not cover N");
     } else {
         return fail(RMSNORM_ERR_PLAN, "unknown variant");
     }
@@ -300,6 +334,11 @@ int finish_plan(rmsnorm_plan_t* p, int64_t M, int64_t N, int dtype, bool vec, co
 // not fit the 128 VGPRs a 1024-thread workgroup allows without spilling).
 constexpr int kWaveSlots[] = {8, 4, 2, 1};
 constexpr int64_t kMaxVectors = 1024LL * 6;       // widest row the 16-byte kernels hold, in vectors
+constexpr int64_t kMaxShiftedChunks = 1024LL * 4;  // widest row the shifted kernel holds, in chunks
+// Shorter rows that start unaligned take the generic kernel: one row per
+// workgroup leaves most lanes idle there (262144 x 130 fp16: 107 us generic
+// against 144 us shifted; 16384 x 513 bf16: 17.7 us shifted against 22.8 us).
+constexpr int64_t kMinShiftedN = 256;
 constexpr int64_t kMaxGrid = 0x7FFFFFFF;
 constexpr int64_t kWaveBytesInFlight = 4096;      // row bytes one wave loads per trip
 constexpr int64_t kWaveBytesInFlightMultiRow = 2048;   // the same when a slot holds several rows
@@ -325,11 +364,20 @@ constexpr int64_t kBytesInFlightPerCu = 64 * 1024; // row bytes resident per com
 //    most about 64 KiB of rows resident per compute unit (max_blocks_per_cu
 //    4 at 16 KiB rows); together 5-6% faster on 32768 x 8192, 4% on
 //    8192 x 3000.
-int choose_plan(int64_t M, int64_t N, int dtype, bool vec, rmsnorm_plan_t* p) {
+int choose_plan(int64_t M, int64_t N, int dtype, Access acc, rmsnorm_plan_t* p) {
     std::memset(p, 0, sizeof(*p));
+    const bool vec = acc.vec;
     const int64_t es = elem_size(dtype);
     const int64_t nvec = ceil_div(N, elems_per_vector(dtype));
-    if (!vec || nvec > kMaxVectors) {
+    const int64_t nchunks = ceil_div(N + elems_per_vector(dtype) - 1, elems_per_vector(dtype));
+    if (!vec && acc.shifted && N >= kMinShiftedN && nchunks <= kMaxShiftedChunks) {
+        // one row per workgroup: 64 threads for short rows, else 256 (up to
+        // 1024 chunks) or 1024 threads, each thread ceil(chunks / threads) chunks
+        p->variant = RMSNORM_VARIANT_SHIFTED;
+        p->row_slots = 1;
+        p->block_threads = nchunks <= 64 ? 64 : (nchunks <= 256 * 4 ? 256 : 1024);
+        p->vectors_per_lane = static_cast<int>(ceil_div(nchunks, p->block_threads));
+    } else if (!vec || nvec > kMaxVectors) {
         p->variant = RMSNORM_VARIANT_GENERIC;
         p->block_threads = N >= 1024 ? 256 : (N >= 256 ? 128 : 64);
         p->row_slots = 1;
@@ -375,7 +423,7 @@ int choose_plan(int64_t M, int64_t N, int dtype, bool vec, rmsnorm_plan_t* p) {
     p->grid = need < kMaxGrid ? need : kMaxGrid;
     p->xcd_group = 1;
     p->max_blocks_per_cu = 0;
-    if (p->variant == RMSNORM_VARIANT_BLOCK) {
+    if (p->variant == RMSNORM_VARIANT_BLOCK || p->variant == RMSNORM_VARIANT_SHIFTED) {
         // about 128 KiB of consecutive rows per XCD (a power of two, at least 8 rows)
         const int64_t row_bytes = N * es;
         int g = 8;
@@ -707,15 +755,15 @@ bool tuned_plan(int64_t M, int64_t N, int dtype, rmsnorm_plan_t* out) {
     return true;
 }
 
-int select_plan(int64_t M, int64_t N, int dtype, bool vec, rmsnorm_plan_t* p, const KernelEntry** k) {
+int select_plan(int64_t M, int64_t N, int dtype, Access acc, rmsnorm_plan_t* p, const KernelEntry** k) {
     rmsnorm_plan_t t;
-    if (tuned_plan(M, N, dtype, &t) && finish_plan(&t, M, N, dtype, vec, k) == RMSNORM_OK) {
+    if (tuned_plan(M, N, dtype, &t) && finish_plan(&t, M, N, dtype, acc, k) == RMSNORM_OK) {
         *p = t;
         return RMSNORM_OK;
     }
     g_last_error.clear();
-    int st = choose_plan(M, N, dtype, vec, p);
-    if (st == RMSNORM_OK) st = finish_plan(p, M, N, dtype, vec, k);
+    int st = choose_plan(M, N, dtype, acc, p);
+    if (st == RMSNORM_OK) st = finish_plan(p, M, N, dtype, acc, k);
     return st;
 }
 
@@ -732,17 +780,17 @@ int fwd_common(const void* x, const void* w, void* y, float* rstd, int64_t M, in
     st = check_args(x, w, y, rstd, M, N, eps, offset, dtype, L, rstd_optional);
     if (st != RMSNORM_OK) return st;
     if (plan_required && !plan) return fail(RMSNORM_ERR_NULL, "plan must be non-NULL");
-    const bool vec = vector_ok(x, w, y, dtype, L, M);
+    const Access acc = access_of(x, w, y, dtype, L, M);
     const int64_t Mb = M > 0 ? L.rows : 0;    // plans cover one batch
     rmsnorm_plan_t p;
     const KernelEntry* k = nullptr;
     if (plan) {
         p = *plan;
-        st = finish_plan(&p, Mb, N, dtype, vec, &k);
+        st = finish_plan(&p, Mb, N, dtype, acc, &k);
         if (st != RMSNORM_OK || M == 0) return st;
     } else {
         if (M == 0) return RMSNORM_OK;
-        st = select_plan(Mb, N, dtype, vec, &p, &k);
+        st = select_plan(Mb, N, dtype, acc, &p, &k);
         if (st != RMSNORM_OK) return st;
     }
     int cu = 0, lds = 0;
@@ -785,7 +833,7 @@ int rmsnorm_plan_query_ex(int64_t M, int64_t N, int dtype, const void* x, const 
     if (st != RMSNORM_OK) return st;
     rmsnorm_plan_t p;
     const KernelEntry* k = nullptr;
-    st = select_plan(M > 0 ? L.rows : 0, N, dtype, vector_ok(x, w, y, dtype, L, M), &p, &k);
+    st = select_plan(M > 0 ? L.rows : 0, N, dtype, access_of(x, w, y, dtype, L, M), &p, &k);
     if (st == RMSNORM_OK) st = resident_grid(&p, k, cu_count, &p.resident_grid);
     if (st != RMSNORM_OK) return st;
     *out = p;
@@ -805,7 +853,7 @@ int rmsnorm_plan_validate(int64_t M, int64_t N, int dtype, const void* x, const 
     if (st != RMSNORM_OK) return st;
     rmsnorm_plan_t p = *plan;
     const KernelEntry* k = nullptr;
-    st = finish_plan(&p, M, N, dtype, vector_ok(x, w, y, dtype, contiguous_layout(M, N), M), &k);
+    st = finish_plan(&p, M, N, dtype, access_of(x, w, y, dtype, contiguous_layout(M, N), M), &k);
     if (st == RMSNORM_OK) st = resident_grid(&p, k, cu_count, &p.resident_grid);
     if (st != RMSNORM_OK) return st;
     *out = p;
@@ -823,6 +871,8 @@ int rmsnorm_plan_resources(const rmsnorm_plan_t* plan, int dtype, int32_t* vgprs
     if (plan->variant == RMSNORM_VARIANT_GENERIC) k = find_kernel(RMSNORM_VARIANT_GENERIC, dtype, 0, 0, 1, false);
     else if (plan->variant == RMSNORM_VARIANT_BLOCK)
         k = find_kernel(RMSNORM_VARIANT_BLOCK, dtype, 0, plan->vectors_per_lane, 1, pf);
+    else if (plan->variant == RMSNORM_VARIANT_SHIFTED)
+        k = find_kernel(RMSNORM_VARIANT_SHIFTED, dtype, 0, plan->vectors_per_lane, 1, false);
     else if (plan->variant == RMSNORM_VARIANT_WAVE)
         k = find_kernel(RMSNORM_VARIANT_WAVE, dtype, plan->lanes_per_row, plan->vectors_per_lane, plan->row_slots, pf);
     if (!k) return fail(RMSNORM_ERR_PLAN, "no compiled kernel for this plan");
@@ -894,7 +944,7 @@ int rmsnorm_plan_set_tuned(int64_t M, int64_t N, int dtype, const rmsnorm_plan_t
     if (M == 0) return fail(RMSNORM_ERR_SHAPE, "a tuned plan needs M > 0");
     rmsnorm_plan_t p = *plan;
     const KernelEntry* k = nullptr;
-    st = finish_plan(&p, M, N, dtype, vector_ok(nullptr, nullptr, nullptr, dtype, contiguous_layout(M, N), M),
+    st = finish_plan(&p, M, N, dtype, access_of(nullptr, nullptr, nullptr, dtype, contiguous_layout(M, N), M),
                      &k);  // aligned pointers
     if (st != RMSNORM_OK) return st;
     std::lock_guard<std::mutex> lock(g_tuned_mu);

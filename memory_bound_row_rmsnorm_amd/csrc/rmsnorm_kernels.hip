@@ -9,7 +9,7 @@
 // vector holds D::EPV = 8 or 4 elements).  Rows may be strided, in one or
 // more batches (the grid's y dimension); a width that is not a multiple of
 // EPV ends in a tail vector moved element by element; rstd may be NULL.
-// Three families:
+// Four families:
 //
 //  * rmsnorm_wave   -- a row lives in a segment of 16, 32 or 64 lanes of one
 //    wavefront, each lane holding VPL 16-byte vectors of it; a wave carries
@@ -20,8 +20,11 @@
 //  * rmsnorm_block  -- one row per workgroup per trip, each thread holding VPT
 //    16-byte vectors; wave sums meet in LDS behind one barrier per trip
 //    (double-buffered partials).  For large N.
-//  * rmsnorm_generic -- any N and any alignment, 2-byte accesses, the row read
-//    a second time (from cache) to normalise.  Correctness fallback.
+//  * rmsnorm_shifted -- rows that do not start 16-byte aligned (contiguous
+//    rows with N % EPV != 0): aligned 16-byte chunks, per-row shifted weights,
+//    element-wise edges.
+//  * rmsnorm_generic -- any N and any alignment, element accesses, the row
+//    read a second time (from cache) to normalise.  Correctness fallback.
 //
 // Each family loops over rows with a grid stride, so a grid smaller than the
 // row count is a persistent grid that keeps offset + w in registers across
@@ -372,6 +375,128 @@ __global__ __launch_bounds__(1024) void rmsnorm_block(KernelArgs a) {
 }
 
 // ---------------------------------------------------------------------------
+// Shifted family: rows that do not start on a 16-byte boundary (contiguous
+// rows of N elements with N % EPV != 0 start a different number of elements
+// past one on every row).  One row per workgroup per trip.  The row is read
+// as the aligned 16-byte chunks that cover it: with `al` the row start's
+// distance in elements past a boundary, chunk c holds row elements
+// c * EPV - al .. c * EPV - al + EPV - 1.  Interior chunks lie inside the row
+// and move with one 16-byte load and store each; the first and last chunk
+// share their 16 bytes with neighbouring rows and move element by element,
+// only the row's own elements.  The weights of chunk c are vectors c - 1 and
+// c of w funnel-shifted by EPV - al elements (v_alignbyte on the packed
+// words).  x and y must sit the same distance past a boundary on every row.
+// ---------------------------------------------------------------------------
+// Words k .. k + 3 of the 8-word concatenation (lo, hi) starting `sh`
+// elements in (0 < sh <= EPV), for the wave-uniform sh of one row.
+template <class D>
+__device__ __forceinline__ u32x4 funnel(const u32x4 lo, const u32x4 hi, int sh) {
+    constexpr int EPW = 4 / static_cast<int>(sizeof(typename D::elem_t));   // elements per word
+    const uint32_t W[9] = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3], 0u};
+    const int q = sh / EPW;                                                 // whole words
+    const uint32_t r = static_cast<uint32_t>((sh % EPW) * sizeof(typename D::elem_t));   // bytes
+    u32x4 o;
+    switch (q) {    // q is the same in every lane: one branch, constant register indices
+#define RMS_FUNNEL_CASE(Q)                                                                   \
+        case Q:                                                                              \
+            for (int k = 0; k < 4; ++k) o[k] = __builtin_amdgcn_alignbyte(W[k + Q + 1], W[k + Q], r); \
+            break;
+        RMS_FUNNEL_CASE(0) RMS_FUNNEL_CASE(1) RMS_FUNNEL_CASE(2) RMS_FUNNEL_CASE(3)
+#undef RMS_FUNNEL_CASE
+        default:
+            o = hi;
+            break;
+    }
+    return o;
+}
+
+// The row's own elements of an edge chunk (row elements j0 .. j0 + EPV - 1,
+// those outside 0 .. N - 1 read as zero and never touched).
+template <class D>
+__device__ __forceinline__ u32x4 load_edge(const u32x4* p, int64_t j0, int64_t N) {
+    typedef typename D::elem_t E;
+    const E* q = reinterpret_cast<const E*>(p);
+    E e[D::EPV];
+#pragma unroll
+    for (int i = 0; i < D::EPV; ++i) e[i] = (j0 + i >= 0 && j0 + i < N) ? q[i] : E(0);
+    return __builtin_bit_cast(u32x4, e);
+}
+
+template <class D>
+__device__ __forceinline__ void store_edge(u32x4* p, u32x4 v, int64_t j0, int64_t N) {
+    typedef typename D::elem_t E;
+    E* q = reinterpret_cast<E*>(p);
+    const auto e = __builtin_bit_cast(E __attribute__((ext_vector_type(D::EPV))), v);
+#pragma unroll
+    for (int i = 0; i < D::EPV; ++i)
+        if (j0 + i >= 0 && j0 + i < N) q[i] = e[i];
+}
+
+template <class D, int VPT>
+__global__ __launch_bounds__(1024) void rmsnorm_shifted(KernelArgs a) {
+    typedef typename D::elem_t E;
+    constexpr int EPV = D::EPV;
+    __shared__ float part[2][16];
+    const int64_t M = a.M;
+    const int64_t N = a.N;
+    const E* xb = static_cast<const E*>(a.x) + batch() * a.x_bs;
+    E* yb = static_cast<E*>(a.y) + batch() * a.y_bs;
+    const u32x4* __restrict__ w = static_cast<const u32x4*>(a.w);
+    const int nfull_w = static_cast<int>(N / EPV), tail_w = static_cast<int>(N % EPV);
+    const int tid = threadIdx.x;
+    const int nt = a.threads;
+    const int lane = tid & 63;
+    const int wid = tid >> 6;
+    const int nw = nt >> 6;
+
+    auto wvec = [&](int k) -> u32x4 { return k < 0 ? kZero : load_vec<D, false, true>(w, k, nfull_w, tail_w); };
+
+    int par = 0;
+    for (int64_t row = grouped_block(a.xcd_group, a.grid); row < M; row += a.grid) {
+        const E* xr = xb + row * a.x_rs;
+        E* yr = yb + row * a.y_rs;
+        // distance past a 16-byte boundary, in elements; the same for y
+        const int al = __builtin_amdgcn_readfirstlane(
+            static_cast<int>((reinterpret_cast<uintptr_t>(xr) & 15u) / sizeof(E)));
+        const u32x4* xc = reinterpret_cast<const u32x4*>(xr - al);
+        u32x4* yc = reinterpret_cast<u32x4*>(yr - al);
+        const int nch = static_cast<int>((al + N + EPV - 1) / EPV);
+        const bool ragged_end = ((al + N) % EPV) != 0;
+
+        u32x4 d[VPT];
+#pragma unroll
+        for (int v = 0; v < VPT; ++v) {
+            const int c = v * nt + tid;
+            const bool edge = (c == 0 && al != 0) || (c == nch - 1 && ragged_end);
+            d[v] = c >= nch ? kZero
+                            : (edge ? load_edge<D>(xc + c, static_cast<int64_t>(c) * EPV - al, N) : load_x(xc + c));
+        }
+        const float ss = segment_allreduce<64>(sum_squares<D, VPT>(d));
+        if (lane == 0) part[par][wid] = ss;
+        __syncthreads();
+        float tot = part[par][0];
+        for (int i = 1; i < nw; ++i) tot += part[par][i];
+        const float r = rsq(__builtin_fmaf(tot, a.inv_n, a.eps));
+#pragma unroll
+        for (int v = 0; v < VPT; ++v) {
+            const int c = v * nt + tid;
+            if (c < nch) {
+                float we[EPV];
+                // (loading these two weight vectors before the reduction measured
+                // slower: the registers they hold cost two waves per SIMD)
+                widen_weights<D>(we, al == 0 ? wvec(c) : funnel<D>(wvec(c - 1), wvec(c), EPV - al), a.offset);
+                const u32x4 o = normalise<D>(d[v], we, r);
+                const bool edge = (c == 0 && al != 0) || (c == nch - 1 && ragged_end);
+                if (edge) store_edge<D>(yc + c, o, static_cast<int64_t>(c) * EPV - al, N);
+                else store_y(yc + c, o);
+            }
+        }
+        if (tid == 0 && a.rstd != nullptr) store_rstd(a.rstd + batch() * M + row, r);
+        par ^= 1;
+    }
+}
+
+// ---------------------------------------------------------------------------
 // Generic family: any N, any element alignment, any strides.  x and y may be
 // the same buffer with the same layout: every element is read and then
 // written by the same thread, and the sum of squares of a row is complete
@@ -430,6 +555,9 @@ __global__ __launch_bounds__(1024) void rmsnorm_generic(KernelArgs a) {
      "rmsnorm_block<" #D "," #V "," #P "," #T ">"}
 #define RMS_BLOCK(D, DT, V, P) RMS_BLOCK_T(D, DT, V, P, true)
 #define RMS_BLOCK2(D, DT, V) RMS_BLOCK(D, DT, V, false), RMS_BLOCK(D, DT, V, true)
+#define RMS_SHIFTED(D, DT, V)                                                                  \
+    {RMSNORM_VARIANT_SHIFTED, DT, 0, V, 1, false, true,                                           \
+     reinterpret_cast<const void*>(&rmsnorm_shifted<D, V>), "rmsnorm_shifted<" #D "," #V ">"}
 // Only instances that fit 128 VGPRs (the budget of a 1024-thread workgroup)
 // without scratch are compiled.  The widest forms leave out the tail path
 // (last argument false), which they have no registers for: they serve
@@ -445,6 +573,7 @@ __global__ __launch_bounds__(1024) void rmsnorm_generic(KernelArgs a) {
     RMS_WAVE2(D, DT, 64, 4, 1), RMS_WAVE2(D, DT, 64, 5, 1),                                     \
     RMS_BLOCK2(D, DT, 1), RMS_BLOCK2(D, DT, 2), RMS_BLOCK2(D, DT, 3), RMS_BLOCK2(D, DT, 4),     \
     RMS_BLOCK(D, DT, 5, false), RMS_BLOCK_T(D, DT, 5, true, false),                             \
+    RMS_SHIFTED(D, DT, 1), RMS_SHIFTED(D, DT, 2), RMS_SHIFTED(D, DT, 3), RMS_SHIFTED(D, DT, 4),   \
     {RMSNORM_VARIANT_GENERIC, DT, 0, 0, 1, false, true,                                         \
      reinterpret_cast<const void*>(&rmsnorm_generic<D>), "rmsnorm_generic<" #D ">"}
 

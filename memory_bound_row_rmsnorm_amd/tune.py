@@ -67,6 +67,17 @@ def candidates(M: int, N: int, dtype: str, quick: bool = False) -> list:
                 raw.append(base.copy(variant=2, lanes_per_row=threads, vectors_per_lane=vpt, row_slots=1,
                                      block_threads=threads, prefetch=0, xcd_group=g, max_blocks_per_cu=cap,
                                      grid=M))
+    else:
+        # rows that start unaligned: the shifted kernel (aligned chunks, per-row shifted weights)
+        nch = -(-(N + 7) // 8)
+        groups = (1, 8, 16) if quick else (1, 4, 8, 16)
+        for threads in (64, 128, 256, 512, 1024):
+            vpt = -(-nch // threads)
+            if threads > max(64, nch) or vpt > 4:
+                continue
+            for g in groups:
+                raw.append(base.copy(variant=4, lanes_per_row=threads, vectors_per_lane=vpt, row_slots=1,
+                                     block_threads=threads, prefetch=0, xcd_group=g, max_blocks_per_cu=0, grid=M))
     for threads in (64, 256, 1024):
         raw.append(base.copy(variant=3, block_threads=threads, prefetch=0, xcd_group=1, max_blocks_per_cu=0,
                              grid=M))
@@ -139,8 +150,8 @@ def describe(p) -> str:
     name = binding.VARIANT_NAMES.get(p.variant, str(p.variant))
     if p.variant == 1:
         s = f"wave {p.lanes_per_row}x{p.vectors_per_lane} lanes x vectors, {p.row_slots} slots, {p.block_threads} thr"
-    elif p.variant == 2:
-        s = f"block {p.block_threads} thr x {p.vectors_per_lane} vectors"
+    elif p.variant in (2, 4):
+        s = f"{name} {p.block_threads} thr x {p.vectors_per_lane} vectors"
     else:
         s = f"{name} {p.block_threads} thr"
     if p.xcd_group > 1:

@@ -8,9 +8,11 @@ Recipe (every workload, every seed):
   1. ``g = torch.Generator('cpu').manual_seed(seed)``
   2. ``zx = torch.randn(M, N, generator=g)`` then ``zw = torch.randn(N, generator=g)``;
      for the outlier-channel workload also ``cols = torch.randperm(N, generator=g)[:k]``
-     with ``k = round(0.01 * N)``.
-  3. ``x = sigma * zx`` (outlier columns multiplied by 50, in fp32), cast once to
-     the dtype; ``w = w_mean + 0.1 * zw`` cast once to the dtype.
+     with ``k = round(0.01 * N)``; for the outlier-entry workload instead
+     ``hit = torch.rand(M, N, generator=g) < 0.01``.
+  3. ``x = sigma * zx`` (outlier columns, or outlier entries, multiplied by 50,
+     in fp32), cast once to the dtype; ``w = w_mean + 0.1 * zw`` cast once to
+     the dtype.
 
 The shapes, dtypes, value spreads, eps and offset are those of the row RMSNorm
 workloads the pages discuss: the 16384 x 512 bf16 shape measured in "Why cutile's
@@ -43,6 +45,7 @@ class Workload:
     eps: float
     offset: float
     outlier_channels: bool = False   # 1% of the columns scaled by 50
+    outlier_entries: bool = False    # each entry scaled by 50 with probability 0.01
 
     @property
     def elem_bytes(self) -> int:
@@ -65,6 +68,8 @@ WORKLOADS = {
         Workload("rmsnorm_8192x3000_bf16_offset1", 8192, 3000, "bf16", 2.0, 0.0, 1e-6, 1.0),
         Workload("rmsnorm_32768x8192_bf16_outliers", 32768, 8192, "bf16", 1.0, 1.0, 1e-5, 0.0,
                  outlier_channels=True),
+        Workload("rmsnorm_32768x8192_bf16_outlier_entries", 32768, 8192, "bf16", 1.0, 1.0, 1e-5, 0.0,
+                 outlier_entries=True),
         Workload("rmsnorm_262144x128_fp16", 262144, 128, "fp16", 100.0, 1.0, 1e-6, 0.0),
         Workload("rmsnorm_262144x128_bf16", 262144, 128, "bf16", 1.0, 1.0, 1e-6, 0.0),
         Workload("rmsnorm_4096x16384_fp16", 4096, 16384, "fp16", 100.0, 1.0, 1e-6, 0.0),
@@ -93,6 +98,9 @@ def make_inputs(wl: Workload, seed: int = 0, rows: int | None = None):
     if wl.outlier_channels:
         cols = torch.randperm(wl.N, generator=g)[: outlier_count(wl.N)]
         x[:, cols] *= 50.0
+    if wl.outlier_entries:
+        hit = torch.rand(M, wl.N, generator=g) < 0.01
+        x[hit] *= 50.0
     w = zw.mul_(0.1).add_(wl.w_mean)
     td = TORCH_DTYPES[wl.dtype]
     return x.to(td), w.to(td)

@@ -161,10 +161,21 @@ def test_huge_row_counts_loop_with_prefetch():
     assert p.grid == 0x7FFFFFFF and p.trips > 1 and p.prefetch == 1
 
 
-@pytest.mark.parametrize("N,x", [(7, None), (3001, None), (127, None), (512, A + 2), (512, A + 8),
-                                 (49160, None), (1 << 17, None)])
-def test_unaligned_or_odd_rows_take_the_generic_kernel(N, x):
-    p = host_plan(10, N, x=x)
+@pytest.mark.parametrize("N", [257, 3001, 1025, 32761])
+def test_ragged_contiguous_rows_take_the_shifted_kernel(N):
+    p = host_plan(10, N)                       # rows start a varying distance past a 16-byte boundary
+    assert p.variant == bnd.VARIANT_SHIFTED and p.vec_elems == 8
+    assert p.block_threads * p.vectors_per_lane * 8 >= N + 7 and p.rows_per_trip == 1
+    f = host_plan(10, N, dtype=FP16, x=A + 2, y=A + 2 + 0x1000000)    # equally misaligned x and y
+    assert f.variant == bnd.VARIANT_SHIFTED
+
+
+@pytest.mark.parametrize("N,x,w", [(512, A + 2, None), (512, A + 8, None),   # x and y not equally aligned
+                                   (3001, None, A + 2),                        # w not 16-byte aligned
+                                   (49160, None, None), (1 << 17, None, None),  # wider than the kernels hold
+                                   (7, None, None), (255, None, None)])         # short unaligned rows
+def test_unaligned_or_very_wide_rows_take_the_generic_kernel(N, x, w):
+    p = host_plan(10, N, x=x, w=w)
     assert p.variant == bnd.VARIANT_GENERIC and p.vec_elems == 1
 
 
@@ -417,7 +428,8 @@ def test_layouts_choose_the_vector_kernels_when_rows_stay_aligned():
     # ragged widths on aligned rows: the vector kernels with their tail path
     p = query_ex(4096, 3001, layout=(0, 3008, 0, 3008, 0))
     assert p.variant == bnd.VARIANT_BLOCK and p.block_threads * p.vectors_per_lane * 8 >= 3001
-    assert query_ex(4096, 3001).variant == bnd.VARIANT_GENERIC      # contiguous rows of 3001 are unaligned
+    assert query_ex(4096, 3001).variant == bnd.VARIANT_SHIFTED      # contiguous rows of 3001 are unaligned
+    assert query_ex(4096, 3001, layout=(0, 3001, 0, 3002, 0)).variant == bnd.VARIANT_GENERIC   # y differs
     assert query_ex(4096, 100, layout=(0, 104, 0, 104, 0)).variant == bnd.VARIANT_WAVE
     # batches: the plan covers one batch's rows
     p = query_ex(8 * 1000, 512, layout=(1000, 512, 1024 * 512, 512, 1000 * 512))

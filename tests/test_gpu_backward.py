@@ -45,7 +45,8 @@ def run_bwd(bnd, wl, x, w, dy, r32, plan=None, what=""):
 
 
 FULL = {"rmsnorm_64x512_bf16": None, "rmsnorm_16384x512_bf16": None, "rmsnorm_8192x3000_bf16_offset1": None,
-        "rmsnorm_32768x8192_bf16_outliers": 4096, "rmsnorm_262144x128_fp16": 65536,
+        "rmsnorm_32768x8192_bf16_outliers": 4096, "rmsnorm_32768x8192_bf16_outlier_entries": 2048,
+        "rmsnorm_262144x128_fp16": 65536,
         "rmsnorm_262144x128_bf16": 65536, "rmsnorm_4096x16384_fp16": 1024}
 
 

@@ -220,3 +220,77 @@ def test_fp32_sweep(bnd, N):
             torch.cuda.synchronize()
             ye, re = parity.oracle_fp32(x, w, 1e-6, offset)
             parity.compare_fp32(y, r, ye, re, f"fp32 sweep M={M} N={N} off={offset}")
+
+
+# ---------------------------------------------------------------------------
+# The shifted kernel: rows that do not start 16-byte aligned.
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float16, torch.float32])
+@pytest.mark.parametrize("N", [1, 7, 9, 100, 1001, 3001, 8191, 20001])
+def test_shifted_every_instance(bnd, dtype, N):
+    M = 37 if N < 8000 else 11
+    sigma = 100.0 if dtype == torch.float16 else 1.0
+    x = draw((M, N), dtype, 91, sigma).to(DEV)
+    w = (1.0 + 0.1 * draw((N,), torch.float32, 92)).to(dtype).to(DEV)
+    xc, wc = x.cpu(), w.cpu()
+    if dtype == torch.float32:
+        ref = parity.oracle_fp32(xc, wc, 1e-6, 1.0)
+    else:
+        dt = "bf16" if dtype == torch.bfloat16 else "fp16"
+        ref = parity.oracle_for(xc, wc, 1e-6, 1.0, dt)
+    base = bnd.plan_query_ex(x, w)
+    es = x.element_size()
+    epv = 16 // es
+    if (N * es) % 16 == 0 or -(-(N + epv - 1) // epv) > 4096:
+        # aligned rows take the vector kernels, rows wider than 4096 chunks the generic one
+        assert base.as_dict()["variant_name"] != "shifted"
+        return
+    # the rule takes the shifted kernel from 256 elements up; explicit plans run it at any width
+    assert base.as_dict()["variant_name"] == ("shifted" if N >= 256 else "generic")
+    ran = 0
+    for threads in (64, 128, 256, 512, 1024):
+        for vpt in (1, 2, 3, 4):
+            for grid in (M, 5):
+                p = base.copy(variant=bnd.VARIANT_SHIFTED, block_threads=threads, vectors_per_lane=vpt,
+                              row_slots=1, prefetch=0, grid=grid, xcd_group=1, max_blocks_per_cu=0)
+                if bnd.plan_validate(M, N, x.dtype, p, x.data_ptr(), w.data_ptr(), x.data_ptr()) is None:
+                    continue                     # does not cover N (the in-place pointers are equally aligned)
+                y_base = filled(M * N + 16, dtype)
+                y = y_base.as_strided((M, N), (N, 1), 8)
+                announce("shifted", M, N, dtype, threads, vpt, grid)
+                out, rstd = bnd.rmsnorm_fwd_ex(x, w, 1e-6, 1.0, out=y, plan=p)
+                torch.cuda.synchronize()
+                what = f"shifted {M}x{N} {dtype} {threads}x{vpt} grid {grid}"
+                if dtype == torch.float32:
+                    parity.compare_fp32(out, rstd, ref[0], ref[1], what)
+                else:
+                    parity.compare(out, rstd, ref[0], ref[1], dt, what)
+                mask = view_mask(y_base.numel(), (M, N), (N, 1), 8)
+                assert bool((y_base.cpu().view(INT_VIEW[dtype])[~mask] == SENTINEL[dtype]).all()), what
+                ran += 1
+    assert ran >= (2 if N > 8000 else 6), ran
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+def test_equally_misaligned_operands(bnd, dtype):
+    M, N = 300, 512                                            # rows of 16-byte multiples, bases 1 element off
+    xb = draw((M * N + 1,), dtype, 95).to(DEV)
+    x = xb[1:].view(M, N)
+    w = (1.0 + 0.1 * draw((N,), torch.float32, 96)).to(dtype).to(DEV)
+    y_base = filled(M * N + 9, dtype)
+    y = y_base.as_strided((M, N), (N, 1), 1)
+    plan = check(bnd, x, w, y, y_base, (M, N), (N, 1), 1, what="misaligned bases")
+    assert plan.as_dict()["variant_name"] == "shifted"
+
+
+def test_shifted_in_place(bnd):
+    M, N = 257, 3001
+    x = draw((M, N), torch.float16, 97, 100.0).to(DEV)
+    w = (1.0 + 0.1 * draw((N,), torch.float32, 98)).to(torch.float16).to(DEV)
+    xc = x.cpu()
+    announce("shifted in place", M, N)
+    assert bnd.plan_query_ex(x, w, x).as_dict()["variant_name"] == "shifted"
+    out, rstd = bnd.rmsnorm_fwd_ex(x, w, 1e-6, 0.0, out=x)
+    torch.cuda.synchronize()
+    yr, rr = parity.oracle_for(xc, w.cpu(), 1e-6, 0.0, "fp16")
+    parity.compare(out, rstd, yr, rr, "fp16", "shifted in place")
