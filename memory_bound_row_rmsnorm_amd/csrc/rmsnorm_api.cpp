@@ -218,7 +218,8 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 // final partial vector moves element by element).
 bool vector_ok(const void* x, const void* w, const void* y, int dtype, const Layout& L, int64_t M) {
     const int64_t es = elem_size(dtype);
-    const bool rows_ok = (L.x_rs * es) % 16 == 0 && (L.y_rs * es) % 16 == 0;
+    const bool rows_ok = (L.x_rs * es) % 16 == 0 && (L.y_rs * es) % 16 == 0 &&
+                         L.x_rs * es / 16 < INT32_MAX && L.y_rs * es / 16 < INT32_MAX;
     const bool batches_ok = L.batches(M) <= 1 || ((L.x_bs * es) % 16 == 0 && (L.y_bs * es) % 16 == 0);
     return aligned16(x) && aligned16(w) && aligned16(y) && rows_ok && batches_ok;
 }
@@ -493,6 +494,10 @@ int launch(const KernelEntry* k, const rmsnorm_plan_t* p, const void* x, const v
         a.y_rs = L.y_rs;
         a.x_bs = L.x_bs;
         a.y_bs = L.y_bs;
+        // the vector kernels' row strides in 16-byte vectors (checked to fit 31 bits by vector_ok)
+        const int64_t epv = elems_per_vector(dtype);
+        a.x_rsv = static_cast<int32_t>(L.x_rs / epv);
+        a.y_rsv = static_cast<int32_t>(L.y_rs / epv);
         void* args[] = {&a};
         hipError_t e = hipLaunchKernel(k->func, dim3(static_cast<unsigned>(p->grid), static_cast<unsigned>(nb)),
                                        dim3(static_cast<unsigned>(p->block_threads)), args, dyn_lds,

@@ -28,9 +28,11 @@ struct KernelArgs {
     int64_t grid;
     int32_t threads;
     int32_t xcd_group;
-    int64_t x_rs;       // row stride of x, elements
+    int32_t x_rsv;      // row stride of x in 16-byte vectors (vector kernels; < 2^31)
+    int32_t y_rsv;      // row stride of y in 16-byte vectors
     int64_t x_bs;       // batch stride of x, elements
     const void* w;
+    int64_t x_rs;       // row stride of x, elements (element-wise kernels)
     // the rest: needed after the loads are in flight
     void* y;
     float* rstd;

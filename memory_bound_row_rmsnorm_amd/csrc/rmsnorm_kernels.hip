@@ -100,8 +100,14 @@ constexpr u32x4 kZero = {0u, 0u, 0u, 0u};
 
 // Batches of rows run as the grid's y dimension: batch b = blockIdx.y starts
 // b * bs elements into x and y and b * M entries into rstd, and its rows are
-// rs elements apart (no division anywhere).
+// rs elements apart (no division anywhere).  The first batch (every launch
+// without batches) skips the offset arithmetic.
 __device__ __forceinline__ int64_t batch() { return static_cast<int64_t>(blockIdx.y); }
+
+template <class T>
+__device__ __forceinline__ T* batch_base(T* p, int64_t stride) {
+    return __builtin_expect(blockIdx.y == 0, 1) ? p : p + batch() * stride;
+}
 
 // The last vector of a row whose width is not a multiple of EPV holds only
 // `tail` elements: they move one element at a time, so nothing past column
@@ -190,12 +196,12 @@ __global__ __launch_bounds__(1024) void rmsnorm_wave(KernelArgs a) {
     constexpr int SEG = 64 / LANES;       // rows per slot
     constexpr int ROWS = SEG * SLOTS;     // rows per wave per trip
     const int64_t M = a.M;
-    const u32x4* __restrict__ x = static_cast<const u32x4*>(a.x) + batch() * vectors<D>(a.x_bs);
+    const u32x4* __restrict__ x = batch_base(static_cast<const u32x4*>(a.x), vectors<D>(a.x_bs));
     const u32x4* __restrict__ w = static_cast<const u32x4*>(a.w);
-    u32x4* __restrict__ y = static_cast<u32x4*>(a.y) + batch() * vectors<D>(a.y_bs);
+    u32x4* __restrict__ y = batch_base(static_cast<u32x4*>(a.y), vectors<D>(a.y_bs));
     const int nfull = static_cast<int>(static_cast<uint64_t>(a.N) / D::EPV);
     const int tail = static_cast<int>(static_cast<uint64_t>(a.N) % D::EPV);
-    const int64_t x_rs = vectors<D>(a.x_rs), y_rs = vectors<D>(a.y_rs);
+    const int x_rs = a.x_rsv, y_rs = a.y_rsv;   // vectors (32-bit: one short multiply per row)
     const int lane = threadIdx.x & 63;
     const int seg = lane / LANES;
     const int li = lane % LANES;
@@ -216,7 +222,19 @@ __global__ __launch_bounds__(1024) void rmsnorm_wave(KernelArgs a) {
 #pragma unroll
             for (int v = 0; v < VPL; ++v) {
                 const int c = v * LANES + li;
-                d[s][v] = row < M ? load_vec<D, kStreamX, TAIL>(xr, c, nfull, tail) : kZero;
+                d[s][v] = (row < M && c < nfull) ? load_x(xr + c) : kZero;
+            }
+        }
+        // tail vectors: a pass of their own, skipped as a whole when N % EPV == 0
+        if constexpr (TAIL) {
+            if (__builtin_expect(tail != 0, 0)) {
+#pragma unroll
+                for (int s = 0; s < SLOTS; ++s) {
+                    const int64_t row = gg * ROWS + seg + s * SEG;
+#pragma unroll
+                    for (int v = 0; v < VPL; ++v)
+                        if (row < M && v * LANES + li == nfull) d[s][v] = load_tail<D>(x + row * x_rs + nfull, tail);
+                }
             }
         }
     };
@@ -301,12 +319,12 @@ template <class D, int VPT, bool PREFETCH, bool TAIL>
 __global__ __launch_bounds__(1024) void rmsnorm_block(KernelArgs a) {
     __shared__ float part[2][16];
     const int64_t M = a.M;
-    const u32x4* __restrict__ x = static_cast<const u32x4*>(a.x) + batch() * vectors<D>(a.x_bs);
+    const u32x4* __restrict__ x = batch_base(static_cast<const u32x4*>(a.x), vectors<D>(a.x_bs));
     const u32x4* __restrict__ w = static_cast<const u32x4*>(a.w);
-    u32x4* __restrict__ y = static_cast<u32x4*>(a.y) + batch() * vectors<D>(a.y_bs);
+    u32x4* __restrict__ y = batch_base(static_cast<u32x4*>(a.y), vectors<D>(a.y_bs));
     const int nfull = static_cast<int>(static_cast<uint64_t>(a.N) / D::EPV);
     const int tail = static_cast<int>(static_cast<uint64_t>(a.N) % D::EPV);
-    const int64_t x_rs = vectors<D>(a.x_rs), y_rs = vectors<D>(a.y_rs);
+    const int x_rs = a.x_rsv, y_rs = a.y_rsv;   // vectors (32-bit: one short multiply per row)
     const int tid = threadIdx.x;
     const int nt = a.threads;
     const int lane = tid & 63;
@@ -320,7 +338,14 @@ __global__ __launch_bounds__(1024) void rmsnorm_block(KernelArgs a) {
         const u32x4* xr = x + rr * x_rs;
         const bool live = rr < M;
 #pragma unroll
-        for (int v = 0; v < VPT; ++v) d[v] = live ? load_vec<D, kStreamX, TAIL>(xr, v * nt + tid, nfull, tail) : kZero;
+        for (int v = 0; v < VPT; ++v) d[v] = (live && v * nt + tid < nfull) ? load_x(xr + v * nt + tid) : kZero;
+        if constexpr (TAIL) {
+            if (__builtin_expect(tail != 0, 0)) {
+#pragma unroll
+                for (int v = 0; v < VPT; ++v)
+                    if (live && v * nt + tid == nfull) d[v] = load_tail<D>(xr + nfull, tail);
+            }
+        }
     };
 
     u32x4 d[VPT];
@@ -567,12 +592,12 @@ __global__ __launch_bounds__(1024) void rmsnorm_generic(KernelArgs a) {
     RMS_WAVE2(D, DT, 16, 1, 1), RMS_WAVE2(D, DT, 16, 1, 2), RMS_WAVE2(D, DT, 16, 1, 4),         \
     RMS_WAVE2(D, DT, 32, 1, 1), RMS_WAVE2(D, DT, 32, 1, 2), RMS_WAVE2(D, DT, 32, 1, 4),         \
     RMS_WAVE2(D, DT, 64, 1, 1), RMS_WAVE2(D, DT, 64, 1, 2), RMS_WAVE2(D, DT, 64, 1, 4),         \
-    RMS_WAVE(D, DT, 64, 1, 8, false), RMS_WAVE_T(D, DT, 64, 1, 8, true, false),                 \
-    RMS_WAVE2(D, DT, 64, 2, 1), RMS_WAVE2(D, DT, 64, 2, 2), RMS_WAVE(D, DT, 64, 2, 4, false),   \
-    RMS_WAVE2(D, DT, 64, 3, 1), RMS_WAVE2(D, DT, 64, 3, 2),                                     \
+    RMS_WAVE_T(D, DT, 64, 1, 8, false, false), RMS_WAVE_T(D, DT, 64, 1, 8, true, false),        \
+    RMS_WAVE2(D, DT, 64, 2, 1), RMS_WAVE2(D, DT, 64, 2, 2), RMS_WAVE_T(D, DT, 64, 2, 4, false, false), \
+    RMS_WAVE2(D, DT, 64, 3, 1), RMS_WAVE_T(D, DT, 64, 3, 2, false, false), RMS_WAVE(D, DT, 64, 3, 2, true), \
     RMS_WAVE2(D, DT, 64, 4, 1), RMS_WAVE2(D, DT, 64, 5, 1),                                     \
     RMS_BLOCK2(D, DT, 1), RMS_BLOCK2(D, DT, 2), RMS_BLOCK2(D, DT, 3), RMS_BLOCK2(D, DT, 4),     \
-    RMS_BLOCK(D, DT, 5, false), RMS_BLOCK_T(D, DT, 5, true, false),                             \
+    RMS_BLOCK(D, DT, 5, false),                                                                 \
     RMS_SHIFTED(D, DT, 1), RMS_SHIFTED(D, DT, 2), RMS_SHIFTED(D, DT, 3), RMS_SHIFTED(D, DT, 4),   \
     {RMSNORM_VARIANT_GENERIC, DT, 0, 0, 1, false, true,                                         \
      reinterpret_cast<const void*>(&rmsnorm_generic<D>), "rmsnorm_generic<" #D ">"}
