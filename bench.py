@@ -135,11 +135,13 @@ def traffic_from_counters(wl, name: str, directory: str) -> dict:
     }
 
 
-def cpu_baseline(wl, x_cpu, w_cpu, seconds: float):
+def cpu_baseline(wl, x_cpu, w_cpu, seconds: float, threads: int = 0):
     import oracle
     from memory_bound_row_rmsnorm_amd import workloads
 
     o = oracle.default()
+    if threads > 0:
+        o.set_threads(threads)
     xb, wb = workloads.to_bits(x_cpu), workloads.to_bits(w_cpu)
     o.rmsnorm_fwd(xb[:8], wb, wl.eps, wl.offset, wl.dtype)      # load, touch
     reps, t0 = 0, time.perf_counter()
@@ -294,6 +296,8 @@ def main() -> int:
     ap.add_argument("--traffic-from", default=None, metavar="DIR",
                     help="write profiles/traffic_<workload>.json from rocprofv3 counter CSVs in DIR "
                          "and exit (no GPU needed)")
+    ap.add_argument("--cpu-threads", type=int, default=0,
+                    help="threads of the CPU oracle baseline (0 = the OpenMP default: all host cores)")
     ap.add_argument("--tuned", default=None, metavar="JSON",
                     help="register the tuned plans of this file (python -m memory_bound_row_rmsnorm_amd.tune "
                          "--save) before planning")
@@ -458,7 +462,7 @@ def main() -> int:
     }
     if not args.no_cpu_baseline and args.kernel == "rmsnorm":
         log(f"cpu baseline: oracle for about {args.cpu_seconds:.0f} s")
-        out["cpu_baseline"] = cpu_baseline(wl, x0, w0, args.cpu_seconds)
+        out["cpu_baseline"] = cpu_baseline(wl, x0, w0, args.cpu_seconds, args.cpu_threads)
     print(json.dumps(out), flush=True)
     return 0
 

@@ -721,7 +721,10 @@ int launch_bwd(const KernelEntry* k, const rmsnorm_plan_t* p, const void* x, con
     void* rargs[] = {&partials, &dw, &G, &Nn, &vec4};
     const int64_t groups = vec4 ? N / 4 : N;        // column groups, 16 per workgroup
     const int64_t blocks = ceil_div(groups, 16);
-    hipError_t e = hipLaunchKernel(rmsnorm_impl::dw_reduce_kernel(), dim3(static_cast<unsigned>(blocks)), dim3(256),
+    // 64-way splits (1024 threads) once there are enough partial rows to share
+    const int split = G >= 128 ? 64 : 16;
+    hipError_t e = hipLaunchKernel(rmsnorm_impl::dw_reduce_kernel(split), dim3(static_cast<unsigned>(blocks)),
+                                   dim3(static_cast<unsigned>(16 * split)),
                                    rargs, 0, s);
     if (e != hipSuccess) return fail(RMSNORM_ERR_HIP, std::string("hipLaunchKernel(rmsnorm_dw_reduce): ") + hipGetErrorString(e));
     return RMSNORM_OK;

@@ -349,64 +349,61 @@ __global__ __launch_bounds__(1024) void rmsnorm_bwd_generic(BwdArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// Column pass: dw[j] = sum over the G partial rows.  A workgroup of 256
-// threads covers 64 columns (16 groups of 4) and splits the G partial rows 16
-// ways: thread (s, q) adds rows s, s + 16, s + 32, ... of columns 4q .. 4q + 3
-// in that order, and the 16 sub-sums are then added in order of s through
-// LDS -- a fixed order, so dw is the same on every run.  A wave reads four
-// partial rows of 256 contiguous bytes per load.  With vec4 (N % 4 == 0 and
-// dw 16-byte aligned; the workspace always is) columns move as float4,
-// otherwise one column per lane of a group.
+// Column pass: dw[j] = sum over the G partial rows.  A workgroup covers 64
+// columns (16 groups of 4) and splits the G partial rows SPLIT ways: thread
+// (s, q) adds rows s, s + SPLIT, s + 2 SPLIT, ... of columns 4q .. 4q + 3 in
+// that order; the SPLIT sub-sums then meet in LDS in a fixed order (groups of
+// 8 in order, then the groups in order), so dw is the same on every run.
+// SPLIT = 64 (1024 threads) gives every thread few rows: the partial rows
+// were just written from other XCDs' caches, and each sequential round of
+// loads costs a trip to memory.  With vec4 (N % 4 == 0 and dw 16-byte
+// aligned; the workspace always is) columns move as float4, otherwise one
+// column per lane of a group.
 // ---------------------------------------------------------------------------
 constexpr int kRedCols4 = 16;    // column groups per workgroup
-constexpr int kRedSplit = 16;    // ways each column's partial rows are split
 
-__global__ __launch_bounds__(256) void rmsnorm_dw_reduce(const float* __restrict__ partials,
-                                                         float* __restrict__ dw, int64_t G, int64_t N,
-                                                         int32_t vec4) {
-    __shared__ float4 red[kRedSplit][kRedCols4];
+__device__ __forceinline__ float4 add4(float4 a, const float4 b) {
+    a.x += b.x;
+    a.y += b.y;
+    a.z += b.z;
+    a.w += b.w;
+    return a;
+}
+
+template <int SPLIT>
+__global__ __launch_bounds__(16 * SPLIT) void rmsnorm_dw_reduce(const float* __restrict__ partials,
+                                                                float* __restrict__ dw, int64_t G, int64_t N,
+                                                                int32_t vec4) {
+    static_assert(SPLIT == 16 || SPLIT == 64, "split 16 or 64");
+    __shared__ float4 red[SPLIT][kRedCols4];
     const int q = threadIdx.x % kRedCols4;
     const int sp = threadIdx.x / kRedCols4;
     float4 acc = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
-    if (vec4) {
-        const int64_t c = (static_cast<int64_t>(blockIdx.x) * kRedCols4 + q) * 4;
-        if (c < N) {
-            int64_t i = sp;
+    const int64_t c = vec4 ? (static_cast<int64_t>(blockIdx.x) * kRedCols4 + q) * 4
+                           : static_cast<int64_t>(blockIdx.x) * kRedCols4 + q;
+    if (c < N) {
+        if (vec4) {
 #pragma unroll 4
-            for (; i < G; i += kRedSplit) {
-                const float4 p = *reinterpret_cast<const float4*>(partials + i * N + c);
-                acc.x += p.x;
-                acc.y += p.y;
-                acc.z += p.z;
-                acc.w += p.w;
-            }
-        }
-        red[sp][q] = acc;
-        __syncthreads();
-        if (sp == 0 && c < N) {
-            float4 t = red[0][q];
-            for (int k = 1; k < kRedSplit; ++k) {
-                const float4 u = red[k][q];
-                t.x += u.x;
-                t.y += u.y;
-                t.z += u.z;
-                t.w += u.w;
-            }
-            *reinterpret_cast<float4*>(dw + c) = t;
-        }
-    } else {
-        const int64_t c = static_cast<int64_t>(blockIdx.x) * kRedCols4 + q;
-        if (c < N) {
+            for (int64_t i = sp; i < G; i += SPLIT) acc = add4(acc, *reinterpret_cast<const float4*>(partials + i * N + c));
+        } else {
 #pragma unroll 4
-            for (int64_t i = sp; i < G; i += kRedSplit) acc.x += partials[i * N + c];
+            for (int64_t i = sp; i < G; i += SPLIT) acc.x += partials[i * N + c];
         }
-        red[sp][q] = acc;
-        __syncthreads();
-        if (sp == 0 && c < N) {
-            float t = red[0][q].x;
-            for (int k = 1; k < kRedSplit; ++k) t += red[k][q].x;
-            dw[c] = t;
-        }
+    }
+    red[sp][q] = acc;
+    __syncthreads();
+    constexpr int GROUPS = SPLIT / 8;    // 2 or 8 groups of 8 sub-sums
+    if (sp < GROUPS) {      // group sp reads and then overwrites only its own slots
+        float4 t = red[sp * 8][q];
+        for (int k = 1; k < 8; ++k) t = add4(t, red[sp * 8 + k][q]);
+        red[sp * 8][q] = t;
+    }
+    __syncthreads();
+    if (sp == 0 && c < N) {
+        float4 t = red[0][q];
+        for (int k = 1; k < GROUPS; ++k) t = add4(t, red[k * 8][q]);
+        if (vec4) *reinterpret_cast<float4*>(dw + c) = t;
+        else dw[c] = t.x;
     }
 }
 
@@ -448,6 +445,9 @@ const KernelEntry* bwd_kernel_table(int* count) {
     return kBwdTable;
 }
 
-const void* dw_reduce_kernel() { return reinterpret_cast<const void*>(&rmsnorm_dw_reduce); }
+const void* dw_reduce_kernel(int split) {
+    return split == 64 ? reinterpret_cast<const void*>(&rmsnorm_dw_reduce<64>)
+                       : reinterpret_cast<const void*>(&rmsnorm_dw_reduce<16>);
+}
 
 }  // namespace rmsnorm_impl

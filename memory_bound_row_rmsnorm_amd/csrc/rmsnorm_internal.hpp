@@ -80,6 +80,6 @@ const KernelEntry* kernel_table(int* count);
 // The column pass takes (const float* partials, float* dw, int64_t G, int64_t N,
 // int32_t vec4): vec4 = 1 when N % 4 == 0 and dw is 16-byte aligned.
 const KernelEntry* bwd_kernel_table(int* count);
-const void* dw_reduce_kernel();
+const void* dw_reduce_kernel(int split);   // split 16 (256 threads) or 64 (1024 threads)
 
 }  // namespace rmsnorm_impl

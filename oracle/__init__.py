@@ -90,6 +90,8 @@ class Oracle:
         lib.oracle_rmsnorm_bwd.restype = ctypes.c_int
         lib.oracle_max_threads.argtypes = []
         lib.oracle_max_threads.restype = ctypes.c_int
+        lib.oracle_set_threads.argtypes = [ctypes.c_int]
+        lib.oracle_set_threads.restype = None
         self.path = path
         self._lib = lib
 
@@ -184,6 +186,10 @@ class Oracle:
     def max_threads(self) -> int:
         """Threads the OpenMP loop uses (OMP_NUM_THREADS, else all cores)."""
         return int(self._lib.oracle_max_threads())
+
+    def set_threads(self, n: int) -> None:
+        """Threads for later calls (timing only; results do not depend on it)."""
+        self._lib.oracle_set_threads(int(n))
 
 
 _default: Oracle | None = None

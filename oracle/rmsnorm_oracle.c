@@ -284,6 +284,17 @@ int oracle_rmsnorm_bwd(const uint16_t* x, const uint16_t* w, const uint16_t* dy,
     return 0;
 }
 
+/* Threads the OpenMP loops use from now on (n >= 1); a timing knob only, the
+   results do not depend on it. */
+void oracle_set_threads(int n)
+{
+#ifdef _OPENMP
+    if (n >= 1) omp_set_num_threads(n);
+#else
+    (void)n;
+#endif
+}
+
 /* Threads the OpenMP loop above will use (1 without OpenMP). */
 int oracle_max_threads(void)
 {
