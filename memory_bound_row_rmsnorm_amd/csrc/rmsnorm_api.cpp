@@ -404,9 +404,11 @@ int choose_plan(int64_t M, int64_t N, int dtype, Access acc, rmsnorm_plan_t* p) 
     } else {
         p->variant = RMSNORM_VARIANT_BLOCK;
         p->row_slots = 1;
-        // 256 threads up to 6 vectors each; wider rows take 1024-thread
-        // workgroups (4096 x 16384: 47.5 us against 49.5 us with 512 x 4)
-        p->block_threads = nvec <= 256 * 6 ? 256 : 1024;
+        // 256 threads up to 4 vectors each, 512 up to 3, then 1024-thread
+        // workgroups (4096 x 10240 bf16: 29.7 us with 512 x 3 against 30.2 us
+        // with 256 x 5; 4096 x 12288 bf16: 35.3 us with 512 x 3, where six
+        // 16-bit vectors per thread have no compiled kernel)
+        p->block_threads = nvec <= 256 * 4 ? 256 : (nvec <= 512 * 3 ? 512 : 1024);
         p->vectors_per_lane = static_cast<int>(ceil_div(nvec, p->block_threads));
         // rows wider than the compiled instances hold (or a ragged width the
         // widest ones have no tail path for) take the generic kernel
@@ -653,8 +655,12 @@ int choose_bwd_plan(int64_t M, int64_t N, const void* x, const void* w, const vo
         p->vectors_per_lane = static_cast<int>(ceil_div(nvec, p->lanes_per_row));
         const int64_t per_slot = N * 2 * (64 / p->lanes_per_row);
         p->row_slots = 1;
+        // A row per 64-lane wave: one row per trip, the next trip's loads
+        // issued ahead (16384 x 512: 13.5 us against 15.0 us with four rows
+        // per wave loaded up front in one trip).  Shorter rows: several
+        // slots (flat within 3% on 262144 x 128).
         for (int sl : kBwdWaveSlots) {
-            if (sl * per_slot <= kWaveBytesInFlight &&
+            if (p->lanes_per_row < 64 && sl * per_slot <= kWaveBytesInFlight &&
                 find_bwd_kernel(RMSNORM_VARIANT_WAVE, dtype, p->lanes_per_row, p->vectors_per_lane, sl, false)) {
                 p->row_slots = sl;
                 break;

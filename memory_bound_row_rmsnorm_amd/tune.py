@@ -169,8 +169,8 @@ def tune_shape(M: int, N: int, dtype: str, quick: bool = False, log=print) -> li
     bufs = Buffers(M, N, dtype)
     cu = torch.cuda.get_device_properties(0).multi_processor_count
     nbytes = algorithmic_bytes(M, N)
-    est_us = nbytes / 5.0e3 + 2.0
-    steps = int(min(2000, max(20, 10000.0 / est_us)))
+    est_us = nbytes / 5.0e6 + 2.0      # at 5 TB/s (5e6 bytes per microsecond), plus the launch floor
+    steps = int(min(2000, max(20, 10000.0 / est_us)))   # about 10 ms of launches per replay
     results = []
     for i, p in enumerate(cands):
         dev_plan = binding.plan_validate(M, N, dtype, p, bufs.x[0].data_ptr(), bufs.w.data_ptr(),

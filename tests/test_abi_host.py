@@ -151,9 +151,21 @@ def test_planner_choices_for_the_workloads():
     p = host_plan(3, 40960)
     assert (p.block_threads, p.vectors_per_lane, p.max_blocks_per_cu) == (1024, 5, 0)
     assert host_plan(3, 49152).variant == bnd.VARIANT_GENERIC     # six 16-bit vectors per thread do not fit
+    p = host_plan(4096, 12288)
+    assert (p.variant, p.block_threads, p.vectors_per_lane) == (bnd.VARIANT_BLOCK, 512, 3)
     for M, N in ((16384, 512), (262144, 128), (64, 256)):
         p = host_plan(M, N)
         assert (p.xcd_group, p.max_blocks_per_cu) == (1, 0)
+
+
+def test_every_aligned_width_takes_a_16_byte_kernel():
+    """No width the 16-byte kernels can hold falls through to the generic kernel:
+    up to 1024 x 5 vectors of 8 for 16-bit rows, 1024 x 6 vectors of 4 for fp32."""
+    for dtype, epv, widest in (("bf16", 8, 1024 * 5 * 8), ("fp16", 8, 1024 * 5 * 8), ("fp32", 4, 1024 * 6 * 4)):
+        for N in range(epv, widest + 1, epv):
+            p = query_ex(1024, N, dtype)
+            assert p.variant in (bnd.VARIANT_WAVE, bnd.VARIANT_BLOCK), (dtype, N)
+            assert p.lanes_per_row * p.vectors_per_lane * epv >= N, (dtype, N)
 
 
 def test_huge_row_counts_loop_with_prefetch():
@@ -267,7 +279,8 @@ def test_bwd_plans_and_workspace():
     # trips and the grid is at most one workgroup per unit
     p = plan(16384, 512)
     assert (p.variant, p.lanes_per_row, p.vectors_per_lane, p.block_threads) == (bnd.VARIANT_WAVE, 64, 1, 1024)
-    assert (p.grid, p.rows_per_trip, p.trips, p.prefetch) == (256, 64, 1, 0) and ws(16384, 512) == 256 * 512 * 4
+    assert (p.row_slots, p.grid, p.rows_per_trip, p.trips, p.prefetch) == (1, 256, 16, 4, 1)
+    assert ws(16384, 512) == 256 * 512 * 4
     p = plan(262144, 128, FP16)
     assert (p.variant, p.lanes_per_row, p.row_slots, p.grid, p.prefetch) == (bnd.VARIANT_WAVE, 16, 2, 256, 1)
     p = plan(32768, 8192)
@@ -292,7 +305,7 @@ def test_bwd_plans_and_workspace():
 def test_bwd_plans_that_do_not_fit_are_rejected():
     good = bnd.Plan()
     assert lib.rmsnorm_bwd_plan_query(100, 512, BF16, None, None, None, 256, ctypes.byref(good)) == OK
-    for p in (good.copy(prefetch=1),            # the 4-slot wave shape has no prefetching form
+    for p in (good.copy(row_slots=4, prefetch=1),   # the 4-slot wave shape has no prefetching form
               good.copy(prefetch=2), good.copy(xcd_group=2), good.copy(max_blocks_per_cu=4),
               good.copy(vectors_per_lane=3), good.copy(block_threads=1024, lanes_per_row=16, row_slots=1,
                                                        vectors_per_lane=1),

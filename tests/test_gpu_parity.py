@@ -146,7 +146,8 @@ def test_xcd_group_and_occupancy_cap_cover_every_row(bnd, name):
 # 3. Sweep of widths around powers of two and tile edges.
 # ---------------------------------------------------------------------------
 SWEEP_N = [1, 2, 3, 7, 8, 9, 63, 64, 65, 127, 128, 129, 255, 256, 511, 512, 513, 1000, 1023,
-           1024, 1025, 2047, 3000, 4095, 4096, 4097, 8191, 8192, 16383, 16384, 16385, 32768]
+           1024, 1025, 2047, 3000, 4095, 4096, 4097, 8191, 8192, 10240, 11001, 12288, 12290, 16383,
+           16384, 16385, 32768]
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "fp16"])
