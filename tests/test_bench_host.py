@@ -1,0 +1,68 @@
+"""Host-side checks of bench.py's contract pieces: the metric name, the one-GPU
+guard, and the counter arithmetic behind roofline.traffic (no GPU needed)."""
+import json
+import os
+import subprocess
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+sys.path.insert(0, ROOT)
+import bench  # noqa: E402
+from memory_bound_row_rmsnorm_amd import workloads  # noqa: E402
+
+
+def test_metric_name_of_the_default_workload():
+    wl = workloads.WORKLOADS[workloads.HEADLINE]
+    assert bench.metric_name("fwd", wl.M, wl.N, wl.dtype) == \
+        "achieved HBM GB/s and % of MI355X peak, RMSNorm fwd 16384x512 bf16"
+    assert bench.metric_name("bwd", 32768, 8192, "bf16").endswith("RMSNorm bwd 32768x8192 bf16")
+
+
+def test_more_than_one_gpu_is_refused_with_a_message():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode == 2
+    assert "one GPU only" in r.stderr and r.stdout == ""
+
+
+def _write_counters(d, name, kernel, counter, kernel_name, kib):
+    path = os.path.join(d, f"{name}_{kernel}_{counter}_counter_collection.csv")
+    with open(path, "w") as f:
+        f.write("Kernel_Name,Counter_Name,Counter_Value\n")
+        for v in (kib, kib, kib * 1.5):         # the median ignores one outlier dispatch
+            f.write(f"{kernel_name},{counter},{v}\n")
+
+
+def test_traffic_is_scaled_by_the_copy_kernels_reading(tmp_path):
+    """FETCH_SIZE reading half the bytes for the copy must double the kernel's reading too."""
+    name = "rmsnorm_16384x512_bf16"
+    wl = workloads.WORKLOADS[name]
+    copy_bytes = wl.M * wl.N * 2
+    _write_counters(tmp_path, name, "copy", "FETCH_SIZE", "__amd_rocclr_copyBuffer", copy_bytes / 2 / 1024)
+    _write_counters(tmp_path, name, "copy", "WRITE_SIZE", "__amd_rocclr_copyBuffer", copy_bytes / 1024)
+    _write_counters(tmp_path, name, "rmsnorm", "FETCH_SIZE", "rmsnorm_wave<...>", (copy_bytes + 1024) / 2 / 1024)
+    _write_counters(tmp_path, name, "rmsnorm", "WRITE_SIZE", "rmsnorm_wave<...>", (copy_bytes + 65536) / 1024)
+    t = bench.traffic_from_counters(wl, name, str(tmp_path))
+    assert t["fetch_scale"] == pytest.approx(2.0) and t["write_scale"] == pytest.approx(1.0)
+    assert t["fetch_bytes_per_launch"] == copy_bytes + 1024
+    assert t["write_bytes_per_launch"] == copy_bytes + 65536
+    assert t["traffic_bytes_per_launch"] == 2 * copy_bytes + 1024 + 65536
+    assert t["kernel_source_sha256"] == bench.kernel_source_sha256()
+    assert "resident_grid" not in t["plan"]
+
+
+def test_stale_traffic_is_reported_as_null(tmp_path, monkeypatch):
+    name = "rmsnorm_16384x512_bf16"
+    plan = {"variant": 1, "grid": 1024, "resident_grid": 2048}
+    (tmp_path / "profiles").mkdir()
+    doc = {"kernel_source_sha256": "0" * 64, "plan": bench.plan_key(plan), "traffic_bytes_per_launch": 123}
+    (tmp_path / "profiles" / f"traffic_{name}.json").write_text(json.dumps(doc))
+    monkeypatch.setattr(bench, "ROOT", str(tmp_path))
+    monkeypatch.setattr(bench, "kernel_source_sha256", lambda: "1" * 64)
+    assert bench.measured_traffic(name, plan) is None                  # other kernel sources
+    monkeypatch.setattr(bench, "kernel_source_sha256", lambda: "0" * 64)
+    assert bench.measured_traffic(name, plan) == 123
+    assert bench.measured_traffic(name, dict(plan, grid=512)) is None   # another launch plan
+    assert bench.measured_traffic("rmsnorm_64x512_bf16", plan) is None  # no summary at all
