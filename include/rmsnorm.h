@@ -75,7 +75,9 @@ typedef enum rmsnorm_variant {
     RMSNORM_VARIANT_BLOCK = 2,   /* one row per workgroup, cross-wave LDS reduce */
     RMSNORM_VARIANT_GENERIC = 3, /* any N and alignment: scalar I/O, row read twice */
     RMSNORM_VARIANT_SHIFTED = 4  /* rows not 16-byte aligned (N % 8 != 0, contiguous): one row
-                                    per workgroup, aligned 16-byte chunks, shifted weights */
+                                    per workgroup, aligned 16-byte chunks, shifted weights.
+                                    Edge chunks are read whole (the aligned 16 bytes that hold
+                                    row elements) and written element by element */
 } rmsnorm_variant_t;
 
 /*
@@ -94,7 +96,10 @@ typedef enum rmsnorm_variant {
  *                     issued before its first reduction.  1 otherwise
  *   block_threads     workgroup size (a multiple of 64, at most 1024)
  *   prefetch          WAVE, BLOCK: 1 = load the next trip's rows before this
- *                     trip's reduction (pays off when workgroups loop); 0 otherwise
+ *                     trip's reduction (pays off when workgroups loop);
+ *                     SHIFTED: 1 = fetch the row's weights with its x and pass
+ *                     neighbouring weight vectors between lanes, 0 = fetch them
+ *                     after the row's reduction; 0 otherwise
  *   xcd_group         1 to 64: the rows of this many consecutive workgroups
  *                     run on one XCD (MI355X hands workgroup b to XCD b mod 8;
  *                     the workgroup index is permuted within windows of

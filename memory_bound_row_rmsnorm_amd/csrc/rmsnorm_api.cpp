@@ -316,8 +316,8 @@ int finish_plan(rmsnorm_plan_t* p, int64_t M, int64_t N, int dtype, Access acc, 
         p->row_slots = 1;
         p->lanes_per_row = p->block_threads;
         p->rows_per_trip = 1;
-        if (p->prefetch != 0) return fail(RMSNORM_ERR_PLAN, "the shifted kernel has no prefetching form");
-        k = find_kernel(RMSNORM_VARIANT_SHIFTED, dtype, 0, p->vectors_per_lane, 1, false);
+        if (p->prefetch != 0 && p->prefetch != 1) return fail(RMSNORM_ERR_PLAN, "prefetch must be 0 or 1");
+        k = find_kernel(RMSNORM_VARIANT_SHIFTED, dtype, 0, p->vectors_per_lane, 1, p->prefetch != 0);
         if (k && static_cast<int64_t>(p->block_threads) * p->vectors_per_lane * epv < N + epv - 1)
             return fail(RMSNORM_ERR_PLAN, "shifted plan does not cover N");
     } else {
@@ -336,10 +336,11 @@ int finish_plan(rmsnorm_plan_t* p, int64_t M, int64_t N, int dtype, Access acc, 
 constexpr int kWaveSlots[] = {8, 4, 2, 1};
 constexpr int64_t kMaxVectors = 1024LL * 6;       // widest row the 16-byte kernels hold, in vectors
 constexpr int64_t kMaxShiftedChunks = 1024LL * 4;  // widest row the shifted kernel holds, in chunks
-// Shorter rows that start unaligned take the generic kernel: one row per
-// workgroup leaves most lanes idle there (262144 x 130 fp16: 107 us generic
-// against 144 us shifted; 16384 x 513 bf16: 17.7 us shifted against 22.8 us).
-constexpr int64_t kMinShiftedN = 256;
+// Shorter rows that start unaligned take the generic kernel.  From 128
+// elements up the shifted kernel is ahead even with most of its one wave idle
+// (262144 x 130 fp16: 93.6 us against 103.4 us generic; 262144 x 255 bf16:
+// 96.8 against 138.5 us).
+constexpr int64_t kMinShiftedN = 128;
 constexpr int64_t kMaxGrid = 0x7FFFFFFF;
 constexpr int64_t kWaveBytesInFlight = 4096;      // row bytes one wave loads per trip
 constexpr int64_t kWaveBytesInFlightMultiRow = 2048;   // the same when a slot holds several rows
@@ -372,11 +373,14 @@ int choose_plan(int64_t M, int64_t N, int dtype, Access acc, rmsnorm_plan_t* p) 
     const int64_t nvec = ceil_div(N, elems_per_vector(dtype));
     const int64_t nchunks = ceil_div(N + elems_per_vector(dtype) - 1, elems_per_vector(dtype));
     if (!vec && acc.shifted && N >= kMinShiftedN && nchunks <= kMaxShiftedChunks) {
-        // one row per workgroup: 64 threads for short rows, else 256 (up to
-        // 1024 chunks) or 1024 threads, each thread ceil(chunks / threads) chunks
+        // one row per workgroup: the fewest threads (64 to 1024) that hold the
+        // row's chunks with at most 3 per thread (32768 x 8191 bf16: 194 us with
+        // 512 x 3 against 305 us with 1024 x 2; 8192 x 3001 bf16: 20.0 us with
+        // 128 x 3 against 26.2 us with 256 x 2)
         p->variant = RMSNORM_VARIANT_SHIFTED;
         p->row_slots = 1;
-        p->block_threads = nchunks <= 64 ? 64 : (nchunks <= 256 * 4 ? 256 : 1024);
+        p->block_threads = 64;
+        while (p->block_threads < 1024 && nchunks > 3LL * p->block_threads) p->block_threads *= 2;
         p->vectors_per_lane = static_cast<int>(ceil_div(nchunks, p->block_threads));
     } else if (!vec || nvec > kMaxVectors) {
         p->variant = RMSNORM_VARIANT_GENERIC;
@@ -438,7 +442,12 @@ int choose_plan(int64_t M, int64_t N, int dtype, Access acc, rmsnorm_plan_t* p) 
         if (cap < kMaxThreadsPerCu / p->block_threads) p->max_blocks_per_cu = static_cast<int>(cap);
     }
     p->prefetch = 0;
-    if (p->variant != RMSNORM_VARIANT_GENERIC && p->grid < need &&
+    if (p->variant == RMSNORM_VARIANT_SHIFTED) {
+        // weights fetched with the row and passed between lanes up to 256
+        // threads (8192 x 3001 bf16: 20.0 against 22.0 us), after the
+        // reduction above (32768 x 8191 bf16: 194 against 210 us)
+        p->prefetch = p->block_threads <= 256 ? 1 : 0;
+    } else if (p->variant != RMSNORM_VARIANT_GENERIC && p->grid < need &&
         find_kernel(p->variant, dtype, p->variant == RMSNORM_VARIANT_WAVE ? p->lanes_per_row : 0,
                     p->vectors_per_lane, p->row_slots, true))
         p->prefetch = 1;
@@ -886,7 +895,7 @@ int rmsnorm_plan_resources(const rmsnorm_plan_t* plan, int dtype, int32_t* vgprs
     else if (plan->variant == RMSNORM_VARIANT_BLOCK)
         k = find_kernel(RMSNORM_VARIANT_BLOCK, dtype, 0, plan->vectors_per_lane, 1, pf);
     else if (plan->variant == RMSNORM_VARIANT_SHIFTED)
-        k = find_kernel(RMSNORM_VARIANT_SHIFTED, dtype, 0, plan->vectors_per_lane, 1, false);
+        k = find_kernel(RMSNORM_VARIANT_SHIFTED, dtype, 0, plan->vectors_per_lane, 1, pf);
     else if (plan->variant == RMSNORM_VARIANT_WAVE)
         k = find_kernel(RMSNORM_VARIANT_WAVE, dtype, plan->lanes_per_row, plan->vectors_per_lane, plan->row_slots, pf);
     if (!k) return fail(RMSNORM_ERR_PLAN, "no compiled kernel for this plan");

@@ -405,12 +405,22 @@ __global__ __launch_bounds__(1024) void rmsnorm_block(KernelArgs a) {
 // past one on every row).  One row per workgroup per trip.  The row is read
 // as the aligned 16-byte chunks that cover it: with `al` the row start's
 // distance in elements past a boundary, chunk c holds row elements
-// c * EPV - al .. c * EPV - al + EPV - 1.  Interior chunks lie inside the row
-// and move with one 16-byte load and store each; the first and last chunk
-// share their 16 bytes with neighbouring rows and move element by element,
-// only the row's own elements.  The weights of chunk c are vectors c - 1 and
-// c of w funnel-shifted by EPV - al elements (v_alignbyte on the packed
-// words).  x and y must sit the same distance past a boundary on every row.
+// c * EPV - al .. c * EPV - al + EPV - 1.  Every chunk, the two edge chunks
+// included, is loaded whole; the edge chunks' elements outside the row (the
+// neighbouring rows', or bytes next to the tensor inside the same aligned 16
+// bytes, so on a page the row's own elements share) are set to zero before
+// use and are never written: edge chunks are stored element by element.
+// The weights of chunk c are w vectors c - 1 and c funnel-shifted by
+// EPV - al elements (v_alignbyte on the packed words).  w is 16-byte
+// aligned, and its last vector is read whole in the same way.
+//
+// WPRE picks when the weights are fetched.  false: both vectors after the
+// row's reduction (registers stay free for loads in flight: faster with 512
+// and 1024 threads).  true: vector c with the row's loads, vector c - 1 from
+// the lane below (DPP wave shift) or, for lane 0, from the last lane of the
+// wave below through LDS (faster with up to 256 threads, where a row has
+// fewer waves to hide the weights' latency behind).
+// x and y must sit the same distance past a boundary on every row.
 // ---------------------------------------------------------------------------
 // Words k .. k + 3 of the 8-word concatenation (lo, hi) starting `sh`
 // elements in (0 < sh <= EPV), for the wave-uniform sh of one row.
@@ -435,46 +445,65 @@ __device__ __forceinline__ u32x4 funnel(const u32x4 lo, const u32x4 hi, int sh) 
     return o;
 }
 
-// The row's own elements of an edge chunk (row elements j0 .. j0 + EPV - 1,
-// those outside 0 .. N - 1 read as zero and never touched).
+// A chunk holding row elements j0 .. j0 + EPV - 1 with those outside
+// 0 .. n - 1 set to zero.
 template <class D>
-__device__ __forceinline__ u32x4 load_edge(const u32x4* p, int64_t j0, int64_t N) {
-    typedef typename D::elem_t E;
-    const E* q = reinterpret_cast<const E*>(p);
-    E e[D::EPV];
+__device__ __forceinline__ u32x4 keep_row(u32x4 v, int j0, int n) {
+    constexpr int EPW = 4 / static_cast<int>(sizeof(typename D::elem_t));
+    const int lo = -j0, hi = n - j0;    // kept: lo <= i < hi
 #pragma unroll
-    for (int i = 0; i < D::EPV; ++i) e[i] = (j0 + i >= 0 && j0 + i < N) ? q[i] : E(0);
-    return __builtin_bit_cast(u32x4, e);
+    for (int k = 0; k < 4; ++k) {
+        if constexpr (EPW == 2) {
+            const uint32_t m = ((2 * k >= lo && 2 * k < hi) ? 0x0000FFFFu : 0u) |
+                               ((2 * k + 1 >= lo && 2 * k + 1 < hi) ? 0xFFFF0000u : 0u);
+            v[k] &= m;
+        } else {
+            v[k] = (k >= lo && k < hi) ? v[k] : 0u;
+        }
+    }
+    return v;
 }
 
+// The row's own elements of an edge chunk, stored one at a time.
 template <class D>
-__device__ __forceinline__ void store_edge(u32x4* p, u32x4 v, int64_t j0, int64_t N) {
+__device__ __forceinline__ void store_edge(u32x4* p, u32x4 v, int j0, int n) {
     typedef typename D::elem_t E;
     E* q = reinterpret_cast<E*>(p);
     const auto e = __builtin_bit_cast(E __attribute__((ext_vector_type(D::EPV))), v);
 #pragma unroll
     for (int i = 0; i < D::EPV; ++i)
-        if (j0 + i >= 0 && j0 + i < N) q[i] = e[i];
+        if (j0 + i >= 0 && j0 + i < n) q[i] = e[i];
 }
 
-template <class D, int VPT>
+// Each lane's v from the lane below (DPP wave_shr:1); lane 0 takes `lane0`.
+__device__ __forceinline__ u32x4 from_lane_below(const u32x4 v, const u32x4 lane0) {
+    u32x4 o;
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+        o[k] = static_cast<uint32_t>(__builtin_amdgcn_update_dpp(static_cast<int>(lane0[k]), static_cast<int>(v[k]),
+                                                                 0x138, 0xF, 0xF, false));
+    return o;
+}
+
+template <class D, int VPT, bool WPRE>
 __global__ __launch_bounds__(1024) void rmsnorm_shifted(KernelArgs a) {
     typedef typename D::elem_t E;
     constexpr int EPV = D::EPV;
     __shared__ float part[2][16];
+    __shared__ u32x4 top[WPRE ? 2 : 1][WPRE ? VPT : 1][16];   // each wave's last lane's weights (WPRE)
     const int64_t M = a.M;
-    const int64_t N = a.N;
+    const int n = static_cast<int>(a.N);      // at most 4096 chunks: 32-bit element indices
     const E* xb = static_cast<const E*>(a.x) + batch() * a.x_bs;
     E* yb = static_cast<E*>(a.y) + batch() * a.y_bs;
     const u32x4* __restrict__ w = static_cast<const u32x4*>(a.w);
-    const int nfull_w = static_cast<int>(N / EPV), tail_w = static_cast<int>(N % EPV);
+    const int nvec_w = (n + EPV - 1) / EPV;
     const int tid = threadIdx.x;
     const int nt = a.threads;
     const int lane = tid & 63;
     const int wid = tid >> 6;
     const int nw = nt >> 6;
 
-    auto wvec = [&](int k) -> u32x4 { return k < 0 ? kZero : load_vec<D, false, true>(w, k, nfull_w, tail_w); };
+    auto wvec = [&](int k) -> u32x4 { return (k >= 0 && k < nvec_w) ? w[k] : kZero; };
 
     int par = 0;
     for (int64_t row = grouped_block(a.xcd_group, a.grid); row < M; row += a.grid) {
@@ -485,16 +514,26 @@ __global__ __launch_bounds__(1024) void rmsnorm_shifted(KernelArgs a) {
             static_cast<int>((reinterpret_cast<uintptr_t>(xr) & 15u) / sizeof(E)));
         const u32x4* xc = reinterpret_cast<const u32x4*>(xr - al);
         u32x4* yc = reinterpret_cast<u32x4*>(yr - al);
-        const int nch = static_cast<int>((al + N + EPV - 1) / EPV);
-        const bool ragged_end = ((al + N) % EPV) != 0;
+        const int nch = (al + n + EPV - 1) / EPV;
 
         u32x4 d[VPT];
+        u32x4 wv[WPRE ? VPT : 1];
 #pragma unroll
         for (int v = 0; v < VPT; ++v) {
             const int c = v * nt + tid;
-            const bool edge = (c == 0 && al != 0) || (c == nch - 1 && ragged_end);
-            d[v] = c >= nch ? kZero
-                            : (edge ? load_edge<D>(xc + c, static_cast<int64_t>(c) * EPV - al, N) : load_x(xc + c));
+            d[v] = c < nch ? load_x(xc + c) : kZero;
+            if constexpr (WPRE) wv[v] = wvec(c);
+        }
+#pragma unroll
+        for (int v = 0; v < VPT; ++v) {
+            const int j0 = (v * nt + tid) * EPV - al;
+            if (j0 < 0 || j0 + EPV > n) d[v] = keep_row<D>(d[v], j0, n);
+        }
+        if constexpr (WPRE) {
+            if (lane == 63) {
+#pragma unroll
+                for (int v = 0; v < VPT; ++v) top[par][v][wid] = wv[v];
+            }
         }
         const float ss = segment_allreduce<64>(sum_squares<D, VPT>(d));
         if (lane == 0) part[par][wid] = ss;
@@ -505,14 +544,24 @@ __global__ __launch_bounds__(1024) void rmsnorm_shifted(KernelArgs a) {
 #pragma unroll
         for (int v = 0; v < VPT; ++v) {
             const int c = v * nt + tid;
+            u32x4 wc;
+            if constexpr (WPRE) {
+                wc = wv[v];
+                if (al != 0) {
+                    // vector c - 1: the lane below's, or for lane 0 the last lane's of
+                    // the wave below (of the last wave, one vector back, for wave 0)
+                    u32x4 below = kZero;
+                    if (lane == 0 && c > 0) below = wid > 0 ? top[par][v][wid - 1] : top[par][v > 0 ? v - 1 : 0][nw - 1];
+                    wc = funnel<D>(from_lane_below(wv[v], below), wc, EPV - al);
+                }
+            }
             if (c < nch) {
+                if constexpr (!WPRE) wc = al == 0 ? wvec(c) : funnel<D>(wvec(c - 1), wvec(c), EPV - al);
                 float we[EPV];
-                // (loading these two weight vectors before the reduction measured
-                // slower: the registers they hold cost two waves per SIMD)
-                widen_weights<D>(we, al == 0 ? wvec(c) : funnel<D>(wvec(c - 1), wvec(c), EPV - al), a.offset);
+                widen_weights<D>(we, wc, a.offset);
                 const u32x4 o = normalise<D>(d[v], we, r);
-                const bool edge = (c == 0 && al != 0) || (c == nch - 1 && ragged_end);
-                if (edge) store_edge<D>(yc + c, o, static_cast<int64_t>(c) * EPV - al, N);
+                const int j0 = c * EPV - al;
+                if (j0 < 0 || j0 + EPV > n) store_edge<D>(yc + c, o, j0, n);
                 else store_y(yc + c, o);
             }
         }
@@ -580,9 +629,10 @@ __global__ __launch_bounds__(1024) void rmsnorm_generic(KernelArgs a) {
      "rmsnorm_block<" #D "," #V "," #P "," #T ">"}
 #define RMS_BLOCK(D, DT, V, P) RMS_BLOCK_T(D, DT, V, P, true)
 #define RMS_BLOCK2(D, DT, V) RMS_BLOCK(D, DT, V, false), RMS_BLOCK(D, DT, V, true)
-#define RMS_SHIFTED(D, DT, V)                                                                  \
-    {RMSNORM_VARIANT_SHIFTED, DT, 0, V, 1, false, true,                                           \
-     reinterpret_cast<const void*>(&rmsnorm_shifted<D, V>), "rmsnorm_shifted<" #D "," #V ">"}
+#define RMS_SHIFTED_P(D, DT, V, P)                                                             \
+    {RMSNORM_VARIANT_SHIFTED, DT, 0, V, 1, P, true,                                               \
+     reinterpret_cast<const void*>(&rmsnorm_shifted<D, V, P>), "rmsnorm_shifted<" #D "," #V "," #P ">"}
+#define RMS_SHIFTED(D, DT, V) RMS_SHIFTED_P(D, DT, V, false), RMS_SHIFTED_P(D, DT, V, true)
 // Only instances that fit 128 VGPRs (the budget of a 1024-thread workgroup)
 // without scratch are compiled.  The widest forms leave out the tail path
 // (last argument false), which they have no registers for: they serve

@@ -75,9 +75,10 @@ def candidates(M: int, N: int, dtype: str, quick: bool = False) -> list:
             vpt = -(-nch // threads)
             if threads > max(64, nch) or vpt > 4:
                 continue
-            for g in groups:
+            for g, wpre in itertools.product(groups, (0, 1)):   # weights after the reduction / with the row
                 raw.append(base.copy(variant=4, lanes_per_row=threads, vectors_per_lane=vpt, row_slots=1,
-                                     block_threads=threads, prefetch=0, xcd_group=g, max_blocks_per_cu=0, grid=M))
+                                     block_threads=threads, prefetch=wpre, xcd_group=g, max_blocks_per_cu=0,
+                                     grid=M))
     for threads in (64, 256, 1024):
         raw.append(base.copy(variant=3, block_threads=threads, prefetch=0, xcd_group=1, max_blocks_per_cu=0,
                              grid=M))
@@ -159,7 +160,7 @@ def describe(p) -> str:
     if p.max_blocks_per_cu:
         s += f", <= {p.max_blocks_per_cu} WG/CU"
     if p.prefetch:
-        s += ", prefetch"
+        s += ", weights with the row" if p.variant == 4 else ", prefetch"
     return s
 
 

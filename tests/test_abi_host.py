@@ -182,10 +182,21 @@ def test_ragged_contiguous_rows_take_the_shifted_kernel(N):
     assert f.variant == bnd.VARIANT_SHIFTED
 
 
+@pytest.mark.parametrize("N,threads,vpt,prefetch", [(129, 64, 1, 1), (257, 64, 1, 1), (513, 64, 2, 1), (3001, 128, 3, 1),
+                                                    (6001, 256, 3, 1), (8191, 512, 3, 0), (16383, 1024, 3, 0),
+                                                    (32761, 1024, 4, 0)])
+def test_shifted_rule(N, threads, vpt, prefetch):
+    """The fewest threads holding the row's chunks at most 3 per thread; weights fetched with the row
+    up to 256 threads."""
+    p = host_plan(10, N)
+    assert (p.variant, p.block_threads, p.vectors_per_lane, p.prefetch) == (bnd.VARIANT_SHIFTED, threads, vpt,
+                                                                            prefetch)
+
+
 @pytest.mark.parametrize("N,x,w", [(512, A + 2, None), (512, A + 8, None),   # x and y not equally aligned
                                    (3001, None, A + 2),                        # w not 16-byte aligned
                                    (49160, None, None), (1 << 17, None, None),  # wider than the kernels hold
-                                   (7, None, None), (255, None, None)])         # short unaligned rows
+                                   (7, None, None), (127, None, None)])         # short unaligned rows
 def test_unaligned_or_very_wide_rows_take_the_generic_kernel(N, x, w):
     p = host_plan(10, N, x=x, w=w)
     assert p.variant == bnd.VARIANT_GENERIC and p.vec_elems == 1

@@ -4,6 +4,8 @@ rstd left out.  Every case writes y into a view of a larger buffer filled with a
 that nothing outside the view changed."""
 from __future__ import annotations
 
+import itertools
+
 import numpy as np
 import pytest
 import torch
@@ -245,22 +247,20 @@ def test_shifted_every_instance(bnd, dtype, N):
         # aligned rows take the vector kernels, rows wider than 4096 chunks the generic one
         assert base.as_dict()["variant_name"] != "shifted"
         return
-    # the rule takes the shifted kernel from 256 elements up; explicit plans run it at any width
-    assert base.as_dict()["variant_name"] == ("shifted" if N >= 256 else "generic")
+    # the rule takes the shifted kernel from 128 elements up; explicit plans run it at any width
+    assert base.as_dict()["variant_name"] == ("shifted" if N >= 128 else "generic")
     ran = 0
-    for threads in (64, 128, 256, 512, 1024):
-        for vpt in (1, 2, 3, 4):
-            for grid in (M, 5):
+    for threads, vpt, grid, pf in itertools.product((64, 128, 256, 512, 1024), (1, 2, 3, 4), (M, 5), (0, 1)):
                 p = base.copy(variant=bnd.VARIANT_SHIFTED, block_threads=threads, vectors_per_lane=vpt,
-                              row_slots=1, prefetch=0, grid=grid, xcd_group=1, max_blocks_per_cu=0)
+                              row_slots=1, prefetch=pf, grid=grid, xcd_group=1, max_blocks_per_cu=0)
                 if bnd.plan_validate(M, N, x.dtype, p, x.data_ptr(), w.data_ptr(), x.data_ptr()) is None:
                     continue                     # does not cover N (the in-place pointers are equally aligned)
                 y_base = filled(M * N + 16, dtype)
                 y = y_base.as_strided((M, N), (N, 1), 8)
-                announce("shifted", M, N, dtype, threads, vpt, grid)
+                announce("shifted", M, N, dtype, threads, vpt, grid, pf)
                 out, rstd = bnd.rmsnorm_fwd_ex(x, w, 1e-6, 1.0, out=y, plan=p)
                 torch.cuda.synchronize()
-                what = f"shifted {M}x{N} {dtype} {threads}x{vpt} grid {grid}"
+                what = f"shifted {M}x{N} {dtype} {threads}x{vpt} grid {grid} weights-with-row {pf}"
                 if dtype == torch.float32:
                     parity.compare_fp32(out, rstd, ref[0], ref[1], what)
                 else:
@@ -268,7 +268,51 @@ def test_shifted_every_instance(bnd, dtype, N):
                 mask = view_mask(y_base.numel(), (M, N), (N, 1), 8)
                 assert bool((y_base.cpu().view(INT_VIEW[dtype])[~mask] == SENTINEL[dtype]).all()), what
                 ran += 1
-    assert ran >= (2 if N > 8000 else 6), ran
+    assert ran >= (4 if N > 8000 else 12), ran
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+@pytest.mark.parametrize("N,lead", [(3001, 3), (1025, 1), (8191, 5), (300, 7)])
+def test_shifted_reads_whole_edge_chunks_but_uses_only_the_row(bnd, dtype, N, lead):
+    """The shifted kernel loads the aligned 16 bytes around each row's ends, and w's last vector whole:
+    NaN in those bytes (before the first row, after the last, after w) must not reach y or rstd, and
+    sentinels around y must survive."""
+    M = 29
+    es = torch.tensor([], dtype=dtype).element_size()
+    epv = 16 // es
+    nan = float("nan")
+    x_base = torch.full((M * N + 2 * epv + lead,), nan, dtype=dtype)
+    x_base[lead:lead + M * N] = draw((M * N,), dtype, 101)
+    x_base = x_base.to(DEV)
+    x = x_base[lead:lead + M * N].view(M, N)
+    w_base = torch.full((N + 2 * epv,), nan, dtype=dtype)
+    w_base[:N] = (1.0 + 0.1 * draw((N,), torch.float32, 102)).to(dtype)
+    w_base = w_base.to(DEV)
+    w = w_base[:N]
+    y_base = filled(M * N + 2 * epv + lead, dtype)
+    y = y_base.as_strided((M, N), (N, 1), lead)
+    plan = bnd.plan_query_ex(x, w, y)
+    assert plan.as_dict()["variant_name"] == "shifted"
+    xc, wc = x.cpu(), w.cpu()
+    if dtype == torch.float32:
+        ref = parity.oracle_fp32(xc, wc, 1e-6, 0.0)
+    else:
+        ref = parity.oracle_for(xc, wc, 1e-6, 0.0, "bf16")
+    for pf in (0, 1):
+        p = bnd.plan_validate(M, N, dtype, plan.copy(prefetch=pf), x.data_ptr(), w.data_ptr(), y.data_ptr())
+        assert p is not None
+        y_base.copy_(filled(y_base.numel(), dtype))
+        announce("shifted edges", M, N, dtype, lead, pf)
+        out, rstd = bnd.rmsnorm_fwd_ex(x, w, 1e-6, 0.0, out=y, plan=p)
+        torch.cuda.synchronize()
+        what = f"shifted edges {M}x{N} {dtype} lead {lead} weights-with-row {pf}"
+        assert bool(torch.isfinite(out.float()).all()) and bool(torch.isfinite(rstd).all()), what
+        if dtype == torch.float32:
+            parity.compare_fp32(out, rstd, ref[0], ref[1], what)
+        else:
+            parity.compare(out, rstd, ref[0], ref[1], "bf16", what)
+        mask = view_mask(y_base.numel(), (M, N), (N, 1), lead)
+        assert bool((y_base.cpu().view(INT_VIEW[dtype])[~mask] == SENTINEL[dtype]).all()), what
 
 
 @pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
