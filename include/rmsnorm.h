@@ -74,29 +74,36 @@ typedef enum rmsnorm_variant {
     RMSNORM_VARIANT_WAVE = 1,    /* one or more rows per 64-lane wavefront, no LDS */
     RMSNORM_VARIANT_BLOCK = 2,   /* one row per workgroup, cross-wave LDS reduce */
     RMSNORM_VARIANT_GENERIC = 3, /* any N and alignment: scalar I/O, row read twice */
-    RMSNORM_VARIANT_SHIFTED = 4  /* rows not 16-byte aligned (N % 8 != 0, contiguous): one row
+    RMSNORM_VARIANT_SHIFTED = 4, /* rows not 16-byte aligned (N % 8 != 0, contiguous): one row
                                     per workgroup, aligned 16-byte chunks, shifted weights.
                                     Edge chunks are read whole (the aligned 16 bytes that hold
                                     row elements) and written element by element */
+    RMSNORM_VARIANT_SHIFTED_WAVE = 5 /* the same chunks for rows of at most 64 * vectors_per_lane
+                                        chunks: one row per wave per slot, row_slots rows per
+                                        wave per trip, no LDS */
 } rmsnorm_variant_t;
 
 /*
  * Launch plan: which kernel runs and how the rows are spread over the chip.
  *
- *   variant           RMSNORM_VARIANT_WAVE / _BLOCK / _GENERIC
+ *   variant           RMSNORM_VARIANT_WAVE / _BLOCK / _GENERIC / _SHIFTED /
+ *                     _SHIFTED_WAVE
  *   vec_elems         elements per lane access: 16 bytes' worth, 8 (bf16, fp16)
- *                     or 4 (fp32),
- *                     for WAVE and BLOCK, 1 for GENERIC
- *   lanes_per_row     WAVE: lanes sharing one row (16, 32 or 64);
- *                     BLOCK and GENERIC: threads per row (= block_threads)
- *   vectors_per_lane  16-byte vectors each lane holds per row (WAVE, BLOCK);
- *                     lanes_per_row * vectors_per_lane * vec_elems >= N
- *   row_slots         WAVE: row slots per wave per trip; a slot is
- *                     64/lanes_per_row rows, and all of a trip's loads are
+ *                     or 4 (fp32), for every family but GENERIC (1)
+ *   lanes_per_row     WAVE: lanes sharing one row (16, 32 or 64); SHIFTED_WAVE:
+ *                     64; BLOCK, SHIFTED and GENERIC: threads per row
+ *                     (= block_threads)
+ *   vectors_per_lane  16-byte vectors (SHIFTED, SHIFTED_WAVE: aligned chunks)
+ *                     each lane holds per row; lanes_per_row * vectors_per_lane
+ *                     * vec_elems >= N, and >= N + vec_elems - 1 for the
+ *                     shifted families, whose rows straddle one more chunk
+ *   row_slots         WAVE, SHIFTED_WAVE: row slots per wave per trip; a slot
+ *                     is 64/lanes_per_row rows, and all of a trip's loads are
  *                     issued before its first reduction.  1 otherwise
  *   block_threads     workgroup size (a multiple of 64, at most 1024)
- *   prefetch          WAVE, BLOCK: 1 = load the next trip's rows before this
- *                     trip's reduction (pays off when workgroups loop);
+ *   prefetch          WAVE, BLOCK, SHIFTED_WAVE: 1 = load the next trip's rows
+ *                     before this trip's reduction (pays off when workgroups
+ *                     loop);
  *                     SHIFTED: 1 = fetch the row's weights with its x and pass
  *                     neighbouring weight vectors between lanes, 0 = fetch them
  *                     after the row's reduction; 0 otherwise

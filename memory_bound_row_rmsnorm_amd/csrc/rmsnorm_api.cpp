@@ -252,7 +252,7 @@ const KernelEntry* find_kernel(int variant, int dtype, int lanes, int vpl, int s
     for (int i = 0; i < n; ++i) {
         const KernelEntry& k = t[i];
         if (k.variant != variant || k.dtype != dtype || k.prefetch != prefetch) continue;
-        if (variant == RMSNORM_VARIANT_WAVE &&
+        if ((variant == RMSNORM_VARIANT_WAVE || variant == RMSNORM_VARIANT_SHIFTED_WAVE) &&
             (k.lanes_per_row != lanes || k.vectors_per_lane != vpl || k.row_slots != slots))
             continue;
         if ((variant == RMSNORM_VARIANT_BLOCK || variant == RMSNORM_VARIANT_SHIFTED) && k.vectors_per_lane != vpl)
@@ -320,6 +320,18 @@ int finish_plan(rmsnorm_plan_t* p, int64_t M, int64_t N, int dtype, Access acc, 
         k = find_kernel(RMSNORM_VARIANT_SHIFTED, dtype, 0, p->vectors_per_lane, 1, p->prefetch != 0);
         if (k && static_cast<int64_t>(p->block_threads) * p->vectors_per_lane * epv < N + epv - 1)
             return fail(RMSNORM_ERR_PLAN, "shifted plan does not cover N");
+    } else if (p->variant == RMSNORM_VARIANT_SHIFTED_WAVE) {
+        if (!acc.shifted)
+            return fail(RMSNORM_ERR_PLAN, "the shifted kernels need x and y equally aligned with the same layout, "
+                                          "16-byte aligned w, and rows that are not 16-byte aligned");
+        const int epv = elems_per_vector(dtype);
+        p->vec_elems = epv;
+        p->lanes_per_row = 64;
+        if (p->prefetch != 0 && p->prefetch != 1) return fail(RMSNORM_ERR_PLAN, "prefetch must be 0 or 1");
+        k = find_kernel(RMSNORM_VARIANT_SHIFTED_WAVE, dtype, 64, p->vectors_per_lane, p->row_slots, p->prefetch != 0);
+        if (k && 64LL * p->vectors_per_lane * epv < N + epv - 1)
+            return fail(RMSNORM_ERR_PLAN, "shifted wave plan does not cover N");
+        p->rows_per_trip = static_cast<int64_t>(p->block_threads / 64) * p->row_slots;
     } else {
         return fail(RMSNORM_ERR_PLAN, "unknown variant");
     }
@@ -336,11 +348,12 @@ int finish_plan(rmsnorm_plan_t* p, int64_t M, int64_t N, int dtype, Access acc, 
 constexpr int kWaveSlots[] = {8, 4, 2, 1};
 constexpr int64_t kMaxVectors = 1024LL * 6;       // widest row the 16-byte kernels hold, in vectors
 constexpr int64_t kMaxShiftedChunks = 1024LL * 4;  // widest row the shifted kernel holds, in chunks
-// Shorter rows that start unaligned take the generic kernel.  From 128
-// elements up the shifted kernel is ahead even with most of its one wave idle
-// (262144 x 130 fp16: 93.6 us against 103.4 us generic; 262144 x 255 bf16:
-// 96.8 against 138.5 us).
-constexpr int64_t kMinShiftedN = 128;
+constexpr int64_t kMaxShiftedWaveChunks = 64 * 2;  // widest row the shifted wave kernel holds, in chunks
+constexpr int kShiftedWaveSlots = 4;               // rows per wave per trip of the shifted wave plans
+// Unaligned rows shorter than this take the generic kernel.  The shifted wave
+// kernel is ahead of it down to short rows (262144 x 36 bf16: 61.3 against
+// 66.9 us; 262144 x 100 bf16: 62.2 against 89.5 us).
+constexpr int64_t kMinShiftedWaveN = 16;
 constexpr int64_t kMaxGrid = 0x7FFFFFFF;
 constexpr int64_t kWaveBytesInFlight = 4096;      // row bytes one wave loads per trip
 constexpr int64_t kWaveBytesInFlightMultiRow = 2048;   // the same when a slot holds several rows
@@ -372,7 +385,17 @@ int choose_plan(int64_t M, int64_t N, int dtype, Access acc, rmsnorm_plan_t* p) 
     const int64_t es = elem_size(dtype);
     const int64_t nvec = ceil_div(N, elems_per_vector(dtype));
     const int64_t nchunks = ceil_div(N + elems_per_vector(dtype) - 1, elems_per_vector(dtype));
-    if (!vec && acc.shifted && N >= kMinShiftedN && nchunks <= kMaxShiftedChunks) {
+    if (!vec && acc.shifted && N >= kMinShiftedWaveN && nchunks <= kMaxShiftedWaveChunks) {
+        // one row per wave per slot, four slots per wave, 4-wave workgroups
+        // (262144 x 257 bf16: 73 us, against 97 us with one row per 64-thread
+        // workgroup and 163 us generic; 16384 x 1001 bf16: 14.4 us with four
+        // slots against 16.0 us with two)
+        p->variant = RMSNORM_VARIANT_SHIFTED_WAVE;
+        p->lanes_per_row = 64;
+        p->vectors_per_lane = static_cast<int>(ceil_div(nchunks, 64));
+        p->block_threads = kWaveBlockThreads;
+        p->row_slots = kShiftedWaveSlots;
+    } else if (!vec && acc.shifted && nchunks > kMaxShiftedWaveChunks && nchunks <= kMaxShiftedChunks) {
         // one row per workgroup: the fewest threads (64 to 1024) that hold the
         // row's chunks with at most 3 per thread (32768 x 8191 bf16: 194 us with
         // 512 x 3 against 305 us with 1024 x 2; 8192 x 3001 bf16: 20.0 us with
@@ -424,7 +447,7 @@ int choose_plan(int64_t M, int64_t N, int dtype, Access acc, rmsnorm_plan_t* p) 
         }
     }
     int64_t rows_per_trip = 1;
-    if (p->variant == RMSNORM_VARIANT_WAVE)
+    if (p->variant == RMSNORM_VARIANT_WAVE || p->variant == RMSNORM_VARIANT_SHIFTED_WAVE)
         rows_per_trip = static_cast<int64_t>(p->block_threads / 64) * (64 / p->lanes_per_row) * p->row_slots;
     const int64_t need = M > 0 ? ceil_div(M, rows_per_trip) : 1;
     p->grid = need < kMaxGrid ? need : kMaxGrid;
@@ -448,7 +471,9 @@ int choose_plan(int64_t M, int64_t N, int dtype, Access acc, rmsnorm_plan_t* p) 
         // reduction above (32768 x 8191 bf16: 194 against 210 us)
         p->prefetch = p->block_threads <= 256 ? 1 : 0;
     } else if (p->variant != RMSNORM_VARIANT_GENERIC && p->grid < need &&
-        find_kernel(p->variant, dtype, p->variant == RMSNORM_VARIANT_WAVE ? p->lanes_per_row : 0,
+        find_kernel(p->variant, dtype,
+                    p->variant == RMSNORM_VARIANT_WAVE || p->variant == RMSNORM_VARIANT_SHIFTED_WAVE
+                        ? p->lanes_per_row : 0,
                     p->vectors_per_lane, p->row_slots, true))
         p->prefetch = 1;
     return RMSNORM_OK;
@@ -896,6 +921,8 @@ int rmsnorm_plan_resources(const rmsnorm_plan_t* plan, int dtype, int32_t* vgprs
         k = find_kernel(RMSNORM_VARIANT_BLOCK, dtype, 0, plan->vectors_per_lane, 1, pf);
     else if (plan->variant == RMSNORM_VARIANT_SHIFTED)
         k = find_kernel(RMSNORM_VARIANT_SHIFTED, dtype, 0, plan->vectors_per_lane, 1, pf);
+    else if (plan->variant == RMSNORM_VARIANT_SHIFTED_WAVE)
+        k = find_kernel(RMSNORM_VARIANT_SHIFTED_WAVE, dtype, 64, plan->vectors_per_lane, plan->row_slots, pf);
     else if (plan->variant == RMSNORM_VARIANT_WAVE)
         k = find_kernel(RMSNORM_VARIANT_WAVE, dtype, plan->lanes_per_row, plan->vectors_per_lane, plan->row_slots, pf);
     if (!k) return fail(RMSNORM_ERR_PLAN, "no compiled kernel for this plan");

@@ -571,6 +571,130 @@ __global__ __launch_bounds__(1024) void rmsnorm_shifted(KernelArgs a) {
 }
 
 // ---------------------------------------------------------------------------
+// Shifted wave family: the shifted kernel's chunk scheme for rows of at most
+// 64 * VPL chunks, one row per wave per slot, SLOTS rows per wave per trip,
+// no LDS and no barrier.  A row's distance past a 16-byte boundary is the
+// same in all lanes of its wave.  The weights do not depend on the row: each
+// lane fetches w vectors c - 1 and c of its chunks once, after the first
+// trip's rows, and funnel-shifts them for each row.
+// ---------------------------------------------------------------------------
+template <class D, int VPL, int SLOTS, bool PREFETCH>
+__global__ __launch_bounds__(1024) void rmsnorm_shifted_wave(KernelArgs a) {
+    typedef typename D::elem_t E;
+    constexpr int EPV = D::EPV;
+    const int64_t M = a.M;
+    const int n = static_cast<int>(a.N);      // at most 64 * VPL chunks
+    const E* xb = static_cast<const E*>(a.x) + batch() * a.x_bs;
+    E* yb = static_cast<E*>(a.y) + batch() * a.y_bs;
+    const u32x4* __restrict__ w = static_cast<const u32x4*>(a.w);
+    const int nvec_w = (n + EPV - 1) / EPV;
+    const int lane = threadIdx.x & 63;
+    const int wpb = a.threads >> 6;
+    const int wid = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
+    const int64_t nwaves = a.grid * wpb;
+    int64_t g = grouped_block(a.xcd_group, a.grid) * wpb + wid;
+
+    // rows past the end keep an in-range address and load nothing
+    auto row_of = [&](int64_t gg, int s) -> int64_t { return gg * SLOTS + s; };
+    auto offset_of = [&](int64_t row) -> int {
+        const E* xr = xb + (row < M ? row : 0) * a.x_rs;
+        return __builtin_amdgcn_readfirstlane(static_cast<int>((reinterpret_cast<uintptr_t>(xr) & 15u) / sizeof(E)));
+    };
+    auto load_trip = [&](u32x4 (&d)[SLOTS][VPL], int64_t gg) {
+#pragma unroll
+        for (int s = 0; s < SLOTS; ++s) {
+            const int64_t row = row_of(gg, s);
+            const int al = offset_of(row);
+            const int nch = (al + n + EPV - 1) / EPV;
+            const u32x4* xc = reinterpret_cast<const u32x4*>(xb + (row < M ? row : 0) * a.x_rs - al);
+#pragma unroll
+            for (int v = 0; v < VPL; ++v) {
+                const int c = v * 64 + lane;
+                d[s][v] = (row < M && c < nch) ? load_x(xc + c) : kZero;
+            }
+        }
+    };
+
+    u32x4 d[SLOTS][VPL];
+    load_trip(d, g);
+    u32x4 wlo[VPL], whi[VPL];
+#pragma unroll
+    for (int v = 0; v < VPL; ++v) {
+        const int c = v * 64 + lane;
+        wlo[v] = (c >= 1 && c - 1 < nvec_w) ? w[c - 1] : kZero;
+        whi[v] = c < nvec_w ? w[c] : kZero;
+    }
+
+    auto finish_trip = [&](u32x4 (&dd)[SLOTS][VPL], int64_t gg) {
+        float r[SLOTS];
+#pragma unroll
+        for (int s = 0; s < SLOTS; ++s) {
+            const int al = offset_of(row_of(gg, s));
+#pragma unroll
+            for (int v = 0; v < VPL; ++v) {
+                const int j0 = (v * 64 + lane) * EPV - al;
+                if (j0 < 0 || j0 + EPV > n) dd[s][v] = keep_row<D>(dd[s][v], j0, n);
+            }
+            const float ss = segment_allreduce<64>(sum_squares<D, VPL>(dd[s]));
+            r[s] = rsq(__builtin_fmaf(ss, a.inv_n, a.eps));
+        }
+#pragma unroll
+        for (int s = 0; s < SLOTS; ++s) {
+            const int64_t row = row_of(gg, s);
+            const int al = offset_of(row);
+            const int nch = (al + n + EPV - 1) / EPV;
+            u32x4* yc = reinterpret_cast<u32x4*>(yb + (row < M ? row : 0) * a.y_rs - al);
+#pragma unroll
+            for (int v = 0; v < VPL; ++v) {
+                const int c = v * 64 + lane;
+                if (row < M && c < nch) {
+                    float we[EPV];
+                    widen_weights<D>(we, al == 0 ? whi[v] : funnel<D>(wlo[v], whi[v], EPV - al), a.offset);
+                    const u32x4 o = normalise<D>(dd[s][v], we, r[s]);
+                    const int j0 = c * EPV - al;
+                    if (j0 < 0 || j0 + EPV > n) store_edge<D>(yc + c, o, j0, n);
+                    else store_y(yc + c, o);
+                }
+            }
+        }
+        if (a.rstd != nullptr) {
+            float* rstd = a.rstd + batch() * M;
+#pragma unroll
+            for (int s = 0; s < SLOTS; ++s) {
+                const int64_t row = row_of(gg, s);
+                if (lane == 0 && row < M) store_rstd(rstd + row, r[s]);
+            }
+        }
+    };
+
+    if constexpr (!PREFETCH) {
+        if ((g + nwaves) * SLOTS >= M) {
+            finish_trip(d, g);
+            return;
+        }
+    }
+    for (;;) {
+        const int64_t gn = g + nwaves;
+        const bool more = gn * SLOTS < M;
+        u32x4 dn[SLOTS][VPL];
+        if constexpr (PREFETCH) {
+            if (more) load_trip(dn, gn);
+        }
+        finish_trip(d, g);
+        if (!more) break;
+        g = gn;
+        if constexpr (PREFETCH) {
+#pragma unroll
+            for (int s = 0; s < SLOTS; ++s)
+#pragma unroll
+                for (int v = 0; v < VPL; ++v) d[s][v] = dn[s][v];
+        } else {
+            load_trip(d, g);
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
 // Generic family: any N, any element alignment, any strides.  x and y may be
 // the same buffer with the same layout: every element is read and then
 // written by the same thread, and the sum of squares of a row is complete
@@ -633,6 +757,11 @@ __global__ __launch_bounds__(1024) void rmsnorm_generic(KernelArgs a) {
     {RMSNORM_VARIANT_SHIFTED, DT, 0, V, 1, P, true,                                               \
      reinterpret_cast<const void*>(&rmsnorm_shifted<D, V, P>), "rmsnorm_shifted<" #D "," #V "," #P ">"}
 #define RMS_SHIFTED(D, DT, V) RMS_SHIFTED_P(D, DT, V, false), RMS_SHIFTED_P(D, DT, V, true)
+#define RMS_SHIFTED_WAVE_P(D, DT, V, S, P)                                                     \
+    {RMSNORM_VARIANT_SHIFTED_WAVE, DT, 64, V, S, P, true,                                         \
+     reinterpret_cast<const void*>(&rmsnorm_shifted_wave<D, V, S, P>),                            \
+     "rmsnorm_shifted_wave<" #D "," #V "," #S "," #P ">"}
+#define RMS_SHIFTED_WAVE(D, DT, V, S) RMS_SHIFTED_WAVE_P(D, DT, V, S, false), RMS_SHIFTED_WAVE_P(D, DT, V, S, true)
 // Only instances that fit 128 VGPRs (the budget of a 1024-thread workgroup)
 // without scratch are compiled.  The widest forms leave out the tail path
 // (last argument false), which they have no registers for: they serve
@@ -649,6 +778,9 @@ __global__ __launch_bounds__(1024) void rmsnorm_generic(KernelArgs a) {
     RMS_BLOCK2(D, DT, 1), RMS_BLOCK2(D, DT, 2), RMS_BLOCK2(D, DT, 3), RMS_BLOCK2(D, DT, 4),     \
     RMS_BLOCK(D, DT, 5, false),                                                                 \
     RMS_SHIFTED(D, DT, 1), RMS_SHIFTED(D, DT, 2), RMS_SHIFTED(D, DT, 3), RMS_SHIFTED(D, DT, 4),   \
+    RMS_SHIFTED_WAVE(D, DT, 1, 1), RMS_SHIFTED_WAVE(D, DT, 1, 2), RMS_SHIFTED_WAVE(D, DT, 1, 4),   \
+    RMS_SHIFTED_WAVE(D, DT, 2, 1), RMS_SHIFTED_WAVE(D, DT, 2, 2),                                 \
+    RMS_SHIFTED_WAVE_P(D, DT, 2, 4, false),                                                      \
     {RMSNORM_VARIANT_GENERIC, DT, 0, 0, 1, false, true,                                         \
      reinterpret_cast<const void*>(&rmsnorm_generic<D>), "rmsnorm_generic<" #D ">"}
 

@@ -68,8 +68,15 @@ def candidates(M: int, N: int, dtype: str, quick: bool = False) -> list:
                                      block_threads=threads, prefetch=0, xcd_group=g, max_blocks_per_cu=cap,
                                      grid=M))
     else:
-        # rows that start unaligned: the shifted kernel (aligned chunks, per-row shifted weights)
+        # rows that start unaligned: the shifted kernels (aligned chunks, per-row shifted weights)
         nch = -(-(N + 7) // 8)
+        if nch <= 128:
+            vpl = -(-nch // 64)
+            for slots, threads, pf in itertools.product((1, 2, 4), (64, 128, 256, 512), (0, 1)):
+                rows_per_trip = (threads // 64) * slots
+                raw.append(base.copy(variant=5, lanes_per_row=64, vectors_per_lane=vpl, row_slots=slots,
+                                     block_threads=threads, prefetch=pf, xcd_group=1, max_blocks_per_cu=0,
+                                     grid=-(-M // rows_per_trip)))
         groups = (1, 8, 16) if quick else (1, 4, 8, 16)
         for threads in (64, 128, 256, 512, 1024):
             vpt = -(-nch // threads)
@@ -149,8 +156,8 @@ def time_plan(plan, bufs: Buffers, M: int, N: int, dtype: str, steps: int, reps:
 
 def describe(p) -> str:
     name = binding.VARIANT_NAMES.get(p.variant, str(p.variant))
-    if p.variant == 1:
-        s = f"wave {p.lanes_per_row}x{p.vectors_per_lane} lanes x vectors, {p.row_slots} slots, {p.block_threads} thr"
+    if p.variant in (1, 5):
+        s = f"{name} {p.lanes_per_row}x{p.vectors_per_lane} lanes x vectors, {p.row_slots} slots, {p.block_threads} thr"
     elif p.variant in (2, 4):
         s = f"{name} {p.block_threads} thr x {p.vectors_per_lane} vectors"
     else:

@@ -16,7 +16,7 @@ bnd = pytest.importorskip("memory_bound_row_rmsnorm_amd.binding",
 lib = bnd.lib
 
 OK, NULL, SHAPE, DTYPE, SCALAR, OVERLAP, HIP, DEVICE, PLAN = range(9)
-BF16, FP16 = 0, 1
+BF16, FP16, FP32 = 0, 1, 2
 A = 0x10000000  # fake, 256-byte aligned, never dereferenced: every call below fails validation
 
 
@@ -174,29 +174,39 @@ def test_huge_row_counts_loop_with_prefetch():
 
 
 @pytest.mark.parametrize("N", [257, 3001, 1025, 32761])
-def test_ragged_contiguous_rows_take_the_shifted_kernel(N):
+def test_ragged_contiguous_rows_take_a_shifted_kernel(N):
     p = host_plan(10, N)                       # rows start a varying distance past a 16-byte boundary
-    assert p.variant == bnd.VARIANT_SHIFTED and p.vec_elems == 8
-    assert p.block_threads * p.vectors_per_lane * 8 >= N + 7 and p.rows_per_trip == 1
+    assert p.variant in (bnd.VARIANT_SHIFTED, bnd.VARIANT_SHIFTED_WAVE) and p.vec_elems == 8
+    assert p.lanes_per_row * p.vectors_per_lane * 8 >= N + 7
+    assert p.rows_per_trip == (1 if p.variant == bnd.VARIANT_SHIFTED else p.block_threads // 64 * p.row_slots)
     f = host_plan(10, N, dtype=FP16, x=A + 2, y=A + 2 + 0x1000000)    # equally misaligned x and y
-    assert f.variant == bnd.VARIANT_SHIFTED
+    assert f.variant == p.variant
 
 
-@pytest.mark.parametrize("N,threads,vpt,prefetch", [(129, 64, 1, 1), (257, 64, 1, 1), (513, 64, 2, 1), (3001, 128, 3, 1),
-                                                    (6001, 256, 3, 1), (8191, 512, 3, 0), (16383, 1024, 3, 0),
-                                                    (32761, 1024, 4, 0)])
+@pytest.mark.parametrize("N,threads,vpt,prefetch", [(1018, 64, 3, 1), (3001, 128, 3, 1), (6001, 256, 3, 1),
+                                                    (8191, 512, 3, 0), (16383, 1024, 3, 0), (32761, 1024, 4, 0)])
 def test_shifted_rule(N, threads, vpt, prefetch):
-    """The fewest threads holding the row's chunks at most 3 per thread; weights fetched with the row
-    up to 256 threads."""
+    """Rows wider than 128 chunks: the fewest threads holding the row's chunks at most 3 per thread;
+    weights fetched with the row up to 256 threads."""
     p = host_plan(10, N)
     assert (p.variant, p.block_threads, p.vectors_per_lane, p.prefetch) == (bnd.VARIANT_SHIFTED, threads, vpt,
                                                                             prefetch)
 
 
+@pytest.mark.parametrize("N,dtype,vpl,slots", [(17, BF16, 1, 4), (129, BF16, 1, 4), (257, BF16, 1, 4),
+                                               (505, BF16, 1, 4), (513, BF16, 2, 4), (1017, BF16, 2, 4),
+                                               (130, FP16, 1, 4), (509, FP32, 2, 4)])
+def test_shifted_wave_rule(N, dtype, vpl, slots):
+    """Rows of 16 elements up to 128 chunks: one row per wave per slot, four slots."""
+    p = host_plan(100000, N, dtype=dtype)
+    assert (p.variant, p.lanes_per_row, p.vectors_per_lane, p.row_slots) == (bnd.VARIANT_SHIFTED_WAVE, 64, vpl, slots)
+    assert p.rows_per_trip == 4 * slots and p.grid == -(-100000 // (4 * slots)) and p.trips == 1
+
+
 @pytest.mark.parametrize("N,x,w", [(512, A + 2, None), (512, A + 8, None),   # x and y not equally aligned
                                    (3001, None, A + 2),                        # w not 16-byte aligned
                                    (49160, None, None), (1 << 17, None, None),  # wider than the kernels hold
-                                   (7, None, None), (127, None, None)])         # short unaligned rows
+                                   (7, None, None), (15, None, None)])          # short unaligned rows
 def test_unaligned_or_very_wide_rows_take_the_generic_kernel(N, x, w):
     p = host_plan(10, N, x=x, w=w)
     assert p.variant == bnd.VARIANT_GENERIC and p.vec_elems == 1

@@ -247,8 +247,11 @@ def test_shifted_every_instance(bnd, dtype, N):
         # aligned rows take the vector kernels, rows wider than 4096 chunks the generic one
         assert base.as_dict()["variant_name"] != "shifted"
         return
-    # the rule takes the shifted kernel from 128 elements up; explicit plans run it at any width
-    assert base.as_dict()["variant_name"] == ("shifted" if N >= 128 else "generic")
+    # the rule takes a shifted kernel from 16 elements up (the wave form up to 128 chunks); explicit
+    # plans run the block form at any width
+    nch = -(-(N + epv - 1) // epv)
+    expect = "generic" if N < 16 else ("shifted_wave" if nch <= 128 else "shifted")
+    assert base.as_dict()["variant_name"] == expect
     ran = 0
     for threads, vpt, grid, pf in itertools.product((64, 128, 256, 512, 1024), (1, 2, 3, 4), (M, 5), (0, 1)):
                 p = base.copy(variant=bnd.VARIANT_SHIFTED, block_threads=threads, vectors_per_lane=vpt,
@@ -271,8 +274,53 @@ def test_shifted_every_instance(bnd, dtype, N):
     assert ran >= (4 if N > 8000 else 12), ran
 
 
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float16, torch.float32])
+@pytest.mark.parametrize("N", [9, 100, 129, 300, 505, 513, 1001, 1017])
+def test_shifted_wave_every_instance(bnd, dtype, N):
+    """The wave form of the shifted kernel: every compiled instance that covers N, one trip and
+    persistent grids, next-trip prefetch on and off."""
+    M = 37
+    sigma = 100.0 if dtype == torch.float16 else 1.0
+    x = draw((M, N), dtype, 93, sigma).to(DEV)
+    w = (1.0 + 0.1 * draw((N,), torch.float32, 94)).to(dtype).to(DEV)
+    xc, wc = x.cpu(), w.cpu()
+    if dtype == torch.float32:
+        ref = parity.oracle_fp32(xc, wc, 1e-6, 0.0)
+    else:
+        dt = "bf16" if dtype == torch.bfloat16 else "fp16"
+        ref = parity.oracle_for(xc, wc, 1e-6, 0.0, dt)
+    es = x.element_size()
+    if (N * es) % 16 == 0:
+        return                                   # aligned rows never take a shifted kernel
+    base = bnd.plan_query_ex(x, w)
+    ran = 0
+    for vpl, slots, threads, pf in itertools.product((1, 2), (1, 2, 4), (64, 256), (0, 1)):
+        rows = threads // 64 * slots
+        for grid in (-(-M // rows), 2):
+            p = base.copy(variant=bnd.VARIANT_SHIFTED_WAVE, lanes_per_row=64, block_threads=threads,
+                          vectors_per_lane=vpl, row_slots=slots, prefetch=pf, grid=grid, xcd_group=1,
+                          max_blocks_per_cu=0)
+            if bnd.plan_validate(M, N, x.dtype, p, x.data_ptr(), w.data_ptr(), x.data_ptr()) is None:
+                continue                         # does not cover N, or no such instance
+            y_base = filled(M * N + 16, dtype)
+            y = y_base.as_strided((M, N), (N, 1), 8)
+            announce("shifted wave", M, N, dtype, vpl, slots, threads, pf, grid)
+            out, rstd = bnd.rmsnorm_fwd_ex(x, w, 1e-6, 0.0, out=y, plan=p)
+            torch.cuda.synchronize()
+            what = f"shifted wave {M}x{N} {dtype} vpl {vpl} slots {slots} {threads} thr pf {pf} grid {grid}"
+            if dtype == torch.float32:
+                parity.compare_fp32(out, rstd, ref[0], ref[1], what)
+            else:
+                parity.compare(out, rstd, ref[0], ref[1], dt, what)
+            mask = view_mask(y_base.numel(), (M, N), (N, 1), 8)
+            assert bool((y_base.cpu().view(INT_VIEW[dtype])[~mask] == SENTINEL[dtype]).all()), what
+            ran += 1
+    nch = -(-(N + 16 // es - 1) // (16 // es))
+    assert ran >= (8 if nch > 128 else 16) or nch > 128, ran
+
+
 @pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
-@pytest.mark.parametrize("N,lead", [(3001, 3), (1025, 1), (8191, 5), (300, 7)])
+@pytest.mark.parametrize("N,lead", [(3001, 3), (1025, 1), (8191, 5), (300, 7), (129, 2), (1017, 6)])
 def test_shifted_reads_whole_edge_chunks_but_uses_only_the_row(bnd, dtype, N, lead):
     """The shifted kernel loads the aligned 16 bytes around each row's ends, and w's last vector whole:
     NaN in those bytes (before the first row, after the last, after w) must not reach y or rstd, and
@@ -292,7 +340,7 @@ def test_shifted_reads_whole_edge_chunks_but_uses_only_the_row(bnd, dtype, N, le
     y_base = filled(M * N + 2 * epv + lead, dtype)
     y = y_base.as_strided((M, N), (N, 1), lead)
     plan = bnd.plan_query_ex(x, w, y)
-    assert plan.as_dict()["variant_name"] == "shifted"
+    assert plan.as_dict()["variant_name"].startswith("shifted")
     xc, wc = x.cpu(), w.cpu()
     if dtype == torch.float32:
         ref = parity.oracle_fp32(xc, wc, 1e-6, 0.0)
@@ -300,6 +348,8 @@ def test_shifted_reads_whole_edge_chunks_but_uses_only_the_row(bnd, dtype, N, le
         ref = parity.oracle_for(xc, wc, 1e-6, 0.0, "bf16")
     for pf in (0, 1):
         p = bnd.plan_validate(M, N, dtype, plan.copy(prefetch=pf), x.data_ptr(), w.data_ptr(), y.data_ptr())
+        if p is None and pf == 1 and plan.variant == bnd.VARIANT_SHIFTED_WAVE:
+            continue                             # the widest wave instance has no prefetching form
         assert p is not None
         y_base.copy_(filled(y_base.numel(), dtype))
         announce("shifted edges", M, N, dtype, lead, pf)
@@ -324,7 +374,7 @@ def test_equally_misaligned_operands(bnd, dtype):
     y_base = filled(M * N + 9, dtype)
     y = y_base.as_strided((M, N), (N, 1), 1)
     plan = check(bnd, x, w, y, y_base, (M, N), (N, 1), 1, what="misaligned bases")
-    assert plan.as_dict()["variant_name"] == "shifted"
+    assert plan.as_dict()["variant_name"].startswith("shifted")
 
 
 def test_shifted_in_place(bnd):
