@@ -51,7 +51,7 @@ extern "C" {
 typedef enum rmsnorm_dtype {
     RMSNORM_BF16 = 0,
     RMSNORM_FP16 = 1,
-    RMSNORM_FP32 = 2     /* forward only */
+    RMSNORM_FP32 = 2     /* forward and backward; four elements per 16-byte vector */
 } rmsnorm_dtype_t;
 
 /* Status codes. */

@@ -121,14 +121,13 @@ bool ranges_overlap(const void* a, int64_t abytes, const void* b, int64_t bbytes
 int elem_size(int dtype) { return dtype == RMSNORM_FP32 ? 4 : 2; }
 int elems_per_vector(int dtype) { return 16 / elem_size(dtype); }
 
-// Forward calls take all three dtypes; the backward keeps to 16-bit ones.
-int check_shape_dtype(int64_t M, int64_t N, int dtype, bool forward = true) {
+// Forward and backward calls take all three dtypes.
+int check_shape_dtype(int64_t M, int64_t N, int dtype) {
     if (M < 0) return fail(RMSNORM_ERR_SHAPE, "M must be >= 0");
     if (N <= 0) return fail(RMSNORM_ERR_SHAPE, "N must be >= 1");
     if (M > 0 && N > INT64_MAX / 4 / M) return fail(RMSNORM_ERR_SHAPE, "M*N*4 bytes overflows int64");
-    if (dtype != RMSNORM_BF16 && dtype != RMSNORM_FP16 && !(forward && dtype == RMSNORM_FP32))
-        return fail(RMSNORM_ERR_DTYPE, forward ? "dtype must be RMSNORM_BF16, RMSNORM_FP16 or RMSNORM_FP32"
-                                               : "dtype must be RMSNORM_BF16 or RMSNORM_FP16");
+    if (dtype != RMSNORM_BF16 && dtype != RMSNORM_FP16 && dtype != RMSNORM_FP32)
+        return fail(RMSNORM_ERR_DTYPE, "dtype must be RMSNORM_BF16, RMSNORM_FP16 or RMSNORM_FP32");
     return RMSNORM_OK;
 }
 
@@ -548,7 +547,7 @@ int launch(const KernelEntry* k, const rmsnorm_plan_t* p, const void* x, const v
 // ---------------------------------------------------------------------------
 // Backward: argument checks, planning, launch.
 // ---------------------------------------------------------------------------
-constexpr int64_t kBwdMaxVectorN = 1024LL * 2 * 8;   // widest row of the 16-byte backward kernels
+constexpr int64_t kBwdMaxVectors = 1024LL * 2;      // widest row of the 16-byte backward kernels, in vectors
 constexpr int kBwdWaveThreads = 1024;                // 16 waves share one LDS reduction of dw
 constexpr int64_t kBwdMaxLds = 64 * 1024;
 constexpr int64_t kBwdPlanCus = 256;                 // compute units the backward plan assumes
@@ -577,13 +576,14 @@ int64_t bwd_wave_lds(const rmsnorm_plan_t* p, int64_t N) {
 
 int check_bwd_args(const void* x, const void* w, const void* dy, const float* rstd, const void* dx,
                    const float* dw, int64_t M, int64_t N, float offset, int dtype) {
-    int st = check_shape_dtype(M, N, dtype, false);
+    int st = check_shape_dtype(M, N, dtype);
     if (st != RMSNORM_OK) return st;
     if (!dw) return fail(RMSNORM_ERR_NULL, "dw must be non-NULL");
     if (M > 0 && (!x || !w || !dy || !rstd || !dx))
         return fail(RMSNORM_ERR_NULL, "x, w, dy, rstd and dx must be non-NULL");
     if (!std::isfinite(offset)) return fail(RMSNORM_ERR_SCALAR, "offset must be finite");
-    const int64_t xb = M * N * 2, wb = N * 2, rb = M * 4, db = N * 4;
+    const int64_t es = elem_size(dtype);
+    const int64_t xb = M * N * es, wb = N * es, rb = M * 4, db = N * 4;
     if (M > 0) {
         if (ranges_overlap(dx, xb, x, xb)) return fail(RMSNORM_ERR_OVERLAP, "dx overlaps x");
         if (dx != dy && ranges_overlap(dx, xb, dy, xb)) return fail(RMSNORM_ERR_OVERLAP, "dx partially overlaps dy");
@@ -597,16 +597,18 @@ int check_bwd_args(const void* x, const void* w, const void* dy, const float* rs
 }
 
 int check_workspace(const void* ws, int64_t ws_bytes, int64_t need, const void* x, const void* w,
-                    const void* dy, const float* rstd, const void* dx, const float* dw, int64_t M, int64_t N) {
+                    const void* dy, const float* rstd, const void* dx, const float* dw, int64_t M, int64_t N,
+                    int dtype) {
     if (need == 0) return RMSNORM_OK;
     if (!ws) return fail(RMSNORM_ERR_NULL, "workspace must be non-NULL");
     if (ws_bytes < need)
         return fail(RMSNORM_ERR_SHAPE, "workspace holds " + std::to_string(ws_bytes) + " bytes, plan needs " +
                                            std::to_string(need));
     if ((reinterpret_cast<uintptr_t>(ws) & 15u) != 0) return fail(RMSNORM_ERR_PLAN, "workspace must be 16-byte aligned");
-    const int64_t xb = M * N * 2;
+    const int64_t es = elem_size(dtype);
+    const int64_t xb = M * N * es;
     if (ranges_overlap(ws, need, x, xb) || ranges_overlap(ws, need, dy, xb) || ranges_overlap(ws, need, dx, xb) ||
-        ranges_overlap(ws, need, w, N * 2) || ranges_overlap(ws, need, rstd, M * 4) ||
+        ranges_overlap(ws, need, w, N * es) || ranges_overlap(ws, need, rstd, M * 4) ||
         ranges_overlap(ws, need, dw, N * 4))
         return fail(RMSNORM_ERR_OVERLAP, "workspace overlaps an argument");
     return RMSNORM_OK;
@@ -630,14 +632,15 @@ int finish_bwd_plan(rmsnorm_plan_t* p, int64_t M, int64_t N, int dtype, const vo
         p->rows_per_trip = 1;
         k = pf ? nullptr : find_bwd_kernel(RMSNORM_VARIANT_GENERIC, dtype, 0, 0, 1, false);
     } else if (p->variant == RMSNORM_VARIANT_WAVE || p->variant == RMSNORM_VARIANT_BLOCK) {
-        if (N % 8 != 0) return fail(RMSNORM_ERR_PLAN, "16-byte kernels need N % 8 == 0");
+        const int epv = elems_per_vector(dtype);
+        if (N % epv != 0) return fail(RMSNORM_ERR_PLAN, "16-byte kernels need N to be a multiple of vec_elems");
         if (!aligned16(x) || !aligned16(w) || !aligned16(dy) || !aligned16(dx))
             return fail(RMSNORM_ERR_PLAN, "16-byte kernels need 16-byte aligned x, w, dy and dx");
-        p->vec_elems = 8;
+        p->vec_elems = epv;
         if (p->variant == RMSNORM_VARIANT_WAVE) {
             k = find_bwd_kernel(RMSNORM_VARIANT_WAVE, dtype, p->lanes_per_row, p->vectors_per_lane, p->row_slots, pf);
             if (k) {
-                if (static_cast<int64_t>(p->lanes_per_row) * p->vectors_per_lane * 8 < N)
+                if (static_cast<int64_t>(p->lanes_per_row) * p->vectors_per_lane * epv < N)
                     return fail(RMSNORM_ERR_PLAN, "wave plan does not cover N");
                 if (bwd_wave_lds(p, N) > kBwdMaxLds)
                     return fail(RMSNORM_ERR_PLAN, "wave plan needs more than 64 KiB of LDS for dw partials");
@@ -648,7 +651,7 @@ int finish_bwd_plan(rmsnorm_plan_t* p, int64_t M, int64_t N, int dtype, const vo
             p->lanes_per_row = p->block_threads;
             k = find_bwd_kernel(RMSNORM_VARIANT_BLOCK, dtype, 0, p->vectors_per_lane, 1, pf);
             if (k) {
-                if (static_cast<int64_t>(p->block_threads) * p->vectors_per_lane * 8 < N)
+                if (static_cast<int64_t>(p->block_threads) * p->vectors_per_lane * epv < N)
                     return fail(RMSNORM_ERR_PLAN, "block plan does not cover N");
                 p->rows_per_trip = 1;
             }
@@ -675,19 +678,20 @@ int choose_bwd_plan(int64_t M, int64_t N, const void* x, const void* w, const vo
                     int dtype, rmsnorm_plan_t* p) {
     std::memset(p, 0, sizeof(*p));
     p->xcd_group = 1;
-    const bool vec_ok = (N % 8 == 0) && aligned16(x) && aligned16(w) && aligned16(dy) && aligned16(dx) &&
-                        N <= kBwdMaxVectorN;
+    const int64_t epv = elems_per_vector(dtype);
+    const bool vec_ok = (N % epv == 0) && aligned16(x) && aligned16(w) && aligned16(dy) && aligned16(dx) &&
+                        N / epv <= kBwdMaxVectors;
     if (!vec_ok) {
         p->variant = RMSNORM_VARIANT_GENERIC;
         p->block_threads = N >= 1024 ? 256 : (N >= 256 ? 128 : 64);
         p->row_slots = 1;
-    } else if (N / 8 <= 128) {
-        const int64_t nvec = N / 8;
+    } else if (N / epv <= 128) {
+        const int64_t nvec = N / epv;
         p->variant = RMSNORM_VARIANT_WAVE;
         p->block_threads = kBwdWaveThreads;
         p->lanes_per_row = nvec <= 16 ? 16 : (nvec <= 32 ? 32 : 64);
         p->vectors_per_lane = static_cast<int>(ceil_div(nvec, p->lanes_per_row));
-        const int64_t per_slot = N * 2 * (64 / p->lanes_per_row);
+        const int64_t per_slot = N * elem_size(dtype) * (64 / p->lanes_per_row);
         p->row_slots = 1;
         // A row per 64-lane wave: one row per trip, the next trip's loads
         // issued ahead (16384 x 512: 13.5 us against 15.0 us with four rows
@@ -701,7 +705,7 @@ int choose_bwd_plan(int64_t M, int64_t N, const void* x, const void* w, const vo
             }
         }
     } else {
-        const int64_t nvec = N / 8;
+        const int64_t nvec = N / epv;
         p->variant = RMSNORM_VARIANT_BLOCK;
         p->row_slots = 1;
         p->block_threads = nvec <= 512 ? 256 : (nvec <= 1024 ? 512 : 1024);
@@ -776,7 +780,7 @@ int bwd_common(const void* x, const void* w, const void* dy, const float* rstd, 
     int st = finish_bwd_plan(p, M, N, dtype, x, w, dy, dx, &k);
     if (st != RMSNORM_OK) return st;
     const int64_t need = M > 0 ? p->grid * N * 4 : 0;
-    st = check_workspace(ws, ws_bytes, need, x, w, dy, rstd, dx, dw, M, N);
+    st = check_workspace(ws, ws_bytes, need, x, w, dy, rstd, dx, dw, M, N, dtype);
     if (st != RMSNORM_OK) return st;
     int cu = 0;
     st = device_info(&cu);
@@ -941,7 +945,7 @@ int rmsnorm_bwd_plan_query(int64_t M, int64_t N, int dtype, const void* x, const
                            int32_t cu_count, rmsnorm_plan_t* out) {
     g_last_error.clear();
     if (!out) return fail(RMSNORM_ERR_NULL, "out must be non-NULL");
-    int st = check_shape_dtype(M, N, dtype, false);
+    int st = check_shape_dtype(M, N, dtype);
     if (st != RMSNORM_OK) return st;
     rmsnorm_plan_t p;
     const KernelEntry* k = nullptr;
@@ -957,7 +961,7 @@ int rmsnorm_bwd_workspace_size(int64_t M, int64_t N, int dtype, const void* x, c
                                int64_t* bytes) {
     g_last_error.clear();
     if (!bytes) return fail(RMSNORM_ERR_NULL, "bytes must be non-NULL");
-    int st = check_shape_dtype(M, N, dtype, false);
+    int st = check_shape_dtype(M, N, dtype);
     if (st != RMSNORM_OK) return st;
     rmsnorm_plan_t p;
     choose_bwd_plan(M, N, x, dx, dy, dx, dtype, &p);

@@ -9,7 +9,8 @@
 //     dx[m,k]  = r (g_k dy[m,k] - r^2 c[m] x[m,k])
 //     dw[j]    = sum_m dy[m,j] x[m,j] r[m]
 //
-// All arithmetic is fp32; x, w, dy and dx are bf16 or fp16, rstd and dw fp32.
+// All arithmetic is fp32; x, w, dy and dx are bf16, fp16 or fp32 (D: eight
+// 16-bit or four fp32 elements per 16-byte vector), rstd and dw fp32.
 //
 // Two passes.  The row pass runs a grid of G workgroups that loop over rows
 // (a persistent grid: each workgroup keeps its columns' share of dw in
@@ -35,44 +36,39 @@ constexpr u32x4 kZero = {0u, 0u, 0u, 0u};
 __device__ __forceinline__ u32x4 stream_load(const u32x4* p) { return __builtin_nontemporal_load(p); }
 __device__ __forceinline__ void stream_store(u32x4* p, u32x4 v) { __builtin_nontemporal_store(v, p); }
 
-// sum over this lane's 8 columns of one vector of dy * g * x
+// sum over this lane's D::EPV columns of one vector of dy * g * x
 template <class D>
-__device__ __forceinline__ float dot_dgx(const u32x4 dq, const u32x4 xq, const float (&g)[8], float acc) {
+__device__ __forceinline__ float dot_dgx(const u32x4 dq, const u32x4 xq, const float (&g)[D::EPV], float acc) {
+    float d[D::EPV], xv[D::EPV];
+    D::widen(dq, d);
+    D::widen(xq, xv);
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-        acc = __builtin_fmaf(D::lo(dq[k]) * g[2 * k], D::lo(xq[k]), acc);
-        acc = __builtin_fmaf(D::hi(dq[k]) * g[2 * k + 1], D::hi(xq[k]), acc);
-    }
+    for (int k = 0; k < D::EPV; ++k) acc = __builtin_fmaf(d[k] * g[k], xv[k], acc);
     return acc;
 }
 
 // dx for one vector, and dw partials += dy * x * r
 template <class D>
-__device__ __forceinline__ u32x4 grad_vector(const u32x4 dq, const u32x4 xq, const float (&g)[8], float r,
-                                             float r2c, float (&dwp)[8]) {
-    u32x4 o;
+__device__ __forceinline__ u32x4 grad_vector(const u32x4 dq, const u32x4 xq, const float (&g)[D::EPV], float r,
+                                             float r2c, float (&dwp)[D::EPV]) {
+    float d[D::EPV], xv[D::EPV], o[D::EPV];
+    D::widen(dq, d);
+    D::widen(xq, xv);
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-        const float d0 = D::lo(dq[k]), d1 = D::hi(dq[k]);
-        const float x0 = D::lo(xq[k]), x1 = D::hi(xq[k]);
-        const float v0 = r * (g[2 * k] * d0 - r2c * x0);
-        const float v1 = r * (g[2 * k + 1] * d1 - r2c * x1);
-        dwp[2 * k] = __builtin_fmaf(d0 * x0, r, dwp[2 * k]);
-        dwp[2 * k + 1] = __builtin_fmaf(d1 * x1, r, dwp[2 * k + 1]);
-        o[k] = D::pack(v0, v1);
+    for (int k = 0; k < D::EPV; ++k) {
+        o[k] = r * (g[k] * d[k] - r2c * xv[k]);
+        dwp[k] = __builtin_fmaf(d[k] * xv[k], r, dwp[k]);
     }
-    return o;
+    return D::narrow(o);
 }
 
 // offset + w widened from one packed 16-byte weight vector, at the point of
 // use (the block family keeps w packed: 4 VGPRs per vector instead of 8)
 template <class D>
-__device__ __forceinline__ void widen_g(float (&g)[8], const u32x4 q, float offset) {
+__device__ __forceinline__ void widen_g(float (&g)[D::EPV], const u32x4 q, float offset) {
+    D::widen(q, g);
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-        g[2 * k] = offset + D::lo(q[k]);
-        g[2 * k + 1] = offset + D::hi(q[k]);
-    }
+    for (int k = 0; k < D::EPV; ++k) g[k] = offset + g[k];
 }
 
 }  // namespace
@@ -95,7 +91,7 @@ __global__ __launch_bounds__(1024) void rmsnorm_bwd_wave(BwdArgs a) {
     u32x4* __restrict__ dx = static_cast<u32x4*>(a.dx);
     const int64_t M = a.M;
     const int N = static_cast<int>(a.N);
-    const int nvec = N >> 3;
+    const int nvec = N / D::EPV;
     const int lane = threadIdx.x & 63;
     const int seg = lane / LANES;
     const int li = lane % LANES;
@@ -103,14 +99,14 @@ __global__ __launch_bounds__(1024) void rmsnorm_bwd_wave(BwdArgs a) {
     const int wid = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
     const int64_t nwaves = a.grid * wpb;
 
-    float g[VPL][8];
-    float dwp[VPL][8];
+    float g[VPL][D::EPV];
+    float dwp[VPL][D::EPV];
 #pragma unroll
     for (int v = 0; v < VPL; ++v) {
         const int c = v * LANES + li;
         widen_g<D>(g[v], c < nvec ? w[c] : kZero, a.offset);
 #pragma unroll
-        for (int k = 0; k < 8; ++k) dwp[v][k] = 0.0f;
+        for (int k = 0; k < D::EPV; ++k) dwp[v][k] = 0.0f;
     }
 
     auto load_trip = [&](u32x4 (&xd)[SLOTS][VPL], u32x4 (&dd)[SLOTS][VPL], float (&r)[SLOTS], int64_t gg) {
@@ -181,7 +177,7 @@ __global__ __launch_bounds__(1024) void rmsnorm_bwd_wave(BwdArgs a) {
         const int c = v * LANES + li;
         if (c < nvec) {
 #pragma unroll
-            for (int k = 0; k < 8; ++k) mine[c * 8 + k] = dwp[v][k];
+            for (int k = 0; k < D::EPV; ++k) mine[c * D::EPV + k] = dwp[v][k];
         }
     }
     __syncthreads();
@@ -210,7 +206,7 @@ __global__ __launch_bounds__(1024) void rmsnorm_bwd_block(BwdArgs a) {
     const float* __restrict__ rstd = a.rstd;
     u32x4* __restrict__ dx = static_cast<u32x4*>(a.dx);
     const int64_t M = a.M;
-    const int nvec = static_cast<int>(a.N >> 3);
+    const int nvec = static_cast<int>(a.N / D::EPV);
     const int tid = threadIdx.x;
     const int nt = a.threads;
     const int lane = tid & 63;
@@ -218,13 +214,13 @@ __global__ __launch_bounds__(1024) void rmsnorm_bwd_block(BwdArgs a) {
     const int nw = nt >> 6;
 
     u32x4 wq[VPT];
-    float dwp[VPT][8];
+    float dwp[VPT][D::EPV];
 #pragma unroll
     for (int v = 0; v < VPT; ++v) {
         const int c = v * nt + tid;
         wq[v] = c < nvec ? w[c] : kZero;
 #pragma unroll
-        for (int k = 0; k < 8; ++k) dwp[v][k] = 0.0f;
+        for (int k = 0; k < D::EPV; ++k) dwp[v][k] = 0.0f;
     }
 
     auto load_row = [&](u32x4 (&xd)[VPT], u32x4 (&dd)[VPT], float& r, int64_t rr) {
@@ -256,7 +252,7 @@ __global__ __launch_bounds__(1024) void rmsnorm_bwd_block(BwdArgs a) {
         float t = 0.0f;
 #pragma unroll
         for (int v = 0; v < VPT; ++v) {
-            float g[8];
+            float g[D::EPV];
             widen_g<D>(g, wq[v], a.offset);
             t = dot_dgx<D>(dd[v], xd[v], g, t);
         }
@@ -270,7 +266,7 @@ __global__ __launch_bounds__(1024) void rmsnorm_bwd_block(BwdArgs a) {
 #pragma unroll
         for (int v = 0; v < VPT; ++v) {
             const int c = v * nt + tid;
-            float g[8];
+            float g[D::EPV];
             widen_g<D>(g, wq[v], a.offset);
             const u32x4 o = grad_vector<D>(dd[v], xd[v], g, r, r2c, dwp[v]);
             if (c < nvec) stream_store(out + c, o);
@@ -293,14 +289,14 @@ __global__ __launch_bounds__(1024) void rmsnorm_bwd_block(BwdArgs a) {
         const int c = v * nt + tid;
         if (c < nvec) {
 #pragma unroll
-            for (int k = 0; k < 8; ++k) dst[c * 8 + k] = dwp[v][k];
+            for (int k = 0; k < D::EPV; ++k) dst[c * D::EPV + k] = dwp[v][k];
         }
     }
 }
 
 // ---------------------------------------------------------------------------
 // Row pass, generic (any N and alignment): one row per workgroup per trip,
-// 2-byte accesses, the row read twice (c first, then dx), and the
+// element-wide accesses, the row read twice (c first, then dx), and the
 // workgroup's partial row of dw updated in the workspace in place (each
 // workgroup owns its own partial row, so no other workgroup touches it).
 // dx may be the same buffer as dy: each element is read, then written, by
@@ -309,10 +305,11 @@ __global__ __launch_bounds__(1024) void rmsnorm_bwd_block(BwdArgs a) {
 template <class D>
 __global__ __launch_bounds__(1024) void rmsnorm_bwd_generic(BwdArgs a) {
     __shared__ float part[2][16];
-    const uint16_t* x = static_cast<const uint16_t*>(a.x);
-    const uint16_t* __restrict__ w = static_cast<const uint16_t*>(a.w);
-    const uint16_t* dy = static_cast<const uint16_t*>(a.dy);
-    uint16_t* dx = static_cast<uint16_t*>(a.dx);
+    typedef typename D::elem_t E;
+    const E* x = static_cast<const E*>(a.x);
+    const E* __restrict__ w = static_cast<const E*>(a.w);
+    const E* dy = static_cast<const E*>(a.dy);
+    E* dx = static_cast<E*>(a.dx);
     const int64_t M = a.M;
     const int64_t N = a.N;
     const int tid = threadIdx.x;
@@ -325,9 +322,9 @@ __global__ __launch_bounds__(1024) void rmsnorm_bwd_generic(BwdArgs a) {
 
     int par = 0;
     for (int64_t row = blockIdx.x; row < M; row += a.grid) {
-        const uint16_t* xr = x + row * N;
-        const uint16_t* dr = dy + row * N;
-        uint16_t* out = dx + row * N;
+        const E* xr = x + row * N;
+        const E* dr = dy + row * N;
+        E* out = dx + row * N;
         const float r = a.rstd[row];
         float t = 0.0f;
         for (int64_t j = tid; j < N; j += nt)
@@ -420,8 +417,9 @@ __global__ __launch_bounds__(16 * SPLIT) void rmsnorm_dw_reduce(const float* __r
      reinterpret_cast<const void*>(&rmsnorm_bwd_block<D, V, P>),                               \
      "rmsnorm_bwd_block<" #D "," #V "," #P ">"}
 // Only instances that fit 128 VGPRs without scratch: the block family holds
-// at most two vectors of x and dy per thread (rows up to 1024 x 2 x 8 = 16384),
-// and the widest wave shapes have no prefetching form.
+// at most two vectors of x and dy per thread (rows up to 1024 x 2 vectors:
+// 16384 16-bit or 8192 fp32 elements), and the widest wave shapes have no
+// prefetching form.
 #define RMS_BWD_FAMILY(D, DT)                                                                  \
     RMS_BWD_WAVE2(D, DT, 16, 1, 1), RMS_BWD_WAVE2(D, DT, 16, 1, 2),                            \
     RMS_BWD_WAVE2(D, DT, 32, 1, 1), RMS_BWD_WAVE2(D, DT, 32, 1, 2),                            \
@@ -438,6 +436,7 @@ namespace rmsnorm_impl {
 static const KernelEntry kBwdTable[] = {
     RMS_BWD_FAMILY(BF16, RMSNORM_BF16),
     RMS_BWD_FAMILY(FP16, RMSNORM_FP16),
+    RMS_BWD_FAMILY(F32, RMSNORM_FP32),
 };
 
 const KernelEntry* bwd_kernel_table(int* count) {

@@ -88,6 +88,11 @@ class Oracle:
             ctypes.c_int, _U16P, _F64P, _F64P, _F64P, _F64P,
         ]
         lib.oracle_rmsnorm_bwd.restype = ctypes.c_int
+        lib.oracle_rmsnorm_bwd_f64.argtypes = [
+            _F64P, _F64P, _F64P, _F64P, ctypes.c_int64, ctypes.c_int64, ctypes.c_double,
+            _F64P, _F64P, _F64P, _F64P,
+        ]
+        lib.oracle_rmsnorm_bwd_f64.restype = ctypes.c_int
         lib.oracle_max_threads.argtypes = []
         lib.oracle_max_threads.restype = ctypes.c_int
         lib.oracle_set_threads.argtypes = [ctypes.c_int]
@@ -183,6 +188,31 @@ class Oracle:
             return dx, dw, ex, sc, ws
         return dx, dw
 
+    def rmsnorm_bwd_f64(self, x, w, dy, rstd, offset: float):
+        """Backward on fp64 inputs (fp32 values widen exactly), no codec.
+        Returns (dx before rounding, dw, dx term scale, dw term scale), all
+        float64; ``offset`` is used as given (pass an fp32 value)."""
+        x = np.ascontiguousarray(x, dtype=np.float64)
+        dy = np.ascontiguousarray(dy, dtype=np.float64)
+        w = np.ascontiguousarray(w, dtype=np.float64)
+        if x.ndim != 2 or dy.shape != x.shape or w.shape != (x.shape[1],):
+            raise ValueError(f"shape mismatch: x {x.shape}, dy {dy.shape}, w {w.shape}")
+        M, N = x.shape
+        r = np.ascontiguousarray(rstd, dtype=np.float64)
+        if r.shape != (M,):
+            raise ValueError(f"rstd must have shape [{M}]")
+        ex = np.empty((M, N), dtype=np.float64)
+        dw = np.empty((N,), dtype=np.float64)
+        sc = np.empty((M, N), dtype=np.float64)
+        ws = np.empty((N,), dtype=np.float64)
+        rc = self._lib.oracle_rmsnorm_bwd_f64(
+            x.ctypes.data_as(_F64P), w.ctypes.data_as(_F64P), dy.ctypes.data_as(_F64P), r.ctypes.data_as(_F64P),
+            M, N, float(offset), ex.ctypes.data_as(_F64P), dw.ctypes.data_as(_F64P), sc.ctypes.data_as(_F64P),
+            ws.ctypes.data_as(_F64P))
+        if rc != 0:
+            raise ValueError(f"oracle rejected arguments (M={M}, N={N})")
+        return ex, dw, sc, ws
+
     def max_threads(self) -> int:
         """Threads the OpenMP loop uses (OMP_NUM_THREADS, else all cores)."""
         return int(self._lib.oracle_max_threads())
@@ -223,6 +253,10 @@ def rmsnorm_fwd_f64(x, w, eps: float, offset: float):
 
 def rmsnorm_bwd(x_bits, w_bits, dy_bits, rstd, offset: float, dtype: str, want_exact: bool = False):
     return default().rmsnorm_bwd(x_bits, w_bits, dy_bits, rstd, offset, dtype, want_exact)
+
+
+def rmsnorm_bwd_f64(x, w, dy, rstd, offset: float):
+    return default().rmsnorm_bwd_f64(x, w, dy, rstd, offset)
 
 
 def max_threads() -> int:

@@ -284,6 +284,54 @@ int oracle_rmsnorm_bwd(const uint16_t* x, const uint16_t* w, const uint16_t* dy,
     return 0;
 }
 
+/*
+ * The same backward on fp64 inputs with no codec on either side, for inputs
+ * of a wider type (fp32 values widen to fp64 exactly).  Same formula and
+ * summation order as oracle_rmsnorm_bwd; dx is returned unrounded.
+ *   x, dy [M*N] fp64; w [N] fp64; rstd [M] fp64; offset fp64 (an fp32 value)
+ *   dx_exact [M*N], dw [N] fp64 outputs; dx_scale [M*N], dw_scale [N] as above
+ *   (either may be NULL)
+ */
+int oracle_rmsnorm_bwd_f64(const double* x, const double* w, const double* dy, const double* rstd,
+                           int64_t M, int64_t N, double offset, double* dx_exact, double* dw,
+                           double* dx_scale, double* dw_scale)
+{
+    if (M < 0 || N <= 0) return -1;
+
+#pragma omp parallel for schedule(static)
+    for (int64_t m = 0; m < M; ++m) {
+        const double* xr = x + m * N;
+        const double* dyr = dy + m * N;
+        const double r = rstd[m];
+        double c = 0.0, cabs = 0.0;
+        for (int64_t j = 0; j < N; ++j) {
+            const double t = dyr[j] * (offset + w[j]) * xr[j];
+            c += t;
+            cabs += fabs(t);
+        }
+        c /= (double)N;
+        cabs /= (double)N;
+        for (int64_t k = 0; k < N; ++k) {
+            const double gk = offset + w[k];
+            const double v = r * (gk * dyr[k] - r * r * c * xr[k]);
+            dx_exact[m * N + k] = v;
+            if (dx_scale) dx_scale[m * N + k] = fabs(r * gk * dyr[k]) + fabs(r * r * r * xr[k]) * cabs;
+        }
+    }
+
+    for (int64_t j = 0; j < N; ++j) {
+        double acc = 0.0, aabs = 0.0;
+        for (int64_t m = 0; m < M; ++m) {
+            const double t = dy[m * N + j] * x[m * N + j] * rstd[m];
+            acc += t;
+            aabs += fabs(t);
+        }
+        dw[j] = acc;
+        if (dw_scale) dw_scale[j] = aabs;
+    }
+    return 0;
+}
+
 /* Threads the OpenMP loops use from now on (n >= 1); a timing knob only, the
    results do not depend on it. */
 void oracle_set_threads(int n)

@@ -594,6 +594,56 @@ def pin_bwd_constant_row(o):
                 assert np.allclose(dw, M * c * r[0], rtol=1e-15, atol=0), (dtype, c, eps)
 
 
+def pin_bwd_f64_path(o):
+    """The fp64-input backward (the fp32 path's oracle): equal, bit for bit, to the codec backward on
+    16-bit inputs; against central differences of the fp64 forward and torch float64 autograd on
+    fp32 inputs; dw of one row is dy x r exactly."""
+    rng = np.random.default_rng(59)
+    for dtype in ("bf16", "fp16"):
+        x, w, dy, xd, wd, dyd, r = _bwd_case(o, rng, 4, 37, dtype, 1e-6, 1.0)
+        _, dw, dxe, dxs, dws = o.rmsnorm_bwd(x, w, dy, r, 1.0, dtype, want_exact=True)
+        ex, dw2, sc, ws = o.rmsnorm_bwd_f64(xd, wd, dyd, r, fp32(1.0))
+        assert np.array_equal(ex, dxe) and np.array_equal(dw2, dw), dtype
+        assert np.array_equal(sc, dxs) and np.array_equal(ws, dws), dtype
+    f32 = lambda a: np.asarray(a, dtype=np.float32).astype(np.float64)
+    for M, N, eps, offset in ((3, 7, 1e-6, 0.0), (2, 16, 0.5, 1.0), (1, 1, 1e-3, 0.0)):
+        xd = f32(rng.normal(0, 3, size=(M, N)))
+        wd = f32(rng.normal(0.3, 0.5, size=N))
+        dyd = f32(rng.normal(0, 1, size=(M, N)))
+        e, off = fp32(eps), fp32(offset)
+        _, r = o.rmsnorm_fwd_f64(xd, wd, e, off)
+        dxe, dw, _, _ = o.rmsnorm_bwd_f64(xd, wd, dyd, r, off)
+
+        def loss(xx, ww):
+            y, _ = o.rmsnorm_fwd_f64(xx, ww, e, off)
+            return float(np.sum(dyd * y))
+
+        fd_x = np.empty_like(xd)
+        for idx in np.ndindex(*xd.shape):
+            h = 1e-6 * max(1.0, abs(xd[idx]))
+            xp, xm = xd.copy(), xd.copy()
+            xp[idx] += h
+            xm[idx] -= h
+            fd_x[idx] = (loss(xp, wd) - loss(xm, wd)) / (2 * h)
+        fd_w = np.empty_like(wd)
+        for j in range(N):
+            h = 1e-6 * max(1.0, abs(wd[j]))
+            wp, wm = wd.copy(), wd.copy()
+            wp[j] += h
+            wm[j] -= h
+            fd_w[j] = (loss(xd, wp) - loss(xd, wm)) / (2 * h)
+        assert np.allclose(dxe, fd_x, rtol=1e-6, atol=1e-7 * (np.max(np.abs(fd_x)) + 1.0)), (M, N)
+        assert np.allclose(dw, fd_w, rtol=1e-6, atol=1e-7 * (np.max(np.abs(fd_w)) + 1.0)), (M, N)
+        xt = torch.tensor(xd, requires_grad=True)
+        wt = torch.tensor(wd, requires_grad=True)
+        y = xt * torch.rsqrt(xt.pow(2).mean(-1, keepdim=True) + e) * (off + wt)
+        y.backward(torch.tensor(dyd))
+        assert np.allclose(dxe, xt.grad.numpy(), rtol=1e-9, atol=1e-12 * np.max(np.abs(dxe))), (M, N)
+        assert np.allclose(dw, wt.grad.numpy(), rtol=1e-9, atol=1e-12 * np.max(np.abs(dw))), (M, N)
+        if M == 1:
+            assert np.array_equal(dw, dyd[0] * xd[0] * r[0])
+
+
 def pin_fp32_path(o):
     """fp32 inputs: the oracle's fp64 forward, then one IEEE round-to-nearest-even to binary32.
 
@@ -671,5 +721,6 @@ ALL_PINS = [
     pin_bwd_torch_autograd,
     pin_bwd_identities,
     pin_bwd_constant_row,
+    pin_bwd_f64_path,
     pin_fp32_path,
 ]

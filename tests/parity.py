@@ -100,8 +100,8 @@ def oracle_for(x_cpu: torch.Tensor, w_cpu: torch.Tensor, eps: float, offset: flo
 # partial rows), with a factor 2 to spare, plus the final rounding.
 # Both sides use the same rstd values.
 # ---------------------------------------------------------------------------
-FRAC_BITS = {"bf16": 7, "fp16": 10}
-MIN_EXP = {"bf16": -126, "fp16": -14}
+FRAC_BITS = {"bf16": 7, "fp16": 10, "fp32": 23}
+MIN_EXP = {"bf16": -126, "fp16": -14, "fp32": -126}
 
 
 def ulp_of(v: np.ndarray, dtype: str) -> np.ndarray:
@@ -112,7 +112,10 @@ def ulp_of(v: np.ndarray, dtype: str) -> np.ndarray:
 
 def compare_bwd(dx_gpu: torch.Tensor, dw_gpu: torch.Tensor, dx_exact: np.ndarray, dx_scale: np.ndarray,
                 dw_exact: np.ndarray, dw_scale: np.ndarray, dtype: str, M: int, G: int, what: str = "") -> dict:
-    dxg = oracle.decode(gpu_bits(dx_gpu).reshape(dx_exact.shape), dtype)
+    if dtype == "fp32":
+        dxg = dx_gpu.cpu().double().numpy().reshape(dx_exact.shape)
+    else:
+        dxg = oracle.decode(gpu_bits(dx_gpu).reshape(dx_exact.shape), dtype)
     err = np.abs(dxg - dx_exact)
     bound = ulp_of(dx_exact, dtype) + 2.0 ** -16 * dx_scale
     bad = ~(err <= bound)
@@ -134,9 +137,16 @@ def compare_bwd(dx_gpu: torch.Tensor, dw_gpu: torch.Tensor, dx_exact: np.ndarray
 
 
 def oracle_bwd_for(x_cpu, w_cpu, dy_cpu, rstd_f32: np.ndarray, offset: float, dtype: str):
-    """Oracle backward on the same rstd values the GPU receives."""
+    """Oracle backward on the same rstd values the GPU receives: (dx bits or None for fp32, dw,
+    dx before rounding, dx term scale, dw term scale).  fp32 inputs widen to fp64 exactly and take
+    the codec-free backward; the bar is then one fp32 ulp of dx plus the arithmetic term."""
+    r = np.asarray(rstd_f32, dtype=np.float64)
+    if dtype == "fp32":
+        ex, dw, sc, ws = oracle.rmsnorm_bwd_f64(x_cpu.double().numpy(), w_cpu.double().numpy(),
+                                                dy_cpu.double().numpy(), r, float(np.float32(offset)))
+        return None, dw, ex, sc, ws
     return oracle.rmsnorm_bwd(workloads.to_bits(x_cpu), workloads.to_bits(w_cpu), workloads.to_bits(dy_cpu),
-                              np.asarray(rstd_f32, dtype=np.float64), offset, dtype, want_exact=True)
+                              r, offset, dtype, want_exact=True)
 
 
 # ---------------------------------------------------------------------------

@@ -262,7 +262,7 @@ def bwd(x=X, w=W, dy=DY, rstd=R, dx=DX, dw=DW, M=4, N=512, offset=0.0, dtype=BF1
     (dict(M=-1), SHAPE),
     (dict(N=0), SHAPE),
     (dict(dtype=7), DTYPE),
-    (dict(dtype=2), DTYPE),                # fp32 is forward only
+    (dict(dtype=3), DTYPE),                # not a dtype code
     (dict(dw=None), NULL),
     (dict(x=None), NULL),
     (dict(dy=None), NULL),
@@ -282,6 +282,19 @@ def bwd(x=X, w=W, dy=DY, rstd=R, dx=DX, dw=DW, M=4, N=512, offset=0.0, dtype=BF1
 def test_bwd_argument_errors(kwargs, status):
     assert bwd(**kwargs) == status, lib.rmsnorm_last_error().decode()
     assert lib.rmsnorm_last_error().decode() != ""
+
+
+@pytest.mark.parametrize("N,variant,lanes,vpl", [(128, 1, 32, 1), (512, 1, 64, 2), (4096, 2, 512, 2),
+                                               (8192, 2, 1024, 2), (8196, 3, 0, 0), (8200, 3, 0, 0),
+                                               (1002, 3, 0, 0)])
+def test_bwd_fp32_plans(N, variant, lanes, vpl):
+    """fp32 rows: four elements per 16-byte vector, so the wave family holds 512 and the block
+    family 8192 elements; other widths take the generic kernel."""
+    p = bnd.Plan()
+    assert lib.rmsnorm_bwd_plan_query(4096, N, FP32, None, None, None, 256, ctypes.byref(p)) == OK
+    assert p.variant == variant
+    if variant != 3:
+        assert (p.vec_elems, p.lanes_per_row, p.vectors_per_lane) == (4, lanes, vpl)
 
 
 def test_bwd_plans_and_workspace():

@@ -62,18 +62,19 @@ def test_bwd_workload(bnd, name):
 
 def bwd_candidates(bnd, M, N, dtype):
     base = bnd.bwd_plan_query(M, N, dtype)
+    epv = 4 if dtype == "fp32" else 8
     out = []
     for pf in (0, 1):
         for lanes in (16, 32, 64):
             for vpl in (1, 2):
                 for slots in (1, 2, 4):
                     for threads in (256, 512, 1024):
-                        if lanes * vpl * 8 >= N:
+                        if lanes * vpl * epv >= N:
                             out.append(base.copy(variant=bnd.VARIANT_WAVE, lanes_per_row=lanes, vectors_per_lane=vpl,
                                                  row_slots=slots, block_threads=threads, prefetch=pf))
         for threads in (64, 128, 256, 512, 1024):
             for vpt in (1, 2):
-                if threads * vpt * 8 >= N:
+                if threads * vpt * epv >= N:
                     out.append(base.copy(variant=bnd.VARIANT_BLOCK, block_threads=threads, vectors_per_lane=vpt,
                                          row_slots=1, prefetch=pf))
     for threads in (64, 256):
@@ -187,3 +188,58 @@ def test_bwd_zero_rows_and_guards(bnd):
     e = parity.oracle_bwd_for(x, w, dy, r32, wl.offset, wl.dtype)
     p = bnd.bwd_plan_query(M, N, wl.dtype)
     parity.compare_bwd(dxv, dwv, e[2], e[3], e[1], e[4], wl.dtype, M, p.grid, "guards")
+
+
+# ---------------------------------------------------------------------------
+# fp32 input: four elements per 16-byte vector.  The oracle is the codec-free
+# fp64 backward on the exactly widened inputs; the bar is one fp32 ulp of dx
+# plus the same arithmetic term as for the 16-bit types.
+# ---------------------------------------------------------------------------
+def fp32_case(M, N, offset, seed):
+    g = torch.Generator().manual_seed(seed)
+    x = torch.randn(M, N, generator=g) * 2.0
+    w = 1.0 + 0.1 * torch.randn(N, generator=g)
+    dy = torch.randn(M, N, generator=g)
+    _, r64 = parity.oracle_fp32(x, w, 1e-6, offset)
+    return x, w, dy, r64.astype(np.float32)
+
+
+@pytest.mark.parametrize("M,N,offset", [(777, 128, 0.0), (777, 500, 1.0), (3000, 512, 0.0), (97, 4096, 1.0),
+                                        (57, 8192, 0.0), (33, 1002, 1.0), (20, 8196, 0.0)])
+def test_bwd_fp32_rule(bnd, M, N, offset):
+    x, w, dy, r32 = fp32_case(M, N, offset, seed=N)
+    xg, wg, dyg = x.to(DEV), w.to(DEV), dy.to(DEV)
+    rg = torch.from_numpy(r32).to(DEV)
+    p = bnd.bwd_plan_query(M, N, "fp32", xg.data_ptr(), dyg.data_ptr(), dyg.data_ptr())
+    announce("bwd fp32", M, N, offset, p.as_dict())
+    dx, dw = bnd.rmsnorm_bwd(xg, wg, dyg, rg, offset)
+    torch.cuda.synchronize()
+    _, dwe, dxe, dxs, dws = parity.oracle_bwd_for(x, w, dy, r32, offset, "fp32")
+    stats = parity.compare_bwd(dx, dw, dxe, dxs, dwe, dws, "fp32", M, p.grid, f"bwd fp32 {M}x{N}")
+    print("bwd fp32", M, N, stats, flush=True)
+
+
+@pytest.mark.parametrize("M,N", [(777, 256), (300, 512), (97, 4096), (45, 8192)])
+def test_bwd_fp32_every_kernel(bnd, M, N):
+    x, w, dy, r32 = fp32_case(M, N, 1.0, seed=N + 1)
+    xg, wg, dyg = x.to(DEV), w.to(DEV), dy.to(DEV)
+    rg = torch.from_numpy(r32).to(DEV)
+    _, dwe, dxe, dxs, dws = parity.oracle_bwd_for(x, w, dy, r32, 1.0, "fp32")
+    ran = 0
+    for plan in bwd_candidates(bnd, M, N, "fp32"):
+        for grid in (1, 5, M):
+            p = plan.copy(grid=grid)
+            dx = torch.empty_like(xg)
+            dw = torch.full((N,), float("nan"), dtype=torch.float32, device=DEV)
+            ws = torch.empty(grid * N + 4, dtype=torch.float32, device=DEV)
+            announce("bwd fp32", M, N, p.as_dict())
+            try:
+                bnd.rmsnorm_bwd_out(xg, wg, dyg, rg, dx, dw, ws, 1.0, plan=p)
+            except bnd.RmsnormError as e:
+                if e.status == 8:
+                    continue
+                raise
+            torch.cuda.synchronize()
+            parity.compare_bwd(dx, dw, dxe, dxs, dwe, dws, "fp32", M, grid, f"bwd fp32 {M}x{N} {p.as_dict()}")
+            ran += 1
+    assert ran >= 12, ran

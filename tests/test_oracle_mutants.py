@@ -53,6 +53,16 @@ MUTANTS = {
     "bwd_dw_times_weight": [("oracle_decode(x[m * N + j], dtype) *\n                                 rstd[m];",
                              "oracle_decode(x[m * N + j], dtype) *\n                                 rstd[m] * (off + oracle_decode(w[j], dtype));")],
     "bwd_dw_wrong_row_stride": [("oracle_decode(dy[m * N + j], dtype)", "oracle_decode(dy[m + j * M], dtype)")],
+    # backward on fp64 inputs (the fp32 path)
+    "bwd_f64_second_term_sign": [("const double v = r * (gk * dyr[k] - r * r * c * xr[k]);",
+                                  "const double v = r * (gk * dyr[k] + r * r * c * xr[k]);")],
+    "bwd_f64_c_without_weight": [("const double t = dyr[j] * (offset + w[j]) * xr[j];",
+                                  "const double t = dyr[j] * xr[j];")],
+    "bwd_f64_offset_ignored": [("const double gk = offset + w[k];", "const double gk = w[k];")],
+    "bwd_f64_dw_without_rstd": [("const double t = dy[m * N + j] * x[m * N + j] * rstd[m];",
+                                 "const double t = dy[m * N + j] * x[m * N + j];")],
+    "bwd_f64_divisor_rows": [("c /= (double)N;\n        cabs /= (double)N;\n        for (int64_t k = 0; k < N; ++k) {\n            const double gk = offset",
+                              "c /= (double)M;\n        cabs /= (double)N;\n        for (int64_t k = 0; k < N; ++k) {\n            const double gk = offset")],
 }
 
 
