@@ -301,6 +301,50 @@ int rmsnorm_bwd_with_plan(const void* x, const void* w, const void* dy, const fl
                           void* stream);
 
 /*
+ * Row layout of the backward's x, dy and dx, as rmsnorm_layout_t for the
+ * forward ("Rmsnorm Kernel Optimization", Verification: the operation runs
+ * over the last dimension of a tensor of any rank).  Row m = b * rows + s
+ * (s < rows) starts at element b * x_batch_stride + s * x_row_stride of x,
+ * likewise of dy and dx; rstd stays [M] contiguous.  rows = 0 means M (one
+ * batch).  dx's rows must be disjoint (batch-major or row-major interleaved,
+ * as y in the forward), x's and dy's may overlap.  With several batches
+ * M < 2^31.  Element strides, >= 0.
+ */
+typedef struct rmsnorm_bwd_layout {
+    int64_t rows;
+    int64_t x_row_stride;
+    int64_t x_batch_stride;
+    int64_t dy_row_stride;
+    int64_t dy_batch_stride;
+    int64_t dx_row_stride;
+    int64_t dx_batch_stride;
+} rmsnorm_bwd_layout_t;
+
+/*
+ * The general backward: rows placed by `layout` (NULL = contiguous [M, N]),
+ * an optional explicit plan (NULL = the library's, as rmsnorm_bwd), the
+ * workspace as above.  dx may be exactly dy with the same row and batch
+ * strides (in place).  The 16-byte kernels run when x, w, dy and dx are
+ * 16-byte aligned, N is a multiple of vec_elems and every stride keeps rows
+ * aligned; the generic kernel otherwise.  Errors as rmsnorm_bwd, plus
+ * RMSNORM_ERR_SHAPE for a bad layout.
+ */
+int rmsnorm_bwd_ex(const void* x, const void* w, const void* dy, const float* rstd, void* dx,
+                   float* dw, int64_t M, int64_t N, float offset, int dtype,
+                   const rmsnorm_bwd_layout_t* layout, const rmsnorm_plan_t* plan, void* workspace,
+                   int64_t workspace_bytes, void* stream);
+
+/* Plan and workspace bytes of rmsnorm_bwd_ex for these sizes, pointers
+ * (alignment only; they may be NULL) and layout.  Host only unless
+ * cu_count <= 0 (plan query). */
+int rmsnorm_bwd_plan_query_ex(int64_t M, int64_t N, int dtype, const void* x, const void* w,
+                              const void* dy, const void* dx, const rmsnorm_bwd_layout_t* layout,
+                              int32_t cu_count, rmsnorm_plan_t* out);
+int rmsnorm_bwd_workspace_size_ex(int64_t M, int64_t N, int dtype, const void* x, const void* w,
+                                  const void* dy, const void* dx,
+                                  const rmsnorm_bwd_layout_t* layout, int64_t* bytes);
+
+/*
  * Completes and checks an explicit forward plan without launching anything:
  * the derived fields (vec_elems, rows_per_trip, trips) and resident_grid (as
  * in rmsnorm_plan_query, cu_count likewise) are filled into *out.  Returns

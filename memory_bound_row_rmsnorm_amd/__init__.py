@@ -18,6 +18,7 @@ __all__ = [
     "library_path", "version", "Plan", "RmsnormError",
     "plan_validate", "set_tuned", "clear_tuned", "tuned_count", "load_tuned",
     "rmsnorm_fwd_ex", "plan_query_ex", "row_layout", "Layout",
+    "rmsnorm_bwd_ex", "bwd_plan_query_ex", "bwd_layout", "BwdLayout",
 ]
 
 

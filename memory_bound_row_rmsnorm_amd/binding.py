@@ -35,6 +35,7 @@ EXPORTED = (
     "rmsnorm_fwd", "rmsnorm_fwd_with_plan", "rmsnorm_fwd_ex", "rmsnorm_plan_query", "rmsnorm_plan_query_ex",
     "rmsnorm_plan_resources",
     "rmsnorm_bwd", "rmsnorm_bwd_with_plan", "rmsnorm_bwd_plan_query", "rmsnorm_bwd_workspace_size",
+    "rmsnorm_bwd_ex", "rmsnorm_bwd_plan_query_ex", "rmsnorm_bwd_workspace_size_ex",
     "rmsnorm_plan_validate", "rmsnorm_plan_set_tuned", "rmsnorm_plan_clear_tuned", "rmsnorm_plan_tuned_count",
     "rmsnorm_status_string", "rmsnorm_last_error", "rmsnorm_version",
 )
@@ -89,6 +90,19 @@ class Layout(ctypes.Structure):
     ]
 
 
+class BwdLayout(ctypes.Structure):
+    """rmsnorm_bwd_layout_t: rows per batch (0 = one batch) and element strides of x, dy and dx."""
+    _fields_ = [
+        ("rows", ctypes.c_int64),
+        ("x_row_stride", ctypes.c_int64),
+        ("x_batch_stride", ctypes.c_int64),
+        ("dy_row_stride", ctypes.c_int64),
+        ("dy_batch_stride", ctypes.c_int64),
+        ("dx_row_stride", ctypes.c_int64),
+        ("dx_batch_stride", ctypes.c_int64),
+    ]
+
+
 def _load():
     if not os.path.exists(LIBRARY):
         raise ImportError(
@@ -121,6 +135,15 @@ def _load():
     lib.rmsnorm_bwd_plan_query.restype = i32
     lib.rmsnorm_bwd_workspace_size.argtypes = [i64, i64, i32, vp, vp, vp, ctypes.POINTER(ctypes.c_int64)]
     lib.rmsnorm_bwd_workspace_size.restype = i32
+    lib.rmsnorm_bwd_ex.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, f32, i32, ctypes.POINTER(BwdLayout),
+                                   ctypes.POINTER(Plan), vp, i64, vp]
+    lib.rmsnorm_bwd_ex.restype = i32
+    lib.rmsnorm_bwd_plan_query_ex.argtypes = [i64, i64, i32, vp, vp, vp, vp, ctypes.POINTER(BwdLayout),
+                                              ctypes.c_int32, ctypes.POINTER(Plan)]
+    lib.rmsnorm_bwd_plan_query_ex.restype = i32
+    lib.rmsnorm_bwd_workspace_size_ex.argtypes = [i64, i64, i32, vp, vp, vp, vp, ctypes.POINTER(BwdLayout),
+                                                  ctypes.POINTER(ctypes.c_int64)]
+    lib.rmsnorm_bwd_workspace_size_ex.restype = i32
     lib.rmsnorm_plan_validate.argtypes = [i64, i64, i32, vp, vp, vp, ctypes.POINTER(Plan), ctypes.c_int32,
                                           ctypes.POINTER(Plan)]
     lib.rmsnorm_plan_validate.restype = i32
@@ -427,3 +450,61 @@ def rmsnorm_bwd(x: torch.Tensor, w: torch.Tensor, dy: torch.Tensor, rstd: torch.
     ws = torch.empty((max(nbytes, 16) + 3) // 4, dtype=torch.float32, device=x.device)
     rmsnorm_bwd_out(x, w, dy, rstd, dx, dw, ws, offset, plan, stream)
     return dx, dw
+
+
+def bwd_layout(x: torch.Tensor, dy: torch.Tensor, dx: torch.Tensor):
+    """(M, N, BwdLayout) of the rows of x, dy and dx (same shape) over their last dimension."""
+    if dy.shape != x.shape or dx.shape != x.shape:
+        raise ValueError(f"dy {tuple(dy.shape)} and dx {tuple(dx.shape)} must have x's shape {tuple(x.shape)}")
+    M, N, rows, xrs, xbs = row_layout(x)
+    _, _, _, yrs, ybs = row_layout(dy)
+    _, _, _, ors, obs = row_layout(dx)
+    return M, N, BwdLayout(rows, xrs, xbs, yrs, ybs, ors, obs)
+
+
+def rmsnorm_bwd_ex(x: torch.Tensor, w: torch.Tensor, dy: torch.Tensor, rstd: torch.Tensor, offset: float = 0.0,
+                   out: torch.Tensor | None = None, plan: Plan | None = None, stream=None):
+    """Backward over the last dimension of x, dy (and dx) of any rank and strides (unit stride in
+    the last dimension), without copies: (dx shaped like x, or written into `out`; dw float32
+    [N]).  rstd: the forward's float32 rstd, contiguous, x.shape[:-1].  bf16, fp16 or fp32."""
+    if not (x.is_cuda and w.is_cuda and dy.is_cuda) or len({x.device, w.device, dy.device}) != 1:
+        raise ValueError("x, w and dy must be tensors on the same GPU")
+    if not (x.dtype == w.dtype == dy.dtype):
+        raise ValueError(f"x, w and dy must share a dtype, got {x.dtype}, {w.dtype}, {dy.dtype}")
+    code = _dtype_code(x.dtype)
+    if w.dim() != 1 or w.shape[0] != x.shape[-1] or not w.is_contiguous():
+        raise ValueError(f"w must be contiguous with shape [{x.shape[-1]}], got {tuple(w.shape)}")
+    if rstd.dtype != torch.float32 or not rstd.is_contiguous() or rstd.shape != x.shape[:-1] or \
+            rstd.device != x.device:
+        raise ValueError(f"rstd must be a contiguous float32 tensor of shape {tuple(x.shape[:-1])} on {x.device}")
+    dx = torch.empty_like(x) if out is None else out
+    if dx.dtype != x.dtype or dx.device != x.device:
+        raise ValueError("out must have x's dtype and device")
+    M, N, lay = bwd_layout(x, dy, dx)
+    dw = torch.empty((N,), dtype=torch.float32, device=x.device)
+    ptrs = (x.data_ptr() or None, w.data_ptr() or None, dy.data_ptr() or None, dx.data_ptr() or None)
+    if plan is None:
+        b = ctypes.c_int64()
+        _check(lib.rmsnorm_bwd_workspace_size_ex(M, N, code, *ptrs, ctypes.byref(lay), ctypes.byref(b)))
+        nbytes = b.value
+    else:
+        nbytes = plan.grid * N * 4 if M > 0 else 0
+    ws = torch.empty((max(nbytes, 16) + 3) // 4, dtype=torch.float32, device=x.device)
+    with torch.cuda.device(x.device):
+        _check(lib.rmsnorm_bwd_ex(x.data_ptr() or None, w.data_ptr() or None, dy.data_ptr() or None,
+                                  rstd.data_ptr() or None, dx.data_ptr() or None, dw.data_ptr(), M, N, offset, code,
+                                  ctypes.byref(lay), ctypes.byref(plan) if plan is not None else None,
+                                  ws.data_ptr(), ws.numel() * 4, _stream_handle(stream)))
+    return dx, dw
+
+
+def bwd_plan_query_ex(x: torch.Tensor, w: torch.Tensor, dy: torch.Tensor, out: torch.Tensor | None = None,
+                      cu_count: int = 0) -> Plan:
+    """The row-pass plan rmsnorm_bwd_ex uses for these tensors."""
+    dx = x if out is None else out
+    M, N, lay = bwd_layout(x, dy, dx)
+    p = Plan()
+    _check(lib.rmsnorm_bwd_plan_query_ex(M, N, _dtype_code(x.dtype), x.data_ptr() or None, w.data_ptr() or None,
+                                         dy.data_ptr() or None, dx.data_ptr() or None, ctypes.byref(lay), cu_count,
+                                         ctypes.byref(p)))
+    return p

@@ -574,8 +574,74 @@ int64_t bwd_wave_lds(const rmsnorm_plan_t* p, int64_t N) {
     return static_cast<int64_t>(p->block_threads / 64) * (64 / p->lanes_per_row) * N * 4;
 }
 
+// Row layout of x, dy and dx for the backward, normalised as the forward's:
+// `rows` rows per batch, strides in elements.
+struct BwdLayout {
+    int64_t rows;
+    int64_t x_rs, x_bs, dy_rs, dy_bs, dx_rs, dx_bs;
+    int64_t batches(int64_t M) const { return rows > 0 ? M / rows : 0; }
+    int64_t span(int64_t M, int64_t N, int64_t rs, int64_t bs) const {
+        if (M == 0) return 0;
+        return (batches(M) - 1) * bs + (rows - 1) * rs + N;
+    }
+    int64_t x_span(int64_t M, int64_t N) const { return span(M, N, x_rs, x_bs); }
+    int64_t dy_span(int64_t M, int64_t N) const { return span(M, N, dy_rs, dy_bs); }
+    int64_t dx_span(int64_t M, int64_t N) const { return span(M, N, dx_rs, dx_bs); }
+};
+
+BwdLayout contiguous_bwd_layout(int64_t M, int64_t N) {
+    return BwdLayout{M > 0 ? M : 1, N, M * N, N, M * N, N, M * N};
+}
+
+// Checks and normalises a backward layout.  dx's rows must not overlap one
+// another (batch-major or row-major interleaved, as the forward's y); x's
+// and dy's rows may (they are only read).  Several batches need M < 2^31
+// (the kernels split a row index with one 32-bit division).
+int normalise_bwd_layout(const rmsnorm_bwd_layout_t* L, int64_t M, int64_t N, BwdLayout* out) {
+    if (!L) {
+        *out = contiguous_bwd_layout(M, N);
+        return RMSNORM_OK;
+    }
+    if (L->rows < 0) return fail(RMSNORM_ERR_SHAPE, "layout rows must be >= 0");
+    const int64_t strides[6] = {L->x_row_stride, L->x_batch_stride, L->dy_row_stride,
+                                L->dy_batch_stride, L->dx_row_stride, L->dx_batch_stride};
+    for (int64_t v : strides)
+        if (v < 0) return fail(RMSNORM_ERR_SHAPE, "layout strides must be >= 0");
+    BwdLayout o;
+    o.rows = (L->rows == 0 || L->rows >= M) ? (M > 0 ? M : 1) : L->rows;
+    if (M > 0 && M % o.rows != 0) return fail(RMSNORM_ERR_SHAPE, "M must be a multiple of layout rows");
+    const int64_t B = M > 0 ? M / o.rows : 1;
+    o.x_rs = L->x_row_stride;
+    o.dy_rs = L->dy_row_stride;
+    o.dx_rs = L->dx_row_stride;
+    o.x_bs = B > 1 ? L->x_batch_stride : 0;
+    o.dy_bs = B > 1 ? L->dy_batch_stride : 0;
+    o.dx_bs = B > 1 ? L->dx_batch_stride : 0;
+    const int64_t lim = INT64_MAX / 4;
+    const int64_t r1 = o.rows > 1 ? o.rows : 1;
+    if (o.x_rs > lim / r1 || o.dy_rs > lim / r1 || o.dx_rs > lim / r1 || o.x_bs > lim / B || o.dy_bs > lim / B ||
+        o.dx_bs > lim / B)
+        return fail(RMSNORM_ERR_SHAPE, "layout spans overflow int64");
+    if (o.rows > 1 && o.dx_rs < N) return fail(RMSNORM_ERR_SHAPE, "dx rows overlap: dx_row_stride < N");
+    if (B > 1) {
+        const bool batch_major = o.dx_bs >= (o.rows - 1) * o.dx_rs + N;
+        const bool interleaved = o.dx_rs >= (B - 1) * o.dx_bs + N && o.dx_bs >= N;
+        if (!batch_major && !interleaved) return fail(RMSNORM_ERR_SHAPE, "dx rows overlap across batches");
+    }
+    if (o.x_span(M, N) > lim || o.dy_span(M, N) > lim || o.dx_span(M, N) > lim)
+        return fail(RMSNORM_ERR_SHAPE, "layout spans overflow int64");
+    if (B > 1 && o.x_bs == o.rows * o.x_rs && o.dy_bs == o.rows * o.dy_rs && o.dx_bs == o.rows * o.dx_rs) {
+        o.rows = M;     // batches that continue each other's row stride are one batch
+        o.x_bs = o.dy_bs = o.dx_bs = 0;
+    }
+    if (o.rows < M && M >= (int64_t{1} << 31))
+        return fail(RMSNORM_ERR_SHAPE, "a backward layout with several batches takes M < 2^31 rows");
+    *out = o;
+    return RMSNORM_OK;
+}
+
 int check_bwd_args(const void* x, const void* w, const void* dy, const float* rstd, const void* dx,
-                   const float* dw, int64_t M, int64_t N, float offset, int dtype) {
+                   const float* dw, int64_t M, int64_t N, float offset, int dtype, const BwdLayout& L) {
     int st = check_shape_dtype(M, N, dtype);
     if (st != RMSNORM_OK) return st;
     if (!dw) return fail(RMSNORM_ERR_NULL, "dw must be non-NULL");
@@ -583,22 +649,38 @@ int check_bwd_args(const void* x, const void* w, const void* dy, const float* rs
         return fail(RMSNORM_ERR_NULL, "x, w, dy, rstd and dx must be non-NULL");
     if (!std::isfinite(offset)) return fail(RMSNORM_ERR_SCALAR, "offset must be finite");
     const int64_t es = elem_size(dtype);
-    const int64_t xb = M * N * es, wb = N * es, rb = M * 4, db = N * 4;
+    const int64_t xb = L.x_span(M, N) * es, yb = L.dy_span(M, N) * es, ob = L.dx_span(M, N) * es;
+    const int64_t wb = N * es, rb = M * 4, db = N * 4;
     if (M > 0) {
-        if (ranges_overlap(dx, xb, x, xb)) return fail(RMSNORM_ERR_OVERLAP, "dx overlaps x");
-        if (dx != dy && ranges_overlap(dx, xb, dy, xb)) return fail(RMSNORM_ERR_OVERLAP, "dx partially overlaps dy");
-        if (ranges_overlap(dx, xb, w, wb) || ranges_overlap(dx, xb, rstd, rb) || ranges_overlap(dx, xb, dw, db))
+        const bool same_layout = L.dx_rs == L.dy_rs && L.dx_bs == L.dy_bs;
+        if (ranges_overlap(dx, ob, x, xb)) return fail(RMSNORM_ERR_OVERLAP, "dx overlaps x");
+        if (dx == dy ? !same_layout : ranges_overlap(dx, ob, dy, yb))
+            return fail(RMSNORM_ERR_OVERLAP, "dx overlaps dy (in place needs dx == dy with the same layout)");
+        if (ranges_overlap(dx, ob, w, wb) || ranges_overlap(dx, ob, rstd, rb) || ranges_overlap(dx, ob, dw, db))
             return fail(RMSNORM_ERR_OVERLAP, "dx overlaps w, rstd or dw");
-        if (ranges_overlap(dw, db, x, xb) || ranges_overlap(dw, db, dy, xb) || ranges_overlap(dw, db, w, wb) ||
+        if (ranges_overlap(dw, db, x, xb) || ranges_overlap(dw, db, dy, yb) || ranges_overlap(dw, db, w, wb) ||
             ranges_overlap(dw, db, rstd, rb))
             return fail(RMSNORM_ERR_OVERLAP, "dw overlaps an input");
     }
     return RMSNORM_OK;
 }
 
+// The 16-byte backward kernels: N a multiple of the vector, 16-byte aligned
+// x, w, dy and dx, strides that keep every row aligned, rows they hold.
+bool bwd_vector_ok(const void* x, const void* w, const void* dy, const void* dx, int dtype, const BwdLayout& L,
+                   int64_t M, int64_t N) {
+    const int64_t es = elem_size(dtype);
+    const int64_t epv = elems_per_vector(dtype);
+    const bool rows_ok = (L.x_rs * es) % 16 == 0 && (L.dy_rs * es) % 16 == 0 && (L.dx_rs * es) % 16 == 0;
+    const bool batches_ok = L.batches(M) <= 1 ||
+                            ((L.x_bs * es) % 16 == 0 && (L.dy_bs * es) % 16 == 0 && (L.dx_bs * es) % 16 == 0);
+    return N % epv == 0 && N / epv <= kBwdMaxVectors && aligned16(x) && aligned16(w) && aligned16(dy) &&
+           aligned16(dx) && rows_ok && batches_ok;
+}
+
 int check_workspace(const void* ws, int64_t ws_bytes, int64_t need, const void* x, const void* w,
                     const void* dy, const float* rstd, const void* dx, const float* dw, int64_t M, int64_t N,
-                    int dtype) {
+                    int dtype, const BwdLayout& L) {
     if (need == 0) return RMSNORM_OK;
     if (!ws) return fail(RMSNORM_ERR_NULL, "workspace must be non-NULL");
     if (ws_bytes < need)
@@ -606,16 +688,15 @@ int check_workspace(const void* ws, int64_t ws_bytes, int64_t need, const void* 
                                            std::to_string(need));
     if ((reinterpret_cast<uintptr_t>(ws) & 15u) != 0) return fail(RMSNORM_ERR_PLAN, "workspace must be 16-byte aligned");
     const int64_t es = elem_size(dtype);
-    const int64_t xb = M * N * es;
-    if (ranges_overlap(ws, need, x, xb) || ranges_overlap(ws, need, dy, xb) || ranges_overlap(ws, need, dx, xb) ||
+    if (ranges_overlap(ws, need, x, L.x_span(M, N) * es) || ranges_overlap(ws, need, dy, L.dy_span(M, N) * es) ||
+        ranges_overlap(ws, need, dx, L.dx_span(M, N) * es) ||
         ranges_overlap(ws, need, w, N * es) || ranges_overlap(ws, need, rstd, M * 4) ||
         ranges_overlap(ws, need, dw, N * 4))
         return fail(RMSNORM_ERR_OVERLAP, "workspace overlaps an argument");
     return RMSNORM_OK;
 }
 
-int finish_bwd_plan(rmsnorm_plan_t* p, int64_t M, int64_t N, int dtype, const void* x, const void* w,
-                    const void* dy, const void* dx, const KernelEntry** kernel) {
+int finish_bwd_plan(rmsnorm_plan_t* p, int64_t M, int64_t N, int dtype, bool vec, const KernelEntry** kernel) {
     if (p->block_threads < 64 || p->block_threads > 1024 || p->block_threads % 64 != 0)
         return fail(RMSNORM_ERR_PLAN, "block_threads must be a multiple of 64 in [64, 1024]");
     if (p->grid < 1 || p->grid > 0x7FFFFFFF) return fail(RMSNORM_ERR_PLAN, "grid must be in [1, 2^31)");
@@ -633,9 +714,9 @@ int finish_bwd_plan(rmsnorm_plan_t* p, int64_t M, int64_t N, int dtype, const vo
         k = pf ? nullptr : find_bwd_kernel(RMSNORM_VARIANT_GENERIC, dtype, 0, 0, 1, false);
     } else if (p->variant == RMSNORM_VARIANT_WAVE || p->variant == RMSNORM_VARIANT_BLOCK) {
         const int epv = elems_per_vector(dtype);
-        if (N % epv != 0) return fail(RMSNORM_ERR_PLAN, "16-byte kernels need N to be a multiple of vec_elems");
-        if (!aligned16(x) || !aligned16(w) || !aligned16(dy) || !aligned16(dx))
-            return fail(RMSNORM_ERR_PLAN, "16-byte kernels need 16-byte aligned x, w, dy and dx");
+        if (!vec)
+            return fail(RMSNORM_ERR_PLAN, "16-byte kernels need N a multiple of vec_elems, at most 2048 vectors, "
+                                          "16-byte aligned x, w, dy and dx, and strides that keep rows aligned");
         p->vec_elems = epv;
         if (p->variant == RMSNORM_VARIANT_WAVE) {
             k = find_bwd_kernel(RMSNORM_VARIANT_WAVE, dtype, p->lanes_per_row, p->vectors_per_lane, p->row_slots, pf);
@@ -674,13 +755,10 @@ int finish_bwd_plan(rmsnorm_plan_t* p, int64_t M, int64_t N, int dtype, const vo
 // workgroup per unit: its barriers then stall the whole unit, which the early
 // loads cover; with two or more workgroups per unit they cover each other,
 // and the extra registers of the prefetching form cost more than they hide.
-int choose_bwd_plan(int64_t M, int64_t N, const void* x, const void* w, const void* dy, const void* dx,
-                    int dtype, rmsnorm_plan_t* p) {
+int choose_bwd_plan(int64_t M, int64_t N, bool vec_ok, int dtype, rmsnorm_plan_t* p) {
     std::memset(p, 0, sizeof(*p));
     p->xcd_group = 1;
     const int64_t epv = elems_per_vector(dtype);
-    const bool vec_ok = (N % epv == 0) && aligned16(x) && aligned16(w) && aligned16(dy) && aligned16(dx) &&
-                        N / epv <= kBwdMaxVectors;
     if (!vec_ok) {
         p->variant = RMSNORM_VARIANT_GENERIC;
         p->block_threads = N >= 1024 ? 256 : (N >= 256 ? 128 : 64);
@@ -733,8 +811,8 @@ int choose_bwd_plan(int64_t M, int64_t N, const void* x, const void* w, const vo
 }
 
 int launch_bwd(const KernelEntry* k, const rmsnorm_plan_t* p, const void* x, const void* w, const void* dy,
-               const float* rstd, void* dx, float* dw, int64_t M, int64_t N, float offset, void* workspace,
-               void* stream) {
+               const float* rstd, void* dx, float* dw, int64_t M, int64_t N, float offset, const BwdLayout& L,
+               void* workspace, void* stream) {
     const hipStream_t s = static_cast<hipStream_t>(stream);
     int64_t G = 0;
     if (M > 0) {
@@ -751,6 +829,13 @@ int launch_bwd(const KernelEntry* k, const rmsnorm_plan_t* p, const void* x, con
         a.offset = offset;
         a.grid = p->grid;
         a.threads = p->block_threads;
+        a.rows = L.rows;
+        a.x_rs = L.x_rs;
+        a.dy_rs = L.dy_rs;
+        a.dx_rs = L.dx_rs;
+        a.x_bs = L.x_bs;
+        a.dy_bs = L.dy_bs;
+        a.dx_bs = L.dx_bs;
         void* args[] = {&a};
         const size_t lds = p->variant == RMSNORM_VARIANT_WAVE ? static_cast<size_t>(bwd_wave_lds(p, N)) : 0;
         hipError_t e = hipLaunchKernel(k->func, dim3(static_cast<unsigned>(p->grid)),
@@ -774,18 +859,46 @@ int launch_bwd(const KernelEntry* k, const rmsnorm_plan_t* p, const void* x, con
     return RMSNORM_OK;
 }
 
+// Every backward entry point: checks, plan (the caller's or the rule),
+// workspace check, launch of the row pass and the column pass.
 int bwd_common(const void* x, const void* w, const void* dy, const float* rstd, void* dx, float* dw, int64_t M,
-               int64_t N, float offset, int dtype, rmsnorm_plan_t* p, void* ws, int64_t ws_bytes, void* stream) {
-    const KernelEntry* k = nullptr;
-    int st = finish_bwd_plan(p, M, N, dtype, x, w, dy, dx, &k);
+               int64_t N, float offset, int dtype, const rmsnorm_bwd_layout_t* layout, const rmsnorm_plan_t* plan,
+               void* ws, int64_t ws_bytes, void* stream) {
+    int st = check_shape_dtype(M, N, dtype);
     if (st != RMSNORM_OK) return st;
-    const int64_t need = M > 0 ? p->grid * N * 4 : 0;
-    st = check_workspace(ws, ws_bytes, need, x, w, dy, rstd, dx, dw, M, N, dtype);
+    BwdLayout L;
+    st = normalise_bwd_layout(layout, M, N, &L);
+    if (st != RMSNORM_OK) return st;
+    st = check_bwd_args(x, w, dy, rstd, dx, dw, M, N, offset, dtype, L);
+    if (st != RMSNORM_OK) return st;
+    const bool vec = bwd_vector_ok(x, w, dy, dx, dtype, L, M, N);
+    rmsnorm_plan_t p;
+    if (plan) p = *plan;
+    else choose_bwd_plan(M, N, vec, dtype, &p);
+    const KernelEntry* k = nullptr;
+    st = finish_bwd_plan(&p, M, N, dtype, vec, &k);
+    if (st != RMSNORM_OK) return st;
+    const int64_t need = M > 0 ? p.grid * N * 4 : 0;
+    st = check_workspace(ws, ws_bytes, need, x, w, dy, rstd, dx, dw, M, N, dtype, L);
     if (st != RMSNORM_OK) return st;
     int cu = 0;
     st = device_info(&cu);
     if (st != RMSNORM_OK) return st;
-    return launch_bwd(k, p, x, w, dy, rstd, dx, dw, M, N, offset, ws, stream);
+    return launch_bwd(k, &p, x, w, dy, rstd, dx, dw, M, N, offset, L, ws, stream);
+}
+
+// Plan and workspace of a backward call, host only (no pointers needed
+// beyond their alignment).
+int bwd_plan_for(int64_t M, int64_t N, int dtype, const void* x, const void* w, const void* dy, const void* dx,
+                 const rmsnorm_bwd_layout_t* layout, rmsnorm_plan_t* p, const KernelEntry** k) {
+    int st = check_shape_dtype(M, N, dtype);
+    if (st != RMSNORM_OK) return st;
+    BwdLayout L;
+    st = normalise_bwd_layout(layout, M, N, &L);
+    if (st != RMSNORM_OK) return st;
+    const bool vec = bwd_vector_ok(x, w, dy, dx, dtype, L, M, N);
+    choose_bwd_plan(M, N, vec, dtype, p);
+    return finish_bwd_plan(p, M, N, dtype, vec, k);
 }
 
 // ---------------------------------------------------------------------------
@@ -943,14 +1056,18 @@ int rmsnorm_plan_resources(const rmsnorm_plan_t* plan, int dtype, int32_t* vgprs
 
 int rmsnorm_bwd_plan_query(int64_t M, int64_t N, int dtype, const void* x, const void* dy, const void* dx,
                            int32_t cu_count, rmsnorm_plan_t* out) {
+    // w is not an argument here: it is taken as aligned like dx
+    return rmsnorm_bwd_plan_query_ex(M, N, dtype, x, dx, dy, dx, nullptr, cu_count, out);
+}
+
+int rmsnorm_bwd_plan_query_ex(int64_t M, int64_t N, int dtype, const void* x, const void* w, const void* dy,
+                              const void* dx, const rmsnorm_bwd_layout_t* layout, int32_t cu_count,
+                              rmsnorm_plan_t* out) {
     g_last_error.clear();
     if (!out) return fail(RMSNORM_ERR_NULL, "out must be non-NULL");
-    int st = check_shape_dtype(M, N, dtype);
-    if (st != RMSNORM_OK) return st;
     rmsnorm_plan_t p;
     const KernelEntry* k = nullptr;
-    choose_bwd_plan(M, N, x, dx, dy, dx, dtype, &p);
-    st = finish_bwd_plan(&p, M, N, dtype, x, dx, dy, dx, &k);
+    int st = bwd_plan_for(M, N, dtype, x, w, dy, dx, layout, &p, &k);
     if (st == RMSNORM_OK) st = resident_grid(&p, k, cu_count, &p.resident_grid);
     if (st != RMSNORM_OK) return st;
     *out = p;
@@ -959,12 +1076,17 @@ int rmsnorm_bwd_plan_query(int64_t M, int64_t N, int dtype, const void* x, const
 
 int rmsnorm_bwd_workspace_size(int64_t M, int64_t N, int dtype, const void* x, const void* dy, const void* dx,
                                int64_t* bytes) {
+    return rmsnorm_bwd_workspace_size_ex(M, N, dtype, x, dx, dy, dx, nullptr, bytes);
+}
+
+int rmsnorm_bwd_workspace_size_ex(int64_t M, int64_t N, int dtype, const void* x, const void* w, const void* dy,
+                                  const void* dx, const rmsnorm_bwd_layout_t* layout, int64_t* bytes) {
     g_last_error.clear();
     if (!bytes) return fail(RMSNORM_ERR_NULL, "bytes must be non-NULL");
-    int st = check_shape_dtype(M, N, dtype);
-    if (st != RMSNORM_OK) return st;
     rmsnorm_plan_t p;
-    choose_bwd_plan(M, N, x, dx, dy, dx, dtype, &p);
+    const KernelEntry* k = nullptr;
+    const int st = bwd_plan_for(M, N, dtype, x, w, dy, dx, layout, &p, &k);
+    if (st != RMSNORM_OK) return st;
     *bytes = M > 0 ? p.grid * N * 4 : 0;
     return RMSNORM_OK;
 }
@@ -972,22 +1094,28 @@ int rmsnorm_bwd_workspace_size(int64_t M, int64_t N, int dtype, const void* x, c
 int rmsnorm_bwd(const void* x, const void* w, const void* dy, const float* rstd, void* dx, float* dw, int64_t M,
                 int64_t N, float offset, int dtype, void* workspace, int64_t workspace_bytes, void* stream) {
     g_last_error.clear();
-    int st = check_bwd_args(x, w, dy, rstd, dx, dw, M, N, offset, dtype);
-    if (st != RMSNORM_OK) return st;
-    rmsnorm_plan_t p;
-    choose_bwd_plan(M, N, x, w, dy, dx, dtype, &p);
-    return bwd_common(x, w, dy, rstd, dx, dw, M, N, offset, dtype, &p, workspace, workspace_bytes, stream);
+    return bwd_common(x, w, dy, rstd, dx, dw, M, N, offset, dtype, nullptr, nullptr, workspace, workspace_bytes,
+                      stream);
 }
 
 int rmsnorm_bwd_with_plan(const void* x, const void* w, const void* dy, const float* rstd, void* dx, float* dw,
                           int64_t M, int64_t N, float offset, int dtype, const rmsnorm_plan_t* plan,
                           void* workspace, int64_t workspace_bytes, void* stream) {
     g_last_error.clear();
-    int st = check_bwd_args(x, w, dy, rstd, dx, dw, M, N, offset, dtype);
-    if (st != RMSNORM_OK) return st;
-    if (!plan) return fail(RMSNORM_ERR_NULL, "plan must be non-NULL");
-    rmsnorm_plan_t p = *plan;
-    return bwd_common(x, w, dy, rstd, dx, dw, M, N, offset, dtype, &p, workspace, workspace_bytes, stream);
+    if (!plan) {
+        const int st = check_shape_dtype(M, N, dtype);
+        return st != RMSNORM_OK ? st : fail(RMSNORM_ERR_NULL, "plan must be non-NULL");
+    }
+    return bwd_common(x, w, dy, rstd, dx, dw, M, N, offset, dtype, nullptr, plan, workspace, workspace_bytes,
+                      stream);
+}
+
+int rmsnorm_bwd_ex(const void* x, const void* w, const void* dy, const float* rstd, void* dx, float* dw, int64_t M,
+                   int64_t N, float offset, int dtype, const rmsnorm_bwd_layout_t* layout,
+                   const rmsnorm_plan_t* plan, void* workspace, int64_t workspace_bytes, void* stream) {
+    g_last_error.clear();
+    return bwd_common(x, w, dy, rstd, dx, dw, M, N, offset, dtype, layout, plan, workspace, workspace_bytes,
+                      stream);
 }
 
 int rmsnorm_plan_set_tuned(int64_t M, int64_t N, int dtype, const rmsnorm_plan_t* plan) {

@@ -71,6 +71,26 @@ __device__ __forceinline__ void widen_g(float (&g)[D::EPV], const u32x4 q, float
     for (int k = 0; k < D::EPV; ++k) g[k] = offset + g[k];
 }
 
+// Element offsets of row m of x, dy and dx (see BwdArgs): one 32-bit
+// division when the rows form several batches, none otherwise.
+struct RowOff {
+    int64_t x, dy, dx;
+};
+
+__device__ __forceinline__ RowOff row_offsets(const BwdArgs& a, int64_t m) {
+    if (a.rows >= a.M) return {m * a.x_rs, m * a.dy_rs, m * a.dx_rs};
+    const uint32_t b = static_cast<uint32_t>(m) / static_cast<uint32_t>(a.rows);
+    const int64_t s = static_cast<int64_t>(static_cast<uint32_t>(m) - b * static_cast<uint32_t>(a.rows));
+    const int64_t bb = b;
+    return {bb * a.x_bs + s * a.x_rs, bb * a.dy_bs + s * a.dy_rs, bb * a.dx_bs + s * a.dx_rs};
+}
+
+// 16-byte vector at element offset off (a multiple of EPV in the vector kernels)
+template <class D, class T>
+__device__ __forceinline__ T* vec_at(T* base, int64_t off) {
+    return base + static_cast<uint64_t>(off) / D::EPV;
+}
+
 }  // namespace
 
 // ---------------------------------------------------------------------------
@@ -114,8 +134,9 @@ __global__ __launch_bounds__(1024) void rmsnorm_bwd_wave(BwdArgs a) {
         for (int s = 0; s < SLOTS; ++s) {
             const int64_t row = gg * ROWS + seg + s * SEG;
             const bool live = row < M;
-            const u32x4* xr = x + row * nvec;
-            const u32x4* dr = dy + row * nvec;
+            const RowOff o = row_offsets(a, live ? row : 0);
+            const u32x4* xr = vec_at<D>(x, o.x);
+            const u32x4* dr = vec_at<D>(dy, o.dy);
 #pragma unroll
             for (int v = 0; v < VPL; ++v) {
                 const int c = v * LANES + li;
@@ -147,7 +168,7 @@ __global__ __launch_bounds__(1024) void rmsnorm_bwd_wave(BwdArgs a) {
             const float cm = segment_allreduce<LANES>(t) * a.inv_n;
             const float r2c = r[s] * r[s] * cm;
             const int64_t row = gi * ROWS + seg + s * SEG;
-            u32x4* out = dx + row * nvec;
+            u32x4* out = vec_at<D>(dx, row_offsets(a, row < M ? row : 0).dx);
 #pragma unroll
             for (int v = 0; v < VPL; ++v) {
                 const int c = v * LANES + li;
@@ -224,8 +245,9 @@ __global__ __launch_bounds__(1024) void rmsnorm_bwd_block(BwdArgs a) {
     }
 
     auto load_row = [&](u32x4 (&xd)[VPT], u32x4 (&dd)[VPT], float& r, int64_t rr) {
-        const u32x4* xr = x + rr * nvec;
-        const u32x4* dr = dy + rr * nvec;
+        const RowOff o = row_offsets(a, rr);
+        const u32x4* xr = vec_at<D>(x, o.x);
+        const u32x4* dr = vec_at<D>(dy, o.dy);
 #pragma unroll
         for (int v = 0; v < VPT; ++v) {
             const int c = v * nt + tid;
@@ -262,7 +284,7 @@ __global__ __launch_bounds__(1024) void rmsnorm_bwd_block(BwdArgs a) {
         float tot = part[par][0];
         for (int i = 1; i < nw; ++i) tot += part[par][i];
         const float r2c = r * r * (tot * a.inv_n);
-        u32x4* out = dx + row * nvec;
+        u32x4* out = vec_at<D>(dx, row_offsets(a, row).dx);
 #pragma unroll
         for (int v = 0; v < VPT; ++v) {
             const int c = v * nt + tid;
@@ -322,9 +344,10 @@ __global__ __launch_bounds__(1024) void rmsnorm_bwd_generic(BwdArgs a) {
 
     int par = 0;
     for (int64_t row = blockIdx.x; row < M; row += a.grid) {
-        const E* xr = x + row * N;
-        const E* dr = dy + row * N;
-        E* out = dx + row * N;
+        const RowOff o = row_offsets(a, row);
+        const E* xr = x + o.x;
+        const E* dr = dy + o.dy;
+        E* out = dx + o.dx;
         const float r = a.rstd[row];
         float t = 0.0f;
         for (int64_t j = tid; j < N; j += nt)

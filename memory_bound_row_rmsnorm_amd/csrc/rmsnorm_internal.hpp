@@ -44,8 +44,11 @@ struct KernelArgs {
 };
 
 // Arguments of every backward row-pass kernel.
-//   x, w, dy : 16-bit element buffers (device); rstd : fp32 [M] (device)
-//   dx : 16-bit [M, N] output; partials : fp32 [grid, N] workspace rows
+//   x, w, dy : element buffers of the dtype (device); rstd : fp32 [M] (device)
+//   dx : output rows of the dtype; partials : fp32 [grid, N] workspace rows
+//   Row m (0 <= m < M) is row m % rows of batch m / rows; it starts at
+//   element (m / rows) * x_bs + (m % rows) * x_rs of x, likewise for dy and
+//   dx, and its rstd is rstd[m].  One batch: rows = M (no division).
 struct BwdArgs {
     const void* x;
     const void* w;
@@ -59,6 +62,9 @@ struct BwdArgs {
     int32_t threads;
     float inv_n;
     float offset;
+    int64_t rows;       // rows per batch; M < 2^31 when rows < M
+    int64_t x_rs, dy_rs, dx_rs;   // row strides, elements
+    int64_t x_bs, dy_bs, dx_bs;   // batch strides, elements
 };
 
 struct KernelEntry {

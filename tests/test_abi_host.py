@@ -506,3 +506,58 @@ def test_widest_instances_refuse_ragged_widths():
     p = bnd.plan_query(4, 24576, "fp32", cu_count=256)
     ragged = bnd.plan_validate(4, 24573, "fp32", p, cu_count=256)
     assert ragged is None                                   # an explicit plan is refused, not run wrong
+
+
+# ---------------------------------------------------------------------------
+# Backward with layouts (host checks and plans; no kernel runs)
+# ---------------------------------------------------------------------------
+def bwd_ex_status(M, N, lay, dtype=BF16, x=A, dy=None, dx=None, ws_bytes=1 << 30):
+    dy = dy if dy is not None else A + 0x40000000
+    dx = dx if dx is not None else A + 0x80000000
+    return lib.rmsnorm_bwd_ex(x, A + 0xC0000000, dy, A + 0xD0000000, dx, A + 0xE0000000, M, N, 0.0, dtype,
+                              ctypes.byref(lay) if lay is not None else None, None, A + 0xF0000000, ws_bytes, None)
+
+
+@pytest.mark.parametrize("lay,M,N,status", [
+    (bnd.BwdLayout(7, 64, 0, 64, 0, 64, 0), 64, 64, SHAPE),              # M not a multiple of rows
+    (bnd.BwdLayout(0, 64, 0, 64, 0, 32, 0), 64, 64, SHAPE),              # dx rows overlap
+    (bnd.BwdLayout(4, 64, 256, 64, 256, 64, 128), 64, 64, SHAPE),        # dx batches overlap
+    (bnd.BwdLayout(0, -1, 0, 64, 0, 64, 0), 64, 64, SHAPE),              # negative stride
+    (bnd.BwdLayout(2, 64, 256, 64, 256, 64, 256), 1 << 31, 64, SHAPE),   # several batches and M >= 2^31
+])
+def test_bwd_ex_layout_errors(lay, M, N, status):
+    assert bwd_ex_status(M, N, lay) == status, lib.rmsnorm_last_error().decode()
+    assert lib.rmsnorm_last_error().decode() != ""
+
+
+def test_bwd_ex_in_place_needs_the_same_layout():
+    lay = bnd.BwdLayout(0, 512, 0, 1024, 0, 512, 0)
+    assert bwd_ex_status(64, 512, lay, dy=A + 0x40000000, dx=A + 0x40000000) == OVERLAP
+    lay = bnd.BwdLayout(0, 512, 0, 1024, 0, 1024, 0)
+    st = bwd_ex_status(64, 512, lay, dy=A + 0x40000000, dx=A + 0x40000000)
+    assert st == HIP, lib.rmsnorm_last_error().decode()          # accepted: fails only at the device
+    assert bwd_ex_status(64, 512, bnd.BwdLayout(0, 512, 0, 512, 0, 512, 0), dx=A + 16) == OVERLAP   # dx over x
+
+
+def bwd_plan_ex(M, N, lay, dtype=BF16, x=A, w=A, dy=A, dx=A):
+    p = bnd.Plan()
+    st = lib.rmsnorm_bwd_plan_query_ex(M, N, dtype, x, w, dy, dx, ctypes.byref(lay) if lay is not None else None,
+                                       256, ctypes.byref(p))
+    assert st == OK, lib.rmsnorm_last_error().decode()
+    return p
+
+
+def test_bwd_ex_plans():
+    contiguous = bwd_plan_ex(4096, 512, None)
+    assert bwd_plan_ex(4096, 512, bnd.BwdLayout(0, 512, 0, 512, 0, 512, 0)).as_dict() == contiguous.as_dict()
+    # a strided view that keeps rows aligned still takes the vector kernels
+    p = bwd_plan_ex(4096, 512, bnd.BwdLayout(32, 1536, 32 * 1536, 512, 32 * 512, 2048, 32 * 2048))
+    assert p.variant == bnd.VARIANT_WAVE and p.as_dict() == contiguous.as_dict()
+    # a row stride that breaks 16-byte alignment takes the generic kernel
+    assert bwd_plan_ex(4096, 512, bnd.BwdLayout(0, 516, 0, 512, 0, 512, 0)).variant == bnd.VARIANT_GENERIC
+    assert bwd_plan_ex(4096, 512, bnd.BwdLayout(32, 512, 32 * 512 + 4, 512, 32 * 512, 512, 32 * 512)).variant == \
+        bnd.VARIANT_GENERIC
+    b = ctypes.c_int64()
+    lay = bnd.BwdLayout(32, 1536, 32 * 1536, 512, 32 * 512, 2048, 32 * 2048)
+    assert lib.rmsnorm_bwd_workspace_size_ex(4096, 512, BF16, A, A, A, A, ctypes.byref(lay), ctypes.byref(b)) == OK
+    assert b.value == p.grid * 512 * 4

@@ -243,3 +243,119 @@ def test_bwd_fp32_every_kernel(bnd, M, N):
             parity.compare_bwd(dx, dw, dxe, dxs, dwe, dws, "fp32", M, grid, f"bwd fp32 {M}x{N} {p.as_dict()}")
             ran += 1
     assert ran >= 12, ran
+
+
+# ---------------------------------------------------------------------------
+# Layouts: rows of x, dy and dx placed by strides (rmsnorm_bwd_ex).  Every case
+# is compared with the oracle on the logical rows, and dx is written into a
+# view of a sentinel-filled buffer whose other elements must not change.
+# ---------------------------------------------------------------------------
+SENT = {torch.bfloat16: (torch.int16, 0x7FC1), torch.float16: (torch.int16, 0x7E01),
+        torch.float32: (torch.int32, 0x7FC00001)}
+
+
+def _draw(shape, dtype, seed, sigma=1.0):
+    g = torch.Generator().manual_seed(seed)
+    return (sigma * torch.randn(*shape, generator=g)).to(dtype)
+
+
+def _filled(numel, dtype):
+    iv, val = SENT[dtype]
+    t = torch.empty(numel, dtype=dtype, device=DEV)
+    t.view(iv).fill_(val)
+    return t
+
+
+def _check_layout_bwd(bnd, x, w, dy, dx, dx_base, offset, what):
+    dt = {torch.bfloat16: "bf16", torch.float16: "fp16", torch.float32: "fp32"}[x.dtype]
+    N = x.shape[-1]
+    xc = x.cpu().reshape(-1, N)
+    wc = w.cpu()
+    dyc = dy.cpu().reshape(-1, N)
+    M = xc.shape[0]
+    if dt == "fp32":
+        _, r64 = parity.oracle_fp32(xc, wc, 1e-6, offset)
+    else:
+        _, r64 = parity.oracle_for(xc, wc, 1e-6, offset, dt)
+    r32 = r64.astype(np.float32)
+    rg = torch.from_numpy(r32).to(DEV).reshape(x.shape[:-1])
+    iv, val = SENT[x.dtype]
+    before = dx_base.cpu().view(iv).clone()
+    p = bnd.bwd_plan_query_ex(x, w, dy, out=dx)
+    announce("bwd layout", what, p.as_dict())
+    out, dw = bnd.rmsnorm_bwd_ex(x, w, dy, rg, offset, out=dx)
+    torch.cuda.synchronize()
+    _, dwe, dxe, dxs, dws = parity.oracle_bwd_for(xc, wc, dyc, r32, offset, dt)
+    parity.compare_bwd(out.cpu().reshape(M, N), dw, dxe, dxs, dwe, dws, dt, M, p.grid, what)
+    # nothing outside dx's view changed
+    idx = torch.arange(dx_base.numel()).as_strided(dx.shape, dx.stride(), dx.storage_offset())
+    mask = torch.zeros(dx_base.numel(), dtype=torch.bool)
+    mask[idx.reshape(-1)] = True
+    after = dx_base.cpu().view(iv)
+    assert bool((after[~mask] == before[~mask]).all()), what
+    return p
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float16, torch.float32])
+def test_bwd_strided_rows(bnd, dtype):
+    M, N = 300, 512
+    xb = _draw((M, 768), dtype, 201).to(DEV)
+    x = xb[:, 128:640]                                   # row stride 768
+    w = (1.0 + 0.1 * _draw((N,), torch.float32, 202)).to(dtype).to(DEV)
+    dyb = _draw((M, 1024), dtype, 203).to(DEV)
+    dy = dyb[:, :N]                                      # row stride 1024
+    dx_base = _filled(M * 640 + 64, dtype)
+    dx = dx_base.as_strided((M, N), (640, 1), 32)        # row stride 640, 32 elements in
+    p = _check_layout_bwd(bnd, x, w, dy, dx, dx_base, 1.0, f"strided 2-D {dtype}")
+    assert p.variant == bnd.VARIANT_WAVE
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+def test_bwd_qk_norm_heads(bnd, dtype):
+    """Rows of head_dim inside a fused QKV projection output [B, S, 3, H, D]: q = [:, :, 0] has rows
+    D apart within a token and 3*H*D apart between tokens (a 4-D view whose leading dimensions
+    collapse into one batch stride)."""
+    B, S, H, D = 2, 33, 8, 128
+    qkv = _draw((B, S, 3, H, D), dtype, 211, 2.0).to(DEV)
+    x = qkv[:, :, 0]
+    dqkv = _draw((B, S, 3, H, D), dtype, 212).to(DEV)
+    dy = dqkv[:, :, 0]
+    w = (1.0 + 0.1 * _draw((D,), torch.float32, 213)).to(dtype).to(DEV)
+    dx_base = _filled(B * S * 3 * H * D, dtype)
+    dx = dx_base.view(B, S, 3, H, D)[:, :, 1]             # written into the k slot of another buffer
+    _check_layout_bwd(bnd, x, w, dy, dx, dx_base, 0.0, f"qk-norm {dtype}")
+
+
+@pytest.mark.parametrize("N", [512, 3000, 1002])
+def test_bwd_batched_slices_and_interleaved(bnd, N):
+    dtype = torch.bfloat16
+    B, S = 4, 70
+    big = _draw((B, S + 9, N), dtype, 221 + N).to(DEV)
+    x = big[:, 3:3 + S]                                  # a sequence slice: batch stride (S + 9) N
+    dy = _draw((S, B, N), dtype, 222 + N).to(DEV).transpose(0, 1)     # interleaved [S, B, N] view
+    w = (0.1 * _draw((N,), torch.float32, 223 + N)).to(dtype).to(DEV)
+    dx_base = _filled(B * (S + 2) * N + 8, dtype)
+    dx = dx_base.as_strided((B, S, N), ((S + 2) * N, N, 1), 8)
+    p = _check_layout_bwd(bnd, x, w, dy, dx, dx_base, 1.0, f"batched N={N}")
+    if N % 8 == 0:
+        assert p.variant != bnd.VARIANT_GENERIC
+
+
+def test_bwd_layout_in_place(bnd):
+    dtype = torch.float16
+    B, S, N = 3, 50, 256
+    x = _draw((B, S, N), dtype, 231, 30.0).to(DEV)
+    buf = _draw((B, S + 5, N), dtype, 232).to(DEV)
+    dy = buf[:, 2:2 + S]
+    dy_copy = dy.clone()
+    w = (1.0 + 0.1 * _draw((N,), torch.float32, 233)).to(dtype).to(DEV)
+    xc = x.cpu().reshape(-1, N)
+    _, r64 = parity.oracle_for(xc, w.cpu(), 1e-6, 0.0, "fp16")
+    r32 = r64.astype(np.float32)
+    rg = torch.from_numpy(r32).to(DEV).reshape(B, S)
+    announce("bwd layout in place")
+    out, dw = bnd.rmsnorm_bwd_ex(x, w, dy, rg, 0.0, out=dy)     # dx over dy, same layout
+    torch.cuda.synchronize()
+    _, dwe, dxe, dxs, dws = parity.oracle_bwd_for(xc, w.cpu(), dy_copy.cpu().reshape(-1, N), r32, 0.0, "fp16")
+    p = bnd.bwd_plan_query_ex(x, w, dy, out=dy)
+    parity.compare_bwd(out.cpu().reshape(-1, N), dw, dxe, dxs, dwe, dws, "fp16", B * S, p.grid, "in place layout")
