@@ -325,12 +325,14 @@ int finish_plan(rmsnorm_plan_t* p, int64_t M, int64_t N, int dtype, Access acc, 
                                           "16-byte aligned w, and rows that are not 16-byte aligned");
         const int epv = elems_per_vector(dtype);
         p->vec_elems = epv;
-        p->lanes_per_row = 64;
         if (p->prefetch != 0 && p->prefetch != 1) return fail(RMSNORM_ERR_PLAN, "prefetch must be 0 or 1");
-        k = find_kernel(RMSNORM_VARIANT_SHIFTED_WAVE, dtype, 64, p->vectors_per_lane, p->row_slots, p->prefetch != 0);
-        if (k && 64LL * p->vectors_per_lane * epv < N + epv - 1)
+        if (p->lanes_per_row != 16 && p->lanes_per_row != 32 && p->lanes_per_row != 64)
+            return fail(RMSNORM_ERR_PLAN, "shifted wave plans take 16, 32 or 64 lanes per row");
+        k = find_kernel(RMSNORM_VARIANT_SHIFTED_WAVE, dtype, p->lanes_per_row, p->vectors_per_lane, p->row_slots,
+                        p->prefetch != 0);
+        if (k && static_cast<int64_t>(p->lanes_per_row) * p->vectors_per_lane * epv < N + epv - 1)
             return fail(RMSNORM_ERR_PLAN, "shifted wave plan does not cover N");
-        p->rows_per_trip = static_cast<int64_t>(p->block_threads / 64) * p->row_slots;
+        p->rows_per_trip = static_cast<int64_t>(p->block_threads / 64) * (64 / p->lanes_per_row) * p->row_slots;
     } else {
         return fail(RMSNORM_ERR_PLAN, "unknown variant");
     }
@@ -348,7 +350,7 @@ constexpr int kWaveSlots[] = {8, 4, 2, 1};
 constexpr int64_t kMaxVectors = 1024LL * 6;       // widest row the 16-byte kernels hold, in vectors
 constexpr int64_t kMaxShiftedChunks = 1024LL * 4;  // widest row the shifted kernel holds, in chunks
 constexpr int64_t kMaxShiftedWaveChunks = 64 * 2;  // widest row the shifted wave kernel holds, in chunks
-constexpr int kShiftedWaveSlots = 4;               // rows per wave per trip of the shifted wave plans
+constexpr int kShiftedWaveSlots = 4;               // slots per wave per trip of the shifted wave plans
 // Unaligned rows shorter than this take the generic kernel.  The shifted wave
 // kernel is ahead of it down to short rows (262144 x 36 bf16: 61.3 against
 // 66.9 us; 262144 x 100 bf16: 62.2 against 89.5 us).
@@ -385,15 +387,17 @@ int choose_plan(int64_t M, int64_t N, int dtype, Access acc, rmsnorm_plan_t* p) 
     const int64_t nvec = ceil_div(N, elems_per_vector(dtype));
     const int64_t nchunks = ceil_div(N + elems_per_vector(dtype) - 1, elems_per_vector(dtype));
     if (!vec && acc.shifted && N >= kMinShiftedWaveN && nchunks <= kMaxShiftedWaveChunks) {
-        // one row per wave per slot, four slots per wave, 4-wave workgroups
+        // a row per segment of the fewest lanes (16, 32, 64) that hold its
+        // chunks, 4-wave workgroups; four slots per wave, two with 16-lane rows
         // (262144 x 257 bf16: 73 us, against 97 us with one row per 64-thread
         // workgroup and 163 us generic; 16384 x 1001 bf16: 14.4 us with four
-        // slots against 16.0 us with two)
+        // slots against 16.0 us with two; 262144 x 100 bf16: 28.0 us with
+        // 16-lane rows and two slots, 29.7 with four, 61.5 with a row per wave)
         p->variant = RMSNORM_VARIANT_SHIFTED_WAVE;
-        p->lanes_per_row = 64;
-        p->vectors_per_lane = static_cast<int>(ceil_div(nchunks, 64));
+        p->lanes_per_row = nchunks <= 16 ? 16 : (nchunks <= 32 ? 32 : 64);
+        p->vectors_per_lane = static_cast<int>(ceil_div(nchunks, p->lanes_per_row));
         p->block_threads = kWaveBlockThreads;
-        p->row_slots = kShiftedWaveSlots;
+        p->row_slots = p->lanes_per_row == 16 ? 2 : kShiftedWaveSlots;
     } else if (!vec && acc.shifted && nchunks > kMaxShiftedWaveChunks && nchunks <= kMaxShiftedChunks) {
         // one row per workgroup: the fewest threads (64 to 1024) that hold the
         // row's chunks with at most 3 per thread (32768 x 8191 bf16: 194 us with
@@ -1039,7 +1043,8 @@ int rmsnorm_plan_resources(const rmsnorm_plan_t* plan, int dtype, int32_t* vgprs
     else if (plan->variant == RMSNORM_VARIANT_SHIFTED)
         k = find_kernel(RMSNORM_VARIANT_SHIFTED, dtype, 0, plan->vectors_per_lane, 1, pf);
     else if (plan->variant == RMSNORM_VARIANT_SHIFTED_WAVE)
-        k = find_kernel(RMSNORM_VARIANT_SHIFTED_WAVE, dtype, 64, plan->vectors_per_lane, plan->row_slots, pf);
+        k = find_kernel(RMSNORM_VARIANT_SHIFTED_WAVE, dtype, plan->lanes_per_row, plan->vectors_per_lane,
+                        plan->row_slots, pf);
     else if (plan->variant == RMSNORM_VARIANT_WAVE)
         k = find_kernel(RMSNORM_VARIANT_WAVE, dtype, plan->lanes_per_row, plan->vectors_per_lane, plan->row_slots, pf);
     if (!k) return fail(RMSNORM_ERR_PLAN, "no compiled kernel for this plan");

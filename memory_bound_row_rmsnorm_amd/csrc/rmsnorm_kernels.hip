@@ -445,6 +445,30 @@ __device__ __forceinline__ u32x4 funnel(const u32x4 lo, const u32x4 hi, int sh) 
     return o;
 }
 
+// funnel() for a shift that differs between lanes (rows of several segments
+// in one wave): words k .. k + 3 of (lo, hi) from `sh` elements in, the word
+// offset picked per lane by selects instead of a branch.
+template <class D>
+__device__ __forceinline__ u32x4 funnel_lane(const u32x4 lo, const u32x4 hi, int sh) {
+    constexpr int EPW = 4 / static_cast<int>(sizeof(typename D::elem_t));
+    const uint32_t W[9] = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3], 0u};
+    const int q = sh / EPW;                                                 // 0 .. 4
+    const uint32_t r = static_cast<uint32_t>((sh % EPW) * sizeof(typename D::elem_t));
+    uint32_t A[5];      // A[k] = W[k + q]
+#pragma unroll
+    for (int k = 0; k < 5; ++k) {
+        uint32_t t = W[k];
+#pragma unroll
+        for (int j = 1; j <= 4; ++j)
+            if (k + j <= 8) t = q == j ? W[k + j] : t;
+        A[k] = t;
+    }
+    u32x4 o;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) o[k] = __builtin_amdgcn_alignbyte(A[k + 1], A[k], r);
+    return o;
+}
+
 // A chunk holding row elements j0 .. j0 + EPV - 1 with those outside
 // 0 .. n - 1 set to zero.
 template <class D>
@@ -571,34 +595,42 @@ __global__ __launch_bounds__(1024) void rmsnorm_shifted(KernelArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// Shifted wave family: the shifted kernel's chunk scheme for rows of at most
-// 64 * VPL chunks, one row per wave per slot, SLOTS rows per wave per trip,
-// no LDS and no barrier.  A row's distance past a 16-byte boundary is the
-// same in all lanes of its wave.  The weights do not depend on the row: each
-// lane fetches w vectors c - 1 and c of its chunks once, after the first
-// trip's rows, and funnel-shifts them for each row.
+// Shifted wave family: the shifted kernel's chunk scheme for short rows, a
+// row per segment of LANES lanes (16, 32 or 64; at most LANES * VPL chunks),
+// SLOTS slots of 64 / LANES rows per wave per trip, no LDS and no barrier.
+// With 64 lanes a row's distance past a 16-byte boundary is uniform in its
+// wave and the weights are shifted by a branch on it; with several rows per
+// wave every lane shifts by its own row's distance.  The weights do not
+// depend on the row: each lane fetches w vectors c - 1 and c of its chunks
+// once, after the first trip's rows, and shifts them for each row.
 // ---------------------------------------------------------------------------
-template <class D, int VPL, int SLOTS, bool PREFETCH>
+template <class D, int LANES, int VPL, int SLOTS, bool PREFETCH>
 __global__ __launch_bounds__(1024) void rmsnorm_shifted_wave(KernelArgs a) {
     typedef typename D::elem_t E;
     constexpr int EPV = D::EPV;
+    constexpr int SEG = 64 / LANES;       // rows per slot
+    constexpr int ROWS = SEG * SLOTS;     // rows per wave per trip
     const int64_t M = a.M;
-    const int n = static_cast<int>(a.N);      // at most 64 * VPL chunks
+    const int n = static_cast<int>(a.N);      // at most LANES * VPL chunks
     const E* xb = static_cast<const E*>(a.x) + batch() * a.x_bs;
     E* yb = static_cast<E*>(a.y) + batch() * a.y_bs;
     const u32x4* __restrict__ w = static_cast<const u32x4*>(a.w);
     const int nvec_w = (n + EPV - 1) / EPV;
     const int lane = threadIdx.x & 63;
+    const int seg = lane / LANES;
+    const int li = lane % LANES;
     const int wpb = a.threads >> 6;
     const int wid = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
     const int64_t nwaves = a.grid * wpb;
     int64_t g = grouped_block(a.xcd_group, a.grid) * wpb + wid;
 
     // rows past the end keep an in-range address and load nothing
-    auto row_of = [&](int64_t gg, int s) -> int64_t { return gg * SLOTS + s; };
+    auto row_of = [&](int64_t gg, int s) -> int64_t { return gg * ROWS + seg + s * SEG; };
     auto offset_of = [&](int64_t row) -> int {
         const E* xr = xb + (row < M ? row : 0) * a.x_rs;
-        return __builtin_amdgcn_readfirstlane(static_cast<int>((reinterpret_cast<uintptr_t>(xr) & 15u) / sizeof(E)));
+        const int al = static_cast<int>((reinterpret_cast<uintptr_t>(xr) & 15u) / sizeof(E));
+        if constexpr (LANES == 64) return __builtin_amdgcn_readfirstlane(al);
+        else return al;
     };
     auto load_trip = [&](u32x4 (&d)[SLOTS][VPL], int64_t gg) {
 #pragma unroll
@@ -609,7 +641,7 @@ __global__ __launch_bounds__(1024) void rmsnorm_shifted_wave(KernelArgs a) {
             const u32x4* xc = reinterpret_cast<const u32x4*>(xb + (row < M ? row : 0) * a.x_rs - al);
 #pragma unroll
             for (int v = 0; v < VPL; ++v) {
-                const int c = v * 64 + lane;
+                const int c = v * LANES + li;
                 d[s][v] = (row < M && c < nch) ? load_x(xc + c) : kZero;
             }
         }
@@ -620,7 +652,7 @@ __global__ __launch_bounds__(1024) void rmsnorm_shifted_wave(KernelArgs a) {
     u32x4 wlo[VPL], whi[VPL];
 #pragma unroll
     for (int v = 0; v < VPL; ++v) {
-        const int c = v * 64 + lane;
+        const int c = v * LANES + li;
         wlo[v] = (c >= 1 && c - 1 < nvec_w) ? w[c - 1] : kZero;
         whi[v] = c < nvec_w ? w[c] : kZero;
     }
@@ -632,10 +664,10 @@ __global__ __launch_bounds__(1024) void rmsnorm_shifted_wave(KernelArgs a) {
             const int al = offset_of(row_of(gg, s));
 #pragma unroll
             for (int v = 0; v < VPL; ++v) {
-                const int j0 = (v * 64 + lane) * EPV - al;
+                const int j0 = (v * LANES + li) * EPV - al;
                 if (j0 < 0 || j0 + EPV > n) dd[s][v] = keep_row<D>(dd[s][v], j0, n);
             }
-            const float ss = segment_allreduce<64>(sum_squares<D, VPL>(dd[s]));
+            const float ss = segment_allreduce<LANES>(sum_squares<D, VPL>(dd[s]));
             r[s] = rsq(__builtin_fmaf(ss, a.inv_n, a.eps));
         }
 #pragma unroll
@@ -646,10 +678,13 @@ __global__ __launch_bounds__(1024) void rmsnorm_shifted_wave(KernelArgs a) {
             u32x4* yc = reinterpret_cast<u32x4*>(yb + (row < M ? row : 0) * a.y_rs - al);
 #pragma unroll
             for (int v = 0; v < VPL; ++v) {
-                const int c = v * 64 + lane;
+                const int c = v * LANES + li;
                 if (row < M && c < nch) {
+                    u32x4 wc;
+                    if constexpr (LANES == 64) wc = al == 0 ? whi[v] : funnel<D>(wlo[v], whi[v], EPV - al);
+                    else wc = funnel_lane<D>(wlo[v], whi[v], EPV - al);
                     float we[EPV];
-                    widen_weights<D>(we, al == 0 ? whi[v] : funnel<D>(wlo[v], whi[v], EPV - al), a.offset);
+                    widen_weights<D>(we, wc, a.offset);
                     const u32x4 o = normalise<D>(dd[s][v], we, r[s]);
                     const int j0 = c * EPV - al;
                     if (j0 < 0 || j0 + EPV > n) store_edge<D>(yc + c, o, j0, n);
@@ -662,20 +697,20 @@ __global__ __launch_bounds__(1024) void rmsnorm_shifted_wave(KernelArgs a) {
 #pragma unroll
             for (int s = 0; s < SLOTS; ++s) {
                 const int64_t row = row_of(gg, s);
-                if (lane == 0 && row < M) store_rstd(rstd + row, r[s]);
+                if (li == 0 && row < M) store_rstd(rstd + row, r[s]);
             }
         }
     };
 
     if constexpr (!PREFETCH) {
-        if ((g + nwaves) * SLOTS >= M) {
+        if ((g + nwaves) * ROWS >= M) {
             finish_trip(d, g);
             return;
         }
     }
     for (;;) {
         const int64_t gn = g + nwaves;
-        const bool more = gn * SLOTS < M;
+        const bool more = gn * ROWS < M;
         u32x4 dn[SLOTS][VPL];
         if constexpr (PREFETCH) {
             if (more) load_trip(dn, gn);
@@ -757,11 +792,12 @@ __global__ __launch_bounds__(1024) void rmsnorm_generic(KernelArgs a) {
     {RMSNORM_VARIANT_SHIFTED, DT, 0, V, 1, P, true,                                               \
      reinterpret_cast<const void*>(&rmsnorm_shifted<D, V, P>), "rmsnorm_shifted<" #D "," #V "," #P ">"}
 #define RMS_SHIFTED(D, DT, V) RMS_SHIFTED_P(D, DT, V, false), RMS_SHIFTED_P(D, DT, V, true)
-#define RMS_SHIFTED_WAVE_P(D, DT, V, S, P)                                                     \
-    {RMSNORM_VARIANT_SHIFTED_WAVE, DT, 64, V, S, P, true,                                         \
-     reinterpret_cast<const void*>(&rmsnorm_shifted_wave<D, V, S, P>),                            \
-     "rmsnorm_shifted_wave<" #D "," #V "," #S "," #P ">"}
-#define RMS_SHIFTED_WAVE(D, DT, V, S) RMS_SHIFTED_WAVE_P(D, DT, V, S, false), RMS_SHIFTED_WAVE_P(D, DT, V, S, true)
+#define RMS_SHIFTED_WAVE_P(D, DT, L, V, S, P)                                                  \
+    {RMSNORM_VARIANT_SHIFTED_WAVE, DT, L, V, S, P, true,                                          \
+     reinterpret_cast<const void*>(&rmsnorm_shifted_wave<D, L, V, S, P>),                         \
+     "rmsnorm_shifted_wave<" #D "," #L "," #V "," #S "," #P ">"}
+#define RMS_SHIFTED_WAVE(D, DT, L, V, S)                                                       \
+    RMS_SHIFTED_WAVE_P(D, DT, L, V, S, false), RMS_SHIFTED_WAVE_P(D, DT, L, V, S, true)
 // Only instances that fit 128 VGPRs (the budget of a 1024-thread workgroup)
 // without scratch are compiled.  The widest forms leave out the tail path
 // (last argument false), which they have no registers for: they serve
@@ -778,9 +814,11 @@ __global__ __launch_bounds__(1024) void rmsnorm_generic(KernelArgs a) {
     RMS_BLOCK2(D, DT, 1), RMS_BLOCK2(D, DT, 2), RMS_BLOCK2(D, DT, 3), RMS_BLOCK2(D, DT, 4),     \
     RMS_BLOCK(D, DT, 5, false),                                                                 \
     RMS_SHIFTED(D, DT, 1), RMS_SHIFTED(D, DT, 2), RMS_SHIFTED(D, DT, 3), RMS_SHIFTED(D, DT, 4),   \
-    RMS_SHIFTED_WAVE(D, DT, 1, 1), RMS_SHIFTED_WAVE(D, DT, 1, 2), RMS_SHIFTED_WAVE(D, DT, 1, 4),   \
-    RMS_SHIFTED_WAVE(D, DT, 2, 1), RMS_SHIFTED_WAVE(D, DT, 2, 2),                                 \
-    RMS_SHIFTED_WAVE_P(D, DT, 2, 4, false),                                                      \
+    RMS_SHIFTED_WAVE(D, DT, 16, 1, 1), RMS_SHIFTED_WAVE(D, DT, 16, 1, 2), RMS_SHIFTED_WAVE(D, DT, 16, 1, 4), \
+    RMS_SHIFTED_WAVE(D, DT, 32, 1, 1), RMS_SHIFTED_WAVE(D, DT, 32, 1, 2), RMS_SHIFTED_WAVE(D, DT, 32, 1, 4), \
+    RMS_SHIFTED_WAVE(D, DT, 64, 1, 1), RMS_SHIFTED_WAVE(D, DT, 64, 1, 2), RMS_SHIFTED_WAVE(D, DT, 64, 1, 4), \
+    RMS_SHIFTED_WAVE(D, DT, 64, 2, 1), RMS_SHIFTED_WAVE(D, DT, 64, 2, 2),                         \
+    RMS_SHIFTED_WAVE_P(D, DT, 64, 2, 4, false),                                                  \
     {RMSNORM_VARIANT_GENERIC, DT, 0, 0, 1, false, true,                                         \
      reinterpret_cast<const void*>(&rmsnorm_generic<D>), "rmsnorm_generic<" #D ">"}
 

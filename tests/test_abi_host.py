@@ -178,7 +178,8 @@ def test_ragged_contiguous_rows_take_a_shifted_kernel(N):
     p = host_plan(10, N)                       # rows start a varying distance past a 16-byte boundary
     assert p.variant in (bnd.VARIANT_SHIFTED, bnd.VARIANT_SHIFTED_WAVE) and p.vec_elems == 8
     assert p.lanes_per_row * p.vectors_per_lane * 8 >= N + 7
-    assert p.rows_per_trip == (1 if p.variant == bnd.VARIANT_SHIFTED else p.block_threads // 64 * p.row_slots)
+    assert p.rows_per_trip == (1 if p.variant == bnd.VARIANT_SHIFTED
+                               else p.block_threads // 64 * (64 // p.lanes_per_row) * p.row_slots)
     f = host_plan(10, N, dtype=FP16, x=A + 2, y=A + 2 + 0x1000000)    # equally misaligned x and y
     assert f.variant == p.variant
 
@@ -193,14 +194,19 @@ def test_shifted_rule(N, threads, vpt, prefetch):
                                                                             prefetch)
 
 
-@pytest.mark.parametrize("N,dtype,vpl,slots", [(17, BF16, 1, 4), (129, BF16, 1, 4), (257, BF16, 1, 4),
-                                               (505, BF16, 1, 4), (513, BF16, 2, 4), (1017, BF16, 2, 4),
-                                               (130, FP16, 1, 4), (509, FP32, 2, 4)])
-def test_shifted_wave_rule(N, dtype, vpl, slots):
-    """Rows of 16 elements up to 128 chunks: one row per wave per slot, four slots."""
+@pytest.mark.parametrize("N,dtype,lanes,vpl", [(17, BF16, 16, 1), (121, BF16, 16, 1), (129, BF16, 32, 1),
+                                               (249, BF16, 32, 1), (257, BF16, 64, 1), (505, BF16, 64, 1),
+                                               (513, BF16, 64, 2), (1017, BF16, 64, 2), (130, FP16, 32, 1),
+                                               (61, FP32, 16, 1), (509, FP32, 64, 2)])
+def test_shifted_wave_rule(N, dtype, lanes, vpl):
+    """Rows of 16 elements up to 128 chunks: a row per segment of 16, 32 or 64 lanes (the fewest
+    that hold its chunks, up to 64), four slots per wave (two with 16-lane rows)."""
     p = host_plan(100000, N, dtype=dtype)
-    assert (p.variant, p.lanes_per_row, p.vectors_per_lane, p.row_slots) == (bnd.VARIANT_SHIFTED_WAVE, 64, vpl, slots)
-    assert p.rows_per_trip == 4 * slots and p.grid == -(-100000 // (4 * slots)) and p.trips == 1
+    slots = 2 if lanes == 16 else 4
+    assert (p.variant, p.lanes_per_row, p.vectors_per_lane, p.row_slots) == (bnd.VARIANT_SHIFTED_WAVE, lanes, vpl,
+                                                                            slots)
+    rows = 4 * (64 // lanes) * slots
+    assert p.rows_per_trip == rows and p.grid == -(-100000 // rows) and p.trips == 1
 
 
 @pytest.mark.parametrize("N,x,w", [(512, A + 2, None), (512, A + 8, None),   # x and y not equally aligned

@@ -275,7 +275,7 @@ def test_shifted_every_instance(bnd, dtype, N):
 
 
 @pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float16, torch.float32])
-@pytest.mark.parametrize("N", [9, 100, 129, 300, 505, 513, 1001, 1017])
+@pytest.mark.parametrize("N", [9, 61, 100, 129, 300, 505, 513, 1001, 1017])
 def test_shifted_wave_every_instance(bnd, dtype, N):
     """The wave form of the shifted kernel: every compiled instance that covers N, one trip and
     persistent grids, next-trip prefetch on and off."""
@@ -294,20 +294,20 @@ def test_shifted_wave_every_instance(bnd, dtype, N):
         return                                   # aligned rows never take a shifted kernel
     base = bnd.plan_query_ex(x, w)
     ran = 0
-    for vpl, slots, threads, pf in itertools.product((1, 2), (1, 2, 4), (64, 256), (0, 1)):
-        rows = threads // 64 * slots
+    for lanes, vpl, slots, threads, pf in itertools.product((16, 32, 64), (1, 2), (1, 2, 4), (64, 256), (0, 1)):
+        rows = threads // 64 * (64 // lanes) * slots
         for grid in (-(-M // rows), 2):
-            p = base.copy(variant=bnd.VARIANT_SHIFTED_WAVE, lanes_per_row=64, block_threads=threads,
+            p = base.copy(variant=bnd.VARIANT_SHIFTED_WAVE, lanes_per_row=lanes, block_threads=threads,
                           vectors_per_lane=vpl, row_slots=slots, prefetch=pf, grid=grid, xcd_group=1,
                           max_blocks_per_cu=0)
             if bnd.plan_validate(M, N, x.dtype, p, x.data_ptr(), w.data_ptr(), x.data_ptr()) is None:
                 continue                         # does not cover N, or no such instance
             y_base = filled(M * N + 16, dtype)
             y = y_base.as_strided((M, N), (N, 1), 8)
-            announce("shifted wave", M, N, dtype, vpl, slots, threads, pf, grid)
+            announce("shifted wave", M, N, dtype, lanes, vpl, slots, threads, pf, grid)
             out, rstd = bnd.rmsnorm_fwd_ex(x, w, 1e-6, 0.0, out=y, plan=p)
             torch.cuda.synchronize()
-            what = f"shifted wave {M}x{N} {dtype} vpl {vpl} slots {slots} {threads} thr pf {pf} grid {grid}"
+            what = f"shifted wave {M}x{N} {dtype} lanes {lanes} vpl {vpl} slots {slots} {threads} thr pf {pf} grid {grid}"
             if dtype == torch.float32:
                 parity.compare_fp32(out, rstd, ref[0], ref[1], what)
             else:
@@ -320,7 +320,7 @@ def test_shifted_wave_every_instance(bnd, dtype, N):
 
 
 @pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
-@pytest.mark.parametrize("N,lead", [(3001, 3), (1025, 1), (8191, 5), (300, 7), (129, 2), (1017, 6)])
+@pytest.mark.parametrize("N,lead", [(3001, 3), (1025, 1), (8191, 5), (300, 7), (129, 2), (1017, 6), (61, 3), (130, 5)])
 def test_shifted_reads_whole_edge_chunks_but_uses_only_the_row(bnd, dtype, N, lead):
     """The shifted kernel loads the aligned 16 bytes around each row's ends, and w's last vector whole:
     NaN in those bytes (before the first row, after the last, after w) must not reach y or rstd, and

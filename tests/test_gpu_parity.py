@@ -306,9 +306,15 @@ def test_python_checks_reject_bad_tensors(bnd):
         bnd.rmsnorm_fwd(x.t(), torch.ones(4, dtype=torch.bfloat16, device=DEV))
     with pytest.raises(ValueError):
         bnd.rmsnorm_fwd(x.double(), torch.ones(64, dtype=torch.float64, device=DEV))   # no fp64 kernels
-    with pytest.raises(bnd.RmsnormError) as e:
-        bnd.rmsnorm_bwd(x.float(), torch.ones(64, device=DEV), x.float(), torch.ones(4, device=DEV))
-    assert e.value.status == 3                                                          # fp32 backward: DTYPE
+    with pytest.raises(ValueError):                                                     # rstd must be float32
+        bnd.rmsnorm_bwd(x, torch.ones(64, dtype=torch.bfloat16, device=DEV), x, torch.ones(4, device=DEV).double())
+    with pytest.raises(ValueError):                                                     # dy must match x
+        bnd.rmsnorm_bwd_ex(x, torch.ones(64, dtype=torch.bfloat16, device=DEV), x[:, :32],
+                           torch.ones(4, device=DEV))
+    with pytest.raises(bnd.RmsnormError) as e:                                          # dx rows overlap
+        bnd.rmsnorm_bwd_ex(x, torch.ones(64, dtype=torch.bfloat16, device=DEV), x, torch.ones(4, device=DEV),
+                           out=torch.empty(112, dtype=torch.bfloat16, device=DEV).as_strided((4, 64), (16, 1)))
+    assert e.value.status == 2
     with pytest.raises(bnd.RmsnormError):
         bnd.rmsnorm_fwd(x, torch.ones(64, dtype=torch.bfloat16, device=DEV), eps=-1.0)
 
