@@ -78,9 +78,13 @@ typedef enum rmsnorm_variant {
                                     per workgroup, aligned 16-byte chunks, shifted weights.
                                     Edge chunks are read whole (the aligned 16 bytes that hold
                                     row elements) and written element by element */
-    RMSNORM_VARIANT_SHIFTED_WAVE = 5 /* the same chunks for rows of at most 64 * vectors_per_lane
-                                        chunks: one row per wave per slot, row_slots rows per
-                                        wave per trip, no LDS */
+    RMSNORM_VARIANT_SHIFTED_WAVE = 5, /* the same chunks for short rows: a row per segment of
+                                         lanes_per_row lanes (16, 32, 64), row_slots slots per
+                                         wave per trip, no LDS */
+    RMSNORM_VARIANT_WIDE = 6     /* aligned rows wider than the block family holds: one row per
+                                    workgroup in tiles of block_threads * vectors_per_lane
+                                    vectors, squares summed in a first pass, the row read again
+                                    (from the caches) to normalise */
 } rmsnorm_variant_t;
 
 /*

@@ -20,9 +20,10 @@ RMSNORM_FP32 = 2          # forward only
 DTYPE_CODES = {torch.bfloat16: RMSNORM_BF16, torch.float16: RMSNORM_FP16, torch.float32: RMSNORM_FP32}
 DTYPE_NAMES = {"bf16": RMSNORM_BF16, "fp16": RMSNORM_FP16, "fp32": RMSNORM_FP32}
 
-VARIANT_AUTO, VARIANT_WAVE, VARIANT_BLOCK, VARIANT_GENERIC, VARIANT_SHIFTED, VARIANT_SHIFTED_WAVE = 0, 1, 2, 3, 4, 5
+VARIANT_AUTO, VARIANT_WAVE, VARIANT_BLOCK, VARIANT_GENERIC, VARIANT_SHIFTED, VARIANT_SHIFTED_WAVE, VARIANT_WIDE = \
+    0, 1, 2, 3, 4, 5, 6
 VARIANT_NAMES = {VARIANT_WAVE: "wave", VARIANT_BLOCK: "block", VARIANT_GENERIC: "generic",
-                 VARIANT_SHIFTED: "shifted", VARIANT_SHIFTED_WAVE: "shifted_wave"}
+                 VARIANT_SHIFTED: "shifted", VARIANT_SHIFTED_WAVE: "shifted_wave", VARIANT_WIDE: "wide"}
 
 STATUS = {
     0: "RMSNORM_OK", 1: "RMSNORM_ERR_NULL", 2: "RMSNORM_ERR_SHAPE", 3: "RMSNORM_ERR_DTYPE",

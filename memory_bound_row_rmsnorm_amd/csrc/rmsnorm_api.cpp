@@ -217,8 +217,9 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 // final partial vector moves element by element).
 bool vector_ok(const void* x, const void* w, const void* y, int dtype, const Layout& L, int64_t M) {
     const int64_t es = elem_size(dtype);
-    const bool rows_ok = (L.x_rs * es) % 16 == 0 && (L.y_rs * es) % 16 == 0 &&
-                         L.x_rs * es / 16 < INT32_MAX && L.y_rs * es / 16 < INT32_MAX;
+    // with one row per batch the row stride is never applied
+    const bool rows_ok = L.rows <= 1 || ((L.x_rs * es) % 16 == 0 && (L.y_rs * es) % 16 == 0 &&
+                                         L.x_rs * es / 16 < INT32_MAX && L.y_rs * es / 16 < INT32_MAX);
     const bool batches_ok = L.batches(M) <= 1 || ((L.x_bs * es) % 16 == 0 && (L.y_bs * es) % 16 == 0);
     return aligned16(x) && aligned16(w) && aligned16(y) && rows_ok && batches_ok;
 }
@@ -254,7 +255,8 @@ const KernelEntry* find_kernel(int variant, int dtype, int lanes, int vpl, int s
         if ((variant == RMSNORM_VARIANT_WAVE || variant == RMSNORM_VARIANT_SHIFTED_WAVE) &&
             (k.lanes_per_row != lanes || k.vectors_per_lane != vpl || k.row_slots != slots))
             continue;
-        if ((variant == RMSNORM_VARIANT_BLOCK || variant == RMSNORM_VARIANT_SHIFTED) && k.vectors_per_lane != vpl)
+        if ((variant == RMSNORM_VARIANT_BLOCK || variant == RMSNORM_VARIANT_SHIFTED || variant == RMSNORM_VARIANT_WIDE) &&
+            k.vectors_per_lane != vpl)
             continue;
         return &k;
     }
@@ -319,6 +321,15 @@ int finish_plan(rmsnorm_plan_t* p, int64_t M, int64_t N, int dtype, Access acc, 
         k = find_kernel(RMSNORM_VARIANT_SHIFTED, dtype, 0, p->vectors_per_lane, 1, p->prefetch != 0);
         if (k && static_cast<int64_t>(p->block_threads) * p->vectors_per_lane * epv < N + epv - 1)
             return fail(RMSNORM_ERR_PLAN, "shifted plan does not cover N");
+    } else if (p->variant == RMSNORM_VARIANT_WIDE) {
+        if (!vec)
+            return fail(RMSNORM_ERR_PLAN, "16-byte kernels need 16-byte aligned x, w and y and 16-byte aligned rows");
+        p->vec_elems = elems_per_vector(dtype);
+        p->row_slots = 1;
+        p->lanes_per_row = p->block_threads;
+        p->rows_per_trip = 1;
+        if (p->prefetch != 0) return fail(RMSNORM_ERR_PLAN, "the wide kernel has no prefetching form");
+        k = find_kernel(RMSNORM_VARIANT_WIDE, dtype, 0, p->vectors_per_lane, 1, false);
     } else if (p->variant == RMSNORM_VARIANT_SHIFTED_WAVE) {
         if (!acc.shifted)
             return fail(RMSNORM_ERR_PLAN, "the shifted kernels need x and y equally aligned with the same layout, "
@@ -349,6 +360,9 @@ int finish_plan(rmsnorm_plan_t* p, int64_t M, int64_t N, int dtype, Access acc, 
 constexpr int kWaveSlots[] = {8, 4, 2, 1};
 constexpr int64_t kMaxVectors = 1024LL * 6;       // widest row the 16-byte kernels hold, in vectors
 constexpr int64_t kMaxShiftedChunks = 1024LL * 4;  // widest row the shifted kernel holds, in chunks
+// vectors per thread per tile of the wide kernel (4096 x 40968 bf16: 134.5 us
+// with 1024 x 2, 140.1 us with 1024 x 4, 373.7 us generic)
+constexpr int kWideVectors = 2;
 constexpr int64_t kMaxShiftedWaveChunks = 64 * 2;  // widest row the shifted wave kernel holds, in chunks
 constexpr int kShiftedWaveSlots = 4;               // slots per wave per trip of the shifted wave plans
 // Unaligned rows shorter than this take the generic kernel.  The shifted wave
@@ -408,9 +422,16 @@ int choose_plan(int64_t M, int64_t N, int dtype, Access acc, rmsnorm_plan_t* p) 
         p->block_threads = 64;
         while (p->block_threads < 1024 && nchunks > 3LL * p->block_threads) p->block_threads *= 2;
         p->vectors_per_lane = static_cast<int>(ceil_div(nchunks, p->block_threads));
-    } else if (!vec || nvec > kMaxVectors) {
+    } else if (!vec) {
         p->variant = RMSNORM_VARIANT_GENERIC;
         p->block_threads = N >= 1024 ? 256 : (N >= 256 ? 128 : 64);
+        p->row_slots = 1;
+    } else if (nvec > kMaxVectors) {
+        // rows wider than the registers of a 1024-thread workgroup hold: two
+        // passes over 1024 x 2 vector tiles
+        p->variant = RMSNORM_VARIANT_WIDE;
+        p->block_threads = 1024;
+        p->vectors_per_lane = kWideVectors;
         p->row_slots = 1;
     } else if (nvec <= 128) {
         p->variant = RMSNORM_VARIANT_WAVE;
@@ -441,12 +462,12 @@ int choose_plan(int64_t M, int64_t N, int dtype, Access acc, rmsnorm_plan_t* p) 
         p->block_threads = nvec <= 256 * 4 ? 256 : (nvec <= 512 * 3 ? 512 : 1024);
         p->vectors_per_lane = static_cast<int>(ceil_div(nvec, p->block_threads));
         // rows wider than the compiled instances hold (or a ragged width the
-        // widest ones have no tail path for) take the generic kernel
+        // widest ones have no tail path for) take the wide kernel
         const KernelEntry* k = find_kernel(RMSNORM_VARIANT_BLOCK, dtype, 0, p->vectors_per_lane, 1, false);
         if (!k || (!k->tails && N % elems_per_vector(dtype) != 0)) {
-            p->variant = RMSNORM_VARIANT_GENERIC;
-            p->block_threads = 256;
-            p->vectors_per_lane = 0;
+            p->variant = RMSNORM_VARIANT_WIDE;
+            p->block_threads = 1024;
+            p->vectors_per_lane = kWideVectors;
         }
     }
     int64_t rows_per_trip = 1;
@@ -456,7 +477,8 @@ int choose_plan(int64_t M, int64_t N, int dtype, Access acc, rmsnorm_plan_t* p) 
     p->grid = need < kMaxGrid ? need : kMaxGrid;
     p->xcd_group = 1;
     p->max_blocks_per_cu = 0;
-    if (p->variant == RMSNORM_VARIANT_BLOCK || p->variant == RMSNORM_VARIANT_SHIFTED) {
+    if (p->variant == RMSNORM_VARIANT_BLOCK || p->variant == RMSNORM_VARIANT_SHIFTED ||
+        p->variant == RMSNORM_VARIANT_WIDE) {
         // about 128 KiB of consecutive rows per XCD (a power of two, at least 8 rows)
         const int64_t row_bytes = N * es;
         int g = 8;
@@ -535,8 +557,8 @@ int launch(const KernelEntry* k, const rmsnorm_plan_t* p, const void* x, const v
         a.y_bs = L.y_bs;
         // the vector kernels' row strides in 16-byte vectors (checked to fit 31 bits by vector_ok)
         const int64_t epv = elems_per_vector(dtype);
-        a.x_rsv = static_cast<int32_t>(L.x_rs / epv);
-        a.y_rsv = static_cast<int32_t>(L.y_rs / epv);
+        a.x_rsv = L.rows <= 1 ? 0 : static_cast<int32_t>(L.x_rs / epv);   // unused with one row per batch
+        a.y_rsv = L.rows <= 1 ? 0 : static_cast<int32_t>(L.y_rs / epv);
         void* args[] = {&a};
         hipError_t e = hipLaunchKernel(k->func, dim3(static_cast<unsigned>(p->grid), static_cast<unsigned>(nb)),
                                        dim3(static_cast<unsigned>(p->block_threads)), args, dyn_lds,
@@ -1042,6 +1064,8 @@ int rmsnorm_plan_resources(const rmsnorm_plan_t* plan, int dtype, int32_t* vgprs
         k = find_kernel(RMSNORM_VARIANT_BLOCK, dtype, 0, plan->vectors_per_lane, 1, pf);
     else if (plan->variant == RMSNORM_VARIANT_SHIFTED)
         k = find_kernel(RMSNORM_VARIANT_SHIFTED, dtype, 0, plan->vectors_per_lane, 1, pf);
+    else if (plan->variant == RMSNORM_VARIANT_WIDE)
+        k = find_kernel(RMSNORM_VARIANT_WIDE, dtype, 0, plan->vectors_per_lane, 1, false);
     else if (plan->variant == RMSNORM_VARIANT_SHIFTED_WAVE)
         k = find_kernel(RMSNORM_VARIANT_SHIFTED_WAVE, dtype, plan->lanes_per_row, plan->vectors_per_lane,
                         plan->row_slots, pf);

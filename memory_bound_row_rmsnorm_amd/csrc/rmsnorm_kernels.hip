@@ -400,6 +400,70 @@ __global__ __launch_bounds__(1024) void rmsnorm_block(KernelArgs a) {
 }
 
 // ---------------------------------------------------------------------------
+// Wide family: aligned rows wider than the block family's registers hold.
+// One row per workgroup per trip, in tiles of T * VPT vectors.  A first pass
+// sums the squares tile by tile with cached loads; after the workgroup's
+// reduction a second pass reads the row again (from the caches: a trip's
+// rows, a few hundred KiB per compute unit, stay within the 256 MB Infinity
+// Cache), normalises and stores it.  HBM still sees each element of x read
+// once and of y written once.
+// ---------------------------------------------------------------------------
+template <class D, int VPT>
+__global__ __launch_bounds__(1024) void rmsnorm_wide(KernelArgs a) {
+    __shared__ float part[2][16];
+    const int64_t M = a.M;
+    const u32x4* __restrict__ x = batch_base(static_cast<const u32x4*>(a.x), vectors<D>(a.x_bs));
+    const u32x4* __restrict__ w = static_cast<const u32x4*>(a.w);
+    u32x4* __restrict__ y = batch_base(static_cast<u32x4*>(a.y), vectors<D>(a.y_bs));
+    const int nfull = static_cast<int>(static_cast<uint64_t>(a.N) / D::EPV);
+    const int tail = static_cast<int>(static_cast<uint64_t>(a.N) % D::EPV);
+    const int nvec = nfull + (tail != 0 ? 1 : 0);
+    const int x_rs = a.x_rsv, y_rs = a.y_rsv;
+    const int tid = threadIdx.x;
+    const int nt = a.threads;
+    const int lane = tid & 63;
+    const int wid = tid >> 6;
+    const int nw = nt >> 6;
+    const int tile = nt * VPT;
+
+    int par = 0;
+    for (int64_t row = grouped_block(a.xcd_group, a.grid); row < M; row += a.grid) {
+        const u32x4* xr = x + row * x_rs;
+        float ss = 0.0f;
+        for (int t0 = 0; t0 < nvec; t0 += tile) {
+            u32x4 d[VPT];
+#pragma unroll
+            for (int v = 0; v < VPT; ++v) d[v] = load_vec<D, false, true>(xr, t0 + v * nt + tid, nfull, tail);
+            ss += sum_squares<D, VPT>(d);
+        }
+        ss = segment_allreduce<64>(ss);
+        if (lane == 0) part[par][wid] = ss;
+        __syncthreads();
+        float tot = part[par][0];
+        for (int i = 1; i < nw; ++i) tot += part[par][i];
+        const float r = rsq(__builtin_fmaf(tot, a.inv_n, a.eps));
+        u32x4* yr = y + row * y_rs;
+        for (int t0 = 0; t0 < nvec; t0 += tile) {
+            u32x4 d[VPT], wq[VPT];
+#pragma unroll
+            for (int v = 0; v < VPT; ++v) {
+                const int c = t0 + v * nt + tid;
+                d[v] = load_vec<D, true, true>(xr, c, nfull, tail);
+                wq[v] = load_vec<D, false, true>(w, c, nfull, tail);
+            }
+#pragma unroll
+            for (int v = 0; v < VPT; ++v) {
+                float we[D::EPV];
+                widen_weights<D>(we, wq[v], a.offset);
+                store_vec<D, true>(yr, t0 + v * nt + tid, nfull, tail, normalise<D>(d[v], we, r));
+            }
+        }
+        if (tid == 0 && a.rstd != nullptr) store_rstd(a.rstd + batch() * M + row, r);
+        par ^= 1;
+    }
+}
+
+// ---------------------------------------------------------------------------
 // Shifted family: rows that do not start on a 16-byte boundary (contiguous
 // rows of N elements with N % EPV != 0 start a different number of elements
 // past one on every row).  One row per workgroup per trip.  The row is read
@@ -788,6 +852,9 @@ __global__ __launch_bounds__(1024) void rmsnorm_generic(KernelArgs a) {
      "rmsnorm_block<" #D "," #V "," #P "," #T ">"}
 #define RMS_BLOCK(D, DT, V, P) RMS_BLOCK_T(D, DT, V, P, true)
 #define RMS_BLOCK2(D, DT, V) RMS_BLOCK(D, DT, V, false), RMS_BLOCK(D, DT, V, true)
+#define RMS_WIDE(D, DT, V)                                                                     \
+    {RMSNORM_VARIANT_WIDE, DT, 0, V, 1, false, true,                                              \
+     reinterpret_cast<const void*>(&rmsnorm_wide<D, V>), "rmsnorm_wide<" #D "," #V ">"}
 #define RMS_SHIFTED_P(D, DT, V, P)                                                             \
     {RMSNORM_VARIANT_SHIFTED, DT, 0, V, 1, P, true,                                               \
      reinterpret_cast<const void*>(&rmsnorm_shifted<D, V, P>), "rmsnorm_shifted<" #D "," #V "," #P ">"}
@@ -813,6 +880,7 @@ __global__ __launch_bounds__(1024) void rmsnorm_generic(KernelArgs a) {
     RMS_WAVE2(D, DT, 64, 4, 1), RMS_WAVE2(D, DT, 64, 5, 1),                                     \
     RMS_BLOCK2(D, DT, 1), RMS_BLOCK2(D, DT, 2), RMS_BLOCK2(D, DT, 3), RMS_BLOCK2(D, DT, 4),     \
     RMS_BLOCK(D, DT, 5, false),                                                                 \
+    RMS_WIDE(D, DT, 2), RMS_WIDE(D, DT, 4),                                                     \
     RMS_SHIFTED(D, DT, 1), RMS_SHIFTED(D, DT, 2), RMS_SHIFTED(D, DT, 3), RMS_SHIFTED(D, DT, 4),   \
     RMS_SHIFTED_WAVE(D, DT, 16, 1, 1), RMS_SHIFTED_WAVE(D, DT, 16, 1, 2), RMS_SHIFTED_WAVE(D, DT, 16, 1, 4), \
     RMS_SHIFTED_WAVE(D, DT, 32, 1, 1), RMS_SHIFTED_WAVE(D, DT, 32, 1, 2), RMS_SHIFTED_WAVE(D, DT, 32, 1, 4), \

@@ -150,7 +150,7 @@ def test_planner_choices_for_the_workloads():
     assert (p.xcd_group, p.max_blocks_per_cu) == (8, 0)
     p = host_plan(3, 40960)
     assert (p.block_threads, p.vectors_per_lane, p.max_blocks_per_cu) == (1024, 5, 0)
-    assert host_plan(3, 49152).variant == bnd.VARIANT_GENERIC     # six 16-bit vectors per thread do not fit
+    assert host_plan(3, 49152).variant == bnd.VARIANT_WIDE        # six 16-bit vectors per thread do not fit
     p = host_plan(4096, 12288)
     assert (p.variant, p.block_threads, p.vectors_per_lane) == (bnd.VARIANT_BLOCK, 512, 3)
     for M, N in ((16384, 512), (262144, 128), (64, 256)):
@@ -166,6 +166,23 @@ def test_every_aligned_width_takes_a_16_byte_kernel():
             p = query_ex(1024, N, dtype)
             assert p.variant in (bnd.VARIANT_WAVE, bnd.VARIANT_BLOCK), (dtype, N)
             assert p.lanes_per_row * p.vectors_per_lane * epv >= N, (dtype, N)
+
+
+@pytest.mark.parametrize("N,dtype", [(40968, "bf16"), (49152, "bf16"), (1 << 17, "fp16"), (1 << 20, "bf16"),
+                                     (24580, "fp32"), (65536, "fp32")])
+def test_rows_wider_than_the_registers_take_the_wide_kernel(N, dtype):
+    p = query_ex(64, N, dtype)
+    assert (p.variant, p.block_threads, p.vectors_per_lane, p.rows_per_trip) == (bnd.VARIANT_WIDE, 1024, 2, 1)
+    assert p.vec_elems == (4 if dtype == "fp32" else 8) and p.grid == 64
+
+
+def test_a_single_ragged_row_takes_the_vector_kernels():
+    """One row: its stride never applies, so a ragged width still moves as 16-byte vectors plus a
+    tail vector."""
+    assert query_ex(1, 3001).variant == bnd.VARIANT_BLOCK
+    assert query_ex(1, 1001).variant == bnd.VARIANT_WAVE
+    assert query_ex(1, 100003).variant == bnd.VARIANT_WIDE
+    assert query_ex(2, 3001).variant == bnd.VARIANT_SHIFTED         # two rows: the second starts unaligned
 
 
 def test_huge_row_counts_loop_with_prefetch():
@@ -211,7 +228,7 @@ def test_shifted_wave_rule(N, dtype, lanes, vpl):
 
 @pytest.mark.parametrize("N,x,w", [(512, A + 2, None), (512, A + 8, None),   # x and y not equally aligned
                                    (3001, None, A + 2),                        # w not 16-byte aligned
-                                   (49160, None, None), (1 << 17, None, None),  # wider than the kernels hold
+                                   (49161, None, None),                        # unaligned, over 4096 chunks
                                    (7, None, None), (15, None, None)])          # short unaligned rows
 def test_unaligned_or_very_wide_rows_take_the_generic_kernel(N, x, w):
     p = host_plan(10, N, x=x, w=w)
@@ -500,13 +517,13 @@ def test_fp32_plans():
     p = query_ex(4, 24576, "fp32")
     assert (p.variant, p.vectors_per_lane) == (bnd.VARIANT_BLOCK, 6)
     assert query_ex(4, 24576, "bf16").variant == bnd.VARIANT_BLOCK          # 1024 x 3 vectors of 8
-    assert query_ex(4, 45056, "bf16").variant == bnd.VARIANT_GENERIC        # wider than 1024 x 5 x 8
+    assert query_ex(4, 45056, "bf16").variant == bnd.VARIANT_WIDE           # wider than 1024 x 5 x 8
     assert query_ex(4, 130, "fp32", layout=(0, 132, 0, 132, 0)).variant == bnd.VARIANT_WAVE
 
 
 def test_widest_instances_refuse_ragged_widths():
-    # fp32 1024 x 6 has no tail path: a ragged row that needs it takes the generic kernel
-    assert query_ex(4, 24576 - 3, "fp32", layout=(0, 24576, 0, 24576, 0)).variant == bnd.VARIANT_GENERIC
+    # fp32 1024 x 6 has no tail path: a ragged row that needs it takes the wide kernel, which has one
+    assert query_ex(4, 24576 - 3, "fp32", layout=(0, 24576, 0, 24576, 0)).variant == bnd.VARIANT_WIDE
     assert query_ex(4, 24576, "fp32").vectors_per_lane == 6
     assert query_ex(4, 40960 - 3, layout=(0, 40960, 0, 40960, 0)).vectors_per_lane == 5   # bf16 1024 x 5 has one
     p = bnd.plan_query(4, 24576, "fp32", cu_count=256)

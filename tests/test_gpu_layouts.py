@@ -388,3 +388,47 @@ def test_shifted_in_place(bnd):
     torch.cuda.synchronize()
     yr, rr = parity.oracle_for(xc, w.cpu(), 1e-6, 0.0, "fp16")
     parity.compare(out, rstd, yr, rr, "fp16", "shifted in place")
+
+
+# ---------------------------------------------------------------------------
+# The wide kernel: aligned rows wider than the block family's registers hold.
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("dtype,N,M", [(torch.bfloat16, 40968, 5), (torch.bfloat16, 65536, 5),
+                                       (torch.float16, 49152, 4), (torch.bfloat16, 100003, 1),
+                                       (torch.float32, 24580, 5), (torch.float32, 65537, 1)])
+def test_wide_rows(bnd, dtype, N, M):
+    """Rows of N elements at a row stride padded to whole 16-byte vectors (ragged N: the tail
+    vector moves element by element)."""
+    sigma = 100.0 if dtype == torch.float16 else 1.0
+    epv = 16 // torch.tensor([], dtype=dtype).element_size()
+    Np = -(-N // epv) * epv
+    x = draw((M, Np), dtype, 301, sigma).to(DEV)[:, :N]
+    w = (1.0 + 0.1 * draw((N,), torch.float32, 302)).to(dtype).to(DEV)
+    xc, wc = x.cpu(), w.cpu()
+    if dtype == torch.float32:
+        ref = parity.oracle_fp32(xc, wc, 1e-6, 1.0)
+    else:
+        dt = "bf16" if dtype == torch.bfloat16 else "fp16"
+        ref = parity.oracle_for(xc, wc, 1e-6, 1.0, dt)
+    y_base = filled(M * Np + 16, dtype)
+    y = y_base.as_strided((M, N), (Np, 1), 0)
+    base = bnd.plan_query_ex(x, w, y)
+    assert base.as_dict()["variant_name"] == "wide"
+    ran = 0
+    for threads, vpt, grid in itertools.product((256, 1024), (2, 4), (M, 2)):
+        p = bnd.plan_validate(M, N, x.dtype, base.copy(block_threads=threads, vectors_per_lane=vpt, grid=grid),
+                              x.data_ptr(), w.data_ptr(), y.data_ptr())
+        assert p is not None
+        y_base.copy_(filled(M * Np + 16, dtype))
+        announce("wide", M, N, dtype, threads, vpt, grid)
+        out, rstd = bnd.rmsnorm_fwd_ex(x, w, 1e-6, 1.0, out=y, plan=p)
+        torch.cuda.synchronize()
+        what = f"wide {M}x{N} {dtype} {threads}x{vpt} grid {grid}"
+        if dtype == torch.float32:
+            parity.compare_fp32(out, rstd, ref[0], ref[1], what)
+        else:
+            parity.compare(out, rstd, ref[0], ref[1], dt, what)
+        mask = view_mask(y_base.numel(), (M, N), (Np, 1), 0)
+        assert bool((y_base.cpu().view(INT_VIEW[dtype])[~mask] == SENTINEL[dtype]).all()), what
+        ran += 1
+    assert ran == 8
