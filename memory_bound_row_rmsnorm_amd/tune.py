@@ -67,6 +67,12 @@ def candidates(M: int, N: int, dtype: str, quick: bool = False) -> list:
                 raw.append(base.copy(variant=2, lanes_per_row=threads, vectors_per_lane=vpt, row_slots=1,
                                      block_threads=threads, prefetch=0, xcd_group=g, max_blocks_per_cu=cap,
                                      grid=M))
+        if nvec > 1024:
+            # rows too wide for a few vectors per thread: the two-pass tiled kernel
+            for threads, vpt, g in itertools.product((256, 512, 1024), (2, 4), groups):
+                raw.append(base.copy(variant=6, lanes_per_row=threads, vectors_per_lane=vpt, row_slots=1,
+                                     block_threads=threads, prefetch=0, xcd_group=g, max_blocks_per_cu=0,
+                                     grid=M))
     else:
         # rows that start unaligned: the shifted kernels (aligned chunks, per-row shifted weights)
         nch = -(-(N + 7) // 8)
@@ -158,7 +164,7 @@ def describe(p) -> str:
     name = binding.VARIANT_NAMES.get(p.variant, str(p.variant))
     if p.variant in (1, 5):
         s = f"{name} {p.lanes_per_row}x{p.vectors_per_lane} lanes x vectors, {p.row_slots} slots, {p.block_threads} thr"
-    elif p.variant in (2, 4):
+    elif p.variant in (2, 4, 6):
         s = f"{name} {p.block_threads} thr x {p.vectors_per_lane} vectors"
     else:
         s = f"{name} {p.block_threads} thr"
