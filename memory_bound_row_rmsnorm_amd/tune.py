@@ -36,20 +36,23 @@ from . import binding
 
 PEAK_GBPS = 8000.0
 ROTATION_X_BYTES = 1 << 30
-TORCH_DTYPES = {"bf16": torch.bfloat16, "fp16": torch.float16}
+TORCH_DTYPES = {"bf16": torch.bfloat16, "fp16": torch.float16, "fp32": torch.float32}
+ELEM_BYTES = {"bf16": 2, "fp16": 2, "fp32": 4}
 
 
-def algorithmic_bytes(M: int, N: int) -> int:
-    """x read and y written once, w read once, fp32 rstd written once (2-byte elements)."""
-    return 2 * M * N * 2 + N * 2 + 4 * M
+def algorithmic_bytes(M: int, N: int, dtype: str = "bf16") -> int:
+    """x read and y written once, w read once, fp32 rstd written once."""
+    es = ELEM_BYTES[dtype]
+    return 2 * M * N * es + N * es + 4 * M
 
 
 def candidates(M: int, N: int, dtype: str, quick: bool = False) -> list:
     """Every valid plan of the search space for this shape (16-byte aligned pointers)."""
     base = binding.plan_query(M, N, dtype, cu_count=256)
     raw = []
-    if N % 8 == 0:
-        nvec = N // 8
+    epv = 16 // ELEM_BYTES[dtype]
+    if N % epv == 0:
+        nvec = N // epv
         threads_set = (64, 128, 256, 512, 1024)
         for lanes, slots, threads in itertools.product((16, 32, 64), (1, 2, 4, 8), threads_set):
             vpl = -(-nvec // lanes)
@@ -75,12 +78,14 @@ def candidates(M: int, N: int, dtype: str, quick: bool = False) -> list:
                                      grid=M))
     else:
         # rows that start unaligned: the shifted kernels (aligned chunks, per-row shifted weights)
-        nch = -(-(N + 7) // 8)
+        nch = -(-(N + epv - 1) // epv)
         if nch <= 128:
-            vpl = -(-nch // 64)
-            for slots, threads, pf in itertools.product((1, 2, 4), (64, 128, 256, 512), (0, 1)):
-                rows_per_trip = (threads // 64) * slots
-                raw.append(base.copy(variant=5, lanes_per_row=64, vectors_per_lane=vpl, row_slots=slots,
+            for lanes, slots, threads, pf in itertools.product((16, 32, 64), (1, 2, 4), (64, 128, 256, 512), (0, 1)):
+                vpl = -(-nch // lanes)
+                if vpl > 2:
+                    continue
+                rows_per_trip = (threads // 64) * (64 // lanes) * slots
+                raw.append(base.copy(variant=5, lanes_per_row=lanes, vectors_per_lane=vpl, row_slots=slots,
                                      block_threads=threads, prefetch=pf, xcd_group=1, max_blocks_per_cu=0,
                                      grid=-(-M // rows_per_trip)))
         groups = (1, 8, 16) if quick else (1, 4, 8, 16)
@@ -111,7 +116,7 @@ class Buffers:
     """Rotation sets of x, y and rstd on the GPU (values: N(0, 1))."""
 
     def __init__(self, M: int, N: int, dtype: str, device="cuda:0"):
-        xbytes = M * N * 2
+        xbytes = M * N * ELEM_BYTES[dtype]
         self.sets = max(2, -(-ROTATION_X_BYTES // xbytes))
         g = torch.Generator(device=device).manual_seed(0)
         td = TORCH_DTYPES[dtype]
@@ -182,7 +187,7 @@ def tune_shape(M: int, N: int, dtype: str, quick: bool = False, log=print) -> li
     cands = candidates(M, N, dtype, quick)
     bufs = Buffers(M, N, dtype)
     cu = torch.cuda.get_device_properties(0).multi_processor_count
-    nbytes = algorithmic_bytes(M, N)
+    nbytes = algorithmic_bytes(M, N, dtype)
     est_us = nbytes / 5.0e6 + 2.0      # at 5 TB/s (5e6 bytes per microsecond), plus the launch floor
     steps = int(min(2000, max(20, 10000.0 / est_us)))   # about 10 ms of launches per replay
     results = []
@@ -212,7 +217,7 @@ def tune_shape(M: int, N: int, dtype: str, quick: bool = False, log=print) -> li
 def markdown_table(M: int, N: int, dtype: str, results: list, top: int = 0) -> str:
     default = binding.plan_query(M, N, dtype, cu_count=256)
     dkey = tuple(getattr(default, f) for f in binding.PLAN_FIELDS if f != "grid")
-    lines = [f"### {M} x {N} {dtype} ({algorithmic_bytes(M, N):,} algorithmic bytes per launch)", "",
+    lines = [f"### {M} x {N} {dtype} ({algorithmic_bytes(M, N, dtype):,} algorithmic bytes per launch)", "",
              "| plan | VGPRs | LDS B | WG/CU | waves/SIMD | us | GB/s | % of 8 TB/s |",
              "|---|---|---|---|---|---|---|---|"]
     rows = results if not top else results[:top]
