@@ -270,7 +270,8 @@ int rmsnorm_plan_resources(const rmsnorm_plan_t* plan, int dtype,
 /*
  * Plan of the backward row pass (variant, lanes, vectors, slots, block
  * threads, grid as for the forward; grid is the number of partial rows).
- * x, dy, dx only inform the alignment check.  cu_count as for
+ * x, dy, dx only inform the alignment check; w, not an argument here, is taken
+ * as 16-byte aligned (as every device allocation is).  cu_count as for
  * rmsnorm_plan_query.  Host only unless cu_count <= 0.
  */
 int rmsnorm_bwd_plan_query(int64_t M, int64_t N, int dtype, const void* x, const void* dy,
@@ -330,8 +331,11 @@ typedef struct rmsnorm_bwd_layout {
  * workspace as above.  dx may be exactly dy with the same row and batch
  * strides (in place).  The 16-byte kernels run when x, w, dy and dx are
  * 16-byte aligned, N is a multiple of vec_elems and every stride keeps rows
- * aligned; the generic kernel otherwise.  Errors as rmsnorm_bwd, plus
- * RMSNORM_ERR_SHAPE for a bad layout.
+ * aligned; the shifted kernel (variant RMSNORM_VARIANT_SHIFTED) when rows are
+ * not 16-byte aligned but x, dy and dx sit equally far past a 16-byte
+ * boundary on every row, w is 16-byte aligned and N >= 16 (at most 2048
+ * 16-byte chunks per row); the generic kernel otherwise.  Errors as
+ * rmsnorm_bwd, plus RMSNORM_ERR_SHAPE for a bad layout.
  */
 int rmsnorm_bwd_ex(const void* x, const void* w, const void* dy, const float* rstd, void* dx,
                    float* dw, int64_t M, int64_t N, float offset, int dtype,

@@ -445,7 +445,11 @@ def rmsnorm_bwd(x: torch.Tensor, w: torch.Tensor, dy: torch.Tensor, rstd: torch.
     dx = torch.empty_like(x)
     dw = torch.empty((N,), dtype=torch.float32, device=x.device)
     if plan is None:
-        nbytes = bwd_workspace_size(M, N, x.dtype, x.data_ptr(), dy.data_ptr(), dx.data_ptr())
+        b = ctypes.c_int64()
+        _check(lib.rmsnorm_bwd_workspace_size_ex(M, N, _dtype_code(x.dtype), x.data_ptr() or None,
+                                                 w.data_ptr() or None, dy.data_ptr() or None,
+                                                 dx.data_ptr() or None, None, ctypes.byref(b)))
+        nbytes = b.value
     else:
         nbytes = plan.grid * N * 4 if M > 0 else 0
     ws = torch.empty((max(nbytes, 16) + 3) // 4, dtype=torch.float32, device=x.device)

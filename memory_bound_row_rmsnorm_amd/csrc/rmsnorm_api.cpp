@@ -580,6 +580,8 @@ constexpr int64_t kBwdPlanCus = 256;                 // compute units the backwa
 constexpr int64_t kBwdPlanWaves = kBwdPlanCus * 16;  // row-pass waves aimed for: 16 per unit
 constexpr int64_t kBwdPartialsGeneric = 1024;        // row-pass grid cap of the generic family
 constexpr int kBwdWaveSlots[] = {4, 2, 1};
+// Unaligned rows shorter than this take the generic kernel.
+constexpr int64_t kBwdMinShiftedN = 16;
 
 const KernelEntry* find_bwd_kernel(int variant, int dtype, int lanes, int vpl, int slots, bool prefetch) {
     int n = 0;
@@ -590,7 +592,8 @@ const KernelEntry* find_bwd_kernel(int variant, int dtype, int lanes, int vpl, i
         if (variant == RMSNORM_VARIANT_WAVE &&
             (k.lanes_per_row != lanes || k.vectors_per_lane != vpl || k.row_slots != slots))
             continue;
-        if (variant == RMSNORM_VARIANT_BLOCK && k.vectors_per_lane != vpl) continue;
+        if ((variant == RMSNORM_VARIANT_BLOCK || variant == RMSNORM_VARIANT_SHIFTED) && k.vectors_per_lane != vpl)
+            continue;
         return &k;
     }
     return nullptr;
@@ -704,6 +707,25 @@ bool bwd_vector_ok(const void* x, const void* w, const void* dy, const void* dx,
            aligned16(dx) && rows_ok && batches_ok;
 }
 
+// The shifted backward kernel: x, dy and dx the same distance past a 16-byte
+// boundary on every row (equally aligned bases, strides that differ by whole
+// 16-byte vectors), w 16-byte aligned, rows of at most 2048 chunks, and not
+// the 16-byte kernels' case.
+bool bwd_shifted_ok(const void* x, const void* w, const void* dy, const void* dx, int dtype, const BwdLayout& L,
+                    int64_t M, int64_t N, bool vec) {
+    if (vec) return false;
+    const int64_t es = elem_size(dtype);
+    const int64_t epv = elems_per_vector(dtype);
+    const uintptr_t xa = reinterpret_cast<uintptr_t>(x), ya = reinterpret_cast<uintptr_t>(dy),
+                    oa = reinterpret_cast<uintptr_t>(dx);
+    const uintptr_t ue = static_cast<uintptr_t>(es);
+    if (xa % ue != 0 || ya % ue != 0 || oa % ue != 0 || xa % 16 != ya % 16 || xa % 16 != oa % 16) return false;
+    auto same_phase = [&](int64_t s1, int64_t s2) { return ((s1 - s2) * es) % 16 == 0; };
+    const bool rows_ok = L.rows <= 1 || (same_phase(L.x_rs, L.dy_rs) && same_phase(L.x_rs, L.dx_rs));
+    const bool batches_ok = L.batches(M) <= 1 || (same_phase(L.x_bs, L.dy_bs) && same_phase(L.x_bs, L.dx_bs));
+    return aligned16(w) && rows_ok && batches_ok && ceil_div(N + epv - 1, epv) <= kBwdMaxVectors;
+}
+
 int check_workspace(const void* ws, int64_t ws_bytes, int64_t need, const void* x, const void* w,
                     const void* dy, const float* rstd, const void* dx, const float* dw, int64_t M, int64_t N,
                     int dtype, const BwdLayout& L) {
@@ -722,7 +744,8 @@ int check_workspace(const void* ws, int64_t ws_bytes, int64_t need, const void* 
     return RMSNORM_OK;
 }
 
-int finish_bwd_plan(rmsnorm_plan_t* p, int64_t M, int64_t N, int dtype, bool vec, const KernelEntry** kernel) {
+int finish_bwd_plan(rmsnorm_plan_t* p, int64_t M, int64_t N, int dtype, bool vec, bool shifted,
+                    const KernelEntry** kernel) {
     if (p->block_threads < 64 || p->block_threads > 1024 || p->block_threads % 64 != 0)
         return fail(RMSNORM_ERR_PLAN, "block_threads must be a multiple of 64 in [64, 1024]");
     if (p->grid < 1 || p->grid > 0x7FFFFFFF) return fail(RMSNORM_ERR_PLAN, "grid must be in [1, 2^31)");
@@ -763,6 +786,19 @@ int finish_bwd_plan(rmsnorm_plan_t* p, int64_t M, int64_t N, int dtype, bool vec
                 p->rows_per_trip = 1;
             }
         }
+    } else if (p->variant == RMSNORM_VARIANT_SHIFTED) {
+        if (!shifted)
+            return fail(RMSNORM_ERR_PLAN, "the shifted backward kernel needs x, dy and dx equally far past a 16-byte "
+                                          "boundary on every row, 16-byte aligned w, rows that are not 16-byte "
+                                          "aligned, and at most 2048 chunks");
+        const int epv = elems_per_vector(dtype);
+        p->vec_elems = epv;
+        p->row_slots = 1;
+        p->lanes_per_row = p->block_threads;
+        p->rows_per_trip = 1;
+        k = find_bwd_kernel(RMSNORM_VARIANT_SHIFTED, dtype, 0, p->vectors_per_lane, 1, pf);
+        if (k && static_cast<int64_t>(p->block_threads) * p->vectors_per_lane * epv < N + epv - 1)
+            return fail(RMSNORM_ERR_PLAN, "shifted plan does not cover N");
     } else {
         return fail(RMSNORM_ERR_PLAN, "unknown variant");
     }
@@ -773,7 +809,8 @@ int finish_bwd_plan(rmsnorm_plan_t* p, int64_t M, int64_t N, int dtype, bool vec
 }
 
 // Backward plan: the forward's families and widths and a persistent row
-// pass.  Its grid G, the number of dw partial rows, is the smallest of: the
+// pass (rows off a 16-byte boundary: the shifted family, at most 2 chunks per
+// thread).  Its grid G, the number of dw partial rows, is the smallest of: the
 // rows' trips (one trip per workgroup), enough workgroups for 16 waves on
 // each of 256 compute units, and 3M/32, which keeps the workspace's write
 // and read within 1/8 of the row pass's 6MN bytes.  The next trip is loaded
@@ -781,11 +818,24 @@ int finish_bwd_plan(rmsnorm_plan_t* p, int64_t M, int64_t N, int dtype, bool vec
 // workgroup per unit: its barriers then stall the whole unit, which the early
 // loads cover; with two or more workgroups per unit they cover each other,
 // and the extra registers of the prefetching form cost more than they hide.
-int choose_bwd_plan(int64_t M, int64_t N, bool vec_ok, int dtype, rmsnorm_plan_t* p) {
+int choose_bwd_plan(int64_t M, int64_t N, bool vec_ok, bool shifted_ok, int dtype, rmsnorm_plan_t* p) {
     std::memset(p, 0, sizeof(*p));
     p->xcd_group = 1;
     const int64_t epv = elems_per_vector(dtype);
-    if (!vec_ok) {
+    if (!vec_ok && shifted_ok && N >= kBwdMinShiftedN) {
+        // one row per workgroup: one chunk per thread up to 128 chunks, then
+        // the fewest threads (up to 1024) that hold the row with at most 2
+        // per thread (16384 x 1001 bf16: 37.8 us with 128 x 1 against 44.6 us
+        // with 64 x 2; 8192 x 3001 bf16: 47.5 us with 256 x 2, 46.6 with
+        // 512 x 1; 16384 x 1002 fp32: 44.0 us with 128 x 2, 45.6 with 256 x 1)
+        const int64_t nchunks = ceil_div(N + epv - 1, epv);
+        const int64_t per_thread = nchunks <= 128 ? 1 : 2;
+        p->variant = RMSNORM_VARIANT_SHIFTED;
+        p->row_slots = 1;
+        p->block_threads = 64;
+        while (p->block_threads < 1024 && nchunks > per_thread * p->block_threads) p->block_threads *= 2;
+        p->vectors_per_lane = static_cast<int>(ceil_div(nchunks, p->block_threads));
+    } else if (!vec_ok) {
         p->variant = RMSNORM_VARIANT_GENERIC;
         p->block_threads = N >= 1024 ? 256 : (N >= 256 ? 128 : 64);
         p->row_slots = 1;
@@ -830,8 +880,8 @@ int choose_bwd_plan(int64_t M, int64_t N, bool vec_ok, int dtype, rmsnorm_plan_t
     if (ahead && p->variant == RMSNORM_VARIANT_WAVE &&
         find_bwd_kernel(RMSNORM_VARIANT_WAVE, dtype, p->lanes_per_row, p->vectors_per_lane, p->row_slots, true))
         p->prefetch = 1;
-    if (ahead && p->variant == RMSNORM_VARIANT_BLOCK &&
-        find_bwd_kernel(RMSNORM_VARIANT_BLOCK, dtype, 0, p->vectors_per_lane, 1, true))
+    if (ahead && (p->variant == RMSNORM_VARIANT_BLOCK || p->variant == RMSNORM_VARIANT_SHIFTED) &&
+        find_bwd_kernel(p->variant, dtype, 0, p->vectors_per_lane, 1, true))
         p->prefetch = 1;
     return RMSNORM_OK;
 }
@@ -898,11 +948,12 @@ int bwd_common(const void* x, const void* w, const void* dy, const float* rstd, 
     st = check_bwd_args(x, w, dy, rstd, dx, dw, M, N, offset, dtype, L);
     if (st != RMSNORM_OK) return st;
     const bool vec = bwd_vector_ok(x, w, dy, dx, dtype, L, M, N);
+    const bool shifted = bwd_shifted_ok(x, w, dy, dx, dtype, L, M, N, vec);
     rmsnorm_plan_t p;
     if (plan) p = *plan;
-    else choose_bwd_plan(M, N, vec, dtype, &p);
+    else choose_bwd_plan(M, N, vec, shifted, dtype, &p);
     const KernelEntry* k = nullptr;
-    st = finish_bwd_plan(&p, M, N, dtype, vec, &k);
+    st = finish_bwd_plan(&p, M, N, dtype, vec, shifted, &k);
     if (st != RMSNORM_OK) return st;
     const int64_t need = M > 0 ? p.grid * N * 4 : 0;
     st = check_workspace(ws, ws_bytes, need, x, w, dy, rstd, dx, dw, M, N, dtype, L);
@@ -923,8 +974,9 @@ int bwd_plan_for(int64_t M, int64_t N, int dtype, const void* x, const void* w, 
     st = normalise_bwd_layout(layout, M, N, &L);
     if (st != RMSNORM_OK) return st;
     const bool vec = bwd_vector_ok(x, w, dy, dx, dtype, L, M, N);
-    choose_bwd_plan(M, N, vec, dtype, p);
-    return finish_bwd_plan(p, M, N, dtype, vec, k);
+    const bool shifted = bwd_shifted_ok(x, w, dy, dx, dtype, L, M, N, vec);
+    choose_bwd_plan(M, N, vec, shifted, dtype, p);
+    return finish_bwd_plan(p, M, N, dtype, vec, shifted, k);
 }
 
 // ---------------------------------------------------------------------------
@@ -1083,10 +1135,13 @@ int rmsnorm_plan_resources(const rmsnorm_plan_t* plan, int dtype, int32_t* vgprs
 }
 
 
+// The queries without a w argument take w as 16-byte aligned (as every device
+// allocation is); only its alignment informs a plan.
+const void* const kAssumedW = reinterpret_cast<const void*>(uintptr_t{256});
+
 int rmsnorm_bwd_plan_query(int64_t M, int64_t N, int dtype, const void* x, const void* dy, const void* dx,
                            int32_t cu_count, rmsnorm_plan_t* out) {
-    // w is not an argument here: it is taken as aligned like dx
-    return rmsnorm_bwd_plan_query_ex(M, N, dtype, x, dx, dy, dx, nullptr, cu_count, out);
+    return rmsnorm_bwd_plan_query_ex(M, N, dtype, x, kAssumedW, dy, dx, nullptr, cu_count, out);
 }
 
 int rmsnorm_bwd_plan_query_ex(int64_t M, int64_t N, int dtype, const void* x, const void* w, const void* dy,
@@ -1105,7 +1160,7 @@ int rmsnorm_bwd_plan_query_ex(int64_t M, int64_t N, int dtype, const void* x, co
 
 int rmsnorm_bwd_workspace_size(int64_t M, int64_t N, int dtype, const void* x, const void* dy, const void* dx,
                                int64_t* bytes) {
-    return rmsnorm_bwd_workspace_size_ex(M, N, dtype, x, dx, dy, dx, nullptr, bytes);
+    return rmsnorm_bwd_workspace_size_ex(M, N, dtype, x, kAssumedW, dy, dx, nullptr, bytes);
 }
 
 int rmsnorm_bwd_workspace_size_ex(int64_t M, int64_t N, int dtype, const void* x, const void* w, const void* dy,

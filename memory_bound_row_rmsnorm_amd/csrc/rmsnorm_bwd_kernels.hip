@@ -317,6 +317,208 @@ __global__ __launch_bounds__(1024) void rmsnorm_bwd_block(BwdArgs a) {
 }
 
 // ---------------------------------------------------------------------------
+// Row pass, shifted family: rows that do not start on a 16-byte boundary (N
+// not a multiple of the vector, or bases past a boundary), one row per
+// workgroup per trip, thread t holding chunks v * T + t.  The row is read as
+// the aligned 16-byte chunks that cover it, as in the forward's shifted
+// kernel (edge chunks read whole, their elements outside the row set to zero,
+// stored element by element); c and dx are computed chunk by chunk with the
+// weights funnel-shifted into the chunk frame.
+//
+// dw cannot be kept in the chunk frame: which columns a chunk holds moves with
+// each row's distance `al` past a boundary.  Each thread keeps column vector
+// c instead (columns c * EPV .. c * EPV + EPV - 1 on every row), whose
+// products dy * x lie in chunk c from position al on and in chunk c + 1 below
+// al.  Chunk c + 1's products come from the lane above (DPP wave shift) or,
+// for a wave's last lane, from the next wave's first lane (the first wave's,
+// one slot on, for the last wave) through LDS, written before the row's
+// barrier.  The elements of w's last vector past the row are set to zero, so
+// the weights of the masked elements are finite and add nothing to c.
+// With PREFETCH the next row is loaded before this row's reduction.  x, dy
+// and dx must sit the same distance past a boundary on every row; dx may be
+// dy (in place: every element is read, then written, by one thread, and the
+// neighbouring rows' elements of an edge chunk are read but never used).
+// ---------------------------------------------------------------------------
+// acc[i] += r * (element i + al of the concatenation (cur, nxt)), for the
+// wave-uniform al of one row: one branch, constant register indices.
+template <int EPV>
+__device__ __forceinline__ void add_columns(float (&acc)[EPV], const float (&cur)[EPV], const float (&nxt)[EPV],
+                                            int al, float r) {
+    switch (al) {
+#define RMS_COLUMN_CASE(A)                                                                           \
+        case A:                                                                                      \
+            if constexpr (A < EPV) {                                                                 \
+                _Pragma("unroll") for (int i = 0; i < EPV; ++i)                                      \
+                    acc[i] = __builtin_fmaf(i + A < EPV ? cur[i + A] : nxt[i + A - EPV], r, acc[i]); \
+            }                                                                                        \
+            break;
+        RMS_COLUMN_CASE(0) RMS_COLUMN_CASE(1) RMS_COLUMN_CASE(2) RMS_COLUMN_CASE(3)
+        RMS_COLUMN_CASE(4) RMS_COLUMN_CASE(5) RMS_COLUMN_CASE(6) RMS_COLUMN_CASE(7)
+#undef RMS_COLUMN_CASE
+        default:
+            break;
+    }
+}
+
+template <class D, int VPT, bool PREFETCH>
+__global__ __launch_bounds__(1024) void rmsnorm_bwd_shifted(BwdArgs a) {
+    typedef typename D::elem_t E;
+    constexpr int EPV = D::EPV;
+    __shared__ float part[2][16];
+    __shared__ float first[2][VPT][16][EPV];     // each wave's first lane's products dy * x
+    const E* x = static_cast<const E*>(a.x);
+    const E* dy = static_cast<const E*>(a.dy);
+    E* dx = static_cast<E*>(a.dx);
+    const u32x4* __restrict__ w = static_cast<const u32x4*>(a.w);
+    const float* __restrict__ rstd = a.rstd;
+    const int64_t M = a.M;
+    const int n = static_cast<int>(a.N);         // at most 2048 chunks: 32-bit element indices
+    const int nvec_w = (n + EPV - 1) / EPV;
+    const int tid = threadIdx.x;
+    const int nt = a.threads;
+    const int lane = tid & 63;
+    const int wid = tid >> 6;
+    const int nw = nt >> 6;
+
+    // w vectors c - 1 and c of each chunk c (the same on every row)
+    auto wvec = [&](int k) -> u32x4 {
+        if (k < 0 || k >= nvec_w) return kZero;
+        return k == nvec_w - 1 ? keep_row<D>(w[k], k * EPV, n) : w[k];
+    };
+    u32x4 wlo[VPT], whi[VPT];
+    float dwp[VPT][EPV];
+#pragma unroll
+    for (int v = 0; v < VPT; ++v) {
+        const int c = v * nt + tid;
+        wlo[v] = wvec(c - 1);
+        whi[v] = wvec(c);
+#pragma unroll
+        for (int k = 0; k < EPV; ++k) dwp[v][k] = 0.0f;
+    }
+    // offset + w in the chunk frame of a row al elements past a boundary
+    auto weights = [&](float (&g)[EPV], int v, int al) {
+        widen_g<D>(g, al == 0 ? whi[v] : funnel<D>(wlo[v], whi[v], EPV - al), a.offset);
+    };
+
+    auto load_row = [&](u32x4 (&xd)[VPT], u32x4 (&dd)[VPT], float& r, int& al, int64_t rr) {
+        const RowOff o = row_offsets(a, rr);
+        al = __builtin_amdgcn_readfirstlane(
+            static_cast<int>((reinterpret_cast<uintptr_t>(x + o.x) & 15u) / sizeof(E)));
+        const u32x4* xc = reinterpret_cast<const u32x4*>(x + o.x - al);
+        const u32x4* dc = reinterpret_cast<const u32x4*>(dy + o.dy - al);
+        const int nch = (al + n + EPV - 1) / EPV;
+#pragma unroll
+        for (int v = 0; v < VPT; ++v) {
+            const int c = v * nt + tid;
+            xd[v] = c < nch ? stream_load(xc + c) : kZero;
+            dd[v] = c < nch ? stream_load(dc + c) : kZero;
+        }
+        r = rstd[rr];
+    };
+
+    int par = 0;
+    int64_t row = blockIdx.x;
+    u32x4 xd[VPT], dd[VPT];
+    float r = 0.0f;
+    int al = 0;
+    if (PREFETCH && row < M) load_row(xd, dd, r, al, row);
+    while (row < M) {
+        const int64_t next = row + a.grid;
+        u32x4 xn[VPT], dn[VPT];
+        float rn = 0.0f;
+        int aln = 0;
+        if constexpr (PREFETCH) {
+            if (next < M) load_row(xn, dn, rn, aln, next);
+        } else {
+            load_row(xd, dd, r, al, row);
+        }
+        const int nch = (al + n + EPV - 1) / EPV;
+#pragma unroll
+        for (int v = 0; v < VPT; ++v) {
+            const int j0 = (v * nt + tid) * EPV - al;
+            if (j0 < 0 || j0 + EPV > n) {
+                xd[v] = keep_row<D>(xd[v], j0, n);
+                dd[v] = keep_row<D>(dd[v], j0, n);
+            }
+        }
+        if (lane == 0) {
+#pragma unroll
+            for (int v = 0; v < VPT; ++v) {
+                float d[EPV], xv[EPV];
+                D::widen(dd[v], d);
+                D::widen(xd[v], xv);
+#pragma unroll
+                for (int k = 0; k < EPV; ++k) first[par][v][wid][k] = d[k] * xv[k];
+            }
+        }
+        float t = 0.0f;
+#pragma unroll
+        for (int v = 0; v < VPT; ++v) {
+            float g[EPV];
+            weights(g, v, al);
+            t = dot_dgx<D>(dd[v], xd[v], g, t);
+        }
+        t = segment_allreduce<64>(t);
+        if (lane == 0) part[par][wid] = t;
+        __syncthreads();
+        float tot = part[par][0];
+        for (int i = 1; i < nw; ++i) tot += part[par][i];
+        const float r2c = r * r * (tot * a.inv_n);
+        u32x4* oc = reinterpret_cast<u32x4*>(dx + row_offsets(a, row).dx - al);
+#pragma unroll
+        for (int v = 0; v < VPT; ++v) {
+            const int c = v * nt + tid;
+            float g[EPV], d[EPV], xv[EPV], o[EPV], p[EPV], pn[EPV];
+            weights(g, v, al);
+            D::widen(dd[v], d);
+            D::widen(xd[v], xv);
+#pragma unroll
+            for (int k = 0; k < EPV; ++k) {
+                o[k] = r * (g[k] * d[k] - r2c * xv[k]);
+                p[k] = d[k] * xv[k];
+            }
+            if (c < nch) {
+                const u32x4 ov = D::narrow(o);
+                const int j0 = c * EPV - al;
+                if (j0 < 0 || j0 + EPV > n) store_edge<D>(oc + c, ov, j0, n);
+                else stream_store(oc + c, ov);
+            }
+            // chunk c + 1's products
+#pragma unroll
+            for (int k = 0; k < EPV; ++k) {
+                float up = 0.0f;
+                if (wid + 1 < nw) up = first[par][v][wid + 1][k];
+                else if (v + 1 < VPT) up = first[par][v + 1 < VPT ? v + 1 : 0][0][k];
+                pn[k] = from_lane_above(p[k], up);
+            }
+            add_columns<EPV>(dwp[v], p, pn, al, r);
+        }
+        par ^= 1;
+        row = next;
+        if constexpr (PREFETCH) {
+#pragma unroll
+            for (int v = 0; v < VPT; ++v) {
+                xd[v] = xn[v];
+                dd[v] = dn[v];
+            }
+            r = rn;
+            al = aln;
+        }
+    }
+
+    float* dst = a.partials + static_cast<int64_t>(blockIdx.x) * n;
+#pragma unroll
+    for (int v = 0; v < VPT; ++v) {
+        const int c = v * nt + tid;
+        if (c < nvec_w) {
+#pragma unroll
+            for (int k = 0; k < EPV; ++k)
+                if (c * EPV + k < n) dst[c * EPV + k] = dwp[v][k];
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
 // Row pass, generic (any N and alignment): one row per workgroup per trip,
 // element-wide accesses, the row read twice (c first, then dx), and the
 // workgroup's partial row of dw updated in the workspace in place (each
@@ -439,6 +641,10 @@ __global__ __launch_bounds__(16 * SPLIT) void rmsnorm_dw_reduce(const float* __r
     {RMSNORM_VARIANT_BLOCK, DT, 0, V, 1, P, false,                                                    \
      reinterpret_cast<const void*>(&rmsnorm_bwd_block<D, V, P>),                               \
      "rmsnorm_bwd_block<" #D "," #V "," #P ">"}
+#define RMS_BWD_SHIFTED(D, DT, V, P)                                                           \
+    {RMSNORM_VARIANT_SHIFTED, DT, 0, V, 1, P, false,                                                  \
+     reinterpret_cast<const void*>(&rmsnorm_bwd_shifted<D, V, P>),                             \
+     "rmsnorm_bwd_shifted<" #D "," #V "," #P ">"}
 // Only instances that fit 128 VGPRs without scratch: the block family holds
 // at most two vectors of x and dy per thread (rows up to 1024 x 2 vectors:
 // 16384 16-bit or 8192 fp32 elements), and the widest wave shapes have no
@@ -451,6 +657,8 @@ __global__ __launch_bounds__(16 * SPLIT) void rmsnorm_dw_reduce(const float* __r
     RMS_BWD_WAVE(D, DT, 64, 2, 2, false),                                                      \
     RMS_BWD_BLOCK(D, DT, 1, false), RMS_BWD_BLOCK(D, DT, 1, true),                             \
     RMS_BWD_BLOCK(D, DT, 2, false), RMS_BWD_BLOCK(D, DT, 2, true),                             \
+    RMS_BWD_SHIFTED(D, DT, 1, false), RMS_BWD_SHIFTED(D, DT, 1, true),                         \
+    RMS_BWD_SHIFTED(D, DT, 2, false), RMS_BWD_SHIFTED(D, DT, 2, true),                         \
     {RMSNORM_VARIANT_GENERIC, DT, 0, 0, 1, false, false,                                              \
      reinterpret_cast<const void*>(&rmsnorm_bwd_generic<D>), "rmsnorm_bwd_generic<" #D ">"}
 

@@ -484,95 +484,9 @@ __global__ __launch_bounds__(1024) void rmsnorm_wide(KernelArgs a) {
 // the lane below (DPP wave shift) or, for lane 0, from the last lane of the
 // wave below through LDS (faster with up to 256 threads, where a row has
 // fewer waves to hide the weights' latency behind).
-// x and y must sit the same distance past a boundary on every row.
+// x and y must sit the same distance past a boundary on every row.  The
+// funnel, mask and edge-store helpers are in rmsnorm_device.hpp.
 // ---------------------------------------------------------------------------
-// Words k .. k + 3 of the 8-word concatenation (lo, hi) starting `sh`
-// elements in (0 < sh <= EPV), for the wave-uniform sh of one row.
-template <class D>
-__device__ __forceinline__ u32x4 funnel(const u32x4 lo, const u32x4 hi, int sh) {
-    constexpr int EPW = 4 / static_cast<int>(sizeof(typename D::elem_t));   // elements per word
-    const uint32_t W[9] = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3], 0u};
-    const int q = sh / EPW;                                                 // whole words
-    const uint32_t r = static_cast<uint32_t>((sh % EPW) * sizeof(typename D::elem_t));   // bytes
-    u32x4 o;
-    switch (q) {    // q is the same in every lane: one branch, constant register indices
-#define RMS_FUNNEL_CASE(Q)                                                                   \
-        case Q:                                                                              \
-            for (int k = 0; k < 4; ++k) o[k] = __builtin_amdgcn_alignbyte(W[k + Q + 1], W[k + Q], r); \
-            break;
-        RMS_FUNNEL_CASE(0) RMS_FUNNEL_CASE(1) RMS_FUNNEL_CASE(2) RMS_FUNNEL_CASE(3)
-#undef RMS_FUNNEL_CASE
-        default:
-            o = hi;
-            break;
-    }
-    return o;
-}
-
-// funnel() for a shift that differs between lanes (rows of several segments
-// in one wave): words k .. k + 3 of (lo, hi) from `sh` elements in, the word
-// offset picked per lane by selects instead of a branch.
-template <class D>
-__device__ __forceinline__ u32x4 funnel_lane(const u32x4 lo, const u32x4 hi, int sh) {
-    constexpr int EPW = 4 / static_cast<int>(sizeof(typename D::elem_t));
-    const uint32_t W[9] = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3], 0u};
-    const int q = sh / EPW;                                                 // 0 .. 4
-    const uint32_t r = static_cast<uint32_t>((sh % EPW) * sizeof(typename D::elem_t));
-    uint32_t A[5];      // A[k] = W[k + q]
-#pragma unroll
-    for (int k = 0; k < 5; ++k) {
-        uint32_t t = W[k];
-#pragma unroll
-        for (int j = 1; j <= 4; ++j)
-            if (k + j <= 8) t = q == j ? W[k + j] : t;
-        A[k] = t;
-    }
-    u32x4 o;
-#pragma unroll
-    for (int k = 0; k < 4; ++k) o[k] = __builtin_amdgcn_alignbyte(A[k + 1], A[k], r);
-    return o;
-}
-
-// A chunk holding row elements j0 .. j0 + EPV - 1 with those outside
-// 0 .. n - 1 set to zero.
-template <class D>
-__device__ __forceinline__ u32x4 keep_row(u32x4 v, int j0, int n) {
-    constexpr int EPW = 4 / static_cast<int>(sizeof(typename D::elem_t));
-    const int lo = -j0, hi = n - j0;    // kept: lo <= i < hi
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-        if constexpr (EPW == 2) {
-            const uint32_t m = ((2 * k >= lo && 2 * k < hi) ? 0x0000FFFFu : 0u) |
-                               ((2 * k + 1 >= lo && 2 * k + 1 < hi) ? 0xFFFF0000u : 0u);
-            v[k] &= m;
-        } else {
-            v[k] = (k >= lo && k < hi) ? v[k] : 0u;
-        }
-    }
-    return v;
-}
-
-// The row's own elements of an edge chunk, stored one at a time.
-template <class D>
-__device__ __forceinline__ void store_edge(u32x4* p, u32x4 v, int j0, int n) {
-    typedef typename D::elem_t E;
-    E* q = reinterpret_cast<E*>(p);
-    const auto e = __builtin_bit_cast(E __attribute__((ext_vector_type(D::EPV))), v);
-#pragma unroll
-    for (int i = 0; i < D::EPV; ++i)
-        if (j0 + i >= 0 && j0 + i < n) q[i] = e[i];
-}
-
-// Each lane's v from the lane below (DPP wave_shr:1); lane 0 takes `lane0`.
-__device__ __forceinline__ u32x4 from_lane_below(const u32x4 v, const u32x4 lane0) {
-    u32x4 o;
-#pragma unroll
-    for (int k = 0; k < 4; ++k)
-        o[k] = static_cast<uint32_t>(__builtin_amdgcn_update_dpp(static_cast<int>(lane0[k]), static_cast<int>(v[k]),
-                                                                 0x138, 0xF, 0xF, false));
-    return o;
-}
-
 template <class D, int VPT, bool WPRE>
 __global__ __launch_bounds__(1024) void rmsnorm_shifted(KernelArgs a) {
     typedef typename D::elem_t E;

@@ -309,10 +309,11 @@ def test_bwd_argument_errors(kwargs, status):
 
 @pytest.mark.parametrize("N,variant,lanes,vpl", [(128, 1, 32, 1), (512, 1, 64, 2), (4096, 2, 512, 2),
                                                (8192, 2, 1024, 2), (8196, 3, 0, 0), (8200, 3, 0, 0),
-                                               (1002, 3, 0, 0)])
+                                               (1002, 4, 128, 2), (8189, 4, 1024, 2), (8190, 3, 0, 0)])
 def test_bwd_fp32_plans(N, variant, lanes, vpl):
     """fp32 rows: four elements per 16-byte vector, so the wave family holds 512 and the block
-    family 8192 elements; other widths take the generic kernel."""
+    family 8192 elements, and the shifted family rows of up to 2048 chunks; wider rows take the
+    generic kernel."""
     p = bnd.Plan()
     assert lib.rmsnorm_bwd_plan_query(4096, N, FP32, None, None, None, 256, ctypes.byref(p)) == OK
     assert p.variant == variant
@@ -349,7 +350,7 @@ def test_bwd_plans_and_workspace():
     assert (p.variant, p.block_threads, p.vectors_per_lane, p.grid, p.prefetch) == (bnd.VARIANT_BLOCK, 1024, 2, 256, 1)
     assert plan(64, 8192).grid == 6                              # 3M/32 bounds the workspace traffic
     assert plan(10, 16392).variant == bnd.VARIANT_GENERIC      # wider than the 16-byte kernels hold
-    assert plan(10, 511).variant == bnd.VARIANT_GENERIC
+    assert plan(10, 511).variant == bnd.VARIANT_SHIFTED
     assert plan(10, 512, x=A + 2).variant == bnd.VARIANT_GENERIC
     assert plan(3, 512).grid == 1                               # 3 rows fit one 8-wave workgroup
     assert ws(0, 512) == 0
@@ -584,3 +585,56 @@ def test_bwd_ex_plans():
     lay = bnd.BwdLayout(32, 1536, 32 * 1536, 512, 32 * 512, 2048, 32 * 2048)
     assert lib.rmsnorm_bwd_workspace_size_ex(4096, 512, BF16, A, A, A, A, ctypes.byref(lay), ctypes.byref(b)) == OK
     assert b.value == p.grid * 512 * 4
+
+
+def test_bwd_shifted_plans():
+    """Rows off a 16-byte boundary take the shifted row pass when x, dy and dx sit equally far past
+    a boundary on every row and w is aligned: the fewest threads (64 to 1024) holding the row's
+    chunks at most 2 per thread, rows of 16 to 2048 chunks."""
+    p = bwd_plan_ex(8192, 3001, None)
+    assert (p.variant, p.block_threads, p.vectors_per_lane, p.vec_elems) == (bnd.VARIANT_SHIFTED, 256, 2, 8)
+    assert (p.lanes_per_row, p.rows_per_trip, p.grid, p.prefetch) == (256, 1, 768, 0)
+    p = bwd_plan_ex(32768, 8191, None)
+    assert (p.variant, p.block_threads, p.vectors_per_lane, p.grid, p.prefetch) == \
+        (bnd.VARIANT_SHIFTED, 1024, 2, 256, 1)
+    p = bwd_plan_ex(100, 17, None)                 # 3 chunks: one wave
+    assert (p.variant, p.block_threads, p.vectors_per_lane) == (bnd.VARIANT_SHIFTED, 64, 1)
+    p = bwd_plan_ex(16384, 1001, None)             # 126 chunks: one per thread
+    assert (p.variant, p.block_threads, p.vectors_per_lane) == (bnd.VARIANT_SHIFTED, 128, 1)
+    p = bwd_plan_ex(16384, 1017, None)             # 128 chunks (1017 + 7 elements)
+    assert (p.block_threads, p.vectors_per_lane) == (128, 1)
+    p = bwd_plan_ex(16384, 1018, None)             # 129 chunks: two per thread
+    assert (p.block_threads, p.vectors_per_lane) == (128, 2)
+    assert bwd_plan_ex(16, 16377, None).variant == bnd.VARIANT_SHIFTED      # 2048 chunks
+    assert bwd_plan_ex(16, 16378, None).variant == bnd.VARIANT_GENERIC      # 2049
+    assert bwd_plan_ex(100, 15, None).variant == bnd.VARIANT_GENERIC        # shorter than 16 elements
+    assert bwd_plan_ex(100, 16, None).variant == bnd.VARIANT_WAVE
+    # x, dy and dx must share the distance past a boundary; w must be aligned
+    assert bwd_plan_ex(100, 3001, None, dx=A + 2).variant == bnd.VARIANT_GENERIC
+    assert bwd_plan_ex(100, 3001, None, dy=A + 4).variant == bnd.VARIANT_GENERIC
+    assert bwd_plan_ex(100, 3001, None, w=A + 2).variant == bnd.VARIANT_GENERIC
+    assert bwd_plan_ex(100, 3001, None, x=A + 1, dy=A + 1, dx=A + 1).variant == bnd.VARIANT_GENERIC
+    # aligned rows on equally offset bases are shifted too (every row one element in)
+    assert bwd_plan_ex(100, 512, None, x=A + 2, dy=A + 0x100002, dx=A + 0x200002).variant == bnd.VARIANT_SHIFTED
+    # strides may differ by whole 16-byte vectors, not by less
+    lay = bnd.BwdLayout(0, 3001, 0, 3009, 0, 3017, 0)
+    assert bwd_plan_ex(100, 3001, lay).variant == bnd.VARIANT_SHIFTED
+    lay = bnd.BwdLayout(0, 3001, 0, 3002, 0, 3001, 0)
+    assert bwd_plan_ex(100, 3001, lay).variant == bnd.VARIANT_GENERIC
+    lay = bnd.BwdLayout(4, 3001, 4 * 3001 + 8, 3001, 4 * 3001 + 8, 3001, 4 * 3001 + 1)
+    assert bwd_plan_ex(100, 3001, lay).variant == bnd.VARIANT_GENERIC    # batch strides out of phase
+    lay = bnd.BwdLayout(4, 3001, 4 * 3001 + 8, 3001, 4 * 3001 + 16, 3001, 4 * 3001 + 24)
+    assert bwd_plan_ex(100, 3001, lay).variant == bnd.VARIANT_SHIFTED
+
+
+def test_bwd_shifted_plans_that_do_not_fit_are_rejected():
+    good = bwd_plan_ex(100, 3001, None)
+    base = dict(x=A, w=A, dy=A + 0x10000000, dx=A + 0x20000000)
+    for p, N in ((good.copy(vectors_per_lane=3), 3001),                   # no such instance
+                 (good.copy(block_threads=128, lanes_per_row=128), 3001),  # 128 x 2 chunks < 376
+                 (good.copy(prefetch=2), 3001),
+                 (good, 3000)):                                            # aligned rows: not shifted
+        st = lib.rmsnorm_bwd_with_plan(base["x"], base["w"], base["dy"], A + 0x30000000, base["dx"],
+                                       A + 0x40000000, 100, N, 0.0, BF16, ctypes.byref(p), A + 0x50000000,
+                                       1 << 24, None)
+        assert st == PLAN, (p.as_dict(), N, lib.rmsnorm_last_error().decode())

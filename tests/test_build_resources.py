@@ -38,7 +38,7 @@ def kernels():
 def test_every_family_is_compiled(kernels):
     names = " ".join(kernels)
     for family in ("rmsnorm_wave", "rmsnorm_block", "rmsnorm_wide", "rmsnorm_shifted", "rmsnorm_shifted_wave",
-                   "rmsnorm_generic", "rmsnorm_bwd_wave", "rmsnorm_bwd_block", "rmsnorm_bwd_generic",
+                   "rmsnorm_generic", "rmsnorm_bwd_wave", "rmsnorm_bwd_block", "rmsnorm_bwd_shifted", "rmsnorm_bwd_generic",
                    "rmsnorm_dw_reduce"):
         assert family in names, family
 

@@ -359,3 +359,112 @@ def test_bwd_layout_in_place(bnd):
     _, dwe, dxe, dxs, dws = parity.oracle_bwd_for(xc, w.cpu(), dy_copy.cpu().reshape(-1, N), r32, 0.0, "fp16")
     p = bnd.bwd_plan_query_ex(x, w, dy, out=dy)
     parity.compare_bwd(out.cpu().reshape(-1, N), dw, dxe, dxs, dwe, dws, "fp16", B * S, p.grid, "in place layout")
+
+
+# ---------------------------------------------------------------------------
+# Rows off a 16-byte boundary: the shifted row pass (aligned chunks, weights
+# shifted per row, dw kept per column across rows of different shifts).
+# ---------------------------------------------------------------------------
+TDT = {"bf16": torch.bfloat16, "fp16": torch.float16, "fp32": torch.float32}
+EPV = {"bf16": 8, "fp16": 8, "fp32": 4}
+
+
+def any_case(M, N, dtype, offset, seed, sigma=2.0):
+    """x, w, dy of `dtype` on the CPU and the rstd both sides use (the oracle
+    forward's, rounded to fp32)."""
+    g = torch.Generator().manual_seed(seed)
+    x = (sigma * torch.randn(M, N, generator=g)).to(TDT[dtype])
+    w = (1.0 + 0.1 * torch.randn(N, generator=g)).to(TDT[dtype])
+    dy = torch.randn(M, N, generator=g).to(TDT[dtype])
+    if dtype == "fp32":
+        _, r64 = parity.oracle_fp32(x, w, 1e-6, offset)
+    else:
+        _, r64 = parity.oracle_for(x, w, 1e-6, offset, dtype)
+    return x, w, dy, r64.astype(np.float32)
+
+
+@pytest.mark.parametrize("M,N,dtype,offset", [
+    (300, 3001, "bf16", 1.0), (777, 1001, "fp16", 0.0), (97, 8191, "bf16", 0.0),
+    (33, 16377, "bf16", 1.0), (500, 17, "bf16", 0.0), (1000, 100, "fp16", 1.0),
+    (2000, 257, "bf16", 1.0), (300, 1002, "fp32", 0.0), (50, 8189, "fp32", 1.0), (41, 4097, "fp32", 0.0)])
+def test_bwd_shifted_rule(bnd, M, N, dtype, offset):
+    x, w, dy, r32 = any_case(M, N, dtype, offset, seed=N + M)
+    xg, wg, dyg = x.to(DEV), w.to(DEV), dy.to(DEV)
+    rg = torch.from_numpy(r32).to(DEV)
+    p = bnd.bwd_plan_query(M, N, dtype, xg.data_ptr(), dyg.data_ptr(), dyg.data_ptr())
+    announce("bwd shifted", M, N, dtype, offset, p.as_dict())
+    assert p.variant == bnd.VARIANT_SHIFTED
+    dx, dw = bnd.rmsnorm_bwd(xg, wg, dyg, rg, offset)
+    dx2, dw2 = bnd.rmsnorm_bwd(xg, wg, dyg, rg, offset)
+    torch.cuda.synchronize()
+    _, dwe, dxe, dxs, dws = parity.oracle_bwd_for(x, w, dy, r32, offset, dtype)
+    stats = parity.compare_bwd(dx, dw, dxe, dxs, dwe, dws, dtype, M, p.grid, f"bwd shifted {M}x{N} {dtype}")
+    assert torch.equal(dx, dx2) and torch.equal(dw, dw2)          # the same bits on every run
+    print("bwd shifted", M, N, dtype, stats, flush=True)
+
+
+@pytest.mark.parametrize("M,N,dtype", [(97, 3001, "bf16"), (200, 1001, "fp16"), (60, 1003, "fp32"),
+                                       (150, 33, "bf16")])
+def test_bwd_shifted_every_kernel(bnd, M, N, dtype):
+    x, w, dy, r32 = any_case(M, N, dtype, 1.0, seed=N + 7)
+    xg, wg, dyg = x.to(DEV), w.to(DEV), dy.to(DEV)
+    rg = torch.from_numpy(r32).to(DEV)
+    _, dwe, dxe, dxs, dws = parity.oracle_bwd_for(x, w, dy, r32, 1.0, dtype)
+    base = bnd.bwd_plan_query(M, N, dtype)
+    epv = EPV[dtype]
+    ran = 0
+    for pf in (0, 1):
+        for threads in (64, 128, 256, 512, 1024):
+            for vpt in (1, 2):
+                if threads * vpt * epv < N + epv - 1:
+                    continue
+                for grid in (1, 5, M):
+                    p = base.copy(variant=bnd.VARIANT_SHIFTED, block_threads=threads, vectors_per_lane=vpt,
+                                  prefetch=pf, grid=grid)
+                    dx = torch.empty_like(xg)
+                    dw = torch.full((N,), float("nan"), dtype=torch.float32, device=DEV)
+                    ws = torch.empty(grid * N + 4, dtype=torch.float32, device=DEV)
+                    announce("bwd shifted", M, N, dtype, p.as_dict())
+                    bnd.rmsnorm_bwd_out(xg, wg, dyg, rg, dx, dw, ws, 1.0, plan=p)
+                    torch.cuda.synchronize()
+                    parity.compare_bwd(dx, dw, dxe, dxs, dwe, dws, dtype, M, grid,
+                                       f"bwd shifted {M}x{N} {dtype} {p.as_dict()}")
+                    ran += 1
+    assert ran >= 12, ran
+
+
+def test_bwd_shifted_in_place(bnd):
+    M, N = 300, 3001
+    x, w, dy, r32 = any_case(M, N, "bf16", 1.0, seed=41)
+    xg, wg, dyg = x.to(DEV), w.to(DEV), dy.to(DEV)
+    rg = torch.from_numpy(r32).to(DEV)
+    dw = torch.empty(N, dtype=torch.float32, device=DEV)
+    ws = torch.empty(bnd.bwd_workspace_size(M, N, "bf16") // 4 + 4, dtype=torch.float32, device=DEV)
+    announce("bwd shifted in place")
+    bnd.rmsnorm_bwd_out(xg, wg, dyg, rg, dyg, dw, ws, 1.0)          # dx written over dy
+    torch.cuda.synchronize()
+    e = parity.oracle_bwd_for(x, w, dy, r32, 1.0, "bf16")
+    p = bnd.bwd_plan_query(M, N, "bf16")
+    assert p.variant == bnd.VARIANT_SHIFTED
+    parity.compare_bwd(dyg, dw, e[2], e[3], e[1], e[4], "bf16", M, p.grid, "shifted in place")
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+def test_bwd_shifted_edges_ignore_their_neighbours(bnd, dtype):
+    """Rows 3 elements past a boundary with NaN between them (x and dy), w followed by NaN inside its
+    last 16 bytes, dx into a sentinel buffer: the edge chunks' outside elements and w's tail must
+    not reach c, dx or dw, and nothing outside dx's rows may change."""
+    M, N, S = 120, 1001, 1001 + 3 + 8
+    tdt = TDT[dtype]
+    x0, w0, dy0, _ = any_case(M, N, dtype, 1.0, seed=43)
+    xb = torch.full((M, S), float("nan"), dtype=tdt)
+    xb[:, 3:3 + N] = x0
+    dyb = torch.full((M, S), float("nan"), dtype=tdt)
+    dyb[:, 3:3 + N] = dy0
+    wb = torch.full((N + 16,), float("nan"), dtype=tdt)
+    wb[:N] = w0
+    x, dy, w = xb.to(DEV)[:, 3:3 + N], dyb.to(DEV)[:, 3:3 + N], wb.to(DEV)[:N]
+    dx_base = _filled(M * S + 16, tdt)
+    dx = dx_base.as_strided((M, N), (S, 1), 3)
+    p = _check_layout_bwd(bnd, x, w, dy, dx, dx_base, 1.0, f"shifted edges {dtype}")
+    assert p.variant == bnd.VARIANT_SHIFTED
