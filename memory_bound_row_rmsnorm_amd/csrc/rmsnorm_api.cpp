@@ -582,6 +582,7 @@ constexpr int64_t kBwdPartialsGeneric = 1024;        // row-pass grid cap of the
 constexpr int kBwdWaveSlots[] = {4, 2, 1};
 // Unaligned rows shorter than this take the generic kernel.
 constexpr int64_t kBwdMinShiftedN = 16;
+constexpr int64_t kBwdMaxShiftedWaveChunks = 64;   // one chunk per lane of a 64-lane segment
 
 const KernelEntry* find_bwd_kernel(int variant, int dtype, int lanes, int vpl, int slots, bool prefetch) {
     int n = 0;
@@ -589,7 +590,7 @@ const KernelEntry* find_bwd_kernel(int variant, int dtype, int lanes, int vpl, i
     for (int i = 0; i < n; ++i) {
         const KernelEntry& k = t[i];
         if (k.variant != variant || k.dtype != dtype || k.prefetch != prefetch) continue;
-        if (variant == RMSNORM_VARIANT_WAVE &&
+        if ((variant == RMSNORM_VARIANT_WAVE || variant == RMSNORM_VARIANT_SHIFTED_WAVE) &&
             (k.lanes_per_row != lanes || k.vectors_per_lane != vpl || k.row_slots != slots))
             continue;
         if ((variant == RMSNORM_VARIANT_BLOCK || variant == RMSNORM_VARIANT_SHIFTED) && k.vectors_per_lane != vpl)
@@ -799,6 +800,24 @@ int finish_bwd_plan(rmsnorm_plan_t* p, int64_t M, int64_t N, int dtype, bool vec
         k = find_bwd_kernel(RMSNORM_VARIANT_SHIFTED, dtype, 0, p->vectors_per_lane, 1, pf);
         if (k && static_cast<int64_t>(p->block_threads) * p->vectors_per_lane * epv < N + epv - 1)
             return fail(RMSNORM_ERR_PLAN, "shifted plan does not cover N");
+    } else if (p->variant == RMSNORM_VARIANT_SHIFTED_WAVE) {
+        if (!shifted)
+            return fail(RMSNORM_ERR_PLAN, "the shifted backward kernels need x, dy and dx equally far past a 16-byte "
+                                          "boundary on every row, 16-byte aligned w, rows that are not 16-byte "
+                                          "aligned, and at most 2048 chunks");
+        const int epv = elems_per_vector(dtype);
+        p->vec_elems = epv;
+        if (p->lanes_per_row != 16 && p->lanes_per_row != 32 && p->lanes_per_row != 64)
+            return fail(RMSNORM_ERR_PLAN, "shifted wave plans take 16, 32 or 64 lanes per row");
+        k = find_bwd_kernel(RMSNORM_VARIANT_SHIFTED_WAVE, dtype, p->lanes_per_row, p->vectors_per_lane,
+                            p->row_slots, pf);
+        if (k) {
+            if (static_cast<int64_t>(p->lanes_per_row) * p->vectors_per_lane * epv < N + epv - 1)
+                return fail(RMSNORM_ERR_PLAN, "shifted wave plan does not cover N");
+            if (bwd_wave_lds(p, N) > kBwdMaxLds)
+                return fail(RMSNORM_ERR_PLAN, "wave plan needs more than 64 KiB of LDS for dw partials");
+            p->rows_per_trip = static_cast<int64_t>(p->block_threads / 64) * (64 / p->lanes_per_row) * p->row_slots;
+        }
     } else {
         return fail(RMSNORM_ERR_PLAN, "unknown variant");
     }
@@ -822,7 +841,28 @@ int choose_bwd_plan(int64_t M, int64_t N, bool vec_ok, bool shifted_ok, int dtyp
     std::memset(p, 0, sizeof(*p));
     p->xcd_group = 1;
     const int64_t epv = elems_per_vector(dtype);
-    if (!vec_ok && shifted_ok && N >= kBwdMinShiftedN) {
+    const int64_t shifted_chunks = ceil_div(N + epv - 1, epv);
+    if (!vec_ok && shifted_ok && N >= kBwdMinShiftedN && shifted_chunks <= kBwdMaxShiftedWaveChunks) {
+        // a row per segment of the fewest lanes (16, 32, 64) that hold its
+        // chunks, one chunk per lane; several rows per wave: slots as in the
+        // wave family; a row per wave: two slots (262144 x 257 bf16: 119 us,
+        // against 132 us with one slot and the next trip loaded ahead;
+        // 65536 x 300 bf16: 35.6 against 39.1 us).  No prefetching form is
+        // taken: with the rows of a trip loaded together it gained nothing.
+        p->variant = RMSNORM_VARIANT_SHIFTED_WAVE;
+        p->block_threads = kBwdWaveThreads;
+        p->lanes_per_row = shifted_chunks <= 16 ? 16 : (shifted_chunks <= 32 ? 32 : 64);
+        p->vectors_per_lane = 1;
+        const int64_t per_slot = N * elem_size(dtype) * (64 / p->lanes_per_row);
+        p->row_slots = p->lanes_per_row == 64 ? 2 : 1;
+        for (int sl : kBwdWaveSlots) {
+            if (p->lanes_per_row < 64 && sl * per_slot <= kWaveBytesInFlight &&
+                find_bwd_kernel(RMSNORM_VARIANT_SHIFTED_WAVE, dtype, p->lanes_per_row, 1, sl, false)) {
+                p->row_slots = sl;
+                break;
+            }
+        }
+    } else if (!vec_ok && shifted_ok && N >= kBwdMinShiftedN) {
         // one row per workgroup: one chunk per thread up to 128 chunks, then
         // the fewest threads (up to 1024) that hold the row with at most 2
         // per thread (16384 x 1001 bf16: 37.8 us with 128 x 1 against 44.6 us
@@ -866,7 +906,7 @@ int choose_bwd_plan(int64_t M, int64_t N, bool vec_ok, bool shifted_ok, int dtyp
         p->vectors_per_lane = static_cast<int>(ceil_div(nvec, p->block_threads));
     }
     int64_t rows_per_trip = 1;
-    if (p->variant == RMSNORM_VARIANT_WAVE)
+    if (p->variant == RMSNORM_VARIANT_WAVE || p->variant == RMSNORM_VARIANT_SHIFTED_WAVE)
         rows_per_trip = static_cast<int64_t>(p->block_threads / 64) * (64 / p->lanes_per_row) * p->row_slots;
     const int64_t need = M > 0 ? ceil_div(M, rows_per_trip) : 1;
     int64_t cap = kBwdPartialsGeneric;
@@ -913,7 +953,8 @@ int launch_bwd(const KernelEntry* k, const rmsnorm_plan_t* p, const void* x, con
         a.dy_bs = L.dy_bs;
         a.dx_bs = L.dx_bs;
         void* args[] = {&a};
-        const size_t lds = p->variant == RMSNORM_VARIANT_WAVE ? static_cast<size_t>(bwd_wave_lds(p, N)) : 0;
+        const bool wave = p->variant == RMSNORM_VARIANT_WAVE || p->variant == RMSNORM_VARIANT_SHIFTED_WAVE;
+        const size_t lds = wave ? static_cast<size_t>(bwd_wave_lds(p, N)) : 0;
         hipError_t e = hipLaunchKernel(k->func, dim3(static_cast<unsigned>(p->grid)),
                                        dim3(static_cast<unsigned>(p->block_threads)), args, lds, s);
         if (e != hipSuccess)

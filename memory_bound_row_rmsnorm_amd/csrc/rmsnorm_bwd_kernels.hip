@@ -519,6 +519,192 @@ __global__ __launch_bounds__(1024) void rmsnorm_bwd_shifted(BwdArgs a) {
 }
 
 // ---------------------------------------------------------------------------
+// Row pass, shifted wave family: short rows off a 16-byte boundary (at most
+// LANES chunks) with a row per segment of LANES lanes (16, 32 or 64) and
+// SLOTS slots of 64 / LANES rows per wave per trip; lane li of a segment holds
+// chunk li of its row and keeps column vector li of dw.  As in the shifted
+// kernel the weights are funnel-shifted into each row's chunk frame and the
+// products of chunk li + 1 come from the lane above; a segment's last lane
+// has none (with one chunk per lane, its column vector's upper elements lie
+// past the row).  With 64 lanes a row's shift is uniform in its wave and both
+// shifts branch on it; with several rows per wave every lane shifts by its own
+// row's distance past a boundary (funnel_lane for the weights, a three-stage
+// select for the products).  No barrier until the end, where the partials of
+// the segments and waves are added in LDS in a fixed order, as in the wave
+// family.  Dynamic LDS: (waves per workgroup) x (64 / LANES) x N floats.
+// ---------------------------------------------------------------------------
+// add_columns() for a shift that differs between lanes: the pair (cur, nxt)
+// shifted down by al elements in stages of 4, 2 and 1 (whole-vector selects
+// between a value and its shuffle, so the pair stays in registers), then
+// acc[i] += r * element i.
+typedef float f32x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+__device__ __forceinline__ void add_columns_lane(float (&acc)[8], const float (&cur)[8], const float (&nxt)[8],
+                                                 int al, float r) {
+    f32x16 W = {cur[0], cur[1], cur[2], cur[3], cur[4], cur[5], cur[6], cur[7],
+                nxt[0], nxt[1], nxt[2], nxt[3], nxt[4], nxt[5], nxt[6], nxt[7]};
+    const f32x16 S4 = __builtin_shufflevector(W, W, 4, 5, 6, 7, 8, 9, 10, 11, 12, 13, 14, 15, 15, 15, 15, 15);
+    W = (al & 4) ? S4 : W;
+    const f32x16 S2 = __builtin_shufflevector(W, W, 2, 3, 4, 5, 6, 7, 8, 9, 10, 11, 12, 13, 14, 15, 15, 15);
+    W = (al & 2) ? S2 : W;
+    const f32x16 S1 = __builtin_shufflevector(W, W, 1, 2, 3, 4, 5, 6, 7, 8, 9, 10, 11, 12, 13, 14, 15, 15);
+    W = (al & 1) ? S1 : W;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) acc[i] = __builtin_fmaf(W[i], r, acc[i]);
+}
+
+__device__ __forceinline__ void add_columns_lane(float (&acc)[4], const float (&cur)[4], const float (&nxt)[4],
+                                                 int al, float r) {
+    f32x8 W = {cur[0], cur[1], cur[2], cur[3], nxt[0], nxt[1], nxt[2], nxt[3]};
+    const f32x8 S2 = __builtin_shufflevector(W, W, 2, 3, 4, 5, 6, 7, 7, 7);
+    W = (al & 2) ? S2 : W;
+    const f32x8 S1 = __builtin_shufflevector(W, W, 1, 2, 3, 4, 5, 6, 7, 7);
+    W = (al & 1) ? S1 : W;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) acc[i] = __builtin_fmaf(W[i], r, acc[i]);
+}
+
+template <class D, int LANES, int SLOTS, bool PREFETCH>
+__global__ __launch_bounds__(1024) void rmsnorm_bwd_shifted_wave(BwdArgs a) {
+    typedef typename D::elem_t E;
+    constexpr int EPV = D::EPV;
+    constexpr int SEG = 64 / LANES;
+    constexpr int ROWS = SEG * SLOTS;
+    extern __shared__ float lds_part[];
+    const E* x = static_cast<const E*>(a.x);
+    const E* dy = static_cast<const E*>(a.dy);
+    E* dx = static_cast<E*>(a.dx);
+    const u32x4* __restrict__ w = static_cast<const u32x4*>(a.w);
+    const float* __restrict__ rstd = a.rstd;
+    const int64_t M = a.M;
+    const int n = static_cast<int>(a.N);
+    const int nvec_w = (n + EPV - 1) / EPV;
+    const int lane = threadIdx.x & 63;
+    const int seg = lane / LANES;
+    const int li = lane % LANES;
+    const int wpb = a.threads >> 6;
+    const int wid = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
+    const int64_t nwaves = a.grid * wpb;
+
+    auto wvec = [&](int k) -> u32x4 {
+        if (k < 0 || k >= nvec_w) return kZero;
+        return k == nvec_w - 1 ? keep_row<D>(w[k], k * EPV, n) : w[k];
+    };
+    const u32x4 wlo = wvec(li - 1), whi = wvec(li);
+    float dwp[EPV];
+#pragma unroll
+    for (int k = 0; k < EPV; ++k) dwp[k] = 0.0f;
+
+    // distance of row m's start past a 16-byte boundary, in elements
+    auto shift_of = [&](const E* p) -> int {
+        const int s = static_cast<int>((reinterpret_cast<uintptr_t>(p) & 15u) / sizeof(E));
+        if constexpr (LANES == 64) return __builtin_amdgcn_readfirstlane(s);
+        else return s;
+    };
+    auto load_trip = [&](u32x4 (&xd)[SLOTS], u32x4 (&dd)[SLOTS], float (&r)[SLOTS], int (&al)[SLOTS],
+                         int64_t gg) {
+#pragma unroll
+        for (int s = 0; s < SLOTS; ++s) {
+            const int64_t row = gg * ROWS + seg + s * SEG;
+            const bool live = row < M;
+            const RowOff o = row_offsets(a, live ? row : 0);
+            const int as = shift_of(x + o.x);
+            const int nch = (as + n + EPV - 1) / EPV;
+            const u32x4* xc = reinterpret_cast<const u32x4*>(x + o.x - as);
+            const u32x4* dc = reinterpret_cast<const u32x4*>(dy + o.dy - as);
+            xd[s] = (live && li < nch) ? stream_load(xc + li) : kZero;
+            dd[s] = (live && li < nch) ? stream_load(dc + li) : kZero;
+            r[s] = live ? rstd[row] : 0.0f;
+            al[s] = as;
+        }
+    };
+
+    int64_t gi = static_cast<int64_t>(blockIdx.x) * wpb + wid;
+    u32x4 xd[SLOTS], dd[SLOTS];
+    float r[SLOTS];
+    int al[SLOTS];
+    if (PREFETCH && gi * ROWS < M) load_trip(xd, dd, r, al, gi);
+    while (gi * ROWS < M) {
+        const int64_t gn = gi + nwaves;
+        u32x4 xn[SLOTS], dn[SLOTS];
+        float rn[SLOTS];
+        int aln[SLOTS];
+        if constexpr (PREFETCH) {
+            if (gn * ROWS < M) load_trip(xn, dn, rn, aln, gn);
+        } else {
+            load_trip(xd, dd, r, al, gi);
+        }
+#pragma unroll
+        for (int s = 0; s < SLOTS; ++s) {
+            const int64_t row = gi * ROWS + seg + s * SEG;
+            const bool live = row < M;
+            const int as = al[s];
+            const int j0 = li * EPV - as;
+            u32x4 xv4 = xd[s], dv4 = dd[s];
+            if (j0 < 0 || j0 + EPV > n) {
+                xv4 = keep_row<D>(xv4, j0, n);
+                dv4 = keep_row<D>(dv4, j0, n);
+            }
+            float g[EPV], d[EPV], xv[EPV], o[EPV], p[EPV], pn[EPV];
+            if constexpr (LANES == 64) widen_g<D>(g, funnel<D>(wlo, whi, EPV - as), a.offset);
+            else widen_g<D>(g, funnel_lane<D>(wlo, whi, EPV - as), a.offset);
+            const float cm = segment_allreduce<LANES>(dot_dgx<D>(dv4, xv4, g, 0.0f)) * a.inv_n;
+            const float rs = r[s];
+            const float r2c = rs * rs * cm;
+            D::widen(dv4, d);
+            D::widen(xv4, xv);
+#pragma unroll
+            for (int k = 0; k < EPV; ++k) {
+                o[k] = rs * (g[k] * d[k] - r2c * xv[k]);
+                p[k] = d[k] * xv[k];
+            }
+            const int nch = (as + n + EPV - 1) / EPV;
+            if (live && li < nch) {
+                u32x4* oc = reinterpret_cast<u32x4*>(dx + row_offsets(a, row).dx - as);
+                const u32x4 ov = D::narrow(o);
+                if (j0 < 0 || j0 + EPV > n) store_edge<D>(oc + li, ov, j0, n);
+                else stream_store(oc + li, ov);
+            }
+#pragma unroll
+            for (int k = 0; k < EPV; ++k) {
+                const float up = from_lane_above(p[k], 0.0f);
+                pn[k] = li == LANES - 1 ? 0.0f : up;
+            }
+            if constexpr (LANES == 64) add_columns<EPV>(dwp, p, pn, as, rs);
+            else add_columns_lane(dwp, p, pn, as, rs);
+        }
+        gi = gn;
+        if constexpr (PREFETCH) {
+#pragma unroll
+            for (int s = 0; s < SLOTS; ++s) {
+                xd[s] = xn[s];
+                dd[s] = dn[s];
+                r[s] = rn[s];
+                al[s] = aln[s];
+            }
+        }
+    }
+
+    // every segment of every wave holds column vectors 0 .. LANES - 1: add
+    // them in a fixed order through LDS, then one partial row per workgroup
+    float* mine = lds_part + static_cast<int64_t>(wid * SEG + seg) * n;
+    if (li < nvec_w) {
+#pragma unroll
+        for (int k = 0; k < EPV; ++k)
+            if (li * EPV + k < n) mine[li * EPV + k] = dwp[k];
+    }
+    __syncthreads();
+    const int parts = wpb * SEG;
+    float* dst = a.partials + static_cast<int64_t>(blockIdx.x) * n;
+    for (int col = threadIdx.x; col < n; col += a.threads) {
+        float acc = lds_part[col];
+        for (int i = 1; i < parts; ++i) acc += lds_part[static_cast<int64_t>(i) * n + col];
+        dst[col] = acc;
+    }
+}
+
+// ---------------------------------------------------------------------------
 // Row pass, generic (any N and alignment): one row per workgroup per trip,
 // element-wide accesses, the row read twice (c first, then dx), and the
 // workgroup's partial row of dw updated in the workspace in place (each
@@ -645,10 +831,17 @@ __global__ __launch_bounds__(16 * SPLIT) void rmsnorm_dw_reduce(const float* __r
     {RMSNORM_VARIANT_SHIFTED, DT, 0, V, 1, P, false,                                                  \
      reinterpret_cast<const void*>(&rmsnorm_bwd_shifted<D, V, P>),                             \
      "rmsnorm_bwd_shifted<" #D "," #V "," #P ">"}
+#define RMS_BWD_SHIFTED_WAVE(D, DT, L, S, P)                                                   \
+    {RMSNORM_VARIANT_SHIFTED_WAVE, DT, L, 1, S, P, false,                                             \
+     reinterpret_cast<const void*>(&rmsnorm_bwd_shifted_wave<D, L, S, P>),                     \
+     "rmsnorm_bwd_shifted_wave<" #D "," #L "," #S "," #P ">"}
+#define RMS_BWD_SHIFTED_WAVE2(D, DT, L, S)                                                     \
+    RMS_BWD_SHIFTED_WAVE(D, DT, L, S, false), RMS_BWD_SHIFTED_WAVE(D, DT, L, S, true)
 // Only instances that fit 128 VGPRs without scratch: the block family holds
 // at most two vectors of x and dy per thread (rows up to 1024 x 2 vectors:
-// 16384 16-bit or 8192 fp32 elements), and the widest wave shapes have no
-// prefetching form.
+// 16384 16-bit or 8192 fp32 elements), and the widest wave shapes and the
+// 4-slot shifted wave shapes with several rows per wave have no prefetching
+// form.
 #define RMS_BWD_FAMILY(D, DT)                                                                  \
     RMS_BWD_WAVE2(D, DT, 16, 1, 1), RMS_BWD_WAVE2(D, DT, 16, 1, 2),                            \
     RMS_BWD_WAVE2(D, DT, 32, 1, 1), RMS_BWD_WAVE2(D, DT, 32, 1, 2),                            \
@@ -659,6 +852,11 @@ __global__ __launch_bounds__(16 * SPLIT) void rmsnorm_dw_reduce(const float* __r
     RMS_BWD_BLOCK(D, DT, 2, false), RMS_BWD_BLOCK(D, DT, 2, true),                             \
     RMS_BWD_SHIFTED(D, DT, 1, false), RMS_BWD_SHIFTED(D, DT, 1, true),                         \
     RMS_BWD_SHIFTED(D, DT, 2, false), RMS_BWD_SHIFTED(D, DT, 2, true),                         \
+    RMS_BWD_SHIFTED_WAVE2(D, DT, 16, 1), RMS_BWD_SHIFTED_WAVE2(D, DT, 16, 2),                   \
+    RMS_BWD_SHIFTED_WAVE(D, DT, 16, 4, false), RMS_BWD_SHIFTED_WAVE2(D, DT, 32, 1),             \
+    RMS_BWD_SHIFTED_WAVE2(D, DT, 32, 2), RMS_BWD_SHIFTED_WAVE(D, DT, 32, 4, false),             \
+    RMS_BWD_SHIFTED_WAVE2(D, DT, 64, 1), RMS_BWD_SHIFTED_WAVE2(D, DT, 64, 2),                   \
+    RMS_BWD_SHIFTED_WAVE2(D, DT, 64, 4),                                                       \
     {RMSNORM_VARIANT_GENERIC, DT, 0, 0, 1, false, false,                                              \
      reinterpret_cast<const void*>(&rmsnorm_bwd_generic<D>), "rmsnorm_bwd_generic<" #D ">"}
 

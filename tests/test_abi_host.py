@@ -597,8 +597,19 @@ def test_bwd_shifted_plans():
     p = bwd_plan_ex(32768, 8191, None)
     assert (p.variant, p.block_threads, p.vectors_per_lane, p.grid, p.prefetch) == \
         (bnd.VARIANT_SHIFTED, 1024, 2, 256, 1)
-    p = bwd_plan_ex(100, 17, None)                 # 3 chunks: one wave
-    assert (p.variant, p.block_threads, p.vectors_per_lane) == (bnd.VARIANT_SHIFTED, 64, 1)
+    # rows of at most 64 chunks: a row per 16/32/64-lane segment, one chunk per lane
+    p = bwd_plan_ex(100, 17, None)                 # 3 chunks
+    assert (p.variant, p.lanes_per_row, p.vectors_per_lane, p.row_slots, p.block_threads) == \
+        (bnd.VARIANT_SHIFTED_WAVE, 16, 1, 4, 1024)
+    p = bwd_plan_ex(262144, 100, None)             # 13 chunks, 4 slots of four rows per wave
+    assert (p.lanes_per_row, p.row_slots, p.rows_per_trip, p.grid, p.prefetch) == (16, 4, 256, 256, 0)
+    p = bwd_plan_ex(16384, 249, None)              # 32 chunks
+    assert (p.variant, p.lanes_per_row, p.row_slots) == (bnd.VARIANT_SHIFTED_WAVE, 32, 4)
+    p = bwd_plan_ex(262144, 257, None)             # 33 chunks: a row per wave, two slots
+    assert (p.variant, p.lanes_per_row, p.row_slots, p.grid, p.prefetch) == (bnd.VARIANT_SHIFTED_WAVE, 64, 2, 256, 0)
+    assert bwd_plan_ex(16384, 505, None).variant == bnd.VARIANT_SHIFTED_WAVE   # 64 chunks
+    p = bwd_plan_ex(16384, 506, None)              # 65 chunks: one row per workgroup
+    assert (p.variant, p.block_threads, p.vectors_per_lane) == (bnd.VARIANT_SHIFTED, 128, 1)
     p = bwd_plan_ex(16384, 1001, None)             # 126 chunks: one per thread
     assert (p.variant, p.block_threads, p.vectors_per_lane) == (bnd.VARIANT_SHIFTED, 128, 1)
     p = bwd_plan_ex(16384, 1017, None)             # 128 chunks (1017 + 7 elements)
@@ -630,7 +641,13 @@ def test_bwd_shifted_plans():
 def test_bwd_shifted_plans_that_do_not_fit_are_rejected():
     good = bwd_plan_ex(100, 3001, None)
     base = dict(x=A, w=A, dy=A + 0x10000000, dx=A + 0x20000000)
+    sw = bwd_plan_ex(100, 300, None)
     for p, N in ((good.copy(vectors_per_lane=3), 3001),                   # no such instance
+                 (sw.copy(lanes_per_row=32), 300),                         # 32 lanes x 1 chunk < 39
+                 (sw.copy(lanes_per_row=128), 300),
+                 (sw.copy(vectors_per_lane=2), 300),                       # one chunk per lane only
+                 (sw.copy(row_slots=4, prefetch=1, lanes_per_row=16), 100),  # no such instance
+                 (sw, 512),                                                # aligned rows
                  (good.copy(block_threads=128, lanes_per_row=128), 3001),  # 128 x 2 chunks < 376
                  (good.copy(prefetch=2), 3001),
                  (good, 3000)):                                            # aligned rows: not shifted

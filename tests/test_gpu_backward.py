@@ -386,14 +386,18 @@ def any_case(M, N, dtype, offset, seed, sigma=2.0):
 @pytest.mark.parametrize("M,N,dtype,offset", [
     (300, 3001, "bf16", 1.0), (777, 1001, "fp16", 0.0), (97, 8191, "bf16", 0.0),
     (33, 16377, "bf16", 1.0), (500, 17, "bf16", 0.0), (1000, 100, "fp16", 1.0),
-    (2000, 257, "bf16", 1.0), (300, 1002, "fp32", 0.0), (50, 8189, "fp32", 1.0), (41, 4097, "fp32", 0.0)])
+    (2000, 257, "bf16", 1.0), (300, 1002, "fp32", 0.0), (50, 8189, "fp32", 1.0), (41, 4097, "fp32", 0.0),
+    (3000, 249, "bf16", 0.0), (777, 61, "fp32", 1.0), (600, 505, "fp16", 0.0), (5000, 36, "bf16", 1.0),
+    (4099, 300, "bf16", 1.0)])
 def test_bwd_shifted_rule(bnd, M, N, dtype, offset):
     x, w, dy, r32 = any_case(M, N, dtype, offset, seed=N + M)
     xg, wg, dyg = x.to(DEV), w.to(DEV), dy.to(DEV)
     rg = torch.from_numpy(r32).to(DEV)
     p = bnd.bwd_plan_query(M, N, dtype, xg.data_ptr(), dyg.data_ptr(), dyg.data_ptr())
     announce("bwd shifted", M, N, dtype, offset, p.as_dict())
-    assert p.variant == bnd.VARIANT_SHIFTED
+    epv = EPV[dtype]
+    chunks = -(-(N + epv - 1) // epv)
+    assert p.variant == (bnd.VARIANT_SHIFTED_WAVE if chunks <= 64 else bnd.VARIANT_SHIFTED)
     dx, dw = bnd.rmsnorm_bwd(xg, wg, dyg, rg, offset)
     dx2, dw2 = bnd.rmsnorm_bwd(xg, wg, dyg, rg, offset)
     torch.cuda.synchronize()
@@ -403,8 +407,22 @@ def test_bwd_shifted_rule(bnd, M, N, dtype, offset):
     print("bwd shifted", M, N, dtype, stats, flush=True)
 
 
+def shifted_wave_candidates(bnd, base, N, epv):
+    out = []
+    for pf in (0, 1):
+        for lanes in (16, 32, 64):
+            for slots in (1, 2, 4):
+                for threads in (256, 1024):
+                    if lanes * epv >= N + epv - 1:
+                        out.append(base.copy(variant=bnd.VARIANT_SHIFTED_WAVE, lanes_per_row=lanes,
+                                             vectors_per_lane=1, row_slots=slots, block_threads=threads,
+                                             prefetch=pf))
+    return out
+
+
 @pytest.mark.parametrize("M,N,dtype", [(97, 3001, "bf16"), (200, 1001, "fp16"), (60, 1003, "fp32"),
-                                       (150, 33, "bf16")])
+                                       (150, 33, "bf16"), (777, 100, "bf16"), (500, 250, "fp16"),
+                                       (300, 61, "fp32"), (333, 505, "bf16")])
 def test_bwd_shifted_every_kernel(bnd, M, N, dtype):
     x, w, dy, r32 = any_case(M, N, dtype, 1.0, seed=N + 7)
     xg, wg, dyg = x.to(DEV), w.to(DEV), dy.to(DEV)
@@ -430,6 +448,23 @@ def test_bwd_shifted_every_kernel(bnd, M, N, dtype):
                     parity.compare_bwd(dx, dw, dxe, dxs, dwe, dws, dtype, M, grid,
                                        f"bwd shifted {M}x{N} {dtype} {p.as_dict()}")
                     ran += 1
+    for plan in shifted_wave_candidates(bnd, base, N, epv):
+        for grid in (1, 3, M):
+            p = plan.copy(grid=grid)
+            dx = torch.empty_like(xg)
+            dw = torch.full((N,), float("nan"), dtype=torch.float32, device=DEV)
+            ws = torch.empty(grid * N + 4, dtype=torch.float32, device=DEV)
+            announce("bwd shifted wave", M, N, dtype, p.as_dict())
+            try:
+                bnd.rmsnorm_bwd_out(xg, wg, dyg, rg, dx, dw, ws, 1.0, plan=p)
+            except bnd.RmsnormError as e:
+                if e.status == 8:
+                    continue
+                raise
+            torch.cuda.synchronize()
+            parity.compare_bwd(dx, dw, dxe, dxs, dwe, dws, dtype, M, grid,
+                               f"bwd shifted wave {M}x{N} {dtype} {p.as_dict()}")
+            ran += 1
     assert ran >= 12, ran
 
 
@@ -449,12 +484,12 @@ def test_bwd_shifted_in_place(bnd):
     parity.compare_bwd(dyg, dw, e[2], e[3], e[1], e[4], "bf16", M, p.grid, "shifted in place")
 
 
-@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
-def test_bwd_shifted_edges_ignore_their_neighbours(bnd, dtype):
+@pytest.mark.parametrize("dtype,N", [("bf16", 1001), ("fp32", 1001), ("bf16", 100), ("fp32", 61)])
+def test_bwd_shifted_edges_ignore_their_neighbours(bnd, dtype, N):
     """Rows 3 elements past a boundary with NaN between them (x and dy), w followed by NaN inside its
     last 16 bytes, dx into a sentinel buffer: the edge chunks' outside elements and w's tail must
     not reach c, dx or dw, and nothing outside dx's rows may change."""
-    M, N, S = 120, 1001, 1001 + 3 + 8
+    M, S = 120, N + 3 + 8
     tdt = TDT[dtype]
     x0, w0, dy0, _ = any_case(M, N, dtype, 1.0, seed=43)
     xb = torch.full((M, S), float("nan"), dtype=tdt)
@@ -466,5 +501,5 @@ def test_bwd_shifted_edges_ignore_their_neighbours(bnd, dtype):
     x, dy, w = xb.to(DEV)[:, 3:3 + N], dyb.to(DEV)[:, 3:3 + N], wb.to(DEV)[:N]
     dx_base = _filled(M * S + 16, tdt)
     dx = dx_base.as_strided((M, N), (S, 1), 3)
-    p = _check_layout_bwd(bnd, x, w, dy, dx, dx_base, 1.0, f"shifted edges {dtype}")
-    assert p.variant == bnd.VARIANT_SHIFTED
+    p = _check_layout_bwd(bnd, x, w, dy, dx, dx_base, 1.0, f"shifted edges {dtype} {N}")
+    assert p.variant in (bnd.VARIANT_SHIFTED, bnd.VARIANT_SHIFTED_WAVE)
