@@ -84,14 +84,16 @@ typedef enum rmsnorm_variant {
     RMSNORM_VARIANT_WIDE = 6     /* aligned rows wider than the block family holds: one row per
                                     workgroup in tiles of block_threads * vectors_per_lane
                                     vectors, squares summed in a first pass, the row read again
-                                    (from the caches) to normalise */
+                                    (from the caches) to normalise.  Backward: one tile per
+                                    row (dw of every vector in registers), c formed in a first
+                                    pass, dx in a second that reads x and dy again */
 } rmsnorm_variant_t;
 
 /*
  * Launch plan: which kernel runs and how the rows are spread over the chip.
  *
  *   variant           RMSNORM_VARIANT_WAVE / _BLOCK / _GENERIC / _SHIFTED /
- *                     _SHIFTED_WAVE
+ *                     _SHIFTED_WAVE / _WIDE
  *   vec_elems         elements per lane access: 16 bytes' worth, 8 (bf16, fp16)
  *                     or 4 (fp32), for every family but GENERIC (1)
  *   lanes_per_row     WAVE: lanes sharing one row (16, 32 or 64); SHIFTED_WAVE:
@@ -329,12 +331,13 @@ typedef struct rmsnorm_bwd_layout {
  * The general backward: rows placed by `layout` (NULL = contiguous [M, N]),
  * an optional explicit plan (NULL = the library's, as rmsnorm_bwd), the
  * workspace as above.  dx may be exactly dy with the same row and batch
- * strides (in place).  The 16-byte kernels run when x, w, dy and dx are
- * 16-byte aligned, N is a multiple of vec_elems and every stride keeps rows
- * aligned; the shifted kernel (variant RMSNORM_VARIANT_SHIFTED) when rows are
- * not 16-byte aligned but x, dy and dx sit equally far past a 16-byte
- * boundary on every row, w is 16-byte aligned and N >= 16 (at most 2048
- * 16-byte chunks per row); the generic kernel otherwise.  Errors as
+ * strides (in place).  The 16-byte kernels (wave, block, wide) run when x, w,
+ * dy and dx are 16-byte aligned, N is a multiple of vec_elems, every stride
+ * keeps rows aligned and a row has at most 32768 16-bit or 24576 fp32
+ * elements; the shifted kernels (RMSNORM_VARIANT_SHIFTED_WAVE up
+ * to 64 chunks, RMSNORM_VARIANT_SHIFTED up to 2048) when rows are not
+ * 16-byte aligned but x, dy and dx sit equally far past a 16-byte boundary on
+ * every row, w is 16-byte aligned and N >= 16; the generic kernel otherwise.  Errors as
  * rmsnorm_bwd, plus RMSNORM_ERR_SHAPE for a bad layout.
  */
 int rmsnorm_bwd_ex(const void* x, const void* w, const void* dy, const float* rstd, void* dx,

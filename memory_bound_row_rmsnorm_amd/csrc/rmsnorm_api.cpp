@@ -573,7 +573,11 @@ int launch(const KernelEntry* k, const rmsnorm_plan_t* p, const void* x, const v
 // ---------------------------------------------------------------------------
 // Backward: argument checks, planning, launch.
 // ---------------------------------------------------------------------------
-constexpr int64_t kBwdMaxVectors = 1024LL * 2;      // widest row of the 16-byte backward kernels, in vectors
+constexpr int64_t kBwdMaxVectors = 1024LL * 2;      // widest row the block and shifted kernels hold, in vectors
+constexpr int kBwdWideThreads = 1024;
+// vectors per thread the wide backward kernel is compiled for (dw of more
+// would not fit 128 VGPRs without spilling)
+int bwd_wide_max_vectors(int dtype) { return dtype == RMSNORM_FP32 ? 6 : 4; }
 constexpr int kBwdWaveThreads = 1024;                // 16 waves share one LDS reduction of dw
 constexpr int64_t kBwdMaxLds = 64 * 1024;
 constexpr int64_t kBwdPlanCus = 256;                 // compute units the backward plan assumes
@@ -593,7 +597,8 @@ const KernelEntry* find_bwd_kernel(int variant, int dtype, int lanes, int vpl, i
         if ((variant == RMSNORM_VARIANT_WAVE || variant == RMSNORM_VARIANT_SHIFTED_WAVE) &&
             (k.lanes_per_row != lanes || k.vectors_per_lane != vpl || k.row_slots != slots))
             continue;
-        if ((variant == RMSNORM_VARIANT_BLOCK || variant == RMSNORM_VARIANT_SHIFTED) && k.vectors_per_lane != vpl)
+        if ((variant == RMSNORM_VARIANT_BLOCK || variant == RMSNORM_VARIANT_SHIFTED || variant == RMSNORM_VARIANT_WIDE) &&
+            k.vectors_per_lane != vpl)
             continue;
         return &k;
     }
@@ -696,7 +701,8 @@ int check_bwd_args(const void* x, const void* w, const void* dy, const float* rs
 }
 
 // The 16-byte backward kernels: N a multiple of the vector, 16-byte aligned
-// x, w, dy and dx, strides that keep every row aligned, rows they hold.
+// x, w, dy and dx, strides that keep every row aligned, rows they hold (the
+// wide kernel's widest).
 bool bwd_vector_ok(const void* x, const void* w, const void* dy, const void* dx, int dtype, const BwdLayout& L,
                    int64_t M, int64_t N) {
     const int64_t es = elem_size(dtype);
@@ -704,8 +710,8 @@ bool bwd_vector_ok(const void* x, const void* w, const void* dy, const void* dx,
     const bool rows_ok = (L.x_rs * es) % 16 == 0 && (L.dy_rs * es) % 16 == 0 && (L.dx_rs * es) % 16 == 0;
     const bool batches_ok = L.batches(M) <= 1 ||
                             ((L.x_bs * es) % 16 == 0 && (L.dy_bs * es) % 16 == 0 && (L.dx_bs * es) % 16 == 0);
-    return N % epv == 0 && N / epv <= kBwdMaxVectors && aligned16(x) && aligned16(w) && aligned16(dy) &&
-           aligned16(dx) && rows_ok && batches_ok;
+    return N % epv == 0 && N / epv <= int64_t{kBwdWideThreads} * bwd_wide_max_vectors(dtype) && aligned16(x) &&
+           aligned16(w) && aligned16(dy) && aligned16(dx) && rows_ok && batches_ok;
 }
 
 // The shifted backward kernel: x, dy and dx the same distance past a 16-byte
@@ -745,6 +751,10 @@ int check_workspace(const void* ws, int64_t ws_bytes, int64_t need, const void* 
     return RMSNORM_OK;
 }
 
+const char* const kBwdVecNeeds =
+    "16-byte kernels need N a multiple of vec_elems, at most 4096 vectors (6144 with fp32), 16-byte aligned x, "
+    "w, dy and dx, and strides that keep rows aligned";
+
 int finish_bwd_plan(rmsnorm_plan_t* p, int64_t M, int64_t N, int dtype, bool vec, bool shifted,
                     const KernelEntry** kernel) {
     if (p->block_threads < 64 || p->block_threads > 1024 || p->block_threads % 64 != 0)
@@ -765,8 +775,7 @@ int finish_bwd_plan(rmsnorm_plan_t* p, int64_t M, int64_t N, int dtype, bool vec
     } else if (p->variant == RMSNORM_VARIANT_WAVE || p->variant == RMSNORM_VARIANT_BLOCK) {
         const int epv = elems_per_vector(dtype);
         if (!vec)
-            return fail(RMSNORM_ERR_PLAN, "16-byte kernels need N a multiple of vec_elems, at most 2048 vectors, "
-                                          "16-byte aligned x, w, dy and dx, and strides that keep rows aligned");
+            return fail(RMSNORM_ERR_PLAN, kBwdVecNeeds);
         p->vec_elems = epv;
         if (p->variant == RMSNORM_VARIANT_WAVE) {
             k = find_bwd_kernel(RMSNORM_VARIANT_WAVE, dtype, p->lanes_per_row, p->vectors_per_lane, p->row_slots, pf);
@@ -787,6 +796,15 @@ int finish_bwd_plan(rmsnorm_plan_t* p, int64_t M, int64_t N, int dtype, bool vec
                 p->rows_per_trip = 1;
             }
         }
+    } else if (p->variant == RMSNORM_VARIANT_WIDE) {
+        if (!vec) return fail(RMSNORM_ERR_PLAN, kBwdVecNeeds);
+        p->vec_elems = elems_per_vector(dtype);
+        p->row_slots = 1;
+        p->lanes_per_row = p->block_threads;
+        p->rows_per_trip = 1;
+        k = find_bwd_kernel(RMSNORM_VARIANT_WIDE, dtype, 0, p->vectors_per_lane, 1, pf);
+        if (k && static_cast<int64_t>(p->block_threads) * p->vectors_per_lane * p->vec_elems < N)
+            return fail(RMSNORM_ERR_PLAN, "wide plan does not cover N");
     } else if (p->variant == RMSNORM_VARIANT_SHIFTED) {
         if (!shifted)
             return fail(RMSNORM_ERR_PLAN, "the shifted backward kernel needs x, dy and dx equally far past a 16-byte "
@@ -898,12 +916,18 @@ int choose_bwd_plan(int64_t M, int64_t N, bool vec_ok, bool shifted_ok, int dtyp
                 break;
             }
         }
-    } else {
+    } else if (N / epv <= kBwdMaxVectors) {
         const int64_t nvec = N / epv;
         p->variant = RMSNORM_VARIANT_BLOCK;
         p->row_slots = 1;
         p->block_threads = nvec <= 512 ? 256 : (nvec <= 1024 ? 512 : 1024);
         p->vectors_per_lane = static_cast<int>(ceil_div(nvec, p->block_threads));
+    } else {
+        // rows wider than x and dy can stay in registers: two passes over the row
+        p->variant = RMSNORM_VARIANT_WIDE;
+        p->row_slots = 1;
+        p->block_threads = kBwdWideThreads;
+        p->vectors_per_lane = static_cast<int>(ceil_div(N / epv, kBwdWideThreads));
     }
     int64_t rows_per_trip = 1;
     if (p->variant == RMSNORM_VARIANT_WAVE || p->variant == RMSNORM_VARIANT_SHIFTED_WAVE)

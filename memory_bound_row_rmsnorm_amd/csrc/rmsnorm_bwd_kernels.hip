@@ -317,6 +317,91 @@ __global__ __launch_bounds__(1024) void rmsnorm_bwd_block(BwdArgs a) {
 }
 
 // ---------------------------------------------------------------------------
+// Row pass, wide family: aligned rows too wide for x and dy to stay in a
+// 1024-thread workgroup's registers next to dw (more than 2 vectors per
+// thread).  One row per workgroup per trip, thread t owning vectors v * T + t
+// as in the block family, but x and dy are not held: the first pass reads
+// them (cached loads) and forms c, the second reads them again, from the
+// caches (one row per compute unit in flight, at most 160 KiB of x and dy),
+// and writes dx.  Each thread keeps dw for its VPT column vectors in
+// registers across its rows.  dx may be dy: each element is read, then
+// written, by one thread.
+// ---------------------------------------------------------------------------
+template <class D, int VPT>
+__global__ __launch_bounds__(1024) void rmsnorm_bwd_wide(BwdArgs a) {
+    __shared__ float part[2][16];
+    const u32x4* __restrict__ x = static_cast<const u32x4*>(a.x);
+    const u32x4* __restrict__ w = static_cast<const u32x4*>(a.w);
+    const u32x4* dy = static_cast<const u32x4*>(a.dy);
+    const float* __restrict__ rstd = a.rstd;
+    u32x4* dx = static_cast<u32x4*>(a.dx);
+    const int64_t M = a.M;
+    const int nvec = static_cast<int>(a.N / D::EPV);
+    const int tid = threadIdx.x;
+    const int nt = a.threads;
+    const int lane = tid & 63;
+    const int wid = tid >> 6;
+    const int nw = nt >> 6;
+
+    u32x4 wq[VPT];
+    float dwp[VPT][D::EPV];
+#pragma unroll
+    for (int v = 0; v < VPT; ++v) {
+        const int c = v * nt + tid;
+        wq[v] = c < nvec ? w[c] : kZero;
+#pragma unroll
+        for (int k = 0; k < D::EPV; ++k) dwp[v][k] = 0.0f;
+    }
+
+    int par = 0;
+    for (int64_t row = blockIdx.x; row < M; row += a.grid) {
+        const RowOff o = row_offsets(a, row);
+        const u32x4* xr = vec_at<D>(x, o.x);
+        const u32x4* dr = vec_at<D>(dy, o.dy);
+        const float r = rstd[row];
+        float t = 0.0f;
+#pragma unroll
+        for (int v = 0; v < VPT; ++v) {
+            const int c = v * nt + tid;
+            if (c < nvec) {
+                float g[D::EPV];
+                widen_g<D>(g, wq[v], a.offset);
+                t = dot_dgx<D>(dr[c], xr[c], g, t);
+            }
+        }
+        t = segment_allreduce<64>(t);
+        if (lane == 0) part[par][wid] = t;
+        __syncthreads();
+        float tot = part[par][0];
+        for (int i = 1; i < nw; ++i) tot += part[par][i];
+        const float r2c = r * r * (tot * a.inv_n);
+        u32x4* out = vec_at<D>(dx, o.dx);
+#pragma unroll
+        for (int v = 0; v < VPT; ++v) {
+            const int c = v * nt + tid;
+            if (c < nvec) {
+                float g[D::EPV];
+                widen_g<D>(g, wq[v], a.offset);
+                const u32x4 xq = stream_load(xr + c);
+                const u32x4 dq = stream_load(dr + c);
+                stream_store(out + c, grad_vector<D>(dq, xq, g, r, r2c, dwp[v]));
+            }
+        }
+        par ^= 1;
+    }
+
+    float* dst = a.partials + static_cast<int64_t>(blockIdx.x) * a.N;
+#pragma unroll
+    for (int v = 0; v < VPT; ++v) {
+        const int c = v * nt + tid;
+        if (c < nvec) {
+#pragma unroll
+            for (int k = 0; k < D::EPV; ++k) dst[c * D::EPV + k] = dwp[v][k];
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
 // Row pass, shifted family: rows that do not start on a 16-byte boundary (N
 // not a multiple of the vector, or bases past a boundary), one row per
 // workgroup per trip, thread t holding chunks v * T + t.  The row is read as
@@ -827,6 +912,9 @@ __global__ __launch_bounds__(16 * SPLIT) void rmsnorm_dw_reduce(const float* __r
     {RMSNORM_VARIANT_BLOCK, DT, 0, V, 1, P, false,                                                    \
      reinterpret_cast<const void*>(&rmsnorm_bwd_block<D, V, P>),                               \
      "rmsnorm_bwd_block<" #D "," #V "," #P ">"}
+#define RMS_BWD_WIDE(D, DT, V)                                                                 \
+    {RMSNORM_VARIANT_WIDE, DT, 0, V, 1, false, false,                                                 \
+     reinterpret_cast<const void*>(&rmsnorm_bwd_wide<D, V>), "rmsnorm_bwd_wide<" #D "," #V ">"}
 #define RMS_BWD_SHIFTED(D, DT, V, P)                                                           \
     {RMSNORM_VARIANT_SHIFTED, DT, 0, V, 1, P, false,                                                  \
      reinterpret_cast<const void*>(&rmsnorm_bwd_shifted<D, V, P>),                             \
@@ -841,7 +929,8 @@ __global__ __launch_bounds__(16 * SPLIT) void rmsnorm_dw_reduce(const float* __r
 // at most two vectors of x and dy per thread (rows up to 1024 x 2 vectors:
 // 16384 16-bit or 8192 fp32 elements), and the widest wave shapes and the
 // 4-slot shifted wave shapes with several rows per wave have no prefetching
-// form.
+// form.  The wide family holds dw for up to 4 vectors per thread (rows up to
+// 32768 16-bit elements), 6 with fp32 (24576 elements).
 #define RMS_BWD_FAMILY(D, DT)                                                                  \
     RMS_BWD_WAVE2(D, DT, 16, 1, 1), RMS_BWD_WAVE2(D, DT, 16, 1, 2),                            \
     RMS_BWD_WAVE2(D, DT, 32, 1, 1), RMS_BWD_WAVE2(D, DT, 32, 1, 2),                            \
@@ -850,6 +939,7 @@ __global__ __launch_bounds__(16 * SPLIT) void rmsnorm_dw_reduce(const float* __r
     RMS_BWD_WAVE(D, DT, 64, 2, 2, false),                                                      \
     RMS_BWD_BLOCK(D, DT, 1, false), RMS_BWD_BLOCK(D, DT, 1, true),                             \
     RMS_BWD_BLOCK(D, DT, 2, false), RMS_BWD_BLOCK(D, DT, 2, true),                             \
+    RMS_BWD_WIDE(D, DT, 3), RMS_BWD_WIDE(D, DT, 4),                                            \
     RMS_BWD_SHIFTED(D, DT, 1, false), RMS_BWD_SHIFTED(D, DT, 1, true),                         \
     RMS_BWD_SHIFTED(D, DT, 2, false), RMS_BWD_SHIFTED(D, DT, 2, true),                         \
     RMS_BWD_SHIFTED_WAVE2(D, DT, 16, 1), RMS_BWD_SHIFTED_WAVE2(D, DT, 16, 2),                   \
@@ -866,6 +956,7 @@ static const KernelEntry kBwdTable[] = {
     RMS_BWD_FAMILY(BF16, RMSNORM_BF16),
     RMS_BWD_FAMILY(FP16, RMSNORM_FP16),
     RMS_BWD_FAMILY(F32, RMSNORM_FP32),
+    RMS_BWD_WIDE(F32, RMSNORM_FP32, 5), RMS_BWD_WIDE(F32, RMSNORM_FP32, 6),
 };
 
 const KernelEntry* bwd_kernel_table(int* count) {

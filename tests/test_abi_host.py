@@ -308,12 +308,13 @@ def test_bwd_argument_errors(kwargs, status):
 
 
 @pytest.mark.parametrize("N,variant,lanes,vpl", [(128, 1, 32, 1), (512, 1, 64, 2), (4096, 2, 512, 2),
-                                               (8192, 2, 1024, 2), (8196, 3, 0, 0), (8200, 3, 0, 0),
+                                               (8192, 2, 1024, 2), (8196, 6, 1024, 3), (8200, 6, 1024, 3),
+                                               (24576, 6, 1024, 6), (24580, 3, 0, 0),
                                                (1002, 4, 128, 2), (8189, 4, 1024, 2), (8190, 3, 0, 0)])
 def test_bwd_fp32_plans(N, variant, lanes, vpl):
     """fp32 rows: four elements per 16-byte vector, so the wave family holds 512 and the block
-    family 8192 elements, and the shifted family rows of up to 2048 chunks; wider rows take the
-    generic kernel."""
+    family 8192 elements, the wide family 24576 and the shifted family rows of up to 2048 chunks;
+    wider rows take the generic kernel."""
     p = bnd.Plan()
     assert lib.rmsnorm_bwd_plan_query(4096, N, FP32, None, None, None, 256, ctypes.byref(p)) == OK
     assert p.variant == variant
@@ -349,7 +350,10 @@ def test_bwd_plans_and_workspace():
     p = plan(4096, 16384, FP16)
     assert (p.variant, p.block_threads, p.vectors_per_lane, p.grid, p.prefetch) == (bnd.VARIANT_BLOCK, 1024, 2, 256, 1)
     assert plan(64, 8192).grid == 6                              # 3M/32 bounds the workspace traffic
-    assert plan(10, 16392).variant == bnd.VARIANT_GENERIC      # wider than the 16-byte kernels hold
+    p = plan(10, 16392)                                          # wider than registers hold: two passes
+    assert (p.variant, p.block_threads, p.vectors_per_lane, p.prefetch) == (bnd.VARIANT_WIDE, 1024, 3, 0)
+    assert (plan(4096, 32768).variant, plan(4096, 32768).vectors_per_lane) == (bnd.VARIANT_WIDE, 4)
+    assert plan(10, 32776).variant == bnd.VARIANT_GENERIC      # wider than the 16-byte kernels hold
     assert plan(10, 511).variant == bnd.VARIANT_SHIFTED
     assert plan(10, 512, x=A + 2).variant == bnd.VARIANT_GENERIC
     assert plan(3, 512).grid == 1                               # 3 rows fit one 8-wave workgroup
@@ -654,4 +658,16 @@ def test_bwd_shifted_plans_that_do_not_fit_are_rejected():
         st = lib.rmsnorm_bwd_with_plan(base["x"], base["w"], base["dy"], A + 0x30000000, base["dx"],
                                        A + 0x40000000, 100, N, 0.0, BF16, ctypes.byref(p), A + 0x50000000,
                                        1 << 24, None)
+        assert st == PLAN, (p.as_dict(), N, lib.rmsnorm_last_error().decode())
+
+
+def test_bwd_wide_plans_that_do_not_fit_are_rejected():
+    good = bnd.Plan()
+    assert lib.rmsnorm_bwd_plan_query(100, 24576, BF16, None, None, None, 256, ctypes.byref(good)) == OK
+    assert (good.variant, good.vectors_per_lane, good.grid) == (bnd.VARIANT_WIDE, 3, 9)
+    for p, N in ((good.copy(prefetch=1), 24576),                  # no prefetching form
+                 (good.copy(vectors_per_lane=5), 24576),          # not compiled for 16-bit data
+                 (good.copy(block_threads=512), 24576),           # 512 x 3 vectors < 3072
+                 (good, 24580)):                                  # rows not 16-byte aligned
+        st = lib.rmsnorm_bwd_with_plan(X, W, DY, R, DX, DW, 100, N, 0.0, BF16, ctypes.byref(p), WS, 1 << 24, None)
         assert st == PLAN, (p.as_dict(), N, lib.rmsnorm_last_error().decode())

@@ -77,6 +77,11 @@ def bwd_candidates(bnd, M, N, dtype):
                 if threads * vpt * epv >= N:
                     out.append(base.copy(variant=bnd.VARIANT_BLOCK, block_threads=threads, vectors_per_lane=vpt,
                                          row_slots=1, prefetch=pf))
+    for threads in (256, 512, 1024):
+        for vpt in (3, 4, 6):
+            if threads * vpt * epv >= N:
+                out.append(base.copy(variant=bnd.VARIANT_WIDE, block_threads=threads, vectors_per_lane=vpt,
+                                     row_slots=1, prefetch=0))
     for threads in (64, 256):
         out.append(base.copy(variant=bnd.VARIANT_GENERIC, block_threads=threads, prefetch=0))
     return out
@@ -503,3 +508,75 @@ def test_bwd_shifted_edges_ignore_their_neighbours(bnd, dtype, N):
     dx = dx_base.as_strided((M, N), (S, 1), 3)
     p = _check_layout_bwd(bnd, x, w, dy, dx, dx_base, 1.0, f"shifted edges {dtype} {N}")
     assert p.variant in (bnd.VARIANT_SHIFTED, bnd.VARIANT_SHIFTED_WAVE)
+
+
+
+# ---------------------------------------------------------------------------
+# Aligned rows wider than x and dy can stay in registers: the wide row pass
+# (two passes over each row, dw in registers).
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("M,N,dtype,offset", [
+    (40, 16392, "bf16", 1.0), (33, 18432, "bf16", 0.0), (20, 32768, "fp16", 1.0), (25, 24576, "fp32", 0.0),
+    (30, 8196, "fp32", 1.0), (9, 20480, "bf16", 1.0), (300, 16400, "bf16", 0.0)])
+def test_bwd_wide_rule(bnd, M, N, dtype, offset):
+    x, w, dy, r32 = any_case(M, N, dtype, offset, seed=N + 2 * M)
+    xg, wg, dyg = x.to(DEV), w.to(DEV), dy.to(DEV)
+    rg = torch.from_numpy(r32).to(DEV)
+    p = bnd.bwd_plan_query(M, N, dtype, xg.data_ptr(), dyg.data_ptr(), dyg.data_ptr())
+    announce("bwd wide", M, N, dtype, offset, p.as_dict())
+    assert p.variant == bnd.VARIANT_WIDE
+    dx, dw = bnd.rmsnorm_bwd(xg, wg, dyg, rg, offset)
+    dx2, dw2 = bnd.rmsnorm_bwd(xg, wg, dyg, rg, offset)
+    torch.cuda.synchronize()
+    _, dwe, dxe, dxs, dws = parity.oracle_bwd_for(x, w, dy, r32, offset, dtype)
+    stats = parity.compare_bwd(dx, dw, dxe, dxs, dwe, dws, dtype, M, p.grid, f"bwd wide {M}x{N} {dtype}")
+    assert torch.equal(dx, dx2) and torch.equal(dw, dw2)
+    print("bwd wide", M, N, dtype, stats, flush=True)
+
+
+@pytest.mark.parametrize("M,N,dtype", [(40, 24576, "bf16"), (21, 16392, "fp16"), (17, 12292, "fp32")])
+def test_bwd_wide_every_kernel(bnd, M, N, dtype):
+    x, w, dy, r32 = any_case(M, N, dtype, 1.0, seed=N + 11)
+    xg, wg, dyg = x.to(DEV), w.to(DEV), dy.to(DEV)
+    rg = torch.from_numpy(r32).to(DEV)
+    _, dwe, dxe, dxs, dws = parity.oracle_bwd_for(x, w, dy, r32, 1.0, dtype)
+    base = bnd.bwd_plan_query(M, N, dtype)
+    epv = EPV[dtype]
+    ran = 0
+    for threads in (576, 768, 1024):
+        for vpt in (3, 4, 5, 6):
+            if threads * vpt * epv < N:
+                continue
+            for grid in (1, 5, M):
+                p = base.copy(variant=bnd.VARIANT_WIDE, block_threads=threads, vectors_per_lane=vpt, grid=grid,
+                              prefetch=0)
+                dx = torch.empty_like(xg)
+                dw = torch.full((N,), float("nan"), dtype=torch.float32, device=DEV)
+                ws = torch.empty(grid * N + 4, dtype=torch.float32, device=DEV)
+                announce("bwd wide", M, N, dtype, p.as_dict())
+                try:
+                    bnd.rmsnorm_bwd_out(xg, wg, dyg, rg, dx, dw, ws, 1.0, plan=p)
+                except bnd.RmsnormError as e:
+                    if e.status == 8:
+                        continue
+                    raise
+                torch.cuda.synchronize()
+                parity.compare_bwd(dx, dw, dxe, dxs, dwe, dws, dtype, M, grid, f"bwd wide {M}x{N} {p.as_dict()}")
+                ran += 1
+    assert ran >= 6, ran
+
+
+def test_bwd_wide_in_place(bnd):
+    M, N = 50, 18432
+    x, w, dy, r32 = any_case(M, N, "bf16", 1.0, seed=61)
+    xg, wg, dyg = x.to(DEV), w.to(DEV), dy.to(DEV)
+    rg = torch.from_numpy(r32).to(DEV)
+    dw = torch.empty(N, dtype=torch.float32, device=DEV)
+    ws = torch.empty(bnd.bwd_workspace_size(M, N, "bf16") // 4 + 4, dtype=torch.float32, device=DEV)
+    announce("bwd wide in place")
+    bnd.rmsnorm_bwd_out(xg, wg, dyg, rg, dyg, dw, ws, 1.0)          # dx written over dy
+    torch.cuda.synchronize()
+    e = parity.oracle_bwd_for(x, w, dy, r32, 1.0, "bf16")
+    p = bnd.bwd_plan_query(M, N, "bf16")
+    assert p.variant == bnd.VARIANT_WIDE
+    parity.compare_bwd(dyg, dw, e[2], e[3], e[1], e[4], "bf16", M, p.grid, "wide in place")
