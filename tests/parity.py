@@ -92,8 +92,9 @@ def oracle_for(x_cpu: torch.Tensor, w_cpu: torch.Tensor, eps: float, offset: flo
 # size of the terms it is computed from:
 #   |dx_gpu - dx_exact| <= ulp_dtype(dx_exact) + 2^-16 * (|r g dy| + |r^3 x| mean_j |dy g x|)
 # one ulp for the single rounding to the dtype, and 2^-16 (about 1.5e-5) for
-# fp32 products and a tree of at most 16384 fp32 additions in c (first-order
-# bound (32 + 6 + 16) * 2^-24, with a factor 4 to spare).
+# fp32 products and the additions in c: at most 32 in sequence per thread (rows
+# of up to 32768 elements in the 16-byte kernels), a 6-level wave tree and 16
+# waves (first-order bound (32 + 6 + 16) * 2^-24, with a factor 4 to spare).
 #   |dw_gpu - dw_exact| <= 2 K 2^-24 sum_m |dy x r| + 2^-23 |dw_exact|
 # where K = ceil(M / G) + G + 64 bounds the sequential fp32 additions along
 # any one column (rows of one workgroup, its waves and segments, then the G
@@ -105,13 +106,17 @@ MIN_EXP = {"bf16": -126, "fp16": -14, "fp32": -126}
 
 
 def ulp_of(v: np.ndarray, dtype: str) -> np.ndarray:
-    _, e = np.frexp(np.abs(v))                      # |v| = m 2^e, m in [0.5, 1)
-    exp = np.maximum(e - 1, MIN_EXP[dtype])
-    return np.ldexp(1.0, exp - FRAC_BITS[dtype])
+    """Spacing of the dtype's values at v: 2^(floor(log2 |v|) - fraction bits), and the subnormal
+    spacing 2^(min exponent - fraction bits) at and below the smallest normal (zero included).
+    2^floor(log2 |v|) is |v| with its fp64 fraction bits cleared."""
+    a = np.ascontiguousarray(np.abs(np.asarray(v, dtype=np.float64)))
+    p2 = (a.view(np.uint64) & np.uint64(0x7FF0000000000000)).view(np.float64)
+    return np.maximum(p2, 2.0 ** MIN_EXP[dtype]) * 2.0 ** -FRAC_BITS[dtype]
 
 
-def compare_bwd(dx_gpu: torch.Tensor, dw_gpu: torch.Tensor, dx_exact: np.ndarray, dx_scale: np.ndarray,
-                dw_exact: np.ndarray, dw_scale: np.ndarray, dtype: str, M: int, G: int, what: str = "") -> dict:
+def compare_dx(dx_gpu: torch.Tensor, dx_exact: np.ndarray, dx_scale: np.ndarray, dtype: str,
+               what: str = "") -> float:
+    """dx against the oracle's exact dx with the bound above; returns the largest error / bound."""
     if dtype == "fp32":
         dxg = dx_gpu.cpu().double().numpy().reshape(dx_exact.shape)
     else:
@@ -123,6 +128,13 @@ def compare_bwd(dx_gpu: torch.Tensor, dw_gpu: torch.Tensor, dx_exact: np.ndarray
         i = np.unravel_index(int(np.argmax(np.where(bad, err / bound, 0))), err.shape)
         raise AssertionError(f"{what}: dx off at {i}: gpu {dxg[i]!r} exact {dx_exact[i]!r} bound {bound[i]!r} "
                              f"({int(bad.sum())} elements out of bound)")
+    return float(np.max(err / bound)) if err.size else 0.0
+
+
+def compare_dw(dw_gpu: torch.Tensor, dw_exact: np.ndarray, dw_scale: np.ndarray, M: int, G: int,
+               what: str = "") -> float:
+    """dw against the oracle's dw with the bound above (G = the row pass's grid); returns the
+    largest error / bound."""
     dwg = dw_gpu.cpu().numpy().astype(np.float64)
     K = -(-M // max(G, 1)) + G + 64
     wbound = 2 * K * 2.0 ** -24 * dw_scale + 2.0 ** -23 * np.abs(dw_exact) + 1e-30
@@ -132,8 +144,13 @@ def compare_bwd(dx_gpu: torch.Tensor, dw_gpu: torch.Tensor, dx_exact: np.ndarray
         j = int(np.argmax(np.where(wbad, werr / wbound, 0)))
         raise AssertionError(f"{what}: dw[{j}] gpu {dwg[j]!r} exact {dw_exact[j]!r} bound {wbound[j]!r} "
                              f"({int(wbad.sum())} columns out of bound)")
-    return {"dx_max_err_over_bound": float(np.max(err / bound)) if err.size else 0.0,
-            "dw_max_err_over_bound": float(np.max(werr / wbound)) if werr.size else 0.0}
+    return float(np.max(werr / wbound)) if werr.size else 0.0
+
+
+def compare_bwd(dx_gpu: torch.Tensor, dw_gpu: torch.Tensor, dx_exact: np.ndarray, dx_scale: np.ndarray,
+                dw_exact: np.ndarray, dw_scale: np.ndarray, dtype: str, M: int, G: int, what: str = "") -> dict:
+    return {"dx_max_err_over_bound": compare_dx(dx_gpu, dx_exact, dx_scale, dtype, what),
+            "dw_max_err_over_bound": compare_dw(dw_gpu, dw_exact, dw_scale, M, G, what)}
 
 
 def oracle_bwd_for(x_cpu, w_cpu, dy_cpu, rstd_f32: np.ndarray, offset: float, dtype: str):

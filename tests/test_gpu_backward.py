@@ -60,6 +60,41 @@ def test_bwd_workload(bnd, name):
     print(name, stats, flush=True)
 
 
+@pytest.mark.parametrize("name", list(workloads.WORKLOADS))
+def test_bwd_workload_full_size(bnd, name):
+    """Every workload at full size with the plan the benchmark times: every dx element and every dw
+    column against the oracle, which runs over the rows in chunks (dw summed over the chunks in
+    fp64)."""
+    wl = workloads.WORKLOADS[name]
+    M, N = wl.M, wl.N
+    announce("bwd full-size", name, M, N, wl.dtype)
+    x, w = workloads.make_inputs(wl, seed=0)
+    dy = workloads.make_grad(wl, seed=0)
+    _, r64 = parity.oracle_for(x, w, wl.eps, wl.offset, wl.dtype)
+    r32 = r64.astype(np.float32)
+    xg, wg, dyg = x.to(DEV), w.to(DEV), dy.to(DEV)
+    rg = torch.from_numpy(r32).to(DEV)
+    p = bnd.bwd_plan_query(M, N, wl.dtype, xg.data_ptr(), dyg.data_ptr(), xg.data_ptr())
+    dx, dw = bnd.rmsnorm_bwd(xg, wg, dyg, rg, wl.offset)
+    torch.cuda.synchronize()
+    del xg, dyg
+    dx = dx.cpu()
+    xb, wb, dyb = workloads.to_bits(x), workloads.to_bits(w), workloads.to_bits(dy)
+    rows = max(1, (1 << 24) // N)
+    dwe = np.zeros(N)
+    dws = np.zeros(N)
+    dx_worst = 0.0
+    for m0 in range(0, M, rows):
+        m1 = min(M, m0 + rows)
+        _, dw_c, ex, sc, ws_c = parity.oracle.rmsnorm_bwd(xb[m0:m1], wb, dyb[m0:m1], r32[m0:m1], wl.offset,
+                                                          wl.dtype, want_exact=True)
+        dx_worst = max(dx_worst, parity.compare_dx(dx[m0:m1], ex, sc, wl.dtype, f"{name} rows {m0}:{m1}"))
+        dwe += dw_c
+        dws += ws_c
+    dw_worst = parity.compare_dw(dw, dwe, dws, M, p.grid, name)
+    print(name, p.as_dict(), {"dx_max_err_over_bound": dx_worst, "dw_max_err_over_bound": dw_worst}, flush=True)
+
+
 def bwd_candidates(bnd, M, N, dtype):
     base = bnd.bwd_plan_query(M, N, dtype)
     epv = 4 if dtype == "fp32" else 8
