@@ -140,6 +140,18 @@ def traffic_from_counters(wl, name: str, directory: str) -> dict:
     }
 
 
+def host_cpu_model() -> str:
+    """The host processor's model name (Linux /proc/cpuinfo), or "unknown"."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(wl, x_cpu, w_cpu, seconds: float, threads: int = 0):
     import oracle
     from memory_bound_row_rmsnorm_amd import workloads
@@ -161,6 +173,7 @@ def cpu_baseline(wl, x_cpu, w_cpu, seconds: float, threads: int = 0):
         "value": round(gbps, 3),
         "unit": "GB/s",
         "cores": o.max_threads(),
+        "host_cpu": host_cpu_model(),
         "kind": "oracle",
         "sample": f"{reps} full passes of the fp64 oracle over one {wl.M}x{wl.N} {wl.dtype} batch "
                   f"({dt:.1f} s wall), same algorithmic bytes per pass as a GPU step",
@@ -260,6 +273,8 @@ def bench_backward(args, wl, name, dev) -> int:
             "workspace_bytes": ws_bytes,
             "workspace_traffic_bytes_per_step": 2 * ws_bytes,
             "rotation_sets": sets,
+            "inputs_sha256": {"x": workloads.sha256_of(x0), "w": workloads.sha256_of(w0),
+                              "dy": workloads.sha256_of(dy0)},
             "launch": "graph",
             "plan": plan.as_dict(),
             "pct_of_peak": round(100 * gbps / PEAK_GBPS, 2),
@@ -281,7 +296,7 @@ def bench_backward(args, wl, name, dev) -> int:
             if dt >= args.cpu_seconds:
                 break
         out["cpu_baseline"] = {"value": round(reps * nbytes / dt / 1e9, 3), "unit": "GB/s",
-                               "cores": o.max_threads(), "kind": "oracle",
+                               "cores": o.max_threads(), "host_cpu": host_cpu_model(), "kind": "oracle",
                                "sample": f"{reps} full passes of the fp64 oracle backward over one batch ({dt:.1f} s)"}
     print(json.dumps(out), flush=True)
     return 0
@@ -447,6 +462,8 @@ def main() -> int:
             "offset": wl.offset,
             "algorithmic_bytes_per_step": nbytes,
             "rotation_sets": sets,
+            # the first rotation set's inputs (seed 0), as drawn by workloads.make_inputs
+            "inputs_sha256": {"x": workloads.sha256_of(x0), "w": workloads.sha256_of(w0)},
             "inputs": ("cold in HBM" if sets * x_bytes >= ROTATION_X_BYTES
                        else "warm: rows may be cache-resident (Infinity Cache); not an HBM figure"),
             "launch": args.mode,
