@@ -114,6 +114,20 @@ def make_grad(wl: Workload, seed: int = 0, rows: int | None = None) -> torch.Ten
     return torch.randn(M, wl.N, generator=g, dtype=torch.float32).to(TORCH_DTYPES[wl.dtype])
 
 
+def fill_normal_(t: torch.Tensor, seed: int, sigma: float = 1.0, mean: float = 0.0,
+                 chunk: int = 1 << 26) -> torch.Tensor:
+    """Fill ``t`` in place with mean + sigma * N(0, 1), drawn in fp32 on the tensor's own device
+    from a generator seeded with ``seed``, ``chunk`` elements at a time, then rounded to t's dtype.
+    For tensors too large to draw on the host (several GiB of rows)."""
+    g = torch.Generator(device=t.device).manual_seed(seed)
+    flat = t.view(-1)
+    for i in range(0, flat.numel(), chunk):
+        n = min(chunk, flat.numel() - i)
+        z = torch.randn(n, generator=g, device=t.device, dtype=torch.float32)
+        flat[i:i + n] = z.mul_(sigma).add_(mean)
+    return t
+
+
 def to_bits(t: torch.Tensor) -> np.ndarray:
     """Bit patterns of a CPU 16-bit tensor as a uint16 numpy array (no copy of values)."""
     if t.dtype not in (torch.bfloat16, torch.float16):
