@@ -379,7 +379,9 @@ def main() -> int:
                               ys[0].data_ptr())
     if args.plan:
         plan = plan.copy(**json.loads(args.plan))
-    res = binding.plan_resources(plan, wl.dtype)
+    # the instance this call launches (the plan's, or its exact-width wave form) and its resources
+    res = binding.kernel_query(wl.M, wl.N, wl.dtype, xs[0].data_ptr(), w_dev.data_ptr(), ys[0].data_ptr(),
+                               plan=plan)
     log("plan", plan.as_dict(), "resources", res)
 
     lib = binding.lib

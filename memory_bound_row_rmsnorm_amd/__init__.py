@@ -13,7 +13,7 @@ only) can be imported on a machine without the built library.
 from __future__ import annotations
 
 __all__ = [
-    "rmsnorm_fwd", "rmsnorm_fwd_out", "plan_query", "plan_resources", "status_string",
+    "rmsnorm_fwd", "rmsnorm_fwd_out", "plan_query", "plan_resources", "kernel_query", "status_string",
     "rmsnorm_bwd", "rmsnorm_bwd_out", "bwd_plan_query", "bwd_workspace_size",
     "library_path", "version", "Plan", "RmsnormError",
     "plan_validate", "set_tuned", "clear_tuned", "tuned_count", "load_tuned",

@@ -34,7 +34,7 @@ STATUS = {
 # Every symbol include/rmsnorm.h declares.
 EXPORTED = (
     "rmsnorm_fwd", "rmsnorm_fwd_with_plan", "rmsnorm_fwd_ex", "rmsnorm_plan_query", "rmsnorm_plan_query_ex",
-    "rmsnorm_plan_resources",
+    "rmsnorm_plan_resources", "rmsnorm_fwd_kernel_query",
     "rmsnorm_bwd", "rmsnorm_bwd_with_plan", "rmsnorm_bwd_plan_query", "rmsnorm_bwd_workspace_size",
     "rmsnorm_bwd_ex", "rmsnorm_bwd_plan_query_ex", "rmsnorm_bwd_workspace_size_ex",
     "rmsnorm_plan_validate", "rmsnorm_plan_set_tuned", "rmsnorm_plan_clear_tuned", "rmsnorm_plan_tuned_count",
@@ -127,6 +127,9 @@ def _load():
     i32p = ctypes.POINTER(ctypes.c_int32)
     lib.rmsnorm_plan_resources.argtypes = [ctypes.POINTER(Plan), i32, i32p, i32p, i32p, i32p]
     lib.rmsnorm_plan_resources.restype = i32
+    lib.rmsnorm_fwd_kernel_query.argtypes = [i64, i64, i32, vp, vp, vp, ctypes.POINTER(Plan),
+                                             ctypes.POINTER(ctypes.c_char_p), i32p, i32p, i32p]
+    lib.rmsnorm_fwd_kernel_query.restype = i32
     lib.rmsnorm_bwd.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, f32, i32, vp, i64, vp]
     lib.rmsnorm_bwd.restype = i32
     lib.rmsnorm_bwd_with_plan.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, f32, i32,
@@ -331,6 +334,23 @@ def plan_resources(plan: Plan, dtype) -> dict:
     _check(lib.rmsnorm_plan_resources(ctypes.byref(plan), _dtype_code(dtype), ctypes.byref(v),
                                       ctypes.byref(s), ctypes.byref(l), ctypes.byref(sc)))
     return {"vgprs": v.value, "lds_bytes": l.value, "scratch_bytes": sc.value}
+
+
+def kernel_query(M: int, N: int, dtype, x_ptr: int = 0, w_ptr: int = 0, y_ptr: int = 0,
+                 plan: Plan | None = None, resources: bool = True) -> dict:
+    """The kernel instance a forward launch over contiguous [M, N] rows with these pointers and
+    plan (None = the library's) runs, and (``resources``, needs a GPU) its VGPRs, LDS bytes and
+    scratch bytes."""
+    name = ctypes.c_char_p()
+    v, l, sc = (ctypes.c_int32() for _ in range(3))
+    refs = (ctypes.byref(v), ctypes.byref(l), ctypes.byref(sc)) if resources else (None, None, None)
+    _check(lib.rmsnorm_fwd_kernel_query(M, N, _dtype_code(dtype), x_ptr or None, w_ptr or None, y_ptr or None,
+                                        ctypes.byref(plan) if plan is not None else None, ctypes.byref(name),
+                                        *refs))
+    out = {"kernel": name.value.decode()}
+    if resources:
+        out.update({"vgprs": v.value, "lds_bytes": l.value, "scratch_bytes": sc.value})
+    return out
 
 
 def version() -> int:

@@ -265,6 +265,26 @@ const KernelEntry* find_kernel(int variant, int dtype, int lanes, int vpl, int s
 
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
+// The instance a launch of plan p with kernel k runs: the exact-width wave
+// form when the call fits it (a non-prefetching wave plan without XCD remap
+// whose segment shape and workgroup size have an exact form, one batch of
+// contiguous rows of exactly lanes * vectors vectors, one trip,
+// fewer than kExactMaxRows rows, row numbers of the whole grid below 2^31),
+// k otherwise.  M is the rows of one batch, `batches` the batch count.  Host
+// only.
+const KernelEntry* launch_instance(const KernelEntry* k, const rmsnorm_plan_t* p, int64_t M, int64_t N, int dtype,
+                                   const Layout& L, int64_t batches) {
+    if (k->variant != RMSNORM_VARIANT_WAVE || k->prefetch || p->xcd_group != 1) return k;
+    if (batches != 1 || M >= rmsnorm_impl::kExactMaxRows) return k;
+    if (M > 1 && (L.x_rs != N || L.y_rs != N)) return k;
+    if (N != static_cast<int64_t>(p->lanes_per_row) * p->vectors_per_lane * elems_per_vector(dtype)) return k;
+    const int64_t covered = p->grid * p->rows_per_trip;
+    if (covered < M || covered >= (int64_t{1} << 31)) return k;
+    const KernelEntry* e = rmsnorm_impl::exact_wave_kernel(dtype, p->lanes_per_row, p->vectors_per_lane,
+                                                           p->row_slots, p->block_threads);
+    return e ? e : k;
+}
+
 // Fill the derived fields and check the plan against the call (`vec`: the
 // call's pointers and strides suit the 16-byte kernels).  Host only.
 int finish_plan(rmsnorm_plan_t* p, int64_t M, int64_t N, int dtype, Access acc, const KernelEntry** kernel) {
@@ -531,6 +551,7 @@ constexpr int64_t kMaxGridY = 65535;
 int launch(const KernelEntry* k, const rmsnorm_plan_t* p, const void* x, const void* w, void* y,
            float* rstd, int64_t M, int64_t N, float eps, float offset, int dtype, const Layout& L,
            int64_t batches, int lds_per_cu, void* stream) {
+    k = launch_instance(k, p, M, N, dtype, L, batches);
     // occupancy cap: (cap + 1) workgroups of this much LDS do not fit a unit
     size_t dyn_lds = 0;
     if (p->max_blocks_per_cu > 0 && lds_per_cu > 0)
@@ -1165,6 +1186,38 @@ int rmsnorm_plan_validate(int64_t M, int64_t N, int dtype, const void* x, const 
     if (st == RMSNORM_OK) st = resident_grid(&p, k, cu_count, &p.resident_grid);
     if (st != RMSNORM_OK) return st;
     *out = p;
+    return RMSNORM_OK;
+}
+
+int rmsnorm_fwd_kernel_query(int64_t M, int64_t N, int dtype, const void* x, const void* w, const void* y,
+                             const rmsnorm_plan_t* plan, const char** kernel_name, int32_t* vgprs,
+                             int32_t* lds_bytes, int32_t* scratch) {
+    g_last_error.clear();
+    int st = check_shape_dtype(M, N, dtype);
+    if (st != RMSNORM_OK) return st;
+    if (M == 0) return fail(RMSNORM_ERR_SHAPE, "M == 0 launches nothing");
+    const Layout L = contiguous_layout(M, N);
+    const Access acc = access_of(x, w, y, dtype, L, M);
+    rmsnorm_plan_t p;
+    if (plan) {
+        p = *plan;
+    } else {
+        st = rmsnorm_plan_query(M, N, dtype, x, w, y, 256, &p);
+        if (st != RMSNORM_OK) return st;
+    }
+    const KernelEntry* k = nullptr;
+    st = finish_plan(&p, M, N, dtype, acc, &k);
+    if (st != RMSNORM_OK) return st;
+    k = launch_instance(k, &p, M, N, dtype, L, 1);
+    if (kernel_name) *kernel_name = k->name;
+    if (vgprs || lds_bytes || scratch) {
+        hipFuncAttributes attr;
+        hipError_t e = hipFuncGetAttributes(&attr, k->func);
+        if (e != hipSuccess) return fail(RMSNORM_ERR_HIP, std::string("hipFuncGetAttributes: ") + hipGetErrorString(e));
+        if (vgprs) *vgprs = attr.numRegs;
+        if (lds_bytes) *lds_bytes = static_cast<int32_t>(attr.sharedSizeBytes);
+        if (scratch) *scratch = static_cast<int32_t>(attr.localSizeBytes);
+    }
     return RMSNORM_OK;
 }
 

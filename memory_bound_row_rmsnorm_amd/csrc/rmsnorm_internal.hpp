@@ -82,6 +82,14 @@ struct KernelEntry {
 // The compiled instances (defined in rmsnorm_kernels.hip).
 const KernelEntry* kernel_table(int* count);
 
+// The exact-width wave form with this row segment shape and workgroup size,
+// or nullptr.  It serves one-trip, one-batch, unremapped, non-prefetching
+// launches of a wave plan over contiguous rows of exactly lanes * vpl
+// vectors, with M below kExactMaxRows; its arguments are KernelArgs as for
+// every forward kernel.
+const KernelEntry* exact_wave_kernel(int dtype, int lanes, int vpl, int slots, int threads);
+constexpr int64_t kExactMaxRows = (int64_t{1} << 31) - (int64_t{1} << 16);
+
 // Backward row-pass instances and the column-pass kernel (rmsnorm_bwd_kernels.hip).
 // The column pass takes (const float* partials, float* dw, int64_t G, int64_t N,
 // int32_t vec4): vec4 = 1 when N % 4 == 0 and dw is 16-byte aligned.

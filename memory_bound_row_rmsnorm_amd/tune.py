@@ -194,12 +194,14 @@ def tune_shape(M: int, N: int, dtype: str, quick: bool = False, log=print) -> li
     for i, p in enumerate(cands):
         dev_plan = binding.plan_validate(M, N, dtype, p, bufs.x[0].data_ptr(), bufs.w.data_ptr(),
                                          bufs.y[0].data_ptr(), cu_count=0)
-        res = binding.plan_resources(dev_plan, dtype)
+        res = binding.kernel_query(M, N, dtype, bufs.x[0].data_ptr(), bufs.w.data_ptr(), bufs.y[0].data_ptr(),
+                                   plan=dev_plan)
         us = time_plan(dev_plan, bufs, M, N, dtype, steps)
         wg_per_cu = dev_plan.resident_grid / cu
         r = {
             "plan": {f: getattr(dev_plan, f) for f in binding.PLAN_FIELDS},
             "describe": describe(dev_plan),
+            "kernel": res["kernel"],
             "vgprs": res["vgprs"], "lds_bytes": res["lds_bytes"], "scratch_bytes": res["scratch_bytes"],
             "wg_per_cu": wg_per_cu,
             "waves_per_simd": wg_per_cu * (dev_plan.block_threads // 64) / 4.0,

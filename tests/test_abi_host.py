@@ -671,3 +671,45 @@ def test_bwd_wide_plans_that_do_not_fit_are_rejected():
                  (good, 24580)):                                  # rows not 16-byte aligned
         st = lib.rmsnorm_bwd_with_plan(X, W, DY, R, DX, DW, 100, N, 0.0, BF16, ctypes.byref(p), WS, 1 << 24, None)
         assert st == PLAN, (p.as_dict(), N, lib.rmsnorm_last_error().decode())
+
+
+# ---------------------------------------------------------------------------
+# The instance a launch runs: the exact-width wave form where the call fits it.
+# ---------------------------------------------------------------------------
+EXACT_WIDTHS = [("bf16", 128), ("bf16", 256), ("bf16", 512), ("bf16", 1024), ("fp16", 512), ("fp32", 64),
+                ("fp32", 512)]
+
+
+@pytest.mark.parametrize("dtype,N", EXACT_WIDTHS)
+def test_exact_widths_launch_the_exact_wave_form(dtype, N):
+    for M in (1, 7, 16384, 262144):
+        q = bnd.kernel_query(M, N, dtype, A, A, A + (1 << 30), resources=False)
+        assert q["kernel"].startswith("rmsnorm_wave_exact<"), (M, N, dtype, q)
+        plan = bnd.plan_query(M, N, dtype, cu_count=256)
+        shape = f",{plan.lanes_per_row},{plan.vectors_per_lane},{plan.row_slots},{plan.block_threads // 64}>"
+        assert q["kernel"].endswith(shape), (q, plan.as_dict())
+
+
+def test_other_launches_keep_the_general_instance():
+    M, N = 16384, 512
+    base = bnd.plan_query(M, N, "bf16", cu_count=256)
+
+    def name(plan=None, n=N, m=M):
+        return bnd.kernel_query(m, n, "bf16", A, A, A + (1 << 30), plan=plan, resources=False)["kernel"]
+
+    assert name().startswith("rmsnorm_wave_exact<")
+    # a persistent grid, a remap, prefetching: the general instance
+    assert name(base.copy(grid=64)).startswith("rmsnorm_wave<")
+    assert name(base.copy(xcd_group=2)).startswith("rmsnorm_wave<")
+    assert name(base.copy(prefetch=1)).startswith("rmsnorm_wave<")
+    # a width below the plan's full row (masked columns); a single ragged row (a tail vector;
+    # several ragged contiguous rows start unaligned and take a shifted kernel)
+    assert name(n=504).startswith("rmsnorm_wave<")
+    assert name(n=500, m=1).startswith("rmsnorm_wave<")
+    # no exact form for this segment shape or workgroup size
+    assert name(base.copy(row_slots=8)).startswith("rmsnorm_wave<")
+    assert name(base.copy(block_threads=512, grid=512)).startswith("rmsnorm_wave<")
+    # other families are untouched
+    assert name(n=8192).startswith("rmsnorm_block<")
+    with pytest.raises(bnd.RmsnormError):
+        name(m=0)

@@ -166,6 +166,44 @@ def test_sweep(bnd, N, dtype):
 
 
 # ---------------------------------------------------------------------------
+# 3b. The exact-width wave forms: the instance the rule's launches take over
+#     contiguous rows of exactly 16, 32, 64 or 128 vectors.  Each one, named
+#     through rmsnorm_fwd_kernel_query, over row counts that end inside a
+#     workgroup (and one row), both offsets, and with rstd not written.
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("dtype", ["bf16", "fp16", "fp32"])
+@pytest.mark.parametrize("vectors", [16, 32, 64, 128])
+def test_exact_wave_forms(bnd, vectors, dtype):
+    N = vectors * (4 if dtype == "fp32" else 8)
+    g = torch.Generator().manual_seed(7 * N + len(dtype))
+    td = workloads.TORCH_DTYPES[dtype]
+    sigma = 100.0 if dtype == "fp16" else 1.0
+    for M in (1, 5, 63, 1000, 4099):
+        x = (torch.randn(M, N, generator=g) * sigma).to(td)
+        w = (1 + 0.1 * torch.randn(N, generator=g)).to(td)
+        xg, wg = x.to(DEV), w.to(DEV)
+        y = torch.full_like(xg, float("nan"))
+        r = torch.full((M,), float("nan"), dtype=torch.float32, device=DEV)
+        q = bnd.kernel_query(M, N, dtype, xg.data_ptr(), wg.data_ptr(), y.data_ptr())
+        assert q["kernel"].startswith("rmsnorm_wave_exact<") and q["scratch_bytes"] == 0, q
+        offset = 1.0 if M == 63 else 0.0
+        announce("exact", M, N, dtype, offset, q)
+        bnd.rmsnorm_fwd_out(xg, wg, y, r, 1e-6, offset)
+        torch.cuda.synchronize()
+        if dtype == "fp32":
+            ye, re = parity.oracle_fp32(x, w, 1e-6, offset)
+            parity.compare_fp32(y, r, ye, re, f"exact M={M} N={N} fp32")
+        else:
+            y_ref, r_ref = parity.oracle_for(x, w, 1e-6, offset, dtype)
+            parity.compare(y, r, y_ref, r_ref, dtype, f"exact M={M} N={N} {dtype}")
+        # rstd not written: the same y
+        y2, r2 = bnd.rmsnorm_fwd_ex(xg, wg, 1e-6, offset, want_rstd=False)
+        torch.cuda.synchronize()
+        assert r2 is None and torch.equal(y2.view(torch.int16 if dtype != "fp32" else torch.int32),
+                                          y.view(torch.int16 if dtype != "fp32" else torch.int32))
+
+
+# ---------------------------------------------------------------------------
 # 4. Guard bands: NaN around x and w must not leak in; sentinels around y and
 #    rstd must not be written.  Aligned offsets take the 16-byte kernels,
 #    odd offsets the generic kernel.
@@ -328,4 +366,6 @@ def test_kernels_do_not_spill(bnd):
             res = bnd.plan_resources(plan, dtype)
             seen[(name, dtype)] = res
             assert res["scratch_bytes"] == 0, (name, dtype, res)
+            launched = bnd.kernel_query(wl.M, wl.N, dtype, plan=plan)
+            assert launched["scratch_bytes"] == 0, (name, dtype, launched)
     print(seen)
