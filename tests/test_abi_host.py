@@ -713,3 +713,12 @@ def test_other_launches_keep_the_general_instance():
     assert name(n=8192).startswith("rmsnorm_block<")
     with pytest.raises(bnd.RmsnormError):
         name(m=0)
+
+
+def test_exact_form_row_limit():
+    """32-bit row numbers: from 2^31 - 2^16 rows on, the general instance runs."""
+    limit = (1 << 31) - (1 << 16)
+    below = bnd.kernel_query(limit - 1, 512, "bf16", A, A, A + (1 << 40), resources=False)["kernel"]
+    at = bnd.kernel_query(limit, 512, "bf16", A, A, A + (1 << 40), resources=False)["kernel"]
+    assert below.startswith("rmsnorm_wave_exact<"), below
+    assert at.startswith("rmsnorm_wave<"), at
