@@ -1010,12 +1010,14 @@ int launch_bwd(const KernelEntry* k, const rmsnorm_plan_t* p, const void* x, con
     int64_t Nn = N;
     int32_t vec4 = (N % 4 == 0 && aligned16(dw)) ? 1 : 0;
     void* rargs[] = {&partials, &dw, &G, &Nn, &vec4};
-    const int64_t groups = vec4 ? N / 4 : N;        // column groups, 16 per workgroup
-    const int64_t blocks = ceil_div(groups, 16);
-    // 64-way splits (1024 threads) once there are enough partial rows to share
+    const int64_t groups = vec4 ? N / 4 : N;        // column groups
+    // 4 groups per workgroup up to 256 groups (more workgroups share the reads), 16 above
+    const int cols = groups <= 256 ? 4 : 16;
+    const int64_t blocks = ceil_div(groups, cols);
+    // 64-way splits once there are enough partial rows to share
     const int split = G >= 128 ? 64 : 16;
-    hipError_t e = hipLaunchKernel(rmsnorm_impl::dw_reduce_kernel(split), dim3(static_cast<unsigned>(blocks)),
-                                   dim3(static_cast<unsigned>(16 * split)),
+    hipError_t e = hipLaunchKernel(rmsnorm_impl::dw_reduce_kernel(split, cols), dim3(static_cast<unsigned>(blocks)),
+                                   dim3(static_cast<unsigned>(cols * split)),
                                    rargs, 0, s);
     if (e != hipSuccess) return fail(RMSNORM_ERR_HIP, std::string("hipLaunchKernel(rmsnorm_dw_reduce): ") + hipGetErrorString(e));
     return RMSNORM_OK;

@@ -842,18 +842,21 @@ __global__ __launch_bounds__(1024) void rmsnorm_bwd_generic(BwdArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// Column pass: dw[j] = sum over the G partial rows.  A workgroup covers 64
-// columns (16 groups of 4) and splits the G partial rows SPLIT ways: thread
-// (s, q) adds rows s, s + SPLIT, s + 2 SPLIT, ... of columns 4q .. 4q + 3 in
+// Column pass: dw[j] = sum over the G partial rows.  A workgroup covers COLS
+// column groups (of 4 columns, or of 1) and splits the G partial rows SPLIT
+// ways: thread (s, q) adds rows s, s + SPLIT, s + 2 SPLIT, ... of group q in
 // that order; the SPLIT sub-sums then meet in LDS in a fixed order (groups of
-// 8 in order, then the groups in order), so dw is the same on every run.
-// SPLIT = 64 (1024 threads) gives every thread few rows: the partial rows
+// 8 in order, then the groups in order), so dw is the same on every run and
+// for either COLS.  SPLIT = 64 gives every thread few rows: the partial rows
 // were just written from other XCDs' caches, and each sequential round of
-// loads costs a trip to memory.  With vec4 (N % 4 == 0 and dw 16-byte
-// aligned; the workspace always is) columns move as float4, otherwise one
-// column per lane of a group.
+// loads costs a trip to memory.  COLS trades workgroups for width: measured
+// on MI355X after a kernel that writes the partial rows, 4 groups per
+// workgroup (256 threads) are faster up to 256 groups (G = 256, N = 512: 2.50
+// against 2.88 us; N = 1024: 2.90 against 3.14 us) and 16 (1024 threads)
+// above (N = 2048: 3.46 against 3.68 us; G = 512, N = 8192: 9.29 against
+// 14.75 us).  With vec4 (N % 4 == 0 and dw 16-byte aligned; the workspace
+// always is) columns move as float4, otherwise one column per lane of a group.
 // ---------------------------------------------------------------------------
-constexpr int kRedCols4 = 16;    // column groups per workgroup
 
 __device__ __forceinline__ float4 add4(float4 a, const float4 b) {
     a.x += b.x;
@@ -863,17 +866,17 @@ __device__ __forceinline__ float4 add4(float4 a, const float4 b) {
     return a;
 }
 
-template <int SPLIT>
-__global__ __launch_bounds__(16 * SPLIT) void rmsnorm_dw_reduce(const float* __restrict__ partials,
+template <int SPLIT, int COLS>
+__global__ __launch_bounds__(COLS * SPLIT) void rmsnorm_dw_reduce(const float* __restrict__ partials,
                                                                 float* __restrict__ dw, int64_t G, int64_t N,
                                                                 int32_t vec4) {
     static_assert(SPLIT == 16 || SPLIT == 64, "split 16 or 64");
-    __shared__ float4 red[SPLIT][kRedCols4];
-    const int q = threadIdx.x % kRedCols4;
-    const int sp = threadIdx.x / kRedCols4;
+    __shared__ float4 red[SPLIT][COLS];
+    const int q = threadIdx.x % COLS;
+    const int sp = threadIdx.x / COLS;
     float4 acc = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
-    const int64_t c = vec4 ? (static_cast<int64_t>(blockIdx.x) * kRedCols4 + q) * 4
-                           : static_cast<int64_t>(blockIdx.x) * kRedCols4 + q;
+    const int64_t c = vec4 ? (static_cast<int64_t>(blockIdx.x) * COLS + q) * 4
+                           : static_cast<int64_t>(blockIdx.x) * COLS + q;
     if (c < N) {
         if (vec4) {
 #pragma unroll 4
@@ -964,9 +967,11 @@ const KernelEntry* bwd_kernel_table(int* count) {
     return kBwdTable;
 }
 
-const void* dw_reduce_kernel(int split) {
-    return split == 64 ? reinterpret_cast<const void*>(&rmsnorm_dw_reduce<64>)
-                       : reinterpret_cast<const void*>(&rmsnorm_dw_reduce<16>);
+const void* dw_reduce_kernel(int split, int cols) {
+    if (split == 64) return cols == 4 ? reinterpret_cast<const void*>(&rmsnorm_dw_reduce<64, 4>)
+                                      : reinterpret_cast<const void*>(&rmsnorm_dw_reduce<64, 16>);
+    return cols == 4 ? reinterpret_cast<const void*>(&rmsnorm_dw_reduce<16, 4>)
+                     : reinterpret_cast<const void*>(&rmsnorm_dw_reduce<16, 16>);
 }
 
 }  // namespace rmsnorm_impl

@@ -94,6 +94,7 @@ constexpr int64_t kExactMaxRows = (int64_t{1} << 31) - (int64_t{1} << 16);
 // The column pass takes (const float* partials, float* dw, int64_t G, int64_t N,
 // int32_t vec4): vec4 = 1 when N % 4 == 0 and dw is 16-byte aligned.
 const KernelEntry* bwd_kernel_table(int* count);
-const void* dw_reduce_kernel(int split);   // split 16 (256 threads) or 64 (1024 threads)
+// split 16 or 64, cols (column groups per workgroup) 4 or 16: cols * split threads
+const void* dw_reduce_kernel(int split, int cols);
 
 }  // namespace rmsnorm_impl
