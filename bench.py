@@ -140,6 +140,21 @@ def traffic_from_counters(wl, name: str, directory: str) -> dict:
     }
 
 
+def load_copy_ceiling():
+    """libcopy_ceiling.so (built with the package): the streaming copy the forward is measured
+    against.  Raises when it has not been built."""
+    import ctypes
+
+    path = os.path.join(ROOT, "memory_bound_row_rmsnorm_amd", "libcopy_ceiling.so")
+    if not os.path.exists(path):
+        raise SystemExit(f"{path} is not built: run python -m memory_bound_row_rmsnorm_amd.build")
+    lib = ctypes.CDLL(path)
+    vp, i64, i32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32
+    lib.copy_ceiling.argtypes = [vp, vp, i64, i32, i32, i64, vp]
+    lib.copy_ceiling.restype = ctypes.c_int
+    return lib
+
+
 def host_cpu_model() -> str:
     """The host processor's model name (Linux /proc/cpuinfo), or "unknown"."""
     try:
@@ -323,10 +338,14 @@ def main() -> int:
                          "--save) before planning")
     ap.add_argument("--pass", dest="direction", choices=["fwd", "bwd"], default="fwd",
                     help="bwd: time the backward (row pass + dw column pass) instead")
-    ap.add_argument("--kernel", choices=["rmsnorm", "copy"], default="rmsnorm",
-                    help="copy: time a plain device copy of x into y instead (same rotation, "
-                         "2*M*N*s bytes per step), the practical ceiling and the counter "
-                         "calibration reference")
+    ap.add_argument("--kernel", choices=["rmsnorm", "copy", "hip_copy"], default="rmsnorm",
+                    help="copy: time torch's device copy of x into y instead (the runtime's copy "
+                         "kernel; same rotation, 2*M*N*s bytes per step), the counter calibration "
+                         "reference; hip_copy: the streaming copy of libcopy_ceiling.so (16-byte "
+                         "non-temporal accesses, --copy-vpl KiB per wave), the practical ceiling")
+    ap.add_argument("--copy-vpl", type=int, default=4, choices=[1, 2, 4, 8],
+                    help="hip_copy: contiguous KiB each wave moves per run")
+    ap.add_argument("--copy-threads", type=int, default=256, help="hip_copy: workgroup size")
     args = ap.parse_args()
 
     if args.traffic_from:
@@ -392,9 +411,20 @@ def main() -> int:
     def launch_copy(i: int, stream_handle):
         ys[i % sets].copy_(xs[i % sets])
 
+    copy_lib = load_copy_ceiling() if args.kernel == "hip_copy" else None
+    copy_bytes = wl.M * wl.N * wl.elem_bytes
+
+    def launch_hip_copy(i: int, stream_handle):
+        st = copy_lib.copy_ceiling(xs[i % sets].data_ptr(), ys[i % sets].data_ptr(), copy_bytes, args.copy_vpl,
+                                   args.copy_threads, 0, stream_handle)
+        if st != 0:
+            raise RuntimeError(f"copy_ceiling returned {st}")
+
     def launch(i: int, stream_handle):
         if args.kernel == "copy":
             return launch_copy(i, stream_handle)
+        if args.kernel == "hip_copy":
+            return launch_hip_copy(i, stream_handle)
         xp, wp, yp, rp = argv[i % sets]
         st = lib.rmsnorm_fwd_with_plan(xp, wp, yp, rp, wl.M, wl.N, wl.eps, wl.offset, code, pplan,
                                        stream_handle)
@@ -470,6 +500,8 @@ def main() -> int:
                        else "warm: rows may be cache-resident (Infinity Cache); not an HBM figure"),
             "launch": args.mode,
             "kernel": args.kernel,
+            **({"copy": {"kib_per_wave_run": args.copy_vpl, "threads": args.copy_threads}}
+               if args.kernel == "hip_copy" else {}),
             "plan": {k: v for k, v in plan.as_dict().items()},
             "kernel_resources": res,
             "pct_of_peak": round(100 * gbps / PEAK_GBPS, 2),

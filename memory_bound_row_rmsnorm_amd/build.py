@@ -1,4 +1,5 @@
-"""Build librmsnorm_mi355x.so in-tree with hipcc for gfx950.
+"""Build librmsnorm_mi355x.so (and libcopy_ceiling.so, the copy the benchmark
+measures against) in-tree with hipcc for gfx950.
 
     python -m memory_bound_row_rmsnorm_amd.build
 
@@ -21,6 +22,9 @@ RESOURCES = os.path.join(BUILD_DIR, "kernel_resources.txt")
 
 SOURCES = [os.path.join(CSRC, "rmsnorm_kernels.hip"), os.path.join(CSRC, "rmsnorm_bwd_kernels.hip"),
            os.path.join(CSRC, "rmsnorm_api.cpp")]
+# the copy the benchmark measures the forward against (not part of the RMSNorm library)
+COPY_LIBRARY = os.path.join(HERE, "libcopy_ceiling.so")
+COPY_SOURCES = [os.path.join(CSRC, "copy_ceiling.hip")]
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950",
@@ -43,14 +47,20 @@ def hipcc() -> str:
 
 
 def build(verbose: bool = False) -> str:
+    """Build the RMSNorm library (returned) and the copy-ceiling library."""
+    _build_one(COPY_LIBRARY, COPY_SOURCES, os.path.join(BUILD_DIR, "copy_ceiling_resources.txt"), verbose)
+    return _build_one(LIBRARY, SOURCES, RESOURCES, verbose)
+
+
+def _build_one(library: str, sources: list, resources: str, verbose: bool) -> str:
     os.makedirs(BUILD_DIR, exist_ok=True)
-    tmp = f"{LIBRARY}.{os.getpid()}.tmp"
-    cmd = [hipcc(), *HIPCC_FLAGS, "-o", tmp, *SOURCES]
+    tmp = f"{library}.{os.getpid()}.tmp"
+    cmd = [hipcc(), *HIPCC_FLAGS, "-o", tmp, *sources]
     if verbose:
         print(" ".join(cmd), flush=True)
     proc = subprocess.run(cmd, capture_output=True, text=True)
     remarks = [ln for ln in proc.stderr.splitlines() if "remark:" in ln]
-    with open(RESOURCES, "w") as f:
+    with open(resources, "w") as f:
         f.write("\n".join(remarks) + "\n")
     other = [ln for ln in proc.stderr.splitlines()
              if "remark:" not in ln and "packed-fp32-ops" not in ln and ln.strip()]
@@ -59,8 +69,8 @@ def build(verbose: bool = False) -> str:
         raise RuntimeError(f"hipcc failed with exit code {proc.returncode}")
     if verbose and other:
         sys.stderr.write("\n".join(other) + "\n")
-    os.replace(tmp, LIBRARY)
-    return LIBRARY
+    os.replace(tmp, library)
+    return library
 
 
 if __name__ == "__main__":

@@ -1,0 +1,75 @@
+// copy_ceiling.hip -- the practical HBM ceiling the row RMSNorm is measured
+// against: a plain streaming copy that moves the bytes the forward moves
+// (x read once, y written once), with the same 16-byte non-temporal accesses.
+// It computes nothing and is not part of the RMSNorm path; the benchmark
+// times it under the same rotation and graph replay as the forward
+// (bench.py --kernel hip_copy).
+//
+// Each wave copies runs of VPL contiguous KiB: lane l moves the 16-byte
+// vectors run * 64 * VPL + v * 64 + l, v < VPL, all loads before the first
+// store.  Waves loop over runs with a grid stride.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+template <int VPL>
+__global__ __launch_bounds__(1024) void copy_runs(const u32x4* __restrict__ src, u32x4* __restrict__ dst,
+                                                  int64_t nvec) {
+    const int lane = threadIdx.x & 63;
+    const int64_t waves_per_block = blockDim.x >> 6;
+    const int64_t nwaves = static_cast<int64_t>(gridDim.x) * waves_per_block;
+    for (int64_t run = static_cast<int64_t>(blockIdx.x) * waves_per_block + (threadIdx.x >> 6);
+         run * 64 * VPL < nvec; run += nwaves) {
+        const int64_t base = run * 64 * VPL + lane;
+        u32x4 d[VPL];
+#pragma unroll
+        for (int v = 0; v < VPL; ++v)
+            d[v] = base + v * 64 < nvec ? __builtin_nontemporal_load(src + base + v * 64) : u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+        for (int v = 0; v < VPL; ++v)
+            if (base + v * 64 < nvec) __builtin_nontemporal_store(d[v], dst + base + v * 64);
+    }
+}
+
+}  // namespace
+
+extern "C" {
+
+// Copy `bytes` bytes from src to dst (device pointers, 16-byte aligned, not
+// overlapping; bytes a multiple of 16) on `stream` (NULL = null stream).
+// vpl: KiB per wave per run, 1, 2, 4 or 8; threads: workgroup size, a
+// multiple of 64 up to 1024; grid: workgroups, or <= 0 for one run per wave.
+// Returns 0, 1 for bad arguments (checked before any HIP call), 2 when the
+// launch fails.
+int copy_ceiling(const void* src, void* dst, int64_t bytes, int32_t vpl, int32_t threads, int64_t grid,
+                 void* stream) {
+    if (bytes < 0 || bytes % 16 != 0) return 1;
+    if (bytes > 0 && (!src || !dst)) return 1;
+    if ((reinterpret_cast<uintptr_t>(src) | reinterpret_cast<uintptr_t>(dst)) & 15u) return 1;
+    if (threads < 64 || threads > 1024 || threads % 64 != 0) return 1;
+    const void* k = nullptr;
+    switch (vpl) {
+        case 1: k = reinterpret_cast<const void*>(&copy_runs<1>); break;
+        case 2: k = reinterpret_cast<const void*>(&copy_runs<2>); break;
+        case 4: k = reinterpret_cast<const void*>(&copy_runs<4>); break;
+        case 8: k = reinterpret_cast<const void*>(&copy_runs<8>); break;
+        default: return 1;
+    }
+    const char* s0 = static_cast<const char*>(src);
+    const char* d0 = static_cast<const char*>(dst);
+    if (s0 < d0 + bytes && d0 < s0 + bytes) return 1;
+    if (bytes == 0) return 0;
+    int64_t nvec = bytes / 16;
+    const int64_t per_block = static_cast<int64_t>(threads / 64) * 64 * vpl;
+    int64_t g = grid > 0 ? grid : (nvec + per_block - 1) / per_block;
+    if (g > 0x7FFFFFFF) g = 0x7FFFFFFF;
+    void* args[] = {&src, &dst, &nvec};
+    hipError_t e = hipLaunchKernel(k, dim3(static_cast<unsigned>(g)), dim3(static_cast<unsigned>(threads)), args, 0,
+                                   static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? 0 : 2;
+}
+
+}  // extern "C"

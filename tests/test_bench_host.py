@@ -66,3 +66,17 @@ def test_stale_traffic_is_reported_as_null(tmp_path, monkeypatch):
     assert bench.measured_traffic(name, plan) == 123
     assert bench.measured_traffic(name, dict(plan, grid=512)) is None   # another launch plan
     assert bench.measured_traffic("rmsnorm_64x512_bf16", plan) is None  # no summary at all
+
+
+def test_copy_ceiling_library_rejects_bad_arguments_before_any_hip_call():
+    """libcopy_ceiling.so (the practical ceiling bench.py --kernel hip_copy times) checks its
+    arguments on the host; every call below fails before a launch."""
+    lib = bench.load_copy_ceiling()
+    a, b = 0x10000000, 0x20000000
+    assert lib.copy_ceiling(a, b, 0, 4, 256, 0, None) == 0            # nothing to copy: no launch
+    assert lib.copy_ceiling(a, b, 100, 4, 256, 0, None) == 1          # not a multiple of 16 bytes
+    assert lib.copy_ceiling(a + 8, b, 1024, 4, 256, 0, None) == 1     # misaligned source
+    assert lib.copy_ceiling(a, b, 1024, 3, 256, 0, None) == 1         # no such run length
+    assert lib.copy_ceiling(a, b, 1024, 4, 100, 0, None) == 1         # workgroup not whole waves
+    assert lib.copy_ceiling(a, a + 512, 1024, 4, 256, 0, None) == 1   # overlap
+    assert lib.copy_ceiling(None, b, 1024, 4, 256, 0, None) == 1
