@@ -231,15 +231,17 @@ bool vector_ok(const void* x, const void* w, const void* y, int dtype, const Lay
 struct Access {
     bool vec;
     bool shifted;
+    bool contiguous;   // one batch of rows N elements apart (or a single row), x and y alike
 };
 
-Access access_of(const void* x, const void* w, const void* y, int dtype, const Layout& L, int64_t M) {
+Access access_of(const void* x, const void* w, const void* y, int dtype, const Layout& L, int64_t M, int64_t N) {
     const uintptr_t es = static_cast<uintptr_t>(elem_size(dtype));
     const uintptr_t xa = reinterpret_cast<uintptr_t>(x), ya = reinterpret_cast<uintptr_t>(y);
     const bool same_layout = L.x_rs == L.y_rs && (L.batches(M) <= 1 || L.x_bs == L.y_bs);
     Access a;
     a.vec = vector_ok(x, w, y, dtype, L, M);
     a.shifted = !a.vec && aligned16(w) && xa % es == 0 && ya % es == 0 && xa % 16 == ya % 16 && same_layout;
+    a.contiguous = L.batches(M) <= 1 && (M <= 1 || L.rows <= 1 || (L.x_rs == N && L.y_rs == N));
     return a;
 }
 
@@ -322,6 +324,18 @@ int finish_plan(rmsnorm_plan_t* p, int64_t M, int64_t N, int dtype, Access acc, 
             p->row_slots = 1;
             p->lanes_per_row = p->block_threads;
             k = find_kernel(RMSNORM_VARIANT_BLOCK, dtype, 0, p->vectors_per_lane, 1, p->prefetch != 0);
+            if (!k && p->prefetch == 0) {
+                // shapes only the exact-width block form holds: one batch of contiguous rows of
+                // exactly block_threads * vectors_per_lane vectors, one trip
+                const KernelEntry* e = rmsnorm_impl::exact_block_kernel(dtype, p->vectors_per_lane, p->block_threads);
+                if (e) {
+                    if (!acc.contiguous || N != static_cast<int64_t>(p->block_threads) * p->vectors_per_lane * epv)
+                        return fail(RMSNORM_ERR_PLAN, "this block shape runs only over one batch of contiguous rows of "
+                                                      "exactly block_threads * vectors_per_lane vectors");
+                    if (p->grid < M) return fail(RMSNORM_ERR_PLAN, "this block shape runs one trip: grid must cover M");
+                    k = e;
+                }
+            }
             if (k) {
                 const int64_t cap = static_cast<int64_t>(p->block_threads) * p->vectors_per_lane * epv;
                 if (cap < N) return fail(RMSNORM_ERR_PLAN, "block plan does not cover N");
@@ -481,9 +495,18 @@ int choose_plan(int64_t M, int64_t N, int dtype, Access acc, rmsnorm_plan_t* p) 
         // 16-bit vectors per thread have no compiled kernel)
         p->block_threads = nvec <= 256 * 4 ? 256 : (nvec <= 512 * 3 ? 512 : 1024);
         p->vectors_per_lane = static_cast<int>(ceil_div(nvec, p->block_threads));
+        // contiguous 16-bit rows of exactly 16384 elements, one trip: the exact-width block
+        // form, 256 threads x 8 vectors (4096 x 16384 fp16: 45.7 us against 47.4 us with
+        // 1024 x 2)
+        if (acc.contiguous && N == 256 * 8 * elems_per_vector(dtype) && M <= kMaxGrid &&
+            rmsnorm_impl::exact_block_kernel(dtype, 8, 256)) {
+            p->block_threads = 256;
+            p->vectors_per_lane = 8;
+        }
         // rows wider than the compiled instances hold (or a ragged width the
         // widest ones have no tail path for) take the wide kernel
         const KernelEntry* k = find_kernel(RMSNORM_VARIANT_BLOCK, dtype, 0, p->vectors_per_lane, 1, false);
+        if (!k) k = rmsnorm_impl::exact_block_kernel(dtype, p->vectors_per_lane, p->block_threads);
         if (!k || (!k->tails && N % elems_per_vector(dtype) != 0)) {
             p->variant = RMSNORM_VARIANT_WIDE;
             p->block_threads = 1024;
@@ -508,6 +531,10 @@ int choose_plan(int64_t M, int64_t N, int dtype, Access acc, rmsnorm_plan_t* p) 
         int64_t cap = kBytesInFlightPerCu / row_bytes;
         if (cap < 2) cap = 2;
         if (cap < kMaxThreadsPerCu / p->block_threads) p->max_blocks_per_cu = static_cast<int>(cap);
+        // the exact-width block form: at most 3 workgroups (96 KiB of rows) per CU (4096 x 16384
+        // fp16: 45.9 us, against 46.2 with 4, 46.7 with 5, 47.0 uncapped (6 fit), 47.8 with 2)
+        if (p->variant == RMSNORM_VARIANT_BLOCK && p->vectors_per_lane == 8 && p->block_threads == 256)
+            p->max_blocks_per_cu = 3;
     }
     p->prefetch = 0;
     if (p->variant == RMSNORM_VARIANT_SHIFTED) {
@@ -1111,7 +1138,7 @@ int fwd_common(const void* x, const void* w, void* y, float* rstd, int64_t M, in
     st = check_args(x, w, y, rstd, M, N, eps, offset, dtype, L, rstd_optional);
     if (st != RMSNORM_OK) return st;
     if (plan_required && !plan) return fail(RMSNORM_ERR_NULL, "plan must be non-NULL");
-    const Access acc = access_of(x, w, y, dtype, L, M);
+    const Access acc = access_of(x, w, y, dtype, L, M, N);
     const int64_t Mb = M > 0 ? L.rows : 0;    // plans cover one batch
     rmsnorm_plan_t p;
     const KernelEntry* k = nullptr;
@@ -1164,7 +1191,7 @@ int rmsnorm_plan_query_ex(int64_t M, int64_t N, int dtype, const void* x, const 
     if (st != RMSNORM_OK) return st;
     rmsnorm_plan_t p;
     const KernelEntry* k = nullptr;
-    st = select_plan(M > 0 ? L.rows : 0, N, dtype, access_of(x, w, y, dtype, L, M), &p, &k);
+    st = select_plan(M > 0 ? L.rows : 0, N, dtype, access_of(x, w, y, dtype, L, M, N), &p, &k);
     if (st == RMSNORM_OK) st = resident_grid(&p, k, cu_count, &p.resident_grid);
     if (st != RMSNORM_OK) return st;
     *out = p;
@@ -1184,7 +1211,7 @@ int rmsnorm_plan_validate(int64_t M, int64_t N, int dtype, const void* x, const 
     if (st != RMSNORM_OK) return st;
     rmsnorm_plan_t p = *plan;
     const KernelEntry* k = nullptr;
-    st = finish_plan(&p, M, N, dtype, access_of(x, w, y, dtype, contiguous_layout(M, N), M), &k);
+    st = finish_plan(&p, M, N, dtype, access_of(x, w, y, dtype, contiguous_layout(M, N), M, N), &k);
     if (st == RMSNORM_OK) st = resident_grid(&p, k, cu_count, &p.resident_grid);
     if (st != RMSNORM_OK) return st;
     *out = p;
@@ -1199,7 +1226,7 @@ int rmsnorm_fwd_kernel_query(int64_t M, int64_t N, int dtype, const void* x, con
     if (st != RMSNORM_OK) return st;
     if (M == 0) return fail(RMSNORM_ERR_SHAPE, "M == 0 launches nothing");
     const Layout L = contiguous_layout(M, N);
-    const Access acc = access_of(x, w, y, dtype, L, M);
+    const Access acc = access_of(x, w, y, dtype, L, M, N);
     rmsnorm_plan_t p;
     if (plan) {
         p = *plan;
@@ -1232,8 +1259,10 @@ int rmsnorm_plan_resources(const rmsnorm_plan_t* plan, int dtype, int32_t* vgprs
     const KernelEntry* k = nullptr;
     const bool pf = plan->prefetch != 0;
     if (plan->variant == RMSNORM_VARIANT_GENERIC) k = find_kernel(RMSNORM_VARIANT_GENERIC, dtype, 0, 0, 1, false);
-    else if (plan->variant == RMSNORM_VARIANT_BLOCK)
+    else if (plan->variant == RMSNORM_VARIANT_BLOCK) {
         k = find_kernel(RMSNORM_VARIANT_BLOCK, dtype, 0, plan->vectors_per_lane, 1, pf);
+        if (!k && !pf) k = rmsnorm_impl::exact_block_kernel(dtype, plan->vectors_per_lane, plan->block_threads);
+    }
     else if (plan->variant == RMSNORM_VARIANT_SHIFTED)
         k = find_kernel(RMSNORM_VARIANT_SHIFTED, dtype, 0, plan->vectors_per_lane, 1, pf);
     else if (plan->variant == RMSNORM_VARIANT_WIDE)
@@ -1330,7 +1359,7 @@ int rmsnorm_plan_set_tuned(int64_t M, int64_t N, int dtype, const rmsnorm_plan_t
     if (M == 0) return fail(RMSNORM_ERR_SHAPE, "a tuned plan needs M > 0");
     rmsnorm_plan_t p = *plan;
     const KernelEntry* k = nullptr;
-    st = finish_plan(&p, M, N, dtype, access_of(nullptr, nullptr, nullptr, dtype, contiguous_layout(M, N), M),
+    st = finish_plan(&p, M, N, dtype, access_of(nullptr, nullptr, nullptr, dtype, contiguous_layout(M, N), M, N),
                      &k);  // aligned pointers
     if (st != RMSNORM_OK) return st;
     std::lock_guard<std::mutex> lock(g_tuned_mu);

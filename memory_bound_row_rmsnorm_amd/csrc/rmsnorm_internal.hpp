@@ -90,6 +90,12 @@ const KernelEntry* kernel_table(int* count);
 const KernelEntry* exact_wave_kernel(int dtype, int lanes, int vpl, int slots, int threads);
 constexpr int64_t kExactMaxRows = (int64_t{1} << 31) - (int64_t{1} << 16);
 
+// The exact-width block form with this many vectors per thread and
+// workgroup size, or nullptr.  It holds one row of exactly threads * vpt
+// vectors per workgroup and runs one trip over one batch of contiguous rows;
+// block plans with vpt vectors per thread exist only through it.
+const KernelEntry* exact_block_kernel(int dtype, int vpt, int threads);
+
 // Backward row-pass instances and the column-pass kernel (rmsnorm_bwd_kernels.hip).
 // The column pass takes (const float* partials, float* dw, int64_t G, int64_t N,
 // int32_t vec4): vec4 = 1 when N % 4 == 0 and dw is 16-byte aligned.

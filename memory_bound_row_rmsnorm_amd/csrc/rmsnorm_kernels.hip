@@ -468,6 +468,58 @@ __global__ __launch_bounds__(1024) void rmsnorm_block(KernelArgs a) {
 }
 
 // ---------------------------------------------------------------------------
+// Exact-width block form: one row of exactly T * VPT vectors per workgroup,
+// contiguous rows in one batch, one trip (grid >= M), the block family's
+// XCD row placement.  The weights stay packed and are widened at use, so 8
+// vectors per thread fit in 128 VGPRs at four 256-thread workgroups per CU,
+// where the block family's fp32 weights would need 64 more registers.
+// Measured on MI355X at 4096 x 16384 fp16 with inputs cold in HBM (one
+// process, one box): 45.7 us, against 47.4 us for the rule's 1024 x 2 block
+// plan and 47.0 us for the tuner's 512 x 4.  The dispatcher plans it only for
+// calls it fits (finish_plan).
+// ---------------------------------------------------------------------------
+template <class D, int VPT, int T>
+__global__ __launch_bounds__(T) __attribute__((amdgpu_waves_per_eu(4))) void rmsnorm_block_exact(KernelArgs a) {
+    constexpr int NW = T / 64;
+    constexpr int RV = T * VPT;           // vectors per row, and the row stride
+    __shared__ float part[NW];
+    const u32x4* __restrict__ x = static_cast<const u32x4*>(a.x);
+    const u32x4* __restrict__ w = static_cast<const u32x4*>(a.w);
+    u32x4* __restrict__ y = static_cast<u32x4*>(a.y);
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wid = tid >> 6;
+    const int64_t row = grouped_block(a.xcd_group, a.grid);
+    // no early exit past the last row: every thread reaches the barrier
+    const bool live = row < a.M;
+    const u32x4* xr = x + row * RV + tid;
+    u32x4 d[VPT];
+#pragma unroll
+    for (int v = 0; v < VPT; ++v) d[v] = live ? load_x(xr + v * T) : kZero;
+    u32x4 wq[VPT];
+#pragma unroll
+    for (int v = 0; v < VPT; ++v) wq[v] = w[v * T + tid];
+
+    const float ss = segment_allreduce<64>(sum_squares<D, VPT>(d));
+    if (lane == 0) part[wid] = ss;
+    __syncthreads();
+    float tot = part[0];
+#pragma unroll
+    for (int i = 1; i < NW; ++i) tot += part[i];
+    const float r = rsq(__builtin_fmaf(tot, a.inv_n, a.eps));
+    if (live) {
+        u32x4* yr = y + row * RV + tid;
+#pragma unroll
+        for (int v = 0; v < VPT; ++v) {
+            float we[D::EPV];
+            widen_weights<D>(we, wq[v], a.offset);
+            store_y(yr + v * T, normalise<D>(d[v], we, r));
+        }
+        if (tid == 0 && a.rstd != nullptr) store_rstd(a.rstd + row, r);
+    }
+}
+
+// ---------------------------------------------------------------------------
 // Wide family: aligned rows wider than the block family's registers hold.
 // One row per workgroup per trip, in tiles of T * VPT vectors.  A first pass
 // sums the squares tile by tile with cached loads; after the workgroup's
@@ -908,6 +960,23 @@ static const ExactEntry kExactTable[] = {
     RMS_EXACT_FAMILY(FP16, RMSNORM_FP16),
     RMS_EXACT_FAMILY(F32, RMSNORM_FP32),
 };
+
+// The exact-width block forms: 256 threads x 8 vectors, 16-bit rows of 16384 elements.
+#define RMS_BLOCK_EXACT(D, DT, V, T)                                                           \
+    {RMSNORM_VARIANT_BLOCK, DT, 0, V, 1, false, false,                                            \
+     reinterpret_cast<const void*>(&rmsnorm_block_exact<D, V, T>),                                \
+     "rmsnorm_block_exact<" #D "," #V "," #T ">"}
+
+static const ExactEntry kExactBlockTable[] = {
+    {RMS_BLOCK_EXACT(BF16, RMSNORM_BF16, 8, 256), 256},
+    {RMS_BLOCK_EXACT(FP16, RMSNORM_FP16, 8, 256), 256},
+};
+
+const KernelEntry* exact_block_kernel(int dtype, int vpt, int threads) {
+    for (const ExactEntry& e : kExactBlockTable)
+        if (e.k.dtype == dtype && e.k.vectors_per_lane == vpt && e.threads == threads) return &e.k;
+    return nullptr;
+}
 
 const KernelEntry* exact_wave_kernel(int dtype, int lanes, int vpl, int slots, int threads) {
     for (const ExactEntry& e : kExactTable)

@@ -145,9 +145,11 @@ def test_planner_choices_for_the_workloads():
     p = host_plan(8192, 3000)
     assert (p.variant, p.block_threads, p.vectors_per_lane) == (bnd.VARIANT_BLOCK, 256, 2)
     assert (p.xcd_group, p.max_blocks_per_cu) == (16, 0)
-    p = host_plan(4096, 16384, FP16)
+    p = host_plan(4096, 16384, FP16)      # contiguous rows of exactly 2048 vectors: the exact-width block form
+    assert (p.variant, p.block_threads, p.vectors_per_lane) == (bnd.VARIANT_BLOCK, 256, 8)
+    assert (p.xcd_group, p.max_blocks_per_cu) == (8, 3)
+    p = host_plan(4096, 16376, FP16)      # one vector short: the 1024-thread block plan
     assert (p.variant, p.block_threads, p.vectors_per_lane) == (bnd.VARIANT_BLOCK, 1024, 2)
-    assert (p.xcd_group, p.max_blocks_per_cu) == (8, 0)
     p = host_plan(3, 40960)
     assert (p.block_threads, p.vectors_per_lane, p.max_blocks_per_cu) == (1024, 5, 0)
     assert host_plan(3, 49152).variant == bnd.VARIANT_WIDE        # six 16-bit vectors per thread do not fit
@@ -722,3 +724,24 @@ def test_exact_form_row_limit():
     at = bnd.kernel_query(limit, 512, "bf16", A, A, A + (1 << 40), resources=False)["kernel"]
     assert below.startswith("rmsnorm_wave_exact<"), below
     assert at.startswith("rmsnorm_wave<"), at
+
+
+def test_exact_block_form_is_planned_only_where_it_fits():
+    """256 threads x 8 vectors exist only as the exact-width block form: contiguous rows of
+    exactly 16384 16-bit elements in one batch, one trip."""
+    q = bnd.kernel_query(4096, 16384, "fp16", A, A, A + (1 << 30), resources=False)
+    assert q["kernel"] == "rmsnorm_block_exact<FP16,8,256>", q
+    base = bnd.plan_query(4096, 16384, "bf16", cu_count=256)
+    assert (base.block_threads, base.vectors_per_lane) == (256, 8)
+    # a persistent grid or a ragged width cannot take it
+    assert bnd.plan_validate(4096, 16384, "bf16", base, cu_count=256) is not None
+    assert bnd.plan_validate(4096, 16384, "bf16", base.copy(grid=1024), cu_count=256) is None
+    assert bnd.plan_validate(4096, 16000, "bf16", base, cu_count=256) is None
+    # rows of a strided layout: the rule plans the 1024-thread block family instead
+    lay = bnd.Layout(0, 20000, 0, 16384, 0)
+    p = bnd.Plan()
+    assert lib.rmsnorm_plan_query_ex(4096, 16384, BF16, A, A, A + (1 << 30), bnd.ctypes.byref(lay), 256,
+                                     bnd.ctypes.byref(p)) == OK
+    assert (p.block_threads, p.vectors_per_lane) == (1024, 2)
+    # fp32 keeps its rule
+    assert bnd.plan_query(4096, 8192, "fp32", cu_count=256).vectors_per_lane != 8

@@ -127,6 +127,9 @@ def test_xcd_group_and_occupancy_cap_cover_every_row(bnd, name):
             for grid in (base.grid, 37):
                 p = base.copy(xcd_group=group, max_blocks_per_cu=cap, grid=grid,
                               prefetch=1 if grid < base.grid and base.variant != bnd.VARIANT_GENERIC else 0)
+                if grid < M and (base.block_threads, base.vectors_per_lane) == (256, 8):
+                    # the exact-width block form runs one trip only: loop with the general block plan
+                    p = p.copy(block_threads=1024, vectors_per_lane=2, lanes_per_row=1024)
                 announce(name, p.as_dict())
                 y = torch.full((M, wl.N), nan, dtype=torch.int32, device=DEV).to(torch.int16).view(xg.dtype)
                 r = torch.full((M,), float("nan"), dtype=torch.float32, device=DEV)
@@ -201,6 +204,42 @@ def test_exact_wave_forms(bnd, vectors, dtype):
         torch.cuda.synchronize()
         assert r2 is None and torch.equal(y2.view(torch.int16 if dtype != "fp32" else torch.int32),
                                           y.view(torch.int16 if dtype != "fp32" else torch.int32))
+
+
+# ---------------------------------------------------------------------------
+# 3c. The exact-width block form (contiguous 16-bit rows of exactly 16384
+#     elements, 256 threads x 8 vectors, one trip): named through
+#     rmsnorm_fwd_kernel_query, over row counts that leave XCD windows ragged,
+#     both offsets, rstd not written, in place, and with XCD groups and caps.
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("dtype", ["bf16", "fp16"])
+def test_exact_block_form(bnd, dtype):
+    N = 16384
+    g = torch.Generator().manual_seed(16384 + len(dtype))
+    td = workloads.TORCH_DTYPES[dtype]
+    sigma = 100.0 if dtype == "fp16" else 1.0
+    for M, offset, group, cap in ((1, 0.0, 8, 0), (5, 1.0, 8, 0), (77, 0.0, 8, 0), (389, 1.0, 3, 2), (389, 0.0, 64, 5)):
+        x = (torch.randn(M, N, generator=g) * sigma).to(td)
+        w = (1 + 0.1 * torch.randn(N, generator=g)).to(td)
+        xg, wg = x.to(DEV), w.to(DEV)
+        y = torch.full_like(xg, float("nan"))
+        r = torch.full((M,), float("nan"), dtype=torch.float32, device=DEV)
+        plan = bnd.plan_query(M, N, dtype, xg.data_ptr(), wg.data_ptr(), y.data_ptr()).copy(
+            xcd_group=group, max_blocks_per_cu=cap)
+        q = bnd.kernel_query(M, N, dtype, xg.data_ptr(), wg.data_ptr(), y.data_ptr(), plan=plan)
+        assert q["kernel"].startswith("rmsnorm_block_exact<") and q["scratch_bytes"] == 0, q
+        announce("exact block", M, dtype, offset, plan.as_dict(), q)
+        bnd.rmsnorm_fwd_out(xg, wg, y, r, 1e-6, offset, plan=plan)
+        torch.cuda.synchronize()
+        y_ref, r_ref = parity.oracle_for(x, w, 1e-6, offset, dtype)
+        parity.compare(y, r, y_ref, r_ref, dtype, f"exact block M={M} {dtype}")
+        y2, r2 = bnd.rmsnorm_fwd_ex(xg, wg, 1e-6, offset, want_rstd=False, plan=plan)
+        torch.cuda.synchronize()
+        assert r2 is None and torch.equal(y2.view(torch.int16), y.view(torch.int16))
+        xi = xg.clone()
+        bnd.rmsnorm_fwd_out(xi, wg, xi, r, 1e-6, offset, plan=plan)       # in place
+        torch.cuda.synchronize()
+        assert torch.equal(xi.view(torch.int16), y.view(torch.int16))
 
 
 # ---------------------------------------------------------------------------
@@ -305,6 +344,11 @@ def test_deterministic_and_grid_independent(bnd, name):
         y1, r1 = bnd.rmsnorm_fwd(xg, wg, wl.eps, wl.offset)
         assert torch.equal(y0.view(torch.int16), y1.view(torch.int16)) and torch.equal(r0, r1)
     plan = bnd.plan_query(M, wl.N, wl.dtype)
+    if plan.variant == bnd.VARIANT_BLOCK and (plan.block_threads, plan.vectors_per_lane) == (256, 8):
+        # the exact-width block form runs one trip only: grid independence of the general block
+        # plan, against its own one-trip result (a different reduction tree)
+        plan = plan.copy(block_threads=1024, vectors_per_lane=2, lanes_per_row=1024)
+        y0, r0 = bnd.rmsnorm_fwd(xg, wg, wl.eps, wl.offset, plan=plan)
     for grid in (1, 2, 7, 64):
         y2, r2 = bnd.rmsnorm_fwd(xg, wg, wl.eps, wl.offset, plan=plan.copy(grid=grid))
         assert torch.equal(y0.view(torch.int16), y2.view(torch.int16)) and torch.equal(r0, r2), grid
