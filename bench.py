@@ -494,6 +494,8 @@ def main() -> int:
             "offset": wl.offset,
             "algorithmic_bytes_per_step": nbytes,
             "rotation_sets": sets,
+            # where y lies relative to x (first rotation set): on wide rows the HBM rate depends on it
+            "y_minus_x_bytes": ys[0].data_ptr() - xs[0].data_ptr(),
             # the first rotation set's inputs (seed 0), as drawn by workloads.make_inputs
             "inputs_sha256": {"x": workloads.sha256_of(x0), "w": workloads.sha256_of(w0)},
             "inputs": ("cold in HBM" if sets * x_bytes >= ROTATION_X_BYTES
