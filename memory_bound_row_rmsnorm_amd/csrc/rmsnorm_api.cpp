@@ -267,6 +267,21 @@ const KernelEntry* find_kernel(int variant, int dtype, int lanes, int vpl, int s
 
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
+// A dispatch holds fewer than 2^32 work-items per grid dimension (the packet's
+// grid size is 32 bits) and fewer than 2^31 workgroups: the largest grid of
+// `threads`-thread workgroups one launch takes.  Larger row counts loop.
+int64_t grid_limit(int threads) {
+    const int64_t by_items = ((int64_t{1} << 32) - 1) / (threads > 0 ? threads : 1);
+    return by_items < 0x7FFFFFFF ? by_items : 0x7FFFFFFF;
+}
+
+int check_grid(const rmsnorm_plan_t* p) {
+    if (p->grid < 1 || p->grid > 0x7FFFFFFF) return fail(RMSNORM_ERR_PLAN, "grid must be in [1, 2^31)");
+    if (p->grid > grid_limit(p->block_threads))
+        return fail(RMSNORM_ERR_PLAN, "grid * block_threads must stay below 2^32 work-items");
+    return RMSNORM_OK;
+}
+
 // The instance a launch of plan p with kernel k runs: the exact-width wave
 // form when the call fits it (a non-prefetching wave plan without XCD remap
 // whose segment shape and workgroup size have an exact form, one batch of
@@ -293,7 +308,7 @@ int finish_plan(rmsnorm_plan_t* p, int64_t M, int64_t N, int dtype, Access acc, 
     const bool vec = acc.vec;
     if (p->block_threads < 64 || p->block_threads > 1024 || p->block_threads % 64 != 0)
         return fail(RMSNORM_ERR_PLAN, "block_threads must be a multiple of 64 in [64, 1024]");
-    if (p->grid < 1 || p->grid > 0x7FFFFFFF) return fail(RMSNORM_ERR_PLAN, "grid must be in [1, 2^31)");
+    if (check_grid(p) != RMSNORM_OK) return RMSNORM_ERR_PLAN;
     if (p->xcd_group < 1 || p->xcd_group > 64) return fail(RMSNORM_ERR_PLAN, "xcd_group must be in [1, 64]");
     if (p->max_blocks_per_cu != 0 && (p->max_blocks_per_cu < 2 || p->max_blocks_per_cu > 32))
         return fail(RMSNORM_ERR_PLAN, "max_blocks_per_cu must be 0 or in [2, 32]");
@@ -403,7 +418,6 @@ constexpr int kShiftedWaveSlots = 4;               // slots per wave per trip of
 // kernel is ahead of it down to short rows (262144 x 36 bf16: 61.3 against
 // 66.9 us; 262144 x 100 bf16: 62.2 against 89.5 us).
 constexpr int64_t kMinShiftedWaveN = 16;
-constexpr int64_t kMaxGrid = 0x7FFFFFFF;
 constexpr int64_t kWaveBytesInFlight = 4096;      // row bytes one wave loads per trip
 constexpr int64_t kWaveBytesInFlightMultiRow = 2048;   // the same when a slot holds several rows
 constexpr int64_t kXcdGroupBytes = 128 * 1024;    // consecutive row bytes per XCD (block family)
@@ -498,7 +512,7 @@ int choose_plan(int64_t M, int64_t N, int dtype, Access acc, rmsnorm_plan_t* p) 
         // contiguous 16-bit rows of exactly 16384 elements, one trip: the exact-width block
         // form, 256 threads x 8 vectors (4096 x 16384 fp16: 45.7 us against 47.4 us with
         // 1024 x 2)
-        if (acc.contiguous && N == 256 * 8 * elems_per_vector(dtype) && M <= kMaxGrid &&
+        if (acc.contiguous && N == 256 * 8 * elems_per_vector(dtype) && M <= grid_limit(256) &&
             rmsnorm_impl::exact_block_kernel(dtype, 8, 256)) {
             p->block_threads = 256;
             p->vectors_per_lane = 8;
@@ -517,7 +531,7 @@ int choose_plan(int64_t M, int64_t N, int dtype, Access acc, rmsnorm_plan_t* p) 
     if (p->variant == RMSNORM_VARIANT_WAVE || p->variant == RMSNORM_VARIANT_SHIFTED_WAVE)
         rows_per_trip = static_cast<int64_t>(p->block_threads / 64) * (64 / p->lanes_per_row) * p->row_slots;
     const int64_t need = M > 0 ? ceil_div(M, rows_per_trip) : 1;
-    p->grid = need < kMaxGrid ? need : kMaxGrid;
+    p->grid = std::min(need, grid_limit(p->block_threads));
     p->xcd_group = 1;
     p->max_blocks_per_cu = 0;
     if (p->variant == RMSNORM_VARIANT_BLOCK || p->variant == RMSNORM_VARIANT_SHIFTED ||
@@ -807,7 +821,7 @@ int finish_bwd_plan(rmsnorm_plan_t* p, int64_t M, int64_t N, int dtype, bool vec
                     const KernelEntry** kernel) {
     if (p->block_threads < 64 || p->block_threads > 1024 || p->block_threads % 64 != 0)
         return fail(RMSNORM_ERR_PLAN, "block_threads must be a multiple of 64 in [64, 1024]");
-    if (p->grid < 1 || p->grid > 0x7FFFFFFF) return fail(RMSNORM_ERR_PLAN, "grid must be in [1, 2^31)");
+    if (check_grid(p) != RMSNORM_OK) return RMSNORM_ERR_PLAN;
     if (p->prefetch != 0 && p->prefetch != 1) return fail(RMSNORM_ERR_PLAN, "prefetch must be 0 or 1");
     if (p->xcd_group != 1 || p->max_blocks_per_cu != 0)
         return fail(RMSNORM_ERR_PLAN, "backward plans take xcd_group 1 and max_blocks_per_cu 0");
@@ -1040,7 +1054,7 @@ int launch_bwd(const KernelEntry* k, const rmsnorm_plan_t* p, const void* x, con
     const int64_t groups = vec4 ? N / 4 : N;        // column groups
     // 4 groups per workgroup up to 256 groups (more workgroups share the reads), 16 above
     const int cols = groups <= 256 ? 4 : 16;
-    const int64_t blocks = ceil_div(groups, cols);
+    const int64_t blocks = std::min(ceil_div(groups, cols), grid_limit(cols * 64));   // more loop in the kernel
     // 64-way splits once there are enough partial rows to share
     const int split = G >= 128 ? 64 : 16;
     hipError_t e = hipLaunchKernel(rmsnorm_impl::dw_reduce_kernel(split, cols), dim3(static_cast<unsigned>(blocks)),

@@ -874,32 +874,40 @@ __global__ __launch_bounds__(COLS * SPLIT) void rmsnorm_dw_reduce(const float* _
     __shared__ float4 red[SPLIT][COLS];
     const int q = threadIdx.x % COLS;
     const int sp = threadIdx.x / COLS;
-    float4 acc = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
-    const int64_t c = vec4 ? (static_cast<int64_t>(blockIdx.x) * COLS + q) * 4
-                           : static_cast<int64_t>(blockIdx.x) * COLS + q;
-    if (c < N) {
-        if (vec4) {
+    // column blocks of COLS groups; a grid smaller than the blocks loops over
+    // them (the same count in every thread of a workgroup: the barriers stay
+    // uniform)
+    const int64_t groups = vec4 ? N / 4 : N;
+    const int64_t nblocks = (groups + COLS - 1) / COLS;
+    for (int64_t cb = blockIdx.x; cb < nblocks; cb += gridDim.x) {
+        float4 acc = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+        const int64_t c = vec4 ? (cb * COLS + q) * 4 : cb * COLS + q;
+        if (c < N) {
+            if (vec4) {
 #pragma unroll 4
-            for (int64_t i = sp; i < G; i += SPLIT) acc = add4(acc, *reinterpret_cast<const float4*>(partials + i * N + c));
-        } else {
+                for (int64_t i = sp; i < G; i += SPLIT)
+                    acc = add4(acc, *reinterpret_cast<const float4*>(partials + i * N + c));
+            } else {
 #pragma unroll 4
-            for (int64_t i = sp; i < G; i += SPLIT) acc.x += partials[i * N + c];
+                for (int64_t i = sp; i < G; i += SPLIT) acc.x += partials[i * N + c];
+            }
         }
-    }
-    red[sp][q] = acc;
-    __syncthreads();
-    constexpr int GROUPS = SPLIT / 8;    // 2 or 8 groups of 8 sub-sums
-    if (sp < GROUPS) {      // group sp reads and then overwrites only its own slots
-        float4 t = red[sp * 8][q];
-        for (int k = 1; k < 8; ++k) t = add4(t, red[sp * 8 + k][q]);
-        red[sp * 8][q] = t;
-    }
-    __syncthreads();
-    if (sp == 0 && c < N) {
-        float4 t = red[0][q];
-        for (int k = 1; k < GROUPS; ++k) t = add4(t, red[k * 8][q]);
-        if (vec4) *reinterpret_cast<float4*>(dw + c) = t;
-        else dw[c] = t.x;
+        red[sp][q] = acc;
+        __syncthreads();
+        constexpr int GROUPS = SPLIT / 8;    // 2 or 8 groups of 8 sub-sums
+        if (sp < GROUPS) {      // group sp reads and then overwrites only its own slots
+            float4 t = red[sp * 8][q];
+            for (int k = 1; k < 8; ++k) t = add4(t, red[sp * 8 + k][q]);
+            red[sp * 8][q] = t;
+        }
+        __syncthreads();
+        if (sp == 0 && c < N) {
+            float4 t = red[0][q];
+            for (int k = 1; k < GROUPS; ++k) t = add4(t, red[k * 8][q]);
+            if (vec4) *reinterpret_cast<float4*>(dw + c) = t;
+            else dw[c] = t.x;
+        }
+        __syncthreads();    // the next block's partial sums overwrite red
     }
 }
 

@@ -188,8 +188,32 @@ def test_a_single_ragged_row_takes_the_vector_kernels():
 
 
 def test_huge_row_counts_loop_with_prefetch():
+    """A dispatch takes fewer than 2^32 work-items: the grid is capped at (2^32 - 1) // threads
+    and the workgroups loop, loading the next trip ahead."""
     p = host_plan(1 << 40, 8192)
-    assert p.grid == 0x7FFFFFFF and p.trips > 1 and p.prefetch == 1
+    assert p.block_threads == 256 and p.grid == (2 ** 32 - 1) // 256
+    assert p.grid * p.block_threads < 2 ** 32 and p.trips > 1 and p.prefetch == 1
+
+
+@pytest.mark.parametrize("M,N,dtype", [(1 << 24, 2048, BF16), (1 << 24, 16384, FP16), (1 << 30, 512, BF16),
+                                       (1 << 33, 3000, BF16), (1 << 31, 3001, BF16), (1 << 33, 3, BF16)])
+def test_grids_stay_below_2_to_32_work_items(M, N, dtype):
+    """16.8M rows of 2048 bf16 (137 GB of x and y, which fits in 288 GB) ask for 2^24 workgroups of
+    256 threads: the plan caps the grid and loops instead of failing at launch."""
+    p = host_plan(M, N, dtype=dtype)
+    assert p.grid * p.block_threads < 2 ** 32 and p.grid < 2 ** 31
+    assert p.grid * p.rows_per_trip * p.trips >= M
+
+
+def test_plans_past_2_to_32_work_items_are_rejected():
+    M, N = 1 << 24, 2048
+    p = host_plan(M, N)
+    args = (A, A + (1 << 40), A + (2 << 40), A + (3 << 40), M, N, 1e-6, 0.0, BF16)
+    out = bnd.Plan()
+    for grid, status in ((p.grid, OK), (p.grid + 1, PLAN), (1 << 24, PLAN)):
+        q = p.copy(grid=grid)
+        assert lib.rmsnorm_plan_validate(M, N, BF16, args[0], args[1], args[2], ctypes.byref(q), 256,
+                                         ctypes.byref(out)) == status, grid
 
 
 @pytest.mark.parametrize("N", [257, 3001, 1025, 32761])
@@ -718,10 +742,13 @@ def test_other_launches_keep_the_general_instance():
 
 
 def test_exact_form_row_limit():
-    """32-bit row numbers: from 2^31 - 2^16 rows on, the general instance runs."""
-    limit = (1 << 31) - (1 << 16)
-    below = bnd.kernel_query(limit - 1, 512, "bf16", A, A, A + (1 << 40), resources=False)["kernel"]
-    at = bnd.kernel_query(limit, 512, "bf16", A, A, A + (1 << 40), resources=False)["kernel"]
+    """The exact form has no loop: it runs while one grid of fewer than 2^32 work-items covers the
+    rows (16 rows per 256-thread workgroup at N = 512, well inside its 32-bit row numbers); one
+    row more and the grid loops in the general instance."""
+    limit = (2 ** 32 - 1) // 256 * 16
+    assert limit < (1 << 31) - (1 << 16)
+    below = bnd.kernel_query(limit, 512, "bf16", A, A, A + (1 << 40), resources=False)["kernel"]
+    at = bnd.kernel_query(limit + 1, 512, "bf16", A, A, A + (1 << 40), resources=False)["kernel"]
     assert below.startswith("rmsnorm_wave_exact<"), below
     assert at.startswith("rmsnorm_wave<"), at
 
