@@ -5,18 +5,27 @@
 
 A step is one pass of the forward (one kernel launch) over one batch: x [M, N]
 read once, y [M, N] and rstd [M] written once, w [N] read once.  Batches
-rotate over enough distinct (x, y, rstd) buffer sets that the x read by a
-step was last touched at least 1 GiB of x earlier (four times the 256 MB
-Infinity Cache; y is written with non-temporal stores and does not displace
-x there), so its bytes come from HBM: measured, the time per step stops
-changing once the rotation passes about 400 MB of x.  All batches are
-resident in HBM before the timed region.
+rotate over S buffer sets held in one allocation (S copies of x, then S y
+buffers), with S - 1 sets holding at least 1 GiB of x (four times the 256 MB
+Infinity Cache; y is written with non-temporal stores and does not displace x
+there).  Right before the timed launches one untimed walk touches every set in
+order, and the timed launches continue the rotation, so whatever K is, every
+timed launch reads an x that was last touched S - 1 sets earlier: its bytes
+come from HBM (measured, the time per step stops changing once the rotation
+passes about 400 MB of x).  All batches are resident in HBM before the timed
+region.
 
 GB/s = (2*M*N*s + N*s + 4*M) / seconds / 1e9, the read-plus-write formula of
 "Rmsnorm Kernel Optimization" (Verification), with s = 2 bytes per element.
-The timed region is bracketed by torch.cuda.synchronize() and HIP events on
-the stream the kernels run on; in graph mode the K launches are captured once
-into a HIP graph and the timed region replays it.
+The timed region is bracketed by torch.cuda.synchronize(); HIP events on the
+stream the kernels run on time exactly K launches: the start event is recorded
+behind the walk with no host wait, so the K launches are already submitted when
+the GPU reaches it.  In graph mode the K launches (and the walk) are captured
+once into HIP graphs and the timed region replays them.
+
+The default run (the 16384 x 512 bf16 headline) also times the 32768 x 8192
+bf16 workload at four placements of y relative to x and reports it as a nested
+record ("large_workload").
 
 Prints one JSON line on stdout.
 """
@@ -152,7 +161,24 @@ def load_copy_ceiling():
     vp, i64, i32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32
     lib.copy_ceiling.argtypes = [vp, vp, i64, i32, i32, i64, vp]
     lib.copy_ceiling.restype = ctypes.c_int
+    lib.stream_part.argtypes = [vp, vp, i64, i32, i32, vp]
+    lib.stream_part.restype = ctypes.c_int
     return lib
+
+
+# the reference kernels of libcopy_ceiling.so: (name in a kernel trace, mode of stream_part, bytes per
+# x byte moved); hip_copy is copy_ceiling itself
+REFERENCE_KERNELS = {"hip_copy": ("copy_runs", 0, 2), "hip_read": ("read_runs", 1, 1),
+                     "hip_write": ("write_runs", 2, 1), "hip_empty": ("empty_runs", 3, 0)}
+
+
+def step_bytes(wl, kernel: str) -> int:
+    """Bytes one launch of `kernel` moves on workload wl: the forward's algorithmic bytes, or a
+    reference kernel's share of the M*N*s bytes of x (a copy moves them twice)."""
+    if kernel == "rmsnorm":
+        return wl.algorithmic_bytes()
+    x_bytes = wl.M * wl.N * wl.elem_bytes
+    return 2 * x_bytes if kernel == "copy" else REFERENCE_KERNELS[kernel][2] * x_bytes
 
 
 def host_cpu_model() -> str:
@@ -207,22 +233,18 @@ def bench_backward(args, wl, name, dev) -> int:
     from memory_bound_row_rmsnorm_amd import binding, workloads
 
     read_bytes = 2 * wl.M * wl.N * wl.elem_bytes
-    sets = args.sets or max(2, min(256, math.ceil(ROTATION_X_BYTES / read_bytes)))
+    sets = args.sets or rotation_sets(read_bytes)
     log(f"backward {name}: M={wl.M} N={wl.N} {wl.dtype}, {sets} rotation sets")
-    xs, dys, dxs, rs = [], [], [], []
-    x0 = w0 = dy0 = None
-    for k in range(sets):
-        x, w = workloads.make_inputs(wl, seed=k)
-        dy = workloads.make_grad(wl, seed=k)
-        if k == 0:
-            x0, w0, dy0 = x, w, dy
-        xs.append(x.to(dev))
-        dys.append(dy.to(dev))
-        dxs.append(torch.empty_like(xs[-1]))
-    w_dev = w0.to(dev)
-    for k in range(sets):           # rstd of each batch from the forward (input data only)
-        _, r = binding.rmsnorm_fwd(xs[k], w_dev, wl.eps, wl.offset)
-        rs.append(r)
+    x0, w0 = workloads.make_inputs(wl, seed=0)
+    dy0 = workloads.make_grad(wl, seed=0)
+    x_d, dy_d, w_dev = x0.to(dev), dy0.to(dev), w0.to(dev)
+    _, r_d = binding.rmsnorm_fwd(x_d, w_dev, wl.eps, wl.offset)     # rstd from the forward (input data only)
+    # every set holds the same rows (the kernels' time does not depend on the values)
+    xs = [x_d.clone() for _ in range(sets)]
+    dys = [dy_d.clone() for _ in range(sets)]
+    rs = [r_d.clone() for _ in range(sets)]
+    dxs = [torch.empty_like(x_d) for _ in range(sets)]
+    del x_d, dy_d, r_d
     dw = torch.empty(wl.N, dtype=torch.float32, device=dev)
     plan = binding.bwd_plan_query(wl.M, wl.N, wl.dtype, xs[0].data_ptr(), dys[0].data_ptr(), dxs[0].data_ptr())
     if args.plan:
@@ -234,35 +256,14 @@ def bench_backward(args, wl, name, dev) -> int:
     pplan = binding.ctypes.byref(plan)
     code = binding.DTYPE_NAMES[wl.dtype]
 
-    def launch(i, h):
-        k = i % sets
+    def launch(k, h):
         st = lib.rmsnorm_bwd_with_plan(xs[k].data_ptr(), w_dev.data_ptr(), dys[k].data_ptr(), rs[k].data_ptr(),
                                        dxs[k].data_ptr(), dw.data_ptr(), wl.M, wl.N, wl.offset, code, pplan,
                                        ws.data_ptr(), ws.numel() * 4, h)
         if st != 0:
             raise binding.RmsnormError(st, lib.rmsnorm_last_error().decode())
 
-    stream = torch.cuda.current_stream()
-    for i in range(args.warmup):
-        launch(i, stream.cuda_stream or None)
-    torch.cuda.synchronize()
-    graph = torch.cuda.CUDAGraph()
-    cap = torch.cuda.Stream()
-    cap.wait_stream(stream)
-    with torch.cuda.graph(graph, stream=cap):
-        hc = torch.cuda.current_stream().cuda_stream
-        for i in range(args.steps):
-            launch(i, hc)
-    torch.cuda.synchronize()
-    graph.replay()
-    torch.cuda.synchronize()
-    start = torch.cuda.Event(enable_timing=True)
-    end = torch.cuda.Event(enable_timing=True)
-    start.record()
-    graph.replay()
-    end.record()
-    end.synchronize()
-    ms_per_step = start.elapsed_time(end) / args.steps
+    ms_per_step, _ = time_launches(launch, sets, args.steps, args.warmup, args.mode)
     nbytes = bwd_algorithmic_bytes(wl)
     gbps = nbytes / (ms_per_step * 1e-3) / 1e9
     out = {
@@ -290,7 +291,8 @@ def bench_backward(args, wl, name, dev) -> int:
             "rotation_sets": sets,
             "inputs_sha256": {"x": workloads.sha256_of(x0), "w": workloads.sha256_of(w0),
                               "dy": workloads.sha256_of(dy0)},
-            "launch": "graph",
+            "inputs": inputs_label(sets, read_bytes),
+            "launch": args.mode,
             "plan": plan.as_dict(),
             "pct_of_peak": round(100 * gbps / PEAK_GBPS, 2),
         },
@@ -317,20 +319,315 @@ def bench_backward(args, wl, name, dev) -> int:
     return 0
 
 
+def rotation_sets(x_bytes: int, cap: int = 4096) -> int:
+    """Buffer sets for a rotation in which, between two launches on one set, the other sets stream
+    at least ROTATION_X_BYTES of x: ceil(ROTATION_X_BYTES / x_bytes) + 1 (at least 2, at most cap,
+    which only binds below 256 KiB of x per launch)."""
+    return max(2, min(cap, math.ceil(ROTATION_X_BYTES / x_bytes) + 1))
+
+
+def inputs_label(sets: int, x_bytes: int) -> str:
+    """How cold a launch's x is.  Every set is walked once, in order, right before the timed
+    launches, and they rotate over all sets, so between two touches of one x the other sets'
+    x streams (sets - 1) * x_bytes."""
+    between = (sets - 1) * x_bytes
+    if between >= ROTATION_X_BYTES:
+        return f"cold in HBM ({between / 2**20:.0f} MiB of other x between two touches of one x)"
+    return (f"warm: only {between / 2**20:.0f} MiB of other x between two touches of one x; rows may be "
+            "cache-resident (Infinity Cache), not an HBM figure")
+
+
+def time_launches(launch, sets: int, steps: int, warmup: int, mode: str):
+    """Milliseconds per launch of `launch(k, stream_handle)` (set k) and the wall seconds of the
+    bracketed region.
+
+    W eager warm-up launches; then, between two torch.cuda.synchronize() calls, one untimed walk
+    over every set in order (k = 0 .. sets-1), the start event, exactly `steps` launches on sets
+    i % sets, the end event.  The start event sits behind the walk on the same stream with no
+    host wait in between, so the timed launches are already submitted when the GPU reaches it
+    and their submission latency stays outside the events.  In graph mode the timed launches and
+    the walk are each captured once into a HIP graph (both replayed once untimed first)."""
+    import torch
+
+    stream = torch.cuda.current_stream()
+    h = stream.cuda_stream or None
+    for i in range(warmup):
+        launch(i % sets, h)
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    if mode == "graph":
+        timed, walk = torch.cuda.CUDAGraph(), torch.cuda.CUDAGraph()
+        cap = torch.cuda.Stream()
+        cap.wait_stream(stream)
+        with torch.cuda.graph(timed, stream=cap):
+            hc = torch.cuda.current_stream().cuda_stream
+            for i in range(steps):
+                launch(i % sets, hc)
+        with torch.cuda.graph(walk, stream=cap):
+            hc = torch.cuda.current_stream().cuda_stream
+            for k in range(sets):
+                launch(k, hc)
+        torch.cuda.synchronize()
+        timed.replay()
+        walk.replay()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        walk.replay()
+        start.record()
+        timed.replay()
+        end.record()
+    else:
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for k in range(sets):
+            launch(k, h)
+        start.record()
+        for i in range(steps):
+            launch(i % sets, h)
+        end.record()
+    end.synchronize()
+    torch.cuda.synchronize()
+    return start.elapsed_time(end) / steps, time.perf_counter() - t0
+
+
+class Rotation:
+    """`sets` copies of one batch's x in one allocation, followed by `sets` y buffers placed
+    `gap` bytes after the last x (y - x = sets * x_bytes + gap for every set), and rstd [sets, M].
+    Every x holds the same rows (workloads.make_inputs, seed 0): the kernels' time does not depend
+    on the values.  `place(gap)` moves the y buffers to another gap within the allocation."""
+
+    def __init__(self, wl, sets: int, dev, max_gap: int = 0):
+        import torch
+
+        from memory_bound_row_rmsnorm_amd import workloads
+
+        self.wl, self.sets = wl, sets
+        es = wl.elem_bytes
+        self.x_elems = wl.M * wl.N
+        self.x_bytes = self.x_elems * es
+        if max_gap % 256:
+            raise ValueError("gaps must be multiples of 256 bytes")
+        self.x_cpu, self.w_cpu = workloads.make_inputs(wl, seed=0)
+        td = workloads.TORCH_DTYPES[wl.dtype]
+        self.buf = torch.empty(2 * sets * self.x_elems + max_gap // es, dtype=td, device=dev)
+        self.buf[: sets * self.x_elems].view(sets, wl.M, wl.N).copy_(
+            self.x_cpu.to(dev).unsqueeze(0).expand(sets, wl.M, wl.N))
+        self.w = self.w_cpu.to(dev)
+        self.rstd = torch.empty(sets * wl.M, dtype=torch.float32, device=dev)
+        self.max_gap = max_gap
+        self.place(0)
+
+    def place(self, gap: int) -> None:
+        if gap % 256 or gap > self.max_gap:
+            raise ValueError("gap must be a multiple of 256 bytes within the allocation")
+        self.gap = gap
+        self.y_off = self.sets * self.x_elems + gap // self.wl.elem_bytes
+
+    def x(self, k):
+        return self.buf[k * self.x_elems:(k + 1) * self.x_elems].view(self.wl.M, self.wl.N)
+
+    def y(self, k):
+        o = self.y_off + k * self.x_elems
+        return self.buf[o:o + self.x_elems].view(self.wl.M, self.wl.N)
+
+    def pointers(self, k):
+        es = self.wl.elem_bytes
+        base = self.buf.data_ptr()
+        return (base + k * self.x_bytes, self.w.data_ptr(), base + (self.y_off + k * self.x_elems) * es,
+                self.rstd.data_ptr() + k * self.wl.M * 4)
+
+    def y_minus_x(self) -> int:
+        return (self.y_off) * self.wl.elem_bytes
+
+
+def forward_launcher(rot: Rotation, plan, kernel: str = "rmsnorm", copy_vpl: int = 4, copy_threads: int = 256):
+    """launch(k, stream_handle) for set k of the rotation: the forward with `plan`, torch's device
+    copy of x into y, or the streaming copy of libcopy_ceiling.so."""
+    from memory_bound_row_rmsnorm_amd import binding
+
+    wl = rot.wl
+    lib = binding.lib
+    pplan = binding.ctypes.byref(plan)
+    code = binding.DTYPE_NAMES[wl.dtype]
+    copy_lib = load_copy_ceiling() if kernel in REFERENCE_KERNELS else None
+
+    def launch(k: int, h):
+        if kernel == "copy":
+            rot.y(k).copy_(rot.x(k))
+            return
+        xp, wp, yp, rp = rot.pointers(k)
+        if kernel == "hip_copy":
+            st = copy_lib.copy_ceiling(xp, yp, rot.x_bytes, copy_vpl, copy_threads, 0, h)
+            if st != 0:
+                raise RuntimeError(f"copy_ceiling returned {st}")
+            return
+        if kernel in REFERENCE_KERNELS:
+            st = copy_lib.stream_part(xp, yp, rot.x_bytes, REFERENCE_KERNELS[kernel][1], copy_threads, h)
+            if st != 0:
+                raise RuntimeError(f"stream_part returned {st}")
+            return
+        st = lib.rmsnorm_fwd_with_plan(xp, wp, yp, rp, wl.M, wl.N, wl.eps, wl.offset, code, pplan, h)
+        if st != 0:
+            raise binding.RmsnormError(st, lib.rmsnorm_last_error().decode())
+
+    return launch
+
+
+def forward_plan(rot: Rotation, args):
+    from memory_bound_row_rmsnorm_amd import binding
+
+    wl = rot.wl
+    xp, wp, yp, _ = rot.pointers(0)
+    plan = binding.plan_query(wl.M, wl.N, wl.dtype, xp, wp, yp)
+    if args.plan:
+        plan = plan.copy(**json.loads(args.plan))
+    # the instance this call launches (the plan's, or its exact-width form) and its resources
+    res = binding.kernel_query(wl.M, wl.N, wl.dtype, xp, wp, yp, plan=plan)
+    return plan, res
+
+
+def copy_grid_items(nbytes: int, vpl: int, threads: int) -> int:
+    """Work-items of one libcopy_ceiling.so launch (one run of vpl KiB per wave)."""
+    per_block = threads // 64 * 64 * vpl
+    return -(-(nbytes // 16) // per_block) * threads
+
+
+def gbps_of(nbytes: int, ms: float) -> float:
+    return nbytes / (ms * 1e-3) / 1e9 if ms > 0 else 0.0
+
+
+LARGE = "rmsnorm_32768x8192_bf16_outliers"
+# y offsets past the last x at which the large workload is timed, in one allocation: its HBM rate
+# depends on where y lies relative to x
+LARGE_GAPS = (0, 16 << 10, 256 << 10, 16 << 20)
+
+
+def bench_large(args, dev) -> dict:
+    """The 32768 x 8192 bf16 forward (1.07 GB per launch) at each of LARGE_GAPS, same protocol."""
+    import statistics
+
+    import torch
+
+    from memory_bound_row_rmsnorm_amd import workloads
+
+    wl = workloads.WORKLOADS[LARGE]
+    sets = rotation_sets(wl.M * wl.N * wl.elem_bytes)
+    rot = Rotation(wl, sets, dev, max_gap=max(LARGE_GAPS))
+    plan, res = forward_plan(rot, argparse.Namespace(plan=None))
+    nbytes = wl.algorithmic_bytes()
+    placements = []
+    for gap in LARGE_GAPS:
+        rot.place(gap)
+        launch = forward_launcher(rot, plan)
+        ms, _ = time_launches(launch, sets, args.steps, args.warmup, args.mode)
+        placements.append({"y_minus_x_bytes": rot.y_minus_x(), "ms_per_step": round(ms, 6),
+                           "value": round(gbps_of(nbytes, ms), 2)})
+        log(f"{LARGE}: y - x = {rot.y_minus_x()} bytes: {ms * 1e3:.2f} us per step")
+    ms_med = statistics.median(p["ms_per_step"] for p in placements)
+    gbps = gbps_of(nbytes, ms_med)
+    traffic = measured_traffic(LARGE, plan.as_dict())
+    del rot
+    torch.cuda.empty_cache()
+    return {
+        "workload": LARGE, "M": wl.M, "N": wl.N, "dtype": wl.dtype, "eps": wl.eps, "offset": wl.offset,
+        "value": round(gbps, 2), "unit": "GB/s", "ms_per_step": round(ms_med, 6),
+        "statistic": f"median over {len(placements)} placements of y relative to x",
+        "min_ms_per_step": min(p["ms_per_step"] for p in placements),
+        "max_ms_per_step": max(p["ms_per_step"] for p in placements),
+        "pct_of_peak": round(100 * gbps / PEAK_GBPS, 2),
+        "algorithmic_bytes_per_step": nbytes, "rotation_sets": sets, "inputs": inputs_label(sets, wl.M * wl.N * 2),
+        "placements": placements, "plan": plan.as_dict(), "kernel_resources": res,
+        "roofline": {"bound": "hbm", "achieved": round(gbps, 2), "peak": PEAK_GBPS, "unit": "GB/s",
+                     "frac": round(gbps / PEAK_GBPS, 4), "traffic": traffic},
+    }
+
+
+def trace_fit(path: str, wl, rows: list, steps: int, kernel: str, copy_vpl: int, copy_threads: int,
+              fit_from: int) -> dict:
+    """Per-launch kernel durations of a row-count sweep from a rocprofv3 kernel_trace.csv, and the
+    least-squares line t = intercept + bytes / rate over the sweep points with M >= fit_from.
+
+    A sweep point is identified by its dispatch size (work-items), which the rows determine; its
+    timed launches are the last `steps` dispatches of that kernel and size in the trace."""
+    import csv
+    import statistics
+
+    from memory_bound_row_rmsnorm_amd import binding
+
+    if kernel != "rmsnorm" and kernel not in REFERENCE_KERNELS:
+        raise SystemExit("--trace-fit takes --kernel rmsnorm or a libcopy_ceiling.so kernel")
+    marker = "rmsnorm" if kernel == "rmsnorm" else REFERENCE_KERNELS[kernel][0]
+    by_size = {}
+    with open(path) as f:
+        for r in csv.DictReader(f):
+            name = r["Kernel_Name"]
+            if marker not in name:
+                continue
+            items = int(r["Grid_Size_X"]) * int(r["Grid_Size_Y"])
+            by_size.setdefault(items, []).append((int(r["Start_Timestamp"]), int(r["End_Timestamp"]), name))
+    points = []
+    for M in rows:
+        w = wl.with_rows(M)
+        if kernel == "rmsnorm":
+            p = binding.plan_query(M, w.N, w.dtype, cu_count=256)
+            items = p.grid * p.block_threads
+            nbytes = w.algorithmic_bytes()
+        else:
+            items = copy_grid_items(M * w.N * w.elem_bytes, copy_vpl if kernel == "hip_copy" else 4, copy_threads)
+            nbytes = step_bytes(w, kernel)
+        rec = sorted(by_size.get(items, []))
+        if len(rec) < steps:
+            raise SystemExit(f"{path}: {len(rec)} dispatches of {kernel} with {items} work-items, need {steps}")
+        timed = rec[-steps:]
+        d = sorted((e - s) / 1e3 for s, e, _ in timed)
+        span = (timed[-1][0] - timed[0][0]) / 1e3 / (steps - 1) if steps > 1 else None
+        points.append({"M": M, "bytes": nbytes, "kernel": timed[-1][2], "mean_us": round(statistics.mean(d), 4),
+                       "median_us": round(statistics.median(d), 4), "p10_us": round(d[len(d) // 10], 4),
+                       "p90_us": round(d[(9 * len(d)) // 10], 4),
+                       "start_to_start_us": round(span, 4) if span else None,
+                       "gbps_mean": round(gbps_of(nbytes, statistics.mean(d) * 1e-3), 1) if nbytes else None})
+    fit = [q for q in points if q["M"] >= fit_from]
+    n = len(fit)
+    if n >= 2 and any(q["bytes"] for q in fit):
+        xs = [q["bytes"] for q in fit]
+        ts = [q["mean_us"] for q in fit]
+        mx, mt = sum(xs) / n, sum(ts) / n
+        sxx = sum((a - mx) ** 2 for a in xs)
+        slope = sum((a - mx) * (b - mt) for a, b in zip(xs, ts)) / sxx     # us per byte
+        icpt = mt - slope * mx
+        resid = max(abs(b - (icpt + slope * a)) for a, b in zip(xs, ts))
+        line = {"intercept_us": round(icpt, 4), "rate_tb_per_s": round(1e-6 / slope, 4),
+                "max_residual_us": round(resid, 4), "points": n, "from_rows": fit_from}
+    else:
+        line = None
+    return {"trace": path, "kernel": kernel, "N": wl.N, "dtype": wl.dtype, "steps": steps, "points": points,
+            "fit": line}
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=2000)
     ap.add_argument("--warmup", type=int, default=200)
     ap.add_argument("--workload", default=None)
+    ap.add_argument("--rows", type=int, default=0, help="run the workload's recipe with this many rows")
+    ap.add_argument("--sweep-rows", default=None, metavar="M1,M2,...",
+                    help="time the forward (or --kernel) at each row count in turn, one JSON line each, and exit")
     ap.add_argument("--sets", type=int, default=0, help="rotation buffer sets (0 = auto)")
     ap.add_argument("--mode", choices=["graph", "eager"], default="graph")
     ap.add_argument("--plan", default=None, help="JSON object overriding plan fields")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-large", action="store_true",
+                    help="skip the nested 32768x8192 record of the default (headline) run")
     ap.add_argument("--traffic-from", default=None, metavar="DIR",
                     help="write profiles/traffic_<workload>.json from rocprofv3 counter CSVs in DIR "
                          "and exit (no GPU needed)")
+    ap.add_argument("--trace-fit", default=None, metavar="CSV",
+                    help="kernel durations and the intercept/rate line of a --sweep-rows run traced by "
+                         "rocprofv3 --kernel-trace, from its kernel_trace.csv (no GPU needed)")
+    ap.add_argument("--fit-from", type=int, default=1024, help="--trace-fit: fit rows from this M on")
     ap.add_argument("--cpu-threads", type=int, default=0,
                     help="threads of the CPU oracle baseline (0 = the OpenMP default: all host cores)")
     ap.add_argument("--tuned", default=None, metavar="JSON",
@@ -338,11 +635,13 @@ def main() -> int:
                          "--save) before planning")
     ap.add_argument("--pass", dest="direction", choices=["fwd", "bwd"], default="fwd",
                     help="bwd: time the backward (row pass + dw column pass) instead")
-    ap.add_argument("--kernel", choices=["rmsnorm", "copy", "hip_copy"], default="rmsnorm",
+    ap.add_argument("--kernel", choices=["rmsnorm", "copy", *REFERENCE_KERNELS], default="rmsnorm",
                     help="copy: time torch's device copy of x into y instead (the runtime's copy "
                          "kernel; same rotation, 2*M*N*s bytes per step), the counter calibration "
                          "reference; hip_copy: the streaming copy of libcopy_ceiling.so (16-byte "
-                         "non-temporal accesses, --copy-vpl KiB per wave), the practical ceiling")
+                         "non-temporal accesses, --copy-vpl KiB per wave), the practical ceiling; "
+                         "hip_read / hip_write: its read half (x only) and write half (y only); "
+                         "hip_empty: an empty kernel over the copy's grid (launch and completion)")
     ap.add_argument("--copy-vpl", type=int, default=4, choices=[1, 2, 4, 8],
                     help="hip_copy: contiguous KiB each wave moves per run")
     ap.add_argument("--copy-threads", type=int, default=256, help="hip_copy: workgroup size")
@@ -360,6 +659,17 @@ def main() -> int:
         print(json.dumps(t))
         return 0
 
+    if args.trace_fit:
+        from memory_bound_row_rmsnorm_amd import workloads
+
+        if not args.sweep_rows:
+            raise SystemExit("--trace-fit needs the --sweep-rows list of the traced run")
+        wl = workloads.WORKLOADS[args.workload or workloads.HEADLINE]
+        rows = [int(v) for v in args.sweep_rows.split(",")]
+        print(json.dumps(trace_fit(args.trace_fit, wl, rows, args.steps, args.kernel, args.copy_vpl,
+                                   args.copy_threads, args.fit_from)))
+        return 0
+
     if args.gpus != 1:
         log(f"bench.py measures one GPU only: --gpus {args.gpus} is not supported. The row "
             "RMSNorm forward shards over rows with no communication; run one process per GPU.")
@@ -371,108 +681,52 @@ def main() -> int:
 
     name = args.workload or workloads.HEADLINE
     wl = workloads.WORKLOADS[name]
+    if args.rows:
+        wl = wl.with_rows(args.rows)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     if args.direction == "bwd":
         return bench_backward(args, wl, name, dev)
-    per_set = 2 * wl.M * wl.N * wl.elem_bytes + 4 * wl.M
-    x_bytes = wl.M * wl.N * wl.elem_bytes
-    sets = args.sets or max(2, min(256, math.ceil(ROTATION_X_BYTES / x_bytes)))
-
-    log(f"workload {name}: M={wl.M} N={wl.N} {wl.dtype}, {sets} rotation sets "
-        f"({sets * per_set / 2**20:.0f} MiB), mode {args.mode}")
-    xs, ys, rs = [], [], []
-    x0 = w0 = None
-    for k in range(sets):
-        x, w = workloads.make_inputs(wl, seed=k)
-        if k == 0:
-            x0, w0 = x, w
-        xs.append(x.to(dev))
-        ys.append(torch.empty_like(xs[-1]))
-        rs.append(torch.empty(wl.M, dtype=torch.float32, device=dev))
-    w_dev = w0.to(dev)
-
     if args.tuned:
         log("tuned plans registered:", binding.load_tuned(args.tuned))
-    plan = binding.plan_query(wl.M, wl.N, wl.dtype, xs[0].data_ptr(), w_dev.data_ptr(),
-                              ys[0].data_ptr())
-    if args.plan:
-        plan = plan.copy(**json.loads(args.plan))
-    # the instance this call launches (the plan's, or its exact-width wave form) and its resources
-    res = binding.kernel_query(wl.M, wl.N, wl.dtype, xs[0].data_ptr(), w_dev.data_ptr(), ys[0].data_ptr(),
-                               plan=plan)
+
+    if args.sweep_rows:
+        for M in (int(v) for v in args.sweep_rows.split(",")):
+            w = wl.with_rows(M)
+            x_bytes = M * w.N * w.elem_bytes
+            sets = rotation_sets(x_bytes)
+            rot = Rotation(w, sets, dev)
+            plan, res = forward_plan(rot, args)
+            launch = forward_launcher(rot, plan, args.kernel, args.copy_vpl, args.copy_threads)
+            ms, _ = time_launches(launch, sets, args.steps, args.warmup, args.mode)
+            nbytes = step_bytes(w, args.kernel)
+            print(json.dumps({"M": M, "N": w.N, "dtype": w.dtype, "kernel": args.kernel,
+                              "instance": res["kernel"] if args.kernel == "rmsnorm" else args.kernel,
+                              "sets": sets, "steps": args.steps, "ms_per_step": round(ms, 6),
+                              "gbps": round(gbps_of(nbytes, ms), 1), "inputs": inputs_label(sets, x_bytes)}),
+                  flush=True)
+            del rot
+            torch.cuda.empty_cache()
+        return 0
+
+    x_bytes = wl.M * wl.N * wl.elem_bytes
+    sets = args.sets or rotation_sets(x_bytes)
+    log(f"workload {name}: M={wl.M} N={wl.N} {wl.dtype}, {sets} rotation sets "
+        f"({sets * (2 * x_bytes + 4 * wl.M) / 2**20:.0f} MiB), mode {args.mode}")
+    rot = Rotation(wl, sets, dev)
+    plan, res = forward_plan(rot, args)
     log("plan", plan.as_dict(), "resources", res)
+    launch = forward_launcher(rot, plan, args.kernel, args.copy_vpl, args.copy_threads)
+    ms_per_step, wall_s = time_launches(launch, sets, args.steps, args.warmup, args.mode)
+    nbytes = step_bytes(wl, args.kernel)
+    gbps = gbps_of(nbytes, ms_per_step)
+    log(f"{name}: {ms_per_step * 1e3:.3f} us per step, {gbps:.0f} GB/s")
+    y_minus_x = rot.y_minus_x()
+    x0, w0 = rot.x_cpu, rot.w_cpu
+    del rot
+    torch.cuda.empty_cache()
 
-    lib = binding.lib
-    pplan = binding.ctypes.byref(plan)
-    code = binding.DTYPE_NAMES[wl.dtype]
-    argv = [(xs[k].data_ptr(), w_dev.data_ptr(), ys[k].data_ptr(), rs[k].data_ptr()) for k in range(sets)]
-
-    def launch_copy(i: int, stream_handle):
-        ys[i % sets].copy_(xs[i % sets])
-
-    copy_lib = load_copy_ceiling() if args.kernel == "hip_copy" else None
-    copy_bytes = wl.M * wl.N * wl.elem_bytes
-
-    def launch_hip_copy(i: int, stream_handle):
-        st = copy_lib.copy_ceiling(xs[i % sets].data_ptr(), ys[i % sets].data_ptr(), copy_bytes, args.copy_vpl,
-                                   args.copy_threads, 0, stream_handle)
-        if st != 0:
-            raise RuntimeError(f"copy_ceiling returned {st}")
-
-    def launch(i: int, stream_handle):
-        if args.kernel == "copy":
-            return launch_copy(i, stream_handle)
-        if args.kernel == "hip_copy":
-            return launch_hip_copy(i, stream_handle)
-        xp, wp, yp, rp = argv[i % sets]
-        st = lib.rmsnorm_fwd_with_plan(xp, wp, yp, rp, wl.M, wl.N, wl.eps, wl.offset, code, pplan,
-                                       stream_handle)
-        if st != 0:
-            raise binding.RmsnormError(st, lib.rmsnorm_last_error().decode())
-
-    stream = torch.cuda.current_stream()
-    h = stream.cuda_stream or None
-    for i in range(args.warmup):
-        launch(i, h)
-    torch.cuda.synchronize()
-
-    graph = None
-    if args.mode == "graph":
-        # capture the K timed launches once; the timed region replays them
-        graph = torch.cuda.CUDAGraph()
-        cap = torch.cuda.Stream()
-        cap.wait_stream(stream)
-        with torch.cuda.graph(graph, stream=cap):
-            hc = torch.cuda.current_stream().cuda_stream
-            for i in range(args.steps):
-                launch(i, hc)
-        torch.cuda.synchronize()
-        graph.replay()          # untimed replay: first-replay setup stays out of the timing
-        torch.cuda.synchronize()
-
-    start = torch.cuda.Event(enable_timing=True)
-    end = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    t_wall = time.perf_counter()
-    if graph is not None:
-        start.record()
-        graph.replay()
-        end.record()
-    else:
-        start.record()
-        for i in range(args.steps):
-            launch(i, h)
-        end.record()
-    end.synchronize()
-    torch.cuda.synchronize()
-    wall_s = time.perf_counter() - t_wall
-    ms_total = start.elapsed_time(end)
-    ms_per_step = ms_total / args.steps
-    nbytes = wl.algorithmic_bytes() if args.kernel == "rmsnorm" else 2 * wl.M * wl.N * wl.elem_bytes
-    gbps = nbytes / (ms_per_step * 1e-3) / 1e9
-
-    traffic = measured_traffic(name, plan.as_dict()) if args.kernel == "rmsnorm" else None
+    traffic = measured_traffic(name, plan.as_dict()) if (args.kernel == "rmsnorm" and not args.rows) else None
     out = {
         "metric": metric_name("fwd", wl.M, wl.N, wl.dtype),
         "value": round(gbps, 2),
@@ -487,19 +741,18 @@ def main() -> int:
         "dtype": wl.dtype,
         "data": "synthetic",
         "config": {
-            "workload": name,
+            "workload": name if not args.rows else f"{name} with {wl.M} rows",
             "M": wl.M,
             "N": wl.N,
             "eps": wl.eps,
             "offset": wl.offset,
             "algorithmic_bytes_per_step": nbytes,
             "rotation_sets": sets,
-            # where y lies relative to x (first rotation set): on wide rows the HBM rate depends on it
-            "y_minus_x_bytes": ys[0].data_ptr() - xs[0].data_ptr(),
-            # the first rotation set's inputs (seed 0), as drawn by workloads.make_inputs
+            # where y lies relative to x (every set): on wide rows the HBM rate depends on it
+            "y_minus_x_bytes": y_minus_x,
+            # the inputs every rotation set holds (seed 0), as drawn by workloads.make_inputs
             "inputs_sha256": {"x": workloads.sha256_of(x0), "w": workloads.sha256_of(w0)},
-            "inputs": ("cold in HBM" if sets * x_bytes >= ROTATION_X_BYTES
-                       else "warm: rows may be cache-resident (Infinity Cache); not an HBM figure"),
+            "inputs": inputs_label(sets, x_bytes),
             "launch": args.mode,
             "kernel": args.kernel,
             **({"copy": {"kib_per_wave_run": args.copy_vpl, "threads": args.copy_threads}}
@@ -518,6 +771,10 @@ def main() -> int:
             "traffic": traffic,
         },
     }
+    default_run = (name == workloads.HEADLINE and not args.rows and args.kernel == "rmsnorm" and not args.plan
+                   and not args.sets and not args.tuned)
+    if default_run and not args.no_large:
+        out["large_workload"] = bench_large(args, dev)
     if not args.no_cpu_baseline and args.kernel == "rmsnorm":
         log(f"cpu baseline: oracle for about {args.cpu_seconds:.0f} s")
         out["cpu_baseline"] = cpu_baseline(wl, x0, w0, args.cpu_seconds, args.cpu_threads)

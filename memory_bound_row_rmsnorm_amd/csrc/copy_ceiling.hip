@@ -3,7 +3,9 @@
 // (x read once, y written once), with the same 16-byte non-temporal accesses.
 // It computes nothing and is not part of the RMSNorm path; the benchmark
 // times it under the same rotation and graph replay as the forward
-// (bench.py --kernel hip_copy).
+// (bench.py --kernel hip_copy), and its halves -- read only, write only, and
+// an empty launch of the same grid -- to split a launch's time into parts
+// (bench.py --kernel hip_read / hip_write / hip_empty).
 //
 // Each wave copies runs of VPL contiguous KiB: lane l moves the 16-byte
 // vectors run * 64 * VPL + v * 64 + l, v < VPL, all loads before the first
@@ -34,6 +36,71 @@ __global__ __launch_bounds__(1024) void copy_runs(const u32x4* __restrict__ src,
     }
 }
 
+// The halves of a copy, for splitting a launch's time into its parts (the
+// same geometry as copy_runs: lane l of run r touches the 16-byte vectors
+// r * 64 * VPL + v * 64 + l, v < VPL).  read_runs loads its runs and writes
+// one 16-byte fold of each run (1/(64 VPL) of the bytes read) so the loads
+// stay live; write_runs stores a pattern over every vector; empty_runs does
+// nothing (dispatch and completion of the same grid).
+template <int VPL>
+__global__ __launch_bounds__(1024) void read_runs(const u32x4* __restrict__ src, u32x4* __restrict__ dst,
+                                                  int64_t nvec) {
+    const int lane = threadIdx.x & 63;
+    const int64_t waves_per_block = blockDim.x >> 6;
+    const int64_t nwaves = static_cast<int64_t>(gridDim.x) * waves_per_block;
+    for (int64_t run = static_cast<int64_t>(blockIdx.x) * waves_per_block + (threadIdx.x >> 6);
+         run * 64 * VPL < nvec; run += nwaves) {
+        const int64_t base = run * 64 * VPL + lane;
+        u32x4 acc = {0u, 0u, 0u, 0u};
+#pragma unroll
+        for (int v = 0; v < VPL; ++v)
+            if (base + v * 64 < nvec) acc ^= __builtin_nontemporal_load(src + base + v * 64);
+        // fold the wave's 64 lanes into lane 0 with cross-lane shuffles
+        for (int o = 32; o > 0; o >>= 1) {
+            u32x4 t;
+            t.x = __shfl_xor(acc.x, o);
+            t.y = __shfl_xor(acc.y, o);
+            t.z = __shfl_xor(acc.z, o);
+            t.w = __shfl_xor(acc.w, o);
+            acc ^= t;
+        }
+        if (lane == 0) __builtin_nontemporal_store(acc, dst + run);
+    }
+}
+
+template <int VPL>
+__global__ __launch_bounds__(1024) void write_runs(const u32x4* __restrict__, u32x4* __restrict__ dst,
+                                                   int64_t nvec) {
+    const int lane = threadIdx.x & 63;
+    const int64_t waves_per_block = blockDim.x >> 6;
+    const int64_t nwaves = static_cast<int64_t>(gridDim.x) * waves_per_block;
+    for (int64_t run = static_cast<int64_t>(blockIdx.x) * waves_per_block + (threadIdx.x >> 6);
+         run * 64 * VPL < nvec; run += nwaves) {
+        const int64_t base = run * 64 * VPL + lane;
+#pragma unroll
+        for (int v = 0; v < VPL; ++v) {
+            const u32x4 d = {static_cast<uint32_t>(run), static_cast<uint32_t>(v), static_cast<uint32_t>(lane), 0u};
+            if (base + v * 64 < nvec) __builtin_nontemporal_store(d, dst + base + v * 64);
+        }
+    }
+}
+
+__global__ __launch_bounds__(1024) void empty_runs(const u32x4* __restrict__, u32x4* __restrict__, int64_t) {}
+
+int launch_runs(const void* k, const void* src, void* dst, int64_t bytes, int32_t vpl, int32_t threads, int64_t grid,
+                void* stream) {
+    if (bytes == 0) return 0;
+    int64_t nvec = bytes / 16;
+    const int64_t per_block = static_cast<int64_t>(threads / 64) * 64 * vpl;
+    int64_t g = grid > 0 ? grid : (nvec + per_block - 1) / per_block;
+    const int64_t limit = ((int64_t{1} << 32) - 1) / threads;     // fewer than 2^32 work-items
+    if (g > limit) g = limit;
+    void* args[] = {&src, &dst, &nvec};
+    hipError_t e = hipLaunchKernel(k, dim3(static_cast<unsigned>(g)), dim3(static_cast<unsigned>(threads)), args, 0,
+                                   static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? 0 : 2;
+}
+
 }  // namespace
 
 extern "C" {
@@ -61,15 +128,32 @@ int copy_ceiling(const void* src, void* dst, int64_t bytes, int32_t vpl, int32_t
     const char* s0 = static_cast<const char*>(src);
     const char* d0 = static_cast<const char*>(dst);
     if (s0 < d0 + bytes && d0 < s0 + bytes) return 1;
-    if (bytes == 0) return 0;
-    int64_t nvec = bytes / 16;
-    const int64_t per_block = static_cast<int64_t>(threads / 64) * 64 * vpl;
-    int64_t g = grid > 0 ? grid : (nvec + per_block - 1) / per_block;
-    if (g > 0x7FFFFFFF) g = 0x7FFFFFFF;
-    void* args[] = {&src, &dst, &nvec};
-    hipError_t e = hipLaunchKernel(k, dim3(static_cast<unsigned>(g)), dim3(static_cast<unsigned>(threads)), args, 0,
-                                   static_cast<hipStream_t>(stream));
-    return e == hipSuccess ? 0 : 2;
+    return launch_runs(k, src, dst, bytes, vpl, threads, grid, stream);
+}
+
+// The parts of copy_ceiling's copy, with its geometry (vpl 4): mode 1 reads
+// `bytes` from src and writes one 16-byte word per 4 KiB run to dst (dst
+// holds at least bytes / 256 bytes); mode 2 writes `bytes` to dst (src
+// unused); mode 3 launches the same grid with an empty kernel.  Arguments
+// and returns as copy_ceiling.
+int stream_part(const void* src, void* dst, int64_t bytes, int32_t mode, int32_t threads, void* stream) {
+    if (bytes < 0 || bytes % 16 != 0) return 1;
+    if (bytes > 0 && ((mode == 1 && !src) || (mode != 3 && !dst))) return 1;
+    if ((reinterpret_cast<uintptr_t>(src) | reinterpret_cast<uintptr_t>(dst)) & 15u) return 1;
+    if (threads < 64 || threads > 1024 || threads % 64 != 0) return 1;
+    const void* k = nullptr;
+    switch (mode) {
+        case 1: k = reinterpret_cast<const void*>(&read_runs<4>); break;
+        case 2: k = reinterpret_cast<const void*>(&write_runs<4>); break;
+        case 3: k = reinterpret_cast<const void*>(&empty_runs); break;
+        default: return 1;
+    }
+    if (mode == 1) {
+        const char* s0 = static_cast<const char*>(src);
+        const char* d0 = static_cast<const char*>(dst);
+        if (s0 < d0 + bytes / 256 && d0 < s0 + bytes) return 1;
+    }
+    return launch_runs(k, src, dst, bytes, 4, threads, 0, stream);
 }
 
 }  // extern "C"

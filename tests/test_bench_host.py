@@ -80,3 +80,54 @@ def test_copy_ceiling_library_rejects_bad_arguments_before_any_hip_call():
     assert lib.copy_ceiling(a, b, 1024, 4, 100, 0, None) == 1         # workgroup not whole waves
     assert lib.copy_ceiling(a, a + 512, 1024, 4, 256, 0, None) == 1   # overlap
     assert lib.copy_ceiling(None, b, 1024, 4, 256, 0, None) == 1
+
+
+def test_rotation_keeps_a_gib_of_other_x_between_two_touches():
+    """Every timed launch reads an x last touched S - 1 sets earlier; S - 1 sets hold >= 1 GiB."""
+    for x_bytes in (16 << 20, 512 << 20, 46_875_000 + 1, 64 << 20, 128 << 20, 1 << 30, 3 << 30):
+        s = bench.rotation_sets(x_bytes)
+        assert s >= 2 and (s - 1) * x_bytes >= bench.ROTATION_X_BYTES
+        assert bench.inputs_label(s, x_bytes).startswith("cold in HBM")
+    assert bench.rotation_sets(16 << 20) == 65
+    assert bench.rotation_sets(512 << 20) == 3
+    # tiny batches: the set count is capped, and the label says the rows may sit in a cache
+    s = bench.rotation_sets(16 << 10)
+    assert s == 4096 and bench.inputs_label(s, 16 << 10).startswith("warm")
+    assert bench.inputs_label(20, 16 << 20).startswith("warm")
+
+
+def _trace_row(name, start, dur, items, threads=256):
+    return (f'"KERNEL_DISPATCH","Agent 1",1,0,1,1,1,"{name}",1,{start},{start + dur},0,0,8,0,16,'
+            f'{threads},1,1,{items},1,1\n')
+
+
+def test_trace_fit_recovers_intercept_and_rate(tmp_path):
+    """Synthetic trace: t = 2 us + bytes / (7 TB/s) for the forward at several row counts (plus
+    warm-up dispatches that must not count and another kernel that must be ignored)."""
+    from memory_bound_row_rmsnorm_amd import binding
+
+    wl = workloads.WORKLOADS[workloads.HEADLINE]
+    rows = [1024, 4096, 16384, 65536]
+    path = tmp_path / "k_kernel_trace.csv"
+    t = 1_000_000
+    with open(path, "w") as f:
+        f.write('"Kind","Agent_Id","Queue_Id","Stream_Id","Thread_Id","Dispatch_Id","Kernel_Id","Kernel_Name",'
+                '"Correlation_Id","Start_Timestamp","End_Timestamp","LDS_Block_Size","Scratch_Size","VGPR_Count",'
+                '"Accum_VGPR_Count","SGPR_Count","Workgroup_Size_X","Workgroup_Size_Y","Workgroup_Size_Z",'
+                '"Grid_Size_X","Grid_Size_Y","Grid_Size_Z"\n')
+        for M in rows:
+            p = binding.plan_query(M, wl.N, wl.dtype, cu_count=256)
+            items = p.grid * p.block_threads
+            ns = round(2000 + wl.with_rows(M).algorithmic_bytes() / 7e12 * 1e9)
+            for i in range(5):            # warm-up: slower, and before the timed ones
+                f.write(_trace_row("void rmsnorm_wave_exact<...>(...)", t, 3 * ns, items))
+                t += 10 * ns
+            for i in range(10):
+                f.write(_trace_row("void rmsnorm_wave_exact<...>(...)", t, ns, items))
+                f.write(_trace_row("__amd_rocclr_fillBufferAligned", t + ns, 100, items))
+                t += 2 * ns
+    r = bench.trace_fit(str(path), wl, rows, 10, "rmsnorm", 4, 256, fit_from=1024)
+    assert r["fit"]["intercept_us"] == pytest.approx(2.0, abs=0.01)
+    assert r["fit"]["rate_tb_per_s"] == pytest.approx(7.0, rel=1e-3)
+    assert [q["M"] for q in r["points"]] == rows
+    assert all(q["median_us"] == q["mean_us"] for q in r["points"])
