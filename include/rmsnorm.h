@@ -326,6 +326,28 @@ int rmsnorm_bwd_with_plan(const void* x, const void* w, const void* dy, const fl
                           void* stream);
 
 /*
+ * rmsnorm_bwd without a workspace, for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc).  Same arguments, plan rule, results and errors as
+ * rmsnorm_bwd over contiguous [M, N] rows, minus the workspace: the dw
+ * partial rows go to a scratch array of RMSNORM_BWD_SCRATCH_BYTES (16 MiB)
+ * that the library keeps in device memory, one per GPU, for the life of the
+ * process.  The call allocates nothing (no hipMalloc, hipFree or allocating
+ * library routine).  Where the rule's grid needs more partial rows than fit
+ * (grid * N * 4 > RMSNORM_BWD_SCRATCH_BYTES) the grid shrinks to fit and the
+ * row pass loops, so dw may then differ from rmsnorm_bwd's in rounding only;
+ * N > RMSNORM_BWD_SCRATCH_BYTES / 4 is rejected with RMSNORM_ERR_SHAPE before
+ * any HIP call.  All calls on one GPU share its scratch: two calls that run at
+ * the same time on one GPU (different streams, no ordering between them) race
+ * and give wrong dw; calls ordered on one stream do not.  The first call on a
+ * device looks the scratch address up (hipGetSymbolAddress) with that device
+ * current; a failure there returns RMSNORM_ERR_HIP.
+ */
+#define RMSNORM_BWD_SCRATCH_BYTES (16 * 1024 * 1024)
+int rmsnorm_bwd_noalloc(const void* x, const void* w, const void* dy, const float* rstd, void* dx,
+                        float* dw, int64_t M, int64_t N, float offset, int dtype, void* stream);
+
+/*
  * Row layout of the backward's x, dy and dx, as rmsnorm_layout_t for the
  * forward ("Rmsnorm Kernel Optimization", Verification: the operation runs
  * over the last dimension of a tensor of any rank).  Row m = b * rows + s

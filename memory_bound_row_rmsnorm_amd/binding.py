@@ -36,6 +36,7 @@ EXPORTED = (
     "rmsnorm_fwd", "rmsnorm_fwd_with_plan", "rmsnorm_fwd_ex", "rmsnorm_plan_query", "rmsnorm_plan_query_ex",
     "rmsnorm_plan_resources", "rmsnorm_fwd_kernel_query",
     "rmsnorm_bwd", "rmsnorm_bwd_with_plan", "rmsnorm_bwd_plan_query", "rmsnorm_bwd_workspace_size",
+    "rmsnorm_bwd_noalloc",
     "rmsnorm_bwd_ex", "rmsnorm_bwd_plan_query_ex", "rmsnorm_bwd_workspace_size_ex",
     "rmsnorm_plan_validate", "rmsnorm_plan_set_tuned", "rmsnorm_plan_clear_tuned", "rmsnorm_plan_tuned_count",
     "rmsnorm_status_string", "rmsnorm_last_error", "rmsnorm_version",
@@ -132,6 +133,8 @@ def _load():
     lib.rmsnorm_fwd_kernel_query.restype = i32
     lib.rmsnorm_bwd.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, f32, i32, vp, i64, vp]
     lib.rmsnorm_bwd.restype = i32
+    lib.rmsnorm_bwd_noalloc.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, f32, i32, vp]
+    lib.rmsnorm_bwd_noalloc.restype = i32
     lib.rmsnorm_bwd_with_plan.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, f32, i32,
                                           ctypes.POINTER(Plan), vp, i64, vp]
     lib.rmsnorm_bwd_with_plan.restype = i32
@@ -474,6 +477,34 @@ def rmsnorm_bwd(x: torch.Tensor, w: torch.Tensor, dy: torch.Tensor, rstd: torch.
         nbytes = plan.grid * N * 4 if M > 0 else 0
     ws = torch.empty((max(nbytes, 16) + 3) // 4, dtype=torch.float32, device=x.device)
     rmsnorm_bwd_out(x, w, dy, rstd, dx, dw, ws, offset, plan, stream)
+    return dx, dw
+
+
+def rmsnorm_bwd_noalloc_out(x: torch.Tensor, w: torch.Tensor, dy: torch.Tensor, rstd: torch.Tensor,
+                            dx: torch.Tensor, dw: torch.Tensor, offset: float = 0.0, stream=None) -> None:
+    """rmsnorm_bwd_noalloc into caller-provided dx and dw: no workspace, nothing allocated (the
+    library's per-GPU scratch holds the dw partial rows)."""
+    _check_tensors(x, w)
+    M, N = x.shape
+    for t, name in ((dy, "dy"), (dx, "dx")):
+        if t.shape != x.shape or t.dtype != x.dtype or not t.is_contiguous() or t.device != x.device:
+            raise ValueError(f"{name} must be a contiguous tensor shaped and typed like x on x's device")
+    if rstd.dtype != torch.float32 or rstd.shape != (M,) or not rstd.is_contiguous():
+        raise ValueError("rstd must be a contiguous float32 tensor of shape (M,)")
+    if dw.dtype != torch.float32 or dw.shape != (N,) or not dw.is_contiguous():
+        raise ValueError("dw must be a contiguous float32 tensor of shape (N,)")
+    with torch.cuda.device(x.device):      # the scratch of x's device
+        _check(lib.rmsnorm_bwd_noalloc(x.data_ptr() or None, w.data_ptr() or None, dy.data_ptr() or None,
+                                       rstd.data_ptr() or None, dx.data_ptr() or None, dw.data_ptr(), M, N,
+                                       float(offset), _dtype_code(x.dtype), _stream_handle(stream)))
+
+
+def rmsnorm_bwd_noalloc(x: torch.Tensor, w: torch.Tensor, dy: torch.Tensor, rstd: torch.Tensor,
+                        offset: float = 0.0, stream=None):
+    """rmsnorm_bwd without a workspace (the library's scratch); returns (dx, dw)."""
+    dx = torch.empty_like(x)
+    dw = torch.empty((x.shape[1],), dtype=torch.float32, device=x.device)
+    rmsnorm_bwd_noalloc_out(x, w, dy, rstd, dx, dw, offset, stream)
     return dx, dw
 
 

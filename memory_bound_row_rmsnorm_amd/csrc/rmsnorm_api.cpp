@@ -1365,6 +1365,39 @@ int rmsnorm_bwd_ex(const void* x, const void* w, const void* dy, const float* rs
                       stream);
 }
 
+int rmsnorm_bwd_noalloc(const void* x, const void* w, const void* dy, const float* rstd, void* dx, float* dw,
+                        int64_t M, int64_t N, float offset, int dtype, void* stream) {
+    g_last_error.clear();
+    int st = check_shape_dtype(M, N, dtype);
+    if (st != RMSNORM_OK) return st;
+    const BwdLayout L = contiguous_bwd_layout(M, N);
+    st = check_bwd_args(x, w, dy, rstd, dx, dw, M, N, offset, dtype, L);
+    if (st != RMSNORM_OK) return st;
+    constexpr int64_t kScratch = RMSNORM_BWD_SCRATCH_BYTES;
+    if (N > kScratch / 4)
+        return fail(RMSNORM_ERR_SHAPE, "rmsnorm_bwd_noalloc holds one fp32 partial row of N columns in its " +
+                                           std::to_string(kScratch) + "-byte scratch: N must be at most " +
+                                           std::to_string(kScratch / 4));
+    const bool vec = bwd_vector_ok(x, w, dy, dx, dtype, L, M, N);
+    const bool shifted = bwd_shifted_ok(x, w, dy, dx, dtype, L, M, N, vec);
+    rmsnorm_plan_t p;
+    choose_bwd_plan(M, N, vec, shifted, dtype, &p);
+    // the rule's plan, with no more partial rows than the scratch holds (the row pass loops instead)
+    p.grid = std::min<int64_t>(p.grid, kScratch / (N * 4));
+    const KernelEntry* k = nullptr;
+    st = finish_bwd_plan(&p, M, N, dtype, vec, shifted, &k);
+    if (st != RMSNORM_OK) return st;
+    int cu = 0;
+    st = device_info(&cu);
+    if (st != RMSNORM_OK) return st;
+    void* scratch = nullptr;
+    if (M > 0) {
+        const char* err = rmsnorm_impl::bwd_scratch(&scratch);
+        if (err) return fail(RMSNORM_ERR_HIP, std::string("scratch: ") + err);
+    }
+    return launch_bwd(k, &p, x, w, dy, rstd, dx, dw, M, N, offset, L, scratch, stream);
+}
+
 int rmsnorm_plan_set_tuned(int64_t M, int64_t N, int dtype, const rmsnorm_plan_t* plan) {
     g_last_error.clear();
     if (!plan) return fail(RMSNORM_ERR_NULL, "plan must be non-NULL");

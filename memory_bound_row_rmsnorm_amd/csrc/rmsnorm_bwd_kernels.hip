@@ -26,6 +26,8 @@
 #include "rmsnorm_internal.hpp"
 #include "../../include/rmsnorm.h"
 
+#include <mutex>
+
 using namespace rmsnorm_dev;
 using rmsnorm_impl::BwdArgs;
 
@@ -973,6 +975,39 @@ static const KernelEntry kBwdTable[] = {
 const KernelEntry* bwd_kernel_table(int* count) {
     *count = static_cast<int>(sizeof(kBwdTable) / sizeof(kBwdTable[0]));
     return kBwdTable;
+}
+
+// The dw partial rows of rmsnorm_bwd_noalloc, which takes no workspace: a
+// file-scope device array of RMSNORM_BWD_SCRATCH_BYTES that every GPU the
+// library runs on holds for the life of the process (zero-filled when the
+// code object loads; the row pass overwrites every partial row it uses before
+// the column pass reads it, so nothing needs clearing between calls).  On the
+// host `scratch` names a stand-in, not a device address: kernels get the
+// address bwd_scratch() looked up for the current device.
+static __device__ __align__(256) float scratch[RMSNORM_BWD_SCRATCH_BYTES / 4];
+
+namespace {
+constexpr int kScratchDevices = 64;
+struct ScratchSlot {
+    std::once_flag once;
+    hipError_t err = hipSuccess;
+    void* ptr = nullptr;
+};
+ScratchSlot g_scratch[kScratchDevices];
+}  // namespace
+
+const char* bwd_scratch(void** ptr) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hipGetErrorString(e);
+    if (dev < 0 || dev >= kScratchDevices) return "device ordinal out of range";
+    ScratchSlot& s = g_scratch[dev];
+    // once per device, with that device current (it is: dev is the calling thread's device)
+    std::call_once(s.once, [&s]() { s.err = hipGetSymbolAddress(&s.ptr, HIP_SYMBOL(scratch)); });
+    if (s.err != hipSuccess) return hipGetErrorString(s.err);
+    if (s.ptr == nullptr) return "hipGetSymbolAddress returned no address for the scratch array";
+    *ptr = s.ptr;
+    return nullptr;
 }
 
 const void* dw_reduce_kernel(int split, int cols) {

@@ -103,4 +103,9 @@ const KernelEntry* bwd_kernel_table(int* count);
 // split 16 or 64, cols (column groups per workgroup) 4 or 16: cols * split threads
 const void* dw_reduce_kernel(int split, int cols);
 
+// Device address of the current device's RMSNORM_BWD_SCRATCH_BYTES scratch
+// array (rmsnorm_bwd_noalloc's dw partial rows), looked up once per device.
+// Returns nullptr and sets *ptr, or returns the error text.
+const char* bwd_scratch(void** ptr);
+
 }  // namespace rmsnorm_impl

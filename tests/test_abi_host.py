@@ -307,6 +307,34 @@ def bwd(x=X, w=W, dy=DY, rstd=R, dx=DX, dw=DW, M=4, N=512, offset=0.0, dtype=BF1
     return lib.rmsnorm_bwd(x, w, dy, rstd, dx, dw, M, N, offset, dtype, ws, ws_bytes, None)
 
 
+def bwd_noalloc(x=X, w=W, dy=DY, rstd=R, dx=DX, dw=DW, M=4, N=512, offset=0.0, dtype=BF16):
+    return lib.rmsnorm_bwd_noalloc(x, w, dy, rstd, dx, dw, M, N, offset, dtype, None)
+
+
+@pytest.mark.parametrize("kwargs,status", [
+    (dict(M=-1), SHAPE),
+    (dict(N=0), SHAPE),
+    (dict(dtype=7), DTYPE),
+    (dict(dw=None), NULL),
+    (dict(x=None), NULL),
+    (dict(offset=float("nan")), SCALAR),
+    (dict(dx=X), OVERLAP),
+    (dict(dw=DX + 64), OVERLAP),
+    (dict(N=4 * 1024 * 1024 + 8, M=1), SHAPE),     # one partial row of N fp32 exceeds the 16 MiB scratch
+])
+def test_bwd_noalloc_argument_errors(kwargs, status):
+    """rmsnorm_bwd_noalloc checks its arguments, and that a partial row fits its scratch, before
+    any HIP call (these calls make none)."""
+    assert bwd_noalloc(**kwargs) == status
+
+
+def test_bwd_noalloc_scratch_limit_is_the_header_constant():
+    text = open(HEADER).read()
+    assert re.search(r"#define RMSNORM_BWD_SCRATCH_BYTES \(16 \* 1024 \* 1024\)", text)
+    for N in (4 * 1024 * 1024 + 1, 4 * 1024 * 1024 + 8, 1 << 23):
+        assert bwd_noalloc(N=N, M=1) == SHAPE, N
+
+
 @pytest.mark.parametrize("kwargs,status", [
     (dict(M=-1), SHAPE),
     (dict(N=0), SHAPE),
