@@ -18,10 +18,12 @@ region.
 GB/s = (2*M*N*s + N*s + 4*M) / seconds / 1e9, the read-plus-write formula of
 "Rmsnorm Kernel Optimization" (Verification), with s = 2 bytes per element.
 The timed region is bracketed by torch.cuda.synchronize(); HIP events on the
-stream the kernels run on time exactly K launches: the start event is recorded
-behind the walk with no host wait, so the K launches are already submitted when
-the GPU reaches it.  In graph mode the K launches (and the walk) are captured
-once into HIP graphs and the timed region replays them.
+stream the kernels run on time it.  In graph mode (the default) the walk and
+the K launches behind it are captured into one HIP graph, and the walk alone
+into another; the time of the K launches is the first replay's time minus the
+second's, so a graph launch's fixed cost, the same in both, cancels, and the K
+launches run back to back behind the walk as in a long stream of launches.
+The figure is the median of five such pairs of replays.
 
 The default run (the 16384 x 512 bf16 headline) also times the 32768 x 8192
 bf16 workload at four placements of y relative to x and reports it as a nested
@@ -337,16 +339,24 @@ def inputs_label(sets: int, x_bytes: int) -> str:
             "cache-resident (Infinity Cache), not an HBM figure")
 
 
+REGIONS = 5       # timed regions per measurement (median)
+
+
 def time_launches(launch, sets: int, steps: int, warmup: int, mode: str):
     """Milliseconds per launch of `launch(k, stream_handle)` (set k) and the wall seconds of the
     bracketed region.
 
-    W eager warm-up launches; then, between two torch.cuda.synchronize() calls, one untimed walk
-    over every set in order (k = 0 .. sets-1), the start event, exactly `steps` launches on sets
-    i % sets, the end event.  The start event sits behind the walk on the same stream with no
-    host wait in between, so the timed launches are already submitted when the GPU reaches it
-    and their submission latency stays outside the events.  In graph mode the timed launches and
-    the walk are each captured once into a HIP graph (both replayed once untimed first)."""
+    W eager warm-up launches first.  Graph mode: two HIP graphs are captured, the walk (one launch
+    on every set in order, k = 0 .. sets-1) and the walk followed, in the same graph, by exactly
+    `steps` launches on sets i % sets.  Between torch.cuda.synchronize() calls, HIP events on the
+    launch stream time one replay of the second graph and then one of the walk alone; their
+    difference is the time of the `steps` launches running back to back behind the walk, as in a
+    long stream of launches.  A graph launch and its event pair cost about 5-10 us once (the same
+    in both replays, so it cancels; left in, it would add 0.3 us per step at 20 steps).  The
+    result is the median over REGIONS such pairs.  Eager mode: the walk, the start event, `steps`
+    launches, the end event."""
+    import statistics
+
     import torch
 
     stream = torch.cuda.current_stream()
@@ -354,40 +364,58 @@ def time_launches(launch, sets: int, steps: int, warmup: int, mode: str):
     for i in range(warmup):
         launch(i % sets, h)
     torch.cuda.synchronize()
-    start = torch.cuda.Event(enable_timing=True)
-    end = torch.cuda.Event(enable_timing=True)
+
+    def timed(fn):
+        start = torch.cuda.Event(enable_timing=True)
+        end = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        start.record()
+        fn()
+        end.record()
+        end.synchronize()
+        torch.cuda.synchronize()
+        return start.elapsed_time(end)
+
     if mode == "graph":
-        timed, walk = torch.cuda.CUDAGraph(), torch.cuda.CUDAGraph()
+        walk, walk_steps = torch.cuda.CUDAGraph(), torch.cuda.CUDAGraph()
         cap = torch.cuda.Stream()
         cap.wait_stream(stream)
-        with torch.cuda.graph(timed, stream=cap):
-            hc = torch.cuda.current_stream().cuda_stream
-            for i in range(steps):
-                launch(i % sets, hc)
         with torch.cuda.graph(walk, stream=cap):
             hc = torch.cuda.current_stream().cuda_stream
             for k in range(sets):
                 launch(k, hc)
+        with torch.cuda.graph(walk_steps, stream=cap):
+            hc = torch.cuda.current_stream().cuda_stream
+            for k in range(sets):
+                launch(k, hc)
+            for i in range(steps):
+                launch(i % sets, hc)
         torch.cuda.synchronize()
-        timed.replay()
+        walk_steps.replay()         # first replays: set-up stays out
         walk.replay()
         torch.cuda.synchronize()
         t0 = time.perf_counter()
-        walk.replay()
-        start.record()
-        timed.replay()
-        end.record()
-    else:
-        torch.cuda.synchronize()
-        t0 = time.perf_counter()
+        diffs = [timed(walk_steps.replay) - timed(walk.replay) for _ in range(REGIONS)]
+        wall = time.perf_counter() - t0
+        time_launches.regions = [round(d / steps, 6) for d in diffs]
+        return statistics.median(diffs) / steps, wall
+
+    def eager():
         for k in range(sets):
             launch(k, h)
-        start.record()
-        for i in range(steps):
-            launch(i % sets, h)
-        end.record()
+
+    torch.cuda.synchronize()
+    eager()
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    start.record()
+    for i in range(steps):
+        launch(i % sets, h)
+    end.record()
     end.synchronize()
     torch.cuda.synchronize()
+    time_launches.regions = [round(start.elapsed_time(end) / steps, 6)]
     return start.elapsed_time(end) / steps, time.perf_counter() - t0
 
 
@@ -397,7 +425,12 @@ class Rotation:
     Every x holds the same rows (workloads.make_inputs, seed 0): the kernels' time does not depend
     on the values.  `place(gap)` moves the y buffers to another gap within the allocation."""
 
-    def __init__(self, wl, sets: int, dev, max_gap: int = 0):
+    @staticmethod
+    def elems(wl, sets: int, max_gap: int = 0) -> int:
+        """Elements of the allocation a rotation of `sets` sets of wl needs."""
+        return 2 * sets * wl.M * wl.N + max_gap // wl.elem_bytes
+
+    def __init__(self, wl, sets: int, dev, max_gap: int = 0, buf=None):
         import torch
 
         from memory_bound_row_rmsnorm_amd import workloads
@@ -410,7 +443,13 @@ class Rotation:
             raise ValueError("gaps must be multiples of 256 bytes")
         self.x_cpu, self.w_cpu = workloads.make_inputs(wl, seed=0)
         td = workloads.TORCH_DTYPES[wl.dtype]
-        self.buf = torch.empty(2 * sets * self.x_elems + max_gap // es, dtype=td, device=dev)
+        need = Rotation.elems(wl, sets, max_gap)
+        if buf is None:
+            self.buf = torch.empty(need, dtype=td, device=dev)
+        else:                  # a slice of a caller's allocation (one allocation serves a whole sweep)
+            if buf.numel() < need or buf.dtype != td:
+                raise ValueError("the allocation is too small for this rotation")
+            self.buf = buf[:need]
         self.buf[: sets * self.x_elems].view(sets, wl.M, wl.N).copy_(
             self.x_cpu.to(dev).unsqueeze(0).expand(sets, wl.M, wl.N))
         self.w = self.w_cpu.to(dev)
@@ -503,17 +542,19 @@ LARGE = "rmsnorm_32768x8192_bf16_outliers"
 LARGE_GAPS = (0, 16 << 10, 256 << 10, 16 << 20)
 
 
-def bench_large(args, dev) -> dict:
-    """The 32768 x 8192 bf16 forward (1.07 GB per launch) at each of LARGE_GAPS, same protocol."""
-    import statistics
-
-    import torch
-
+def large_rotation(dev):
+    """The rotation of the 32768 x 8192 workload, with room for every gap of LARGE_GAPS."""
     from memory_bound_row_rmsnorm_amd import workloads
 
     wl = workloads.WORKLOADS[LARGE]
-    sets = rotation_sets(wl.M * wl.N * wl.elem_bytes)
-    rot = Rotation(wl, sets, dev, max_gap=max(LARGE_GAPS))
+    return Rotation(wl, rotation_sets(wl.M * wl.N * wl.elem_bytes), dev, max_gap=max(LARGE_GAPS))
+
+
+def bench_large(args, rot) -> dict:
+    """The 32768 x 8192 bf16 forward (1.07 GB per launch) at each of LARGE_GAPS, same protocol."""
+    import statistics
+
+    wl, sets = rot.wl, rot.sets
     plan, res = forward_plan(rot, argparse.Namespace(plan=None))
     nbytes = wl.algorithmic_bytes()
     placements = []
@@ -522,13 +563,12 @@ def bench_large(args, dev) -> dict:
         launch = forward_launcher(rot, plan)
         ms, _ = time_launches(launch, sets, args.steps, args.warmup, args.mode)
         placements.append({"y_minus_x_bytes": rot.y_minus_x(), "ms_per_step": round(ms, 6),
-                           "value": round(gbps_of(nbytes, ms), 2)})
+                           "value": round(gbps_of(nbytes, ms), 2),
+                           "ms_per_step_regions": time_launches.regions})
         log(f"{LARGE}: y - x = {rot.y_minus_x()} bytes: {ms * 1e3:.2f} us per step")
     ms_med = statistics.median(p["ms_per_step"] for p in placements)
     gbps = gbps_of(nbytes, ms_med)
     traffic = measured_traffic(LARGE, plan.as_dict())
-    del rot
-    torch.cuda.empty_cache()
     return {
         "workload": LARGE, "M": wl.M, "N": wl.N, "dtype": wl.dtype, "eps": wl.eps, "offset": wl.offset,
         "value": round(gbps, 2), "unit": "GB/s", "ms_per_step": round(ms_med, 6),
@@ -691,11 +731,16 @@ def main() -> int:
         log("tuned plans registered:", binding.load_tuned(args.tuned))
 
     if args.sweep_rows:
-        for M in (int(v) for v in args.sweep_rows.split(",")):
+        rows = [int(v) for v in args.sweep_rows.split(",")]
+        # one allocation for every row count, as large as the largest rotation needs (allocations
+        # made after others were freed measured up to 7% slower on 16384 x 512)
+        cap = max(Rotation.elems(wl.with_rows(M), rotation_sets(M * wl.N * wl.elem_bytes)) for M in rows)
+        pool = torch.empty(cap, dtype=workloads.TORCH_DTYPES[wl.dtype], device=dev)
+        for M in rows:
             w = wl.with_rows(M)
             x_bytes = M * w.N * w.elem_bytes
             sets = rotation_sets(x_bytes)
-            rot = Rotation(w, sets, dev)
+            rot = Rotation(w, sets, dev, buf=pool)
             plan, res = forward_plan(rot, args)
             launch = forward_launcher(rot, plan, args.kernel, args.copy_vpl, args.copy_threads)
             ms, _ = time_launches(launch, sets, args.steps, args.warmup, args.mode)
@@ -706,13 +751,17 @@ def main() -> int:
                               "gbps": round(gbps_of(nbytes, ms), 1), "inputs": inputs_label(sets, x_bytes)}),
                   flush=True)
             del rot
-            torch.cuda.empty_cache()
         return 0
 
     x_bytes = wl.M * wl.N * wl.elem_bytes
     sets = args.sets or rotation_sets(x_bytes)
     log(f"workload {name}: M={wl.M} N={wl.N} {wl.dtype}, {sets} rotation sets "
         f"({sets * (2 * x_bytes + 4 * wl.M) / 2**20:.0f} MiB), mode {args.mode}")
+    default_run = (name == workloads.HEADLINE and not args.rows and args.kernel == "rmsnorm" and not args.plan
+                   and not args.sets and not args.tuned)
+    # both rotations are allocated before either is timed (an allocation made after a large one was
+    # freed measured up to 7% slower)
+    large_rot = large_rotation(dev) if default_run and not args.no_large else None
     rot = Rotation(wl, sets, dev)
     plan, res = forward_plan(rot, args)
     log("plan", plan.as_dict(), "resources", res)
@@ -723,8 +772,6 @@ def main() -> int:
     log(f"{name}: {ms_per_step * 1e3:.3f} us per step, {gbps:.0f} GB/s")
     y_minus_x = rot.y_minus_x()
     x0, w0 = rot.x_cpu, rot.w_cpu
-    del rot
-    torch.cuda.empty_cache()
 
     traffic = measured_traffic(name, plan.as_dict()) if (args.kernel == "rmsnorm" and not args.rows) else None
     out = {
@@ -761,6 +808,8 @@ def main() -> int:
             "kernel_resources": res,
             "pct_of_peak": round(100 * gbps / PEAK_GBPS, 2),
             "wall_s_timed_region": round(wall_s, 4),
+            # the per-step time of each timed region (the value is their median)
+            "ms_per_step_regions": time_launches.regions,
         },
         "roofline": {
             "bound": "hbm",
@@ -771,10 +820,9 @@ def main() -> int:
             "traffic": traffic,
         },
     }
-    default_run = (name == workloads.HEADLINE and not args.rows and args.kernel == "rmsnorm" and not args.plan
-                   and not args.sets and not args.tuned)
-    if default_run and not args.no_large:
-        out["large_workload"] = bench_large(args, dev)
+    if large_rot is not None:
+        out["large_workload"] = bench_large(args, large_rot)
+    del rot, large_rot
     if not args.no_cpu_baseline and args.kernel == "rmsnorm":
         log(f"cpu baseline: oracle for about {args.cpu_seconds:.0f} s")
         out["cpu_baseline"] = cpu_baseline(wl, x0, w0, args.cpu_seconds, args.cpu_threads)

@@ -113,7 +113,7 @@ typedef enum rmsnorm_variant {
  *                     SHIFTED: 1 = fetch the row's weights with its x and pass
  *                     neighbouring weight vectors between lanes, 0 = fetch them
  *                     after the row's reduction; 0 otherwise
- *   xcd_group         1 to 64: the rows of this many consecutive workgroups
+ *   xcd_group         1 to 256: the rows of this many consecutive workgroups
  *                     run on one XCD (MI355X hands workgroup b to XCD b mod 8;
  *                     the workgroup index is permuted within windows of
  *                     8 * xcd_group workgroups).  1 leaves the order alone

@@ -34,6 +34,7 @@ constexpr int kMaxDevices = 64;
 constexpr int kWaveBlockThreads = 256;   // 4 waves per workgroup for the wave family, one row per slot
 constexpr int kWaveBlockThreadsMultiRow = 128;   // 2 waves when a slot holds several rows
 constexpr int kMaxThreadsPerCu = 2048;   // 4 SIMDs x 8 waves x 64 lanes
+constexpr int kMaxXcdGroup = 256;        // largest xcd_group a plan takes
 
 thread_local std::string g_last_error;
 
@@ -309,7 +310,8 @@ int finish_plan(rmsnorm_plan_t* p, int64_t M, int64_t N, int dtype, Access acc, 
     if (p->block_threads < 64 || p->block_threads > 1024 || p->block_threads % 64 != 0)
         return fail(RMSNORM_ERR_PLAN, "block_threads must be a multiple of 64 in [64, 1024]");
     if (check_grid(p) != RMSNORM_OK) return RMSNORM_ERR_PLAN;
-    if (p->xcd_group < 1 || p->xcd_group > 64) return fail(RMSNORM_ERR_PLAN, "xcd_group must be in [1, 64]");
+    if (p->xcd_group < 1 || p->xcd_group > kMaxXcdGroup)
+        return fail(RMSNORM_ERR_PLAN, "xcd_group must be in [1, " + std::to_string(kMaxXcdGroup) + "]");
     if (p->max_blocks_per_cu != 0 && (p->max_blocks_per_cu < 2 || p->max_blocks_per_cu > 32))
         return fail(RMSNORM_ERR_PLAN, "max_blocks_per_cu must be 0 or in [2, 32]");
     const KernelEntry* k = nullptr;
@@ -421,7 +423,10 @@ constexpr int64_t kMinShiftedWaveN = 16;
 constexpr int64_t kWaveBytesInFlight = 4096;      // row bytes one wave loads per trip
 constexpr int64_t kWaveBytesInFlightMultiRow = 2048;   // the same when a slot holds several rows
 constexpr int64_t kXcdGroupBytes = 128 * 1024;    // consecutive row bytes per XCD (block family)
+constexpr int64_t kXcdGroupBytesLarge = 1024 * 1024;   // the same for batches beyond the Infinity Cache
+constexpr int64_t kInfinityCacheBytes = 256LL * 1024 * 1024;
 constexpr int64_t kBytesInFlightPerCu = 64 * 1024; // row bytes resident per compute unit (block family)
+constexpr int kMinBlocksPerCu = 3;                 // the occupancy cap never goes below this
 
 // Choose family and geometry (host only; no device needed).  A row is
 // nvec = ceil(N / EPV) 16-byte vectors (EPV = 8 for bf16/fp16, 4 for fp32).
@@ -438,10 +443,20 @@ constexpr int64_t kBytesInFlightPerCu = 64 * 1024; // row bytes resident per com
 //    measured faster than a grid of resident workgroups looping over rows on
 //    every shape tried;
 //  * block family: consecutive rows grouped on one XCD, about 128 KiB per
-//    group (xcd_group: 8 rows at 16 KiB rows, 16 at 6000-byte rows), and at
-//    most about 64 KiB of rows resident per compute unit (max_blocks_per_cu
-//    4 at 16 KiB rows); together 5-6% faster on 32768 x 8192, 4% on
-//    8192 x 3000.
+//    group (xcd_group 16 at 6000-byte rows), or about 1 MiB per group when
+//    one batch of x exceeds the 256 MB Infinity Cache (xcd_group 64 at 16 KiB
+//    rows, 128 at 8 KiB, 32 at 32 KiB); and at most about 64 KiB of rows, but
+//    never fewer than 3 workgroups, resident per compute unit
+//    (max_blocks_per_cu 4 at 16 KiB rows, 3 at 24 KiB).  The 128 KiB groups
+//    are 5-6% faster than none on 32768 x 8192 at a favourable placement of
+//    y relative to x, but the rate then follows that placement over a 10%
+//    range (165-181 us); 1 MiB groups hold 169-171 us at every placement
+//    measured, and lift the median over placements by 1-3.5% at 4 KiB to
+//    32 KiB rows.
+//    Below 256 MB the placement does not matter and 128 KiB groups lead
+//    (8192 x 3000: 18.1 us against 18.7 with 384 KiB groups).  A cap of 2 at
+//    24 KiB rows left 512-thread workgroups at 193 us on 21840 x 12288,
+//    against 173 us with 3.
 int choose_plan(int64_t M, int64_t N, int dtype, Access acc, rmsnorm_plan_t* p) {
     std::memset(p, 0, sizeof(*p));
     const bool vec = acc.vec;
@@ -536,14 +551,16 @@ int choose_plan(int64_t M, int64_t N, int dtype, Access acc, rmsnorm_plan_t* p) 
     p->max_blocks_per_cu = 0;
     if (p->variant == RMSNORM_VARIANT_BLOCK || p->variant == RMSNORM_VARIANT_SHIFTED ||
         p->variant == RMSNORM_VARIANT_WIDE) {
-        // about 128 KiB of consecutive rows per XCD (a power of two, at least 8 rows)
+        // about 128 KiB (1 MiB beyond the Infinity Cache) of consecutive rows per XCD: the
+        // nearest power of two rows, at least 8
         const int64_t row_bytes = N * es;
+        const int64_t target = M * row_bytes >= kInfinityCacheBytes ? kXcdGroupBytesLarge : kXcdGroupBytes;
         int g = 8;
-        while (g < 64 && row_bytes * g * 3 < kXcdGroupBytes * 2) g *= 2;  // nearest power of two
+        while (g < kMaxXcdGroup && row_bytes * g * 3 < target * 2) g *= 2;
         p->xcd_group = g;
-        // about 64 KiB of rows in flight per compute unit
+        // about 64 KiB of rows in flight per compute unit, at least 3 workgroups
         int64_t cap = kBytesInFlightPerCu / row_bytes;
-        if (cap < 2) cap = 2;
+        if (cap < kMinBlocksPerCu) cap = kMinBlocksPerCu;
         if (cap < kMaxThreadsPerCu / p->block_threads) p->max_blocks_per_cu = static_cast<int>(cap);
         // the exact-width block form: at most 3 workgroups (96 KiB of rows) per CU (4096 x 16384
         // fp16: 45.9 us, against 46.2 with 4, 46.7 with 5, 47.0 uncapped (6 fit), 47.8 with 2)

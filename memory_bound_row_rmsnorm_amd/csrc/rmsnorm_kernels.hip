@@ -165,9 +165,13 @@ __device__ __forceinline__ void store_vec(u32x4* row, int c, int nfull, int tail
 // (b mod 8) * g + (b / 8) mod g within the window: a transpose of the window,
 // so every index in [0, G) is still used exactly once (a tail shorter
 // than a window keeps its own order).  Consecutive rows then share an L2 and
-// reach HBM as longer runs of neighbouring addresses; measured on MI355X it
-// shortens the 32768 x 8192 forward by 4-5%.
-// (32-bit arithmetic: grids stay below 2^31 workgroups and windows below 2^10.)
+// reach HBM as longer runs of neighbouring addresses.  Measured on MI355X:
+// groups of about 128 KiB of rows shorten the 32768 x 8192 forward by 4-5% at
+// a favourable placement of y relative to x but leave its rate following that
+// placement over a 10% range; groups of about 1 MiB hold it at every
+// placement measured (the planner's choice for batches beyond the 256 MB
+// Infinity Cache).
+// (32-bit arithmetic: grids stay below 2^31 workgroups and windows below 2^12.)
 __device__ __forceinline__ int64_t grouped_block(int g, int64_t G) {
     const uint32_t b = blockIdx.x;
     if (__builtin_expect(g <= 1, 1)) return b;

@@ -60,7 +60,7 @@ def candidates(M: int, N: int, dtype: str, quick: bool = False) -> list:
             raw.append(base.copy(variant=1, lanes_per_row=lanes, vectors_per_lane=vpl, row_slots=slots,
                                  block_threads=threads, prefetch=0, xcd_group=1, max_blocks_per_cu=0,
                                  grid=-(-M // rows_per_trip)))
-        groups = (1, 8, 16) if quick else (1, 4, 8, 16, 32)
+        groups = (1, 8, 16, 64) if quick else (1, 4, 8, 16, 32, 64, 128)
         caps = (0, 4) if quick else (0, 2, 3, 4, 6, 8)
         for threads in threads_set:
             if threads > max(64, nvec):

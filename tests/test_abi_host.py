@@ -124,7 +124,7 @@ def test_host_plans_cover_the_row_one_trip_per_workgroup(M, N):
         if p.max_blocks_per_cu:
             per_cu = min(per_cu, p.max_blocks_per_cu)
         assert p.resident_grid == 256 * per_cu
-        assert 1 <= p.xcd_group <= 64
+        assert 1 <= p.xcd_group <= 256
 
 
 def test_planner_choices_for_the_workloads():
@@ -138,9 +138,10 @@ def test_planner_choices_for_the_workloads():
     assert (p.lanes_per_row, p.row_slots, p.block_threads) == (32, 2, 128)
     p = host_plan(100, 1024)
     assert (p.lanes_per_row, p.vectors_per_lane, p.row_slots) == (64, 2, 2)
-    p = host_plan(32768, 8192)
+    p = host_plan(32768, 8192)            # 512 MiB of x: about 1 MiB of rows per XCD group
     assert (p.variant, p.block_threads, p.vectors_per_lane) == (bnd.VARIANT_BLOCK, 256, 4)
-    assert (p.xcd_group, p.max_blocks_per_cu) == (8, 4)
+    assert (p.xcd_group, p.max_blocks_per_cu) == (64, 4)
+    assert host_plan(16383, 8192).xcd_group == 8          # just under 256 MiB of x: 128 KiB groups
     assert p.resident_grid == 256 * 4
     p = host_plan(8192, 3000)
     assert (p.variant, p.block_threads, p.vectors_per_lane) == (bnd.VARIANT_BLOCK, 256, 2)
@@ -272,7 +273,7 @@ def test_plans_that_do_not_fit_are_rejected_before_launch():
         good.copy(variant=7),
         good.copy(variant=bnd.VARIANT_BLOCK, block_threads=64, vectors_per_lane=8),  # not compiled
         good.copy(xcd_group=0),
-        good.copy(xcd_group=65),
+        good.copy(xcd_group=257),
         good.copy(max_blocks_per_cu=1),
         good.copy(max_blocks_per_cu=33),
         good.copy(max_blocks_per_cu=-2),
