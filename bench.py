@@ -34,6 +34,7 @@ Prints one JSON line on stdout.
 from __future__ import annotations
 
 import argparse
+import dataclasses
 import hashlib
 import json
 import math
@@ -550,27 +551,28 @@ def large_rotation(dev):
     return Rotation(wl, rotation_sets(wl.M * wl.N * wl.elem_bytes), dev, max_gap=max(LARGE_GAPS))
 
 
-def bench_large(args, rot) -> dict:
-    """The 32768 x 8192 bf16 forward (1.07 GB per launch) at each of LARGE_GAPS, same protocol."""
+def bench_placements(args, rot, gaps, plan_json=None) -> dict:
+    """The forward on rotation `rot` with y placed at each of `gaps` bytes after the last x (same
+    protocol each time); the median over the placements is the record's value."""
     import statistics
 
     wl, sets = rot.wl, rot.sets
-    plan, res = forward_plan(rot, argparse.Namespace(plan=None))
+    plan, res = forward_plan(rot, argparse.Namespace(plan=plan_json))
     nbytes = wl.algorithmic_bytes()
     placements = []
-    for gap in LARGE_GAPS:
+    for gap in gaps:
         rot.place(gap)
         launch = forward_launcher(rot, plan)
         ms, _ = time_launches(launch, sets, args.steps, args.warmup, args.mode)
         placements.append({"y_minus_x_bytes": rot.y_minus_x(), "ms_per_step": round(ms, 6),
                            "value": round(gbps_of(nbytes, ms), 2),
                            "ms_per_step_regions": time_launches.regions})
-        log(f"{LARGE}: y - x = {rot.y_minus_x()} bytes: {ms * 1e3:.2f} us per step")
+        log(f"{wl.name} {wl.M}x{wl.N}: y - x = {rot.y_minus_x()} bytes: {ms * 1e3:.2f} us per step")
     ms_med = statistics.median(p["ms_per_step"] for p in placements)
     gbps = gbps_of(nbytes, ms_med)
-    traffic = measured_traffic(LARGE, plan.as_dict())
+    traffic = measured_traffic(wl.name, plan.as_dict())
     return {
-        "workload": LARGE, "M": wl.M, "N": wl.N, "dtype": wl.dtype, "eps": wl.eps, "offset": wl.offset,
+        "workload": wl.name, "M": wl.M, "N": wl.N, "dtype": wl.dtype, "eps": wl.eps, "offset": wl.offset,
         "value": round(gbps, 2), "unit": "GB/s", "ms_per_step": round(ms_med, 6),
         "statistic": f"median over {len(placements)} placements of y relative to x",
         "min_ms_per_step": min(p["ms_per_step"] for p in placements),
@@ -652,6 +654,7 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=200)
     ap.add_argument("--workload", default=None)
     ap.add_argument("--rows", type=int, default=0, help="run the workload's recipe with this many rows")
+    ap.add_argument("--cols", type=int, default=0, help="run the workload's recipe with rows of this many columns")
     ap.add_argument("--sweep-rows", default=None, metavar="M1,M2,...",
                     help="time the forward (or --kernel) at each row count in turn, one JSON line each, and exit")
     ap.add_argument("--sets", type=int, default=0, help="rotation buffer sets (0 = auto)")
@@ -661,6 +664,9 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-large", action="store_true",
                     help="skip the nested 32768x8192 record of the default (headline) run")
+    ap.add_argument("--y-gaps", default=None, metavar="B1,B2,...",
+                    help="time the forward with y placed at each of these byte gaps after the last x (one "
+                         "allocation; --plan applies), print one JSON record of the placements, and exit")
     ap.add_argument("--traffic-from", default=None, metavar="DIR",
                     help="write profiles/traffic_<workload>.json from rocprofv3 counter CSVs in DIR "
                          "and exit (no GPU needed)")
@@ -723,12 +729,22 @@ def main() -> int:
     wl = workloads.WORKLOADS[name]
     if args.rows:
         wl = wl.with_rows(args.rows)
+    if args.cols:
+        wl = dataclasses.replace(wl, N=args.cols)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     if args.direction == "bwd":
         return bench_backward(args, wl, name, dev)
     if args.tuned:
         log("tuned plans registered:", binding.load_tuned(args.tuned))
+
+    if args.y_gaps:
+        gaps = [int(v) for v in args.y_gaps.split(",")]
+        rot = Rotation(wl, args.sets or rotation_sets(wl.M * wl.N * wl.elem_bytes), dev, max_gap=max(gaps))
+        rec = bench_placements(args, rot, gaps, args.plan)
+        rec["metric"] = metric_name("fwd", wl.M, wl.N, wl.dtype)
+        print(json.dumps(rec), flush=True)
+        return 0
 
     if args.sweep_rows:
         rows = [int(v) for v in args.sweep_rows.split(",")]
@@ -757,8 +773,8 @@ def main() -> int:
     sets = args.sets or rotation_sets(x_bytes)
     log(f"workload {name}: M={wl.M} N={wl.N} {wl.dtype}, {sets} rotation sets "
         f"({sets * (2 * x_bytes + 4 * wl.M) / 2**20:.0f} MiB), mode {args.mode}")
-    default_run = (name == workloads.HEADLINE and not args.rows and args.kernel == "rmsnorm" and not args.plan
-                   and not args.sets and not args.tuned)
+    default_run = (name == workloads.HEADLINE and not args.rows and not args.cols and args.kernel == "rmsnorm"
+                   and not args.plan and not args.sets and not args.tuned)
     # both rotations are allocated before either is timed (an allocation made after a large one was
     # freed measured up to 7% slower)
     large_rot = large_rotation(dev) if default_run and not args.no_large else None
@@ -773,7 +789,8 @@ def main() -> int:
     y_minus_x = rot.y_minus_x()
     x0, w0 = rot.x_cpu, rot.w_cpu
 
-    traffic = measured_traffic(name, plan.as_dict()) if (args.kernel == "rmsnorm" and not args.rows) else None
+    reshaped = bool(args.rows or args.cols)
+    traffic = measured_traffic(name, plan.as_dict()) if (args.kernel == "rmsnorm" and not reshaped) else None
     out = {
         "metric": metric_name("fwd", wl.M, wl.N, wl.dtype),
         "value": round(gbps, 2),
@@ -788,7 +805,7 @@ def main() -> int:
         "dtype": wl.dtype,
         "data": "synthetic",
         "config": {
-            "workload": name if not args.rows else f"{name} with {wl.M} rows",
+            "workload": name if not reshaped else f"{name} recipe at {wl.M} x {wl.N}",
             "M": wl.M,
             "N": wl.N,
             "eps": wl.eps,
@@ -821,7 +838,7 @@ def main() -> int:
         },
     }
     if large_rot is not None:
-        out["large_workload"] = bench_large(args, large_rot)
+        out["large_workload"] = bench_placements(args, large_rot, LARGE_GAPS)
     del rot, large_rot
     if not args.no_cpu_baseline and args.kernel == "rmsnorm":
         log(f"cpu baseline: oracle for about {args.cpu_seconds:.0f} s")
