@@ -38,10 +38,11 @@ __global__ __launch_bounds__(1024) void copy_runs(const u32x4* __restrict__ src,
 
 // The halves of a copy, for splitting a launch's time into its parts (the
 // same geometry as copy_runs: lane l of run r touches the 16-byte vectors
-// r * 64 * VPL + v * 64 + l, v < VPL).  read_runs loads its runs and writes
-// one 16-byte fold of each run (1/(64 VPL) of the bytes read) so the loads
-// stay live; write_runs stores a pattern over every vector; empty_runs does
-// nothing (dispatch and completion of the same grid).
+// r * 64 * VPL + v * 64 + l, v < VPL).  read_runs loads its runs and stores
+// only when a lane's xor of them equals a fixed 128-bit pattern (which keeps
+// the loads live; with real data it practically never happens, and a store
+// stays inside dst's bytes / 256); write_runs stores a pattern over every
+// vector; empty_runs does nothing (dispatch and completion of the same grid).
 template <int VPL>
 __global__ __launch_bounds__(1024) void read_runs(const u32x4* __restrict__ src, u32x4* __restrict__ dst,
                                                   int64_t nvec) {
@@ -55,16 +56,8 @@ __global__ __launch_bounds__(1024) void read_runs(const u32x4* __restrict__ src,
 #pragma unroll
         for (int v = 0; v < VPL; ++v)
             if (base + v * 64 < nvec) acc ^= __builtin_nontemporal_load(src + base + v * 64);
-        // fold the wave's 64 lanes into lane 0 with cross-lane shuffles
-        for (int o = 32; o > 0; o >>= 1) {
-            u32x4 t;
-            t.x = __shfl_xor(acc.x, o);
-            t.y = __shfl_xor(acc.y, o);
-            t.z = __shfl_xor(acc.z, o);
-            t.w = __shfl_xor(acc.w, o);
-            acc ^= t;
-        }
-        if (lane == 0) __builtin_nontemporal_store(acc, dst + run);
+        if (acc.x == 0x9e3779b9u && acc.y == 0x7f4a7c15u && acc.z == 0xf39cc060u && acc.w == 0x5ced1a2bu)
+            dst[run] = acc;
     }
 }
 
