@@ -283,21 +283,29 @@ int check_grid(const rmsnorm_plan_t* p) {
     return RMSNORM_OK;
 }
 
-// The instance a launch of plan p with kernel k runs: the exact-width wave
-// form when the call fits it (a non-prefetching wave plan without XCD remap
-// whose segment shape and workgroup size have an exact form, one batch of
-// contiguous rows of exactly lanes * vectors vectors, one trip,
-// fewer than kExactMaxRows rows, row numbers of the whole grid below 2^31),
-// k otherwise.  M is the rows of one batch, `batches` the batch count.  Host
-// only.
+// The instance a launch of plan p with kernel k runs: an exact-width form
+// when the call fits it, k otherwise.  Both need a non-prefetching plan, one
+// batch of contiguous rows of exactly (segment or workgroup) * vectors
+// vectors, one trip, and row numbers of the whole grid below 2^31.  The
+// wave form also needs no XCD remap and fewer than kExactMaxRows rows and
+// keeps the plan's segment shape and workgroup size; the block form (256
+// threads x 4 or 8 vectors) keeps the plan's XCD groups and cap.  M is the
+// rows of one batch, `batches` the batch count.  Host only.
 const KernelEntry* launch_instance(const KernelEntry* k, const rmsnorm_plan_t* p, int64_t M, int64_t N, int dtype,
                                    const Layout& L, int64_t batches) {
-    if (k->variant != RMSNORM_VARIANT_WAVE || k->prefetch || p->xcd_group != 1) return k;
-    if (batches != 1 || M >= rmsnorm_impl::kExactMaxRows) return k;
+    if (k->prefetch || batches != 1) return k;
+    if (k->variant != RMSNORM_VARIANT_WAVE && k->variant != RMSNORM_VARIANT_BLOCK) return k;
     if (M > 1 && (L.x_rs != N || L.y_rs != N)) return k;
-    if (N != static_cast<int64_t>(p->lanes_per_row) * p->vectors_per_lane * elems_per_vector(dtype)) return k;
     const int64_t covered = p->grid * p->rows_per_trip;
     if (covered < M || covered >= (int64_t{1} << 31)) return k;
+    const int64_t epv = elems_per_vector(dtype);
+    if (k->variant == RMSNORM_VARIANT_BLOCK) {
+        if (N != static_cast<int64_t>(p->block_threads) * p->vectors_per_lane * epv) return k;
+        const KernelEntry* e = rmsnorm_impl::exact_block_kernel(dtype, p->vectors_per_lane, p->block_threads);
+        return e ? e : k;
+    }
+    if (p->xcd_group != 1 || M >= rmsnorm_impl::kExactMaxRows) return k;
+    if (N != static_cast<int64_t>(p->lanes_per_row) * p->vectors_per_lane * epv) return k;
     const KernelEntry* e = rmsnorm_impl::exact_wave_kernel(dtype, p->lanes_per_row, p->vectors_per_lane,
                                                            p->row_slots, p->block_threads);
     return e ? e : k;
@@ -562,9 +570,13 @@ int choose_plan(int64_t M, int64_t N, int dtype, Access acc, rmsnorm_plan_t* p) 
         int64_t cap = kBytesInFlightPerCu / row_bytes;
         if (cap < kMinBlocksPerCu) cap = kMinBlocksPerCu;
         if (cap < kMaxThreadsPerCu / p->block_threads) p->max_blocks_per_cu = static_cast<int>(cap);
-        // the exact-width block form: at most 3 workgroups (96 KiB of rows) per CU (4096 x 16384
-        // fp16: 45.9 us, against 46.2 with 4, 46.7 with 5, 47.0 uncapped (6 fit), 47.8 with 2)
-        if (p->variant == RMSNORM_VARIANT_BLOCK && p->vectors_per_lane == 8 && p->block_threads == 256)
+        // the exact-width block forms (launch_instance): at most 3 workgroups per CU
+        // (4096 x 16384 fp16, 256 x 8: 45.9 us against 46.2 with 4, 46.7 with 5, 47.0
+        // uncapped, 47.8 with 2; 32768 x 8192 bf16, 256 x 4: 167.2-168.1 us over eight
+        // placements of y, against 170.0 with 4 and 175.5 with 2)
+        if (p->variant == RMSNORM_VARIANT_BLOCK && acc.contiguous && p->block_threads == 256 &&
+            N == static_cast<int64_t>(p->block_threads) * p->vectors_per_lane * elems_per_vector(dtype) &&
+            p->grid >= M && rmsnorm_impl::exact_block_kernel(dtype, p->vectors_per_lane, p->block_threads))
             p->max_blocks_per_cu = 3;
     }
     p->prefetch = 0;

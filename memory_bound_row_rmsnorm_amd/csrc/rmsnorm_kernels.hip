@@ -476,11 +476,16 @@ __global__ __launch_bounds__(1024) void rmsnorm_block(KernelArgs a) {
 // contiguous rows in one batch, one trip (grid >= M), the block family's
 // XCD row placement.  The weights stay packed and are widened at use, so 8
 // vectors per thread fit in 128 VGPRs at four 256-thread workgroups per CU,
-// where the block family's fp32 weights would need 64 more registers.
-// Measured on MI355X at 4096 x 16384 fp16 with inputs cold in HBM (one
-// process, one box): 45.7 us, against 47.4 us for the rule's 1024 x 2 block
-// plan and 47.0 us for the tuner's 512 x 4.  The dispatcher plans it only for
-// calls it fits (finish_plan).
+// where the block family's fp32 weights would need 64 more registers.  With
+// no row loop, no column mask and no branch around a load, all of a thread's
+// loads issue back to back and the arithmetic starts as each vector lands.
+// Measured on MI355X with inputs cold in HBM, at most 3 workgroups per CU:
+// 4096 x 16384 fp16 (256 x 8) 45.1 us, against 47.4 us for 1024 x 2 block
+// plans and 47.0 us for 512 x 4; 32768 x 8192 bf16 (256 x 4) 167.2-168.1 us
+// (medians over eight placements of y, two boxes) against 169.1-169.9 us for
+// the block family's 256 x 4 at its best cap of 4 (the exact form at 4 per
+// CU: 170.0 us).  Launches switch to it wherever the call fits
+// (launch_instance).
 // ---------------------------------------------------------------------------
 template <class D, int VPT, int T>
 __global__ __launch_bounds__(T) __attribute__((amdgpu_waves_per_eu(4))) void rmsnorm_block_exact(KernelArgs a) {
@@ -494,15 +499,20 @@ __global__ __launch_bounds__(T) __attribute__((amdgpu_waves_per_eu(4))) void rms
     const int lane = tid & 63;
     const int wid = tid >> 6;
     const int64_t row = grouped_block(a.xcd_group, a.grid);
-    // no early exit past the last row: every thread reaches the barrier
+    // no early exit past the last row: every thread reaches the barrier.  A
+    // workgroup past it reads row 0 and stores nothing, so every load is
+    // unconditional: a load under a branch made the compiler wait for the
+    // first vector before issuing the other fifteen loads of the row.
     const bool live = row < a.M;
-    const u32x4* xr = x + row * RV + tid;
+    const u32x4* xr = x + (live ? row : 0) * RV + tid;
     u32x4 d[VPT];
 #pragma unroll
-    for (int v = 0; v < VPT; ++v) d[v] = live ? load_x(xr + v * T) : kZero;
+    for (int v = 0; v < VPT; ++v) d[v] = load_x(xr + v * T);
     u32x4 wq[VPT];
 #pragma unroll
     for (int v = 0; v < VPT; ++v) wq[v] = w[v * T + tid];
+    // nothing that uses a loaded value moves above this point
+    __builtin_amdgcn_sched_barrier(0);
 
     const float ss = segment_allreduce<64>(sum_squares<D, VPT>(d));
     if (lane == 0) part[wid] = ss;
@@ -965,7 +975,8 @@ static const ExactEntry kExactTable[] = {
     RMS_EXACT_FAMILY(F32, RMSNORM_FP32),
 };
 
-// The exact-width block forms: 256 threads x 8 vectors, 16-bit rows of 16384 elements.
+// The exact-width block forms: 256 threads x 8 vectors (16-bit rows of 16384
+// elements) and 256 threads x 4 vectors (16-bit rows of 8192, fp32 rows of 4096).
 #define RMS_BLOCK_EXACT(D, DT, V, T)                                                           \
     {RMSNORM_VARIANT_BLOCK, DT, 0, V, 1, false, false,                                            \
      reinterpret_cast<const void*>(&rmsnorm_block_exact<D, V, T>),                                \
@@ -974,6 +985,9 @@ static const ExactEntry kExactTable[] = {
 static const ExactEntry kExactBlockTable[] = {
     {RMS_BLOCK_EXACT(BF16, RMSNORM_BF16, 8, 256), 256},
     {RMS_BLOCK_EXACT(FP16, RMSNORM_FP16, 8, 256), 256},
+    {RMS_BLOCK_EXACT(BF16, RMSNORM_BF16, 4, 256), 256},
+    {RMS_BLOCK_EXACT(FP16, RMSNORM_FP16, 4, 256), 256},
+    {RMS_BLOCK_EXACT(F32, RMSNORM_FP32, 4, 256), 256},
 };
 
 const KernelEntry* exact_block_kernel(int dtype, int vpt, int threads) {

@@ -140,9 +140,11 @@ def test_planner_choices_for_the_workloads():
     assert (p.lanes_per_row, p.vectors_per_lane, p.row_slots) == (64, 2, 2)
     p = host_plan(32768, 8192)            # 512 MiB of x: about 1 MiB of rows per XCD group
     assert (p.variant, p.block_threads, p.vectors_per_lane) == (bnd.VARIANT_BLOCK, 256, 4)
-    assert (p.xcd_group, p.max_blocks_per_cu) == (64, 4)
+    assert (p.xcd_group, p.max_blocks_per_cu) == (64, 3)  # contiguous exact-width rows: capped at 3
     assert host_plan(16383, 8192).xcd_group == 8          # just under 256 MiB of x: 128 KiB groups
-    assert p.resident_grid == 256 * 4
+    assert p.resident_grid == 256 * 3
+    p = host_plan(32768, 8000)            # not an exact width: the block family's cap of 64 KiB of rows
+    assert (p.block_threads, p.vectors_per_lane, p.max_blocks_per_cu) == (256, 4, 4)
     p = host_plan(8192, 3000)
     assert (p.variant, p.block_threads, p.vectors_per_lane) == (bnd.VARIANT_BLOCK, 256, 2)
     assert (p.xcd_group, p.max_blocks_per_cu) == (16, 0)
@@ -764,8 +766,13 @@ def test_other_launches_keep_the_general_instance():
     # no exact form for this segment shape or workgroup size
     assert name(base.copy(row_slots=8)).startswith("rmsnorm_wave<")
     assert name(base.copy(block_threads=512, grid=512)).startswith("rmsnorm_wave<")
-    # other families are untouched
-    assert name(n=8192).startswith("rmsnorm_block<")
+    # the block family has its own exact forms (rows of exactly 1024 vectors here); a width
+    # below the plan's full row, a persistent grid or prefetching keep the general instance
+    assert name(n=8192) == "rmsnorm_block_exact<BF16,4,256>"
+    assert name(n=8000).startswith("rmsnorm_block<")
+    blk = bnd.plan_query(M, 8192, "bf16", cu_count=256)
+    assert name(blk.copy(grid=1024), n=8192).startswith("rmsnorm_block<")
+    assert name(blk.copy(prefetch=1, grid=1024), n=8192).startswith("rmsnorm_block<")
     with pytest.raises(bnd.RmsnormError):
         name(m=0)
 
@@ -801,3 +808,19 @@ def test_exact_block_form_is_planned_only_where_it_fits():
     assert (p.block_threads, p.vectors_per_lane) == (1024, 2)
     # fp32 keeps its rule
     assert bnd.plan_query(4096, 8192, "fp32", cu_count=256).vectors_per_lane != 8
+
+
+@pytest.mark.parametrize("dtype,N", [("bf16", 8192), ("fp16", 8192), ("fp32", 4096)])
+def test_exact_block_form_256x4(dtype, N):
+    """Contiguous rows of exactly 1024 vectors run the 256 x 4 exact-width block form, capped at
+    3 workgroups per CU; a strided layout or several batches keep the block family and its cap."""
+    code = {"bf16": BF16, "fp16": FP16, "fp32": FP32}[dtype]
+    q = bnd.kernel_query(32768, N, dtype, A, A, A + (1 << 31), resources=False)
+    assert q["kernel"] == f"rmsnorm_block_exact<{ {'bf16': 'BF16', 'fp16': 'FP16', 'fp32': 'F32'}[dtype] },4,256>", q
+    p = host_plan(32768, N, code)
+    assert (p.block_threads, p.vectors_per_lane, p.max_blocks_per_cu) == (256, 4, 3)
+    lay = bnd.Layout(0, N + 64, 0, N, 0)
+    ps = bnd.Plan()
+    assert lib.rmsnorm_plan_query_ex(32768, N, code, A, A, A + (1 << 31), bnd.ctypes.byref(lay), 256,
+                                     bnd.ctypes.byref(ps)) == OK
+    assert (ps.block_threads, ps.vectors_per_lane, ps.max_blocks_per_cu) == (256, 4, 4)

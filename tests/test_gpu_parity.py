@@ -207,18 +207,21 @@ def test_exact_wave_forms(bnd, vectors, dtype):
 
 
 # ---------------------------------------------------------------------------
-# 3c. The exact-width block form (contiguous 16-bit rows of exactly 16384
-#     elements, 256 threads x 8 vectors, one trip): named through
-#     rmsnorm_fwd_kernel_query, over row counts that leave XCD windows ragged,
-#     both offsets, rstd not written, in place, and with XCD groups and caps.
+# 3c. The exact-width block forms (contiguous rows of exactly 2048 vectors,
+#     256 threads x 8, or 1024 vectors, 256 threads x 4; one trip): named
+#     through rmsnorm_fwd_kernel_query, over row counts that leave XCD windows
+#     ragged, both offsets, rstd not written, in place, and with XCD groups
+#     and caps.
 # ---------------------------------------------------------------------------
-@pytest.mark.parametrize("dtype", ["bf16", "fp16"])
-def test_exact_block_form(bnd, dtype):
-    N = 16384
-    g = torch.Generator().manual_seed(16384 + len(dtype))
+@pytest.mark.parametrize("dtype,N", [("bf16", 16384), ("fp16", 16384), ("bf16", 8192), ("fp16", 8192),
+                                     ("fp32", 4096)])
+def test_exact_block_form(bnd, dtype, N):
+    g = torch.Generator().manual_seed(N + len(dtype))
     td = workloads.TORCH_DTYPES[dtype]
+    bits = torch.int32 if dtype == "fp32" else torch.int16
     sigma = 100.0 if dtype == "fp16" else 1.0
-    for M, offset, group, cap in ((1, 0.0, 8, 0), (5, 1.0, 8, 0), (77, 0.0, 8, 0), (389, 1.0, 3, 2), (389, 0.0, 64, 5)):
+    for M, offset, group, cap in ((1, 0.0, 8, 0), (5, 1.0, 8, 0), (77, 0.0, 8, 0), (389, 1.0, 3, 2), (389, 0.0, 64, 5),
+                                  (1031, 0.0, 64, 3)):
         x = (torch.randn(M, N, generator=g) * sigma).to(td)
         w = (1 + 0.1 * torch.randn(N, generator=g)).to(td)
         xg, wg = x.to(DEV), w.to(DEV)
@@ -228,18 +231,22 @@ def test_exact_block_form(bnd, dtype):
             xcd_group=group, max_blocks_per_cu=cap)
         q = bnd.kernel_query(M, N, dtype, xg.data_ptr(), wg.data_ptr(), y.data_ptr(), plan=plan)
         assert q["kernel"].startswith("rmsnorm_block_exact<") and q["scratch_bytes"] == 0, q
-        announce("exact block", M, dtype, offset, plan.as_dict(), q)
+        announce("exact block", M, N, dtype, offset, plan.as_dict(), q)
         bnd.rmsnorm_fwd_out(xg, wg, y, r, 1e-6, offset, plan=plan)
         torch.cuda.synchronize()
-        y_ref, r_ref = parity.oracle_for(x, w, 1e-6, offset, dtype)
-        parity.compare(y, r, y_ref, r_ref, dtype, f"exact block M={M} {dtype}")
+        if dtype == "fp32":
+            ye, re = parity.oracle_fp32(x, w, 1e-6, offset)
+            parity.compare_fp32(y, r, ye, re, f"exact block M={M} N={N} fp32")
+        else:
+            y_ref, r_ref = parity.oracle_for(x, w, 1e-6, offset, dtype)
+            parity.compare(y, r, y_ref, r_ref, dtype, f"exact block M={M} N={N} {dtype}")
         y2, r2 = bnd.rmsnorm_fwd_ex(xg, wg, 1e-6, offset, want_rstd=False, plan=plan)
         torch.cuda.synchronize()
-        assert r2 is None and torch.equal(y2.view(torch.int16), y.view(torch.int16))
+        assert r2 is None and torch.equal(y2.view(bits), y.view(bits))
         xi = xg.clone()
         bnd.rmsnorm_fwd_out(xi, wg, xi, r, 1e-6, offset, plan=plan)       # in place
         torch.cuda.synchronize()
-        assert torch.equal(xi.view(torch.int16), y.view(torch.int16))
+        assert torch.equal(xi.view(bits), y.view(bits))
 
 
 # ---------------------------------------------------------------------------
