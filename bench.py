@@ -522,6 +522,10 @@ def forward_plan(rot: Rotation, args):
     plan = binding.plan_query(wl.M, wl.N, wl.dtype, xp, wp, yp)
     if args.plan:
         plan = plan.copy(**json.loads(args.plan))
+        # the derived fields (trips, rows per trip, resident grid) of the plan as overridden
+        done = binding.plan_validate(wl.M, wl.N, wl.dtype, plan, xp, wp, yp)
+        if done is not None:
+            plan = done
     # the instance this call launches (the plan's, or its exact-width form) and its resources
     res = binding.kernel_query(wl.M, wl.N, wl.dtype, xp, wp, yp, plan=plan)
     return plan, res
