@@ -251,12 +251,16 @@ int rmsnorm_plan_resources(const rmsnorm_plan_t* plan, int dtype,
  * The kernel instance rmsnorm_fwd_with_plan launches for a call over
  * contiguous [M, N] rows with these pointers (alignment only; they may be
  * NULL) and `plan` (NULL = the plan rmsnorm_fwd takes), and its resources.
- * It is the plan's instance, or the exact-width form of a wave plan: the
+ * It is the plan's instance, or an exact-width form: for a wave plan, the
  * wave layout without column masks, strided rows or loop, which serves
  * one-trip, one-batch launches over rows of exactly lanes_per_row *
  * vectors_per_lane vectors without XCD remap or prefetch (widths 128, 256,
- * 512, 1024 for 16-bit dtypes; 64 to 512 for fp32).  rmsnorm_plan_resources
- * reports the plan's general instance.  Any output may be NULL; *kernel_name
+ * 512, 1024 for 16-bit dtypes; 64 to 512 for fp32); for a 256-thread block
+ * plan of 4 or 8 vectors per thread, one row per workgroup without guards,
+ * which serves one-batch launches of exactly M workgroups over rows of
+ * exactly 256 * vectors_per_lane vectors without prefetch (widths 8192 and
+ * 16384 for 16-bit dtypes, 4096 for fp32).  rmsnorm_plan_resources reports
+ * the plan's general instance.  Any output may be NULL; *kernel_name
  * is a static string.  Needs a device when vgprs, lds_bytes or scratch is
  * requested; a NULL plan is planned on the host (as rmsnorm_plan_query with
  * cu_count = 256).  RMSNORM_ERR_SHAPE for M == 0 (nothing is launched).

@@ -289,7 +289,8 @@ int check_grid(const rmsnorm_plan_t* p) {
 // vectors, one trip, and row numbers of the whole grid below 2^31.  The
 // wave form also needs no XCD remap and fewer than kExactMaxRows rows and
 // keeps the plan's segment shape and workgroup size; the block form (256
-// threads x 4 or 8 vectors) keeps the plan's XCD groups and cap.  M is the
+// threads x 4 or 8 vectors) needs a grid of exactly M workgroups and keeps
+// the plan's XCD groups and cap.  M is the
 // rows of one batch, `batches` the batch count.  Host only.
 const KernelEntry* launch_instance(const KernelEntry* k, const rmsnorm_plan_t* p, int64_t M, int64_t N, int dtype,
                                    const Layout& L, int64_t batches) {
@@ -300,7 +301,8 @@ const KernelEntry* launch_instance(const KernelEntry* k, const rmsnorm_plan_t* p
     if (covered < M || covered >= (int64_t{1} << 31)) return k;
     const int64_t epv = elems_per_vector(dtype);
     if (k->variant == RMSNORM_VARIANT_BLOCK) {
-        if (N != static_cast<int64_t>(p->block_threads) * p->vectors_per_lane * epv) return k;
+        // a workgroup per row and no more: the block form has no guard for rows past M
+        if (covered != M || N != static_cast<int64_t>(p->block_threads) * p->vectors_per_lane * epv) return k;
         const KernelEntry* e = rmsnorm_impl::exact_block_kernel(dtype, p->vectors_per_lane, p->block_threads);
         return e ? e : k;
     }
@@ -357,7 +359,8 @@ int finish_plan(rmsnorm_plan_t* p, int64_t M, int64_t N, int dtype, Access acc, 
                     if (!acc.contiguous || N != static_cast<int64_t>(p->block_threads) * p->vectors_per_lane * epv)
                         return fail(RMSNORM_ERR_PLAN, "this block shape runs only over one batch of contiguous rows of "
                                                       "exactly block_threads * vectors_per_lane vectors");
-                    if (p->grid < M) return fail(RMSNORM_ERR_PLAN, "this block shape runs one trip: grid must cover M");
+                    if (p->grid != M)
+                        return fail(RMSNORM_ERR_PLAN, "this block shape runs one trip: grid must equal M");
                     k = e;
                 }
             }
@@ -576,7 +579,7 @@ int choose_plan(int64_t M, int64_t N, int dtype, Access acc, rmsnorm_plan_t* p) 
         // placements of y, against 170.0 with 4 and 175.5 with 2)
         if (p->variant == RMSNORM_VARIANT_BLOCK && acc.contiguous && p->block_threads == 256 &&
             N == static_cast<int64_t>(p->block_threads) * p->vectors_per_lane * elems_per_vector(dtype) &&
-            p->grid >= M && rmsnorm_impl::exact_block_kernel(dtype, p->vectors_per_lane, p->block_threads))
+            p->grid == M && rmsnorm_impl::exact_block_kernel(dtype, p->vectors_per_lane, p->block_threads))
             p->max_blocks_per_cu = 3;
     }
     p->prefetch = 0;

@@ -473,7 +473,7 @@ __global__ __launch_bounds__(1024) void rmsnorm_block(KernelArgs a) {
 
 // ---------------------------------------------------------------------------
 // Exact-width block form: one row of exactly T * VPT vectors per workgroup,
-// contiguous rows in one batch, one trip (grid >= M), the block family's
+// contiguous rows in one batch, one trip (a grid of exactly M), the block family's
 // XCD row placement.  The weights stay packed and are widened at use, so 8
 // vectors per thread fit in 128 VGPRs at four 256-thread workgroups per CU,
 // where the block family's fp32 weights would need 64 more registers.  With
@@ -498,13 +498,13 @@ __global__ __launch_bounds__(T) __attribute__((amdgpu_waves_per_eu(4))) void rms
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wid = tid >> 6;
+    // The grid is exactly M workgroups (launch_instance and finish_plan send
+    // no other), so every workgroup owns a row and no load or store needs a
+    // guard.  Every load is unconditional: a load under a branch made the
+    // compiler wait for the first vector before issuing the other fifteen
+    // loads of the row, and a row-liveness guard cost 0.35 % at 32768 x 8192.
     const int64_t row = grouped_block(a.xcd_group, a.grid);
-    // no early exit past the last row: every thread reaches the barrier.  A
-    // workgroup past it reads row 0 and stores nothing, so every load is
-    // unconditional: a load under a branch made the compiler wait for the
-    // first vector before issuing the other fifteen loads of the row.
-    const bool live = row < a.M;
-    const u32x4* xr = x + (live ? row : 0) * RV + tid;
+    const u32x4* xr = x + row * RV + tid;
     u32x4 d[VPT];
 #pragma unroll
     for (int v = 0; v < VPT; ++v) d[v] = load_x(xr + v * T);
@@ -521,16 +521,14 @@ __global__ __launch_bounds__(T) __attribute__((amdgpu_waves_per_eu(4))) void rms
 #pragma unroll
     for (int i = 1; i < NW; ++i) tot += part[i];
     const float r = rsq(__builtin_fmaf(tot, a.inv_n, a.eps));
-    if (live) {
-        u32x4* yr = y + row * RV + tid;
+    u32x4* yr = y + row * RV + tid;
 #pragma unroll
-        for (int v = 0; v < VPT; ++v) {
-            float we[D::EPV];
-            widen_weights<D>(we, wq[v], a.offset);
-            store_y(yr + v * T, normalise<D>(d[v], we, r));
-        }
-        if (tid == 0 && a.rstd != nullptr) store_rstd(a.rstd + row, r);
+    for (int v = 0; v < VPT; ++v) {
+        float we[D::EPV];
+        widen_weights<D>(we, wq[v], a.offset);
+        store_y(yr + v * T, normalise<D>(d[v], we, r));
     }
+    if (tid == 0 && a.rstd != nullptr) store_rstd(a.rstd + row, r);
 }
 
 // ---------------------------------------------------------------------------

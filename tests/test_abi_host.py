@@ -772,6 +772,7 @@ def test_other_launches_keep_the_general_instance():
     assert name(n=8000).startswith("rmsnorm_block<")
     blk = bnd.plan_query(M, 8192, "bf16", cu_count=256)
     assert name(blk.copy(grid=1024), n=8192).startswith("rmsnorm_block<")
+    assert name(blk.copy(grid=M + 1), n=8192).startswith("rmsnorm_block<")   # a workgroup past the rows
     assert name(blk.copy(prefetch=1, grid=1024), n=8192).startswith("rmsnorm_block<")
     with pytest.raises(bnd.RmsnormError):
         name(m=0)
@@ -799,6 +800,7 @@ def test_exact_block_form_is_planned_only_where_it_fits():
     # a persistent grid or a ragged width cannot take it
     assert bnd.plan_validate(4096, 16384, "bf16", base, cu_count=256) is not None
     assert bnd.plan_validate(4096, 16384, "bf16", base.copy(grid=1024), cu_count=256) is None
+    assert bnd.plan_validate(4096, 16384, "bf16", base.copy(grid=4097), cu_count=256) is None   # exactly M
     assert bnd.plan_validate(4096, 16000, "bf16", base, cu_count=256) is None
     # rows of a strided layout: the rule plans the 1024-thread block family instead
     lay = bnd.Layout(0, 20000, 0, 16384, 0)
