@@ -249,6 +249,38 @@ def test_exact_block_form(bnd, dtype, N):
         assert torch.equal(xi.view(bits), y.view(bits))
 
 
+@pytest.mark.parametrize("dtype,N", [("bf16", 8192), ("fp32", 4096)])
+def test_block_plan_past_the_rows_keeps_the_general_instance(bnd, dtype, N):
+    """The exact-width block forms have no guard for rows past M: a 256 x 4 plan whose grid has
+    workgroups past the last row runs the general block kernel, which masks them.  Its result
+    equals the exact form's bit for bit (the same reduction order) and the oracle's."""
+    M = 389
+    g = torch.Generator().manual_seed(N + 77)
+    td = workloads.TORCH_DTYPES[dtype]
+    bits = torch.int32 if dtype == "fp32" else torch.int16
+    x = torch.randn(M, N, generator=g).to(td)
+    w = (1 + 0.1 * torch.randn(N, generator=g)).to(td)
+    xg, wg = x.to(DEV), w.to(DEV)
+    base = bnd.plan_query(M, N, dtype, xg.data_ptr(), wg.data_ptr(), xg.data_ptr())
+    for grid, group in ((M + 7, 8), (M + 1, 1), (2 * M, 64)):
+        plan = base.copy(grid=grid, xcd_group=group)
+        q = bnd.kernel_query(M, N, dtype, xg.data_ptr(), wg.data_ptr(), xg.data_ptr(), plan=plan)
+        assert q["kernel"].startswith("rmsnorm_block<"), q
+        announce("block past rows", M, N, dtype, grid, group)
+        y = torch.full_like(xg, float("nan"))
+        r = torch.full((M,), float("nan"), dtype=torch.float32, device=DEV)
+        bnd.rmsnorm_fwd_out(xg, wg, y, r, 1e-6, 0.0, plan=plan)
+        y_exact, r_exact = bnd.rmsnorm_fwd(xg, wg, 1e-6, 0.0, plan=base)
+        torch.cuda.synchronize()
+        assert torch.equal(y.view(bits), y_exact.view(bits)) and torch.equal(r, r_exact)
+        if dtype == "fp32":
+            ye, re = parity.oracle_fp32(x, w, 1e-6, 0.0)
+            parity.compare_fp32(y, r, ye, re, f"block past rows grid={grid} fp32")
+        else:
+            y_ref, r_ref = parity.oracle_for(x, w, 1e-6, 0.0, dtype)
+            parity.compare(y, r, y_ref, r_ref, dtype, f"block past rows grid={grid}")
+
+
 # ---------------------------------------------------------------------------
 # 4. Guard bands: NaN around x and w must not leak in; sentinels around y and
 #    rstd must not be written.  Aligned offsets take the 16-byte kernels,
