@@ -39,6 +39,7 @@ import hashlib
 import json
 import math
 import os
+import re
 import sys
 import time
 
@@ -59,15 +60,24 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-# the forward kernels' own sources: a change to any of them voids stored counters
+# the forward kernels' own sources: a change to their code voids stored counters
 FORWARD_SOURCES = ("rmsnorm_kernels.hip", "rmsnorm_device.hpp", "rmsnorm_internal.hpp")
+# comments, string and character literals of C++ source (literals are kept, comments dropped)
+_CXX_TOKENS = re.compile(r'//[^\n]*|/\*.*?\*/|"(?:\\.|[^\\"\n])*"|\'(?:\\.|[^\\\'\n])*\'', re.S)
+
+
+def code_of(source: str) -> str:
+    """The source without comments, whitespace runs collapsed: edits to comments or layout leave
+    it unchanged."""
+    kept = _CXX_TOKENS.sub(lambda m: m.group(0) if m.group(0)[0] in "\"'" else " ", source)
+    return " ".join(kept.split())
 
 
 def kernel_source_sha256() -> str:
     h = hashlib.sha256()
     for name in FORWARD_SOURCES:
-        with open(os.path.join(ROOT, "memory_bound_row_rmsnorm_amd", "csrc", name), "rb") as f:
-            h.update(name.encode() + b"\0" + f.read())
+        with open(os.path.join(ROOT, "memory_bound_row_rmsnorm_amd", "csrc", name)) as f:
+            h.update(name.encode() + b"\0" + code_of(f.read()).encode())
     return h.hexdigest()
 
 

@@ -458,12 +458,13 @@ constexpr int kMinBlocksPerCu = 3;                 // the occupancy cap never go
 //    one batch of x exceeds the 256 MB Infinity Cache (xcd_group 64 at 16 KiB
 //    rows, 128 at 8 KiB, 32 at 32 KiB); and at most about 64 KiB of rows, but
 //    never fewer than 3 workgroups, resident per compute unit
-//    (max_blocks_per_cu 4 at 16 KiB rows, 3 at 24 KiB).  The 128 KiB groups
-//    are 5-6% faster than none on 32768 x 8192 at a favourable placement of
-//    y relative to x, but the rate then follows that placement over a 10%
-//    range (165-181 us); 1 MiB groups hold 169-171 us at every placement
-//    measured, and lift the median over placements by 1-3.5% at 4 KiB to
-//    32 KiB rows.
+//    (max_blocks_per_cu 4 at 16 KiB rows, 3 at 24 KiB; 3 for the exact-width
+//    forms).  With the block family's kernel the 128 KiB groups were 5-6%
+//    faster than none on 32768 x 8192 at a favourable placement of y
+//    relative to x, but the rate then followed that placement over a 10%
+//    range (165-181 us); 1 MiB groups hold 167-169 us (the exact-width form)
+//    at every placement measured, and lift the median over placements by
+//    1-3.5% at 4 KiB to 32 KiB rows.
 //    Below 256 MB the placement does not matter and 128 KiB groups lead
 //    (8192 x 3000: 18.1 us against 18.7 with 384 KiB groups).  A cap of 2 at
 //    24 KiB rows left 512-thread workgroups at 193 us on 21840 x 12288,
@@ -536,7 +537,7 @@ int choose_plan(int64_t M, int64_t N, int dtype, Access acc, rmsnorm_plan_t* p) 
         p->block_threads = nvec <= 256 * 4 ? 256 : (nvec <= 512 * 3 ? 512 : 1024);
         p->vectors_per_lane = static_cast<int>(ceil_div(nvec, p->block_threads));
         // contiguous 16-bit rows of exactly 16384 elements, one trip: the exact-width block
-        // form, 256 threads x 8 vectors (4096 x 16384 fp16: 45.7 us against 47.4 us with
+        // form, 256 threads x 8 vectors (4096 x 16384 fp16: 44.7 us against 47.4 us with
         // 1024 x 2)
         if (acc.contiguous && N == 256 * 8 * elems_per_vector(dtype) && M <= grid_limit(256) &&
             rmsnorm_impl::exact_block_kernel(dtype, 8, 256)) {
@@ -575,7 +576,7 @@ int choose_plan(int64_t M, int64_t N, int dtype, Access acc, rmsnorm_plan_t* p) 
         if (cap < kMaxThreadsPerCu / p->block_threads) p->max_blocks_per_cu = static_cast<int>(cap);
         // the exact-width block forms (launch_instance): at most 3 workgroups per CU
         // (4096 x 16384 fp16, 256 x 8: 45.9 us against 46.2 with 4, 46.7 with 5, 47.0
-        // uncapped, 47.8 with 2; 32768 x 8192 bf16, 256 x 4: 167.2-168.1 us over eight
+        // uncapped, 47.8 with 2; 32768 x 8192 bf16, 256 x 4: 166.6-168.7 us over eight
         // placements of y, against 170.0 with 4 and 175.5 with 2)
         if (p->variant == RMSNORM_VARIANT_BLOCK && acc.contiguous && p->block_threads == 256 &&
             N == static_cast<int64_t>(p->block_threads) * p->vectors_per_lane * elems_per_vector(dtype) &&

@@ -480,12 +480,11 @@ __global__ __launch_bounds__(1024) void rmsnorm_block(KernelArgs a) {
 // no row loop, no column mask and no branch around a load, all of a thread's
 // loads issue back to back and the arithmetic starts as each vector lands.
 // Measured on MI355X with inputs cold in HBM, at most 3 workgroups per CU:
-// 4096 x 16384 fp16 (256 x 8) 45.1 us, against 47.4 us for 1024 x 2 block
-// plans and 47.0 us for 512 x 4; 32768 x 8192 bf16 (256 x 4) 167.2-168.1 us
-// (medians over eight placements of y, two boxes) against 169.1-169.9 us for
-// the block family's 256 x 4 at its best cap of 4 (the exact form at 4 per
-// CU: 170.0 us).  Launches switch to it wherever the call fits
-// (launch_instance).
+// 4096 x 16384 fp16 (256 x 8) 44.7 us, against 47.4 us for 1024 x 2 block
+// plans and 47.0 us for 512 x 4; 32768 x 8192 bf16 (256 x 4) 167.2-167.9 us
+// on three boxes, where the block family's 256 x 4 at its best cap of 4 took
+// 169.1-169.9 us (the exact form at 4 per CU: 170.0 us).  Launches switch to
+// it wherever the call fits (launch_instance).
 // ---------------------------------------------------------------------------
 template <class D, int VPT, int T>
 __global__ __launch_bounds__(T) __attribute__((amdgpu_waves_per_eu(4))) void rmsnorm_block_exact(KernelArgs a) {

@@ -131,3 +131,13 @@ def test_trace_fit_recovers_intercept_and_rate(tmp_path):
     assert r["fit"]["rate_tb_per_s"] == pytest.approx(7.0, rel=1e-3)
     assert [q["M"] for q in r["points"]] == rows
     assert all(q["median_us"] == q["mean_us"] for q in r["points"])
+
+
+def test_counter_hash_ignores_comments_and_layout():
+    """Stored counters stay valid across edits to comments or layout of the kernel sources, and
+    are voided by any change to the code itself (a string literal keeps its comment markers)."""
+    base = 'int f(int a) { return a + 1; }  // add one\nconst char* s = "x//y";\n'
+    assert bench.code_of(base) == bench.code_of('/* adds */ int f(int a)\n{\n    return a + 1;\n}\nconst char* s = "x//y";')
+    assert bench.code_of(base) != bench.code_of(base.replace("a + 1", "a + 2"))
+    assert bench.code_of(base) != bench.code_of(base.replace('"x//y"', '"x/y"'))
+    assert "add one" not in bench.code_of(base) and '"x//y"' in bench.code_of(base)
