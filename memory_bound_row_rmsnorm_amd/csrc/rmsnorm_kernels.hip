@@ -9,7 +9,7 @@
 // vector holds D::EPV = 8 or 4 elements).  Rows may be strided, in one or
 // more batches (the grid's y dimension); a width that is not a multiple of
 // EPV ends in a tail vector moved element by element; rstd may be NULL.
-// Four families:
+// The families:
 //
 //  * rmsnorm_wave   -- a row lives in a segment of 16, 32 or 64 lanes of one
 //    wavefront, each lane holding VPL 16-byte vectors of it; a wave carries
@@ -20,16 +20,20 @@
 //  * rmsnorm_block  -- one row per workgroup per trip, each thread holding VPT
 //    16-byte vectors; wave sums meet in LDS behind one barrier per trip
 //    (double-buffered partials).  For large N.
-//  * rmsnorm_shifted -- rows that do not start 16-byte aligned (contiguous
-//    rows with N % EPV != 0): aligned 16-byte chunks, per-row shifted weights,
-//    element-wise edges.
+//  * rmsnorm_wave_exact, rmsnorm_block_exact -- one-trip forms of the two
+//    above for contiguous rows of exactly their width, with the geometry fixed
+//    at compile time; launches switch to them wherever a call fits.
+//  * rmsnorm_wide   -- aligned rows wider than the block family holds, in tiles.
+//  * rmsnorm_shifted, rmsnorm_shifted_wave -- rows that do not start 16-byte
+//    aligned (contiguous rows with N % EPV != 0): aligned 16-byte chunks,
+//    per-row shifted weights, element-wise edges.
 //  * rmsnorm_generic -- any N and any alignment, element accesses, the row
 //    read a second time (from cache) to normalise.  Correctness fallback.
 //
-// Each family loops over rows with a grid stride, so a grid smaller than the
-// row count is a persistent grid that keeps offset + w in registers across
-// trips (the static persistent schedule of the cuTile listing, re-expressed
-// for wave64 and the 256-CU chip).  Columns at or past N are never loaded or
+// Except for the exact forms, each family loops over rows with a grid stride,
+// so a grid smaller than the row count is a persistent grid that keeps
+// offset + w in registers across trips (the static persistent schedule of the
+// cuTile listing, re-expressed for wave64 and the 256-CU chip).  Columns at or past N are never loaded or
 // stored: loads there yield zero and contribute nothing to the sum of
 // squares, the padding rule of the same listing.
 #include "rmsnorm_device.hpp"
