@@ -350,7 +350,14 @@ def inputs_label(sets: int, x_bytes: int) -> str:
             "cache-resident (Infinity Cache), not an HBM figure")
 
 
-REGIONS = 5       # timed regions per measurement (median)
+REGIONS = 5       # timed regions per measurement (median), at least
+REGION_LAUNCHES = 500   # short runs take more regions, until they time about this many launches in all
+
+
+def regions_for(steps: int) -> int:
+    """Timed regions for `steps` launches each: 5, or more for short runs (25 at 20 steps), so the
+    median is not left to a handful of noisy differences."""
+    return max(REGIONS, min(41, -(-REGION_LAUNCHES // max(steps, 1))))
 
 
 def time_launches(launch, sets: int, steps: int, warmup: int, mode: str):
@@ -364,8 +371,8 @@ def time_launches(launch, sets: int, steps: int, warmup: int, mode: str):
     difference is the time of the `steps` launches running back to back behind the walk, as in a
     long stream of launches.  A graph launch and its event pair cost about 5-10 us once (the same
     in both replays, so it cancels; left in, it would add 0.3 us per step at 20 steps).  The
-    result is the median over REGIONS such pairs.  Eager mode: the walk, the start event, `steps`
-    launches, the end event."""
+    result is the median over `regions_for(steps)` such pairs.  Eager mode: the walk, the start
+    event, `steps` launches, the end event."""
     import statistics
 
     import torch
@@ -406,7 +413,7 @@ def time_launches(launch, sets: int, steps: int, warmup: int, mode: str):
         walk.replay()
         torch.cuda.synchronize()
         t0 = time.perf_counter()
-        diffs = [timed(walk_steps.replay) - timed(walk.replay) for _ in range(REGIONS)]
+        diffs = [timed(walk_steps.replay) - timed(walk.replay) for _ in range(regions_for(steps))]
         wall = time.perf_counter() - t0
         time_launches.regions = [round(d / steps, 6) for d in diffs]
         return statistics.median(diffs) / steps, wall

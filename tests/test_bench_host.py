@@ -141,3 +141,11 @@ def test_counter_hash_ignores_comments_and_layout():
     assert bench.code_of(base) != bench.code_of(base.replace("a + 1", "a + 2"))
     assert bench.code_of(base) != bench.code_of(base.replace('"x//y"', '"x/y"'))
     assert "add one" not in bench.code_of(base) and '"x//y"' in bench.code_of(base)
+
+
+def test_short_runs_take_more_timed_regions():
+    """Each timed region is exactly `steps` launches; short runs take more regions so the median
+    rests on enough of them (about 500 launches in all, at least 5 regions, at most 41)."""
+    assert bench.regions_for(2000) == 5 and bench.regions_for(100) == 5
+    assert bench.regions_for(20) == 25 and bench.regions_for(50) == 10
+    assert bench.regions_for(1) == 41
