@@ -681,7 +681,7 @@ constexpr int64_t kBwdPartialsGeneric = 1024;        // row-pass grid cap of the
 constexpr int kBwdWaveSlots[] = {4, 2, 1};
 // Unaligned rows shorter than this take the generic kernel.
 constexpr int64_t kBwdMinShiftedN = 16;
-constexpr int64_t kBwdMaxShiftedWaveChunks = 64;   // one chunk per lane of a 64-lane segment
+constexpr int64_t kBwdMaxShiftedWaveChunks = 128;  // two chunks per lane of a 64-lane segment
 
 const KernelEntry* find_bwd_kernel(int variant, int dtype, int lanes, int vpl, int slots, bool prefetch) {
     int n = 0;
@@ -957,15 +957,17 @@ int choose_bwd_plan(int64_t M, int64_t N, bool vec_ok, bool shifted_ok, int dtyp
     const int64_t shifted_chunks = ceil_div(N + epv - 1, epv);
     if (!vec_ok && shifted_ok && N >= kBwdMinShiftedN && shifted_chunks <= kBwdMaxShiftedWaveChunks) {
         // a row per segment of the fewest lanes (16, 32, 64) that hold its
-        // chunks, one chunk per lane; several rows per wave: slots as in the
-        // wave family; a row per wave: two slots (262144 x 257 bf16: 119 us,
-        // against 132 us with one slot and the next trip loaded ahead;
-        // 65536 x 300 bf16: 35.6 against 39.1 us).  No prefetching form is
-        // taken: with the rows of a trip loaded together it gained nothing.
+        // chunks, one chunk per lane up to 64 chunks, then two per lane of a
+        // 64-lane wave; several rows per wave: slots as in the wave family; a
+        // row per wave: two slots (262144 x 257 bf16: 119 us, against 132 us
+        // with one slot and the next trip loaded ahead; 65536 x 300 bf16: 35.6
+        // against 39.1 us; 16384 x 1001 bf16: 26.4 us, against 37.8 us with a
+        // 128-thread workgroup per row).  No prefetching form is taken: with
+        // the rows of a trip loaded together it gained nothing.
         p->variant = RMSNORM_VARIANT_SHIFTED_WAVE;
         p->block_threads = kBwdWaveThreads;
         p->lanes_per_row = shifted_chunks <= 16 ? 16 : (shifted_chunks <= 32 ? 32 : 64);
-        p->vectors_per_lane = 1;
+        p->vectors_per_lane = shifted_chunks <= 64 ? 1 : 2;
         const int64_t per_slot = N * elem_size(dtype) * (64 / p->lanes_per_row);
         p->row_slots = p->lanes_per_row == 64 ? 2 : 1;
         for (int sl : kBwdWaveSlots) {
@@ -976,13 +978,12 @@ int choose_bwd_plan(int64_t M, int64_t N, bool vec_ok, bool shifted_ok, int dtyp
             }
         }
     } else if (!vec_ok && shifted_ok && N >= kBwdMinShiftedN) {
-        // one row per workgroup: one chunk per thread up to 128 chunks, then
-        // the fewest threads (up to 1024) that hold the row with at most 2
-        // per thread (16384 x 1001 bf16: 37.8 us with 128 x 1 against 44.6 us
-        // with 64 x 2; 8192 x 3001 bf16: 47.5 us with 256 x 2, 46.6 with
-        // 512 x 1; 16384 x 1002 fp32: 44.0 us with 128 x 2, 45.6 with 256 x 1)
+        // one row per workgroup of the fewest threads (up to 1024) that hold
+        // the row with at most 2 chunks per thread (8192 x 3001 bf16: 47.5 us
+        // with 256 x 2, 46.6 with 512 x 1; 16384 x 1002 fp32: 44.0 us with
+        // 128 x 2, 45.6 with 256 x 1)
         const int64_t nchunks = ceil_div(N + epv - 1, epv);
-        const int64_t per_thread = nchunks <= 128 ? 1 : 2;
+        const int64_t per_thread = 2;
         p->variant = RMSNORM_VARIANT_SHIFTED;
         p->row_slots = 1;
         p->block_threads = 64;

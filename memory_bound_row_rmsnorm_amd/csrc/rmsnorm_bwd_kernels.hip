@@ -607,14 +607,15 @@ __global__ __launch_bounds__(1024) void rmsnorm_bwd_shifted(BwdArgs a) {
 
 // ---------------------------------------------------------------------------
 // Row pass, shifted wave family: short rows off a 16-byte boundary (at most
-// LANES chunks) with a row per segment of LANES lanes (16, 32 or 64) and
-// SLOTS slots of 64 / LANES rows per wave per trip; lane li of a segment holds
-// chunk li of its row and keeps column vector li of dw.  As in the shifted
-// kernel the weights are funnel-shifted into each row's chunk frame and the
-// products of chunk li + 1 come from the lane above; a segment's last lane
-// has none (with one chunk per lane, its column vector's upper elements lie
-// past the row).  With 64 lanes a row's shift is uniform in its wave and both
-// shifts branch on it; with several rows per wave every lane shifts by its own
+// VPL * LANES chunks) with a row per segment of LANES lanes (16, 32 or 64; two
+// chunks per lane only with 64) and SLOTS slots of 64 / LANES rows per wave
+// per trip; lane li of a segment holds chunks v * LANES + li of its row and
+// keeps column vectors v * LANES + li of dw.  As in the shifted kernel the
+// weights are funnel-shifted into each row's chunk frame and the products of
+// chunk c + 1 come from the lane above; a segment's last lane takes them from
+// its first lane's next chunk, or has none past the last chunk (its column
+// vector's upper elements then lie past the row).  With 64 lanes a row's
+// shift is uniform in its wave and both shifts branch on it; with several rows per wave every lane shifts by its own
 // row's distance past a boundary (funnel_lane for the weights, a three-stage
 // select for the products).  No barrier until the end, where the partials of
 // the segments and waves are added in LDS in a fixed order, as in the wave
@@ -652,8 +653,9 @@ __device__ __forceinline__ void add_columns_lane(float (&acc)[4], const float (&
     for (int i = 0; i < 4; ++i) acc[i] = __builtin_fmaf(W[i], r, acc[i]);
 }
 
-template <class D, int LANES, int SLOTS, bool PREFETCH>
+template <class D, int LANES, int VPL, int SLOTS, bool PREFETCH>
 __global__ __launch_bounds__(1024) void rmsnorm_bwd_shifted_wave(BwdArgs a) {
+    static_assert(VPL == 1 || LANES == 64, "two chunks per lane only with a row per wave");
     typedef typename D::elem_t E;
     constexpr int EPV = D::EPV;
     constexpr int SEG = 64 / LANES;
@@ -674,14 +676,21 @@ __global__ __launch_bounds__(1024) void rmsnorm_bwd_shifted_wave(BwdArgs a) {
     const int wid = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
     const int64_t nwaves = a.grid * wpb;
 
+    // lane li of a segment holds chunks v * LANES + li, v < VPL, and keeps
+    // column vector v * LANES + li of dw
     auto wvec = [&](int k) -> u32x4 {
         if (k < 0 || k >= nvec_w) return kZero;
         return k == nvec_w - 1 ? keep_row<D>(w[k], k * EPV, n) : w[k];
     };
-    const u32x4 wlo = wvec(li - 1), whi = wvec(li);
-    float dwp[EPV];
+    u32x4 wlo[VPL], whi[VPL];
+    float dwp[VPL][EPV];
 #pragma unroll
-    for (int k = 0; k < EPV; ++k) dwp[k] = 0.0f;
+    for (int v = 0; v < VPL; ++v) {
+        wlo[v] = wvec(v * LANES + li - 1);
+        whi[v] = wvec(v * LANES + li);
+#pragma unroll
+        for (int k = 0; k < EPV; ++k) dwp[v][k] = 0.0f;
+    }
 
     // distance of row m's start past a 16-byte boundary, in elements
     auto shift_of = [&](const E* p) -> int {
@@ -689,7 +698,7 @@ __global__ __launch_bounds__(1024) void rmsnorm_bwd_shifted_wave(BwdArgs a) {
         if constexpr (LANES == 64) return __builtin_amdgcn_readfirstlane(s);
         else return s;
     };
-    auto load_trip = [&](u32x4 (&xd)[SLOTS], u32x4 (&dd)[SLOTS], float (&r)[SLOTS], int (&al)[SLOTS],
+    auto load_trip = [&](u32x4 (&xd)[SLOTS][VPL], u32x4 (&dd)[SLOTS][VPL], float (&r)[SLOTS], int (&al)[SLOTS],
                          int64_t gg) {
 #pragma unroll
         for (int s = 0; s < SLOTS; ++s) {
@@ -700,21 +709,25 @@ __global__ __launch_bounds__(1024) void rmsnorm_bwd_shifted_wave(BwdArgs a) {
             const int nch = (as + n + EPV - 1) / EPV;
             const u32x4* xc = reinterpret_cast<const u32x4*>(x + o.x - as);
             const u32x4* dc = reinterpret_cast<const u32x4*>(dy + o.dy - as);
-            xd[s] = (live && li < nch) ? stream_load(xc + li) : kZero;
-            dd[s] = (live && li < nch) ? stream_load(dc + li) : kZero;
+#pragma unroll
+            for (int v = 0; v < VPL; ++v) {
+                const int c = v * LANES + li;
+                xd[s][v] = (live && c < nch) ? stream_load(xc + c) : kZero;
+                dd[s][v] = (live && c < nch) ? stream_load(dc + c) : kZero;
+            }
             r[s] = live ? rstd[row] : 0.0f;
             al[s] = as;
         }
     };
 
     int64_t gi = static_cast<int64_t>(blockIdx.x) * wpb + wid;
-    u32x4 xd[SLOTS], dd[SLOTS];
+    u32x4 xd[SLOTS][VPL], dd[SLOTS][VPL];
     float r[SLOTS];
     int al[SLOTS];
     if (PREFETCH && gi * ROWS < M) load_trip(xd, dd, r, al, gi);
     while (gi * ROWS < M) {
         const int64_t gn = gi + nwaves;
-        u32x4 xn[SLOTS], dn[SLOTS];
+        u32x4 xn[SLOTS][VPL], dn[SLOTS][VPL];
         float rn[SLOTS];
         int aln[SLOTS];
         if constexpr (PREFETCH) {
@@ -727,59 +740,92 @@ __global__ __launch_bounds__(1024) void rmsnorm_bwd_shifted_wave(BwdArgs a) {
             const int64_t row = gi * ROWS + seg + s * SEG;
             const bool live = row < M;
             const int as = al[s];
-            const int j0 = li * EPV - as;
-            u32x4 xv4 = xd[s], dv4 = dd[s];
-            if (j0 < 0 || j0 + EPV > n) {
-                xv4 = keep_row<D>(xv4, j0, n);
-                dv4 = keep_row<D>(dv4, j0, n);
+            u32x4 xv4[VPL], dv4[VPL];
+            float g[VPL][EPV];
+            float t = 0.0f;
+#pragma unroll
+            for (int v = 0; v < VPL; ++v) {
+                const int j0 = (v * LANES + li) * EPV - as;
+                xv4[v] = xd[s][v];
+                dv4[v] = dd[s][v];
+                if (j0 < 0 || j0 + EPV > n) {
+                    xv4[v] = keep_row<D>(xv4[v], j0, n);
+                    dv4[v] = keep_row<D>(dv4[v], j0, n);
+                }
+                if constexpr (LANES == 64) widen_g<D>(g[v], funnel<D>(wlo[v], whi[v], EPV - as), a.offset);
+                else widen_g<D>(g[v], funnel_lane<D>(wlo[v], whi[v], EPV - as), a.offset);
+                t = dot_dgx<D>(dv4[v], xv4[v], g[v], t);
             }
-            float g[EPV], d[EPV], xv[EPV], o[EPV], p[EPV], pn[EPV];
-            if constexpr (LANES == 64) widen_g<D>(g, funnel<D>(wlo, whi, EPV - as), a.offset);
-            else widen_g<D>(g, funnel_lane<D>(wlo, whi, EPV - as), a.offset);
-            const float cm = segment_allreduce<LANES>(dot_dgx<D>(dv4, xv4, g, 0.0f)) * a.inv_n;
+            const float cm = segment_allreduce<LANES>(t) * a.inv_n;
             const float rs = r[s];
             const float r2c = rs * rs * cm;
-            D::widen(dv4, d);
-            D::widen(xv4, xv);
-#pragma unroll
-            for (int k = 0; k < EPV; ++k) {
-                o[k] = rs * (g[k] * d[k] - r2c * xv[k]);
-                p[k] = d[k] * xv[k];
-            }
             const int nch = (as + n + EPV - 1) / EPV;
-            if (live && li < nch) {
-                u32x4* oc = reinterpret_cast<u32x4*>(dx + row_offsets(a, row).dx - as);
-                const u32x4 ov = D::narrow(o);
-                if (j0 < 0 || j0 + EPV > n) store_edge<D>(oc + li, ov, j0, n);
-                else stream_store(oc + li, ov);
-            }
+            float p[VPL][EPV];
 #pragma unroll
-            for (int k = 0; k < EPV; ++k) {
-                const float up = from_lane_above(p[k], 0.0f);
-                pn[k] = li == LANES - 1 ? 0.0f : up;
+            for (int v = 0; v < VPL; ++v) {
+                float d[EPV], xv[EPV], o[EPV];
+                D::widen(dv4[v], d);
+                D::widen(xv4[v], xv);
+#pragma unroll
+                for (int k = 0; k < EPV; ++k) {
+                    o[k] = rs * (g[v][k] * d[k] - r2c * xv[k]);
+                    p[v][k] = d[k] * xv[k];
+                }
+                const int c = v * LANES + li;
+                if (live && c < nch) {
+                    u32x4* oc = reinterpret_cast<u32x4*>(dx + row_offsets(a, row).dx - as);
+                    const u32x4 ov = D::narrow(o);
+                    const int j0 = c * EPV - as;
+                    if (j0 < 0 || j0 + EPV > n) store_edge<D>(oc + c, ov, j0, n);
+                    else stream_store(oc + c, ov);
+                }
             }
-            if constexpr (LANES == 64) add_columns<EPV>(dwp, p, pn, as, rs);
-            else add_columns_lane(dwp, p, pn, as, rs);
+            // chunk c + 1's products: the lane above's, or for a segment's last
+            // lane the first lane's next chunk (none past the last chunk)
+#pragma unroll
+            for (int v = 0; v < VPL; ++v) {
+                float pn[EPV];
+#pragma unroll
+                for (int k = 0; k < EPV; ++k) {
+                    float wrap = 0.0f;
+                    if constexpr (VPL > 1) {
+                        if (v + 1 < VPL)
+                            wrap = __builtin_bit_cast(float, __builtin_amdgcn_readlane(
+                                __builtin_bit_cast(int, p[v + 1 < VPL ? v + 1 : 0][k]), 0));
+                    }
+                    const float up = from_lane_above(p[v][k], wrap);
+                    pn[k] = (LANES < 64 && li == LANES - 1) ? 0.0f : up;
+                }
+                if constexpr (LANES == 64) add_columns<EPV>(dwp[v], p[v], pn, as, rs);
+                else add_columns_lane(dwp[v], p[v], pn, as, rs);
+            }
         }
         gi = gn;
         if constexpr (PREFETCH) {
 #pragma unroll
             for (int s = 0; s < SLOTS; ++s) {
-                xd[s] = xn[s];
-                dd[s] = dn[s];
+#pragma unroll
+                for (int v = 0; v < VPL; ++v) {
+                    xd[s][v] = xn[s][v];
+                    dd[s][v] = dn[s][v];
+                }
                 r[s] = rn[s];
                 al[s] = aln[s];
             }
         }
     }
 
-    // every segment of every wave holds column vectors 0 .. LANES - 1: add
-    // them in a fixed order through LDS, then one partial row per workgroup
+    // every segment of every wave holds column vectors 0 .. VPL * LANES - 1:
+    // add them in a fixed order through LDS, then one partial row per workgroup
     float* mine = lds_part + static_cast<int64_t>(wid * SEG + seg) * n;
-    if (li < nvec_w) {
 #pragma unroll
-        for (int k = 0; k < EPV; ++k)
-            if (li * EPV + k < n) mine[li * EPV + k] = dwp[k];
+    for (int v = 0; v < VPL; ++v) {
+        const int c = v * LANES + li;
+        if (c < nvec_w) {
+#pragma unroll
+            for (int k = 0; k < EPV; ++k)
+                if (c * EPV + k < n) mine[c * EPV + k] = dwp[v][k];
+        }
     }
     __syncthreads();
     const int parts = wpb * SEG;
@@ -932,18 +978,20 @@ __global__ __launch_bounds__(COLS * SPLIT) void rmsnorm_dw_reduce(const float* _
     {RMSNORM_VARIANT_SHIFTED, DT, 0, V, 1, P, false,                                                  \
      reinterpret_cast<const void*>(&rmsnorm_bwd_shifted<D, V, P>),                             \
      "rmsnorm_bwd_shifted<" #D "," #V "," #P ">"}
-#define RMS_BWD_SHIFTED_WAVE(D, DT, L, S, P)                                                   \
-    {RMSNORM_VARIANT_SHIFTED_WAVE, DT, L, 1, S, P, false,                                             \
-     reinterpret_cast<const void*>(&rmsnorm_bwd_shifted_wave<D, L, S, P>),                     \
-     "rmsnorm_bwd_shifted_wave<" #D "," #L "," #S "," #P ">"}
+#define RMS_BWD_SHIFTED_WAVE_V(D, DT, L, V, S, P)                                              \
+    {RMSNORM_VARIANT_SHIFTED_WAVE, DT, L, V, S, P, false,                                             \
+     reinterpret_cast<const void*>(&rmsnorm_bwd_shifted_wave<D, L, V, S, P>),                  \
+     "rmsnorm_bwd_shifted_wave<" #D "," #L "," #V "," #S "," #P ">"}
+#define RMS_BWD_SHIFTED_WAVE(D, DT, L, S, P) RMS_BWD_SHIFTED_WAVE_V(D, DT, L, 1, S, P)
 #define RMS_BWD_SHIFTED_WAVE2(D, DT, L, S)                                                     \
     RMS_BWD_SHIFTED_WAVE(D, DT, L, S, false), RMS_BWD_SHIFTED_WAVE(D, DT, L, S, true)
 // Only instances that fit 128 VGPRs without scratch: the block family holds
 // at most two vectors of x and dy per thread (rows up to 1024 x 2 vectors:
-// 16384 16-bit or 8192 fp32 elements), and the widest wave shapes and the
-// 4-slot shifted wave shapes with several rows per wave have no prefetching
-// form.  The wide family holds dw for up to 4 vectors per thread (rows up to
-// 32768 16-bit elements), 6 with fp32 (24576 elements).
+// 16384 16-bit or 8192 fp32 elements), and the widest wave shapes, the
+// 4-slot shifted wave shapes and the two-slot shifted wave shape of two
+// chunks per lane have no prefetching form.  The wide family holds dw for up
+// to 4 vectors per thread (rows up to 32768 16-bit elements), 6 with fp32
+// (24576 elements).
 #define RMS_BWD_FAMILY(D, DT)                                                                  \
     RMS_BWD_WAVE2(D, DT, 16, 1, 1), RMS_BWD_WAVE2(D, DT, 16, 1, 2),                            \
     RMS_BWD_WAVE2(D, DT, 32, 1, 1), RMS_BWD_WAVE2(D, DT, 32, 1, 2),                            \
@@ -959,7 +1007,9 @@ __global__ __launch_bounds__(COLS * SPLIT) void rmsnorm_dw_reduce(const float* _
     RMS_BWD_SHIFTED_WAVE(D, DT, 16, 4, false), RMS_BWD_SHIFTED_WAVE2(D, DT, 32, 1),             \
     RMS_BWD_SHIFTED_WAVE2(D, DT, 32, 2), RMS_BWD_SHIFTED_WAVE(D, DT, 32, 4, false),             \
     RMS_BWD_SHIFTED_WAVE2(D, DT, 64, 1), RMS_BWD_SHIFTED_WAVE2(D, DT, 64, 2),                   \
-    RMS_BWD_SHIFTED_WAVE2(D, DT, 64, 4),                                                       \
+    RMS_BWD_SHIFTED_WAVE(D, DT, 64, 4, false),                                                 \
+    RMS_BWD_SHIFTED_WAVE_V(D, DT, 64, 2, 1, false), RMS_BWD_SHIFTED_WAVE_V(D, DT, 64, 2, 1, true), \
+    RMS_BWD_SHIFTED_WAVE_V(D, DT, 64, 2, 2, false),                                            \
     {RMSNORM_VARIANT_GENERIC, DT, 0, 0, 1, false, false,                                              \
      reinterpret_cast<const void*>(&rmsnorm_bwd_generic<D>), "rmsnorm_bwd_generic<" #D ">"}
 

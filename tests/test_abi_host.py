@@ -411,7 +411,8 @@ def test_bwd_plans_and_workspace():
     assert (p.variant, p.block_threads, p.vectors_per_lane, p.prefetch) == (bnd.VARIANT_WIDE, 1024, 3, 0)
     assert (plan(4096, 32768).variant, plan(4096, 32768).vectors_per_lane) == (bnd.VARIANT_WIDE, 4)
     assert plan(10, 32776).variant == bnd.VARIANT_GENERIC      # wider than the 16-byte kernels hold
-    assert plan(10, 511).variant == bnd.VARIANT_SHIFTED
+    assert plan(10, 511).variant == bnd.VARIANT_SHIFTED_WAVE      # 65 chunks: two per lane of a wave
+    assert plan(10, 1018).variant == bnd.VARIANT_SHIFTED           # 129 chunks: one row per workgroup
     assert plan(10, 512, x=A + 2).variant == bnd.VARIANT_GENERIC
     assert plan(3, 512).grid == 1                               # 3 rows fit one 8-wave workgroup
     assert ws(0, 512) == 0
@@ -658,7 +659,8 @@ def test_bwd_shifted_plans():
     p = bwd_plan_ex(32768, 8191, None)
     assert (p.variant, p.block_threads, p.vectors_per_lane, p.grid, p.prefetch) == \
         (bnd.VARIANT_SHIFTED, 1024, 2, 256, 1)
-    # rows of at most 64 chunks: a row per 16/32/64-lane segment, one chunk per lane
+    # rows of at most 128 chunks: a row per 16/32/64-lane segment, one chunk per lane (two per lane
+    # of a 64-lane wave above 64 chunks)
     p = bwd_plan_ex(100, 17, None)                 # 3 chunks
     assert (p.variant, p.lanes_per_row, p.vectors_per_lane, p.row_slots, p.block_threads) == \
         (bnd.VARIANT_SHIFTED_WAVE, 16, 1, 4, 1024)
@@ -668,15 +670,15 @@ def test_bwd_shifted_plans():
     assert (p.variant, p.lanes_per_row, p.row_slots) == (bnd.VARIANT_SHIFTED_WAVE, 32, 4)
     p = bwd_plan_ex(262144, 257, None)             # 33 chunks: a row per wave, two slots
     assert (p.variant, p.lanes_per_row, p.row_slots, p.grid, p.prefetch) == (bnd.VARIANT_SHIFTED_WAVE, 64, 2, 256, 0)
-    assert bwd_plan_ex(16384, 505, None).variant == bnd.VARIANT_SHIFTED_WAVE   # 64 chunks
-    p = bwd_plan_ex(16384, 506, None)              # 65 chunks: one row per workgroup
-    assert (p.variant, p.block_threads, p.vectors_per_lane) == (bnd.VARIANT_SHIFTED, 128, 1)
-    p = bwd_plan_ex(16384, 1001, None)             # 126 chunks: one per thread
-    assert (p.variant, p.block_threads, p.vectors_per_lane) == (bnd.VARIANT_SHIFTED, 128, 1)
-    p = bwd_plan_ex(16384, 1017, None)             # 128 chunks (1017 + 7 elements)
-    assert (p.block_threads, p.vectors_per_lane) == (128, 1)
-    p = bwd_plan_ex(16384, 1018, None)             # 129 chunks: two per thread
-    assert (p.block_threads, p.vectors_per_lane) == (128, 2)
+    p = bwd_plan_ex(16384, 505, None)              # 64 chunks: one per lane
+    assert (p.variant, p.lanes_per_row, p.vectors_per_lane) == (bnd.VARIANT_SHIFTED_WAVE, 64, 1)
+    # 65 to 128 chunks: a row per wave, two chunks per lane, two slots
+    for n in (506, 513, 1001, 1017):               # 65, 65, 126 and 128 chunks
+        p = bwd_plan_ex(16384, n, None)
+        assert (p.variant, p.lanes_per_row, p.vectors_per_lane, p.row_slots, p.prefetch) == \
+            (bnd.VARIANT_SHIFTED_WAVE, 64, 2, 2, 0), n
+    p = bwd_plan_ex(16384, 1018, None)             # 129 chunks: one row per workgroup, two per thread
+    assert (p.variant, p.block_threads, p.vectors_per_lane) == (bnd.VARIANT_SHIFTED, 128, 2)
     assert bwd_plan_ex(16, 16377, None).variant == bnd.VARIANT_SHIFTED      # 2048 chunks
     assert bwd_plan_ex(16, 16378, None).variant == bnd.VARIANT_GENERIC      # 2049
     assert bwd_plan_ex(100, 15, None).variant == bnd.VARIANT_GENERIC        # shorter than 16 elements
@@ -686,8 +688,11 @@ def test_bwd_shifted_plans():
     assert bwd_plan_ex(100, 3001, None, dy=A + 4).variant == bnd.VARIANT_GENERIC
     assert bwd_plan_ex(100, 3001, None, w=A + 2).variant == bnd.VARIANT_GENERIC
     assert bwd_plan_ex(100, 3001, None, x=A + 1, dy=A + 1, dx=A + 1).variant == bnd.VARIANT_GENERIC
-    # aligned rows on equally offset bases are shifted too (every row one element in)
-    assert bwd_plan_ex(100, 512, None, x=A + 2, dy=A + 0x100002, dx=A + 0x200002).variant == bnd.VARIANT_SHIFTED
+    # aligned rows on equally offset bases are shifted too (every row one element in: 65 chunks)
+    p = bwd_plan_ex(100, 512, None, x=A + 2, dy=A + 0x100002, dx=A + 0x200002)
+    assert (p.variant, p.lanes_per_row, p.vectors_per_lane) == (bnd.VARIANT_SHIFTED_WAVE, 64, 2)
+    assert bwd_plan_ex(100, 2048, None, x=A + 2, dy=A + 0x100002, dx=A + 0x200002).variant == \
+        bnd.VARIANT_SHIFTED
     # strides may differ by whole 16-byte vectors, not by less
     lay = bnd.BwdLayout(0, 3001, 0, 3009, 0, 3017, 0)
     assert bwd_plan_ex(100, 3001, lay).variant == bnd.VARIANT_SHIFTED
@@ -706,7 +711,8 @@ def test_bwd_shifted_plans_that_do_not_fit_are_rejected():
     for p, N in ((good.copy(vectors_per_lane=3), 3001),                   # no such instance
                  (sw.copy(lanes_per_row=32), 300),                         # 32 lanes x 1 chunk < 39
                  (sw.copy(lanes_per_row=128), 300),
-                 (sw.copy(vectors_per_lane=2), 300),                       # one chunk per lane only
+                 (sw.copy(lanes_per_row=32, vectors_per_lane=2), 300),     # two chunks only with 64 lanes
+                 (sw.copy(vectors_per_lane=2, row_slots=2, prefetch=1), 300),  # no such instance
                  (sw.copy(row_slots=4, prefetch=1, lanes_per_row=16), 100),  # no such instance
                  (sw, 512),                                                # aligned rows
                  (good.copy(block_threads=128, lanes_per_row=128), 3001),  # 128 x 2 chunks < 376

@@ -428,7 +428,8 @@ def any_case(M, N, dtype, offset, seed, sigma=2.0):
     (33, 16377, "bf16", 1.0), (500, 17, "bf16", 0.0), (1000, 100, "fp16", 1.0),
     (2000, 257, "bf16", 1.0), (300, 1002, "fp32", 0.0), (50, 8189, "fp32", 1.0), (41, 4097, "fp32", 0.0),
     (3000, 249, "bf16", 0.0), (777, 61, "fp32", 1.0), (600, 505, "fp16", 0.0), (5000, 36, "bf16", 1.0),
-    (4099, 300, "bf16", 1.0)])
+    (4099, 300, "bf16", 1.0), (4099, 513, "bf16", 1.0), (1001, 1017, "fp16", 0.0), (777, 301, "fp32", 1.0),
+    (333, 509, "fp32", 0.0), (2000, 506, "bf16", 0.0)])
 def test_bwd_shifted_rule(bnd, M, N, dtype, offset):
     x, w, dy, r32 = any_case(M, N, dtype, offset, seed=N + M)
     xg, wg, dyg = x.to(DEV), w.to(DEV), dy.to(DEV)
@@ -437,7 +438,7 @@ def test_bwd_shifted_rule(bnd, M, N, dtype, offset):
     announce("bwd shifted", M, N, dtype, offset, p.as_dict())
     epv = EPV[dtype]
     chunks = -(-(N + epv - 1) // epv)
-    assert p.variant == (bnd.VARIANT_SHIFTED_WAVE if chunks <= 64 else bnd.VARIANT_SHIFTED)
+    assert p.variant == (bnd.VARIANT_SHIFTED_WAVE if chunks <= 128 else bnd.VARIANT_SHIFTED)
     dx, dw = bnd.rmsnorm_bwd(xg, wg, dyg, rg, offset)
     dx2, dw2 = bnd.rmsnorm_bwd(xg, wg, dyg, rg, offset)
     torch.cuda.synchronize()
@@ -450,19 +451,20 @@ def test_bwd_shifted_rule(bnd, M, N, dtype, offset):
 def shifted_wave_candidates(bnd, base, N, epv):
     out = []
     for pf in (0, 1):
-        for lanes in (16, 32, 64):
+        for lanes, vpl in ((16, 1), (32, 1), (64, 1), (64, 2)):
             for slots in (1, 2, 4):
                 for threads in (256, 1024):
-                    if lanes * epv >= N + epv - 1:
+                    if lanes * vpl * epv >= N + epv - 1:
                         out.append(base.copy(variant=bnd.VARIANT_SHIFTED_WAVE, lanes_per_row=lanes,
-                                             vectors_per_lane=1, row_slots=slots, block_threads=threads,
+                                             vectors_per_lane=vpl, row_slots=slots, block_threads=threads,
                                              prefetch=pf))
     return out
 
 
 @pytest.mark.parametrize("M,N,dtype", [(97, 3001, "bf16"), (200, 1001, "fp16"), (60, 1003, "fp32"),
                                        (150, 33, "bf16"), (777, 100, "bf16"), (500, 250, "fp16"),
-                                       (300, 61, "fp32"), (333, 505, "bf16")])
+                                       (300, 61, "fp32"), (333, 505, "bf16"), (129, 513, "bf16"),
+                                       (70, 301, "fp32")])
 def test_bwd_shifted_every_kernel(bnd, M, N, dtype):
     x, w, dy, r32 = any_case(M, N, dtype, 1.0, seed=N + 7)
     xg, wg, dyg = x.to(DEV), w.to(DEV), dy.to(DEV)
