@@ -378,11 +378,11 @@ typedef struct rmsnorm_bwd_layout {
  * strides (in place).  The 16-byte kernels (wave, block, wide) run when x, w,
  * dy and dx are 16-byte aligned, N is a multiple of vec_elems, every stride
  * keeps rows aligned and a row has at most 32768 16-bit or 24576 fp32
- * elements; the shifted kernels (RMSNORM_VARIANT_SHIFTED_WAVE up
- * to 128 chunks, RMSNORM_VARIANT_SHIFTED up to 2048) when rows are not
- * 16-byte aligned but x, dy and dx sit equally far past a 16-byte boundary on
- * every row, w is 16-byte aligned and N >= 16; the generic kernel otherwise.  Errors as
- * rmsnorm_bwd, plus RMSNORM_ERR_SHAPE for a bad layout.
+ * elements; the shifted kernels (RMSNORM_VARIANT_SHIFTED_WAVE up to 128
+ * chunks, RMSNORM_VARIANT_SHIFTED up to 2048) when rows are not 16-byte
+ * aligned but x, dy and dx sit equally far past a 16-byte boundary on every
+ * row, w is 16-byte aligned and N >= 16; the generic kernel otherwise.
+ * Errors as rmsnorm_bwd, plus RMSNORM_ERR_SHAPE for a bad layout.
  */
 int rmsnorm_bwd_ex(const void* x, const void* w, const void* dy, const float* rstd, void* dx,
                    float* dw, int64_t M, int64_t N, float offset, int dtype,

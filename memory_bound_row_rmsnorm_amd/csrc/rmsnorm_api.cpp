@@ -677,6 +677,7 @@ constexpr int kBwdWaveThreads = 1024;                // 16 waves share one LDS r
 constexpr int64_t kBwdMaxLds = 64 * 1024;
 constexpr int64_t kBwdPlanCus = 256;                 // compute units the backward plan assumes
 constexpr int64_t kBwdPlanWaves = kBwdPlanCus * 16;  // row-pass waves aimed for: 16 per unit
+constexpr int64_t kBwdShortShiftedWaves = kBwdPlanWaves * 4;  // the same for several shifted rows per wave
 constexpr int64_t kBwdPartialsGeneric = 1024;        // row-pass grid cap of the generic family
 constexpr int kBwdWaveSlots[] = {4, 2, 1};
 // Unaligned rows shorter than this take the generic kernel.
@@ -958,25 +959,20 @@ int choose_bwd_plan(int64_t M, int64_t N, bool vec_ok, bool shifted_ok, int dtyp
     if (!vec_ok && shifted_ok && N >= kBwdMinShiftedN && shifted_chunks <= kBwdMaxShiftedWaveChunks) {
         // a row per segment of the fewest lanes (16, 32, 64) that hold its
         // chunks, one chunk per lane up to 64 chunks, then two per lane of a
-        // 64-lane wave; several rows per wave: slots as in the wave family; a
-        // row per wave: two slots (262144 x 257 bf16: 119 us, against 132 us
-        // with one slot and the next trip loaded ahead; 65536 x 300 bf16: 35.6
-        // against 39.1 us; 16384 x 1001 bf16: 26.4 us, against 37.8 us with a
-        // 128-thread workgroup per row).  No prefetching form is taken: with
-        // the rows of a trip loaded together it gained nothing.
+        // 64-lane wave.  One slot, except a row of one chunk per lane in a
+        // 64-lane wave: two (262144 x 257 bf16: 118 us, against 138 us with
+        // one; 65536 x 300 bf16: 35.3 against 38.9 us).  Several rows per
+        // wave: one slot, against four before (262144 x 36 bf16: 36.6 against
+        // 39.4 us; 262144 x 130 fp16: 67.4 against 76.3 us), with the larger
+        // grid below.  Two chunks per lane: 16384 x 513 bf16 19.0 us, against
+        // 19.8 with two slots and 33.5 with a 128-thread workgroup per row.
+        // No prefetching form is taken: with the rows of a trip loaded
+        // together it gained nothing.
         p->variant = RMSNORM_VARIANT_SHIFTED_WAVE;
         p->block_threads = kBwdWaveThreads;
         p->lanes_per_row = shifted_chunks <= 16 ? 16 : (shifted_chunks <= 32 ? 32 : 64);
         p->vectors_per_lane = shifted_chunks <= 64 ? 1 : 2;
-        const int64_t per_slot = N * elem_size(dtype) * (64 / p->lanes_per_row);
-        p->row_slots = p->lanes_per_row == 64 ? 2 : 1;
-        for (int sl : kBwdWaveSlots) {
-            if (p->lanes_per_row < 64 && sl * per_slot <= kWaveBytesInFlight &&
-                find_bwd_kernel(RMSNORM_VARIANT_SHIFTED_WAVE, dtype, p->lanes_per_row, 1, sl, false)) {
-                p->row_slots = sl;
-                break;
-            }
-        }
+        p->row_slots = (p->lanes_per_row == 64 && p->vectors_per_lane == 1) ? 2 : 1;
     } else if (!vec_ok && shifted_ok && N >= kBwdMinShiftedN) {
         // one row per workgroup of the fewest threads (up to 1024) that hold
         // the row with at most 2 chunks per thread (8192 x 3001 bf16: 47.5 us
@@ -1031,7 +1027,11 @@ int choose_bwd_plan(int64_t M, int64_t N, bool vec_ok, bool shifted_ok, int dtyp
     const int64_t need = M > 0 ? ceil_div(M, rows_per_trip) : 1;
     int64_t cap = kBwdPartialsGeneric;
     if (p->variant != RMSNORM_VARIANT_GENERIC) {
-        cap = kBwdPlanWaves / (p->block_threads / 64);
+        // several short rows per wave off a 16-byte boundary: each row's
+        // shifts are lane arithmetic, which more waves in flight hide, and
+        // the partial rows are short (at most 249 16-bit elements)
+        const bool short_shifted = p->variant == RMSNORM_VARIANT_SHIFTED_WAVE && p->lanes_per_row < 64;
+        cap = (short_shifted ? kBwdShortShiftedWaves : kBwdPlanWaves) / (p->block_threads / 64);
         const int64_t traffic_cap = std::max<int64_t>(3 * M / 32, 1);
         cap = std::min(cap, traffic_cap);
     }

@@ -663,20 +663,21 @@ def test_bwd_shifted_plans():
     # of a 64-lane wave above 64 chunks)
     p = bwd_plan_ex(100, 17, None)                 # 3 chunks
     assert (p.variant, p.lanes_per_row, p.vectors_per_lane, p.row_slots, p.block_threads) == \
-        (bnd.VARIANT_SHIFTED_WAVE, 16, 1, 4, 1024)
-    p = bwd_plan_ex(262144, 100, None)             # 13 chunks, 4 slots of four rows per wave
-    assert (p.lanes_per_row, p.row_slots, p.rows_per_trip, p.grid, p.prefetch) == (16, 4, 256, 256, 0)
-    p = bwd_plan_ex(16384, 249, None)              # 32 chunks
-    assert (p.variant, p.lanes_per_row, p.row_slots) == (bnd.VARIANT_SHIFTED_WAVE, 32, 4)
+        (bnd.VARIANT_SHIFTED_WAVE, 16, 1, 1, 1024)
+    # 13 chunks: one slot of four rows per wave, up to 64 waves per compute unit (1024 workgroups)
+    p = bwd_plan_ex(262144, 100, None)
+    assert (p.lanes_per_row, p.row_slots, p.rows_per_trip, p.grid, p.prefetch) == (16, 1, 64, 1024, 0)
+    p = bwd_plan_ex(16384, 249, None)              # 32 chunks: 512 trips, one per workgroup
+    assert (p.variant, p.lanes_per_row, p.row_slots, p.grid) == (bnd.VARIANT_SHIFTED_WAVE, 32, 1, 512)
     p = bwd_plan_ex(262144, 257, None)             # 33 chunks: a row per wave, two slots
     assert (p.variant, p.lanes_per_row, p.row_slots, p.grid, p.prefetch) == (bnd.VARIANT_SHIFTED_WAVE, 64, 2, 256, 0)
     p = bwd_plan_ex(16384, 505, None)              # 64 chunks: one per lane
     assert (p.variant, p.lanes_per_row, p.vectors_per_lane) == (bnd.VARIANT_SHIFTED_WAVE, 64, 1)
-    # 65 to 128 chunks: a row per wave, two chunks per lane, two slots
+    # 65 to 128 chunks: a row per wave, two chunks per lane, one slot
     for n in (506, 513, 1001, 1017):               # 65, 65, 126 and 128 chunks
         p = bwd_plan_ex(16384, n, None)
-        assert (p.variant, p.lanes_per_row, p.vectors_per_lane, p.row_slots, p.prefetch) == \
-            (bnd.VARIANT_SHIFTED_WAVE, 64, 2, 2, 0), n
+        assert (p.variant, p.lanes_per_row, p.vectors_per_lane, p.row_slots, p.prefetch, p.grid) == \
+            (bnd.VARIANT_SHIFTED_WAVE, 64, 2, 1, 0, 256), n
     p = bwd_plan_ex(16384, 1018, None)             # 129 chunks: one row per workgroup, two per thread
     assert (p.variant, p.block_threads, p.vectors_per_lane) == (bnd.VARIANT_SHIFTED, 128, 2)
     assert bwd_plan_ex(16, 16377, None).variant == bnd.VARIANT_SHIFTED      # 2048 chunks
