@@ -79,7 +79,7 @@ typedef enum rmsnorm_variant {
                                     Edge chunks are read whole (the aligned 16 bytes that hold
                                     row elements) and written element by element */
     RMSNORM_VARIANT_SHIFTED_WAVE = 5, /* the same chunks for short rows: a row per segment of
-                                         lanes_per_row lanes (16, 32, 64), row_slots slots per
+                                         lanes_per_row lanes (8, 16, 32, 64), row_slots slots per
                                          wave per trip, no LDS */
     RMSNORM_VARIANT_WIDE = 6     /* aligned rows wider than the block family holds: one row per
                                     workgroup in tiles of block_threads * vectors_per_lane
@@ -96,9 +96,9 @@ typedef enum rmsnorm_variant {
  *                     _SHIFTED_WAVE / _WIDE
  *   vec_elems         elements per lane access: 16 bytes' worth, 8 (bf16, fp16)
  *                     or 4 (fp32), for every family but GENERIC (1)
- *   lanes_per_row     WAVE: lanes sharing one row (16, 32 or 64); SHIFTED_WAVE:
- *                     64; BLOCK, SHIFTED and GENERIC: threads per row
- *                     (= block_threads)
+ *   lanes_per_row     WAVE: lanes sharing one row (4, 8, 16, 32 or 64);
+ *                     SHIFTED_WAVE: 8, 16, 32 or 64; BLOCK, SHIFTED and
+ *                     GENERIC: threads per row (= block_threads)
  *   vectors_per_lane  16-byte vectors (SHIFTED, SHIFTED_WAVE: aligned chunks)
  *                     each lane holds per row; lanes_per_row * vectors_per_lane
  *                     * vec_elems >= N, and >= N + vec_elems - 1 for the

@@ -399,8 +399,8 @@ int finish_plan(rmsnorm_plan_t* p, int64_t M, int64_t N, int dtype, Access acc, 
         const int epv = elems_per_vector(dtype);
         p->vec_elems = epv;
         if (p->prefetch != 0 && p->prefetch != 1) return fail(RMSNORM_ERR_PLAN, "prefetch must be 0 or 1");
-        if (p->lanes_per_row != 16 && p->lanes_per_row != 32 && p->lanes_per_row != 64)
-            return fail(RMSNORM_ERR_PLAN, "shifted wave plans take 16, 32 or 64 lanes per row");
+        if (p->lanes_per_row != 8 && p->lanes_per_row != 16 && p->lanes_per_row != 32 && p->lanes_per_row != 64)
+            return fail(RMSNORM_ERR_PLAN, "shifted wave plans take 8, 16, 32 or 64 lanes per row");
         k = find_kernel(RMSNORM_VARIANT_SHIFTED_WAVE, dtype, p->lanes_per_row, p->vectors_per_lane, p->row_slots,
                         p->prefetch != 0);
         if (k && static_cast<int64_t>(p->lanes_per_row) * p->vectors_per_lane * epv < N + epv - 1)
@@ -442,10 +442,10 @@ constexpr int kMinBlocksPerCu = 3;                 // the occupancy cap never go
 // Choose family and geometry (host only; no device needed).  A row is
 // nvec = ceil(N / EPV) 16-byte vectors (EPV = 8 for bf16/fp16, 4 for fp32).
 // Rules measured on MI355X with inputs cold in HBM:
-//  * rows of at most 128 vectors: the wave family, 16/32/64 lanes per row
-//    so that a row segment is one 16-byte vector per lane (two at 128), and
-//    enough rows per wave for about 4 KiB of loads per trip (2 KiB in 2-wave
-//    workgroups when a slot holds several rows);
+//  * rows of at most 128 vectors: the wave family, 4/8/16/32/64 lanes per
+//    row so that a row segment is one 16-byte vector per lane (two at 128),
+//    and enough rows per wave for about 4 KiB of loads per trip (2 KiB in
+//    2-wave workgroups when a slot holds several rows of 8 to 32 lanes);
 //  * longer rows: the block family with 256 threads up to 1536 vectors and
 //    1024 beyond, each thread holding ceil(nvec / threads) vectors;
 //  * pointers or row strides that are not 16-byte aligned, or a row wider
@@ -476,17 +476,18 @@ int choose_plan(int64_t M, int64_t N, int dtype, Access acc, rmsnorm_plan_t* p) 
     const int64_t nvec = ceil_div(N, elems_per_vector(dtype));
     const int64_t nchunks = ceil_div(N + elems_per_vector(dtype) - 1, elems_per_vector(dtype));
     if (!vec && acc.shifted && N >= kMinShiftedWaveN && nchunks <= kMaxShiftedWaveChunks) {
-        // a row per segment of the fewest lanes (16, 32, 64) that hold its
-        // chunks, 4-wave workgroups; four slots per wave, two with 16-lane rows
-        // (262144 x 257 bf16: 73 us, against 97 us with one row per 64-thread
-        // workgroup and 163 us generic; 16384 x 1001 bf16: 14.4 us with four
-        // slots against 16.0 us with two; 262144 x 100 bf16: 28.0 us with
-        // 16-lane rows and two slots, 29.7 with four, 61.5 with a row per wave)
+        // a row per segment of the fewest lanes (8, 16, 32, 64) that hold its
+        // chunks, 4-wave workgroups; four slots per wave, two with 8- and
+        // 16-lane rows (262144 x 257 bf16: 73 us, against 97 us with one row
+        // per 64-thread workgroup and 163 us generic; 16384 x 1001 bf16: 14.4
+        // us with four slots against 16.0 us with two; 262144 x 100 bf16: 28.0
+        // us with 16-lane rows and two slots, 29.7 with four, 61.5 with a row
+        // per wave; 262144 x 36 bf16: 16.1 us with 8-lane rows, 22.4 with 16)
         p->variant = RMSNORM_VARIANT_SHIFTED_WAVE;
-        p->lanes_per_row = nchunks <= 16 ? 16 : (nchunks <= 32 ? 32 : 64);
+        p->lanes_per_row = nchunks <= 8 ? 8 : (nchunks <= 16 ? 16 : (nchunks <= 32 ? 32 : 64));
         p->vectors_per_lane = static_cast<int>(ceil_div(nchunks, p->lanes_per_row));
         p->block_threads = kWaveBlockThreads;
-        p->row_slots = p->lanes_per_row == 16 ? 2 : kShiftedWaveSlots;
+        p->row_slots = p->lanes_per_row <= 16 ? 2 : kShiftedWaveSlots;
     } else if (!vec && acc.shifted && nchunks > kMaxShiftedWaveChunks && nchunks <= kMaxShiftedChunks) {
         // one row per workgroup: the fewest threads (64 to 1024) that hold the
         // row's chunks with at most 3 per thread (32768 x 8191 bf16: 194 us with
@@ -510,14 +511,17 @@ int choose_plan(int64_t M, int64_t N, int dtype, Access acc, rmsnorm_plan_t* p) 
         p->row_slots = 1;
     } else if (nvec <= 128) {
         p->variant = RMSNORM_VARIANT_WAVE;
-        p->lanes_per_row = nvec <= 16 ? 16 : (nvec <= 32 ? 32 : 64);
+        p->lanes_per_row = nvec <= 4 ? 4 : (nvec <= 8 ? 8 : (nvec <= 16 ? 16 : (nvec <= 32 ? 32 : 64)));
         p->vectors_per_lane = static_cast<int>(ceil_div(nvec, p->lanes_per_row));
         // Several rows per 64-lane slot (N <= 256): 2 KiB of loads per wave in
         // 2-wave workgroups measured best (262144 x 128: 23.4 against 24.0 us
-        // with 4 KiB in 4-wave workgroups); one row per slot: 4 KiB, 4 waves.
+        // with 4 KiB in 4-wave workgroups; 262144 x 64: 12.6 us with 8-lane
+        // rows, 13.5 with 16), and 4 KiB with 4-lane rows (262144 x 32: 6.4 us
+        // with four slots, 7.1 with two, 11.0 with 16-lane rows); one row per
+        // slot: 4 KiB, 4 waves.
         const bool multi_row = p->lanes_per_row < 64;
         p->block_threads = multi_row ? kWaveBlockThreadsMultiRow : kWaveBlockThreads;
-        const int64_t budget = multi_row ? kWaveBytesInFlightMultiRow : kWaveBytesInFlight;
+        const int64_t budget = (multi_row && p->lanes_per_row > 4) ? kWaveBytesInFlightMultiRow : kWaveBytesInFlight;
         const int64_t per_slot = N * es * (64 / p->lanes_per_row);
         p->row_slots = 1;
         for (int s : kWaveSlots) {
@@ -921,8 +925,8 @@ int finish_bwd_plan(rmsnorm_plan_t* p, int64_t M, int64_t N, int dtype, bool vec
                                           "aligned, and at most 2048 chunks");
         const int epv = elems_per_vector(dtype);
         p->vec_elems = epv;
-        if (p->lanes_per_row != 16 && p->lanes_per_row != 32 && p->lanes_per_row != 64)
-            return fail(RMSNORM_ERR_PLAN, "shifted wave plans take 16, 32 or 64 lanes per row");
+        if (p->lanes_per_row != 8 && p->lanes_per_row != 16 && p->lanes_per_row != 32 && p->lanes_per_row != 64)
+            return fail(RMSNORM_ERR_PLAN, "shifted wave plans take 8, 16, 32 or 64 lanes per row");
         k = find_bwd_kernel(RMSNORM_VARIANT_SHIFTED_WAVE, dtype, p->lanes_per_row, p->vectors_per_lane,
                             p->row_slots, pf);
         if (k) {
@@ -957,7 +961,7 @@ int choose_bwd_plan(int64_t M, int64_t N, bool vec_ok, bool shifted_ok, int dtyp
     const int64_t epv = elems_per_vector(dtype);
     const int64_t shifted_chunks = ceil_div(N + epv - 1, epv);
     if (!vec_ok && shifted_ok && N >= kBwdMinShiftedN && shifted_chunks <= kBwdMaxShiftedWaveChunks) {
-        // a row per segment of the fewest lanes (16, 32, 64) that hold its
+        // a row per segment of the fewest lanes (8, 16, 32, 64) that hold its
         // chunks, one chunk per lane up to 64 chunks, then two per lane of a
         // 64-lane wave.  One slot, except a row of one chunk per lane in a
         // 64-lane wave: two (262144 x 257 bf16: 118 us, against 138 us with
@@ -970,7 +974,7 @@ int choose_bwd_plan(int64_t M, int64_t N, bool vec_ok, bool shifted_ok, int dtyp
         // together it gained nothing.
         p->variant = RMSNORM_VARIANT_SHIFTED_WAVE;
         p->block_threads = kBwdWaveThreads;
-        p->lanes_per_row = shifted_chunks <= 16 ? 16 : (shifted_chunks <= 32 ? 32 : 64);
+        p->lanes_per_row = shifted_chunks <= 8 ? 8 : (shifted_chunks <= 16 ? 16 : (shifted_chunks <= 32 ? 32 : 64));
         p->vectors_per_lane = shifted_chunks <= 64 ? 1 : 2;
         p->row_slots = (p->lanes_per_row == 64 && p->vectors_per_lane == 1) ? 2 : 1;
     } else if (!vec_ok && shifted_ok && N >= kBwdMinShiftedN) {
@@ -993,7 +997,10 @@ int choose_bwd_plan(int64_t M, int64_t N, bool vec_ok, bool shifted_ok, int dtyp
         const int64_t nvec = N / epv;
         p->variant = RMSNORM_VARIANT_WAVE;
         p->block_threads = kBwdWaveThreads;
-        p->lanes_per_row = nvec <= 16 ? 16 : (nvec <= 32 ? 32 : 64);
+        // the fewest lanes (8, 16, 32, 64) that hold the row: 262144 x 40 bf16
+        // 16.7 us with 8-lane rows, 19.7 with 16; 262144 x 32 bf16 14.8 us,
+        // against 16.3 with 4-lane rows and 19.1 with 16
+        p->lanes_per_row = nvec <= 8 ? 8 : (nvec <= 16 ? 16 : (nvec <= 32 ? 32 : 64));
         p->vectors_per_lane = static_cast<int>(ceil_div(nvec, p->lanes_per_row));
         const int64_t per_slot = N * elem_size(dtype) * (64 / p->lanes_per_row);
         p->row_slots = 1;
@@ -1029,9 +1036,13 @@ int choose_bwd_plan(int64_t M, int64_t N, bool vec_ok, bool shifted_ok, int dtyp
     if (p->variant != RMSNORM_VARIANT_GENERIC) {
         // several short rows per wave off a 16-byte boundary: each row's
         // shifts are lane arithmetic, which more waves in flight hide, and
-        // the partial rows are short (at most 249 16-bit elements)
+        // the partial rows are short (at most 249 16-bit elements).  Half as
+        // many with 8-lane rows, which hold twice the rows per wave
+        // (262144 x 36 bf16: 25.4 us at G = 512, 26.6 at 1024).
         const bool short_shifted = p->variant == RMSNORM_VARIANT_SHIFTED_WAVE && p->lanes_per_row < 64;
-        cap = (short_shifted ? kBwdShortShiftedWaves : kBwdPlanWaves) / (p->block_threads / 64);
+        int64_t waves = short_shifted ? kBwdShortShiftedWaves : kBwdPlanWaves;
+        if (short_shifted && p->lanes_per_row == 8) waves /= 2;
+        cap = waves / (p->block_threads / 64);
         const int64_t traffic_cap = std::max<int64_t>(3 * M / 32, 1);
         cap = std::min(cap, traffic_cap);
     }

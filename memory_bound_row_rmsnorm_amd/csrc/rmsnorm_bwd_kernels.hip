@@ -17,7 +17,7 @@
 // registers across all of its rows) and writes one fp32 partial row of dw
 // per workgroup to a workspace [G, N].  The column pass sums the G partial
 // rows in a fixed order, so dw does not depend on timing.  The row pass has
-// the forward's two shapes: rows inside 16/32/64-lane wave segments for
+// the forward's two shapes: rows inside 8/16/32/64-lane wave segments for
 // N <= 1024 (partials of the segments and waves that share columns are
 // added in LDS at the end), and one row per workgroup for larger N (each
 // thread owns distinct columns, so its partial goes straight out).  A
@@ -607,7 +607,7 @@ __global__ __launch_bounds__(1024) void rmsnorm_bwd_shifted(BwdArgs a) {
 
 // ---------------------------------------------------------------------------
 // Row pass, shifted wave family: short rows off a 16-byte boundary (at most
-// VPL * LANES chunks) with a row per segment of LANES lanes (16, 32 or 64; two
+// VPL * LANES chunks) with a row per segment of LANES lanes (8, 16, 32 or 64; two
 // chunks per lane only with 64) and SLOTS slots of 64 / LANES rows per wave
 // per trip; lane li of a segment holds chunks v * LANES + li of its row and
 // keeps column vectors v * LANES + li of dw.  As in the shifted kernel the
@@ -993,6 +993,8 @@ __global__ __launch_bounds__(COLS * SPLIT) void rmsnorm_dw_reduce(const float* _
 // to 4 vectors per thread (rows up to 32768 16-bit elements), 6 with fp32
 // (24576 elements).
 #define RMS_BWD_FAMILY(D, DT)                                                                  \
+    RMS_BWD_WAVE2(D, DT, 4, 1, 1), RMS_BWD_WAVE2(D, DT, 4, 1, 2),                              \
+    RMS_BWD_WAVE2(D, DT, 8, 1, 1), RMS_BWD_WAVE2(D, DT, 8, 1, 2),                              \
     RMS_BWD_WAVE2(D, DT, 16, 1, 1), RMS_BWD_WAVE2(D, DT, 16, 1, 2),                            \
     RMS_BWD_WAVE2(D, DT, 32, 1, 1), RMS_BWD_WAVE2(D, DT, 32, 1, 2),                            \
     RMS_BWD_WAVE2(D, DT, 64, 1, 1), RMS_BWD_WAVE2(D, DT, 64, 1, 2),                            \
@@ -1003,6 +1005,7 @@ __global__ __launch_bounds__(COLS * SPLIT) void rmsnorm_dw_reduce(const float* _
     RMS_BWD_WIDE(D, DT, 3), RMS_BWD_WIDE(D, DT, 4),                                            \
     RMS_BWD_SHIFTED(D, DT, 1, false), RMS_BWD_SHIFTED(D, DT, 1, true),                         \
     RMS_BWD_SHIFTED(D, DT, 2, false), RMS_BWD_SHIFTED(D, DT, 2, true),                         \
+    RMS_BWD_SHIFTED_WAVE2(D, DT, 8, 1), RMS_BWD_SHIFTED_WAVE2(D, DT, 8, 2),                     \
     RMS_BWD_SHIFTED_WAVE2(D, DT, 16, 1), RMS_BWD_SHIFTED_WAVE2(D, DT, 16, 2),                   \
     RMS_BWD_SHIFTED_WAVE(D, DT, 16, 4, false), RMS_BWD_SHIFTED_WAVE2(D, DT, 32, 1),             \
     RMS_BWD_SHIFTED_WAVE2(D, DT, 32, 2), RMS_BWD_SHIFTED_WAVE(D, DT, 32, 4, false),             \

@@ -109,11 +109,16 @@ enum : int {
     DPP_HALF_MIRROR = 0x141,  // lane i <-> 7 - i within each half-row
 };
 
+// Sum over each aligned group of LANES (4, 8 or 16) lanes, in butterfly
+// stages of 2, 4, 8 and 16 lanes; every lane of a group ends with the same
+// bits (each stage adds two equal-valued partials, and a + b == b + a).
+template <int LANES = 16>
 __device__ __forceinline__ float row16_allreduce(float v) {
+    static_assert(LANES == 4 || LANES == 8 || LANES == 16, "a DPP row holds groups of 4, 8 or 16 lanes");
     v += dpp_mov<DPP_QUAD_SWAP1>(v);
     v += dpp_mov<DPP_QUAD_SWAP2>(v);
-    v += dpp_mov<DPP_HALF_MIRROR>(v);
-    v += dpp_mov<DPP_ROW_MIRROR>(v);
+    if constexpr (LANES >= 8) v += dpp_mov<DPP_HALF_MIRROR>(v);
+    if constexpr (LANES >= 16) v += dpp_mov<DPP_ROW_MIRROR>(v);
     return v;
 }
 
@@ -121,13 +126,15 @@ __device__ __forceinline__ float readlane(float v, int lane) {
     return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), lane));
 }
 
-// Sum over each aligned group of LANES lanes (16, 32 or 64); every lane of a
-// group receives the same value.  Row sums are combined through scalar
-// registers (v_readlane), so no LDS and no LDS-unit permutes are involved.
+// Sum over each aligned group of LANES lanes (4, 8, 16, 32 or 64); every lane
+// of a group receives the same value.  Groups wider than a DPP row combine
+// the row sums through scalar registers (v_readlane), so no LDS and no
+// LDS-unit permutes are involved.
 template <int LANES>
 __device__ __forceinline__ float segment_allreduce(float v) {
-    static_assert(LANES == 16 || LANES == 32 || LANES == 64, "segment must be 16, 32 or 64 lanes");
-    v = row16_allreduce(v);
+    static_assert(LANES == 4 || LANES == 8 || LANES == 16 || LANES == 32 || LANES == 64,
+                  "segment must be 4, 8, 16, 32 or 64 lanes");
+    v = row16_allreduce<(LANES < 16 ? LANES : 16)>(v);
     if constexpr (LANES == 32) {
         const float s01 = readlane(v, 0) + readlane(v, 16);
         const float s23 = readlane(v, 32) + readlane(v, 48);

@@ -70,7 +70,7 @@ struct BwdArgs {
 struct KernelEntry {
     int variant;           // rmsnorm_variant_t
     int dtype;             // rmsnorm_dtype_t
-    int lanes_per_row;     // WAVE: 16/32/64; BLOCK, GENERIC: 0 (= block size)
+    int lanes_per_row;     // WAVE: 4/8/16/32/64; SHIFTED_WAVE: 8/16/32/64; others: 0 (= block size)
     int vectors_per_lane;  // WAVE, BLOCK: 16-byte vectors per lane per row; GENERIC: 0
     int row_slots;         // WAVE: slots per wave per trip; others 1
     bool prefetch;         // WAVE, BLOCK: next trip's rows loaded before this trip's reduction

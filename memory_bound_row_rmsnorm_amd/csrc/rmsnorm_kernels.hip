@@ -11,8 +11,8 @@
 // EPV ends in a tail vector moved element by element; rstd may be NULL.
 // The families:
 //
-//  * rmsnorm_wave   -- a row lives in a segment of 16, 32 or 64 lanes of one
-//    wavefront, each lane holding VPL 16-byte vectors of it; a wave carries
+//  * rmsnorm_wave   -- a row lives in a segment of 4, 8, 16, 32 or 64 lanes of
+//    one wavefront, each lane holding VPL 16-byte vectors of it; a wave carries
 //    SLOTS x (64 / LANES) rows per trip and issues every load of the trip
 //    before its first reduction.  Reductions are DPP and v_readlane only, no
 //    LDS.  Several rows per wave for small hidden sizes follows "Rmsnorm
@@ -323,11 +323,13 @@ __global__ __launch_bounds__(1024) void rmsnorm_wave(KernelArgs a) {
 // row numbers (the dispatcher sends M below 2^31 - 2^16 only), no loop.
 // The wave index stays per lane (a scalar one turns each slot's row test into
 // a branch around its load), and the wave's ROWS consecutive rstd values go
-// out in one store.  Measured on MI355X at 16384 x 512 bf16 with inputs cold
-// in HBM, in timing copies on one box in one process: 6.22-6.25 us against
-// 6.31-6.34 us for the same kernel with a scalar wave index, a runtime
-// workgroup size and one rstd store per slot, and 6.39 us for the general
-// wave instance.
+// out in one store (up to 16 rows; the 64 rows of a 4-lane wave are gathered
+// at two instructions a row, so there each slot stores its own: 262144 x 32
+// bf16 took 7.04 us with the gather, 6.09-6.11 us without).  Measured on
+// MI355X at 16384 x 512 bf16 with inputs cold in HBM, in timing copies on one
+// box in one process: 6.22-6.25 us against 6.31-6.34 us for the same kernel
+// with a scalar wave index, a runtime workgroup size and one rstd store per
+// slot, and 6.39 us for the general wave instance.
 // ---------------------------------------------------------------------------
 template <class D, int LANES, int VPL, int SLOTS, int WPB>
 __global__ __launch_bounds__(WPB * 64) void rmsnorm_wave_exact(KernelArgs a) {
@@ -370,15 +372,26 @@ __global__ __launch_bounds__(WPB * 64) void rmsnorm_wave_exact(KernelArgs a) {
             if (row < M) store_y(yr + v * LANES, normalise<D>(d[s][v], we[v], r[s]));
     }
     if (a.rstd != nullptr) {
-        // lane j < ROWS stores row r0 + j: slot j / SEG of segment j % SEG,
-        // whose value every lane of that segment holds (read from its first lane)
-        float rv = 0.0f;
+        if constexpr (ROWS <= 16) {
+            // lane j < ROWS stores row r0 + j: slot j / SEG of segment j % SEG,
+            // whose value every lane of that segment holds (read from its first lane)
+            float rv = 0.0f;
 #pragma unroll
-        for (int j = 0; j < ROWS; ++j) {
-            const float rj = SEG == 1 ? r[j] : readlane(r[j / SEG], (j % SEG) * LANES);
-            rv = lane == j ? rj : rv;
+            for (int j = 0; j < ROWS; ++j) {
+                const float rj = SEG == 1 ? r[j] : readlane(r[j / SEG], (j % SEG) * LANES);
+                rv = lane == j ? rj : rv;
+            }
+            if (lane < ROWS && r0 + lane < M) store_rstd(a.rstd + r0 + lane, rv);
+        } else {
+            // many rows per wave (4-lane rows): gathering them costs two
+            // instructions a row; each slot's first lanes store its SEG
+            // consecutive rows instead
+#pragma unroll
+            for (int s = 0; s < SLOTS; ++s) {
+                const int row = r0 + seg + s * SEG;
+                if (li == 0 && row < M) store_rstd(a.rstd + row, r[s]);
+            }
         }
-        if (lane < ROWS && r0 + lane < M) store_rstd(a.rstd + r0 + lane, rv);
     }
 }
 
@@ -709,7 +722,7 @@ __global__ __launch_bounds__(1024) void rmsnorm_shifted(KernelArgs a) {
 
 // ---------------------------------------------------------------------------
 // Shifted wave family: the shifted kernel's chunk scheme for short rows, a
-// row per segment of LANES lanes (16, 32 or 64; at most LANES * VPL chunks),
+// row per segment of LANES lanes (8, 16, 32 or 64; at most LANES * VPL chunks),
 // SLOTS slots of 64 / LANES rows per wave per trip, no LDS and no barrier.
 // With 64 lanes a row's distance past a 16-byte boundary is uniform in its
 // wave and the weights are shifted by a branch on it; with several rows per
@@ -920,6 +933,8 @@ __global__ __launch_bounds__(1024) void rmsnorm_generic(KernelArgs a) {
 // widths that are a multiple of the vector.  Six vectors per lane fit only
 // for fp32.
 #define RMS_FAMILY(D, DT)                                                                      \
+    RMS_WAVE2(D, DT, 4, 1, 1), RMS_WAVE2(D, DT, 4, 1, 2), RMS_WAVE2(D, DT, 4, 1, 4),            \
+    RMS_WAVE2(D, DT, 8, 1, 1), RMS_WAVE2(D, DT, 8, 1, 2), RMS_WAVE2(D, DT, 8, 1, 4),            \
     RMS_WAVE2(D, DT, 16, 1, 1), RMS_WAVE2(D, DT, 16, 1, 2), RMS_WAVE2(D, DT, 16, 1, 4),         \
     RMS_WAVE2(D, DT, 32, 1, 1), RMS_WAVE2(D, DT, 32, 1, 2), RMS_WAVE2(D, DT, 32, 1, 4),         \
     RMS_WAVE2(D, DT, 64, 1, 1), RMS_WAVE2(D, DT, 64, 1, 2), RMS_WAVE2(D, DT, 64, 1, 4),         \
@@ -931,6 +946,7 @@ __global__ __launch_bounds__(1024) void rmsnorm_generic(KernelArgs a) {
     RMS_BLOCK(D, DT, 5, false),                                                                 \
     RMS_WIDE(D, DT, 2), RMS_WIDE(D, DT, 4),                                                     \
     RMS_SHIFTED(D, DT, 1), RMS_SHIFTED(D, DT, 2), RMS_SHIFTED(D, DT, 3), RMS_SHIFTED(D, DT, 4),   \
+    RMS_SHIFTED_WAVE(D, DT, 8, 1, 1), RMS_SHIFTED_WAVE(D, DT, 8, 1, 2), RMS_SHIFTED_WAVE(D, DT, 8, 1, 4), \
     RMS_SHIFTED_WAVE(D, DT, 16, 1, 1), RMS_SHIFTED_WAVE(D, DT, 16, 1, 2), RMS_SHIFTED_WAVE(D, DT, 16, 1, 4), \
     RMS_SHIFTED_WAVE(D, DT, 32, 1, 1), RMS_SHIFTED_WAVE(D, DT, 32, 1, 2), RMS_SHIFTED_WAVE(D, DT, 32, 1, 4), \
     RMS_SHIFTED_WAVE(D, DT, 64, 1, 1), RMS_SHIFTED_WAVE(D, DT, 64, 1, 2), RMS_SHIFTED_WAVE(D, DT, 64, 1, 4), \
@@ -955,8 +971,8 @@ const KernelEntry* kernel_table(int* count) {
 }
 
 // The exact-width wave forms: the shapes and workgroup sizes the wave rule
-// picks for rows of exactly 16, 32, 64 and 128 vectors (128, 256, 512, 1024
-// 16-bit elements; 64, 128, 256, 512 fp32 ones).
+// picks for rows of exactly 4, 8, 16, 32, 64 and 128 vectors (32 to 1024
+// 16-bit elements; 16 to 512 fp32 ones).
 struct ExactEntry {
     KernelEntry k;
     int threads;
@@ -967,6 +983,7 @@ struct ExactEntry {
       "rmsnorm_wave_exact<" #D "," #L "," #V "," #S "," #W ">"},                                   \
      (W) * 64}
 #define RMS_EXACT_FAMILY(D, DT)                                                                \
+    RMS_WAVE_EXACT(D, DT, 4, 1, 4, 2), RMS_WAVE_EXACT(D, DT, 8, 1, 2, 2),                       \
     RMS_WAVE_EXACT(D, DT, 16, 1, 2, 2), RMS_WAVE_EXACT(D, DT, 32, 1, 2, 2),                     \
     RMS_WAVE_EXACT(D, DT, 64, 1, 4, 4), RMS_WAVE_EXACT(D, DT, 64, 2, 2, 4)
 

@@ -54,7 +54,7 @@ def candidates(M: int, N: int, dtype: str, quick: bool = False) -> list:
     if N % epv == 0:
         nvec = N // epv
         threads_set = (64, 128, 256, 512, 1024)
-        for lanes, slots, threads in itertools.product((16, 32, 64), (1, 2, 4, 8), threads_set):
+        for lanes, slots, threads in itertools.product((4, 8, 16, 32, 64), (1, 2, 4, 8), threads_set):
             vpl = -(-nvec // lanes)
             rows_per_trip = (threads // 64) * (64 // lanes) * slots
             raw.append(base.copy(variant=1, lanes_per_row=lanes, vectors_per_lane=vpl, row_slots=slots,
@@ -80,7 +80,7 @@ def candidates(M: int, N: int, dtype: str, quick: bool = False) -> list:
         # rows that start unaligned: the shifted kernels (aligned chunks, per-row shifted weights)
         nch = -(-(N + epv - 1) // epv)
         if nch <= 128:
-            for lanes, slots, threads, pf in itertools.product((16, 32, 64), (1, 2, 4), (64, 128, 256, 512), (0, 1)):
+            for lanes, slots, threads, pf in itertools.product((8, 16, 32, 64), (1, 2, 4), (64, 128, 256, 512), (0, 1)):
                 vpl = -(-nch // lanes)
                 if vpl > 2:
                     continue

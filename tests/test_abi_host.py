@@ -136,6 +136,20 @@ def test_planner_choices_for_the_workloads():
     assert p.rows_per_trip == 16 and p.grid == 262144 // 16
     p = host_plan(64, 256)
     assert (p.lanes_per_row, p.row_slots, p.block_threads) == (32, 2, 128)
+    # rows of at most 8 vectors: 8-lane segments (2 KiB per wave), at most 4: 4-lane ones (4 KiB)
+    p = host_plan(262144, 64)
+    assert (p.lanes_per_row, p.vectors_per_lane, p.row_slots, p.block_threads) == (8, 1, 2, 128)
+    assert p.rows_per_trip == 32 and p.grid == 262144 // 32
+    p = host_plan(262144, 40)
+    assert (p.lanes_per_row, p.row_slots) == (8, 2)
+    p = host_plan(262144, 32)
+    assert (p.lanes_per_row, p.vectors_per_lane, p.row_slots, p.block_threads) == (4, 1, 4, 128)
+    assert p.rows_per_trip == 128 and p.grid == 262144 // 128
+    p = host_plan(1000, 8)
+    assert (p.lanes_per_row, p.row_slots) == (4, 4)
+    p = host_plan(1000, 72)
+    assert (p.lanes_per_row, p.row_slots) == (16, 2)
+    assert (host_plan(1000, 32, FP32).lanes_per_row, host_plan(1000, 16, FP32).lanes_per_row) == (8, 4)
     p = host_plan(100, 1024)
     assert (p.lanes_per_row, p.vectors_per_lane, p.row_slots) == (64, 2, 2)
     p = host_plan(32768, 8192)            # 512 MiB of x: about 1 MiB of rows per XCD group
@@ -240,15 +254,16 @@ def test_shifted_rule(N, threads, vpt, prefetch):
                                                                             prefetch)
 
 
-@pytest.mark.parametrize("N,dtype,lanes,vpl", [(17, BF16, 16, 1), (121, BF16, 16, 1), (129, BF16, 32, 1),
+@pytest.mark.parametrize("N,dtype,lanes,vpl", [(17, BF16, 8, 1), (57, BF16, 8, 1), (58, BF16, 16, 1),
+                                               (121, BF16, 16, 1), (129, BF16, 32, 1),
                                                (249, BF16, 32, 1), (257, BF16, 64, 1), (505, BF16, 64, 1),
                                                (513, BF16, 64, 2), (1017, BF16, 64, 2), (130, FP16, 32, 1),
-                                               (61, FP32, 16, 1), (509, FP32, 64, 2)])
+                                               (29, FP32, 8, 1), (61, FP32, 16, 1), (509, FP32, 64, 2)])
 def test_shifted_wave_rule(N, dtype, lanes, vpl):
-    """Rows of 16 elements up to 128 chunks: a row per segment of 16, 32 or 64 lanes (the fewest
-    that hold its chunks, up to 64), four slots per wave (two with 16-lane rows)."""
+    """Rows of 16 elements up to 128 chunks: a row per segment of 8, 16, 32 or 64 lanes (the fewest
+    that hold its chunks, up to 64), four slots per wave (two with 8- and 16-lane rows)."""
     p = host_plan(100000, N, dtype=dtype)
-    slots = 2 if lanes == 16 else 4
+    slots = 2 if lanes <= 16 else 4
     assert (p.variant, p.lanes_per_row, p.vectors_per_lane, p.row_slots) == (bnd.VARIANT_SHIFTED_WAVE, lanes, vpl,
                                                                             slots)
     rows = 4 * (64 // lanes) * slots
@@ -399,6 +414,10 @@ def test_bwd_plans_and_workspace():
     assert ws(16384, 512) == 256 * 512 * 4
     p = plan(262144, 128, FP16)
     assert (p.variant, p.lanes_per_row, p.row_slots, p.grid, p.prefetch) == (bnd.VARIANT_WAVE, 16, 2, 256, 1)
+    for n in (16, 40, 64):                 # rows of at most 8 vectors: 8-lane segments, two slots
+        p = plan(262144, n)
+        assert (p.variant, p.lanes_per_row, p.row_slots, p.grid, p.prefetch) == (bnd.VARIANT_WAVE, 8, 2, 256, 1)
+        assert p.rows_per_trip == 256
     p = plan(32768, 8192)
     assert (p.variant, p.block_threads, p.vectors_per_lane, p.grid) == (bnd.VARIANT_BLOCK, 512, 2, 512)
     assert p.prefetch == 0 and ws(32768, 8192) == 512 * 8192 * 4      # two workgroups per unit: no prefetch
@@ -659,11 +678,14 @@ def test_bwd_shifted_plans():
     p = bwd_plan_ex(32768, 8191, None)
     assert (p.variant, p.block_threads, p.vectors_per_lane, p.grid, p.prefetch) == \
         (bnd.VARIANT_SHIFTED, 1024, 2, 256, 1)
-    # rows of at most 128 chunks: a row per 16/32/64-lane segment, one chunk per lane (two per lane
+    # rows of at most 128 chunks: a row per 8/16/32/64-lane segment, one chunk per lane (two per lane
     # of a 64-lane wave above 64 chunks)
     p = bwd_plan_ex(100, 17, None)                 # 3 chunks
     assert (p.variant, p.lanes_per_row, p.vectors_per_lane, p.row_slots, p.block_threads) == \
-        (bnd.VARIANT_SHIFTED_WAVE, 16, 1, 1, 1024)
+        (bnd.VARIANT_SHIFTED_WAVE, 8, 1, 1, 1024)
+    # 5-6 chunks: eight rows per wave, up to 32 waves per compute unit (512 workgroups)
+    p = bwd_plan_ex(262144, 36, None)
+    assert (p.lanes_per_row, p.row_slots, p.rows_per_trip, p.grid, p.prefetch) == (8, 1, 128, 512, 0)
     # 13 chunks: one slot of four rows per wave, up to 64 waves per compute unit (1024 workgroups)
     p = bwd_plan_ex(262144, 100, None)
     assert (p.lanes_per_row, p.row_slots, p.rows_per_trip, p.grid, p.prefetch) == (16, 1, 64, 1024, 0)

@@ -100,7 +100,7 @@ def bwd_candidates(bnd, M, N, dtype):
     epv = 4 if dtype == "fp32" else 8
     out = []
     for pf in (0, 1):
-        for lanes in (16, 32, 64):
+        for lanes in (4, 8, 16, 32, 64):
             for vpl in (1, 2):
                 for slots in (1, 2, 4):
                     for threads in (256, 512, 1024):
@@ -151,6 +151,45 @@ def test_bwd_every_kernel(bnd, name):
             parity.compare_bwd(dx, dw, dx_e[2], dx_e[3], dwe, dx_e[4], wl.dtype, M, grid, f"{name} {p.as_dict()}")
             ran += 1
     assert ran >= 12, ran
+
+
+@pytest.mark.parametrize("M,N,dtype", [(999, 16, "bf16"), (777, 40, "bf16"), (500, 64, "fp16"), (1000, 24, "bf16"),
+                                       (333, 32, "fp32"), (300, 16, "fp32"), (129, 8, "fp16")])
+def test_bwd_short_rows_every_kernel(bnd, M, N, dtype):
+    """Rows of at most 8 vectors: the rule's plan (8-lane segments) and every compiled wave instance
+    that covers the row, 4- and 8-lane segments included, at grids of 1, 5 and M."""
+    x, w, dy, r32 = any_case(M, N, dtype, 1.0, seed=N + 11)
+    xg, wg, dyg = x.to(DEV), w.to(DEV), dy.to(DEV)
+    rg = torch.from_numpy(r32).to(DEV)
+    _, dwe, dxe, dxs, dws = parity.oracle_bwd_for(x, w, dy, r32, 1.0, dtype)
+    base = bnd.bwd_plan_query(M, N, dtype, xg.data_ptr(), dyg.data_ptr(), dyg.data_ptr())
+    assert (base.variant, base.lanes_per_row) == (bnd.VARIANT_WAVE, 8), base.as_dict()
+    dx, dw = bnd.rmsnorm_bwd(xg, wg, dyg, rg, 1.0)
+    torch.cuda.synchronize()
+    parity.compare_bwd(dx, dw, dxe, dxs, dwe, dws, dtype, M, base.grid, f"bwd short rule {M}x{N} {dtype}")
+    ran, lanes_seen = 0, set()
+    for plan in bwd_candidates(bnd, M, N, dtype):
+        if plan.variant != bnd.VARIANT_WAVE:
+            continue
+        for grid in (1, 5, M):
+            p = plan.copy(grid=grid)
+            dx = torch.empty_like(xg)
+            dw = torch.full((N,), float("nan"), dtype=torch.float32, device=DEV)
+            ws = torch.empty(grid * N + 4, dtype=torch.float32, device=DEV)
+            announce("bwd short", M, N, dtype, p.as_dict())
+            try:
+                bnd.rmsnorm_bwd_out(xg, wg, dyg, rg, dx, dw, ws, 1.0, plan=p)
+            except bnd.RmsnormError as e:
+                if e.status == 8:
+                    continue
+                raise
+            torch.cuda.synchronize()
+            parity.compare_bwd(dx, dw, dxe, dxs, dwe, dws, dtype, M, grid, f"bwd short {M}x{N} {dtype} {p.as_dict()}")
+            lanes_seen.add(p.lanes_per_row)
+            ran += 1
+    epv = EPV[dtype]
+    assert 8 in lanes_seen and (4 in lanes_seen or N > 4 * epv), lanes_seen
+    assert ran >= 24, ran
 
 
 def test_bwd_in_place_and_stream(bnd):
@@ -451,7 +490,7 @@ def test_bwd_shifted_rule(bnd, M, N, dtype, offset):
 def shifted_wave_candidates(bnd, base, N, epv):
     out = []
     for pf in (0, 1):
-        for lanes, vpl in ((16, 1), (32, 1), (64, 1), (64, 2)):
+        for lanes, vpl in ((8, 1), (16, 1), (32, 1), (64, 1), (64, 2)):
             for slots in (1, 2, 4):
                 for threads in (256, 1024):
                     if lanes * vpl * epv >= N + epv - 1:
@@ -464,7 +503,8 @@ def shifted_wave_candidates(bnd, base, N, epv):
 @pytest.mark.parametrize("M,N,dtype", [(97, 3001, "bf16"), (200, 1001, "fp16"), (60, 1003, "fp32"),
                                        (150, 33, "bf16"), (777, 100, "bf16"), (500, 250, "fp16"),
                                        (300, 61, "fp32"), (333, 505, "bf16"), (129, 513, "bf16"),
-                                       (70, 301, "fp32")])
+                                       (70, 301, "fp32"), (300, 36, "bf16"), (200, 20, "fp16"),
+                                       (150, 29, "fp32")])
 def test_bwd_shifted_every_kernel(bnd, M, N, dtype):
     x, w, dy, r32 = any_case(M, N, dtype, 1.0, seed=N + 7)
     xg, wg, dyg = x.to(DEV), w.to(DEV), dy.to(DEV)

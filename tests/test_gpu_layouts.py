@@ -275,7 +275,63 @@ def test_shifted_every_instance(bnd, dtype, N):
 
 
 @pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float16, torch.float32])
-@pytest.mark.parametrize("N", [9, 61, 100, 129, 300, 505, 513, 1001, 1017])
+@pytest.mark.parametrize("vectors,tail", [(1, 0), (2, 0), (3, 0), (4, 0), (5, 0), (8, 0), (4, 3), (8, 1)])
+def test_narrow_wave_every_instance(bnd, dtype, vectors, tail):
+    """Rows of at most 8 vectors: every 4- and 8-lane wave instance that covers the row (slots,
+    workgroup sizes, next-trip prefetch, one trip and persistent grids), rows strided by a whole
+    number of vectors, with a ragged tail of `tail` elements cut from the last vector."""
+    es = torch.tensor([], dtype=dtype).element_size()
+    epv = 16 // es
+    if tail >= epv:
+        return
+    N = vectors * epv - tail
+    ld = vectors * epv + epv                       # one spare vector between rows
+    M = 301
+    sigma = 100.0 if dtype == torch.float16 else 1.0
+    xb = draw((M * ld,), dtype, 97 + N, sigma).to(DEV)
+    x = xb.as_strided((M, N), (ld, 1), 0)
+    w = (1.0 + 0.1 * draw((N,), torch.float32, 98)).to(dtype).to(DEV)
+    xc, wc = x.cpu().contiguous(), w.cpu()
+    if dtype == torch.float32:
+        ref = parity.oracle_fp32(xc, wc, 1e-6, 1.0)
+    else:
+        dt = "bf16" if dtype == torch.bfloat16 else "fp16"
+        ref = parity.oracle_for(xc, wc, 1e-6, 1.0, dt)
+    y0_base = filled(M * ld + 16, dtype)
+    y0 = y0_base.as_strided((M, N), (ld, 1), 8)
+    base = bnd.plan_query_ex(x, w, y0)
+    assert base.variant == bnd.VARIANT_WAVE and base.lanes_per_row == (4 if vectors <= 4 else 8), base.as_dict()
+    check(bnd, x, w, y0, y0_base, (M, N), (ld, 1), 8, offset=1.0, what=f"narrow wave rule {M}x{N} ld {ld} {dtype}")
+    ran, lanes_seen = 0, set()
+    for lanes, slots, threads, pf in itertools.product((4, 8), (1, 2, 4), (64, 128, 256), (0, 1)):
+        rows = threads // 64 * (64 // lanes) * slots
+        for grid in (-(-M // rows), 2):
+            p = base.copy(variant=bnd.VARIANT_WAVE, lanes_per_row=lanes, block_threads=threads, vectors_per_lane=1,
+                          row_slots=slots, prefetch=pf, grid=grid, xcd_group=1, max_blocks_per_cu=0)
+            y_base = filled(M * ld + 16, dtype)
+            y = y_base.as_strided((M, N), (ld, 1), 8)
+            what = f"narrow wave {M}x{N} ld {ld} {dtype} lanes {lanes} slots {slots} {threads} thr pf {pf} grid {grid}"
+            announce(what)
+            try:
+                out, rstd = bnd.rmsnorm_fwd_ex(x, w, 1e-6, 1.0, out=y, plan=p)
+            except bnd.RmsnormError as e:
+                if e.status == 8:                # does not cover N, or no such instance
+                    continue
+                raise
+            torch.cuda.synchronize()
+            if dtype == torch.float32:
+                parity.compare_fp32(out.cpu().contiguous(), rstd, ref[0], ref[1], what)
+            else:
+                parity.compare(out.cpu().contiguous(), rstd, ref[0], ref[1], dt, what)
+            mask = view_mask(y_base.numel(), (M, N), (ld, 1), 8)
+            assert bool((y_base.cpu().view(INT_VIEW[dtype])[~mask] == SENTINEL[dtype]).all()), what
+            lanes_seen.add(lanes)
+            ran += 1
+    assert 8 in lanes_seen and (4 in lanes_seen or vectors > 4) and ran >= 20, (lanes_seen, ran)
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float16, torch.float32])
+@pytest.mark.parametrize("N", [9, 17, 29, 36, 61, 100, 129, 300, 505, 513, 1001, 1017])
 def test_shifted_wave_every_instance(bnd, dtype, N):
     """The wave form of the shifted kernel: every compiled instance that covers N, one trip and
     persistent grids, next-trip prefetch on and off."""
@@ -294,7 +350,7 @@ def test_shifted_wave_every_instance(bnd, dtype, N):
         return                                   # aligned rows never take a shifted kernel
     base = bnd.plan_query_ex(x, w)
     ran = 0
-    for lanes, vpl, slots, threads, pf in itertools.product((16, 32, 64), (1, 2), (1, 2, 4), (64, 256), (0, 1)):
+    for lanes, vpl, slots, threads, pf in itertools.product((8, 16, 32, 64), (1, 2), (1, 2, 4), (64, 256), (0, 1)):
         rows = threads // 64 * (64 // lanes) * slots
         for grid in (-(-M // rows), 2):
             p = base.copy(variant=bnd.VARIANT_SHIFTED_WAVE, lanes_per_row=lanes, block_threads=threads,
@@ -320,7 +376,8 @@ def test_shifted_wave_every_instance(bnd, dtype, N):
 
 
 @pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
-@pytest.mark.parametrize("N,lead", [(3001, 3), (1025, 1), (8191, 5), (300, 7), (129, 2), (1017, 6), (61, 3), (130, 5)])
+@pytest.mark.parametrize("N,lead", [(3001, 3), (1025, 1), (8191, 5), (300, 7), (129, 2), (1017, 6), (61, 3), (130, 5),
+                                    (36, 3), (19, 1)])
 def test_shifted_reads_whole_edge_chunks_but_uses_only_the_row(bnd, dtype, N, lead):
     """The shifted kernel loads the aligned 16 bytes around each row's ends, and w's last vector whole:
     NaN in those bytes (before the first row, after the last, after w) must not reach y or rstd, and

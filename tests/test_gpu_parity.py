@@ -61,7 +61,7 @@ def candidate_plans(bnd, M, N, dtype):
     base = bnd.plan_query(M, N, dtype)
     out = []
     for pf in (0, 1):
-        for lanes in (16, 32, 64):
+        for lanes in (4, 8, 16, 32, 64):
             for vpl in range(1, 9):
                 for slots in (1, 2, 4, 8):
                     if lanes * vpl * 8 < N:
@@ -170,12 +170,12 @@ def test_sweep(bnd, N, dtype):
 
 # ---------------------------------------------------------------------------
 # 3b. The exact-width wave forms: the instance the rule's launches take over
-#     contiguous rows of exactly 16, 32, 64 or 128 vectors.  Each one, named
-#     through rmsnorm_fwd_kernel_query, over row counts that end inside a
-#     workgroup (and one row), both offsets, and with rstd not written.
+#     contiguous rows of exactly 4, 8, 16, 32, 64 or 128 vectors.  Each one,
+#     named through rmsnorm_fwd_kernel_query, over row counts that end inside
+#     a workgroup (and one row), both offsets, and with rstd not written.
 # ---------------------------------------------------------------------------
 @pytest.mark.parametrize("dtype", ["bf16", "fp16", "fp32"])
-@pytest.mark.parametrize("vectors", [16, 32, 64, 128])
+@pytest.mark.parametrize("vectors", [4, 8, 16, 32, 64, 128])
 def test_exact_wave_forms(bnd, vectors, dtype):
     N = vectors * (4 if dtype == "fp32" else 8)
     g = torch.Generator().manual_seed(7 * N + len(dtype))
