@@ -709,6 +709,14 @@ int64_t bwd_wave_lds(const rmsnorm_plan_t* p, int64_t N) {
     return static_cast<int64_t>(p->block_threads / 64) * (64 / p->lanes_per_row) * N * 4;
 }
 
+// Dynamic LDS of the shifted row pass: with three chunks per thread, each
+// thread's dw column vectors (vectors_per_lane of vec_elems floats); none
+// with fewer, which keep dw in registers.
+int64_t bwd_shifted_lds(const rmsnorm_plan_t* p, int dtype) {
+    if (p->vectors_per_lane < 3) return 0;
+    return static_cast<int64_t>(p->block_threads) * p->vectors_per_lane * elems_per_vector(dtype) * 4;
+}
+
 // Row layout of x, dy and dx for the backward, normalised as the forward's:
 // `rows` rows per batch, strides in elements.
 struct BwdLayout {
@@ -918,6 +926,8 @@ int finish_bwd_plan(rmsnorm_plan_t* p, int64_t M, int64_t N, int dtype, bool vec
         k = find_bwd_kernel(RMSNORM_VARIANT_SHIFTED, dtype, 0, p->vectors_per_lane, 1, pf);
         if (k && static_cast<int64_t>(p->block_threads) * p->vectors_per_lane * epv < N + epv - 1)
             return fail(RMSNORM_ERR_PLAN, "shifted plan does not cover N");
+        if (k && bwd_shifted_lds(p, dtype) > kBwdMaxLds)
+            return fail(RMSNORM_ERR_PLAN, "shifted plan needs more than 64 KiB of LDS for dw");
     } else if (p->variant == RMSNORM_VARIANT_SHIFTED_WAVE) {
         if (!shifted)
             return fail(RMSNORM_ERR_PLAN, "the shifted backward kernels need x, dy and dx equally far past a 16-byte "
@@ -981,9 +991,15 @@ int choose_bwd_plan(int64_t M, int64_t N, bool vec_ok, bool shifted_ok, int dtyp
         // one row per workgroup of the fewest threads (up to 1024) that hold
         // the row with at most 2 chunks per thread (8192 x 3001 bf16: 47.5 us
         // with 256 x 2, 46.6 with 512 x 1; 16384 x 1002 fp32: 44.0 us with
-        // 128 x 2, 45.6 with 256 x 1)
+        // 128 x 2, 45.6 with 256 x 1).  Rows of 1025 to 1536 chunks would
+        // leave up to half of 1024 x 2 idle: with rows enough for two
+        // 512-thread workgroups per CU, 512 x 3 (32768 x 8191 bf16: 366 us
+        // against 456 us; 4096 x 4097 fp32, 384 workgroups: 52.6 against 47.8)
         const int64_t nchunks = ceil_div(N + epv - 1, epv);
-        const int64_t per_thread = 2;
+        int64_t per_thread = 2;
+        if (nchunks > 1024 && nchunks <= 1536 && 3 * M / 32 >= 512 &&
+            find_bwd_kernel(RMSNORM_VARIANT_SHIFTED, dtype, 0, 3, 1, false))
+            per_thread = 3;
         p->variant = RMSNORM_VARIANT_SHIFTED;
         p->row_slots = 1;
         p->block_threads = 64;
@@ -1085,7 +1101,8 @@ int launch_bwd(const KernelEntry* k, const rmsnorm_plan_t* p, const void* x, con
         a.dx_bs = L.dx_bs;
         void* args[] = {&a};
         const bool wave = p->variant == RMSNORM_VARIANT_WAVE || p->variant == RMSNORM_VARIANT_SHIFTED_WAVE;
-        const size_t lds = wave ? static_cast<size_t>(bwd_wave_lds(p, N)) : 0;
+        size_t lds = wave ? static_cast<size_t>(bwd_wave_lds(p, N)) : 0;
+        if (p->variant == RMSNORM_VARIANT_SHIFTED) lds = static_cast<size_t>(bwd_shifted_lds(p, k->dtype));
         hipError_t e = hipLaunchKernel(k->func, dim3(static_cast<unsigned>(p->grid)),
                                        dim3(static_cast<unsigned>(p->block_threads)), args, lds, s);
         if (e != hipSuccess)

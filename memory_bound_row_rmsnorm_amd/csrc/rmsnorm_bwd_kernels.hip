@@ -425,6 +425,8 @@ __global__ __launch_bounds__(1024) void rmsnorm_bwd_wide(BwdArgs a) {
 // and dx must sit the same distance past a boundary on every row; dx may be
 // dy (in place: every element is read, then written, by one thread, and the
 // neighbouring rows' elements of an edge chunk are read but never used).
+// Dynamic LDS: none up to two chunks per thread; with three, each thread's
+// dw column vectors (threads x 3 x EPV floats).
 // ---------------------------------------------------------------------------
 // acc[i] += r * (element i + al of the concatenation (cur, nxt)), for the
 // wave-uniform al of one row: one branch, constant register indices.
@@ -451,8 +453,17 @@ template <class D, int VPT, bool PREFETCH>
 __global__ __launch_bounds__(1024) void rmsnorm_bwd_shifted(BwdArgs a) {
     typedef typename D::elem_t E;
     constexpr int EPV = D::EPV;
+    constexpr int H = EPV / 4;                   // float4 quarters of a column vector
+    // Up to two chunks per thread, dw and both weight vectors of each chunk
+    // stay in registers.  Three do not fit 128 VGPRs that way: then dw lives
+    // in LDS (each thread reads and writes only its own columns) and w's
+    // vector c - 1 comes from the lane below.
+    constexpr bool LDS_DW = VPT >= 3;
+    constexpr int VR = LDS_DW ? 1 : VPT;         // chunk sets held in registers (wlo, dwp)
     __shared__ float part[2][16];
     __shared__ float first[2][VPT][16][EPV];     // each wave's first lane's products dy * x
+    __shared__ u32x4 wtop[LDS_DW ? VPT : 1][16]; // each wave's last lane's w vector, per chunk set
+    extern __shared__ float4 lds_dw[];           // LDS_DW: [VPT][H][threads], each thread's dw columns
     const E* x = static_cast<const E*>(a.x);
     const E* dy = static_cast<const E*>(a.dy);
     E* dx = static_cast<E*>(a.dx);
@@ -464,27 +475,52 @@ __global__ __launch_bounds__(1024) void rmsnorm_bwd_shifted(BwdArgs a) {
     const int tid = threadIdx.x;
     const int nt = a.threads;
     const int lane = tid & 63;
-    const int wid = tid >> 6;
+    const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int nw = nt >> 6;
 
-    // w vectors c - 1 and c of each chunk c (the same on every row)
+    // w vectors c - 1 and c of each chunk c (the same on every row); with
+    // LDS_DW vector c - 1 comes from the lane below, or for a wave's first
+    // lane from the last lane of the wave below (of the last wave, one chunk
+    // set back, for wave 0)
     auto wvec = [&](int k) -> u32x4 {
         if (k < 0 || k >= nvec_w) return kZero;
         return k == nvec_w - 1 ? keep_row<D>(w[k], k * EPV, n) : w[k];
     };
-    u32x4 wlo[VPT], whi[VPT];
-    float dwp[VPT][EPV];
+    u32x4 whi[VPT], wlo[VR];
+    float dwp[VR][EPV];
 #pragma unroll
     for (int v = 0; v < VPT; ++v) {
         const int c = v * nt + tid;
-        wlo[v] = wvec(c - 1);
         whi[v] = wvec(c);
+        if constexpr (LDS_DW) {
+            if (lane == 63) wtop[v][wid] = whi[v];
 #pragma unroll
-        for (int k = 0; k < EPV; ++k) dwp[v][k] = 0.0f;
+            for (int h = 0; h < H; ++h) lds_dw[(v * H + h) * nt + tid] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+        } else {
+            wlo[v] = wvec(c - 1);
+#pragma unroll
+            for (int k = 0; k < EPV; ++k) dwp[v][k] = 0.0f;
+        }
     }
+    if constexpr (LDS_DW) __syncthreads();
     // offset + w in the chunk frame of a row al elements past a boundary
     auto weights = [&](float (&g)[EPV], int v, int al) {
-        widen_g<D>(g, al == 0 ? whi[v] : funnel<D>(wlo[v], whi[v], EPV - al), a.offset);
+        u32x4 q = whi[v];
+        if (al != 0) {
+            u32x4 lo;
+            if constexpr (LDS_DW) {
+                u32x4 below = kZero;
+                if (lane == 0) {
+                    if (wid > 0) below = wtop[v][wid - 1];
+                    else if (v > 0) below = wtop[v > 0 ? v - 1 : 0][nw - 1];
+                }
+                lo = from_lane_below(whi[v], below);
+            } else {
+                lo = wlo[v < VR ? v : 0];
+            }
+            q = funnel<D>(lo, whi[v], EPV - al);
+        }
+        widen_g<D>(g, q, a.offset);
     };
 
     auto load_row = [&](u32x4 (&xd)[VPT], u32x4 (&dd)[VPT], float& r, int& al, int64_t rr) {
@@ -578,7 +614,24 @@ __global__ __launch_bounds__(1024) void rmsnorm_bwd_shifted(BwdArgs a) {
                 else if (v + 1 < VPT) up = first[par][v + 1 < VPT ? v + 1 : 0][0][k];
                 pn[k] = from_lane_above(p[k], up);
             }
-            add_columns<EPV>(dwp[v], p, pn, al, r);
+            if constexpr (LDS_DW) {
+                float acc[EPV];
+#pragma unroll
+                for (int h = 0; h < H; ++h) {
+                    const float4 q = lds_dw[(v * H + h) * nt + tid];
+                    acc[4 * h] = q.x;
+                    acc[4 * h + 1] = q.y;
+                    acc[4 * h + 2] = q.z;
+                    acc[4 * h + 3] = q.w;
+                }
+                add_columns<EPV>(acc, p, pn, al, r);
+#pragma unroll
+                for (int h = 0; h < H; ++h)
+                    lds_dw[(v * H + h) * nt + tid] =
+                        make_float4(acc[4 * h], acc[4 * h + 1], acc[4 * h + 2], acc[4 * h + 3]);
+            } else {
+                add_columns<EPV>(dwp[v < VR ? v : 0], p, pn, al, r);
+            }
         }
         par ^= 1;
         row = next;
@@ -598,9 +651,23 @@ __global__ __launch_bounds__(1024) void rmsnorm_bwd_shifted(BwdArgs a) {
     for (int v = 0; v < VPT; ++v) {
         const int c = v * nt + tid;
         if (c < nvec_w) {
+            float e[EPV];
+#pragma unroll
+            for (int h = 0; h < H; ++h) {
+                if constexpr (LDS_DW) {
+                    const float4 q = lds_dw[(v * H + h) * nt + tid];
+                    e[4 * h] = q.x;
+                    e[4 * h + 1] = q.y;
+                    e[4 * h + 2] = q.z;
+                    e[4 * h + 3] = q.w;
+                } else {
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) e[4 * h + j] = dwp[v < VR ? v : 0][4 * h + j];
+                }
+            }
 #pragma unroll
             for (int k = 0; k < EPV; ++k)
-                if (c * EPV + k < n) dst[c * EPV + k] = dwp[v][k];
+                if (c * EPV + k < n) dst[c * EPV + k] = e[k];
         }
     }
 }
@@ -1005,6 +1072,7 @@ __global__ __launch_bounds__(COLS * SPLIT) void rmsnorm_dw_reduce(const float* _
     RMS_BWD_WIDE(D, DT, 3), RMS_BWD_WIDE(D, DT, 4),                                            \
     RMS_BWD_SHIFTED(D, DT, 1, false), RMS_BWD_SHIFTED(D, DT, 1, true),                         \
     RMS_BWD_SHIFTED(D, DT, 2, false), RMS_BWD_SHIFTED(D, DT, 2, true),                         \
+    RMS_BWD_SHIFTED(D, DT, 3, false),                                                          \
     RMS_BWD_SHIFTED_WAVE2(D, DT, 8, 1), RMS_BWD_SHIFTED_WAVE2(D, DT, 8, 2),                     \
     RMS_BWD_SHIFTED_WAVE2(D, DT, 16, 1), RMS_BWD_SHIFTED_WAVE2(D, DT, 16, 2),                   \
     RMS_BWD_SHIFTED_WAVE(D, DT, 16, 4, false), RMS_BWD_SHIFTED_WAVE2(D, DT, 32, 1),             \

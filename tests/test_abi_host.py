@@ -675,9 +675,15 @@ def test_bwd_shifted_plans():
     p = bwd_plan_ex(8192, 3001, None)
     assert (p.variant, p.block_threads, p.vectors_per_lane, p.vec_elems) == (bnd.VARIANT_SHIFTED, 256, 2, 8)
     assert (p.lanes_per_row, p.rows_per_trip, p.grid, p.prefetch) == (256, 1, 768, 0)
+    # 1025 chunks: 512 x 3 when the rows fill two 512-thread workgroups per unit, else 1024 x 2
     p = bwd_plan_ex(32768, 8191, None)
     assert (p.variant, p.block_threads, p.vectors_per_lane, p.grid, p.prefetch) == \
+        (bnd.VARIANT_SHIFTED, 512, 3, 512, 0)
+    p = bwd_plan_ex(4096, 8191, None)
+    assert (p.variant, p.block_threads, p.vectors_per_lane, p.grid, p.prefetch) == \
         (bnd.VARIANT_SHIFTED, 1024, 2, 256, 1)
+    assert (bwd_plan_ex(32768, 12281, None).block_threads, bwd_plan_ex(32768, 12282, None).block_threads) == \
+        (512, 1024)                                # 1536 and 1537 chunks
     # rows of at most 128 chunks: a row per 8/16/32/64-lane segment, one chunk per lane (two per lane
     # of a 64-lane wave above 64 chunks)
     p = bwd_plan_ex(100, 17, None)                 # 3 chunks

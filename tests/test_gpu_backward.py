@@ -468,7 +468,7 @@ def any_case(M, N, dtype, offset, seed, sigma=2.0):
     (2000, 257, "bf16", 1.0), (300, 1002, "fp32", 0.0), (50, 8189, "fp32", 1.0), (41, 4097, "fp32", 0.0),
     (3000, 249, "bf16", 0.0), (777, 61, "fp32", 1.0), (600, 505, "fp16", 0.0), (5000, 36, "bf16", 1.0),
     (4099, 300, "bf16", 1.0), (4099, 513, "bf16", 1.0), (1001, 1017, "fp16", 0.0), (777, 301, "fp32", 1.0),
-    (333, 509, "fp32", 0.0), (2000, 506, "bf16", 0.0)])
+    (333, 509, "fp32", 0.0), (2000, 506, "bf16", 0.0), (5600, 8193, "fp16", 1.0)])
 def test_bwd_shifted_rule(bnd, M, N, dtype, offset):
     x, w, dy, r32 = any_case(M, N, dtype, offset, seed=N + M)
     xg, wg, dyg = x.to(DEV), w.to(DEV), dy.to(DEV)
@@ -515,9 +515,9 @@ def test_bwd_shifted_every_kernel(bnd, M, N, dtype):
     ran = 0
     for pf in (0, 1):
         for threads in (64, 128, 256, 512, 1024):
-            for vpt in (1, 2):
-                if threads * vpt * epv < N + epv - 1:
-                    continue
+            for vpt in (1, 2, 3):
+                if threads * vpt * epv < N + epv - 1 or threads * vpt * epv * 4 > 65536 or (vpt == 3 and pf):
+                    continue    # does not cover the row, dw exceeds 64 KiB of LDS, or no such instance
                 for grid in (1, 5, M):
                     p = base.copy(variant=bnd.VARIANT_SHIFTED, block_threads=threads, vectors_per_lane=vpt,
                                   prefetch=pf, grid=grid)
