@@ -27,7 +27,6 @@ import argparse
 import ctypes
 import itertools
 import json
-import math
 import sys
 
 import torch

@@ -5,7 +5,6 @@ names itself.
 """
 from __future__ import annotations
 
-import numpy as np
 import pytest
 import torch
 
