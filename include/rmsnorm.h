@@ -98,14 +98,17 @@ typedef enum rmsnorm_variant {
  *                     or 4 (fp32), for every family but GENERIC (1)
  *   lanes_per_row     WAVE: lanes sharing one row (4, 8, 16, 32 or 64);
  *                     SHIFTED_WAVE: 8, 16, 32 or 64; BLOCK, SHIFTED and
- *                     GENERIC: threads per row (= block_threads)
+ *                     GENERIC: threads per row (= block_threads, or
+ *                     block_threads / row_slots for a backward BLOCK plan)
  *   vectors_per_lane  16-byte vectors (SHIFTED, SHIFTED_WAVE: aligned chunks)
  *                     each lane holds per row; lanes_per_row * vectors_per_lane
  *                     * vec_elems >= N, and >= N + vec_elems - 1 for the
  *                     shifted families, whose rows straddle one more chunk
  *   row_slots         WAVE, SHIFTED_WAVE: row slots per wave per trip; a slot
  *                     is 64/lanes_per_row rows, and all of a trip's loads are
- *                     issued before its first reduction.  1 otherwise
+ *                     issued before its first reduction.  Backward BLOCK: rows
+ *                     per workgroup per trip (1, 2 or 4; lanes_per_row =
+ *                     block_threads / row_slots threads each).  1 otherwise
  *   block_threads     workgroup size (a multiple of 64, at most 1024)
  *   prefetch          WAVE, BLOCK, SHIFTED_WAVE: 1 = load the next trip's rows
  *                     before this trip's reduction (pays off when workgroups

@@ -700,6 +700,7 @@ const KernelEntry* find_bwd_kernel(int variant, int dtype, int lanes, int vpl, i
         if ((variant == RMSNORM_VARIANT_BLOCK || variant == RMSNORM_VARIANT_SHIFTED || variant == RMSNORM_VARIANT_WIDE) &&
             k.vectors_per_lane != vpl)
             continue;
+        if (variant == RMSNORM_VARIANT_BLOCK && k.row_slots != slots) continue;
         return &k;
     }
     return nullptr;
@@ -707,6 +708,14 @@ const KernelEntry* find_bwd_kernel(int variant, int dtype, int lanes, int vpl, i
 
 int64_t bwd_wave_lds(const rmsnorm_plan_t* p, int64_t N) {
     return static_cast<int64_t>(p->block_threads / 64) * (64 / p->lanes_per_row) * N * 4;
+}
+
+// Dynamic LDS of the block row pass: with R rows per workgroup, the dw
+// partials of slots 1 .. R - 1 (VPT vectors of vec_elems floats per thread).
+int64_t bwd_block_lds(const rmsnorm_plan_t* p, int dtype) {
+    if (p->row_slots <= 1) return 0;
+    return static_cast<int64_t>(p->block_threads / p->row_slots) * (p->row_slots - 1) * p->vectors_per_lane *
+           elems_per_vector(dtype) * 4;
 }
 
 // Dynamic LDS of the shifted row pass: with three chunks per thread, each
@@ -895,13 +904,20 @@ int finish_bwd_plan(rmsnorm_plan_t* p, int64_t M, int64_t N, int dtype, bool vec
                 p->rows_per_trip = static_cast<int64_t>(p->block_threads / 64) * (64 / p->lanes_per_row) * p->row_slots;
             }
         } else {
-            p->row_slots = 1;
-            p->lanes_per_row = p->block_threads;
-            k = find_bwd_kernel(RMSNORM_VARIANT_BLOCK, dtype, 0, p->vectors_per_lane, 1, pf);
+            // row_slots rows per workgroup (0 reads as 1), block_threads / row_slots threads each
+            if (p->row_slots <= 1) p->row_slots = 1;
+            if (p->row_slots != 2 && p->row_slots != 4 && p->row_slots != 1)
+                return fail(RMSNORM_ERR_PLAN, "backward block plans take 1, 2 or 4 rows per workgroup");
+            if (p->block_threads % (64 * p->row_slots) != 0)
+                return fail(RMSNORM_ERR_PLAN, "block_threads must give each of the row_slots rows whole waves");
+            p->lanes_per_row = p->block_threads / p->row_slots;
+            k = find_bwd_kernel(RMSNORM_VARIANT_BLOCK, dtype, 0, p->vectors_per_lane, p->row_slots, pf);
             if (k) {
-                if (static_cast<int64_t>(p->block_threads) * p->vectors_per_lane * epv < N)
+                if (static_cast<int64_t>(p->lanes_per_row) * p->vectors_per_lane * epv < N)
                     return fail(RMSNORM_ERR_PLAN, "block plan does not cover N");
-                p->rows_per_trip = 1;
+                if (bwd_block_lds(p, dtype) > kBwdMaxLds)
+                    return fail(RMSNORM_ERR_PLAN, "block plan needs more than 64 KiB of LDS for its slots' dw");
+                p->rows_per_trip = p->row_slots;
             }
         }
     } else if (p->variant == RMSNORM_VARIANT_WIDE) {
@@ -1037,6 +1053,16 @@ int choose_bwd_plan(int64_t M, int64_t N, bool vec_ok, bool shifted_ok, int dtyp
         p->row_slots = 1;
         p->block_threads = nvec <= 512 ? 256 : (nvec <= 1024 ? 512 : 1024);
         p->vectors_per_lane = static_cast<int>(ceil_div(nvec, p->block_threads));
+        // Rows of 256 threads go four to a 1024-thread workgroup: one workgroup
+        // per CU with the next trip's rows loaded ahead, and a quarter of the
+        // partial rows (8192 x 3000 bf16: 31.1 us against 34.7 us with 768
+        // single-row workgroups; 16384 x 2048: 38.5 against 40.0).  Rows of
+        // 512 threads stay one to a workgroup (32768 x 8192: 269-280 us two
+        // to a workgroup against 265 us).
+        if (p->block_threads == 256 && find_bwd_kernel(RMSNORM_VARIANT_BLOCK, dtype, 0, p->vectors_per_lane, 4, true)) {
+            p->row_slots = 4;
+            p->block_threads = 1024;
+        }
     } else {
         // rows wider than x and dy can stay in registers: two passes over the row
         p->variant = RMSNORM_VARIANT_WIDE;
@@ -1047,6 +1073,7 @@ int choose_bwd_plan(int64_t M, int64_t N, bool vec_ok, bool shifted_ok, int dtyp
     int64_t rows_per_trip = 1;
     if (p->variant == RMSNORM_VARIANT_WAVE || p->variant == RMSNORM_VARIANT_SHIFTED_WAVE)
         rows_per_trip = static_cast<int64_t>(p->block_threads / 64) * (64 / p->lanes_per_row) * p->row_slots;
+    if (p->variant == RMSNORM_VARIANT_BLOCK) rows_per_trip = p->row_slots;
     const int64_t need = M > 0 ? ceil_div(M, rows_per_trip) : 1;
     int64_t cap = kBwdPartialsGeneric;
     if (p->variant != RMSNORM_VARIANT_GENERIC) {
@@ -1068,7 +1095,8 @@ int choose_bwd_plan(int64_t M, int64_t N, bool vec_ok, bool shifted_ok, int dtyp
         find_bwd_kernel(RMSNORM_VARIANT_WAVE, dtype, p->lanes_per_row, p->vectors_per_lane, p->row_slots, true))
         p->prefetch = 1;
     if (ahead && (p->variant == RMSNORM_VARIANT_BLOCK || p->variant == RMSNORM_VARIANT_SHIFTED) &&
-        find_bwd_kernel(p->variant, dtype, 0, p->vectors_per_lane, 1, true))
+        find_bwd_kernel(p->variant, dtype, 0, p->vectors_per_lane, p->variant == RMSNORM_VARIANT_BLOCK ? p->row_slots : 1,
+                        true))
         p->prefetch = 1;
     return RMSNORM_OK;
 }
@@ -1103,6 +1131,7 @@ int launch_bwd(const KernelEntry* k, const rmsnorm_plan_t* p, const void* x, con
         const bool wave = p->variant == RMSNORM_VARIANT_WAVE || p->variant == RMSNORM_VARIANT_SHIFTED_WAVE;
         size_t lds = wave ? static_cast<size_t>(bwd_wave_lds(p, N)) : 0;
         if (p->variant == RMSNORM_VARIANT_SHIFTED) lds = static_cast<size_t>(bwd_shifted_lds(p, k->dtype));
+        if (p->variant == RMSNORM_VARIANT_BLOCK) lds = static_cast<size_t>(bwd_block_lds(p, k->dtype));
         hipError_t e = hipLaunchKernel(k->func, dim3(static_cast<unsigned>(p->grid)),
                                        dim3(static_cast<unsigned>(p->block_threads)), args, lds, s);
         if (e != hipSuccess)

@@ -214,89 +214,103 @@ __global__ __launch_bounds__(1024) void rmsnorm_bwd_wave(BwdArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// Row pass, block family (N > 1024): one row per workgroup per trip, thread t
-// holding vectors v * T + t (with PREFETCH the next row is loaded before this
-// row's reduction); c is reduced across waves through LDS (double buffered,
-// one barrier per row); each thread's dw partial covers its own columns and
-// is written straight to the workspace.
+// Row pass, block family (N > 1024): R rows per workgroup per trip, one per
+// slot of T = threads / R threads, thread t of a slot holding vectors
+// v * T + t of its row (with PREFETCH the next trip's rows are loaded before
+// this trip's reductions); c is reduced across each slot's waves through LDS
+// (double buffered, one barrier per trip); each thread's dw partial covers
+// its own columns.  With one slot it is written straight to the workspace;
+// with several, the slots' partials of the same columns are added in LDS in
+// slot order first, so a workgroup still writes one partial row: R times
+// fewer partial rows for the column pass at the same waves per CU.
+// Dynamic LDS: (R - 1) x VPT x T x EPV floats.
 // ---------------------------------------------------------------------------
-template <class D, int VPT, bool PREFETCH>
+template <class D, int VPT, bool PREFETCH, int R>
 __global__ __launch_bounds__(1024) void rmsnorm_bwd_block(BwdArgs a) {
+    constexpr int EPV = D::EPV;
     __shared__ float part[2][16];
+    extern __shared__ float lds_slot[];          // R > 1: [R - 1][VPT][EPV][T], slots 1 .. R - 1
     const u32x4* __restrict__ x = static_cast<const u32x4*>(a.x);
     const u32x4* __restrict__ w = static_cast<const u32x4*>(a.w);
     const u32x4* __restrict__ dy = static_cast<const u32x4*>(a.dy);
     const float* __restrict__ rstd = a.rstd;
     u32x4* __restrict__ dx = static_cast<u32x4*>(a.dx);
     const int64_t M = a.M;
-    const int nvec = static_cast<int>(a.N / D::EPV);
+    const int nvec = static_cast<int>(a.N / EPV);
     const int tid = threadIdx.x;
     const int nt = a.threads;
+    const int T = nt / R;                        // threads per row
+    const int q = R == 1 ? 0 : tid / T;          // slot
+    const int t = R == 1 ? tid : tid - q * T;
     const int lane = tid & 63;
     const int wid = tid >> 6;
-    const int nw = nt >> 6;
+    const int wq = T >> 6;                       // waves per slot
 
-    u32x4 wq[VPT];
-    float dwp[VPT][D::EPV];
+    u32x4 wq4[VPT];
+    float dwp[VPT][EPV];
 #pragma unroll
     for (int v = 0; v < VPT; ++v) {
-        const int c = v * nt + tid;
-        wq[v] = c < nvec ? w[c] : kZero;
+        const int c = v * T + t;
+        wq4[v] = c < nvec ? w[c] : kZero;
 #pragma unroll
-        for (int k = 0; k < D::EPV; ++k) dwp[v][k] = 0.0f;
+        for (int k = 0; k < EPV; ++k) dwp[v][k] = 0.0f;
     }
 
-    auto load_row = [&](u32x4 (&xd)[VPT], u32x4 (&dd)[VPT], float& r, int64_t rr) {
-        const RowOff o = row_offsets(a, rr);
+    // the row of this slot in trip g; rows past the end load zeros and store nothing
+    auto load_row = [&](u32x4 (&xd)[VPT], u32x4 (&dd)[VPT], float& r, int64_t g) {
+        const int64_t rr = g * R + q;
+        const bool live = rr < M;
+        const RowOff o = row_offsets(a, live ? rr : 0);
         const u32x4* xr = vec_at<D>(x, o.x);
         const u32x4* dr = vec_at<D>(dy, o.dy);
 #pragma unroll
         for (int v = 0; v < VPT; ++v) {
-            const int c = v * nt + tid;
-            xd[v] = c < nvec ? stream_load(xr + c) : kZero;
-            dd[v] = c < nvec ? stream_load(dr + c) : kZero;
+            const int c = v * T + t;
+            xd[v] = (live && c < nvec) ? stream_load(xr + c) : kZero;
+            dd[v] = (live && c < nvec) ? stream_load(dr + c) : kZero;
         }
-        r = rstd[rr];
+        r = live ? rstd[rr] : 0.0f;
     };
 
     int par = 0;
-    int64_t row = blockIdx.x;
+    int64_t g = blockIdx.x;
     u32x4 xd[VPT], dd[VPT];
     float r = 0.0f;
-    if (PREFETCH && row < M) load_row(xd, dd, r, row);
-    while (row < M) {
-        const int64_t next = row + a.grid;
+    if (PREFETCH && g * R < M) load_row(xd, dd, r, g);
+    while (g * R < M) {
+        const int64_t next = g + a.grid;
         u32x4 xn[VPT], dn[VPT];
         float rn = 0.0f;
         if constexpr (PREFETCH) {
-            if (next < M) load_row(xn, dn, rn, next);
+            if (next * R < M) load_row(xn, dn, rn, next);
         } else {
-            load_row(xd, dd, r, row);
+            load_row(xd, dd, r, g);
         }
-        float t = 0.0f;
+        float tsum = 0.0f;
 #pragma unroll
         for (int v = 0; v < VPT; ++v) {
-            float g[D::EPV];
-            widen_g<D>(g, wq[v], a.offset);
-            t = dot_dgx<D>(dd[v], xd[v], g, t);
+            float gw[EPV];
+            widen_g<D>(gw, wq4[v], a.offset);
+            tsum = dot_dgx<D>(dd[v], xd[v], gw, tsum);
         }
-        t = segment_allreduce<64>(t);
-        if (lane == 0) part[par][wid] = t;
+        tsum = segment_allreduce<64>(tsum);
+        if (lane == 0) part[par][wid] = tsum;
         __syncthreads();
-        float tot = part[par][0];
-        for (int i = 1; i < nw; ++i) tot += part[par][i];
+        float tot = part[par][q * wq];
+        for (int i = 1; i < wq; ++i) tot += part[par][q * wq + i];
         const float r2c = r * r * (tot * a.inv_n);
-        u32x4* out = vec_at<D>(dx, row_offsets(a, row).dx);
+        const int64_t row = g * R + q;
+        u32x4* out = vec_at<D>(dx, row_offsets(a, row < M ? row : 0).dx);
 #pragma unroll
         for (int v = 0; v < VPT; ++v) {
-            const int c = v * nt + tid;
-            float g[D::EPV];
-            widen_g<D>(g, wq[v], a.offset);
-            const u32x4 o = grad_vector<D>(dd[v], xd[v], g, r, r2c, dwp[v]);
-            if (c < nvec) stream_store(out + c, o);
+            const int c = v * T + t;
+            float gw[EPV];
+            widen_g<D>(gw, wq4[v], a.offset);
+            const u32x4 o = grad_vector<D>(dd[v], xd[v], gw, r, r2c, dwp[v]);
+            if (row < M && c < nvec) stream_store(out + c, o);
         }
         par ^= 1;
-        row = next;
+        g = next;
         if constexpr (PREFETCH) {
 #pragma unroll
             for (int v = 0; v < VPT; ++v) {
@@ -307,13 +321,29 @@ __global__ __launch_bounds__(1024) void rmsnorm_bwd_block(BwdArgs a) {
         }
     }
 
+    if constexpr (R > 1) {
+        // slots 1 .. R - 1 hand their partials to slot 0, which adds them in slot order
+        if (q > 0) {
+#pragma unroll
+            for (int v = 0; v < VPT; ++v)
+#pragma unroll
+                for (int k = 0; k < EPV; ++k) lds_slot[(((q - 1) * VPT + v) * EPV + k) * T + t] = dwp[v][k];
+        }
+        __syncthreads();
+        if (q > 0) return;
+#pragma unroll
+        for (int v = 0; v < VPT; ++v)
+#pragma unroll
+            for (int k = 0; k < EPV; ++k)
+                for (int s2 = 1; s2 < R; ++s2) dwp[v][k] += lds_slot[(((s2 - 1) * VPT + v) * EPV + k) * T + t];
+    }
     float* dst = a.partials + static_cast<int64_t>(blockIdx.x) * a.N;
 #pragma unroll
     for (int v = 0; v < VPT; ++v) {
-        const int c = v * nt + tid;
+        const int c = v * T + t;
         if (c < nvec) {
 #pragma unroll
-            for (int k = 0; k < D::EPV; ++k) dst[c * D::EPV + k] = dwp[v][k];
+            for (int k = 0; k < EPV; ++k) dst[c * EPV + k] = dwp[v][k];
         }
     }
 }
@@ -1034,10 +1064,11 @@ __global__ __launch_bounds__(COLS * SPLIT) void rmsnorm_dw_reduce(const float* _
      reinterpret_cast<const void*>(&rmsnorm_bwd_wave<D, L, V, S, P>),                          \
      "rmsnorm_bwd_wave<" #D "," #L "," #V "," #S "," #P ">"}
 #define RMS_BWD_WAVE2(D, DT, L, V, S) RMS_BWD_WAVE(D, DT, L, V, S, false), RMS_BWD_WAVE(D, DT, L, V, S, true)
-#define RMS_BWD_BLOCK(D, DT, V, P)                                                             \
-    {RMSNORM_VARIANT_BLOCK, DT, 0, V, 1, P, false,                                                    \
-     reinterpret_cast<const void*>(&rmsnorm_bwd_block<D, V, P>),                               \
-     "rmsnorm_bwd_block<" #D "," #V "," #P ">"}
+#define RMS_BWD_BLOCK_R(D, DT, V, R, P)                                                        \
+    {RMSNORM_VARIANT_BLOCK, DT, 0, V, R, P, false,                                                    \
+     reinterpret_cast<const void*>(&rmsnorm_bwd_block<D, V, P, R>),                            \
+     "rmsnorm_bwd_block<" #D "," #V "," #P "," #R ">"}
+#define RMS_BWD_BLOCK(D, DT, V, P) RMS_BWD_BLOCK_R(D, DT, V, 1, P)
 #define RMS_BWD_WIDE(D, DT, V)                                                                 \
     {RMSNORM_VARIANT_WIDE, DT, 0, V, 1, false, false,                                                 \
      reinterpret_cast<const void*>(&rmsnorm_bwd_wide<D, V>), "rmsnorm_bwd_wide<" #D "," #V ">"}
@@ -1069,6 +1100,10 @@ __global__ __launch_bounds__(COLS * SPLIT) void rmsnorm_dw_reduce(const float* _
     RMS_BWD_WAVE(D, DT, 64, 2, 2, false),                                                      \
     RMS_BWD_BLOCK(D, DT, 1, false), RMS_BWD_BLOCK(D, DT, 1, true),                             \
     RMS_BWD_BLOCK(D, DT, 2, false), RMS_BWD_BLOCK(D, DT, 2, true),                             \
+    RMS_BWD_BLOCK_R(D, DT, 1, 2, false), RMS_BWD_BLOCK_R(D, DT, 1, 2, true),                   \
+    RMS_BWD_BLOCK_R(D, DT, 2, 2, false), RMS_BWD_BLOCK_R(D, DT, 2, 2, true),                   \
+    RMS_BWD_BLOCK_R(D, DT, 1, 4, false), RMS_BWD_BLOCK_R(D, DT, 1, 4, true),                   \
+    RMS_BWD_BLOCK_R(D, DT, 2, 4, false), RMS_BWD_BLOCK_R(D, DT, 2, 4, true),                   \
     RMS_BWD_WIDE(D, DT, 3), RMS_BWD_WIDE(D, DT, 4),                                            \
     RMS_BWD_SHIFTED(D, DT, 1, false), RMS_BWD_SHIFTED(D, DT, 1, true),                         \
     RMS_BWD_SHIFTED(D, DT, 2, false), RMS_BWD_SHIFTED(D, DT, 2, true),                         \

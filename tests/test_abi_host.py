@@ -421,8 +421,13 @@ def test_bwd_plans_and_workspace():
     p = plan(32768, 8192)
     assert (p.variant, p.block_threads, p.vectors_per_lane, p.grid) == (bnd.VARIANT_BLOCK, 512, 2, 512)
     assert p.prefetch == 0 and ws(32768, 8192) == 512 * 8192 * 4      # two workgroups per unit: no prefetch
-    p = plan(8192, 3000)
-    assert (p.variant, p.block_threads, p.vectors_per_lane, p.grid) == (bnd.VARIANT_BLOCK, 256, 2, 768)
+    p = plan(8192, 3000)                  # rows of 256 threads, four to a workgroup, next trip ahead
+    assert (p.variant, p.block_threads, p.lanes_per_row, p.row_slots, p.vectors_per_lane) == \
+        (bnd.VARIANT_BLOCK, 1024, 256, 4, 2)
+    assert (p.rows_per_trip, p.grid, p.prefetch, p.trips) == (4, 256, 1, 8)
+    assert ws(8192, 3000) == 256 * 3000 * 4
+    p = plan(100, 2048)                   # 25 trips of 4 rows, 3M/32 = 9 workgroups
+    assert (p.row_slots, p.grid, p.prefetch) == (4, 9, 1)
     p = plan(4096, 16384, FP16)
     assert (p.variant, p.block_threads, p.vectors_per_lane, p.grid, p.prefetch) == (bnd.VARIANT_BLOCK, 1024, 2, 256, 1)
     assert plan(64, 8192).grid == 6                              # 3M/32 bounds the workspace traffic

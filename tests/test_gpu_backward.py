@@ -109,9 +109,10 @@ def bwd_candidates(bnd, M, N, dtype):
                                                  row_slots=slots, block_threads=threads, prefetch=pf))
         for threads in (64, 128, 256, 512, 1024):
             for vpt in (1, 2):
-                if threads * vpt * epv >= N:
-                    out.append(base.copy(variant=bnd.VARIANT_BLOCK, block_threads=threads, vectors_per_lane=vpt,
-                                         row_slots=1, prefetch=pf))
+                for rows in (1, 2, 4):             # rows per workgroup, threads / rows each
+                    if threads // rows >= 64 and threads // rows * vpt * epv >= N:
+                        out.append(base.copy(variant=bnd.VARIANT_BLOCK, block_threads=threads, vectors_per_lane=vpt,
+                                             row_slots=rows, prefetch=pf))
     for threads in (256, 512, 1024):
         for vpt in (3, 4, 6):
             if threads * vpt * epv >= N:
