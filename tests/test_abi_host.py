@@ -428,6 +428,8 @@ def test_bwd_plans_and_workspace():
     assert ws(8192, 3000) == 256 * 3000 * 4
     p = plan(100, 2048)                   # 25 trips of 4 rows, 3M/32 = 9 workgroups
     assert (p.row_slots, p.grid, p.prefetch) == (4, 9, 1)
+    p = plan(4096, 4096, FP32)            # 3M/32 = 384 rounds down to whole CUs: 256, next row ahead
+    assert (p.block_threads, p.row_slots, p.grid, p.prefetch) == (512, 1, 256, 1)
     p = plan(4096, 16384, FP16)
     assert (p.variant, p.block_threads, p.vectors_per_lane, p.grid, p.prefetch) == (bnd.VARIANT_BLOCK, 1024, 2, 256, 1)
     assert plan(64, 8192).grid == 6                              # 3M/32 bounds the workspace traffic
