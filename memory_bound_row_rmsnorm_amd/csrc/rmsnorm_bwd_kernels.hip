@@ -244,14 +244,14 @@ __global__ __launch_bounds__(1024) void rmsnorm_bwd_block(BwdArgs a) {
     const int t = R == 1 ? tid : tid - q * T;
     const int lane = tid & 63;
     const int wid = tid >> 6;
-    const int wq = T >> 6;                       // waves per slot
+    const int wps = T >> 6;                      // waves per slot
 
-    u32x4 wq4[VPT];
+    u32x4 wpk[VPT];                              // packed weights of this thread's vectors
     float dwp[VPT][EPV];
 #pragma unroll
     for (int v = 0; v < VPT; ++v) {
         const int c = v * T + t;
-        wq4[v] = c < nvec ? w[c] : kZero;
+        wpk[v] = c < nvec ? w[c] : kZero;
 #pragma unroll
         for (int k = 0; k < EPV; ++k) dwp[v][k] = 0.0f;
     }
@@ -290,14 +290,14 @@ __global__ __launch_bounds__(1024) void rmsnorm_bwd_block(BwdArgs a) {
 #pragma unroll
         for (int v = 0; v < VPT; ++v) {
             float gw[EPV];
-            widen_g<D>(gw, wq4[v], a.offset);
+            widen_g<D>(gw, wpk[v], a.offset);
             tsum = dot_dgx<D>(dd[v], xd[v], gw, tsum);
         }
         tsum = segment_allreduce<64>(tsum);
         if (lane == 0) part[par][wid] = tsum;
         __syncthreads();
-        float tot = part[par][q * wq];
-        for (int i = 1; i < wq; ++i) tot += part[par][q * wq + i];
+        float tot = part[par][q * wps];
+        for (int i = 1; i < wps; ++i) tot += part[par][q * wps + i];
         const float r2c = r * r * (tot * a.inv_n);
         const int64_t row = g * R + q;
         u32x4* out = vec_at<D>(dx, row_offsets(a, row < M ? row : 0).dx);
@@ -305,7 +305,7 @@ __global__ __launch_bounds__(1024) void rmsnorm_bwd_block(BwdArgs a) {
         for (int v = 0; v < VPT; ++v) {
             const int c = v * T + t;
             float gw[EPV];
-            widen_g<D>(gw, wq4[v], a.offset);
+            widen_g<D>(gw, wpk[v], a.offset);
             const u32x4 o = grad_vector<D>(dd[v], xd[v], gw, r, r2c, dwp[v]);
             if (row < M && c < nvec) stream_store(out + c, o);
         }
