@@ -212,7 +212,7 @@ def test_bwd_in_place_and_stream(bnd):
 
 
 @pytest.mark.parametrize("name", ["rmsnorm_16384x512_bf16", "rmsnorm_32768x8192_bf16_outliers",
-                                  "rmsnorm_262144x128_fp16"])
+                                  "rmsnorm_262144x128_fp16", "rmsnorm_8192x3000_bf16_offset1"])
 def test_bwd_deterministic(bnd, name):
     wl = workloads.WORKLOADS[name]
     announce("bwd determinism", name)
