@@ -174,6 +174,8 @@ def load_copy_ceiling():
     vp, i64, i32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32
     lib.copy_ceiling.argtypes = [vp, vp, i64, i32, i32, i64, vp]
     lib.copy_ceiling.restype = ctypes.c_int
+    lib.copy_ceiling_sched.argtypes = [vp, vp, i64, i32, i32, i64, i32, vp]
+    lib.copy_ceiling_sched.restype = ctypes.c_int
     lib.stream_part.argtypes = [vp, vp, i64, i32, i32, vp]
     lib.stream_part.restype = ctypes.c_int
     return lib
@@ -498,7 +500,8 @@ class Rotation:
         return (self.y_off) * self.wl.elem_bytes
 
 
-def forward_launcher(rot: Rotation, plan, kernel: str = "rmsnorm", copy_vpl: int = 4, copy_threads: int = 256):
+def forward_launcher(rot: Rotation, plan, kernel: str = "rmsnorm", copy_vpl: int = 4, copy_threads: int = 256,
+                     copy_stores: str = "serial"):
     """launch(k, stream_handle) for set k of the rotation: the forward with `plan`, torch's device
     copy of x into y, or the streaming copy of libcopy_ceiling.so."""
     from memory_bound_row_rmsnorm_amd import binding
@@ -508,6 +511,7 @@ def forward_launcher(rot: Rotation, plan, kernel: str = "rmsnorm", copy_vpl: int
     pplan = binding.ctypes.byref(plan)
     code = binding.DTYPE_NAMES[wl.dtype]
     copy_lib = load_copy_ceiling() if kernel in REFERENCE_KERNELS else None
+    serial = {"serial": 1, "pipelined": 0}[copy_stores]
 
     def launch(k: int, h):
         if kernel == "copy":
@@ -515,7 +519,7 @@ def forward_launcher(rot: Rotation, plan, kernel: str = "rmsnorm", copy_vpl: int
             return
         xp, wp, yp, rp = rot.pointers(k)
         if kernel == "hip_copy":
-            st = copy_lib.copy_ceiling(xp, yp, rot.x_bytes, copy_vpl, copy_threads, 0, h)
+            st = copy_lib.copy_ceiling_sched(xp, yp, rot.x_bytes, copy_vpl, copy_threads, 0, serial, h)
             if st != 0:
                 raise RuntimeError(f"copy_ceiling returned {st}")
             return
@@ -712,6 +716,9 @@ def main() -> int:
     ap.add_argument("--copy-vpl", type=int, default=4, choices=[1, 2, 4, 8],
                     help="hip_copy: contiguous KiB each wave moves per run")
     ap.add_argument("--copy-threads", type=int, default=256, help="hip_copy: workgroup size")
+    ap.add_argument("--copy-stores", choices=["serial", "pipelined"], default="serial",
+                    help="hip_copy: one store in flight per wave (each waits for the wave's earlier "
+                         "memory operations), or stores back to back")
     args = ap.parse_args()
 
     if args.traffic_from:
@@ -779,7 +786,7 @@ def main() -> int:
             sets = rotation_sets(x_bytes)
             rot = Rotation(w, sets, dev, buf=pool)
             plan, res = forward_plan(rot, args)
-            launch = forward_launcher(rot, plan, args.kernel, args.copy_vpl, args.copy_threads)
+            launch = forward_launcher(rot, plan, args.kernel, args.copy_vpl, args.copy_threads, args.copy_stores)
             ms, _ = time_launches(launch, sets, args.steps, args.warmup, args.mode)
             nbytes = step_bytes(w, args.kernel)
             print(json.dumps({"M": M, "N": w.N, "dtype": w.dtype, "kernel": args.kernel,
@@ -802,7 +809,7 @@ def main() -> int:
     rot = Rotation(wl, sets, dev)
     plan, res = forward_plan(rot, args)
     log("plan", plan.as_dict(), "resources", res)
-    launch = forward_launcher(rot, plan, args.kernel, args.copy_vpl, args.copy_threads)
+    launch = forward_launcher(rot, plan, args.kernel, args.copy_vpl, args.copy_threads, args.copy_stores)
     ms_per_step, wall_s = time_launches(launch, sets, args.steps, args.warmup, args.mode)
     nbytes = step_bytes(wl, args.kernel)
     gbps = gbps_of(nbytes, ms_per_step)
@@ -840,7 +847,8 @@ def main() -> int:
             "inputs": inputs_label(sets, x_bytes),
             "launch": args.mode,
             "kernel": args.kernel,
-            **({"copy": {"kib_per_wave_run": args.copy_vpl, "threads": args.copy_threads}}
+            **({"copy": {"kib_per_wave_run": args.copy_vpl, "threads": args.copy_threads,
+                         "stores": args.copy_stores}}
                if args.kernel == "hip_copy" else {}),
             "plan": {k: v for k, v in plan.as_dict().items()},
             "kernel_resources": res,

@@ -10,6 +10,18 @@
 // Each wave copies runs of VPL contiguous KiB: lane l moves the 16-byte
 // vectors run * 64 * VPL + v * 64 + l, v < VPL, all loads before the first
 // store.  Waves loop over runs with a grid stride.
+//
+// Two store schedules, both plain code.  Serial: each store waits until every
+// earlier memory operation of the wave has completed, so a wave has one store
+// in flight at a time (what the compiler emits for loads and stores that each
+// sit under their own bounds branch).  Pipelined: the loads are unconditional
+// (a lane past the end re-reads the last vector) and the stores go out back
+// to back, each waiting only for its own load.  Neither wins everywhere.
+// Measured on MI355X with inputs cold in HBM, 256-thread workgroups:
+// 16384 x 512 bf16's bytes 5.94 us pipelined at 8 KiB per wave against 6.09
+// serial; 8192 x 3000 bf16's 16.33 us serial against 17.36 pipelined;
+// 32768 x 8192 bf16's 166.2 us at 1 KiB per wave (one store per lane, so the
+// schedules agree) against 172.1 pipelined and 185.5 serial at 8 KiB.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -17,7 +29,7 @@ namespace {
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
-template <int VPL>
+template <int VPL, bool SERIAL>
 __global__ __launch_bounds__(1024) void copy_runs(const u32x4* __restrict__ src, u32x4* __restrict__ dst,
                                                   int64_t nvec) {
     const int lane = threadIdx.x & 63;
@@ -28,11 +40,17 @@ __global__ __launch_bounds__(1024) void copy_runs(const u32x4* __restrict__ src,
         const int64_t base = run * 64 * VPL + lane;
         u32x4 d[VPL];
 #pragma unroll
-        for (int v = 0; v < VPL; ++v)
-            d[v] = base + v * 64 < nvec ? __builtin_nontemporal_load(src + base + v * 64) : u32x4{0u, 0u, 0u, 0u};
+        for (int v = 0; v < VPL; ++v) {
+            const int64_t c = base + v * 64;
+            d[v] = __builtin_nontemporal_load(src + (c < nvec ? c : nvec - 1));
+        }
 #pragma unroll
-        for (int v = 0; v < VPL; ++v)
-            if (base + v * 64 < nvec) __builtin_nontemporal_store(d[v], dst + base + v * 64);
+        for (int v = 0; v < VPL; ++v) {
+            if (base + v * 64 < nvec) {
+                if constexpr (SERIAL) __builtin_amdgcn_s_waitcnt(0);   // every counter at zero
+                __builtin_nontemporal_store(d[v], dst + base + v * 64);
+            }
+        }
     }
 }
 
@@ -101,27 +119,36 @@ extern "C" {
 // Copy `bytes` bytes from src to dst (device pointers, 16-byte aligned, not
 // overlapping; bytes a multiple of 16) on `stream` (NULL = null stream).
 // vpl: KiB per wave per run, 1, 2, 4 or 8; threads: workgroup size, a
-// multiple of 64 up to 1024; grid: workgroups, or <= 0 for one run per wave.
+// multiple of 64 up to 1024; grid: workgroups, or <= 0 for one run per wave;
+// serial_stores: 1 for the serial store schedule, 0 for the pipelined one.
 // Returns 0, 1 for bad arguments (checked before any HIP call), 2 when the
 // launch fails.
-int copy_ceiling(const void* src, void* dst, int64_t bytes, int32_t vpl, int32_t threads, int64_t grid,
-                 void* stream) {
+int copy_ceiling_sched(const void* src, void* dst, int64_t bytes, int32_t vpl, int32_t threads, int64_t grid,
+                       int32_t serial_stores, void* stream) {
     if (bytes < 0 || bytes % 16 != 0) return 1;
     if (bytes > 0 && (!src || !dst)) return 1;
     if ((reinterpret_cast<uintptr_t>(src) | reinterpret_cast<uintptr_t>(dst)) & 15u) return 1;
     if (threads < 64 || threads > 1024 || threads % 64 != 0) return 1;
+    if (serial_stores != 0 && serial_stores != 1) return 1;
+    const bool ser = serial_stores == 1;
     const void* k = nullptr;
     switch (vpl) {
-        case 1: k = reinterpret_cast<const void*>(&copy_runs<1>); break;
-        case 2: k = reinterpret_cast<const void*>(&copy_runs<2>); break;
-        case 4: k = reinterpret_cast<const void*>(&copy_runs<4>); break;
-        case 8: k = reinterpret_cast<const void*>(&copy_runs<8>); break;
+        case 1: k = ser ? reinterpret_cast<const void*>(&copy_runs<1, true>) : reinterpret_cast<const void*>(&copy_runs<1, false>); break;
+        case 2: k = ser ? reinterpret_cast<const void*>(&copy_runs<2, true>) : reinterpret_cast<const void*>(&copy_runs<2, false>); break;
+        case 4: k = ser ? reinterpret_cast<const void*>(&copy_runs<4, true>) : reinterpret_cast<const void*>(&copy_runs<4, false>); break;
+        case 8: k = ser ? reinterpret_cast<const void*>(&copy_runs<8, true>) : reinterpret_cast<const void*>(&copy_runs<8, false>); break;
         default: return 1;
     }
     const char* s0 = static_cast<const char*>(src);
     const char* d0 = static_cast<const char*>(dst);
     if (s0 < d0 + bytes && d0 < s0 + bytes) return 1;
     return launch_runs(k, src, dst, bytes, vpl, threads, grid, stream);
+}
+
+// copy_ceiling_sched with the serial store schedule.
+int copy_ceiling(const void* src, void* dst, int64_t bytes, int32_t vpl, int32_t threads, int64_t grid,
+                 void* stream) {
+    return copy_ceiling_sched(src, dst, bytes, vpl, threads, grid, 1, stream);
 }
 
 // The parts of copy_ceiling's copy, with its geometry (vpl 4): mode 1 reads

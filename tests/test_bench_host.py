@@ -80,6 +80,9 @@ def test_copy_ceiling_library_rejects_bad_arguments_before_any_hip_call():
     assert lib.copy_ceiling(a, b, 1024, 4, 100, 0, None) == 1         # workgroup not whole waves
     assert lib.copy_ceiling(a, a + 512, 1024, 4, 256, 0, None) == 1   # overlap
     assert lib.copy_ceiling(None, b, 1024, 4, 256, 0, None) == 1
+    assert lib.copy_ceiling_sched(a, b, 0, 4, 256, 0, 0, None) == 0   # either schedule, nothing to copy
+    assert lib.copy_ceiling_sched(a, b, 1024, 4, 256, 0, 2, None) == 1  # no such store schedule
+    assert lib.copy_ceiling_sched(a, b, 100, 4, 256, 0, 0, None) == 1
 
 
 def test_rotation_keeps_a_gib_of_other_x_between_two_touches():
