@@ -264,6 +264,11 @@ def bench_backward(args, wl, name, dev) -> int:
     plan = binding.bwd_plan_query(wl.M, wl.N, wl.dtype, xs[0].data_ptr(), dys[0].data_ptr(), dxs[0].data_ptr())
     if args.plan:
         plan = plan.copy(**json.loads(args.plan))
+        # the derived fields (rows per trip, trips, resident grid) of the plan as overridden
+        done = binding.bwd_plan_validate(wl.M, wl.N, wl.dtype, plan, xs[0].data_ptr(), dys[0].data_ptr(),
+                                         dxs[0].data_ptr())
+        if done is not None:
+            plan = done
     ws_bytes = plan.grid * wl.N * 4
     ws = torch.empty(ws_bytes // 4 + 4, dtype=torch.float32, device=dev)
     log("bwd plan", plan.as_dict(), f"workspace {ws_bytes} bytes")

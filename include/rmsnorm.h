@@ -309,6 +309,19 @@ int rmsnorm_bwd_workspace_size(int64_t M, int64_t N, int dtype, const void* x, c
                                const void* dx, int64_t* bytes);
 
 /*
+ * Completes and checks an explicit backward plan without launching anything
+ * (the counterpart of rmsnorm_plan_validate): the derived fields (vec_elems,
+ * lanes_per_row of block plans, rows_per_trip, trips) and resident_grid
+ * (cu_count as for rmsnorm_plan_query) are filled into *out.  Returns
+ * RMSNORM_ERR_PLAN exactly when rmsnorm_bwd_with_plan would reject the plan
+ * for these sizes and pointers (contiguous rows; alignment only, they may be
+ * NULL; w taken as 16-byte aligned).  Host only unless cu_count <= 0.
+ */
+int rmsnorm_bwd_plan_validate(int64_t M, int64_t N, int dtype, const void* x, const void* dy,
+                              const void* dx, const rmsnorm_plan_t* plan, int32_t cu_count,
+                              rmsnorm_plan_t* out);
+
+/*
  * Row RMSNorm backward.
  *   x, dy   [M, N] dtype, device      w  [N] dtype, device
  *   rstd    [M] fp32, device (from rmsnorm_fwd)

@@ -36,6 +36,7 @@ EXPORTED = (
     "rmsnorm_fwd", "rmsnorm_fwd_with_plan", "rmsnorm_fwd_ex", "rmsnorm_plan_query", "rmsnorm_plan_query_ex",
     "rmsnorm_plan_resources", "rmsnorm_fwd_kernel_query",
     "rmsnorm_bwd", "rmsnorm_bwd_with_plan", "rmsnorm_bwd_plan_query", "rmsnorm_bwd_workspace_size",
+    "rmsnorm_bwd_plan_validate",
     "rmsnorm_bwd_noalloc",
     "rmsnorm_bwd_ex", "rmsnorm_bwd_plan_query_ex", "rmsnorm_bwd_workspace_size_ex",
     "rmsnorm_plan_validate", "rmsnorm_plan_set_tuned", "rmsnorm_plan_clear_tuned", "rmsnorm_plan_tuned_count",
@@ -142,6 +143,9 @@ def _load():
     lib.rmsnorm_bwd_plan_query.restype = i32
     lib.rmsnorm_bwd_workspace_size.argtypes = [i64, i64, i32, vp, vp, vp, ctypes.POINTER(ctypes.c_int64)]
     lib.rmsnorm_bwd_workspace_size.restype = i32
+    lib.rmsnorm_bwd_plan_validate.argtypes = [i64, i64, i32, vp, vp, vp, ctypes.POINTER(Plan), ctypes.c_int32,
+                                              ctypes.POINTER(Plan)]
+    lib.rmsnorm_bwd_plan_validate.restype = i32
     lib.rmsnorm_bwd_ex.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, f32, i32, ctypes.POINTER(BwdLayout),
                                    ctypes.POINTER(Plan), vp, i64, vp]
     lib.rmsnorm_bwd_ex.restype = i32
@@ -420,6 +424,19 @@ def bwd_plan_query(M: int, N: int, dtype, x_ptr: int = 0, dy_ptr: int = 0, dx_pt
     _check(lib.rmsnorm_bwd_plan_query(M, N, _dtype_code(dtype), x_ptr or None, dy_ptr or None,
                                       dx_ptr or None, cu_count, ctypes.byref(p)))
     return p
+
+
+def bwd_plan_validate(M: int, N: int, dtype, plan: Plan, x_ptr: int = 0, dy_ptr: int = 0, dx_ptr: int = 0,
+                      cu_count: int = 0):
+    """The completed backward plan (derived fields, resident_grid), or None if
+    rmsnorm_bwd_with_plan would reject it for these sizes and pointers.  Other errors raise."""
+    out = Plan()
+    st = lib.rmsnorm_bwd_plan_validate(M, N, _dtype_code(dtype), x_ptr or None, dy_ptr or None, dx_ptr or None,
+                                       ctypes.byref(plan), cu_count, ctypes.byref(out))
+    if st == 8:
+        return None
+    _check(st)
+    return out
 
 
 def bwd_workspace_size(M: int, N: int, dtype, x_ptr: int = 0, dy_ptr: int = 0, dx_ptr: int = 0) -> int:

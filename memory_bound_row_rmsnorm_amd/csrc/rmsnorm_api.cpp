@@ -1416,6 +1416,26 @@ int rmsnorm_bwd_plan_query_ex(int64_t M, int64_t N, int dtype, const void* x, co
     return RMSNORM_OK;
 }
 
+int rmsnorm_bwd_plan_validate(int64_t M, int64_t N, int dtype, const void* x, const void* dy, const void* dx,
+                              const rmsnorm_plan_t* plan, int32_t cu_count, rmsnorm_plan_t* out) {
+    g_last_error.clear();
+    if (!plan || !out) return fail(RMSNORM_ERR_NULL, "plan and out must be non-NULL");
+    int st = check_shape_dtype(M, N, dtype);
+    if (st != RMSNORM_OK) return st;
+    BwdLayout L;
+    st = normalise_bwd_layout(nullptr, M, N, &L);
+    if (st != RMSNORM_OK) return st;
+    const bool vec = bwd_vector_ok(x, kAssumedW, dy, dx, dtype, L, M, N);
+    const bool shifted = bwd_shifted_ok(x, kAssumedW, dy, dx, dtype, L, M, N, vec);
+    rmsnorm_plan_t p = *plan;
+    const KernelEntry* k = nullptr;
+    st = finish_bwd_plan(&p, M, N, dtype, vec, shifted, &k);
+    if (st == RMSNORM_OK) st = resident_grid(&p, k, cu_count, &p.resident_grid);
+    if (st != RMSNORM_OK) return st;
+    *out = p;
+    return RMSNORM_OK;
+}
+
 int rmsnorm_bwd_workspace_size(int64_t M, int64_t N, int dtype, const void* x, const void* dy, const void* dx,
                                int64_t* bytes) {
     return rmsnorm_bwd_workspace_size_ex(M, N, dtype, x, kAssumedW, dy, dx, nullptr, bytes);

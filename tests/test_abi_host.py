@@ -481,6 +481,18 @@ def test_plan_validate_matches_what_launches_accept():
         bnd.plan_validate(16384, 0, "bf16", p, cu_count=256)                                  # bad shape raises
 
 
+def test_bwd_plan_validate_fills_the_derived_fields():
+    p = bnd.bwd_plan_query(8192, 3000, "bf16", cu_count=256)
+    assert bnd.bwd_plan_validate(8192, 3000, "bf16", p, cu_count=256).as_dict() == p.as_dict()
+    v = bnd.bwd_plan_validate(8192, 3000, "bf16", p.copy(row_slots=2, block_threads=512, grid=512), cu_count=256)
+    assert (v.lanes_per_row, v.rows_per_trip, v.trips) == (256, 2, 8)     # 8192 rows / (512 x 2 a trip)
+    assert bnd.bwd_plan_validate(8192, 3000, "bf16", p.copy(row_slots=3), cu_count=256) is None
+    assert bnd.bwd_plan_validate(8192, 3000, "bf16", p.copy(xcd_group=8), cu_count=256) is None
+    assert bnd.bwd_plan_validate(8192, 3000, "bf16", p.copy(block_threads=128, row_slots=1), cu_count=256) is None  # 2048 < 3000
+    with pytest.raises(bnd.RmsnormError):
+        bnd.bwd_plan_validate(8192, 0, "bf16", p, cu_count=256)                               # bad shape raises
+
+
 def test_tuned_plan_replaces_the_rule_for_exactly_its_shape(clean_tuned):
     rule = bnd.plan_query(16384, 512, "bf16", cu_count=256)
     tuned = rule.copy(row_slots=2, block_threads=128, grid=4096)
