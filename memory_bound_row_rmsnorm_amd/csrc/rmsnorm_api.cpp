@@ -568,7 +568,8 @@ int choose_plan(int64_t M, int64_t N, int dtype, Access acc, rmsnorm_plan_t* p) 
     if (p->variant == RMSNORM_VARIANT_BLOCK || p->variant == RMSNORM_VARIANT_SHIFTED ||
         p->variant == RMSNORM_VARIANT_WIDE) {
         // about 128 KiB (1 MiB beyond the Infinity Cache) of consecutive rows per XCD: the
-        // nearest power of two rows, at least 8
+        // nearest power of two rows, at least 8 (on 8192 x 3000 bf16, groups of 16 rows took
+        // 18.06 us and of 32 rows 18.30, where 12, 20 or 24 rows took 20.7-21.2 us)
         const int64_t row_bytes = N * es;
         const int64_t target = M * row_bytes >= kInfinityCacheBytes ? kXcdGroupBytesLarge : kXcdGroupBytes;
         int g = 8;
