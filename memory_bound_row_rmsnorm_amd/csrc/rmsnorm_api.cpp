@@ -531,6 +531,16 @@ int choose_plan(int64_t M, int64_t N, int dtype, Access acc, rmsnorm_plan_t* p) 
                 break;
             }
         }
+        // Rows of exactly 64 vectors: half-wave rows, 2 vectors per lane, 4 slots (8 rows and
+        // 8 KiB per wave, 32 rows per workgroup).  Measured on MI355X at 16384 x 512 bf16 with
+        // inputs cold in HBM, exact-width forms in one process: 5.97-5.98 us against
+        // 6.13-6.21 us for 64-lane rows with 4 slots (4 KiB per wave), where a copy of the
+        // same bytes with 8 KiB per wave and stores back to back took 5.94-5.97 us.
+        if (N == 64 * elems_per_vector(dtype) && find_kernel(RMSNORM_VARIANT_WAVE, dtype, 32, 2, 4, false)) {
+            p->lanes_per_row = 32;
+            p->vectors_per_lane = 2;
+            p->row_slots = 4;
+        }
     } else {
         p->variant = RMSNORM_VARIANT_BLOCK;
         p->row_slots = 1;

@@ -937,6 +937,7 @@ __global__ __launch_bounds__(1024) void rmsnorm_generic(KernelArgs a) {
     RMS_WAVE2(D, DT, 8, 1, 1), RMS_WAVE2(D, DT, 8, 1, 2), RMS_WAVE2(D, DT, 8, 1, 4),            \
     RMS_WAVE2(D, DT, 16, 1, 1), RMS_WAVE2(D, DT, 16, 1, 2), RMS_WAVE2(D, DT, 16, 1, 4),         \
     RMS_WAVE2(D, DT, 32, 1, 1), RMS_WAVE2(D, DT, 32, 1, 2), RMS_WAVE2(D, DT, 32, 1, 4),         \
+    RMS_WAVE_T(D, DT, 32, 2, 4, false, false),                                                  \
     RMS_WAVE2(D, DT, 64, 1, 1), RMS_WAVE2(D, DT, 64, 1, 2), RMS_WAVE2(D, DT, 64, 1, 4),         \
     RMS_WAVE_T(D, DT, 64, 1, 8, false, false), RMS_WAVE_T(D, DT, 64, 1, 8, true, false),        \
     RMS_WAVE2(D, DT, 64, 2, 1), RMS_WAVE2(D, DT, 64, 2, 2), RMS_WAVE_T(D, DT, 64, 2, 4, false, false), \
@@ -985,7 +986,8 @@ struct ExactEntry {
 #define RMS_EXACT_FAMILY(D, DT)                                                                \
     RMS_WAVE_EXACT(D, DT, 4, 1, 4, 2), RMS_WAVE_EXACT(D, DT, 8, 1, 2, 2),                       \
     RMS_WAVE_EXACT(D, DT, 16, 1, 2, 2), RMS_WAVE_EXACT(D, DT, 32, 1, 2, 2),                     \
-    RMS_WAVE_EXACT(D, DT, 64, 1, 4, 4), RMS_WAVE_EXACT(D, DT, 64, 2, 2, 4)
+    RMS_WAVE_EXACT(D, DT, 64, 1, 4, 4), RMS_WAVE_EXACT(D, DT, 64, 2, 2, 4),                     \
+    RMS_WAVE_EXACT(D, DT, 32, 2, 4, 4)
 
 static const ExactEntry kExactTable[] = {
     RMS_EXACT_FAMILY(BF16, RMSNORM_BF16),

@@ -128,9 +128,13 @@ def test_host_plans_cover_the_row_one_trip_per_workgroup(M, N):
 
 
 def test_planner_choices_for_the_workloads():
-    p = host_plan(16384, 512)
-    assert (p.variant, p.lanes_per_row, p.vectors_per_lane, p.row_slots) == (bnd.VARIANT_WAVE, 64, 1, 4)
-    assert p.rows_per_trip == 16 and p.grid == 1024
+    p = host_plan(16384, 512)             # rows of exactly 64 vectors: half-wave rows, 8 KiB per wave
+    assert (p.variant, p.lanes_per_row, p.vectors_per_lane, p.row_slots) == (bnd.VARIANT_WAVE, 32, 2, 4)
+    assert p.rows_per_trip == 32 and p.grid == 512 and p.block_threads == 256
+    p = host_plan(16384, 504)             # one vector short of that: 64-lane rows, masked
+    assert (p.lanes_per_row, p.vectors_per_lane, p.row_slots) == (64, 1, 4)
+    p = host_plan(16384, 256, FP32)       # 64 fp32 vectors
+    assert (p.lanes_per_row, p.vectors_per_lane, p.row_slots) == (32, 2, 4)
     p = host_plan(262144, 128, FP16)        # several rows per slot: 2 KiB per wave, 2-wave workgroups
     assert (p.variant, p.lanes_per_row, p.row_slots, p.block_threads) == (bnd.VARIANT_WAVE, 16, 2, 128)
     assert p.rows_per_trip == 16 and p.grid == 262144 // 16
@@ -473,7 +477,8 @@ def clean_tuned():
 
 def test_plan_validate_matches_what_launches_accept():
     p = bnd.plan_query(16384, 512, "bf16", cu_count=256)
-    v = bnd.plan_validate(16384, 512, "bf16", p.copy(row_slots=2, grid=2048), cu_count=256)
+    v = bnd.plan_validate(16384, 512, "bf16", p.copy(lanes_per_row=64, vectors_per_lane=1, row_slots=2, grid=2048),
+                          cu_count=256)
     assert (v.rows_per_trip, v.trips, v.resident_grid) == (8, 1, 2048)
     assert bnd.plan_validate(16384, 512, "bf16", p.copy(vectors_per_lane=7), cu_count=256) is None
     assert bnd.plan_validate(16384, 512, "bf16", p, x_ptr=A + 2, cu_count=256) is None      # unaligned x
@@ -495,7 +500,7 @@ def test_bwd_plan_validate_fills_the_derived_fields():
 
 def test_tuned_plan_replaces_the_rule_for_exactly_its_shape(clean_tuned):
     rule = bnd.plan_query(16384, 512, "bf16", cu_count=256)
-    tuned = rule.copy(row_slots=2, block_threads=128, grid=4096)
+    tuned = rule.copy(lanes_per_row=64, vectors_per_lane=1, row_slots=2, block_threads=128, grid=4096)
     bnd.set_tuned(16384, 512, "bf16", tuned)
     assert bnd.tuned_count() == 1
     got = bnd.plan_query(16384, 512, "bf16", cu_count=256)
@@ -808,17 +813,19 @@ def test_other_launches_keep_the_general_instance():
     def name(plan=None, n=N, m=M):
         return bnd.kernel_query(m, n, "bf16", A, A, A + (1 << 30), plan=plan, resources=False)["kernel"]
 
-    assert name().startswith("rmsnorm_wave_exact<")
+    assert name() == "rmsnorm_wave_exact<BF16,32,2,4,4>"
+    lanes64 = base.copy(lanes_per_row=64, vectors_per_lane=1, grid=1024)
+    assert name(lanes64) == "rmsnorm_wave_exact<BF16,64,1,4,4>"
     # a persistent grid, a remap, prefetching: the general instance
     assert name(base.copy(grid=64)).startswith("rmsnorm_wave<")
     assert name(base.copy(xcd_group=2)).startswith("rmsnorm_wave<")
-    assert name(base.copy(prefetch=1)).startswith("rmsnorm_wave<")
+    assert name(lanes64.copy(prefetch=1)).startswith("rmsnorm_wave<")
     # a width below the plan's full row (masked columns); a single ragged row (a tail vector;
     # several ragged contiguous rows start unaligned and take a shifted kernel)
     assert name(n=504).startswith("rmsnorm_wave<")
     assert name(n=500, m=1).startswith("rmsnorm_wave<")
     # no exact form for this segment shape or workgroup size
-    assert name(base.copy(row_slots=8)).startswith("rmsnorm_wave<")
+    assert name(lanes64.copy(row_slots=8)).startswith("rmsnorm_wave<")
     assert name(base.copy(block_threads=512, grid=512)).startswith("rmsnorm_wave<")
     # the block family has its own exact forms (rows of exactly 1024 vectors here); a width
     # below the plan's full row, a persistent grid or prefetching keep the general instance
@@ -834,9 +841,9 @@ def test_other_launches_keep_the_general_instance():
 
 def test_exact_form_row_limit():
     """The exact form has no loop: it runs while one grid of fewer than 2^32 work-items covers the
-    rows (16 rows per 256-thread workgroup at N = 512, well inside its 32-bit row numbers); one
+    rows (32 rows per 256-thread workgroup at N = 512, well inside its 32-bit row numbers); one
     row more and the grid loops in the general instance."""
-    limit = (2 ** 32 - 1) // 256 * 16
+    limit = (2 ** 32 - 1) // 256 * 32
     assert limit < (1 << 31) - (1 << 16)
     below = bnd.kernel_query(limit, 512, "bf16", A, A, A + (1 << 40), resources=False)["kernel"]
     at = bnd.kernel_query(limit + 1, 512, "bf16", A, A, A + (1 << 40), resources=False)["kernel"]

@@ -36,7 +36,7 @@ def test_registered_plan_is_used_and_correct(bnd):
     wl = workloads.WORKLOADS["rmsnorm_16384x512_bf16"]
     rows = 2048
     rule = bnd.plan_query(rows, wl.N, wl.dtype)
-    tuned = rule.copy(row_slots=2, block_threads=128, grid=rows // 4)
+    tuned = rule.copy(lanes_per_row=64, vectors_per_lane=1, row_slots=2, block_threads=128, grid=rows // 4)
     bnd.set_tuned(rows, wl.N, wl.dtype, tuned)
     try:
         stats, (xg, wg, y) = run_and_check(bnd, wl, rows, "tuned plan")
