@@ -432,6 +432,7 @@ constexpr int kShiftedWaveSlots = 4;               // slots per wave per trip of
 // 66.9 us; 262144 x 100 bf16: 62.2 against 89.5 us).
 constexpr int64_t kMinShiftedWaveN = 16;
 constexpr int64_t kWaveBytesInFlight = 4096;      // row bytes one wave loads per trip
+constexpr int64_t kHalfWaveRowsMinRows = 16384;   // rows from which 64-vector rows take 32-lane segments
 constexpr int64_t kWaveBytesInFlightMultiRow = 2048;   // the same when a slot holds several rows
 constexpr int64_t kXcdGroupBytes = 128 * 1024;    // consecutive row bytes per XCD (block family)
 constexpr int64_t kXcdGroupBytesLarge = 1024 * 1024;   // the same for batches beyond the Infinity Cache
@@ -531,12 +532,15 @@ int choose_plan(int64_t M, int64_t N, int dtype, Access acc, rmsnorm_plan_t* p) 
                 break;
             }
         }
-        // Rows of exactly 64 vectors: half-wave rows, 2 vectors per lane, 4 slots (8 rows and
-        // 8 KiB per wave, 32 rows per workgroup).  Measured on MI355X at 16384 x 512 bf16 with
-        // inputs cold in HBM, exact-width forms in one process: 5.97-5.98 us against
-        // 6.13-6.21 us for 64-lane rows with 4 slots (4 KiB per wave), where a copy of the
-        // same bytes with 8 KiB per wave and stores back to back took 5.94-5.97 us.
-        if (N == 64 * elems_per_vector(dtype) && find_kernel(RMSNORM_VARIANT_WAVE, dtype, 32, 2, 4, false)) {
+        // Rows of exactly 64 vectors, 16384 rows or more: half-wave rows, 2 vectors per lane, 4
+        // slots (8 rows and 8 KiB per wave, 32 rows per workgroup, 512 workgroups or more).
+        // Measured on MI355X at 16384 x 512 bf16 with inputs cold in HBM, exact-width forms in
+        // one process: 5.97-5.98 us against 6.13-6.21 us for 64-lane rows with 4 slots (4 KiB
+        // per wave), where a copy of the same bytes with 8 KiB per wave and stores back to back
+        // took 5.94-5.97 us.  With few rows the longer waves cost more than they save: 64 x 512
+        // took 2.97 us in 2 workgroups against 2.37 us in 4 with 64-lane rows.
+        if (N == 64 * elems_per_vector(dtype) && M >= kHalfWaveRowsMinRows &&
+            find_kernel(RMSNORM_VARIANT_WAVE, dtype, 32, 2, 4, false)) {
             p->lanes_per_row = 32;
             p->vectors_per_lane = 2;
             p->row_slots = 4;

@@ -131,6 +131,8 @@ def test_planner_choices_for_the_workloads():
     p = host_plan(16384, 512)             # rows of exactly 64 vectors: half-wave rows, 8 KiB per wave
     assert (p.variant, p.lanes_per_row, p.vectors_per_lane, p.row_slots) == (bnd.VARIANT_WAVE, 32, 2, 4)
     assert p.rows_per_trip == 32 and p.grid == 512 and p.block_threads == 256
+    p = host_plan(16383, 512)             # fewer rows: 64-lane rows, 4 rows per wave
+    assert (p.lanes_per_row, p.vectors_per_lane, p.row_slots, p.grid) == (64, 1, 4, 1024)
     p = host_plan(16384, 504)             # one vector short of that: 64-lane rows, masked
     assert (p.lanes_per_row, p.vectors_per_lane, p.row_slots) == (64, 1, 4)
     p = host_plan(16384, 256, FP32)       # 64 fp32 vectors

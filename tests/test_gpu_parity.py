@@ -203,6 +203,22 @@ def test_exact_wave_forms(bnd, vectors, dtype):
         torch.cuda.synchronize()
         assert r2 is None and torch.equal(y2.view(torch.int16 if dtype != "fp32" else torch.int32),
                                           y.view(torch.int16 if dtype != "fp32" else torch.int32))
+        if vectors == 64:
+            # the 32-lane form the rule takes from 16384 rows on, here at row counts that end
+            # inside a workgroup of 32 rows
+            plan = bnd.plan_query(M, N, dtype).copy(lanes_per_row=32, vectors_per_lane=2, row_slots=4,
+                                                    block_threads=256, grid=-(-M // 32))
+            q = bnd.kernel_query(M, N, dtype, xg.data_ptr(), wg.data_ptr(), y.data_ptr(), plan=plan)
+            assert q["kernel"].endswith(",32,2,4,4>") and q["scratch_bytes"] == 0, q
+            announce("exact 32-lane", M, N, dtype, offset, q)
+            y3 = torch.full_like(xg, float("nan"))
+            r3 = torch.full((M,), float("nan"), dtype=torch.float32, device=DEV)
+            bnd.rmsnorm_fwd_out(xg, wg, y3, r3, 1e-6, offset, plan=plan)
+            torch.cuda.synchronize()
+            if dtype == "fp32":
+                parity.compare_fp32(y3, r3, ye, re, f"exact 32-lane M={M} N={N} fp32")
+            else:
+                parity.compare(y3, r3, y_ref, r_ref, dtype, f"exact 32-lane M={M} N={N} {dtype}")
 
 
 # ---------------------------------------------------------------------------
